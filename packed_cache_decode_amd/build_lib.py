@@ -1,0 +1,58 @@
+"""Build the HIP library in-tree: packed_cache_decode_amd/libtq_mi355x.so.
+
+    python -m packed_cache_decode_amd.build_lib
+
+Compiles for gfx950 only.  The store translation unit is built without
+floating-point contraction (its bytes must be reproducible bit for bit);
+packed fp32 instructions are disabled for all device code.
+"""
+
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+LIB = os.path.join(HERE, "libtq_mi355x.so")
+BUILD = os.path.join(HERE, "_build")
+
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+ARCH = "gfx950"
+COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
+          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          "-Wno-unused-command-line-argument"]
+SOURCES = [
+    ("tq_host.cpp", []),
+    ("tq_store.hip", ["-ffp-contract=off"]),
+    ("tq_decode.hip", []),
+]
+
+
+def _run(cmd):
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    if r.returncode != 0:
+        sys.stderr.write(r.stdout)
+        raise RuntimeError("build step failed: " + " ".join(cmd))
+    return r.stdout
+
+
+def build(verbose=False):
+    os.makedirs(BUILD, exist_ok=True)
+    objs = []
+    for src, extra in SOURCES:
+        obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+        cmd = [HIPCC, *COMMON, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
+        if src.endswith(".cpp"):
+            cmd = [HIPCC, *COMMON, "-x", "hip", *extra, "-c", os.path.join(CSRC, src), "-o", obj]
+        out = _run(cmd)
+        if verbose and out.strip():
+            print(out)
+        objs.append(obj)
+    tmp = LIB + ".tmp"
+    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs])
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

@@ -1,0 +1,406 @@
+// tq_decode kernels: split-KV paged decode attention over packed slots, and
+// the log-sum-exp combine of the splits.
+//
+// What is computed follows P1 ("vLLM 源码完全拆解(十九):TurboQuant KV Cache
+// 量化"), sections "读取内核" (two stages: per-split partials, then a merge),
+// "程序入口:split 区间怎么算" (kv head = q head / group), "分数计算:FP8 K 与
+// MSE K 的两条路径" (centroid gather, q_rot . c, stored norm, norm correction
+// 1/sqrt(sum c^2 + 1e-16), scale 1/sqrt(d)), "V 的解包" (code * scale + zero)
+// and "在线 softmax" (running max, rescaled sum and accumulator, fp32).
+//
+// Mapping (general path, any head_dim / bits / group size):
+//   grid (split, sequence, kv head), one wavefront each.  The G query heads
+//   of the kv head are rotated once into LDS (q_rot = R q, R = H diag(s)/sqrt(d)
+//   by butterflies), pre-multiplied by sm_scale * log2(e) so the softmax runs
+//   in base 2.  Tokens are taken 64 at a time: first lane = token (scores for
+//   all G heads from the unpacked codes), then lane = coordinates (the V codes
+//   of each token are read as one contiguous row by the whole wavefront, so
+//   every V load is coalesced), accumulating p * v for all G heads.
+//   Partials per (sequence, q head, split): acc[d], running max m (base 2),
+//   running sum l.  The combine weights split s by 2^(m_s - max m).
+#include "tq_internal.h"
+
+namespace tq {
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+struct DecodeArgs {
+  const DevTables* tables;
+  const uint16_t* q;
+  const uint8_t* cache;
+  int64_t num_blocks;
+  const int32_t* block_table;
+  int max_blocks;
+  const int32_t* seq_lens;
+  int Hq;
+  int H;
+  int bs_shift;
+  int chunk;
+  int num_splits;
+  float scale_log2;   // sm_scale * log2(e)
+  float* part;        // [B][Hq][S][D + 2]
+  void* out;
+  int out_fp32;
+};
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+__device__ __forceinline__ float f16_bits_to_f32(uint32_t b) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(b)));
+}
+
+// E4M3FN byte -> float, from the format definition (bias 7, subnormal m*2^-9)
+__device__ __forceinline__ float e4m3fn_to_f32(uint32_t b) {
+  const uint32_t e = (b >> 3) & 15u, m = b & 7u;
+  float mag;
+  if (e == 0)
+    mag = static_cast<float>(m) * (1.0f / 512.0f);
+  else if (e == 15 && m == 7)
+    mag = __uint_as_float(0x7FC00000u);
+  else
+    mag = __uint_as_float(((e + 120u) << 23) | (m << 20));
+  return (b & 0x80u) ? -mag : mag;
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int m = 1; m < 64; m *= 2) x = fmaxf(x, __shfl_xor(x, m, 64));
+  return x;
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int m = 1; m < 64; m *= 2) x += __shfl_xor(x, m, 64);
+  return x;
+}
+
+template <int D, int KB, int G>
+__global__ void __launch_bounds__(64) decode_split_kernel(DecodeArgs a) {
+  constexpr int E = D / 64;
+  constexpr bool kFp8 = KB == 8;
+  constexpr int kKeyCodeBytes = kFp8 ? D : (D * KB + 7) / 8;
+  constexpr int kKeyPacked = kFp8 ? D : kKeyCodeBytes + 2;
+  constexpr int kValOff = kKeyPacked;
+  constexpr int kValCodeBytes = D / 2;
+  constexpr int kSlotRaw = kKeyPacked + kValCodeBytes + 4;
+  constexpr int kSlot = kSlotRaw + (kSlotRaw & 1);
+
+  __shared__ float s_q[G][D];
+  __shared__ float s_cent[16];
+  __shared__ float s_p[G][64];
+  __shared__ float s_vsc[64];
+  __shared__ float s_vzr[64];
+  __shared__ int64_t s_off[64];
+
+  const int lane = threadIdx.x;
+  const int split = blockIdx.x;
+  const int b = blockIdx.y;
+  const int g = blockIdx.z;
+  const int Hq = a.Hq;
+  int T = a.seq_lens[b];
+  const int t_cap = min(a.num_splits * a.chunk, a.max_blocks << a.bs_shift);
+  if (T < 0 || T > t_cap) {
+    if (lane == 0 && split == 0 && g == 0) const_cast<DevTables*>(a.tables)->err_len = 1;
+    T = T < 0 ? 0 : t_cap;
+  }
+  const int t0 = split * a.chunk;
+  const int t1 = min(T, t0 + a.chunk);
+  float* part0 = a.part + ((static_cast<int64_t>(b) * Hq + g * G) * a.num_splits + split) * (D + 2);
+  const int64_t head_stride = static_cast<int64_t>(a.num_splits) * (D + 2);
+
+  if (t0 >= t1) {                      // empty split: acc 0, m -inf, l 0
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      float* p = part0 + j * head_stride;
+      for (int c = lane; c < D; c += 64) p[c] = 0.0f;
+      if (lane == 0) {
+        p[D] = -INFINITY;
+        p[D + 1] = 0.0f;
+      }
+    }
+    return;
+  }
+
+  // ---- rotate the G queries once (MSE keys) ----
+  if (!kFp8 && lane < 16) s_cent[lane] = a.tables->centroids[lane];
+  uint32_t sgn[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int j = E * lane + e;
+    sgn[e] = ((a.tables->sign_bits[j >> 5] >> (j & 31)) & 1u) << 31;
+  }
+  const float rsd = 1.0f / sqrtf(static_cast<float>(D));
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
+    const uint16_t* qp = a.q + (static_cast<int64_t>(b) * Hq + g * G + j) * D + E * lane;
+    float u[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) u[e] = bf16_bits_to_f32(qp[e]);
+    if constexpr (!kFp8) {
+#pragma unroll
+      for (int e = 0; e < E; ++e) u[e] = __uint_as_float(__float_as_uint(u[e]) ^ sgn[e]);
+#pragma unroll
+      for (int hs = 1; hs < E; hs *= 2)
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+          if ((e & hs) == 0) {
+            const float p = u[e], r = u[e + hs];
+            u[e] = p + r;
+            u[e + hs] = p - r;
+          }
+#pragma unroll
+      for (int lm = 1; lm < 64; lm *= 2) {
+        const bool upper = (lane & lm) != 0;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const float o = __shfl_xor(u[e], lm, 64);
+          u[e] = upper ? (o - u[e]) : (u[e] + o);
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < E; ++e) u[e] *= rsd;
+    }
+#pragma unroll
+    for (int e = 0; e < E; ++e) s_q[j][E * lane + e] = u[e] * a.scale_log2;
+  }
+  __syncthreads();
+
+  float m_run[G], l_run[G], acc[G][E];
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
+    m_run[j] = -INFINITY;
+    l_run[j] = 0.0f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[j][e] = 0.0f;
+  }
+
+  const int32_t* bt = a.block_table + static_cast<int64_t>(b) * a.max_blocks;
+  const int64_t row_bytes = static_cast<int64_t>(a.H) * kSlot;
+  const int bs_mask = (1 << a.bs_shift) - 1;
+
+  for (int tb = t0; tb < t1; tb += 64) {
+    const int t = tb + lane;
+    bool valid = t < t1;
+    int64_t off = 0;
+    if (valid) {
+      const int page = bt[t >> a.bs_shift];
+      if (page < 0 || page >= a.num_blocks) {
+        const_cast<DevTables*>(a.tables)->err_page = 1;
+        valid = false;
+      } else {
+        off = (static_cast<int64_t>(page) * (bs_mask + 1) + (t & bs_mask)) * row_bytes +
+              static_cast<int64_t>(g) * kSlot;
+      }
+    }
+    // ---- scores, lane = token ----
+    float sc[G];
+#pragma unroll
+    for (int j = 0; j < G; ++j) sc[j] = 0.0f;
+    float vsc = 0.0f, vzr = 0.0f;
+    if (valid) {
+      const uint8_t* slot = a.cache + off;
+      const uint16_t* s16 = reinterpret_cast<const uint16_t*>(slot);
+      if constexpr (kFp8) {
+        for (int w = 0; w < D / 2; ++w) {
+          const uint32_t two = s16[w];
+          const float k0 = e4m3fn_to_f32(two & 0xFF), k1 = e4m3fn_to_f32(two >> 8);
+#pragma unroll
+          for (int j = 0; j < G; ++j) sc[j] += s_q[j][2 * w] * k0 + s_q[j][2 * w + 1] * k1;
+        }
+      } else {
+        float ss = 0.0f;
+        // codes through a 16-bit window: code j at bits [j*KB, j*KB + KB)
+        uint32_t window = s16[0];
+        int have = 16;     // bits valid in window
+        int next = 1;      // next u16 to read
+#pragma unroll 8
+        for (int c = 0; c < D; ++c) {
+          if (have < KB) {
+            window |= static_cast<uint32_t>(s16[next++]) << have;
+            have += 16;
+          }
+          const int code = window & ((1u << KB) - 1u);
+          window >>= KB;
+          have -= KB;
+          const float cv = s_cent[code];
+          ss += cv * cv;
+#pragma unroll
+          for (int j = 0; j < G; ++j) sc[j] += s_q[j][c] * cv;
+        }
+        const float nrm = f16_bits_to_f32(s16[kKeyCodeBytes / 2]);
+        const float f = nrm / sqrtf(ss + 1e-16f);
+#pragma unroll
+        for (int j = 0; j < G; ++j) sc[j] *= f;
+      }
+      const uint16_t* meta = reinterpret_cast<const uint16_t*>(slot + kValOff + kValCodeBytes);
+      vsc = f16_bits_to_f32(meta[0]);
+      vzr = f16_bits_to_f32(meta[1]);
+    }
+    // ---- online softmax over this block of tokens (base 2) ----
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      const float s = valid ? sc[j] : -INFINITY;
+      const float mx = wave_max(s);
+      const float m_new = fmaxf(m_run[j], mx);
+      const float p = valid ? exp2f(s - m_new) : 0.0f;
+      const float corr = (m_run[j] == -INFINITY) ? 0.0f : exp2f(m_run[j] - m_new);
+      l_run[j] = l_run[j] * corr + wave_sum(p);
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[j][e] *= corr;
+      m_run[j] = m_new;
+      s_p[j][lane] = p;
+    }
+    s_vsc[lane] = vsc;
+    s_vzr[lane] = vzr;
+    s_off[lane] = valid ? off : -1;
+    __syncthreads();
+    // ---- p . v, lane = coordinates [E*lane, E*lane + E) ----
+    const int nt = min(64, t1 - tb);
+    for (int i = 0; i < nt; ++i) {
+      const int64_t o = s_off[i];
+      if (o < 0) continue;
+      const uint8_t* vrow = a.cache + o + kValOff;
+      float vh[E];
+      if constexpr (E == 1) {
+        const uint32_t byte = vrow[lane >> 1];
+        vh[0] = static_cast<float>((byte >> ((lane & 1) * 4)) & 15u);
+      } else {
+#pragma unroll
+        for (int e = 0; e < E; e += 2) {
+          const uint32_t byte = vrow[(E * lane + e) >> 1];
+          vh[e] = static_cast<float>(byte & 15u);
+          vh[e + 1] = static_cast<float>(byte >> 4);
+        }
+      }
+      const float vs = s_vsc[i], vz = s_vzr[i];
+#pragma unroll
+      for (int e = 0; e < E; ++e) vh[e] = vh[e] * vs + vz;
+#pragma unroll
+      for (int j = 0; j < G; ++j) {
+        const float p = s_p[j][i];
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[j][e] += p * vh[e];
+      }
+    }
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
+    float* p = part0 + j * head_stride;
+#pragma unroll
+    for (int e = 0; e < E; ++e) p[E * lane + e] = acc[j][e];
+    if (lane == 0) {
+      p[D] = m_run[j];
+      p[D + 1] = l_run[j];
+    }
+  }
+}
+
+// Merge the splits of one (sequence, q head): weights 2^(m_s - M).
+template <int D>
+__global__ void __launch_bounds__(64) decode_combine_kernel(DecodeArgs a) {
+  constexpr int E = D / 64;
+  const int lane = threadIdx.x;
+  const int64_t bh = blockIdx.x;          // b * Hq + hq
+  const float* part = a.part + bh * a.num_splits * (D + 2);
+  float M = -INFINITY;
+  for (int s = 0; s < a.num_splits; ++s) M = fmaxf(M, part[s * (D + 2) + D]);
+  float acc[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) acc[e] = 0.0f;
+  float L = 0.0f;
+  if (M != -INFINITY) {
+    for (int s = 0; s < a.num_splits; ++s) {
+      const float* p = part + s * (D + 2);
+      const float ms = p[D];
+      if (ms == -INFINITY) continue;
+      const float w = exp2f(ms - M);
+      L += w * p[D + 1];
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[e] += w * p[E * lane + e];
+    }
+  }
+  const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+  if (a.out_fp32) {
+    float* o = static_cast<float*>(a.out) + bh * D + E * lane;
+#pragma unroll
+    for (int e = 0; e < E; ++e) o[e] = acc[e] * inv;
+  } else {
+    uint16_t* o = static_cast<uint16_t*>(a.out) + bh * D + E * lane;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const uint32_t u = __float_as_uint(acc[e] * inv);
+      o[e] = static_cast<uint16_t>((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);   // RNE
+    }
+  }
+}
+
+template <int D, int KB, int G>
+hipError_t launch_t(const DecodeArgs& a, int batch, hipStream_t stream) {
+  hipLaunchKernelGGL((decode_split_kernel<D, KB, G>), dim3(a.num_splits, batch, a.H), dim3(64), 0,
+                     stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((decode_combine_kernel<D>), dim3(batch * a.Hq), dim3(64), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <int D, int KB>
+hipError_t launch_g(const DecodeArgs& a, int G, int batch, hipStream_t stream) {
+  switch (G) {
+    case 1: return launch_t<D, KB, 1>(a, batch, stream);
+    case 2: return launch_t<D, KB, 2>(a, batch, stream);
+    case 4: return launch_t<D, KB, 4>(a, batch, stream);
+    case 8: return launch_t<D, KB, 8>(a, batch, stream);
+    case 16: return launch_t<D, KB, 16>(a, batch, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+DecodePlan plan_decode(const Geometry& g, int batch, int num_q_heads, int max_seq_len) {
+  DecodePlan p;
+  p.chunk = 256;
+  p.num_splits = max_seq_len > 0 ? (max_seq_len + p.chunk - 1) / p.chunk : 1;
+  p.workspace_bytes = static_cast<size_t>(batch) * num_q_heads * p.num_splits *
+                      (g.head_dim + 2) * sizeof(float);
+  p.workspace_bytes = (p.workspace_bytes + 255) & ~static_cast<size_t>(255);
+  return p;
+}
+
+hipError_t launch_decode(const Geometry& g, const DevTables* tables, const DecodePlan& plan,
+                         const uint16_t* q, const uint8_t* cache, int64_t num_blocks,
+                         const int32_t* block_table, int max_blocks_per_seq,
+                         const int32_t* seq_lens, int batch, int num_q_heads, float sm_scale,
+                         void* out, int out_is_fp32, void* workspace, hipStream_t stream) {
+  DecodeArgs a;
+  a.tables = tables;
+  a.q = q;
+  a.cache = cache;
+  a.num_blocks = num_blocks;
+  a.block_table = block_table;
+  a.max_blocks = max_blocks_per_seq;
+  a.seq_lens = seq_lens;
+  a.Hq = num_q_heads;
+  a.H = g.num_kv_heads;
+  a.bs_shift = __builtin_ctz(static_cast<unsigned>(g.block_size));
+  a.chunk = plan.chunk;
+  a.num_splits = plan.num_splits;
+  a.scale_log2 = sm_scale * kLog2e;
+  a.part = static_cast<float*>(workspace);
+  a.out = out;
+  a.out_fp32 = out_is_fp32;
+  const int G = num_q_heads / g.num_kv_heads;
+#define TQ_DEC_CASE(D_, KB_) \
+  if (g.head_dim == D_ && g.key_bits == KB_) return launch_g<D_, KB_>(a, G, batch, stream);
+  TQ_DEC_CASE(64, 3) TQ_DEC_CASE(64, 4) TQ_DEC_CASE(64, 8)
+  TQ_DEC_CASE(128, 3) TQ_DEC_CASE(128, 4) TQ_DEC_CASE(128, 8)
+  TQ_DEC_CASE(256, 3) TQ_DEC_CASE(256, 4) TQ_DEC_CASE(256, 8)
+#undef TQ_DEC_CASE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace tq

@@ -1,0 +1,408 @@
+// Host side of the TurboQuant packed KV-cache library: the C ABI of
+// include/tq.h, the codebook solver, the rotation signs, argument validation
+// and kernel launches.
+//
+// Sources (page title, section):
+//   P1 "vLLM 源码完全拆解(十九):TurboQuant KV Cache 量化" -- presets ("四个
+//      预设对应什么"), Lloyd-Max conditions and the page's numerical recipe
+//      ("Lloyd-Max 的两个最优性条件", "vLLM 的实现:数值积分而不是解析解"),
+//      midpoints ("vLLM 内置的 Lloyd-Max 码本"), slot arithmetic ("从
+//      slot_size 的三项算术开始"), paging ("页内寻址").
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "tq_internal.h"
+
+using tq::DevTables;
+using tq::Geometry;
+
+struct tq_ctx {
+  int preset;
+  int codebook_mode;
+  Geometry geo;
+  int levels;                       // 2^key_bits for MSE keys, 0 for fp8
+  float centroids[tq::kMaxLevels];
+  float midpoints[tq::kMaxLevels];
+  int8_t signs[tq::kMaxHeadDim];
+  float r_d;                        // float32(1 / sqrt(head_dim))
+  int device;
+  DevTables* d_tables;
+};
+
+namespace {
+
+// ---- Lloyd-Max for N(0, sigma^2) ------------------------------------------
+// Fixed point of the two optimality conditions: boundaries at midpoints of
+// neighbouring levels, levels at the conditional mean of their cell, the
+// outer cells open to +-infinity.  Conditional mean of a Gaussian over (a, b):
+//   sigma * (phi(a/sigma) - phi(b/sigma)) / (Phi(b/sigma) - Phi(a/sigma)).
+
+double std_pdf(double z) {
+  if (std::isinf(z)) return 0.0;
+  return std::exp(-0.5 * z * z) / std::sqrt(2.0 * M_PI);
+}
+
+// P(a < Z < b) for a standard normal Z, from whichever tail keeps precision.
+double std_mass(double a, double b) {
+  const double r2 = std::sqrt(2.0);
+  if (a >= 0.0) return 0.5 * (std::erfc(a / r2) - std::erfc(b / r2));
+  if (b <= 0.0) return 0.5 * (std::erfc(-b / r2) - std::erfc(-a / r2));
+  return 1.0 - 0.5 * std::erfc(-a / r2) - 0.5 * std::erfc(b / r2);
+}
+
+double cell_mean(double a, double b, double sigma) {
+  const double za = a / sigma, zb = b / sigma;
+  return sigma * (std_pdf(za) - std_pdf(zb)) / std_mass(za, zb);
+}
+
+bool solve_exact(int d, int bits, std::vector<double>& out) {
+  const int n = 1 << bits;
+  const double sigma = std::sqrt(1.0 / d);
+  const double lo = -3.5 * sigma, hi = 3.5 * sigma;
+  std::vector<double> c(n), nc(n), edges(n + 1);
+  for (int i = 0; i < n; ++i) c[i] = lo + (hi - lo) * (i + 0.5) / n;
+  bool converged = false;
+  for (int it = 0; it < 100000 && !converged; ++it) {
+    edges[0] = -INFINITY;
+    edges[n] = INFINITY;
+    for (int i = 0; i + 1 < n; ++i) edges[i + 1] = (c[i] + c[i + 1]) / 2.0;
+    double delta = 0.0;
+    for (int i = 0; i < n; ++i) {
+      nc[i] = cell_mean(edges[i], edges[i + 1], sigma);
+      delta = std::fmax(delta, std::fabs(nc[i] - c[i]));
+    }
+    c.swap(nc);
+    converged = delta < 1e-14;
+  }
+  if (!converged) return false;
+  // exact symmetry: mirror the positive half
+  out.assign(n, 0.0);
+  for (int i = 0; i < n / 2; ++i) {
+    out[n / 2 + i] = c[n / 2 + i];
+    out[n / 2 - 1 - i] = -c[n / 2 + i];
+  }
+  return true;
+}
+
+double page_pdf(double x, double sigma2) {
+  return std::exp(-x * x / (2.0 * sigma2)) / std::sqrt(2.0 * M_PI * sigma2);
+}
+
+template <class F>
+double trapz200(F f, double a, double b) {
+  const int n = 200;
+  const double h = (b - a) / n;
+  double s = 0.5 * (f(a) + f(b));
+  for (int i = 1; i < n; ++i) s += f(a + i * h);
+  return s * h;
+}
+
+// The page's recipe: 200 trapezoids per integral, outer edges at +-10.5 sigma,
+// stop when no level moves by 1e-10 (returning the levels held at that
+// point), at most 200 iterations.
+void solve_page_trapz(int d, int bits, std::vector<double>& c) {
+  const int n = 1 << bits;
+  const double sigma2 = 1.0 / d;
+  const double sigma = std::sqrt(sigma2);
+  const double lo = -3.5 * sigma, hi = 3.5 * sigma;
+  c.assign(n, 0.0);
+  for (int i = 0; i < n; ++i) c[i] = lo + (hi - lo) * (i + 0.5) / n;
+  std::vector<double> nc(n), edges(n + 1);
+  for (int it = 0; it < 200; ++it) {
+    edges[0] = lo * 3;
+    edges[n] = hi * 3;
+    for (int i = 0; i + 1 < n; ++i) edges[i + 1] = (c[i] + c[i + 1]) / 2.0;
+    double delta = 0.0;
+    for (int i = 0; i < n; ++i) {
+      const double a = edges[i], b = edges[i + 1];
+      const double num = trapz200([&](double x) { return x * page_pdf(x, sigma2); }, a, b);
+      const double den = trapz200([&](double x) { return page_pdf(x, sigma2); }, a, b);
+      nc[i] = den > 1e-15 ? num / den : c[i];
+      delta = std::fmax(delta, std::fabs(nc[i] - c[i]));
+    }
+    if (delta < 1e-10) break;
+    c.swap(nc);
+  }
+}
+
+// SplitMix64 (Steele, Lea and Flood, OOPSLA 2014): sign j is the top bit of
+// the j-th output, 1 -> -1.
+void rotation_signs(uint64_t seed, int d, bool flip, int8_t* s) {
+  uint64_t st = seed;
+  for (int j = 0; j < d; ++j) {
+    if (!flip) {
+      s[j] = 1;
+      continue;
+    }
+    st += 0x9E3779B97F4A7C15ull;
+    uint64_t z = st;
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    z ^= z >> 31;
+    s[j] = (z >> 63) ? -1 : 1;
+  }
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+tq_status check_device(const tq_ctx* ctx) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return TQ_ERR_NO_DEVICE;
+  if (dev != ctx->device) return TQ_ERR_INVALID_ARG;
+  return TQ_OK;
+}
+
+// float32 levels (ascending) and midpoints of the sorted float32 levels,
+// m_i = (c_i + c_{i+1}) / 2 in float32.
+tq_status host_codebook(int d, int bits, int mode, float* cent, float* mid) {
+  if (bits < 1 || bits > 4) return TQ_ERR_UNSUPPORTED;
+  std::vector<double> lv;
+  if (mode == TQ_CODEBOOK_LLOYD_MAX_EXACT) {
+    if (!solve_exact(d, bits, lv)) return TQ_ERR_UNSUPPORTED;
+  } else if (mode == TQ_CODEBOOK_PAGE_TRAPZ) {
+    solve_page_trapz(d, bits, lv);
+  } else {
+    return TQ_ERR_INVALID_ARG;
+  }
+  std::vector<float> f(lv.size());
+  for (size_t i = 0; i < lv.size(); ++i) f[i] = static_cast<float>(lv[i]);
+  for (size_t i = 1; i < f.size(); ++i)
+    for (size_t j = i; j > 0 && f[j - 1] > f[j]; --j) std::swap(f[j - 1], f[j]);
+  const int n = 1 << bits;
+  for (int i = 0; i < n; ++i) cent[i] = f[i];
+  for (int i = 0; i + 1 < n; ++i) mid[i] = (f[i] + f[i + 1]) / 2.0f;
+  return TQ_OK;
+}
+
+int slot_bytes_for(int preset, int d) {
+  const int kb = preset == TQ_K8V4 ? 8 : (preset == TQ_4BIT_NC ? 4 : 3);
+  const int key = kb == 8 ? d : (d * kb + 7) / 8 + 2;
+  const int s = key + (d * 4 + 7) / 8 + 4;
+  return s + (s % 2);
+}
+
+}  // namespace
+
+extern "C" {
+
+tq_status tq_host_codebook(int head_dim, int bits, int codebook_mode, float* centroids_host,
+                           float* midpoints_host) {
+  if (!centroids_host || !midpoints_host) return TQ_ERR_INVALID_ARG;
+  if (head_dim != 64 && head_dim != 128 && head_dim != 256) return TQ_ERR_UNSUPPORTED;
+  return host_codebook(head_dim, bits, codebook_mode, centroids_host, midpoints_host);
+}
+
+tq_status tq_host_rotation_signs(uint64_t rot_seed, int head_dim, int sign_flip,
+                                 int8_t* signs_host) {
+  if (!signs_host) return TQ_ERR_INVALID_ARG;
+  if (head_dim != 64 && head_dim != 128 && head_dim != 256) return TQ_ERR_UNSUPPORTED;
+  rotation_signs(rot_seed, head_dim, sign_flip != 0, signs_host);
+  return TQ_OK;
+}
+
+int64_t tq_host_slot_bytes(int preset, int head_dim) {
+  if (preset < TQ_K8V4 || preset > TQ_K3V4_NC) return -1;
+  if (head_dim != 64 && head_dim != 128 && head_dim != 256) return -1;
+  return slot_bytes_for(preset, head_dim);
+}
+
+const char* tq_status_str(int status) {
+  switch (status) {
+    case TQ_OK: return "ok";
+    case TQ_ERR_INVALID_ARG: return "invalid argument";
+    case TQ_ERR_UNSUPPORTED: return "unsupported configuration";
+    case TQ_ERR_ALIGNMENT: return "misaligned pointer or stride";
+    case TQ_ERR_WORKSPACE: return "workspace too small";
+    case TQ_ERR_HIP: return "HIP runtime error";
+    case TQ_ERR_NO_DEVICE: return "no gfx950 device";
+    default: return "unknown status";
+  }
+}
+
+tq_status tq_codebook_init(tq_ctx** out, int preset, int head_dim, int num_kv_heads,
+                           int block_size, uint64_t rot_seed, int sign_flip, int codebook_mode,
+                           void* stream) {
+  if (!out) return TQ_ERR_INVALID_ARG;
+  *out = nullptr;
+  if (preset < TQ_K8V4 || preset > TQ_K3V4_NC) return TQ_ERR_INVALID_ARG;
+  if (codebook_mode != TQ_CODEBOOK_LLOYD_MAX_EXACT && codebook_mode != TQ_CODEBOOK_PAGE_TRAPZ)
+    return TQ_ERR_INVALID_ARG;
+  if (num_kv_heads < 1 || num_kv_heads > 64) return TQ_ERR_INVALID_ARG;
+  if (head_dim != 64 && head_dim != 128 && head_dim != 256) return TQ_ERR_UNSUPPORTED;
+  if (block_size != 16 && block_size != 32 && block_size != 64 && block_size != 128)
+    return TQ_ERR_UNSUPPORTED;
+
+  tq_ctx* c = new (std::nothrow) tq_ctx();
+  if (!c) return TQ_ERR_INVALID_ARG;
+  c->preset = preset;
+  c->codebook_mode = codebook_mode;
+  Geometry& g = c->geo;
+  g.head_dim = head_dim;
+  g.num_kv_heads = num_kv_heads;
+  g.block_size = block_size;
+  g.key_bits = preset == TQ_K8V4 ? 8 : (preset == TQ_4BIT_NC ? 4 : 3);
+  g.value_bits = 4;
+  g.norm_correction = preset == TQ_K8V4 ? 0 : 1;
+  g.key_code_bytes = g.key_bits == 8 ? head_dim : (head_dim * g.key_bits + 7) / 8;
+  g.key_packed = g.key_bits == 8 ? head_dim : g.key_code_bytes + 2;
+  g.value_code_bytes = (head_dim * g.value_bits + 7) / 8;
+  g.slot = slot_bytes_for(preset, head_dim);
+  c->r_d = static_cast<float>(1.0 / std::sqrt(static_cast<double>(head_dim)));
+
+  c->levels = 0;
+  std::memset(c->centroids, 0, sizeof(c->centroids));
+  std::memset(c->midpoints, 0, sizeof(c->midpoints));
+  if (g.key_bits != 8) {
+    tq_status cs = host_codebook(head_dim, g.key_bits, codebook_mode, c->centroids, c->midpoints);
+    if (cs != TQ_OK) {
+      delete c;
+      return cs;
+    }
+    c->levels = 1 << g.key_bits;
+  }
+  rotation_signs(rot_seed, head_dim, sign_flip != 0, c->signs);
+
+  DevTables host{};
+  std::memcpy(host.centroids, c->centroids, sizeof(host.centroids));
+  std::memcpy(host.midpoints, c->midpoints, sizeof(host.midpoints));
+  for (int j = 0; j < head_dim; ++j)
+    if (c->signs[j] < 0) host.sign_bits[j / 32] |= 1u << (j % 32);
+
+  if (hipGetDevice(&c->device) != hipSuccess) {
+    delete c;
+    return TQ_ERR_NO_DEVICE;
+  }
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, c->device) != hipSuccess ||
+      std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) {
+    delete c;
+    return TQ_ERR_NO_DEVICE;
+  }
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (hipMalloc(&c->d_tables, sizeof(DevTables)) != hipSuccess) {
+    delete c;
+    return TQ_ERR_HIP;
+  }
+  if (hipMemcpyAsync(c->d_tables, &host, sizeof(DevTables), hipMemcpyHostToDevice, st) !=
+          hipSuccess ||
+      hipStreamSynchronize(st) != hipSuccess) {
+    (void)hipFree(c->d_tables);
+    delete c;
+    return TQ_ERR_HIP;
+  }
+  *out = c;
+  return TQ_OK;
+}
+
+tq_status tq_destroy(tq_ctx* ctx) {
+  if (!ctx) return TQ_OK;
+  tq_status st = TQ_OK;
+  if (ctx->d_tables && hipFree(ctx->d_tables) != hipSuccess) st = TQ_ERR_HIP;
+  delete ctx;
+  return st;
+}
+
+int64_t tq_slot_bytes(const tq_ctx* ctx) { return ctx ? ctx->geo.slot : -1; }
+
+int64_t tq_cache_bytes(const tq_ctx* ctx, int64_t num_blocks) {
+  if (!ctx || num_blocks < 0) return -1;
+  return num_blocks * ctx->geo.block_size * ctx->geo.num_kv_heads * ctx->geo.slot;
+}
+
+tq_status tq_get_tables(const tq_ctx* ctx, float* centroids_host, float* midpoints_host,
+                        int8_t* signs_host) {
+  if (!ctx) return TQ_ERR_INVALID_ARG;
+  if (centroids_host && ctx->levels)
+    std::memcpy(centroids_host, ctx->centroids, sizeof(float) * ctx->levels);
+  if (midpoints_host && ctx->levels)
+    std::memcpy(midpoints_host, ctx->midpoints, sizeof(float) * (ctx->levels - 1));
+  if (signs_host) std::memcpy(signs_host, ctx->signs, ctx->geo.head_dim);
+  return TQ_OK;
+}
+
+tq_status tq_store(const tq_ctx* ctx, const void* k, const void* v, int64_t kv_token_stride,
+                   const int64_t* slot_mapping, int64_t num_tokens, uint8_t* cache,
+                   int64_t num_blocks, void* stream) {
+  if (!ctx) return TQ_ERR_INVALID_ARG;
+  if (num_tokens < 0 || num_blocks < 0) return TQ_ERR_INVALID_ARG;
+  if (num_tokens == 0) return TQ_OK;
+  if (!k || !v || !slot_mapping || !cache) return TQ_ERR_INVALID_ARG;
+  const Geometry& g = ctx->geo;
+  if (kv_token_stride < static_cast<int64_t>(g.num_kv_heads) * g.head_dim)
+    return TQ_ERR_INVALID_ARG;
+  if (kv_token_stride % 8 != 0 || !aligned(k, 16) || !aligned(v, 16) || !aligned(cache, 16) ||
+      !aligned(slot_mapping, 8))
+    return TQ_ERR_ALIGNMENT;
+  tq_status ds = check_device(ctx);
+  if (ds != TQ_OK) return ds;
+  hipError_t e = tq::launch_store(g, ctx->d_tables, static_cast<const uint16_t*>(k),
+                                  static_cast<const uint16_t*>(v), kv_token_stride, slot_mapping,
+                                  num_tokens, cache, num_blocks, ctx->r_d,
+                                  static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? TQ_OK : TQ_ERR_HIP;
+}
+
+size_t tq_decode_workspace_bytes(const tq_ctx* ctx, int batch, int num_q_heads,
+                                 int max_seq_len) {
+  if (!ctx || batch < 0 || num_q_heads <= 0 || max_seq_len < 0) return 0;
+  if (num_q_heads % ctx->geo.num_kv_heads != 0) return 0;
+  return tq::plan_decode(ctx->geo, batch, num_q_heads, max_seq_len).workspace_bytes;
+}
+
+tq_status tq_decode(const tq_ctx* ctx, const void* q, const uint8_t* cache, int64_t num_blocks,
+                    const int32_t* block_table, int max_blocks_per_seq, const int32_t* seq_lens,
+                    int batch, int num_q_heads, int max_seq_len, float sm_scale, void* out,
+                    int out_is_fp32, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!ctx) return TQ_ERR_INVALID_ARG;
+  const Geometry& g = ctx->geo;
+  if (batch < 0 || num_q_heads <= 0 || max_seq_len < 0 || num_blocks < 0 ||
+      max_blocks_per_seq < 0)
+    return TQ_ERR_INVALID_ARG;
+  if (num_q_heads % g.num_kv_heads != 0) return TQ_ERR_INVALID_ARG;
+  const int G = num_q_heads / g.num_kv_heads;
+  if (G > 16) return TQ_ERR_UNSUPPORTED;
+  if (batch == 0) return TQ_OK;
+  if (!q || !cache || !block_table || !seq_lens || !out) return TQ_ERR_INVALID_ARG;
+  if (static_cast<int64_t>(max_blocks_per_seq) * g.block_size < max_seq_len)
+    return TQ_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(cache, 16) || !aligned(out, 16) || !aligned(block_table, 4) ||
+      !aligned(seq_lens, 4))
+    return TQ_ERR_ALIGNMENT;
+  tq::DecodePlan plan = tq::plan_decode(g, batch, num_q_heads, max_seq_len);
+  if (plan.workspace_bytes > 0) {
+    if (!workspace || workspace_bytes < plan.workspace_bytes) return TQ_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return TQ_ERR_ALIGNMENT;
+  }
+  tq_status ds = check_device(ctx);
+  if (ds != TQ_OK) return ds;
+  if (!(sm_scale > 0.0f)) sm_scale = 1.0f / std::sqrt(static_cast<float>(g.head_dim));
+  hipError_t e = tq::launch_decode(g, ctx->d_tables, plan, static_cast<const uint16_t*>(q), cache,
+                                   num_blocks, block_table, max_blocks_per_seq, seq_lens, batch,
+                                   num_q_heads, sm_scale, out, out_is_fp32, workspace,
+                                   static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? TQ_OK : TQ_ERR_HIP;
+}
+
+tq_status tq_get_device_error(const tq_ctx* ctx, int32_t* code_host, int clear) {
+  if (!ctx || !code_host) return TQ_ERR_INVALID_ARG;
+  if (hipDeviceSynchronize() != hipSuccess) return TQ_ERR_HIP;
+  int32_t words[3] = {0, 0, 0};
+  if (hipMemcpy(words, &ctx->d_tables->err_slot, sizeof(words), hipMemcpyDeviceToHost) !=
+      hipSuccess)
+    return TQ_ERR_HIP;
+  *code_host = (words[0] ? 1 : 0) | (words[1] ? 2 : 0) | (words[2] ? 4 : 0);
+  if (clear) {
+    const int32_t zero[3] = {0, 0, 0};
+    if (hipMemcpy(&ctx->d_tables->err_slot, zero, sizeof(zero), hipMemcpyHostToDevice) !=
+        hipSuccess)
+      return TQ_ERR_HIP;
+  }
+  return TQ_OK;
+}
+
+}  // extern "C"

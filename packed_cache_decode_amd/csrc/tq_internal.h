@@ -1,0 +1,61 @@
+// Internal definitions shared by the host library and the HIP kernels.
+// Not part of the public ABI (include/tq.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/tq.h"
+
+namespace tq {
+
+constexpr int kMaxHeadDim = 256;
+constexpr int kMaxLevels = 16;
+
+// Device-resident tables of one context (about 200 bytes, one allocation).
+// Sign flips are a bit mask: bit j of sign_bits[j / 32] set means s_j = -1.
+struct DevTables {
+  float centroids[kMaxLevels];
+  float midpoints[kMaxLevels];          // 2^b - 1 entries used
+  uint32_t sign_bits[kMaxHeadDim / 32];
+  int32_t err_slot;                     // sticky: a store slot beyond the cache
+  int32_t err_page;                     // sticky: a page id beyond the cache
+  int32_t err_len;                      // sticky: a sequence length beyond the grid/table
+  int32_t pad[5];
+};
+
+struct Geometry {
+  int head_dim;
+  int num_kv_heads;
+  int block_size;
+  int key_bits;         // 3, 4, or 8 (fp8)
+  int value_bits;       // 4
+  int norm_correction;  // 0 / 1
+  int key_code_bytes;   // ceil(d*kb/8) or d for fp8
+  int key_packed;       // key_code_bytes (+2 for the norm unless fp8)
+  int value_code_bytes; // ceil(d*vb/8)
+  int slot;             // aligned slot bytes
+};
+
+// ---- launchers (defined in the .hip files) ---------------------------------
+
+hipError_t launch_store(const Geometry& g, const DevTables* tables, const uint16_t* k,
+                        const uint16_t* v, int64_t kv_token_stride, const int64_t* slot_mapping,
+                        int64_t num_tokens, uint8_t* cache, int64_t num_blocks, float r_d,
+                        hipStream_t stream);
+
+struct DecodePlan {
+  int chunk;        // tokens per split
+  int num_splits;   // splits per sequence (grid extent)
+  size_t workspace_bytes;
+};
+
+DecodePlan plan_decode(const Geometry& g, int batch, int num_q_heads, int max_seq_len);
+
+hipError_t launch_decode(const Geometry& g, const DevTables* tables, const DecodePlan& plan,
+                         const uint16_t* q, const uint8_t* cache, int64_t num_blocks,
+                         const int32_t* block_table, int max_blocks_per_seq,
+                         const int32_t* seq_lens, int batch, int num_q_heads, float sm_scale,
+                         void* out, int out_is_fp32, void* workspace, hipStream_t stream);
+
+}  // namespace tq

@@ -1,0 +1,289 @@
+// tq_store kernel: quantise one (token, kv head) K/V pair per wavefront and
+// write its slot into the paged cache.
+//
+// What is computed follows P1 ("vLLM 源码完全拆解(十九):TurboQuant KV Cache
+// 量化"), sections "K 的归一化与旋转为什么放在 kernel 外面" (normalise, rotate),
+// "二分查找" (bucketize, ">=" sends a boundary value right), "位打包" (LSB-first
+// codes), "向量范数的存储" (fp16 norm after the codes), "V 的 min/max 均匀量化"
+// and "FP8 K 路径".  The rotation is the seeded-sign Walsh-Hadamard transform
+// done in registers as butterflies instead of the page's dense GEMM.
+//
+// Bit-exactness: every float operation below is a single binary32 operation
+// rounded to nearest even.  Contraction into fused multiply-add is disabled
+// for this file, division and sqrtf compile to their correctly rounded
+// sequences, the norm is a fixed pairwise tree and the butterflies run with
+// stride h = 1, 2, 4, ..., d/2.  The same result therefore comes out of any
+// implementation that follows these steps, and the bytes are comparable bit
+// for bit.
+//
+// Mapping: one wavefront (64 lanes) per vector pair; lane l holds the E = d/64
+// contiguous elements [E*l, E*l + E).  Butterflies with stride below E stay in
+// the lane, larger strides pair lane l with lane l ^ (h / E).  The slot is
+// assembled in LDS and written with 2-byte stores (slots are 2-byte aligned).
+#include "tq_internal.h"
+
+#pragma clang fp contract(off)
+
+namespace tq {
+namespace {
+
+struct StoreArgs {
+  const DevTables* tables;
+  const uint16_t* k;
+  const uint16_t* v;
+  int64_t stride;            // elements between tokens
+  const int64_t* slot_mapping;
+  int64_t num_tokens;
+  uint8_t* cache;
+  int64_t num_slots;         // num_blocks * block_size
+  float r_d;
+  int H;
+  int bs_shift;              // log2(block_size)
+};
+
+constexpr int kWaves = 4;
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// binary32 -> binary16, round to nearest even (v_cvt_f16_f32 in the default mode)
+__device__ __forceinline__ uint16_t f32_to_f16_bits(float x) {
+  return __builtin_bit_cast(uint16_t, static_cast<_Float16>(x));
+}
+
+// OCP E4M3FN from binary32, round to nearest even, |x| >= 448 (and inf)
+// saturates to 448, NaN -> S.1111.111.  Written from the format definition:
+// bias 7, subnormals m * 2^-9, largest finite 1.75 * 2^8.
+__device__ __forceinline__ uint32_t f32_to_e4m3fn(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7FFFFFFFu;
+  if (a > 0x7F800000u) return sign | 0x7Fu;
+  if (a >= 0x43E00000u) return sign | 0x7Eu;          // 448.0f
+  if (a < 0x3C800000u) {                              // below 2^-6: subnormal grid 2^-9
+    const float q = rintf(__uint_as_float(a) * 512.0f);   // exact scaling, then RNE
+    return sign | static_cast<uint32_t>(q);           // q == 8 is the first normal
+  }
+  const uint32_t e = (a >> 23) - 120u;                // 127 - 7
+  uint32_t r = (e << 3) | ((a >> 20) & 7u);
+  const uint32_t rem = a & 0xFFFFFu;
+  if (rem > 0x80000u || (rem == 0x80000u && (r & 1u))) ++r;
+  return sign | r;
+}
+
+template <int D, int KB>
+__global__ void __launch_bounds__(64 * kWaves) store_kernel(StoreArgs a) {
+  constexpr int E = D / 64;
+  constexpr bool kFp8 = KB == 8;
+  constexpr int kLevels = kFp8 ? 0 : (1 << KB);
+  constexpr int kKeyCodeBytes = kFp8 ? D : (D * KB + 7) / 8;
+  constexpr int kKeyPacked = kFp8 ? D : kKeyCodeBytes + 2;
+  constexpr int kValCodeBytes = D / 2;
+  constexpr int kSlotRaw = kKeyPacked + kValCodeBytes + 4;
+  constexpr int kSlot = kSlotRaw + (kSlotRaw & 1);
+
+  __shared__ uint8_t s_code[kWaves][D];
+  __shared__ __align__(4) uint8_t s_slot[kWaves][kSlot + 2];
+
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int H = a.H;
+
+  float mid[kLevels > 0 ? kLevels - 1 : 1];
+#pragma unroll
+  for (int m = 0; m < kLevels - 1; ++m) mid[m] = a.tables->midpoints[m];
+  uint32_t sgn[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int j = E * lane + e;
+    sgn[e] = ((a.tables->sign_bits[j >> 5] >> (j & 31)) & 1u) << 31;
+  }
+
+  const int64_t total = a.num_tokens * H;
+  for (int64_t vec = static_cast<int64_t>(blockIdx.x) * kWaves + wave; vec < total;
+       vec += static_cast<int64_t>(gridDim.x) * kWaves) {
+    const int64_t n = vec / H;
+    const int h = static_cast<int>(vec - n * H);
+    const int64_t slot = a.slot_mapping[n];
+    if (slot < 0) continue;                       // padding token
+    if (slot >= a.num_slots) {
+      if (lane == 0) const_cast<DevTables*>(a.tables)->err_slot = 1;
+      continue;
+    }
+    const int64_t page = slot >> a.bs_shift;
+    const int64_t row = slot - (page << a.bs_shift);
+    uint8_t* dst = a.cache + ((page << a.bs_shift) + row) * (static_cast<int64_t>(H) * kSlot) +
+                   static_cast<int64_t>(h) * kSlot;
+    const int64_t src = n * a.stride + static_cast<int64_t>(h) * D + E * lane;
+
+    // ---------------- K ----------------
+    float x[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) x[e] = bf16_bits_to_f32(a.k[src + e]);
+
+    if constexpr (kFp8) {
+#pragma unroll
+      for (int e = 0; e < E; ++e) s_slot[wave][E * lane + e] = static_cast<uint8_t>(f32_to_e4m3fn(x[e]));
+    } else {
+      // sum of squares: in-lane levels, then across lanes (a balanced tree
+      // in index order; x*x of a bf16 value is exact)
+      float sq[E];
+#pragma unroll
+      for (int e = 0; e < E; ++e) sq[e] = x[e] * x[e];
+#pragma unroll
+      for (int w = 1; w < E; w *= 2)
+#pragma unroll
+        for (int e = 0; e < E; e += 2 * w) sq[e] = sq[e] + sq[e + w];
+      float ss = sq[0];
+#pragma unroll
+      for (int m = 1; m < 64; m *= 2) ss = ss + __shfl_xor(ss, m, 64);
+      const float nrm = sqrtf(ss);
+      const float alpha = (1.0f / (nrm + 1e-8f)) * a.r_d;
+
+      // sign flips (exact), then butterflies h = 1, 2, ..., D/2
+      float u[E];
+#pragma unroll
+      for (int e = 0; e < E; ++e) u[e] = __uint_as_float(__float_as_uint(x[e]) ^ sgn[e]);
+#pragma unroll
+      for (int hs = 1; hs < E; hs *= 2)
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+          if ((e & hs) == 0) {
+            const float p = u[e], q = u[e + hs];
+            u[e] = p + q;
+            u[e + hs] = p - q;
+          }
+#pragma unroll
+      for (int lm = 1; lm < 64; lm *= 2) {
+        const bool upper = (lane & lm) != 0;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const float o = __shfl_xor(u[e], lm, 64);
+          u[e] = upper ? (o - u[e]) : (u[e] + o);
+        }
+      }
+      // y = u * alpha, code = #{m : y >= mid_m}
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const float y = u[e] * alpha;
+        int c = 0;
+#pragma unroll
+        for (int m = 0; m < kLevels - 1; ++m) c += (y >= mid[m]) ? 1 : 0;
+        s_code[wave][E * lane + e] = static_cast<uint8_t>(c);
+      }
+      if (lane == 0) {
+        const uint16_t nb = f32_to_f16_bits(nrm);
+        s_slot[wave][kKeyCodeBytes] = static_cast<uint8_t>(nb & 0xFF);
+        s_slot[wave][kKeyCodeBytes + 1] = static_cast<uint8_t>(nb >> 8);
+      }
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      // LSB-first bit stream: byte j holds stream bits [8j, 8j + 8)
+      for (int j = lane; j < kKeyCodeBytes; j += 64) {
+        uint32_t byte = 0;
+        if constexpr (KB == 4) {
+          byte = s_code[wave][2 * j] | (s_code[wave][2 * j + 1] << 4);
+        } else {
+#pragma unroll
+          for (int bit = 0; bit < 8; ++bit) {
+            const int p = 8 * j + bit;
+            byte |= ((s_code[wave][p / KB] >> (p % KB)) & 1u) << bit;
+          }
+        }
+        s_slot[wave][j] = static_cast<uint8_t>(byte);
+      }
+    }
+
+    // ---------------- V ----------------
+    float vv[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) vv[e] = bf16_bits_to_f32(a.v[src + e]);
+    float lo = vv[0], hi = vv[0];
+#pragma unroll
+    for (int e = 1; e < E; ++e) {
+      lo = fminf(lo, vv[e]);
+      hi = fmaxf(hi, vv[e]);
+    }
+#pragma unroll
+    for (int m = 1; m < 64; m *= 2) {
+      lo = fminf(lo, __shfl_xor(lo, m, 64));
+      hi = fmaxf(hi, __shfl_xor(hi, m, 64));
+    }
+    float sc = (hi - lo) / 15.0f;
+    if (!(sc > 1e-8f)) sc = 1e-8f;
+    const float isc = 1.0f / sc;
+    uint32_t q[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const float t = (vv[e] - lo) * isc + 0.5f;
+      int qi = static_cast<int>(truncf(t));
+      qi = qi < 0 ? 0 : (qi > 15 ? 15 : qi);
+      q[e] = static_cast<uint32_t>(qi);
+    }
+    if constexpr (E == 1) {
+      const uint32_t other = __shfl_xor(q[0], 1, 64);
+      if ((lane & 1) == 0) s_slot[wave][kKeyPacked + (lane >> 1)] = static_cast<uint8_t>(q[0] | (other << 4));
+    } else {
+#pragma unroll
+      for (int e = 0; e < E; e += 2)
+        s_slot[wave][kKeyPacked + (E * lane + e) / 2] = static_cast<uint8_t>(q[e] | (q[e + 1] << 4));
+    }
+    if (lane == 0) {
+      const uint16_t sb = f32_to_f16_bits(sc);
+      const uint16_t zb = f32_to_f16_bits(lo);
+      uint8_t* m = &s_slot[wave][kKeyPacked + kValCodeBytes];
+      m[0] = static_cast<uint8_t>(sb & 0xFF);
+      m[1] = static_cast<uint8_t>(sb >> 8);
+      m[2] = static_cast<uint8_t>(zb & 0xFF);
+      m[3] = static_cast<uint8_t>(zb >> 8);
+      if (kSlot != kSlotRaw) m[4] = 0;
+    }
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+
+    // write the assembled slot: kSlot / 2 two-byte stores
+    uint16_t* d16 = reinterpret_cast<uint16_t*>(dst);
+    for (int j = lane; j < kSlot / 2; j += 64)
+      d16[j] = static_cast<uint16_t>(s_slot[wave][2 * j] | (s_slot[wave][2 * j + 1] << 8));
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  }
+}
+
+template <int D, int KB>
+hipError_t launch_store_t(const StoreArgs& a, hipStream_t stream) {
+  const int64_t total = a.num_tokens * a.H;
+  int64_t blocks = (total + kWaves - 1) / kWaves;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL((store_kernel<D, KB>), dim3(static_cast<unsigned>(blocks)),
+                     dim3(64 * kWaves), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_store(const Geometry& g, const DevTables* tables, const uint16_t* k,
+                        const uint16_t* v, int64_t kv_token_stride, const int64_t* slot_mapping,
+                        int64_t num_tokens, uint8_t* cache, int64_t num_blocks, float r_d,
+                        hipStream_t stream) {
+  StoreArgs a;
+  a.tables = tables;
+  a.k = k;
+  a.v = v;
+  a.stride = kv_token_stride;
+  a.slot_mapping = slot_mapping;
+  a.num_tokens = num_tokens;
+  a.cache = cache;
+  a.num_slots = num_blocks * g.block_size;
+  a.r_d = r_d;
+  a.H = g.num_kv_heads;
+  a.bs_shift = __builtin_ctz(static_cast<unsigned>(g.block_size));
+#define TQ_STORE_CASE(D_, KB_) \
+  if (g.head_dim == D_ && g.key_bits == KB_) return launch_store_t<D_, KB_>(a, stream);
+  TQ_STORE_CASE(64, 3) TQ_STORE_CASE(64, 4) TQ_STORE_CASE(64, 8)
+  TQ_STORE_CASE(128, 3) TQ_STORE_CASE(128, 4) TQ_STORE_CASE(128, 8)
+  TQ_STORE_CASE(256, 3) TQ_STORE_CASE(256, 4) TQ_STORE_CASE(256, 8)
+#undef TQ_STORE_CASE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace tq

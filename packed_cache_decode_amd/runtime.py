@@ -1,0 +1,74 @@
+"""A small convenience layer over the C ABI: a context plus its decode
+workspace, with torch tensors for device memory and streams.
+
+All computation happens in the HIP library; this only sizes buffers and
+passes pointers.
+"""
+
+import torch
+
+from . import _lib
+
+PRESET_IDS = _lib.PRESETS
+
+
+class PackedKVCache:
+    """One context (codebook, signs, geometry) on the current device."""
+
+    def __init__(self, preset, head_dim, num_kv_heads, block_size, rot_seed, sign_flip=True,
+                 codebook_mode="exact", device="cuda"):
+        self.device = torch.device(device)
+        self.preset = preset
+        self.head_dim = head_dim
+        self.num_kv_heads = num_kv_heads
+        self.block_size = block_size
+        with torch.cuda.device(self.device):
+            self.ctx = _lib.tq_codebook_init(preset, head_dim, num_kv_heads, block_size, rot_seed,
+                                             sign_flip, codebook_mode)
+        self.slot_bytes = _lib.tq_slot_bytes(self.ctx)
+        self._ws = None
+
+    def close(self):
+        if self.ctx:
+            _lib.tq_destroy(self.ctx)
+            self.ctx = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def new_cache(self, num_blocks, fill=0):
+        shape = (num_blocks, self.block_size, self.num_kv_heads, self.slot_bytes)
+        return torch.full(shape, fill, dtype=torch.uint8, device=self.device)
+
+    def store(self, k, v, slot_mapping, cache, stream=None):
+        """k, v: bf16 [N, H, d] (or [N, stride] with heads packed first);
+        slot_mapping: int64 [N]; cache: uint8 [num_blocks, bs, H, slot]."""
+        n = slot_mapping.shape[0]
+        stride = k.stride(0)
+        assert k.stride(0) == v.stride(0) and k.dtype == v.dtype == torch.bfloat16
+        _lib.tq_store(self.ctx, k, v, stride, slot_mapping, n, cache, cache.shape[0], stream)
+
+    def workspace(self, batch, num_q_heads, max_seq_len):
+        nbytes = _lib.tq_decode_workspace_bytes(self.ctx, batch, num_q_heads, max_seq_len)
+        if self._ws is None or self._ws.numel() < nbytes:
+            self._ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=self.device)
+        return self._ws, nbytes
+
+    def decode(self, q, cache, block_table, seq_lens, max_seq_len, out=None, out_fp32=False,
+               sm_scale=0.0, stream=None):
+        """q: bf16 [B, Hq, d]; block_table: int32 [B, max_blocks]; seq_lens: int32 [B]."""
+        B, Hq, d = q.shape
+        if out is None:
+            out = torch.empty((B, Hq, d), dtype=torch.float32 if out_fp32 else torch.bfloat16,
+                              device=q.device)
+        ws, nbytes = self.workspace(B, Hq, max_seq_len)
+        _lib.tq_decode(self.ctx, q, cache, cache.shape[0], block_table, block_table.shape[1],
+                       seq_lens, B, Hq, max_seq_len, sm_scale, out, out.dtype == torch.float32,
+                       ws, ws.numel(), stream)
+        return out
+
+    def device_error(self, clear=True):
+        return _lib.tq_get_device_error(self.ctx, clear)

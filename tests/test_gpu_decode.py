@@ -1,0 +1,154 @@
+"""GPU parity of tq_decode against the oracle's float64 attention over the
+dequantised cache: max-abs 2e-3 with fp32 output, plus half a bf16 ulp of
+the reference with bf16 output (rounding to bf16 alone can exceed 2e-3 for
+|o| >= 1).
+
+Small cases decode a cache written by the oracle (so the decode is tested on
+its own); full-size cases decode the cache the GPU store wrote, and compare
+sampled (sequence, head) outputs with the oracle, which encodes those
+sequences itself.
+"""
+
+import numpy as np
+import pytest
+
+from gpu_util import OracleSide, check_decode, to_dev
+from packed_cache_decode_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def _decode_from_oracle_cache(w, seed=11, sign_flip=True, lens=None, sm_scale=None, zero_q=False,
+                              out_fp32=True):
+    from packed_cache_decode_amd.runtime import PackedKVCache
+    inp = synth.generate(w)
+    if lens is not None:
+        inp.seq_lens = np.minimum(np.asarray(lens, np.int32), inp.seq_lens)
+    if zero_q:
+        inp.q = np.zeros_like(inp.q)
+    ors = OracleSide(w.preset, w.head_dim, seed, sign_flip)
+    cache = np.zeros((inp.num_blocks, w.block_size, w.num_kv_heads, ors.lay.slot_size_aligned), np.uint8)
+    ors.store(cache, inp.k, inp.v, inp.slot_mapping)
+    want = ors.decode(inp.q, cache, inp.block_table, inp.seq_lens, w.num_kv_heads, sm_scale)
+    tq = PackedKVCache(w.preset, w.head_dim, w.num_kv_heads, w.block_size, seed, sign_flip)
+    max_len = int(max(1, inp.seq_lens.max()))
+    out = tq.decode(to_dev(inp.q), to_dev(cache), to_dev(inp.block_table), to_dev(inp.seq_lens),
+                    max_len, out_fp32=out_fp32, sm_scale=sm_scale or 0.0)
+    torch.cuda.synchronize()
+    assert tq.device_error() == 0
+    tq.close()
+    got = out.float().cpu().numpy()
+    return got, want
+
+
+def _wl(preset, G=4, H=2, d=128, bs=16, lens=(1, 700), B=4, seed=1):
+    return synth.Workload(f"dec_{preset}", preset, batch=B, num_q_heads=G * H, num_kv_heads=H,
+                          head_dim=d, block_size=bs, seed=seed, len_range=lens)
+
+
+PRESETS = ["turboquant_4bit_nc", "turboquant_k3v4_nc", "turboquant_k8v4"]
+
+
+@pytest.mark.parametrize("preset", PRESETS)
+@pytest.mark.parametrize("G", [1, 4, 8])
+def test_decode_small_parity_fp32(preset, G):
+    got, want = _decode_from_oracle_cache(_wl(preset, G=G, seed=G))
+    err = check_decode(got, want, bf16_out=False)
+    print(f"{preset} G={G}: max abs {err:.2e}")
+
+
+@pytest.mark.parametrize("preset", PRESETS)
+def test_decode_small_parity_bf16(preset):
+    got, want = _decode_from_oracle_cache(_wl(preset, G=4, seed=21), out_fp32=False)
+    check_decode(got, want, bf16_out=True)
+
+
+@pytest.mark.parametrize("preset", PRESETS)
+def test_decode_ragged_and_tiny_lengths(preset):
+    # 0, 1, a page minus one, a page, a page plus one, several chunks + tail
+    w = _wl(preset, G=2, B=7, lens=(600, 600), seed=5)
+    got, want = _decode_from_oracle_cache(w, lens=[0, 1, 15, 16, 17, 257, 600])
+    check_decode(got, want, bf16_out=False)
+    assert np.all(got[0] == 0.0)
+
+
+@pytest.mark.parametrize("bs,d", [(32, 128), (128, 128), (16, 64), (16, 256)])
+def test_decode_block_sizes_and_head_dims(bs, d):
+    got, want = _decode_from_oracle_cache(_wl("turboquant_4bit_nc", G=4, d=d, bs=bs, seed=bs + d))
+    check_decode(got, want, bf16_out=False)
+
+
+def test_decode_pure_hadamard_custom_scale_zero_query():
+    w = _wl("turboquant_k3v4_nc", G=4, seed=8)
+    got, want = _decode_from_oracle_cache(w, sign_flip=False, sm_scale=0.05)
+    check_decode(got, want, bf16_out=False)
+    got, want = _decode_from_oracle_cache(w, zero_q=True)
+    check_decode(got, want, bf16_out=False)
+
+
+def test_decode_bad_page_id_sets_error():
+    from packed_cache_decode_amd.runtime import PackedKVCache
+    w = _wl("turboquant_4bit_nc", G=1, H=1, B=1, lens=(40, 40))
+    inp = synth.generate(w)
+    tq = PackedKVCache(w.preset, 128, 1, 16, 3)
+    cache = tq.new_cache(inp.num_blocks)
+    bt = inp.block_table.copy()
+    bt[0, 1] = inp.num_blocks + 7
+    tq.decode(to_dev(inp.q), cache, to_dev(bt), to_dev(inp.seq_lens), 40, out_fp32=True)
+    torch.cuda.synchronize()
+    assert tq.device_error() == 2
+    tq.close()
+
+
+def test_decode_deterministic():
+    w = _wl("turboquant_4bit_nc", G=4, seed=2)
+    a, _ = _decode_from_oracle_cache(w)
+    b, _ = _decode_from_oracle_cache(w)
+    assert np.array_equal(a, b)
+
+
+FULL = ["tiny", "llama3_8b", "k3v4_gqa8", "k8v4_32k", "long_131k"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_decode_full_size_sampled(name):
+    """Full-size workload: GPU store, then GPU decode with bf16 output (the
+    configuration the benchmark times); sampled (sequence, kv head) groups are
+    compared with the oracle, which encodes those sequences itself."""
+    from packed_cache_decode_amd.runtime import PackedKVCache
+    w = synth.WORKLOADS[name]
+    print(f"[decode full] {name}: generating", flush=True)
+    inp = synth.generate(w)
+    seed = 777
+    tq = PackedKVCache(w.preset, w.head_dim, w.num_kv_heads, w.block_size, seed)
+    cache = tq.new_cache(inp.num_blocks)
+    tq.store(to_dev(inp.k), to_dev(inp.v), to_dev(inp.slot_mapping), cache)
+    max_len = int(inp.seq_lens.max())
+    out = tq.decode(to_dev(inp.q), cache, to_dev(inp.block_table), to_dev(inp.seq_lens), max_len)
+    torch.cuda.synchronize()
+    assert tq.device_error() == 0
+    got = out.float().cpu().numpy()
+    tq.close()
+    del cache
+    ors = OracleSide(w.preset, w.head_dim, seed)
+    rng = np.random.default_rng(1)
+    B, H, G = w.batch, w.num_kv_heads, w.gqa
+    picks = [(int(b), int(g)) for b, g in zip(rng.choice(B, size=min(B, 3), replace=False),
+                                              rng.integers(0, H, size=min(B, 3)))]
+    offs = inp.token_offsets()
+    worst = 0.0
+    for b, g in picks:
+        T = int(inp.seq_lens[b])
+        kk = inp.k[offs[b]:offs[b] + T, g:g + 1]
+        vv = inp.v[offs[b]:offs[b] + T, g:g + 1]
+        slots = ors.encode(kk, vv)                         # [T, 1, slot]
+        npages = -(-T // w.block_size)
+        local = np.zeros((npages, w.block_size, 1, slots.shape[-1]), np.uint8)
+        t = np.arange(T)
+        local[t // w.block_size, t % w.block_size] = slots
+        qb = inp.q[b:b + 1, g * G:(g + 1) * G]
+        want = ors.decode(qb, local, np.arange(npages)[None], np.array([T]), 1)
+        worst = max(worst, check_decode(got[b:b + 1, g * G:(g + 1) * G], want, bf16_out=True))
+    print(f"[decode full] {name}: sampled {picks}, max abs err {worst:.2e}", flush=True)

@@ -171,7 +171,8 @@ size_t tq_decode_workspace_bytes(const tq_ctx* ctx, int batch, int num_q_heads,
  *   out            device, [batch][num_q_heads][head_dim], bf16 when
  *                  out_is_fp32 == 0, fp32 otherwise
  *   workspace      device, >= tq_decode_workspace_bytes(...) bytes, 256-byte
- *                  aligned; contents need no initialisation
+ *                  aligned; contents need no initialisation; calls that
+ *                  share a workspace must not overlap
  */
 tq_status tq_decode(const tq_ctx* ctx, const void* q, const uint8_t* cache, int64_t num_blocks,
                     const int32_t* block_table, int max_blocks_per_seq, const int32_t* seq_lens,

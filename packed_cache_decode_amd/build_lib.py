@@ -25,6 +25,7 @@ SOURCES = [
     ("tq_host.cpp", []),
     ("tq_store.hip", ["-ffp-contract=off"]),
     ("tq_decode.hip", []),
+    ("tq_decode_mfma.hip", ["-fno-honor-nans"]),
 ]
 
 

@@ -363,6 +363,22 @@ hipError_t launch_g(const DecodeArgs& a, int G, int batch, hipStream_t stream) {
 
 DecodePlan plan_decode(const Geometry& g, int batch, int num_q_heads, int max_seq_len) {
   DecodePlan p;
+  if (mfma_decode_eligible(g, num_q_heads)) {
+    // about 256 workgroups (one per CU: one wavefront per kv head), 16-token
+    // slabs, at least 8 slabs per split so the per-workgroup set-up is amortised
+    const int slabs = max_seq_len > 0 ? (max_seq_len + 15) / 16 : 1;
+    int s = batch > 0 ? (256 + batch - 1) / batch : 1;
+    const int s_max = (slabs + 7) / 8;
+    s = s < 1 ? 1 : (s > s_max ? s_max : s);
+    p.mfma = 1;
+    p.chunk = 16 * ((slabs + s - 1) / s);
+    if (p.chunk > 16 * 256) p.chunk = 16 * 256;       // page offsets of a split fit in LDS
+    p.num_splits = max_seq_len > 0 ? (max_seq_len + p.chunk - 1) / p.chunk : 1;
+    p.workspace_bytes = mfma_partial_bytes(batch, num_q_heads, p.num_splits);
+    p.workspace_bytes = (p.workspace_bytes + 255) & ~static_cast<size_t>(255);
+    return p;
+  }
+  p.mfma = 0;
   p.chunk = 256;
   p.num_splits = max_seq_len > 0 ? (max_seq_len + p.chunk - 1) / p.chunk : 1;
   p.workspace_bytes = static_cast<size_t>(batch) * num_q_heads * p.num_splits *
@@ -377,6 +393,10 @@ hipError_t launch_decode(const Geometry& g, const DevTables* tables, const Decod
                          const int32_t* seq_lens, int batch, int num_q_heads, float sm_scale,
                          void* out, int out_is_fp32, void* workspace, hipStream_t stream) {
   DecodeArgs a;
+  if (plan.mfma)
+    return launch_decode_mfma(g, tables, plan, q, cache, num_blocks, block_table, max_blocks_per_seq,
+                              seq_lens, batch, num_q_heads, sm_scale, out, out_is_fp32, workspace,
+                              stream);
   a.tables = tables;
   a.q = q;
   a.cache = cache;

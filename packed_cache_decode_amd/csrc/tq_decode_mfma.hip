@@ -1,0 +1,815 @@
+// tq_decode on gfx950 matrix cores: split-KV paged decode attention over
+// packed slots for head_dim 128, 4- or 3-bit Lloyd-Max keys, block sizes
+// that are multiples of 16 and up to 16 query heads per kv head.
+//
+// What is computed is the same as in the general kernel (tq_decode.hip),
+// following P1 ("vLLM 源码完全拆解(十九):TurboQuant KV Cache 量化"),
+// sections "分数计算" (q_rot . centroid, stored norm, norm correction
+// 1/sqrt(sum c^2 + 1e-16)), "V 的解包" (code * scale + zero), "在线 softmax"
+// and "读取内核" (split partials, log-sum-exp merge).
+//
+// Mapping.  A workgroup is one (split, sequence) with one wavefront per kv
+// head, so every byte of a page is read by one CU.  A wavefront walks the
+// split 16 tokens at a time (a slab: 16 rows of a page) with three MFMA
+// contractions:
+//   scores  S[t][h] = sum_c C[t][c] Q[h][c]     v_mfma_f32_16x16x32_f16
+//   norms   N[t][t] = sum_c C[t][c] C[t][c]     (diagonal of C C^T)
+//   values  O[h][c] += sum_t W[h][t] V[t][c]    v_mfma_f32_16x16x16_f16
+// C are the centroids of the slab's K codes, looked up per code byte (two
+// codes) in LDS tables; Q the rotated queries (rows >= G are zero); W = p *
+// scale and V the integer V codes, exact in f16.  f16 alone is not precise
+// enough for the scores (outlier keys make them large), so C and Q are
+// carried as f16 hi + lo pairs (lo scaled by 2^11 to stay normal): the
+// score uses Chi.Qhi + Chi.Qlo + 2^-11 Clo.Qhi and the norm Chi.Chi +
+// 2^-10 Chi.Clo.  The per-token term zero * p and the softmax sums stay in
+// fp32.  The running maximum is lazy: the accumulators are rescaled only
+// when a head's maximum grows by more than kLazy (base 2), so p <= 2^kLazy.
+//
+// Layouts (lane l, row r16 = l % 16, group g4 = l / 16):
+//   A operand  : row r16, k = [8*g4, 8*g4+8) (x32) or [4*g4, 4*g4+4) (x16)
+//   B operand  : column r16, same k
+//   D          : column r16, rows 4*g4 .. 4*g4+3
+// Coordinates are permuted so each lane reads contiguous bytes: score MFMA
+// kk in group g4 covers coordinates 32*g4 + 8*kk + [0, 8); value tile m,
+// column j covers coordinate 8*j + m.
+//
+// Two ways to fetch a slab:
+//   staged  (even head counts): the wavefront loads its head's bytes of the
+//           16 rows with 16-byte loads (3 per lane), three slabs ahead, and
+//           parks them in a private LDS region from which each lane reads
+//           its operands; no barriers, the wavefronts run independently.
+//   direct  (any head count): each lane loads its operand bytes straight
+//           from memory, one slab ahead.
+// Slots of 134 / 118 bytes are only 2-byte aligned, so fields are read as
+// aligned dwords and re-aligned with a funnel shift.  A second small kernel
+// merges the splits (a fused last-workgroup merge needs a device-scope
+// release in every workgroup, which on this part costs far more than a
+// launch).
+#include "tq_internal.h"
+
+namespace tq {
+namespace {
+
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4), aligned(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2), aligned(4)));
+
+constexpr int kD = 128;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLoScale = 2048.0f;          // lo parts are stored x 2^11
+constexpr int kRec = kD + 4;                 // partial record: O[128], m, l, z, pad
+constexpr float kLazy = 6.0f;                // rescale when the max grows by > 2^6
+constexpr int kMaxChunkPages = 256;          // pages of one split staged in LDS
+constexpr int kTabLoOff = 272;               // lo table offset (dwords): other banks
+
+struct MfmaArgs {
+  const DevTables* tables;
+  const uint16_t* q;
+  const uint8_t* cache;
+  int64_t num_blocks;
+  const int32_t* block_table;
+  int max_blocks;
+  const int32_t* seq_lens;
+  int Hq;
+  int H;
+  int G;
+  int bs_shift;
+  int chunk;           // tokens per split, a multiple of 16
+  int num_splits;
+  float scale_log2;    // sm_scale * log2(e)
+  float* part;         // [B][Hq][S][kRec]
+  void* out;
+  int out_fp32;
+};
+
+__device__ __forceinline__ uint32_t funnel(uint32_t hi, uint32_t lo, uint32_t sh) {
+  return __builtin_amdgcn_alignbyte(hi, lo, sh);
+}
+
+__device__ __forceinline__ uint32_t pack_h2(_Float16 a, _Float16 b) {
+  return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, a)) |
+         (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, b)) << 16);
+}
+
+__device__ __forceinline__ float f16_bits_to_f32(uint32_t b) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(b)));
+}
+
+// reductions over the lane pair (l, l ^ 16) and (l, l ^ 32)
+__device__ __forceinline__ float max_x16(float x) {
+  auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
+}
+__device__ __forceinline__ float max_x32(float x) {
+  auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
+}
+__device__ __forceinline__ float sum_x16(float x) {
+  auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(s[0]) + __uint_as_float(s[1]);
+}
+__device__ __forceinline__ float sum_x32(float x) {
+  auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(s[0]) + __uint_as_float(s[1]);
+}
+__device__ __forceinline__ float lane_value(float x, int src_lane) {
+  return __int_as_float(__builtin_amdgcn_ds_bpermute(src_lane << 2, __float_as_int(x)));
+}
+
+// Running state of one wavefront (G query heads of one kv head).
+struct RunState {
+  f4 O[8];          // O[h][8*r16 + m]: tile m, rows 4*g4 + r
+  float m_run;      // running (lazy) max, base 2, of head r16
+  float l_part;     // sum of p over this lane's rows, head r16
+  float z_part;     // sum of p * zero over this lane's rows, head r16
+};
+
+// Operand bytes of one slab for one lane, already re-aligned.
+template <int KB>
+struct SlabOps {
+  uint32_t kw[KB == 4 ? 4 : 3];   // K codes of token r16, coordinates [32*g4, 32*g4 + 32)
+  uint32_t X[4];                  // V codes of token 4*g4 + r, coordinates [8*r16, 8*r16 + 8)
+  uint32_t n[4];                  // K norm (f16 bits) of token 4*g4 + r
+  uint32_t sz[4];                 // V scale (low half) and zero (high half) of token 4*g4 + r
+};
+
+// centroid tables: entry e holds two codes (low code first); hi and lo parts
+template <int KB>
+__device__ __forceinline__ void build_tables(const MfmaArgs& a, uint32_t* s_tab) {
+  constexpr int kTab = KB == 4 ? 256 : 64;
+  for (int e = threadIdx.x; e < kTab; e += blockDim.x) {
+    const int c0 = e & ((1 << KB) - 1), c1 = e >> KB;
+    const float v0 = a.tables->centroids[c0], v1 = a.tables->centroids[c1];
+    const _Float16 h0 = static_cast<_Float16>(v0), h1 = static_cast<_Float16>(v1);
+    const _Float16 l0 = static_cast<_Float16>((v0 - static_cast<float>(h0)) * kLoScale);
+    const _Float16 l1 = static_cast<_Float16>((v1 - static_cast<float>(h1)) * kLoScale);
+    s_tab[e] = pack_h2(h0, h1);
+    s_tab[kTabLoOff + e] = pack_h2(l0, l1);
+  }
+}
+
+// rotate the G queries of kv head g (q_rot = H diag(s) q / sqrt(128)) and
+// split them into f16 hi / lo; lane (h = r16, g4) holds coordinates
+// [32*g4, 32*g4 + 32) of head h, as the four score-MFMA B operands
+__device__ __forceinline__ void load_queries(const MfmaArgs& a, int b, int g, int r16, int g4,
+                                             h8 (&qhi)[4], h8 (&qlo)[4]) {
+  float x[32];
+  const bool live = r16 < a.G;
+  const uint16_t* qp = a.q + (static_cast<int64_t>(b) * a.Hq + g * a.G + (live ? r16 : 0)) * kD + 32 * g4;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const u32x4 w = *reinterpret_cast<const u32x4*>(qp + 8 * i);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      x[8 * i + 2 * j] = __uint_as_float(w[j] << 16);
+      x[8 * i + 2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u);
+    }
+  }
+  const uint32_t sb = a.tables->sign_bits[g4];
+#pragma unroll
+  for (int j = 0; j < 32; ++j) x[j] = __uint_as_float(__float_as_uint(x[j]) ^ (((sb >> j) & 1u) << 31));
+#pragma unroll
+  for (int hs = 1; hs < 32; hs *= 2)
+#pragma unroll
+    for (int j = 0; j < 32; ++j)
+      if ((j & hs) == 0) {
+        const float p = x[j], r = x[j + hs];
+        x[j] = p + r;
+        x[j + hs] = p - r;
+      }
+  // strides 32 and 64 cross lane groups: partner lane l ^ 16, l ^ 32
+#pragma unroll
+  for (int j = 0; j < 32; ++j) {
+    auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(x[j]), __float_as_uint(x[j]), false, false);
+    const float o = (g4 & 1) ? __uint_as_float(sw[0]) : __uint_as_float(sw[1]);
+    x[j] = (g4 & 1) ? (o - x[j]) : (x[j] + o);
+  }
+#pragma unroll
+  for (int j = 0; j < 32; ++j) {
+    auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x[j]), __float_as_uint(x[j]), false, false);
+    const float o = (g4 & 2) ? __uint_as_float(sw[0]) : __uint_as_float(sw[1]);
+    x[j] = (g4 & 2) ? (o - x[j]) : (x[j] + o);
+  }
+  const float rsd = 0.08838834764831845f;    // 1/sqrt(128); the softmax scale is applied in fp32
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float v = live ? x[8 * kk + e] * rsd : 0.0f;
+      const _Float16 hv = static_cast<_Float16>(v);
+      qhi[kk][e] = hv;
+      qlo[kk][e] = static_cast<_Float16>(v - static_cast<float>(hv));
+    }
+}
+
+// One slab: scores, norm correction, online softmax, P.V.
+template <int KB>
+__device__ __forceinline__ void process_slab(const SlabOps<KB>& op, int valid_rows,
+                                             const uint32_t* s_tab, const h8 (&qhi)[4],
+                                             const h8 (&qlo)[4], bool head_live, float fscale,
+                                             int g4, RunState& st) {
+  // ---- K: codes -> centroid hi / lo operands, score and norm MFMAs ----
+  f4 Shi = {0.f, 0.f, 0.f, 0.f}, Slo = {0.f, 0.f, 0.f, 0.f};
+  f4 Nhi = {0.f, 0.f, 0.f, 0.f}, Nx = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    uint32_t idx[4];
+    if constexpr (KB == 4) {
+#pragma unroll
+      for (int p = 0; p < 4; ++p) idx[p] = (op.kw[kk] >> (8 * p)) & 0xFFu;
+    } else {
+      // 24 bits per MFMA step: bits [24*kk, 24*kk + 24) of the lane's 96
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const int bit = 24 * kk + 6 * p;
+        const int w = bit >> 5, o = bit & 31;
+        uint32_t v = op.kw[w] >> o;
+        if (o > 26) v |= op.kw[w + 1] << (32 - o);
+        idx[p] = v & 63u;
+      }
+    }
+    u32x4 hi, lo;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      hi[p] = s_tab[idx[p]];
+      lo[p] = s_tab[kTabLoOff + idx[p]];
+    }
+    const h8 chi = __builtin_bit_cast(h8, hi);
+    const h8 clo = __builtin_bit_cast(h8, lo);
+    Shi = __builtin_amdgcn_mfma_f32_16x16x32_f16(chi, qhi[kk], Shi, 0, 0, 0);
+    Shi = __builtin_amdgcn_mfma_f32_16x16x32_f16(chi, qlo[kk], Shi, 0, 0, 0);
+    Slo = __builtin_amdgcn_mfma_f32_16x16x32_f16(clo, qhi[kk], Slo, 0, 0, 0);
+    Nhi = __builtin_amdgcn_mfma_f32_16x16x32_f16(chi, chi, Nhi, 0, 0, 0);
+    Nx = __builtin_amdgcn_mfma_f32_16x16x32_f16(chi, clo, Nx, 0, 0, 0);
+  }
+
+  // ---- scores of this lane's 4 tokens (rows 4*g4 + r) for head r16 ----
+  const int diag_src = 20 * g4;            // lane 16*g4 + 4*g4 (+ r) holds N[4*g4+r][4*g4+r]
+  float s[4], pm = -INFINITY;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const float nd = Nhi[r] + (2.0f / kLoScale) * Nx[r];
+    const float nn = lane_value(nd, diag_src + r);
+    const float fac = fscale * f16_bits_to_f32(op.n[r]) * __builtin_amdgcn_rsqf(nn + 1e-16f);
+    const float dot = Shi[r] + Slo[r] * (1.0f / kLoScale);
+    s[r] = (4 * g4 + r < valid_rows) ? dot * fac : -INFINITY;
+    pm = fmaxf(pm, s[r]);
+  }
+  pm = max_x32(max_x16(pm));
+  // lazy running maximum: rescale only when a head's maximum grows by more
+  // than kLazy (base 2), so p <= 2^kLazy; a V scale large enough for p * scale
+  // to overflow f16 forces an exact maximum (p <= 1) for that slab
+  float sc[4], zr[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const bool row_ok = 4 * g4 + r < valid_rows;
+    // masked rows may hold stale bytes: their scale and zero are not used
+    sc[r] = row_ok ? f16_bits_to_f32(op.sz[r] & 0xFFFFu) : 0.0f;
+    zr[r] = row_ok ? f16_bits_to_f32(op.sz[r] >> 16) : 0.0f;
+  }
+  const float sc_max = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+  const float thr = __any(sc_max > 1000.0f) ? 0.0f : kLazy;
+  if (__any(pm > st.m_run + thr)) {
+    const float m_new = fmaxf(st.m_run, pm);
+    const float corr = __builtin_amdgcn_exp2f(st.m_run - m_new);   // 0 on the first slab
+    st.l_part *= corr;
+    st.z_part *= corr;
+    // O rows are heads 4*g4 + r; their factors sit in lanes r16 = head
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float cr = lane_value(corr, 4 * g4 + r);
+#pragma unroll
+      for (int m = 0; m < 8; ++m) st.O[m][r] *= cr;
+    }
+    st.m_run = m_new;
+  }
+  h4 W;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const float p = __builtin_amdgcn_exp2f(s[r] - st.m_run);      // 0 for masked rows
+    st.l_part += p;
+    st.z_part += p * zr[r];
+    W[r] = static_cast<_Float16>(head_live ? p * sc[r] : 0.0f);
+  }
+
+  // ---- V: codes of tokens 4*g4 + r at coordinates 8*r16 + m ----
+  const h2 b1024 = {static_cast<_Float16>(1024.0f), static_cast<_Float16>(1024.0f)};
+  const h2 b64 = {static_cast<_Float16>(64.0f), static_cast<_Float16>(64.0f)};
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    // byte kb of each token's dword -> [x0, 0, x1, 0]
+    const uint32_t sel = kb | (0x0Cu << 8) | ((4u + kb) << 16) | (0x0Cu << 24);
+    const uint32_t p01 = __builtin_amdgcn_perm(op.X[1], op.X[0], sel);
+    const uint32_t p23 = __builtin_amdgcn_perm(op.X[3], op.X[2], sel);
+    // low nibble -> 1024 + code, high nibble -> 64 + code (exact f16), minus the bias
+    h2 lo01 = __builtin_bit_cast(h2, (p01 & 0x000F000Fu) | 0x64006400u);
+    h2 lo23 = __builtin_bit_cast(h2, (p23 & 0x000F000Fu) | 0x64006400u);
+    h2 hi01 = __builtin_bit_cast(h2, (p01 & 0x00F000F0u) | 0x54005400u);
+    h2 hi23 = __builtin_bit_cast(h2, (p23 & 0x00F000F0u) | 0x54005400u);
+    lo01 -= b1024;
+    lo23 -= b1024;
+    hi01 -= b64;
+    hi23 -= b64;
+    const h4 Blo = {lo01[0], lo01[1], lo23[0], lo23[1]};
+    const h4 Bhi = {hi01[0], hi01[1], hi23[0], hi23[1]};
+    st.O[2 * kb] = __builtin_amdgcn_mfma_f32_16x16x16f16(W, Blo, st.O[2 * kb], 0, 0, 0);
+    st.O[2 * kb + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(W, Bhi, st.O[2 * kb + 1], 0, 0, 0);
+  }
+}
+
+// page ids of this split -> byte offsets in LDS (-1: outside the cache)
+__device__ __forceinline__ void stage_page_offsets(const MfmaArgs& a, int b, int t0, int t1,
+                                                   int64_t page_bytes, int64_t* s_page_off) {
+  const int p_first = t0 >> a.bs_shift;
+  const int n_pages = t1 > t0 ? ((t1 - 1) >> a.bs_shift) - p_first + 1 : 0;
+  const int32_t* bt = a.block_table + static_cast<int64_t>(b) * a.max_blocks;
+  for (int i = threadIdx.x; i < n_pages; i += blockDim.x) {
+    const int page = bt[p_first + i];
+    if (page < 0 || page >= a.num_blocks) {
+      const_cast<DevTables*>(a.tables)->err_page = 1;
+      s_page_off[i] = -1;
+    } else {
+      s_page_off[i] = static_cast<int64_t>(page) * page_bytes;
+    }
+  }
+}
+
+// slab starting at token t -> uniform base pointer, nullptr for a bad page
+__device__ __forceinline__ const uint8_t* slab_ptr(const MfmaArgs& a, const int64_t* s_page_off,
+                                                   int p_first, int t, int64_t row_bytes) {
+  const int64_t po = s_page_off[(t >> a.bs_shift) - p_first];
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(po));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(static_cast<uint64_t>(po) >> 32));
+  if (hi == 0xFFFFFFFFu) return nullptr;
+  const int64_t u = static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
+  return a.cache + u + static_cast<int64_t>(t & ((1 << a.bs_shift) - 1)) * row_bytes;
+}
+
+// write this wavefront's split partials: O rows are heads 4*g4 + r
+__device__ __forceinline__ void store_partials(const MfmaArgs& a, int b, int g, int split, int g4,
+                                               int r16, const RunState& st) {
+  const float l_part = sum_x32(sum_x16(st.l_part));
+  const float z_part = sum_x32(sum_x16(st.z_part));
+  const int G = a.G;
+  const int64_t rec0 = (static_cast<int64_t>(b) * a.Hq + g * G) * a.num_splits + split;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int h = 4 * g4 + r;
+    if (h < G) {
+      float* rec = a.part + (rec0 + static_cast<int64_t>(h) * a.num_splits) * kRec;
+      // tile m column r16 is coordinate 8*r16 + m
+      *reinterpret_cast<float4*>(rec + 8 * r16) = make_float4(st.O[0][r], st.O[1][r], st.O[2][r], st.O[3][r]);
+      *reinterpret_cast<float4*>(rec + 8 * r16 + 4) = make_float4(st.O[4][r], st.O[5][r], st.O[6][r], st.O[7][r]);
+    }
+  }
+  if (g4 == 0 && r16 < G) {
+    float* rec = a.part + (rec0 + static_cast<int64_t>(r16) * a.num_splits) * kRec;
+    rec[kD] = st.m_run;
+    rec[kD + 1] = l_part;
+    rec[kD + 2] = z_part;
+  }
+}
+
+// Merge the splits of one (sequence, query head): 8 groups of 32 threads
+// take every 8th split, each thread four coordinates; the groups' partial
+// sums meet in LDS.  Split s is weighted by 2^(m_s - max m).
+__global__ void __launch_bounds__(256) decode_merge_kernel(MfmaArgs a) {
+  __shared__ float s_m[8];
+  __shared__ float4 s_acc[8][kD / 4];
+  __shared__ float s_l[8];
+  const int bh = blockIdx.x;                 // b * Hq + hq
+  const int b = bh / a.Hq;
+  const int grp = threadIdx.x >> 5, ln = threadIdx.x & 31;
+  const int c4 = ln * 4;
+  int T = a.seq_lens[b];
+  const int t_cap = min(a.num_splits * a.chunk, a.max_blocks << a.bs_shift);
+  T = T < 0 ? 0 : (T > t_cap ? t_cap : T);
+  const int nsp = (T + a.chunk - 1) / a.chunk;
+  const float* recs = a.part + static_cast<int64_t>(bh) * a.num_splits * kRec;
+  float M = -INFINITY;
+  for (int sp = grp; sp < nsp; sp += 8) M = fmaxf(M, recs[sp * kRec + kD]);
+  if (ln == 0) s_m[grp] = M;
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 8; ++i) M = fmaxf(M, s_m[i]);
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  float L = 0.0f;
+#pragma unroll 4
+  for (int sp = grp; sp < nsp; sp += 8) {
+    const float* rec = recs + sp * kRec;
+    const float w = __builtin_amdgcn_exp2f(rec[kD] - M);
+    const float z = rec[kD + 2];
+    const float4 v = *reinterpret_cast<const float4*>(rec + c4);
+    acc.x += w * (v.x + z);
+    acc.y += w * (v.y + z);
+    acc.z += w * (v.z + z);
+    acc.w += w * (v.w + z);
+    L += w * rec[kD + 1];
+  }
+  s_acc[grp][ln] = acc;
+  if (ln == 0) s_l[grp] = L;
+  __syncthreads();
+  if (grp != 0) return;
+#pragma unroll
+  for (int i = 1; i < 8; ++i) {
+    const float4 o = s_acc[i][ln];
+    acc.x += o.x;
+    acc.y += o.y;
+    acc.z += o.z;
+    acc.w += o.w;
+    L += s_l[i];
+  }
+  const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+  const float r4[4] = {acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv};
+  const int64_t oi = static_cast<int64_t>(bh) * kD + c4;
+  if (a.out_fp32) {
+    *reinterpret_cast<float4*>(static_cast<float*>(a.out) + oi) = make_float4(r4[0], r4[1], r4[2], r4[3]);
+  } else {
+    uint32_t pk[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      uint32_t u0 = __float_as_uint(r4[2 * i]), u1 = __float_as_uint(r4[2 * i + 1]);
+      u0 = (u0 + 0x7FFFu + ((u0 >> 16) & 1u)) >> 16;     // round to nearest even
+      u1 = (u1 + 0x7FFFu + ((u1 >> 16) & 1u)) >> 16;
+      pk[i] = u0 | (u1 << 16);
+    }
+    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + oi) = make_uint2(pk[0], pk[1]);
+  }
+}
+
+__device__ __forceinline__ int clamp_len(const MfmaArgs& a, int b, int split) {
+  int T = a.seq_lens[b];
+  const int t_cap = min(a.num_splits * a.chunk, a.max_blocks << a.bs_shift);
+  if (T < 0 || T > t_cap) {
+    if (threadIdx.x == 0 && split == 0) const_cast<DevTables*>(a.tables)->err_len = 1;
+    T = T < 0 ? 0 : t_cap;
+  }
+  return T;
+}
+
+// ============================================================================
+// direct: every lane loads its own operand bytes (any head count)
+// ============================================================================
+
+template <int KB>
+struct RawSlab {
+  uint32_t k[KB == 4 ? 5 : 4];   // K code dwords (+1 for re-alignment)
+  uint32_t v[4][2];              // V code dword pairs
+  uint32_t n[4];
+  uint32_t sz[4];
+};
+
+template <int KB>
+struct DirectGeo {
+  uint32_t k_off4, k_sh;
+  uint32_t v_off4[4], v_sh[4];
+  uint32_t n_off[4], s_off[4];
+  bool s_aligned[4];
+};
+
+template <int KB>
+__device__ __forceinline__ void direct_load(const uint8_t* __restrict__ base, const DirectGeo<KB>& lg,
+                                            RawSlab<KB>& s) {
+  const u32x4 k4 = *reinterpret_cast<const u32x4*>(base + lg.k_off4);
+  s.k[0] = k4[0];
+  s.k[1] = k4[1];
+  s.k[2] = k4[2];
+  s.k[3] = k4[3];
+  if constexpr (KB == 4) s.k[4] = *reinterpret_cast<const uint32_t*>(base + lg.k_off4 + 16);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const u32x2 v2 = *reinterpret_cast<const u32x2*>(base + lg.v_off4[r]);
+    s.v[r][0] = v2[0];
+    s.v[r][1] = v2[1];
+    s.n[r] = *reinterpret_cast<const uint16_t*>(base + lg.n_off[r]);
+    // the 4-byte (scale, zero) field ends the slot: never read past it
+    if (lg.s_aligned[r]) {
+      s.sz[r] = *reinterpret_cast<const uint32_t*>(base + lg.s_off[r]);
+    } else {
+      const uint32_t lo16 = *reinterpret_cast<const uint16_t*>(base + lg.s_off[r]);
+      const uint32_t hi16 = *reinterpret_cast<const uint16_t*>(base + lg.s_off[r] + 2);
+      s.sz[r] = lo16 | (hi16 << 16);
+    }
+  }
+}
+
+template <int KB>
+__device__ __forceinline__ SlabOps<KB> direct_ops(const RawSlab<KB>& s, const DirectGeo<KB>& lg) {
+  SlabOps<KB> op;
+#pragma unroll
+  for (int i = 0; i < (KB == 4 ? 4 : 3); ++i) op.kw[i] = funnel(s.k[i + 1], s.k[i], lg.k_sh);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    op.X[r] = funnel(s.v[r][1], s.v[r][0], lg.v_sh[r]);
+    op.n[r] = s.n[r];
+    op.sz[r] = s.sz[r];
+  }
+  return op;
+}
+
+template <int KB, int SLOT>
+__global__ void __launch_bounds__(512) decode_direct_kernel(MfmaArgs a) {
+  constexpr int kKCB = (kD * KB) / 8;           // K code bytes: 64 or 48
+  constexpr int kKP = kKCB + 2;                 // K packed (codes + norm)
+  constexpr int kVCB = kD / 2;                  // V code bytes
+  constexpr int kLaneKB = KB == 4 ? 16 : 12;    // K bytes per lane per slab
+
+  __shared__ uint32_t s_tab[kTabLoOff + 256];
+  __shared__ int64_t s_page_off[kMaxChunkPages];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int r16 = lane & 15;
+  const int g4 = lane >> 4;
+  const int b = blockIdx.y;
+  const int split = blockIdx.x;
+  const int H = a.H;
+  const int64_t row_bytes = static_cast<int64_t>(H) * SLOT;
+  const int64_t page_bytes = static_cast<int64_t>(1 << a.bs_shift) * row_bytes;
+
+  build_tables<KB>(a, s_tab);
+  const int T = clamp_len(a, b, split);
+  const int t0 = split * a.chunk;
+  const int t1 = min(T, t0 + a.chunk);
+  stage_page_offsets(a, b, t0, t1, page_bytes, s_page_off);
+  __syncthreads();
+
+  const int g = wave;
+  if (t0 < t1 && g < H) {
+    h8 qhi[4], qlo[4];
+    load_queries(a, b, g, r16, g4, qhi, qlo);
+    // rows 4*g4 + r: row_bytes is even, so a field's alignment depends on r
+    // and the head only and is uniform across the wavefront
+    DirectGeo<KB> lg;
+    const uint32_t head_off = static_cast<uint32_t>(g * SLOT);
+    const uint32_t rb = static_cast<uint32_t>(row_bytes);
+    const uint32_t k_off = r16 * rb + head_off + kLaneKB * g4;
+    lg.k_off4 = k_off & ~3u;
+    lg.k_sh = k_off & 3u;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const uint32_t row = (4 * g4 + r) * rb;
+      lg.v_off4[r] = (row + head_off + kKP + 4 * r16) & ~3u;
+      lg.v_sh[r] = (row + head_off + kKP + 4 * r16) & 3u;
+      lg.n_off[r] = row + head_off + kKCB;
+      lg.s_off[r] = row + head_off + kKP + kVCB;
+      lg.s_aligned[r] = (lg.s_off[r] & 3u) == 0;
+    }
+    RunState st;
+#pragma unroll
+    for (int m = 0; m < 8; ++m) st.O[m] = f4{0.f, 0.f, 0.f, 0.f};
+    st.m_run = -INFINITY;
+    st.l_part = 0.0f;
+    st.z_part = 0.0f;
+    const bool head_live = r16 < a.G;
+    const int p_first = t0 >> a.bs_shift;
+
+    RawSlab<KB> sa, sb;
+    const uint8_t* pa = slab_ptr(a, s_page_off, p_first, t0, row_bytes);
+    if (pa) direct_load(pa, lg, sa);
+    const uint8_t* pb = t0 + 16 < t1 ? slab_ptr(a, s_page_off, p_first, t0 + 16, row_bytes) : nullptr;
+    if (pb) direct_load(pb, lg, sb);
+    for (int t = t0; t < t1; t += 32) {
+      if (pa) process_slab<KB>(direct_ops(sa, lg), t1 - t, s_tab, qhi, qlo, head_live, a.scale_log2, g4, st);
+      pa = t + 32 < t1 ? slab_ptr(a, s_page_off, p_first, t + 32, row_bytes) : nullptr;
+      if (pa) direct_load(pa, lg, sa);
+      if (t + 16 >= t1) break;
+      if (pb) process_slab<KB>(direct_ops(sb, lg), t1 - t - 16, s_tab, qhi, qlo, head_live, a.scale_log2, g4, st);
+      pb = t + 48 < t1 ? slab_ptr(a, s_page_off, p_first, t + 48, row_bytes) : nullptr;
+      if (pb) direct_load(pb, lg, sb);
+    }
+    store_partials(a, b, g, split, g4, r16, st);
+  }
+}
+
+// ============================================================================
+// staged: each wavefront loads its head's 16 rows with 16-byte loads into a
+// private LDS region, three slabs ahead (even head counts)
+// ============================================================================
+
+// A wavefront's bytes of one row: from its slot start rounded down to 4 to
+// its slot end rounded up to 4 (136 bytes for 134-byte slots, 120 for 118),
+// fetched as 16-byte chunks plus one 8-byte tail, never past the slot end
+// rounded up to 4 (the last head's slot ends the row, the last row the cache).
+template <int SLOT>
+struct StageShape {
+  static constexpr int kSpan = SLOT + 2;               // bytes fetched per row
+  static constexpr int kC16 = (kSpan - 8) / 16;        // 16-byte chunks per row
+  static_assert(16 * kC16 + 8 == kSpan, "row span must be 16-byte chunks plus 8");
+  static constexpr int kRow = 16 * (kC16 + 1);         // LDS bytes per row (16-aligned)
+  static constexpr int kStage = 16 * kRow;             // LDS bytes per slab
+  static constexpr int kChunks = 16 * kC16;            // 16-byte chunks per slab
+  static constexpr int kLoads16 = (kChunks + 63) / 64; // 16-byte loads per lane
+};
+
+template <int SLOT>
+struct StageRegs {
+  u32x4 d[StageShape<SLOT>::kLoads16];
+  u32x2 tail;                                          // lanes 0..15: row lane's last 8 bytes
+  bool ok;                                             // page inside the cache
+};
+
+template <int SLOT>
+__device__ __forceinline__ void stage_load(const uint8_t* base, int lane, uint32_t head_off4,
+                                           uint32_t rb, StageRegs<SLOT>& sr) {
+  using S = StageShape<SLOT>;
+  sr.ok = base != nullptr;
+  if (!sr.ok) return;
+#pragma unroll
+  for (int j = 0; j < S::kLoads16; ++j) {
+    const int c = lane + 64 * j;
+    if (S::kChunks % 64 == 0 || c < S::kChunks) {
+      const int row = c / S::kC16, cc = c - row * S::kC16;
+      sr.d[j] = *reinterpret_cast<const u32x4*>(base + row * rb + head_off4 + 16u * cc);
+    }
+  }
+  if (lane < 16)
+    sr.tail = *reinterpret_cast<const u32x2*>(base + lane * rb + head_off4 + 16u * S::kC16);
+}
+
+template <int SLOT>
+__device__ __forceinline__ void stage_store(uint8_t* lds, int lane, const StageRegs<SLOT>& sr) {
+  using S = StageShape<SLOT>;
+#pragma unroll
+  for (int j = 0; j < S::kLoads16; ++j) {
+    const int c = lane + 64 * j;
+    if (S::kChunks % 64 == 0 || c < S::kChunks) {
+      const int row = c / S::kC16, cc = c - row * S::kC16;
+      *reinterpret_cast<u32x4*>(lds + row * S::kRow + 16 * cc) = sr.d[j];
+    }
+  }
+  if (lane < 16) *reinterpret_cast<u32x2*>(lds + lane * S::kRow + 16 * S::kC16) = sr.tail;
+}
+
+// operands of one lane from the LDS copy of the slab (slot of row t at
+// t * kRow + sh, sh = 0 or 2; reads stay inside the fetched span)
+template <int KB, int SLOT>
+__device__ __forceinline__ SlabOps<KB> staged_ops(const uint8_t* lds, int r16, int g4, uint32_t sh) {
+  using S = StageShape<SLOT>;
+  constexpr int kKCB = (kD * KB) / 8;
+  constexpr int kKP = kKCB + 2;
+  constexpr int kVCB = kD / 2;
+  constexpr int kLaneKB = KB == 4 ? 16 : 12;
+  SlabOps<KB> op;
+  {
+    const uint32_t o = r16 * S::kRow + sh + kLaneKB * g4;
+    const uint32_t* p = reinterpret_cast<const uint32_t*>(lds + (o & ~3u));
+    uint32_t w[kLaneKB / 4 + 1];
+#pragma unroll
+    for (int i = 0; i < kLaneKB / 4 + 1; ++i) w[i] = p[i];
+#pragma unroll
+    for (int i = 0; i < kLaneKB / 4; ++i) op.kw[i] = funnel(w[i + 1], w[i], o & 3u);
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const uint32_t rowo = (4 * g4 + r) * S::kRow + sh;
+    const uint32_t vo = rowo + kKP + 4 * r16;
+    const uint32_t* pv = reinterpret_cast<const uint32_t*>(lds + (vo & ~3u));
+    op.X[r] = funnel(pv[1], pv[0], vo & 3u);
+    op.n[r] = *reinterpret_cast<const uint16_t*>(lds + rowo + kKCB);
+    const uint32_t so = rowo + kKP + kVCB;
+    const uint32_t* ps = reinterpret_cast<const uint32_t*>(lds + (so & ~3u));
+    op.sz[r] = funnel(ps[1], ps[0], so & 3u);
+  }
+  return op;
+}
+
+template <int KB, int SLOT>
+__global__ void __launch_bounds__(512) decode_staged_kernel(MfmaArgs a) {
+  using S = StageShape<SLOT>;
+  constexpr int kMaxWaves = 8;
+
+  __shared__ uint32_t s_tab[kTabLoOff + 256];
+  __shared__ int64_t s_page_off[kMaxChunkPages];
+  __shared__ __align__(16) uint8_t s_stage[kMaxWaves][3][S::kStage + 16];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int r16 = lane & 15;
+  const int g4 = lane >> 4;
+  const int b = blockIdx.y;
+  const int split = blockIdx.x;
+  const int H = a.H;
+  const int64_t row_bytes = static_cast<int64_t>(H) * SLOT;
+  const int64_t page_bytes = static_cast<int64_t>(1 << a.bs_shift) * row_bytes;
+
+  build_tables<KB>(a, s_tab);
+  const int T = clamp_len(a, b, split);
+  const int t0 = split * a.chunk;
+  const int t1 = min(T, t0 + a.chunk);
+  stage_page_offsets(a, b, t0, t1, page_bytes, s_page_off);
+  __syncthreads();
+
+  const int g = wave;
+  if (t0 < t1 && g < H) {
+    h8 qhi[4], qlo[4];
+    load_queries(a, b, g, r16, g4, qhi, qlo);
+    const uint32_t rb = static_cast<uint32_t>(row_bytes);
+    const uint32_t head_off = static_cast<uint32_t>(g * SLOT);
+    const uint32_t head_off4 = head_off & ~3u;               // rows start 4-aligned (H even)
+    const uint32_t sh = head_off & 3u;
+    RunState st;
+#pragma unroll
+    for (int m = 0; m < 8; ++m) st.O[m] = f4{0.f, 0.f, 0.f, 0.f};
+    st.m_run = -INFINITY;
+    st.l_part = 0.0f;
+    st.z_part = 0.0f;
+    const bool head_live = r16 < a.G;
+    const int p_first = t0 >> a.bs_shift;
+    uint8_t* lds0 = s_stage[wave][0];
+    uint8_t* lds1 = s_stage[wave][1];
+    uint8_t* lds2 = s_stage[wave][2];
+
+    // three slabs in flight in registers, each with its own LDS buffer
+    StageRegs<SLOT> r0, r1, r2;
+    auto load = [&](int t, StageRegs<SLOT>& r) {
+      if (t < t1)
+        stage_load<SLOT>(slab_ptr(a, s_page_off, p_first, t, row_bytes), lane, head_off4, rb, r);
+      else
+        r.ok = false;
+    };
+    auto step = [&](int t, StageRegs<SLOT>& r, uint8_t* lds) {
+      // slab t is in r: park it in LDS, refill r with slab t + 48, compute slab t
+      const bool ok = r.ok;
+      if (ok) stage_store<SLOT>(lds, lane, r);
+      load(t + 48, r);
+      if (ok)
+        process_slab<KB>(staged_ops<KB, SLOT>(lds, r16, g4, sh), t1 - t, s_tab, qhi, qlo,
+                         head_live, a.scale_log2, g4, st);
+    };
+    load(t0, r0);
+    load(t0 + 16, r1);
+    load(t0 + 32, r2);
+    for (int t = t0; t < t1; t += 48) {
+      step(t, r0, lds0);
+      if (t + 16 >= t1) break;
+      step(t + 16, r1, lds1);
+      if (t + 32 >= t1) break;
+      step(t + 32, r2, lds2);
+    }
+    store_partials(a, b, g, split, g4, r16, st);
+  }
+}
+
+}  // namespace
+
+bool mfma_decode_eligible(const Geometry& g, int num_q_heads) {
+  const int G = num_q_heads / g.num_kv_heads;
+  return g.head_dim == kD && (g.key_bits == 4 || g.key_bits == 3) && g.block_size % 16 == 0 &&
+         G >= 1 && G <= 16 && g.num_kv_heads <= 8 && (g.slot == 134 || g.slot == 118);
+}
+
+size_t mfma_partial_bytes(int batch, int num_q_heads, int num_splits) {
+  return static_cast<size_t>(batch) * num_q_heads * num_splits * kRec * sizeof(float);
+}
+
+hipError_t launch_decode_mfma(const Geometry& g, const DevTables* tables, const DecodePlan& plan,
+                              const uint16_t* q, const uint8_t* cache, int64_t num_blocks,
+                              const int32_t* block_table, int max_blocks_per_seq,
+                              const int32_t* seq_lens, int batch, int num_q_heads, float sm_scale,
+                              void* out, int out_is_fp32, void* workspace, hipStream_t stream) {
+  MfmaArgs a;
+  a.tables = tables;
+  a.q = q;
+  a.cache = cache;
+  a.num_blocks = num_blocks;
+  a.block_table = block_table;
+  a.max_blocks = max_blocks_per_seq;
+  a.seq_lens = seq_lens;
+  a.Hq = num_q_heads;
+  a.H = g.num_kv_heads;
+  a.G = num_q_heads / g.num_kv_heads;
+  a.bs_shift = __builtin_ctz(static_cast<unsigned>(g.block_size));
+  a.chunk = plan.chunk;
+  a.num_splits = plan.num_splits;
+  a.scale_log2 = sm_scale * kLog2e;
+  a.part = static_cast<float*>(workspace);
+  a.out = out;
+  a.out_fp32 = out_is_fp32;
+  const dim3 grid(plan.num_splits, batch);
+  const dim3 block(64 * g.num_kv_heads);
+  const bool staged = (g.num_kv_heads % 2) == 0;
+  if (g.key_bits == 4) {
+    if (staged)
+      hipLaunchKernelGGL((decode_staged_kernel<4, 134>), grid, block, 0, stream, a);
+    else
+      hipLaunchKernelGGL((decode_direct_kernel<4, 134>), grid, block, 0, stream, a);
+  } else {
+    if (staged)
+      hipLaunchKernelGGL((decode_staged_kernel<3, 118>), grid, block, 0, stream, a);
+    else
+      hipLaunchKernelGGL((decode_direct_kernel<3, 118>), grid, block, 0, stream, a);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // merge: one workgroup per (sequence, query head)
+  hipLaunchKernelGGL(decode_merge_kernel, dim3(batch * num_q_heads), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace tq

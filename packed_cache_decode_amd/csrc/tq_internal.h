@@ -45,10 +45,19 @@ hipError_t launch_store(const Geometry& g, const DevTables* tables, const uint16
                         hipStream_t stream);
 
 struct DecodePlan {
+  int mfma;         // 1: matrix-core kernel (tq_decode_mfma.hip), 0: general kernel
   int chunk;        // tokens per split
   int num_splits;   // splits per sequence (grid extent)
   size_t workspace_bytes;
 };
+
+bool mfma_decode_eligible(const Geometry& g, int num_q_heads);
+size_t mfma_partial_bytes(int batch, int num_q_heads, int num_splits);
+hipError_t launch_decode_mfma(const Geometry& g, const DevTables* tables, const DecodePlan& plan,
+                              const uint16_t* q, const uint8_t* cache, int64_t num_blocks,
+                              const int32_t* block_table, int max_blocks_per_seq,
+                              const int32_t* seq_lens, int batch, int num_q_heads, float sm_scale,
+                              void* out, int out_is_fp32, void* workspace, hipStream_t stream);
 
 DecodePlan plan_decode(const Geometry& g, int batch, int num_q_heads, int max_seq_len);
 

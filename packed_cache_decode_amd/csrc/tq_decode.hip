@@ -364,10 +364,12 @@ hipError_t launch_g(const DecodeArgs& a, int G, int batch, hipStream_t stream) {
 DecodePlan plan_decode(const Geometry& g, int batch, int num_q_heads, int max_seq_len) {
   DecodePlan p;
   if (mfma_decode_eligible(g, num_q_heads)) {
-    // about 256 workgroups (one per CU: one wavefront per kv head), 16-token
-    // slabs, at least 8 slabs per split so the per-workgroup set-up is amortised
+    // about 3072 wavefronts (12 per CU: 256 CUs, 3 per SIMD) over
+    // (split, sequence, kv head), 16-token slabs, at least 8 slabs per split
+    // so the per-wavefront set-up is amortised
     const int slabs = max_seq_len > 0 ? (max_seq_len + 15) / 16 : 1;
-    int s = batch > 0 ? (256 + batch - 1) / batch : 1;
+    const int per_split = batch * g.num_kv_heads;
+    int s = per_split > 0 ? (3072 + per_split - 1) / per_split : 1;
     const int s_max = (slabs + 7) / 8;
     s = s < 1 ? 1 : (s > s_max ? s_max : s);
     p.mfma = 1;

@@ -63,7 +63,7 @@ constexpr float kLoScale = 2048.0f;          // lo parts are stored x 2^11
 constexpr int kRec = kD + 4;                 // partial record: O[128], m, l, z, pad
 constexpr float kLazy = 6.0f;                // rescale when the max grows by > 2^6
 constexpr int kMaxChunkPages = 256;          // pages of one split staged in LDS
-constexpr int kTabLoOff = 272;               // lo table offset (dwords): other banks
+constexpr int kBufferWord3 = 0x00020000;     // raw buffer resource, 32-bit data format (gfx9 family)
 
 struct MfmaArgs {
   const DevTables* tables;
@@ -136,9 +136,11 @@ struct SlabOps {
   uint32_t sz[4];                 // V scale (low half) and zero (high half) of token 4*g4 + r
 };
 
-// centroid tables: entry e holds two codes (low code first); hi and lo parts
+// centroid table: entry e holds two codes (low code first) as {hi pair, lo
+// pair}, so one 8-byte LDS read fetches both parts (random reads of a small
+// table cost the same per instruction for 4 and 8 bytes per lane)
 template <int KB>
-__device__ __forceinline__ void build_tables(const MfmaArgs& a, uint32_t* s_tab) {
+__device__ __forceinline__ void build_tables(const MfmaArgs& a, u32x2* s_tab) {
   constexpr int kTab = KB == 4 ? 256 : 64;
   for (int e = threadIdx.x; e < kTab; e += blockDim.x) {
     const int c0 = e & ((1 << KB) - 1), c1 = e >> KB;
@@ -146,8 +148,7 @@ __device__ __forceinline__ void build_tables(const MfmaArgs& a, uint32_t* s_tab)
     const _Float16 h0 = static_cast<_Float16>(v0), h1 = static_cast<_Float16>(v1);
     const _Float16 l0 = static_cast<_Float16>((v0 - static_cast<float>(h0)) * kLoScale);
     const _Float16 l1 = static_cast<_Float16>((v1 - static_cast<float>(h1)) * kLoScale);
-    s_tab[e] = pack_h2(h0, h1);
-    s_tab[kTabLoOff + e] = pack_h2(l0, l1);
+    s_tab[e] = u32x2{pack_h2(h0, h1), pack_h2(l0, l1)};
   }
 }
 
@@ -155,7 +156,7 @@ __device__ __forceinline__ void build_tables(const MfmaArgs& a, uint32_t* s_tab)
 // split them into f16 hi / lo; lane (h = r16, g4) holds coordinates
 // [32*g4, 32*g4 + 32) of head h, as the four score-MFMA B operands
 __device__ __forceinline__ void load_queries(const MfmaArgs& a, int b, int g, int r16, int g4,
-                                             h8 (&qhi)[4], h8 (&qlo)[4]) {
+                                             float fscale, h8 (&qhi)[4], h8 (&qlo)[4]) {
   float x[32];
   const bool live = r16 < a.G;
   const uint16_t* qp = a.q + (static_cast<int64_t>(b) * a.Hq + g * a.G + (live ? r16 : 0)) * kD + 32 * g4;
@@ -193,27 +194,40 @@ __device__ __forceinline__ void load_queries(const MfmaArgs& a, int b, int g, in
     const float o = (g4 & 2) ? __uint_as_float(sw[0]) : __uint_as_float(sw[1]);
     x[j] = (g4 & 2) ? (o - x[j]) : (x[j] + o);
   }
-  const float rsd = 0.08838834764831845f;    // 1/sqrt(128); the softmax scale is applied in fp32
+  // 1/sqrt(128) of the rotation times the softmax scale (base 2): scores come
+  // out of the MFMAs ready for exp2
+  const float qs = 0.08838834764831845f * fscale;
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float v = live ? x[8 * kk + e] * rsd : 0.0f;
+      const float v = live ? x[8 * kk + e] * qs : 0.0f;
       const _Float16 hv = static_cast<_Float16>(v);
       qhi[kk][e] = hv;
       qlo[kk][e] = static_cast<_Float16>(v - static_cast<float>(hv));
     }
 }
 
-// One slab: scores, norm correction, online softmax, P.V.
+// (x & m) | c for c with no bits under m, as one v_bfi_b32 (the compiler
+// splits it into two instructions when both constants are literals; the mask
+// is kept in a register instead)
+__device__ __forceinline__ uint32_t insert_bits(uint32_t x, uint32_t m, uint32_t c) {
+  uint32_t r;
+  asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(r) : "v"(m), "v"(x), "s"(c));
+  return r;
+}
+
+// One slab: scores, norm correction, online softmax, P.V.  Rows of query
+// heads >= G have q = 0: their scores, weights and O rows are finite and
+// never stored.
 template <int KB>
 __device__ __forceinline__ void process_slab(const SlabOps<KB>& op, int valid_rows,
-                                             const uint32_t* s_tab, const h8 (&qhi)[4],
-                                             const h8 (&qlo)[4], bool head_live, float fscale,
-                                             int g4, RunState& st) {
+                                             const u32x2* s_tab, const h8 (&qhi)[4],
+                                             const h8 (&qlo)[4], int g4, RunState& st) {
   // ---- K: codes -> centroid hi / lo operands, score and norm MFMAs ----
+  // (the norm accumulator starts at the 1e-16 of the correction's denominator)
   f4 Shi = {0.f, 0.f, 0.f, 0.f}, Slo = {0.f, 0.f, 0.f, 0.f};
-  f4 Nhi = {0.f, 0.f, 0.f, 0.f}, Nx = {0.f, 0.f, 0.f, 0.f};
+  f4 Nhi = {1e-16f, 1e-16f, 1e-16f, 1e-16f}, Nx = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) {
     uint32_t idx[4];
@@ -234,8 +248,9 @@ __device__ __forceinline__ void process_slab(const SlabOps<KB>& op, int valid_ro
     u32x4 hi, lo;
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
-      hi[p] = s_tab[idx[p]];
-      lo[p] = s_tab[kTabLoOff + idx[p]];
+      const u32x2 e = s_tab[idx[p]];
+      hi[p] = e[0];
+      lo[p] = e[1];
     }
     const h8 chi = __builtin_bit_cast(h8, hi);
     const h8 clo = __builtin_bit_cast(h8, lo);
@@ -246,34 +261,36 @@ __device__ __forceinline__ void process_slab(const SlabOps<KB>& op, int valid_ro
     Nx = __builtin_amdgcn_mfma_f32_16x16x32_f16(chi, clo, Nx, 0, 0, 0);
   }
 
-  // ---- scores of this lane's 4 tokens (rows 4*g4 + r) for head r16 ----
+  // ---- scores (base 2) of this lane's 4 tokens (rows 4*g4 + r), head r16 ----
   const int diag_src = 20 * g4;            // lane 16*g4 + 4*g4 (+ r) holds N[4*g4+r][4*g4+r]
   float s[4], pm = -INFINITY;
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const float nd = Nhi[r] + (2.0f / kLoScale) * Nx[r];
-    const float nn = lane_value(nd, diag_src + r);
-    const float fac = fscale * f16_bits_to_f32(op.n[r]) * __builtin_amdgcn_rsqf(nn + 1e-16f);
-    const float dot = Shi[r] + Slo[r] * (1.0f / kLoScale);
-    s[r] = (4 * g4 + r < valid_rows) ? dot * fac : -INFINITY;
-    pm = fmaxf(pm, s[r]);
-  }
-  pm = max_x32(max_x16(pm));
-  // lazy running maximum: rescale only when a head's maximum grows by more
-  // than kLazy (base 2), so p <= 2^kLazy; a V scale large enough for p * scale
-  // to overflow f16 forces an exact maximum (p <= 1) for that slab
-  float sc[4], zr[4];
+  uint32_t szm[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const bool row_ok = 4 * g4 + r < valid_rows;
-    // masked rows may hold stale bytes: their scale and zero are not used
-    sc[r] = row_ok ? f16_bits_to_f32(op.sz[r] & 0xFFFFu) : 0.0f;
-    zr[r] = row_ok ? f16_bits_to_f32(op.sz[r] >> 16) : 0.0f;
+    const float nd = Nhi[r] + (2.0f / kLoScale) * Nx[r];
+    const float nn = lane_value(nd, diag_src + r);
+    const float fac = f16_bits_to_f32(op.n[r]) * __builtin_amdgcn_rsqf(nn);
+    const float dot = Shi[r] + Slo[r] * (1.0f / kLoScale);
+    s[r] = row_ok ? dot * fac : -INFINITY;
+    pm = fmaxf(pm, s[r]);
+    szm[r] = row_ok ? op.sz[r] : 0u;       // rows past the end may hold stale bytes
   }
+  float sc[4], zr[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    sc[r] = f16_bits_to_f32(szm[r] & 0xFFFFu);
+    zr[r] = f16_bits_to_f32(szm[r] >> 16);
+  }
+  // Lazy running maximum: the accumulators are rescaled only when some
+  // lane's rows exceed the head's running max by more than kLazy (base 2),
+  // so p <= 2^kLazy; where p * scale could overflow f16 (scale > 1000) the
+  // lane allows no growth (p <= 1).  A rescale moves the whole head to its
+  // exact maximum, so every lane of a head always shares one running max.
   const float sc_max = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
-  const float thr = __any(sc_max > 1000.0f) ? 0.0f : kLazy;
+  const float thr = sc_max > 1000.0f ? 0.0f : kLazy;
   if (__any(pm > st.m_run + thr)) {
-    const float m_new = fmaxf(st.m_run, pm);
+    const float m_new = fmaxf(st.m_run, max_x32(max_x16(pm)));
     const float corr = __builtin_amdgcn_exp2f(st.m_run - m_new);   // 0 on the first slab
     st.l_part *= corr;
     st.z_part *= corr;
@@ -292,7 +309,7 @@ __device__ __forceinline__ void process_slab(const SlabOps<KB>& op, int valid_ro
     const float p = __builtin_amdgcn_exp2f(s[r] - st.m_run);      // 0 for masked rows
     st.l_part += p;
     st.z_part += p * zr[r];
-    W[r] = static_cast<_Float16>(head_live ? p * sc[r] : 0.0f);
+    W[r] = static_cast<_Float16>(p * sc[r]);
   }
 
   // ---- V: codes of tokens 4*g4 + r at coordinates 8*r16 + m ----
@@ -305,10 +322,10 @@ __device__ __forceinline__ void process_slab(const SlabOps<KB>& op, int valid_ro
     const uint32_t p01 = __builtin_amdgcn_perm(op.X[1], op.X[0], sel);
     const uint32_t p23 = __builtin_amdgcn_perm(op.X[3], op.X[2], sel);
     // low nibble -> 1024 + code, high nibble -> 64 + code (exact f16), minus the bias
-    h2 lo01 = __builtin_bit_cast(h2, (p01 & 0x000F000Fu) | 0x64006400u);
-    h2 lo23 = __builtin_bit_cast(h2, (p23 & 0x000F000Fu) | 0x64006400u);
-    h2 hi01 = __builtin_bit_cast(h2, (p01 & 0x00F000F0u) | 0x54005400u);
-    h2 hi23 = __builtin_bit_cast(h2, (p23 & 0x00F000F0u) | 0x54005400u);
+    h2 lo01 = __builtin_bit_cast(h2, insert_bits(p01, 0x000F000Fu, 0x64006400u));
+    h2 lo23 = __builtin_bit_cast(h2, insert_bits(p23, 0x000F000Fu, 0x64006400u));
+    h2 hi01 = __builtin_bit_cast(h2, insert_bits(p01, 0x00F000F0u, 0x54005400u));
+    h2 hi23 = __builtin_bit_cast(h2, insert_bits(p23, 0x00F000F0u, 0x54005400u));
     lo01 -= b1024;
     lo23 -= b1024;
     hi01 -= b64;
@@ -348,6 +365,41 @@ __device__ __forceinline__ const uint8_t* slab_ptr(const MfmaArgs& a, const int6
   return a.cache + u + static_cast<int64_t>(t & ((1 << a.bs_shift) - 1)) * row_bytes;
 }
 
+// Buffer resource of the 16 rows of the slab starting at token t.  A slab
+// past the split end or on a bad page gets an empty range (every load of it
+// returns zeros without touching memory) and ok = false, so the prefetch is
+// issued unconditionally: with a fixed number of loads per slab the compiler
+// waits only for the oldest slab in flight instead of draining every load.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t slab_rsrc(const MfmaArgs& a, const int64_t* s_page_off,
+                                                          int p_first, int t, int t1,
+                                                          int64_t row_bytes, bool& ok) {
+  const uint8_t* p = t < t1 ? slab_ptr(a, s_page_off, p_first, t, row_bytes) : nullptr;
+  ok = p != nullptr;
+  const int bytes = ok ? static_cast<int>(16 * row_bytes) : 0;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(ok ? p : a.cache), 0, bytes,
+                                           kBufferWord3);
+}
+
+// Tokens of sequence b the kernels attend to: seq_lens[b] clamped to what the
+// block table and the splits can address; a cache without pages holds none
+// (its page ids are all out of range, which the page staging reports).
+__device__ __forceinline__ int effective_len(const MfmaArgs& a, int b) {
+  int T = a.seq_lens[b];
+  const int t_cap = min(a.num_splits * a.chunk, a.max_blocks << a.bs_shift);
+  T = T < 0 ? 0 : (T > t_cap ? t_cap : T);
+  return a.num_blocks > 0 ? T : 0;
+}
+
+__device__ __forceinline__ int clamp_len(const MfmaArgs& a, int b, int split) {
+  const int T = a.seq_lens[b];
+  const int t_cap = min(a.num_splits * a.chunk, a.max_blocks << a.bs_shift);
+  if (threadIdx.x == 0 && split == 0 && blockIdx.z == 0) {
+    if (T < 0 || T > t_cap) const_cast<DevTables*>(a.tables)->err_len = 1;
+    if (T > 0 && a.num_blocks <= 0) const_cast<DevTables*>(a.tables)->err_page = 1;
+  }
+  return effective_len(a, b);
+}
+
 // write this wavefront's split partials: O rows are heads 4*g4 + r
 __device__ __forceinline__ void store_partials(const MfmaArgs& a, int b, int g, int split, int g4,
                                                int r16, const RunState& st) {
@@ -384,9 +436,7 @@ __global__ void __launch_bounds__(256) decode_merge_kernel(MfmaArgs a) {
   const int b = bh / a.Hq;
   const int grp = threadIdx.x >> 5, ln = threadIdx.x & 31;
   const int c4 = ln * 4;
-  int T = a.seq_lens[b];
-  const int t_cap = min(a.num_splits * a.chunk, a.max_blocks << a.bs_shift);
-  T = T < 0 ? 0 : (T > t_cap ? t_cap : T);
+  const int T = effective_len(a, b);
   const int nsp = (T + a.chunk - 1) / a.chunk;
   const float* recs = a.part + static_cast<int64_t>(bh) * a.num_splits * kRec;
   float M = -INFINITY;
@@ -438,16 +488,6 @@ __global__ void __launch_bounds__(256) decode_merge_kernel(MfmaArgs a) {
     }
     *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + oi) = make_uint2(pk[0], pk[1]);
   }
-}
-
-__device__ __forceinline__ int clamp_len(const MfmaArgs& a, int b, int split) {
-  int T = a.seq_lens[b];
-  const int t_cap = min(a.num_splits * a.chunk, a.max_blocks << a.bs_shift);
-  if (T < 0 || T > t_cap) {
-    if (threadIdx.x == 0 && split == 0) const_cast<DevTables*>(a.tables)->err_len = 1;
-    T = T < 0 ? 0 : t_cap;
-  }
-  return T;
 }
 
 // ============================================================================
@@ -517,7 +557,7 @@ __global__ void __launch_bounds__(512) decode_direct_kernel(MfmaArgs a) {
   constexpr int kVCB = kD / 2;                  // V code bytes
   constexpr int kLaneKB = KB == 4 ? 16 : 12;    // K bytes per lane per slab
 
-  __shared__ uint32_t s_tab[kTabLoOff + 256];
+  __shared__ u32x2 s_tab[256];
   __shared__ int64_t s_page_off[kMaxChunkPages];
 
   const int tid = threadIdx.x;
@@ -541,7 +581,7 @@ __global__ void __launch_bounds__(512) decode_direct_kernel(MfmaArgs a) {
   const int g = wave;
   if (t0 < t1 && g < H) {
     h8 qhi[4], qlo[4];
-    load_queries(a, b, g, r16, g4, qhi, qlo);
+    load_queries(a, b, g, r16, g4, a.scale_log2, qhi, qlo);
     // rows 4*g4 + r: row_bytes is even, so a field's alignment depends on r
     // and the head only and is uniform across the wavefront
     DirectGeo<KB> lg;
@@ -565,7 +605,6 @@ __global__ void __launch_bounds__(512) decode_direct_kernel(MfmaArgs a) {
     st.m_run = -INFINITY;
     st.l_part = 0.0f;
     st.z_part = 0.0f;
-    const bool head_live = r16 < a.G;
     const int p_first = t0 >> a.bs_shift;
 
     RawSlab<KB> sa, sb;
@@ -574,11 +613,11 @@ __global__ void __launch_bounds__(512) decode_direct_kernel(MfmaArgs a) {
     const uint8_t* pb = t0 + 16 < t1 ? slab_ptr(a, s_page_off, p_first, t0 + 16, row_bytes) : nullptr;
     if (pb) direct_load(pb, lg, sb);
     for (int t = t0; t < t1; t += 32) {
-      if (pa) process_slab<KB>(direct_ops(sa, lg), t1 - t, s_tab, qhi, qlo, head_live, a.scale_log2, g4, st);
+      if (pa) process_slab<KB>(direct_ops(sa, lg), t1 - t, s_tab, qhi, qlo, g4, st);
       pa = t + 32 < t1 ? slab_ptr(a, s_page_off, p_first, t + 32, row_bytes) : nullptr;
       if (pa) direct_load(pa, lg, sa);
       if (t + 16 >= t1) break;
-      if (pb) process_slab<KB>(direct_ops(sb, lg), t1 - t - 16, s_tab, qhi, qlo, head_live, a.scale_log2, g4, st);
+      if (pb) process_slab<KB>(direct_ops(sb, lg), t1 - t - 16, s_tab, qhi, qlo, g4, st);
       pb = t + 48 < t1 ? slab_ptr(a, s_page_off, p_first, t + 48, row_bytes) : nullptr;
       if (pb) direct_load(pb, lg, sb);
     }
@@ -610,25 +649,41 @@ template <int SLOT>
 struct StageRegs {
   u32x4 d[StageShape<SLOT>::kLoads16];
   u32x2 tail;                                          // lanes 0..15: row lane's last 8 bytes
-  bool ok;                                             // page inside the cache
+  bool ok;                                             // a real slab (else a dummy load)
+};
+
+// Per-lane byte offsets (from a slab's first row) of the lane's 16-byte
+// chunks and 8-byte tail; lanes without a chunk of their own re-read the last
+// one and lanes 16..63 re-read a tail, so every lane issues the same loads.
+template <int SLOT>
+struct StageOffsets {
+  uint32_t d[StageShape<SLOT>::kLoads16];
+  uint32_t tail;
 };
 
 template <int SLOT>
-__device__ __forceinline__ void stage_load(const uint8_t* base, int lane, uint32_t head_off4,
-                                           uint32_t rb, StageRegs<SLOT>& sr) {
+__device__ __forceinline__ StageOffsets<SLOT> stage_offsets(int lane, uint32_t head_off4, uint32_t rb) {
   using S = StageShape<SLOT>;
-  sr.ok = base != nullptr;
-  if (!sr.ok) return;
+  StageOffsets<SLOT> o;
 #pragma unroll
   for (int j = 0; j < S::kLoads16; ++j) {
-    const int c = lane + 64 * j;
-    if (S::kChunks % 64 == 0 || c < S::kChunks) {
-      const int row = c / S::kC16, cc = c - row * S::kC16;
-      sr.d[j] = *reinterpret_cast<const u32x4*>(base + row * rb + head_off4 + 16u * cc);
-    }
+    int c = lane + 64 * j;
+    if (c >= S::kChunks) c = S::kChunks - 1;
+    const int row = c / S::kC16, cc = c - row * S::kC16;
+    o.d[j] = row * rb + head_off4 + 16u * cc;
   }
-  if (lane < 16)
-    sr.tail = *reinterpret_cast<const u32x2*>(base + lane * rb + head_off4 + 16u * S::kC16);
+  o.tail = (lane & 15) * rb + head_off4 + 16u * S::kC16;
+  return o;
+}
+
+template <int SLOT>
+__device__ __forceinline__ void stage_load(__amdgpu_buffer_rsrc_t rs, const StageOffsets<SLOT>& o,
+                                           StageRegs<SLOT>& sr) {
+  using S = StageShape<SLOT>;
+#pragma unroll
+  for (int j = 0; j < S::kLoads16; ++j)
+    sr.d[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, o.d[j], 0, 0));
+  sr.tail = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, o.tail, 0, 0));
 }
 
 template <int SLOT>
@@ -679,21 +734,19 @@ __device__ __forceinline__ SlabOps<KB> staged_ops(const uint8_t* lds, int r16, i
 }
 
 template <int KB, int SLOT>
-__global__ void __launch_bounds__(512) decode_staged_kernel(MfmaArgs a) {
+__global__ void __launch_bounds__(64, KB == 4 ? 3 : 2) decode_staged_kernel(MfmaArgs a) {
   using S = StageShape<SLOT>;
-  constexpr int kMaxWaves = 8;
 
-  __shared__ uint32_t s_tab[kTabLoOff + 256];
+  __shared__ u32x2 s_tab[256];
   __shared__ int64_t s_page_off[kMaxChunkPages];
-  __shared__ __align__(16) uint8_t s_stage[kMaxWaves][3][S::kStage + 16];
+  __shared__ __align__(16) uint8_t s_stage[S::kStage + 16];
 
-  const int tid = threadIdx.x;
-  const int wave = tid >> 6;
-  const int lane = tid & 63;
+  const int lane = threadIdx.x;
   const int r16 = lane & 15;
   const int g4 = lane >> 4;
-  const int b = blockIdx.y;
   const int split = blockIdx.x;
+  const int b = blockIdx.y;
+  const int g = blockIdx.z;                  // kv head
   const int H = a.H;
   const int64_t row_bytes = static_cast<int64_t>(H) * SLOT;
   const int64_t page_bytes = static_cast<int64_t>(1 << a.bs_shift) * row_bytes;
@@ -705,10 +758,9 @@ __global__ void __launch_bounds__(512) decode_staged_kernel(MfmaArgs a) {
   stage_page_offsets(a, b, t0, t1, page_bytes, s_page_off);
   __syncthreads();
 
-  const int g = wave;
-  if (t0 < t1 && g < H) {
+  if (t0 < t1) {
     h8 qhi[4], qlo[4];
-    load_queries(a, b, g, r16, g4, qhi, qlo);
+    load_queries(a, b, g, r16, g4, a.scale_log2, qhi, qlo);
     const uint32_t rb = static_cast<uint32_t>(row_bytes);
     const uint32_t head_off = static_cast<uint32_t>(g * SLOT);
     const uint32_t head_off4 = head_off & ~3u;               // rows start 4-aligned (H even)
@@ -719,38 +771,35 @@ __global__ void __launch_bounds__(512) decode_staged_kernel(MfmaArgs a) {
     st.m_run = -INFINITY;
     st.l_part = 0.0f;
     st.z_part = 0.0f;
-    const bool head_live = r16 < a.G;
     const int p_first = t0 >> a.bs_shift;
-    uint8_t* lds0 = s_stage[wave][0];
-    uint8_t* lds1 = s_stage[wave][1];
-    uint8_t* lds2 = s_stage[wave][2];
+    // One LDS buffer suffices: a wavefront's LDS accesses complete in issue
+    // order, so the next slab's writes never overtake this slab's reads.
+    uint8_t* lds = s_stage;
+    const StageOffsets<SLOT> so = stage_offsets<SLOT>(lane, head_off4, rb);
 
-    // three slabs in flight in registers, each with its own LDS buffer
-    StageRegs<SLOT> r0, r1, r2;
+    // two slabs in flight in registers
+    StageRegs<SLOT> r0, r1;
     auto load = [&](int t, StageRegs<SLOT>& r) {
-      if (t < t1)
-        stage_load<SLOT>(slab_ptr(a, s_page_off, p_first, t, row_bytes), lane, head_off4, rb, r);
-      else
-        r.ok = false;
+      bool ok;
+      const __amdgpu_buffer_rsrc_t rs = slab_rsrc(a, s_page_off, p_first, t, t1, row_bytes, ok);
+      r.ok = ok;
+      stage_load<SLOT>(rs, so, r);
     };
-    auto step = [&](int t, StageRegs<SLOT>& r, uint8_t* lds) {
-      // slab t is in r: park it in LDS, refill r with slab t + 48, compute slab t
+    auto step = [&](int t, StageRegs<SLOT>& r) {
+      // slab t is in r: park it in LDS, refill r with slab t + 32, compute slab t
       const bool ok = r.ok;
-      if (ok) stage_store<SLOT>(lds, lane, r);
-      load(t + 48, r);
+      stage_store<SLOT>(lds, lane, r);
+      load(t + 32, r);
       if (ok)
-        process_slab<KB>(staged_ops<KB, SLOT>(lds, r16, g4, sh), t1 - t, s_tab, qhi, qlo,
-                         head_live, a.scale_log2, g4, st);
+        process_slab<KB>(staged_ops<KB, SLOT>(lds, r16, g4, sh), t1 - t, s_tab, qhi, qlo, g4, st);
     };
     load(t0, r0);
     load(t0 + 16, r1);
-    load(t0 + 32, r2);
-    for (int t = t0; t < t1; t += 48) {
-      step(t, r0, lds0);
-      if (t + 16 >= t1) break;
-      step(t + 16, r1, lds1);
-      if (t + 32 >= t1) break;
-      step(t + 32, r2, lds2);
+    // whole rounds of two steps, no early exit: a step past the split end
+    // only moves a dummy slab, which keeps the load count per step fixed
+    for (int t = t0; t < t1; t += 32) {
+      step(t, r0);
+      step(t + 16, r1);
     }
     store_partials(a, b, g, split, g4, r16, st);
   }
@@ -791,17 +840,20 @@ hipError_t launch_decode_mfma(const Geometry& g, const DevTables* tables, const 
   a.part = static_cast<float*>(workspace);
   a.out = out;
   a.out_fp32 = out_is_fp32;
-  const dim3 grid(plan.num_splits, batch);
-  const dim3 block(64 * g.num_kv_heads);
   const bool staged = (g.num_kv_heads % 2) == 0;
-  if (g.key_bits == 4) {
-    if (staged)
-      hipLaunchKernelGGL((decode_staged_kernel<4, 134>), grid, block, 0, stream, a);
+  if (staged) {
+    // one wavefront per workgroup: (split, sequence, kv head)
+    const dim3 grid(plan.num_splits, batch, g.num_kv_heads);
+    if (g.key_bits == 4)
+      hipLaunchKernelGGL((decode_staged_kernel<4, 134>), grid, dim3(64), 0, stream, a);
     else
-      hipLaunchKernelGGL((decode_direct_kernel<4, 134>), grid, block, 0, stream, a);
+      hipLaunchKernelGGL((decode_staged_kernel<3, 118>), grid, dim3(64), 0, stream, a);
   } else {
-    if (staged)
-      hipLaunchKernelGGL((decode_staged_kernel<3, 118>), grid, block, 0, stream, a);
+    // one wavefront per kv head in a workgroup per (split, sequence)
+    const dim3 grid(plan.num_splits, batch);
+    const dim3 block(64 * g.num_kv_heads);
+    if (g.key_bits == 4)
+      hipLaunchKernelGGL((decode_direct_kernel<4, 134>), grid, block, 0, stream, a);
     else
       hipLaunchKernelGGL((decode_direct_kernel<3, 118>), grid, block, 0, stream, a);
   }

@@ -364,12 +364,13 @@ hipError_t launch_g(const DecodeArgs& a, int G, int batch, hipStream_t stream) {
 DecodePlan plan_decode(const Geometry& g, int batch, int num_q_heads, int max_seq_len) {
   DecodePlan p;
   if (mfma_decode_eligible(g, num_q_heads)) {
-    // about 3072 wavefronts (12 per CU: 256 CUs, 3 per SIMD) over
-    // (split, sequence, kv head), 16-token slabs, at least 8 slabs per split
-    // so the per-wavefront set-up is amortised
+    // one resident round of wavefronts (256 CUs x the kernel's wavefronts per
+    // CU) over (split, sequence, kv head), 16-token slabs, at least 8 slabs
+    // per split so the per-wavefront set-up is amortised
     const int slabs = max_seq_len > 0 ? (max_seq_len + 15) / 16 : 1;
     const int per_split = batch * g.num_kv_heads;
-    int s = per_split > 0 ? (3072 + per_split - 1) / per_split : 1;
+    const int target = 256 * mfma_waves_per_cu(g);
+    int s = per_split > 0 ? (target + per_split - 1) / per_split : 1;
     const int s_max = (slabs + 7) / 8;
     s = s < 1 ? 1 : (s > s_max ? s_max : s);
     p.mfma = 1;

@@ -54,6 +54,8 @@ typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef _Float16 h4 __attribute__((ext_vector_type(4)));
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef float f4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf8v __attribute__((ext_vector_type(8)));
+typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4), aligned(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2), aligned(4)));
 
@@ -217,13 +219,28 @@ __device__ __forceinline__ uint32_t insert_bits(uint32_t x, uint32_t m, uint32_t
   return r;
 }
 
-// One slab: scores, norm correction, online softmax, P.V.  Rows of query
-// heads >= G have q = 0: their scores, weights and O rows are finite and
-// never stored.
+// the G queries of kv head g as bf16 B operands of the FP8-key score MFMA
+// (keys are stored unrotated, so q is used as given); lane (h = r16, g4)
+// holds coordinates [32*g4, 32*g4 + 32) of head h, zero for h >= G
+__device__ __forceinline__ void load_queries_bf16(const MfmaArgs& a, int b, int g, int r16, int g4,
+                                                  bf8v (&qb)[4]) {
+  const bool live = r16 < a.G;
+  const uint16_t* qp = a.q + (static_cast<int64_t>(b) * a.Hq + g * a.G + (live ? r16 : 0)) * kD + 32 * g4;
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    u32x4 w = *reinterpret_cast<const u32x4*>(qp + 8 * kk);
+    if (!live) w = u32x4{0u, 0u, 0u, 0u};
+    qb[kk] = __builtin_bit_cast(bf8v, w);
+  }
+}
+
+// Scores (base 2) of a slab's 4 rows held by this lane (tokens 4*g4 + r,
+// head r16) for 3/4-bit keys: centroid MFMAs plus the norm correction.
+// Rows at or past valid_rows get -inf.
 template <int KB>
-__device__ __forceinline__ void process_slab(const SlabOps<KB>& op, int valid_rows,
-                                             const u32x2* s_tab, const h8 (&qhi)[4],
-                                             const h8 (&qlo)[4], int g4, RunState& st) {
+__device__ __forceinline__ void score_slab(const SlabOps<KB>& op, int valid_rows,
+                                           const u32x2* s_tab, const h8 (&qhi)[4],
+                                           const h8 (&qlo)[4], int g4, float (&s)[4]) {
   // ---- K: codes -> centroid hi / lo operands, score and norm MFMAs ----
   // (the norm accumulator starts at the 1e-16 of the correction's denominator)
   f4 Shi = {0.f, 0.f, 0.f, 0.f}, Slo = {0.f, 0.f, 0.f, 0.f};
@@ -260,27 +277,58 @@ __device__ __forceinline__ void process_slab(const SlabOps<KB>& op, int valid_ro
     Nhi = __builtin_amdgcn_mfma_f32_16x16x32_f16(chi, chi, Nhi, 0, 0, 0);
     Nx = __builtin_amdgcn_mfma_f32_16x16x32_f16(chi, clo, Nx, 0, 0, 0);
   }
-
-  // ---- scores (base 2) of this lane's 4 tokens (rows 4*g4 + r), head r16 ----
   const int diag_src = 20 * g4;            // lane 16*g4 + 4*g4 (+ r) holds N[4*g4+r][4*g4+r]
-  float s[4], pm = -INFINITY;
-  uint32_t szm[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    const bool row_ok = 4 * g4 + r < valid_rows;
     const float nd = Nhi[r] + (2.0f / kLoScale) * Nx[r];
     const float nn = lane_value(nd, diag_src + r);
     const float fac = f16_bits_to_f32(op.n[r]) * __builtin_amdgcn_rsqf(nn);
     const float dot = Shi[r] + Slo[r] * (1.0f / kLoScale);
-    s[r] = row_ok ? dot * fac : -INFINITY;
-    pm = fmaxf(pm, s[r]);
-    szm[r] = row_ok ? op.sz[r] : 0u;       // rows past the end may hold stale bytes
+    s[r] = 4 * g4 + r < valid_rows ? dot * fac : -INFINITY;
   }
+}
+
+// Operand bytes of one slab for one lane, FP8 keys (slots of 196 bytes,
+// 4-byte aligned, no norm).
+struct SlabOps8 {
+  u32x4 k[2];                     // K bytes of token r16, coordinates [32*g4, 32*g4 + 32)
+  uint32_t X[4];                  // V codes of token 4*g4 + r, coordinates [8*r16, 8*r16 + 8)
+  uint32_t sz[4];                 // V scale (low half) and zero (high half) of token 4*g4 + r
+};
+
+// Scores (base 2) for FP8 keys: E4M3 bytes convert exactly to bf16 (two per
+// instruction) and meet the bf16 query in one MFMA per 32 coordinates;
+// products are exact and accumulate in fp32.
+__device__ __forceinline__ void score_slab8(const SlabOps8& op, int valid_rows, const bf8v (&qb)[4],
+                                            float scale_log2, int g4, float (&s)[4]) {
+  f4 S = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    const uint32_t w0 = op.k[kk >> 1][2 * (kk & 1)], w1 = op.k[kk >> 1][2 * (kk & 1) + 1];
+    const bf2 c0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false);
+    const bf2 c1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true);
+    const bf2 c2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false);
+    const bf2 c3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true);
+    const bf8v a = {c0[0], c0[1], c1[0], c1[1], c2[0], c2[1], c3[0], c3[1]};
+    S = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qb[kk], S, 0, 0, 0);
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) s[r] = 4 * g4 + r < valid_rows ? S[r] * scale_log2 : -INFINITY;
+}
+
+// Online softmax and P.V of one slab from its scores (base 2, -inf for masked
+// rows).  Rows of query heads >= G have q = 0: their scores, weights and O
+// rows are finite and never stored.
+__device__ __forceinline__ void softmax_pv(const float (&s)[4], int valid_rows, const uint32_t (&sz)[4],
+                                           const uint32_t (&X)[4], int g4, RunState& st) {
+  float pm = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
   float sc[4], zr[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    sc[r] = f16_bits_to_f32(szm[r] & 0xFFFFu);
-    zr[r] = f16_bits_to_f32(szm[r] >> 16);
+    // rows past the end may hold stale bytes: scale and zero read as 0
+    const uint32_t szm = 4 * g4 + r < valid_rows ? sz[r] : 0u;
+    sc[r] = f16_bits_to_f32(szm & 0xFFFFu);
+    zr[r] = f16_bits_to_f32(szm >> 16);
   }
   // Lazy running maximum: the accumulators are rescaled only when some
   // lane's rows exceed the head's running max by more than kLazy (base 2),
@@ -319,8 +367,8 @@ __device__ __forceinline__ void process_slab(const SlabOps<KB>& op, int valid_ro
   for (int kb = 0; kb < 4; ++kb) {
     // byte kb of each token's dword -> [x0, 0, x1, 0]
     const uint32_t sel = kb | (0x0Cu << 8) | ((4u + kb) << 16) | (0x0Cu << 24);
-    const uint32_t p01 = __builtin_amdgcn_perm(op.X[1], op.X[0], sel);
-    const uint32_t p23 = __builtin_amdgcn_perm(op.X[3], op.X[2], sel);
+    const uint32_t p01 = __builtin_amdgcn_perm(X[1], X[0], sel);
+    const uint32_t p23 = __builtin_amdgcn_perm(X[3], X[2], sel);
     // low nibble -> 1024 + code, high nibble -> 64 + code (exact f16), minus the bias
     h2 lo01 = __builtin_bit_cast(h2, insert_bits(p01, 0x000F000Fu, 0x64006400u));
     h2 lo23 = __builtin_bit_cast(h2, insert_bits(p23, 0x000F000Fu, 0x64006400u));
@@ -335,6 +383,16 @@ __device__ __forceinline__ void process_slab(const SlabOps<KB>& op, int valid_ro
     st.O[2 * kb] = __builtin_amdgcn_mfma_f32_16x16x16f16(W, Blo, st.O[2 * kb], 0, 0, 0);
     st.O[2 * kb + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(W, Bhi, st.O[2 * kb + 1], 0, 0, 0);
   }
+}
+
+// One slab of 3/4-bit keys: scores, norm correction, online softmax, P.V.
+template <int KB>
+__device__ __forceinline__ void process_slab(const SlabOps<KB>& op, int valid_rows,
+                                             const u32x2* s_tab, const h8 (&qhi)[4],
+                                             const h8 (&qlo)[4], int g4, RunState& st) {
+  float s[4];
+  score_slab<KB>(op, valid_rows, s_tab, qhi, qlo, g4, s);
+  softmax_pv(s, valid_rows, op.sz, op.X, g4, st);
 }
 
 // page ids of this split -> byte offsets in LDS (-1: outside the cache)
@@ -631,14 +689,16 @@ __global__ void __launch_bounds__(512) decode_direct_kernel(MfmaArgs a) {
 // ============================================================================
 
 // A wavefront's bytes of one row: from its slot start rounded down to 4 to
-// its slot end rounded up to 4 (136 bytes for 134-byte slots, 120 for 118),
-// fetched as 16-byte chunks plus one 8-byte tail, never past the slot end
-// rounded up to 4 (the last head's slot ends the row, the last row the cache).
+// its slot end rounded up to 4 (136 bytes for 134-byte slots, 120 for 118,
+// 196 for 196), fetched as 16-byte chunks plus one 8- or 4-byte tail, never
+// past the slot end rounded up to 4 (the last head's slot ends the row, the
+// last row the cache).
 template <int SLOT>
 struct StageShape {
-  static constexpr int kSpan = SLOT + 2;               // bytes fetched per row
-  static constexpr int kC16 = (kSpan - 8) / 16;        // 16-byte chunks per row
-  static_assert(16 * kC16 + 8 == kSpan, "row span must be 16-byte chunks plus 8");
+  static constexpr int kSpan = SLOT % 4 == 0 ? SLOT : SLOT + 2;   // bytes fetched per row
+  static constexpr int kTail = kSpan % 16;             // 4 or 8
+  static_assert(kTail == 4 || kTail == 8, "row span must be 16-byte chunks plus 4 or 8");
+  static constexpr int kC16 = (kSpan - kTail) / 16;    // 16-byte chunks per row
   static constexpr int kRow = 16 * (kC16 + 1);         // LDS bytes per row (16-aligned)
   static constexpr int kStage = 16 * kRow;             // LDS bytes per slab
   static constexpr int kChunks = 16 * kC16;            // 16-byte chunks per slab
@@ -648,12 +708,12 @@ struct StageShape {
 template <int SLOT>
 struct StageRegs {
   u32x4 d[StageShape<SLOT>::kLoads16];
-  u32x2 tail;                                          // lanes 0..15: row lane's last 8 bytes
+  u32x2 tail;                                          // lanes 0..15: the row's last 4 or 8 bytes
   bool ok;                                             // a real slab (else a dummy load)
 };
 
 // Per-lane byte offsets (from a slab's first row) of the lane's 16-byte
-// chunks and 8-byte tail; lanes without a chunk of their own re-read the last
+// chunks and its tail; lanes without a chunk of their own re-read the last
 // one and lanes 16..63 re-read a tail, so every lane issues the same loads.
 template <int SLOT>
 struct StageOffsets {
@@ -683,7 +743,10 @@ __device__ __forceinline__ void stage_load(__amdgpu_buffer_rsrc_t rs, const Stag
 #pragma unroll
   for (int j = 0; j < S::kLoads16; ++j)
     sr.d[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, o.d[j], 0, 0));
-  sr.tail = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, o.tail, 0, 0));
+  if constexpr (S::kTail == 8)
+    sr.tail = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, o.tail, 0, 0));
+  else
+    sr.tail[0] = __builtin_amdgcn_raw_buffer_load_b32(rs, o.tail, 0, 0);
 }
 
 template <int SLOT>
@@ -697,7 +760,12 @@ __device__ __forceinline__ void stage_store(uint8_t* lds, int lane, const StageR
       *reinterpret_cast<u32x4*>(lds + row * S::kRow + 16 * cc) = sr.d[j];
     }
   }
-  if (lane < 16) *reinterpret_cast<u32x2*>(lds + lane * S::kRow + 16 * S::kC16) = sr.tail;
+  if (lane < 16) {
+    if constexpr (S::kTail == 8)
+      *reinterpret_cast<u32x2*>(lds + lane * S::kRow + 16 * S::kC16) = sr.tail;
+    else
+      *reinterpret_cast<uint32_t*>(lds + lane * S::kRow + 16 * S::kC16) = sr.tail[0];
+  }
 }
 
 // operands of one lane from the LDS copy of the slab (slot of row t at
@@ -733,8 +801,30 @@ __device__ __forceinline__ SlabOps<KB> staged_ops(const uint8_t* lds, int r16, i
   return op;
 }
 
+// resident wavefronts per SIMD the staged kernel is built for (its register
+// budget: 512 / waves): FP8 keys need the fewest registers, 3-bit keys the most
+template <int KB>
+constexpr int kStagedWavesPerSimd = KB == 8 ? 4 : (KB == 4 ? 3 : 2);
+
+// operands of one lane from the LDS copy of a slab of 196-byte slots (row t
+// at t * kRow, every field 4-byte aligned)
+__device__ __forceinline__ SlabOps8 staged_ops8(const uint8_t* lds, int r16, int g4) {
+  using S = StageShape<196>;
+  SlabOps8 op;
+  const uint8_t* kp = lds + r16 * S::kRow + 32 * g4;
+  op.k[0] = *reinterpret_cast<const u32x4*>(kp);
+  op.k[1] = *reinterpret_cast<const u32x4*>(kp + 16);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const uint8_t* row = lds + (4 * g4 + r) * S::kRow;
+    op.X[r] = *reinterpret_cast<const uint32_t*>(row + kD + 4 * r16);
+    op.sz[r] = *reinterpret_cast<const uint32_t*>(row + kD + kD / 2);
+  }
+  return op;
+}
+
 template <int KB, int SLOT>
-__global__ void __launch_bounds__(64, KB == 4 ? 3 : 2) decode_staged_kernel(MfmaArgs a) {
+__global__ void __launch_bounds__(64, kStagedWavesPerSimd<KB>) decode_staged_kernel(MfmaArgs a) {
   using S = StageShape<SLOT>;
 
   __shared__ u32x2 s_tab[256];
@@ -751,7 +841,7 @@ __global__ void __launch_bounds__(64, KB == 4 ? 3 : 2) decode_staged_kernel(Mfma
   const int64_t row_bytes = static_cast<int64_t>(H) * SLOT;
   const int64_t page_bytes = static_cast<int64_t>(1 << a.bs_shift) * row_bytes;
 
-  build_tables<KB>(a, s_tab);
+  if constexpr (KB != 8) build_tables<KB>(a, s_tab);
   const int T = clamp_len(a, b, split);
   const int t0 = split * a.chunk;
   const int t1 = min(T, t0 + a.chunk);
@@ -760,10 +850,14 @@ __global__ void __launch_bounds__(64, KB == 4 ? 3 : 2) decode_staged_kernel(Mfma
 
   if (t0 < t1) {
     h8 qhi[4], qlo[4];
-    load_queries(a, b, g, r16, g4, a.scale_log2, qhi, qlo);
+    bf8v qb[4];
+    if constexpr (KB == 8)
+      load_queries_bf16(a, b, g, r16, g4, qb);
+    else
+      load_queries(a, b, g, r16, g4, a.scale_log2, qhi, qlo);
     const uint32_t rb = static_cast<uint32_t>(row_bytes);
     const uint32_t head_off = static_cast<uint32_t>(g * SLOT);
-    const uint32_t head_off4 = head_off & ~3u;               // rows start 4-aligned (H even)
+    const uint32_t head_off4 = head_off & ~3u;   // rows start 4-aligned (H even or 196-byte slots)
     const uint32_t sh = head_off & 3u;
     RunState st;
 #pragma unroll
@@ -790,8 +884,16 @@ __global__ void __launch_bounds__(64, KB == 4 ? 3 : 2) decode_staged_kernel(Mfma
       const bool ok = r.ok;
       stage_store<SLOT>(lds, lane, r);
       load(t + 32, r);
-      if (ok)
-        process_slab<KB>(staged_ops<KB, SLOT>(lds, r16, g4, sh), t1 - t, s_tab, qhi, qlo, g4, st);
+      if (ok) {
+        if constexpr (KB == 8) {
+          const SlabOps8 op = staged_ops8(lds, r16, g4);
+          float sc[4];
+          score_slab8(op, t1 - t, qb, a.scale_log2, g4, sc);
+          softmax_pv(sc, t1 - t, op.sz, op.X, g4, st);
+        } else {
+          process_slab<KB>(staged_ops<KB, SLOT>(lds, r16, g4, sh), t1 - t, s_tab, qhi, qlo, g4, st);
+        }
+      }
     };
     load(t0, r0);
     load(t0 + 16, r1);
@@ -807,10 +909,20 @@ __global__ void __launch_bounds__(64, KB == 4 ? 3 : 2) decode_staged_kernel(Mfma
 
 }  // namespace
 
+int mfma_waves_per_cu(const Geometry& g) {
+  const int per_simd = g.key_bits == 8 ? kStagedWavesPerSimd<8>
+                     : (g.key_bits == 4 ? kStagedWavesPerSimd<4> : kStagedWavesPerSimd<3>);
+  return 4 * per_simd;
+}
+
 bool mfma_decode_eligible(const Geometry& g, int num_q_heads) {
   const int G = num_q_heads / g.num_kv_heads;
-  return g.head_dim == kD && (g.key_bits == 4 || g.key_bits == 3) && g.block_size % 16 == 0 &&
-         G >= 1 && G <= 16 && g.num_kv_heads <= 8 && (g.slot == 134 || g.slot == 118);
+  if (g.head_dim != kD || g.block_size % 16 != 0 || G < 1 || G > 16) return false;
+  if (g.key_bits == 8) return g.slot == 196;
+  // odd head counts leave rows 2-byte aligned: the direct kernel, one
+  // workgroup of one wavefront per kv head, takes them (at most 8 heads)
+  return (g.key_bits == 4 || g.key_bits == 3) && (g.slot == 134 || g.slot == 118) &&
+         (g.num_kv_heads % 2 == 0 || g.num_kv_heads <= 8);
 }
 
 size_t mfma_partial_bytes(int batch, int num_q_heads, int num_splits) {
@@ -840,11 +952,13 @@ hipError_t launch_decode_mfma(const Geometry& g, const DevTables* tables, const 
   a.part = static_cast<float*>(workspace);
   a.out = out;
   a.out_fp32 = out_is_fp32;
-  const bool staged = (g.num_kv_heads % 2) == 0;
+  const bool staged = g.key_bits == 8 || (g.num_kv_heads % 2) == 0;
   if (staged) {
     // one wavefront per workgroup: (split, sequence, kv head)
     const dim3 grid(plan.num_splits, batch, g.num_kv_heads);
-    if (g.key_bits == 4)
+    if (g.key_bits == 8)
+      hipLaunchKernelGGL((decode_staged_kernel<8, 196>), grid, dim3(64), 0, stream, a);
+    else if (g.key_bits == 4)
       hipLaunchKernelGGL((decode_staged_kernel<4, 134>), grid, dim3(64), 0, stream, a);
     else
       hipLaunchKernelGGL((decode_staged_kernel<3, 118>), grid, dim3(64), 0, stream, a);

@@ -52,6 +52,7 @@ struct DecodePlan {
 };
 
 bool mfma_decode_eligible(const Geometry& g, int num_q_heads);
+int mfma_waves_per_cu(const Geometry& g);
 size_t mfma_partial_bytes(int batch, int num_q_heads, int num_splits);
 hipError_t launch_decode_mfma(const Geometry& g, const DevTables* tables, const DecodePlan& plan,
                               const uint16_t* q, const uint8_t* cache, int64_t num_blocks,

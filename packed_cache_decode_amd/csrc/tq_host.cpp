@@ -14,6 +14,7 @@
 #include <cstdio>
 #include <cstring>
 #include <new>
+#include <limits>
 #include <vector>
 
 #include "tq_internal.h"
@@ -179,6 +180,102 @@ tq_status host_codebook(int d, int bits, int mode, float* cent, float* mid) {
   return TQ_OK;
 }
 
+// The device's bin arithmetic, replayed on the host (IEEE fmaf and floorf
+// give the device's results): the code of y from the bins of t.
+uint32_t bin_code(const DevTables& t, float y) {
+  const float f = std::floor(std::fmaf(y, t.bin_scale, t.bin_bias));
+  int i = std::isnan(f) ? 0 : (f < 0.0f ? 0 : (f > static_cast<float>(t.bin_count - 1) ? t.bin_count - 1
+                                                                                       : static_cast<int>(f)));
+  float thr;
+  std::memcpy(&thr, &t.bins[i][0], 4);
+  return t.bins[i][1] + (y >= thr ? 1u : 0u);
+}
+
+// Bucketize bins for midpoints mid[0..n_mid-1] (ascending fp32): see
+// DevTables.  Bin j covers [(j + phi) / 2^k, (j + 1 + phi) / 2^k): 2^-k is at
+// most the smallest midpoint gap, and the offset phi keeps every midpoint
+// (the central one is 0) clear of the edges by 4x the fma's rounding error.
+// The table is then checked against the count on every midpoint, its float
+// neighbours and every edge's neighbours.  Returns false if no (k, phi)
+// works within kMaxBins bins.
+bool build_bins(const float* mid, int n_mid, DevTables& t) {
+  double min_gap = 1e30;
+  for (int i = 0; i + 1 < n_mid; ++i) min_gap = std::min(min_gap, static_cast<double>(mid[i + 1]) - mid[i]);
+  if (!(min_gap > 0)) return false;
+  int k0 = 0;
+  while (std::ldexp(1.0, -k0) > min_gap) ++k0;
+  // a bin without a midpoint gets a NaN threshold: y >= NaN is false for
+  // every y, +inf included
+  const float inf = std::numeric_limits<float>::infinity();
+  const float none = std::numeric_limits<float>::quiet_NaN();
+  uint32_t none_bits;
+  std::memcpy(&none_bits, &none, 4);
+  const double phis[] = {0.5, 0.25, 0.75, 0.125, 0.375, 0.625, 0.875};
+  for (int k = k0; k <= k0 + 2; ++k) {
+    for (double phi : phis) {
+      const double w = std::ldexp(1.0, -k);
+      const long jlo = static_cast<long>(std::floor(mid[0] / w - phi)) - 1;
+      const long jhi = static_cast<long>(std::floor(mid[n_mid - 1] / w - phi)) + 1;
+      const long count = jhi - jlo + 2;                // bin 0 + bins jlo .. jhi
+      if (count > tq::kMaxBins) continue;
+      // fma(y, 2^k, bias) below 2^6 in magnitude is off by at most 2^-19
+      const double margin = std::ldexp(1.0, -17 - k);
+      bool clear = true;
+      for (int i = 0; i < n_mid && clear; ++i) {
+        const double e = (std::round(mid[i] / w - phi) + phi) * w;   // nearest edge
+        if (std::fabs(static_cast<double>(mid[i]) - e) <= margin) clear = false;
+      }
+      if (!clear) continue;
+      DevTables c = t;
+      std::memset(c.bins, 0, sizeof(c.bins));
+      c.bins[0][0] = none_bits;
+      c.bins[0][1] = 0;
+      for (long j = jlo; j <= jhi; ++j) {
+        const double e = (j + phi) * w;
+        uint32_t base = 0;
+        float thr = none;
+        for (int i = 0; i < n_mid; ++i) {
+          if (mid[i] <= e) ++base;
+          else if (mid[i] < e + w) thr = mid[i];
+        }
+        std::memcpy(&c.bins[j - jlo + 1][0], &thr, 4);
+        c.bins[j - jlo + 1][1] = base;
+      }
+      c.bin_count = static_cast<int32_t>(count);
+      c.bin_scale = static_cast<float>(std::ldexp(1.0, k));
+      c.bin_bias = static_cast<float>(1 - jlo - phi);
+      // check: midpoints, their neighbours, edges' neighbours, zeros, NaN, +-inf
+      std::vector<float> probe = {0.0f, -0.0f, inf, -inf, std::numeric_limits<float>::quiet_NaN(),
+                                  1e30f, -1e30f};
+      for (int i = 0; i < n_mid; ++i) {
+        probe.push_back(mid[i]);
+        probe.push_back(std::nextafter(mid[i], inf));
+        probe.push_back(std::nextafter(mid[i], -inf));
+      }
+      for (long j = jlo - 1; j <= jhi + 2; ++j) {
+        const float e = static_cast<float>((j + phi) * w);
+        float lo = e, hi = e;
+        for (int r = 0; r < 4; ++r) {
+          probe.push_back(lo);
+          probe.push_back(hi);
+          lo = std::nextafter(lo, -inf);
+          hi = std::nextafter(hi, inf);
+        }
+      }
+      bool ok = true;
+      for (float y : probe) {
+        uint32_t want = 0;
+        for (int i = 0; i < n_mid; ++i) want += y >= mid[i] ? 1u : 0u;
+        if (bin_code(c, y) != want) ok = false;
+      }
+      if (!ok) continue;
+      t = c;
+      return true;
+    }
+  }
+  return false;
+}
+
 int slot_bytes_for(int preset, int d) {
   const int kb = preset == TQ_K8V4 ? 8 : (preset == TQ_4BIT_NC ? 4 : 3);
   const int key = kb == 8 ? d : (d * kb + 7) / 8 + 2;
@@ -272,6 +369,8 @@ tq_status tq_codebook_init(tq_ctx** out, int preset, int head_dim, int num_kv_he
   std::memcpy(host.midpoints, c->midpoints, sizeof(host.midpoints));
   for (int j = 0; j < head_dim; ++j)
     if (c->signs[j] < 0) host.sign_bits[j / 32] |= 1u << (j % 32);
+  g.bins_ok = c->levels && build_bins(c->midpoints, c->levels - 1, host);
+  if (!g.bins_ok) host.bin_count = 0;
 
   if (hipGetDevice(&c->device) != hipSuccess) {
     delete c;

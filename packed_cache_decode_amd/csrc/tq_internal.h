@@ -12,8 +12,21 @@ namespace tq {
 constexpr int kMaxHeadDim = 256;
 constexpr int kMaxLevels = 16;
 
-// Device-resident tables of one context (about 200 bytes, one allocation).
+constexpr int kMaxBins = 64;
+
+// Device-resident tables of one context (under 1 KB, one allocation).
 // Sign flips are a bit mask: bit j of sign_bits[j / 32] set means s_j = -1.
+//
+// Bucketize bins (MSE keys): the count #{m : y >= mid_m} equals
+//   base + (y >= thr)  for  {thr, base} = bins[i],
+//   i = clamp(floor(fma(y, bin_scale, bin_bias)), 0, bin_count - 1),
+// where bin_scale = 2^k makes every bin [(j + phi) / 2^k, (j + 1 + phi) / 2^k) no wider than
+// the smallest midpoint gap (so it holds at most one midpoint, thr, or NaN),
+// base counts the midpoints at or below the bin's lower edge, and bin 0 (base
+// 0, thr NaN) takes everything below the first edge and NaN (whose integer
+// conversion is 0).  The host checks that no midpoint lies within 4x the
+// fma's rounding error of an edge, so a value rounded into the neighbouring
+// bin still gets the same count; bin_count == 0 means no such table exists.
 struct DevTables {
   float centroids[kMaxLevels];
   float midpoints[kMaxLevels];          // 2^b - 1 entries used
@@ -21,7 +34,11 @@ struct DevTables {
   int32_t err_slot;                     // sticky: a store slot beyond the cache
   int32_t err_page;                     // sticky: a page id beyond the cache
   int32_t err_len;                      // sticky: a sequence length beyond the grid/table
-  int32_t pad[5];
+  int32_t bin_count;
+  float bin_scale;
+  float bin_bias;
+  int32_t pad[2];
+  uint32_t bins[kMaxBins][2];           // {float bits of thr, base}
 };
 
 struct Geometry {
@@ -35,6 +52,7 @@ struct Geometry {
   int key_packed;       // key_code_bytes (+2 for the norm unless fp8)
   int value_code_bytes; // ceil(d*vb/8)
   int slot;             // aligned slot bytes
+  int bins_ok;          // the bucketize bins of the device tables exist
 };
 
 // ---- launchers (defined in the .hip files) ---------------------------------

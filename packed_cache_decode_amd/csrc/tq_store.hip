@@ -249,6 +249,271 @@ __global__ void __launch_bounds__(64 * kWaves) store_kernel(StoreArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// head_dim 128: four lanes per vector, 32 contiguous coordinates per lane, 16
+// vectors per wavefront.  The same fp32 contract as above, reorganised so that
+// five of the seven butterfly stages and five of the seven levels of the norm
+// tree stay inside a lane and the other two are DPP quad exchanges; the code
+// of a coordinate comes from the bucketize bins (one compare) instead of a
+// compare per midpoint; codes, V nibbles and FP8 bytes are packed in
+// registers and written as 2-byte stores (134/118-byte slots are 2-byte
+// aligned) or 4-byte stores (196-byte slots).
+// ---------------------------------------------------------------------------
+
+typedef uint32_t u32x4s __attribute__((ext_vector_type(4)));
+
+// value of the partner lane in the quad (lane ^ 1 or lane ^ 2)
+template <int X>
+__device__ __forceinline__ float quad_xor(float v) {
+  constexpr int ctrl = X == 1 ? 0xB1 : 0x4E;          // quad_perm [1,0,3,2] / [2,3,0,1]
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), ctrl, 0xF, 0xF, false));
+}
+
+// butterfly across the quad: the lower lane of the pair keeps a + b, the
+// upper lane a - b, computed as a + (-b) (the same IEEE operation)
+template <int X>
+__device__ __forceinline__ float butterfly_x(float u, uint32_t upper_sign) {
+  const float o = quad_xor<X>(u);
+  return o + __uint_as_float(__float_as_uint(u) ^ upper_sign);
+}
+
+__device__ __forceinline__ void store_u16s(uint8_t* dst, const uint32_t* w, int n16) {
+  uint16_t* d = reinterpret_cast<uint16_t*>(dst);
+#pragma unroll
+  for (int i = 0; i < n16; ++i) d[i] = static_cast<uint16_t>(w[i >> 1] >> (16 * (i & 1)));
+}
+
+template <int KB>
+__global__ void __launch_bounds__(256) store128_kernel(StoreArgs a) {
+  constexpr int D = 128, E = 32;
+  constexpr bool kFp8 = KB == 8;
+  constexpr int kKeyCodeBytes = kFp8 ? D : (D * KB) / 8;
+  constexpr int kKeyPacked = kFp8 ? D : kKeyCodeBytes + 2;
+  constexpr int kValCodeBytes = D / 2;
+  constexpr int kSlot = kKeyPacked + kValCodeBytes + 4;    // 196 / 134 / 118, even
+  static_assert(kSlot % 2 == 0, "slot must be even");
+
+  __shared__ uint32_t s_bins[kMaxBins][2];
+  if constexpr (!kFp8) {
+    for (int i = threadIdx.x; i < kMaxBins; i += blockDim.x) {
+      s_bins[i][0] = a.tables->bins[i][0];
+      s_bins[i][1] = a.tables->bins[i][1];
+    }
+    __syncthreads();
+  }
+  const int lane = threadIdx.x & 63;
+  const int qd = lane & 3;                    // quarter of the vector
+  const int vsub = lane >> 2;                 // vector of the wavefront
+  const uint32_t up1 = (qd & 1) ? 0x80000000u : 0u;
+  const uint32_t up2 = (qd & 2) ? 0x80000000u : 0u;
+  const int nbins = a.tables->bin_count;
+  const float bscale = a.tables->bin_scale, bbias = a.tables->bin_bias;
+  // sign flips of coordinates 32*qd + [0, 32) as per-dword masks on the bf16
+  // pairs (bit 15: even coordinate, bit 31: odd)
+  uint32_t smask[16];
+  {
+    const uint32_t sb = a.tables->sign_bits[qd];
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      smask[i] = (((sb >> (2 * i)) & 1u) << 15) | (((sb >> (2 * i + 1)) & 1u) << 31);
+  }
+
+  const int H = a.H;
+  const uint32_t total = static_cast<uint32_t>(a.num_tokens) * static_cast<uint32_t>(H);
+  const uint32_t wave_id = blockIdx.x * 4 + (threadIdx.x >> 6);
+  for (uint32_t base = wave_id * 16; base < total; base += gridDim.x * 64) {
+    const uint32_t vec = base + vsub;
+    const bool live = vec < total;
+    const uint32_t vv = live ? vec : base;    // a vector inside the batch
+    const uint32_t n = vv / static_cast<uint32_t>(H);
+    const int h = static_cast<int>(vv - n * static_cast<uint32_t>(H));
+    const int64_t slot = a.slot_mapping[n];
+    const bool in_range = slot < a.num_slots;
+    if (live && slot >= 0 && !in_range && qd == 0) const_cast<DevTables*>(a.tables)->err_slot = 1;
+    const bool do_store = live && slot >= 0 && in_range;
+    const int64_t src = static_cast<int64_t>(n) * a.stride + static_cast<int64_t>(h) * D + E * qd;
+
+    // ---------------- K ----------------
+    const u32x4s* kp = reinterpret_cast<const u32x4s*>(a.k + src);
+    uint32_t kw[16];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const u32x4s t = kp[i];
+      kw[4 * i] = t[0];
+      kw[4 * i + 1] = t[1];
+      kw[4 * i + 2] = t[2];
+      kw[4 * i + 3] = t[3];
+    }
+    uint32_t kout[kFp8 ? 8 : (KB == 4 ? 4 : 3)];
+    uint32_t norm_bits = 0;
+    if constexpr (kFp8) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        uint32_t w = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t bw = kw[2 * i + (j >> 1)];
+          const float x = (j & 1) ? __uint_as_float(bw & 0xFFFF0000u) : __uint_as_float(bw << 16);
+          w |= f32_to_e4m3fn(x) << (8 * j);
+        }
+        kout[i] = w;
+      }
+    } else {
+      float x[E];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        x[2 * i] = __uint_as_float(kw[i] << 16);
+        x[2 * i + 1] = __uint_as_float(kw[i] & 0xFFFF0000u);
+      }
+      // sum of squares: the balanced tree in index order, 5 levels in the lane
+      float sq[E];
+#pragma unroll
+      for (int e = 0; e < E; ++e) sq[e] = x[e] * x[e];
+#pragma unroll
+      for (int w = 1; w < E; w *= 2)
+#pragma unroll
+        for (int e = 0; e < E; e += 2 * w) sq[e] = sq[e] + sq[e + w];
+      float ss = sq[0];
+      ss = ss + quad_xor<1>(ss);
+      ss = ss + quad_xor<2>(ss);
+      const float nrm = sqrtf(ss);
+      const float alpha = (1.0f / (nrm + 1e-8f)) * a.r_d;
+      norm_bits = f32_to_f16_bits(nrm);
+
+      // sign flips on the bf16 pairs (exact), then butterflies h = 1 .. 64
+      float u[E];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const uint32_t w = kw[i] ^ smask[i];
+        u[2 * i] = __uint_as_float(w << 16);
+        u[2 * i + 1] = __uint_as_float(w & 0xFFFF0000u);
+      }
+#pragma unroll
+      for (int hs = 1; hs < E; hs *= 2)
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+          if ((e & hs) == 0) {
+            const float p = u[e], q = u[e + hs];
+            u[e] = p + q;
+            u[e + hs] = p - q;
+          }
+#pragma unroll
+      for (int e = 0; e < E; ++e) u[e] = butterfly_x<1>(u[e], up1);
+#pragma unroll
+      for (int e = 0; e < E; ++e) u[e] = butterfly_x<2>(u[e], up2);
+      // codes: y = u * alpha, code = base + (y >= thr) of y's bin
+      uint32_t code[E];
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const float y = u[e] * alpha;
+        const float t = __builtin_fmaf(y, bscale, bbias);
+        int bi = static_cast<int>(floorf(t));
+        bi = bi < 0 ? 0 : (bi > nbins - 1 ? nbins - 1 : bi);
+        const uint32_t thr = s_bins[bi][0], cb = s_bins[bi][1];
+        code[e] = cb + (y >= __uint_as_float(thr) ? 1u : 0u);
+      }
+      if constexpr (KB == 4) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          uint32_t w = 0;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) w |= code[8 * i + j] << (4 * j);
+          kout[i] = w;
+        }
+      } else {
+        // 96-bit LSB-first stream: code e at bits [3e, 3e + 3)
+        uint64_t lo = 0, hi = 0;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const int b = 3 * e;
+          if (b + 3 <= 64) lo |= static_cast<uint64_t>(code[e]) << b;
+          else if (b >= 64) hi |= static_cast<uint64_t>(code[e]) << (b - 64);
+          else {
+            lo |= static_cast<uint64_t>(code[e]) << b;
+            hi |= static_cast<uint64_t>(code[e]) >> (64 - b);
+          }
+        }
+        kout[0] = static_cast<uint32_t>(lo);
+        kout[1] = static_cast<uint32_t>(lo >> 32);
+        kout[2] = static_cast<uint32_t>(hi);
+      }
+    }
+
+    // ---------------- V ----------------
+    const u32x4s* vp = reinterpret_cast<const u32x4s*>(a.v + src);
+    float vv_[E];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const u32x4s t = vp[i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        vv_[8 * i + 2 * j] = __uint_as_float(t[j] << 16);
+        vv_[8 * i + 2 * j + 1] = __uint_as_float(t[j] & 0xFFFF0000u);
+      }
+    }
+    float lo = vv_[0], hi = vv_[0];
+#pragma unroll
+    for (int e = 1; e < E; ++e) {
+      lo = fminf(lo, vv_[e]);
+      hi = fmaxf(hi, vv_[e]);
+    }
+    lo = fminf(lo, quad_xor<1>(lo));
+    hi = fmaxf(hi, quad_xor<1>(hi));
+    lo = fminf(lo, quad_xor<2>(lo));
+    hi = fmaxf(hi, quad_xor<2>(hi));
+    float sc = (hi - lo) / 15.0f;
+    if (!(sc > 1e-8f)) sc = 1e-8f;
+    const float isc = 1.0f / sc;
+    uint32_t vout[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint32_t w = 0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float t = (vv_[8 * i + j] - lo) * isc + 0.5f;
+        int qi = static_cast<int>(truncf(t));
+        qi = qi < 0 ? 0 : (qi > 15 ? 15 : qi);
+        w |= static_cast<uint32_t>(qi) << (4 * j);
+      }
+      vout[i] = w;
+    }
+
+    // ---------------- slot ----------------
+    if (do_store) {
+      const int64_t page = slot >> a.bs_shift;
+      const int64_t row = slot - (page << a.bs_shift);
+      uint8_t* dst = a.cache + ((page << a.bs_shift) + row) * (static_cast<int64_t>(H) * kSlot) +
+                     static_cast<int64_t>(h) * kSlot;
+      if constexpr (kFp8) {
+        uint32_t* d32 = reinterpret_cast<uint32_t*>(dst);      // 196-byte slots: 4-byte aligned
+#pragma unroll
+        for (int i = 0; i < 8; ++i) d32[8 * qd + i] = kout[i];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) d32[(kKeyPacked >> 2) + 4 * qd + i] = vout[i];
+      } else {
+        store_u16s(dst + (kKeyCodeBytes / 4) * qd, kout, kKeyCodeBytes / 8);
+        if (qd == 0) *reinterpret_cast<uint16_t*>(dst + kKeyCodeBytes) = static_cast<uint16_t>(norm_bits);
+        store_u16s(dst + kKeyPacked + 16 * qd, vout, 8);
+      }
+      if (qd == 3) {
+        uint16_t* m = reinterpret_cast<uint16_t*>(dst + kKeyPacked + kValCodeBytes);
+        m[0] = f32_to_f16_bits(sc);
+        m[1] = f32_to_f16_bits(lo);
+      }
+    }
+  }
+}
+
+template <int KB>
+hipError_t launch_store128(const StoreArgs& a, hipStream_t stream) {
+  const int64_t total = a.num_tokens * a.H;
+  int64_t blocks = (total + 63) / 64;               // 64 vectors per 256-thread block
+  if (blocks > 8192) blocks = 8192;
+  hipLaunchKernelGGL((store128_kernel<KB>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0,
+                     stream, a);
+  return hipGetLastError();
+}
+
 template <int D, int KB>
 hipError_t launch_store_t(const StoreArgs& a, hipStream_t stream) {
   const int64_t total = a.num_tokens * a.H;
@@ -277,6 +542,15 @@ hipError_t launch_store(const Geometry& g, const DevTables* tables, const uint16
   a.r_d = r_d;
   a.H = g.num_kv_heads;
   a.bs_shift = __builtin_ctz(static_cast<unsigned>(g.block_size));
+  // head_dim 128 takes the four-lanes-per-vector kernel when the bucketize
+  // bins exist (always, for the Lloyd-Max codebooks) and the vector count fits
+  // 32-bit indexing
+  if (g.head_dim == 128 && num_tokens * g.num_kv_heads < (int64_t{1} << 31) &&
+      (g.key_bits == 8 || g.bins_ok)) {
+    if (g.key_bits == 8) return launch_store128<8>(a, stream);
+    if (g.key_bits == 4) return launch_store128<4>(a, stream);
+    return launch_store128<3>(a, stream);
+  }
 #define TQ_STORE_CASE(D_, KB_) \
   if (g.head_dim == D_ && g.key_bits == KB_) return launch_store_t<D_, KB_>(a, stream);
   TQ_STORE_CASE(64, 3) TQ_STORE_CASE(64, 4) TQ_STORE_CASE(64, 8)

@@ -164,6 +164,29 @@ def main():
         if evs:
             evs[3].record()
 
+    # plain streaming probes of the same session: the read used as the cache
+    # flush (1 GiB) and a device copy (256 MiB read + 256 MiB written)
+    def probe(fn, reps=5):
+        fn()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(reps)]
+        for e0, e1 in ev:
+            e0.record()
+            fn()
+            e1.record()
+        torch.cuda.synchronize()
+        return float(np.median([e0.elapsed_time(e1) for e0, e1 in ev])) * 1e-3
+
+    copy_src = torch.ones(1 << 26, dtype=torch.int32, device=dev)
+    copy_dst = torch.empty_like(copy_src)
+    t_read = probe(lambda: torch.amax(flush, dim=0, out=sink))
+    t_copy = probe(lambda: copy_dst.copy_(copy_src))
+    hbm_probe = {"read_gbs": round(flush.numel() * 4 / t_read / 1e9, 1),
+                 "copy_gbs": round(2 * copy_src.numel() * 4 / t_copy / 1e9, 1),
+                 "note": "torch amax over 1 GiB; torch copy of 256 MiB (read + write bytes)"}
+    del copy_src, copy_dst
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -217,6 +240,7 @@ def main():
                            "traffic": None, "kernel": "tq_store",
                            "alg_bytes_per_launch": st_bytes},
         "wall_ms_per_step_incl_flush": round(wall / args.steps * 1e3, 3),
+        "hbm_probe": hbm_probe,
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)

@@ -266,7 +266,25 @@ typedef uint32_t u32x4s __attribute__((ext_vector_type(4)));
 template <int X>
 __device__ __forceinline__ float quad_xor(float v) {
   constexpr int ctrl = X == 1 ? 0xB1 : 0x4E;          // quad_perm [1,0,3,2] / [2,3,0,1]
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), ctrl, 0xF, 0xF, false));
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), ctrl, 0xF, 0xF, true));
+}
+
+// floor(t) as int32, NaN -> 0 (v_cvt_flr_i32_f32), clamped to [0, hi]
+__device__ __forceinline__ int floor_clamp(float t, int hi) {
+  int i;
+  asm("v_cvt_flr_i32_f32 %0, %1" : "=v"(i) : "v"(t));
+  int r;
+  asm("v_med3_i32 %0, %1, 0, %2" : "=v"(r) : "v"(i), "v"(hi));
+  return r;
+}
+
+// trunc(t) as int32 (t >= 0 here), clamped to [0, 15]
+__device__ __forceinline__ uint32_t trunc_clamp15(float t) {
+  int i;
+  asm("v_cvt_i32_f32 %0, %1" : "=v"(i) : "v"(t));
+  int r;
+  asm("v_med3_i32 %0, %1, 0, 15" : "=v"(r) : "v"(i));
+  return static_cast<uint32_t>(r);
 }
 
 // butterfly across the quad: the lower lane of the pair keeps a + b, the
@@ -283,7 +301,11 @@ __device__ __forceinline__ void store_u16s(uint8_t* dst, const uint32_t* w, int 
   for (int i = 0; i < n16; ++i) d[i] = static_cast<uint16_t>(w[i >> 1] >> (16 * (i & 1)));
 }
 
-template <int KB>
+// kRows: H divides 16 and a cache row (H slots) is a multiple of 16 bytes, so
+// a wavefront's 16 vectors are 16 / H whole tokens; their rows are assembled
+// in LDS and written with 16-byte stores.  Otherwise each lane writes its
+// fields with 2- or 4-byte stores.
+template <int KB, bool kRows>
 __global__ void __launch_bounds__(256) store128_kernel(StoreArgs a) {
   constexpr int D = 128, E = 32;
   constexpr bool kFp8 = KB == 8;
@@ -294,6 +316,7 @@ __global__ void __launch_bounds__(256) store128_kernel(StoreArgs a) {
   static_assert(kSlot % 2 == 0, "slot must be even");
 
   __shared__ uint32_t s_bins[kMaxBins][2];
+  __shared__ __align__(16) uint8_t s_rows[kRows ? 4 : 1][kRows ? 16 * kSlot : 16];
   if constexpr (!kFp8) {
     for (int i = threadIdx.x; i < kMaxBins; i += blockDim.x) {
       s_bins[i][0] = a.tables->bins[i][0];
@@ -321,28 +344,51 @@ __global__ void __launch_bounds__(256) store128_kernel(StoreArgs a) {
   const int H = a.H;
   const uint32_t total = static_cast<uint32_t>(a.num_tokens) * static_cast<uint32_t>(H);
   const uint32_t wave_id = blockIdx.x * 4 + (threadIdx.x >> 6);
-  for (uint32_t base = wave_id * 16; base < total; base += gridDim.x * 64) {
-    const uint32_t vec = base + vsub;
-    const bool live = vec < total;
-    const uint32_t vv = live ? vec : base;    // a vector inside the batch
-    const uint32_t n = vv / static_cast<uint32_t>(H);
-    const int h = static_cast<int>(vv - n * static_cast<uint32_t>(H));
-    const int64_t slot = a.slot_mapping[n];
+  const uint32_t stride = gridDim.x * 64;
+
+  // 16 vectors' K, V and slot ids; a lane past the end of the batch fetches
+  // the group's first vector (its results are dropped)
+  struct Fetch {
+    u32x4s k[4], v[4];
+    int64_t slot;
+    uint32_t n;
+    int h;
+  };
+  auto fetch = [&](uint32_t b) {
+    Fetch f;
+    const uint32_t vec = b + vsub;
+    const uint32_t vv = vec < total ? vec : (b < total ? b : 0u);   // a vector inside the batch
+    f.n = vv / static_cast<uint32_t>(H);
+    f.h = static_cast<int>(vv - f.n * static_cast<uint32_t>(H));
+    f.slot = a.slot_mapping[f.n];
+    const int64_t src = static_cast<int64_t>(f.n) * a.stride + static_cast<int64_t>(f.h) * D + E * qd;
+    const u32x4s* kp = reinterpret_cast<const u32x4s*>(a.k + src);
+    const u32x4s* vp = reinterpret_cast<const u32x4s*>(a.v + src);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) f.k[i] = kp[i];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) f.v[i] = vp[i];
+    return f;
+  };
+
+  auto process = [&](const Fetch& f, uint32_t base) {
+    const bool live = base + vsub < total;
+    const uint32_t n = f.n;
+    const int h = f.h;
+    const int64_t slot = f.slot;
     const bool in_range = slot < a.num_slots;
     if (live && slot >= 0 && !in_range && qd == 0) const_cast<DevTables*>(a.tables)->err_slot = 1;
     const bool do_store = live && slot >= 0 && in_range;
-    const int64_t src = static_cast<int64_t>(n) * a.stride + static_cast<int64_t>(h) * D + E * qd;
+    (void)n;
 
     // ---------------- K ----------------
-    const u32x4s* kp = reinterpret_cast<const u32x4s*>(a.k + src);
     uint32_t kw[16];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const u32x4s t = kp[i];
-      kw[4 * i] = t[0];
-      kw[4 * i + 1] = t[1];
-      kw[4 * i + 2] = t[2];
-      kw[4 * i + 3] = t[3];
+      kw[4 * i] = f.k[i][0];
+      kw[4 * i + 1] = f.k[i][1];
+      kw[4 * i + 2] = f.k[i][2];
+      kw[4 * i + 3] = f.k[i][3];
     }
     uint32_t kout[kFp8 ? 8 : (KB == 4 ? 4 : 3)];
     uint32_t norm_bits = 0;
@@ -359,16 +405,19 @@ __global__ void __launch_bounds__(256) store128_kernel(StoreArgs a) {
         kout[i] = w;
       }
     } else {
-      float x[E];
+      // sign flips on the bf16 pairs (exact)
+      float u[E];
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        x[2 * i] = __uint_as_float(kw[i] << 16);
-        x[2 * i + 1] = __uint_as_float(kw[i] & 0xFFFF0000u);
+        const uint32_t w = kw[i] ^ smask[i];
+        u[2 * i] = __uint_as_float(w << 16);
+        u[2 * i + 1] = __uint_as_float(w & 0xFFFF0000u);
       }
-      // sum of squares: the balanced tree in index order, 5 levels in the lane
+      // sum of squares (a flipped sign squares to the same value): the
+      // balanced tree in index order, 5 levels in the lane
       float sq[E];
 #pragma unroll
-      for (int e = 0; e < E; ++e) sq[e] = x[e] * x[e];
+      for (int e = 0; e < E; ++e) sq[e] = u[e] * u[e];
 #pragma unroll
       for (int w = 1; w < E; w *= 2)
 #pragma unroll
@@ -380,14 +429,7 @@ __global__ void __launch_bounds__(256) store128_kernel(StoreArgs a) {
       const float alpha = (1.0f / (nrm + 1e-8f)) * a.r_d;
       norm_bits = f32_to_f16_bits(nrm);
 
-      // sign flips on the bf16 pairs (exact), then butterflies h = 1 .. 64
-      float u[E];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const uint32_t w = kw[i] ^ smask[i];
-        u[2 * i] = __uint_as_float(w << 16);
-        u[2 * i + 1] = __uint_as_float(w & 0xFFFF0000u);
-      }
+      // butterflies h = 1 .. 64
 #pragma unroll
       for (int hs = 1; hs < E; hs *= 2)
 #pragma unroll
@@ -406,9 +448,7 @@ __global__ void __launch_bounds__(256) store128_kernel(StoreArgs a) {
 #pragma unroll
       for (int e = 0; e < E; ++e) {
         const float y = u[e] * alpha;
-        const float t = __builtin_fmaf(y, bscale, bbias);
-        int bi = static_cast<int>(floorf(t));
-        bi = bi < 0 ? 0 : (bi > nbins - 1 ? nbins - 1 : bi);
+        const int bi = floor_clamp(__builtin_fmaf(y, bscale, bbias), nbins - 1);
         const uint32_t thr = s_bins[bi][0], cb = s_bins[bi][1];
         code[e] = cb + (y >= __uint_as_float(thr) ? 1u : 0u);
       }
@@ -440,11 +480,10 @@ __global__ void __launch_bounds__(256) store128_kernel(StoreArgs a) {
     }
 
     // ---------------- V ----------------
-    const u32x4s* vp = reinterpret_cast<const u32x4s*>(a.v + src);
     float vv_[E];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const u32x4s t = vp[i];
+      const u32x4s t = f.v[i];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         vv_[8 * i + 2 * j] = __uint_as_float(t[j] << 16);
@@ -470,16 +509,60 @@ __global__ void __launch_bounds__(256) store128_kernel(StoreArgs a) {
       uint32_t w = 0;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const float t = (vv_[8 * i + j] - lo) * isc + 0.5f;
-        int qi = static_cast<int>(truncf(t));
-        qi = qi < 0 ? 0 : (qi > 15 ? 15 : qi);
-        w |= static_cast<uint32_t>(qi) << (4 * j);
+        w |= trunc_clamp15((vv_[8 * i + j] - lo) * isc + 0.5f) << (4 * j);
       }
       vout[i] = w;
     }
 
     // ---------------- slot ----------------
-    if (do_store) {
+    if constexpr (kRows) {
+      // the 16 vectors' slots, back to back, are 16 / H whole cache rows
+      uint8_t* rows = s_rows[threadIdx.x >> 6];
+      uint8_t* sp = rows + vsub * kSlot;
+      if constexpr (kFp8) {
+        uint32_t* d32 = reinterpret_cast<uint32_t*>(sp);        // 196-byte slots: 4-byte aligned
+#pragma unroll
+        for (int i = 0; i < 8; ++i) d32[8 * qd + i] = kout[i];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) d32[(kKeyPacked >> 2) + 4 * qd + i] = vout[i];
+      } else {
+        store_u16s(sp + (kKeyCodeBytes / 4) * qd, kout, kKeyCodeBytes / 8);
+        if (qd == 0) *reinterpret_cast<uint16_t*>(sp + kKeyCodeBytes) = static_cast<uint16_t>(norm_bits);
+        store_u16s(sp + kKeyPacked + 16 * qd, vout, 8);
+      }
+      if (qd == 3) {
+        uint16_t* m = reinterpret_cast<uint16_t*>(sp + kKeyPacked + kValCodeBytes);
+        m[0] = f32_to_f16_bits(sc);
+        m[1] = f32_to_f16_bits(lo);
+      }
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      const int row_chunks = H * kSlot / 16;
+      const uint32_t tok0 = base / static_cast<uint32_t>(H);
+      // a token's slot sits in the lanes of its vectors (lane 4 * H * tt for
+      // token tok0 + tt): taken from there, no reload from memory
+      const uint32_t slot_lo = static_cast<uint32_t>(slot);
+      const uint32_t slot_hi = static_cast<uint32_t>(static_cast<uint64_t>(slot) >> 32);
+#pragma unroll
+      for (int r = 0; r < (kSlot + 63) / 64; ++r) {   // kSlot chunks of 16 bytes
+        const int c = lane + 64 * r;
+        const int tt = (c < kSlot ? c : 0) / row_chunks;
+        const int src_lane = 4 * H * tt;
+        const uint32_t lo = __builtin_amdgcn_ds_bpermute(src_lane << 2, static_cast<int>(slot_lo));
+        const uint32_t hi = __builtin_amdgcn_ds_bpermute(src_lane << 2, static_cast<int>(slot_hi));
+        const int64_t ts = static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
+        const uint32_t tok = tok0 + tt;
+        if (c < kSlot && tok < static_cast<uint32_t>(a.num_tokens)) {
+          if (ts >= 0 && ts < a.num_slots) {
+            const u32x4s d = *reinterpret_cast<const u32x4s*>(rows + 16 * c);
+            *reinterpret_cast<u32x4s*>(a.cache + ts * (static_cast<int64_t>(H) * kSlot) +
+                                       16 * (c - tt * row_chunks)) = d;
+          }
+        }
+      }
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    } else if (do_store) {
       const int64_t page = slot >> a.bs_shift;
       const int64_t row = slot - (page << a.bs_shift);
       uint8_t* dst = a.cache + ((page << a.bs_shift) + row) * (static_cast<int64_t>(H) * kSlot) +
@@ -501,16 +584,24 @@ __global__ void __launch_bounds__(256) store128_kernel(StoreArgs a) {
         m[1] = f32_to_f16_bits(lo);
       }
     }
-  }
+  };
+
+  for (uint32_t base = wave_id * 16; base < total; base += stride) process(fetch(base), base);
 }
 
 template <int KB>
 hipError_t launch_store128(const StoreArgs& a, hipStream_t stream) {
+  constexpr int kSlot = KB == 8 ? 196 : (KB == 4 ? 134 : 118);
   const int64_t total = a.num_tokens * a.H;
   int64_t blocks = (total + 63) / 64;               // 64 vectors per 256-thread block
   if (blocks > 8192) blocks = 8192;
-  hipLaunchKernelGGL((store128_kernel<KB>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0,
-                     stream, a);
+  const bool rows = 16 % a.H == 0 && (static_cast<int64_t>(a.H) * kSlot) % 16 == 0;
+  if (rows)
+    hipLaunchKernelGGL((store128_kernel<KB, true>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0,
+                       stream, a);
+  else
+    hipLaunchKernelGGL((store128_kernel<KB, false>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0,
+                       stream, a);
   return hipGetLastError();
 }
 

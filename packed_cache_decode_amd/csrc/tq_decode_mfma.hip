@@ -1,27 +1,29 @@
 // tq_decode on gfx950 matrix cores: split-KV paged decode attention over
-// packed slots for head_dim 128, 4- or 3-bit Lloyd-Max keys, block sizes
-// that are multiples of 16 and up to 16 query heads per kv head.
+// packed slots for head_dim 128 (4- or 3-bit Lloyd-Max keys, or FP8 E4M3
+// keys), block sizes that are multiples of 16 and up to 16 query heads per
+// kv head.
 //
 // What is computed is the same as in the general kernel (tq_decode.hip),
 // following P1 ("vLLM 源码完全拆解(十九):TurboQuant KV Cache 量化"),
 // sections "分数计算" (q_rot . centroid, stored norm, norm correction
-// 1/sqrt(sum c^2 + 1e-16)), "V 的解包" (code * scale + zero), "在线 softmax"
-// and "读取内核" (split partials, log-sum-exp merge).
+// 1/sqrt(sum c^2 + 1e-16)), "FP8 K" (q . k, keys unrotated), "V 的解包"
+// (code * scale + zero), "在线 softmax" and "读取内核" (split partials,
+// log-sum-exp merge).
 //
-// Mapping.  A workgroup is one (split, sequence) with one wavefront per kv
-// head, so every byte of a page is read by one CU.  A wavefront walks the
-// split 16 tokens at a time (a slab: 16 rows of a page) with three MFMA
-// contractions:
-//   scores  S[t][h] = sum_c C[t][c] Q[h][c]     v_mfma_f32_16x16x32_f16
-//   norms   N[t][t] = sum_c C[t][c] C[t][c]     (diagonal of C C^T)
+// Mapping.  A workgroup is one wavefront for one (split, sequence, kv head).
+// It walks the split 16 tokens at a time (a slab: 16 rows of a page) with
+// MFMA contractions:
+//   scores  S[t][h] = sum_c C[t][c] Q[h][c]     v_mfma_f32_16x16x32_f16 / _bf16
+//   norms   N[t][t] = sum_c C[t][c] C[t][c]     (diagonal of C C^T, MSE keys)
 //   values  O[h][c] += sum_t W[h][t] V[t][c]    v_mfma_f32_16x16x16_f16
-// C are the centroids of the slab's K codes, looked up per code byte (two
-// codes) in LDS tables; Q the rotated queries (rows >= G are zero); W = p *
-// scale and V the integer V codes, exact in f16.  f16 alone is not precise
-// enough for the scores (outlier keys make them large), so C and Q are
-// carried as f16 hi + lo pairs (lo scaled by 2^11 to stay normal): the
-// score uses Chi.Qhi + Chi.Qlo + 2^-11 Clo.Qhi and the norm Chi.Chi +
-// 2^-10 Chi.Clo.  The per-token term zero * p and the softmax sums stay in
+// For MSE keys C are the centroids of the slab's K codes, looked up per code
+// byte (two codes) in an LDS table; f16 alone is not precise enough for the
+// scores (outlier keys make them large), so C and Q are carried as f16 hi +
+// lo pairs (lo scaled by 2^11 to stay normal): the score uses Chi.Qhi +
+// Chi.Qlo + 2^-11 Clo.Qhi and the norm Chi.Chi + 2^-10 Chi.Clo.  FP8 keys
+// convert exactly to bf16 and meet the bf16 query directly.  Q holds the
+// (rotated) queries, rows >= G zero; W = p * scale and V the integer V codes,
+// exact in f16.  The per-token term zero * p and the softmax sums stay in
 // fp32.  The running maximum is lazy: the accumulators are rescaled only
 // when a head's maximum grows by more than kLazy (base 2), so p <= 2^kLazy.
 //
@@ -33,18 +35,15 @@
 // kk in group g4 covers coordinates 32*g4 + 8*kk + [0, 8); value tile m,
 // column j covers coordinate 8*j + m.
 //
-// Two ways to fetch a slab:
-//   staged  (even head counts): the wavefront loads its head's bytes of the
-//           16 rows with 16-byte loads (3 per lane), three slabs ahead, and
-//           parks them in a private LDS region from which each lane reads
-//           its operands; no barriers, the wavefronts run independently.
-//   direct  (any head count): each lane loads its operand bytes straight
-//           from memory, one slab ahead.
-// Slots of 134 / 118 bytes are only 2-byte aligned, so fields are read as
-// aligned dwords and re-aligned with a funnel shift.  A second small kernel
-// merges the splits (a fused last-workgroup merge needs a device-scope
-// release in every workgroup, which on this part costs far more than a
-// launch).
+// Loads.  Each lane fetches exactly its operand bytes with buffer loads
+// (K bytes of one token; V codes, norm, scale and zero of four tokens).
+// Slots of 134 / 118 bytes leave rows only 2-byte aligned; the loads are
+// unaligned, which the memory path serves.  The buffer range of a slab
+// covers its 16 rows; a slab past the split end or on a bad page gets an
+// empty range, so every step issues the same loads and the compiler's waits
+// cover one slab.  A second small kernel merges the splits (a fused
+// last-workgroup merge needs a device-scope release in every workgroup,
+// which on this part costs far more than a launch).
 #include "tq_internal.h"
 
 namespace tq {
@@ -64,7 +63,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLoScale = 2048.0f;          // lo parts are stored x 2^11
 constexpr int kRec = kD + 4;                 // partial record: O[128], m, l, z, pad
 constexpr float kLazy = 6.0f;                // rescale when the max grows by > 2^6
-constexpr int kMaxChunkPages = 256;          // pages of one split staged in LDS
+constexpr int kMaxChunkPages = 256;          // pages of one split (byte offsets in LDS)
 constexpr int kBufferWord3 = 0x00020000;     // raw buffer resource, 32-bit data format (gfx9 family)
 
 struct MfmaArgs {
@@ -86,10 +85,6 @@ struct MfmaArgs {
   void* out;
   int out_fp32;
 };
-
-__device__ __forceinline__ uint32_t funnel(uint32_t hi, uint32_t lo, uint32_t sh) {
-  return __builtin_amdgcn_alignbyte(hi, lo, sh);
-}
 
 __device__ __forceinline__ uint32_t pack_h2(_Float16 a, _Float16 b) {
   return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, a)) |
@@ -549,287 +544,83 @@ __global__ void __launch_bounds__(256) decode_merge_kernel(MfmaArgs a) {
 }
 
 // ============================================================================
-// direct: every lane loads its own operand bytes (any head count)
+// direct: each lane loads exactly its operand bytes with buffer loads (rows
+// of 134/118-byte slots are only 2-byte aligned; the loads are unaligned,
+// which the memory path handles), two slabs ahead, one wavefront per
+// (split, sequence, kv head)
 // ============================================================================
 
 template <int KB>
-struct RawSlab {
-  uint32_t k[KB == 4 ? 5 : 4];   // K code dwords (+1 for re-alignment)
-  uint32_t v[4][2];              // V code dword pairs
-  uint32_t n[4];
-  uint32_t sz[4];
+struct DirectRegs {
+  uint32_t k[KB == 8 ? 8 : (KB == 4 ? 4 : 3)];   // K bytes of token r16 (32 coordinates)
+  uint32_t X[4];                                  // V codes of token 4*g4 + r, coords [8*r16, 8*r16 + 8)
+  uint32_t n[4];                                  // K norm (f16) of token 4*g4 + r (MSE keys)
+  uint32_t sz[4];                                 // V scale | zero of token 4*g4 + r
+  bool ok;
 };
 
-template <int KB>
-struct DirectGeo {
-  uint32_t k_off4, k_sh;
-  uint32_t v_off4[4], v_sh[4];
-  uint32_t n_off[4], s_off[4];
-  bool s_aligned[4];
+// byte offsets, from the slab's first row, of the lane's operands
+struct DirectOffsets {
+  uint32_t k;
+  uint32_t row[4];       // slot start of token 4*g4 + r
+  uint32_t x[4];         // its V codes for coordinates [8*r16, 8*r16 + 8)
 };
-
-template <int KB>
-__device__ __forceinline__ void direct_load(const uint8_t* __restrict__ base, const DirectGeo<KB>& lg,
-                                            RawSlab<KB>& s) {
-  const u32x4 k4 = *reinterpret_cast<const u32x4*>(base + lg.k_off4);
-  s.k[0] = k4[0];
-  s.k[1] = k4[1];
-  s.k[2] = k4[2];
-  s.k[3] = k4[3];
-  if constexpr (KB == 4) s.k[4] = *reinterpret_cast<const uint32_t*>(base + lg.k_off4 + 16);
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const u32x2 v2 = *reinterpret_cast<const u32x2*>(base + lg.v_off4[r]);
-    s.v[r][0] = v2[0];
-    s.v[r][1] = v2[1];
-    s.n[r] = *reinterpret_cast<const uint16_t*>(base + lg.n_off[r]);
-    // the 4-byte (scale, zero) field ends the slot: never read past it
-    if (lg.s_aligned[r]) {
-      s.sz[r] = *reinterpret_cast<const uint32_t*>(base + lg.s_off[r]);
-    } else {
-      const uint32_t lo16 = *reinterpret_cast<const uint16_t*>(base + lg.s_off[r]);
-      const uint32_t hi16 = *reinterpret_cast<const uint16_t*>(base + lg.s_off[r] + 2);
-      s.sz[r] = lo16 | (hi16 << 16);
-    }
-  }
-}
-
-template <int KB>
-__device__ __forceinline__ SlabOps<KB> direct_ops(const RawSlab<KB>& s, const DirectGeo<KB>& lg) {
-  SlabOps<KB> op;
-#pragma unroll
-  for (int i = 0; i < (KB == 4 ? 4 : 3); ++i) op.kw[i] = funnel(s.k[i + 1], s.k[i], lg.k_sh);
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    op.X[r] = funnel(s.v[r][1], s.v[r][0], lg.v_sh[r]);
-    op.n[r] = s.n[r];
-    op.sz[r] = s.sz[r];
-  }
-  return op;
-}
 
 template <int KB, int SLOT>
-__global__ void __launch_bounds__(512) decode_direct_kernel(MfmaArgs a) {
-  constexpr int kKCB = (kD * KB) / 8;           // K code bytes: 64 or 48
-  constexpr int kKP = kKCB + 2;                 // K packed (codes + norm)
-  constexpr int kVCB = kD / 2;                  // V code bytes
-  constexpr int kLaneKB = KB == 4 ? 16 : 12;    // K bytes per lane per slab
-
-  __shared__ u32x2 s_tab[256];
-  __shared__ int64_t s_page_off[kMaxChunkPages];
-
-  const int tid = threadIdx.x;
-  const int wave = tid >> 6;
-  const int lane = tid & 63;
-  const int r16 = lane & 15;
-  const int g4 = lane >> 4;
-  const int b = blockIdx.y;
-  const int split = blockIdx.x;
-  const int H = a.H;
-  const int64_t row_bytes = static_cast<int64_t>(H) * SLOT;
-  const int64_t page_bytes = static_cast<int64_t>(1 << a.bs_shift) * row_bytes;
-
-  build_tables<KB>(a, s_tab);
-  const int T = clamp_len(a, b, split);
-  const int t0 = split * a.chunk;
-  const int t1 = min(T, t0 + a.chunk);
-  stage_page_offsets(a, b, t0, t1, page_bytes, s_page_off);
-  __syncthreads();
-
-  const int g = wave;
-  if (t0 < t1 && g < H) {
-    h8 qhi[4], qlo[4];
-    load_queries(a, b, g, r16, g4, a.scale_log2, qhi, qlo);
-    // rows 4*g4 + r: row_bytes is even, so a field's alignment depends on r
-    // and the head only and is uniform across the wavefront
-    DirectGeo<KB> lg;
-    const uint32_t head_off = static_cast<uint32_t>(g * SLOT);
-    const uint32_t rb = static_cast<uint32_t>(row_bytes);
-    const uint32_t k_off = r16 * rb + head_off + kLaneKB * g4;
-    lg.k_off4 = k_off & ~3u;
-    lg.k_sh = k_off & 3u;
+__device__ __forceinline__ DirectOffsets direct_offsets(int r16, int g4, uint32_t head_off, uint32_t rb) {
+  constexpr int kKP = KB == 8 ? kD : (kD * KB) / 8 + 2;
+  constexpr int kLaneKB = KB == 8 ? 32 : (KB == 4 ? 16 : 12);
+  DirectOffsets o;
+  o.k = r16 * rb + head_off + kLaneKB * g4;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const uint32_t row = (4 * g4 + r) * rb;
-      lg.v_off4[r] = (row + head_off + kKP + 4 * r16) & ~3u;
-      lg.v_sh[r] = (row + head_off + kKP + 4 * r16) & 3u;
-      lg.n_off[r] = row + head_off + kKCB;
-      lg.s_off[r] = row + head_off + kKP + kVCB;
-      lg.s_aligned[r] = (lg.s_off[r] & 3u) == 0;
-    }
-    RunState st;
-#pragma unroll
-    for (int m = 0; m < 8; ++m) st.O[m] = f4{0.f, 0.f, 0.f, 0.f};
-    st.m_run = -INFINITY;
-    st.l_part = 0.0f;
-    st.z_part = 0.0f;
-    const int p_first = t0 >> a.bs_shift;
-
-    RawSlab<KB> sa, sb;
-    const uint8_t* pa = slab_ptr(a, s_page_off, p_first, t0, row_bytes);
-    if (pa) direct_load(pa, lg, sa);
-    const uint8_t* pb = t0 + 16 < t1 ? slab_ptr(a, s_page_off, p_first, t0 + 16, row_bytes) : nullptr;
-    if (pb) direct_load(pb, lg, sb);
-    for (int t = t0; t < t1; t += 32) {
-      if (pa) process_slab<KB>(direct_ops(sa, lg), t1 - t, s_tab, qhi, qlo, g4, st);
-      pa = t + 32 < t1 ? slab_ptr(a, s_page_off, p_first, t + 32, row_bytes) : nullptr;
-      if (pa) direct_load(pa, lg, sa);
-      if (t + 16 >= t1) break;
-      if (pb) process_slab<KB>(direct_ops(sb, lg), t1 - t - 16, s_tab, qhi, qlo, g4, st);
-      pb = t + 48 < t1 ? slab_ptr(a, s_page_off, p_first, t + 48, row_bytes) : nullptr;
-      if (pb) direct_load(pb, lg, sb);
-    }
-    store_partials(a, b, g, split, g4, r16, st);
+  for (int r = 0; r < 4; ++r) {
+    o.row[r] = (4 * g4 + r) * rb + head_off;
+    o.x[r] = o.row[r] + kKP + 4 * r16;
   }
-}
-
-// ============================================================================
-// staged: each wavefront loads its head's 16 rows with 16-byte loads into a
-// private LDS region, three slabs ahead (even head counts)
-// ============================================================================
-
-// A wavefront's bytes of one row: from its slot start rounded down to 4 to
-// its slot end rounded up to 4 (136 bytes for 134-byte slots, 120 for 118,
-// 196 for 196), fetched as 16-byte chunks plus one 8- or 4-byte tail, never
-// past the slot end rounded up to 4 (the last head's slot ends the row, the
-// last row the cache).
-template <int SLOT>
-struct StageShape {
-  static constexpr int kSpan = SLOT % 4 == 0 ? SLOT : SLOT + 2;   // bytes fetched per row
-  static constexpr int kTail = kSpan % 16;             // 4 or 8
-  static_assert(kTail == 4 || kTail == 8, "row span must be 16-byte chunks plus 4 or 8");
-  static constexpr int kC16 = (kSpan - kTail) / 16;    // 16-byte chunks per row
-  static constexpr int kRow = 16 * (kC16 + 1);         // LDS bytes per row (16-aligned)
-  static constexpr int kStage = 16 * kRow;             // LDS bytes per slab
-  static constexpr int kChunks = 16 * kC16;            // 16-byte chunks per slab
-  static constexpr int kLoads16 = (kChunks + 63) / 64; // 16-byte loads per lane
-};
-
-template <int SLOT>
-struct StageRegs {
-  u32x4 d[StageShape<SLOT>::kLoads16];
-  u32x2 tail;                                          // lanes 0..15: the row's last 4 or 8 bytes
-  bool ok;                                             // a real slab (else a dummy load)
-};
-
-// Per-lane byte offsets (from a slab's first row) of the lane's 16-byte
-// chunks and its tail; lanes without a chunk of their own re-read the last
-// one and lanes 16..63 re-read a tail, so every lane issues the same loads.
-template <int SLOT>
-struct StageOffsets {
-  uint32_t d[StageShape<SLOT>::kLoads16];
-  uint32_t tail;
-};
-
-template <int SLOT>
-__device__ __forceinline__ StageOffsets<SLOT> stage_offsets(int lane, uint32_t head_off4, uint32_t rb) {
-  using S = StageShape<SLOT>;
-  StageOffsets<SLOT> o;
-#pragma unroll
-  for (int j = 0; j < S::kLoads16; ++j) {
-    int c = lane + 64 * j;
-    if (c >= S::kChunks) c = S::kChunks - 1;
-    const int row = c / S::kC16, cc = c - row * S::kC16;
-    o.d[j] = row * rb + head_off4 + 16u * cc;
-  }
-  o.tail = (lane & 15) * rb + head_off4 + 16u * S::kC16;
   return o;
 }
 
-template <int SLOT>
-__device__ __forceinline__ void stage_load(__amdgpu_buffer_rsrc_t rs, const StageOffsets<SLOT>& o,
-                                           StageRegs<SLOT>& sr) {
-  using S = StageShape<SLOT>;
+template <int KB, int SLOT>
+__device__ __forceinline__ void direct_load2(__amdgpu_buffer_rsrc_t rs, const DirectOffsets& o,
+                                             DirectRegs<KB>& d) {
+  constexpr int kKCB = KB == 8 ? kD : (kD * KB) / 8;
+  constexpr int kKP = KB == 8 ? kD : kKCB + 2;
+  if constexpr (KB == 4) {
+    const u32x4 t = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, o.k, 0, 0));
+    d.k[0] = t[0]; d.k[1] = t[1]; d.k[2] = t[2]; d.k[3] = t[3];
+  } else if constexpr (KB == 3) {
+    typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
+    const u32x3 t = __builtin_bit_cast(u32x3, __builtin_amdgcn_raw_buffer_load_b96(rs, o.k, 0, 0));
+    d.k[0] = t[0]; d.k[1] = t[1]; d.k[2] = t[2];
+  } else {
 #pragma unroll
-  for (int j = 0; j < S::kLoads16; ++j)
-    sr.d[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, o.d[j], 0, 0));
-  if constexpr (S::kTail == 8)
-    sr.tail = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, o.tail, 0, 0));
-  else
-    sr.tail[0] = __builtin_amdgcn_raw_buffer_load_b32(rs, o.tail, 0, 0);
-}
-
-template <int SLOT>
-__device__ __forceinline__ void stage_store(uint8_t* lds, int lane, const StageRegs<SLOT>& sr) {
-  using S = StageShape<SLOT>;
-#pragma unroll
-  for (int j = 0; j < S::kLoads16; ++j) {
-    const int c = lane + 64 * j;
-    if (S::kChunks % 64 == 0 || c < S::kChunks) {
-      const int row = c / S::kC16, cc = c - row * S::kC16;
-      *reinterpret_cast<u32x4*>(lds + row * S::kRow + 16 * cc) = sr.d[j];
+    for (int i = 0; i < 2; ++i) {
+      const u32x4 t = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, o.k + 16 * i, 0, 0));
+      d.k[4 * i] = t[0]; d.k[4 * i + 1] = t[1]; d.k[4 * i + 2] = t[2]; d.k[4 * i + 3] = t[3];
     }
   }
-  if (lane < 16) {
-    if constexpr (S::kTail == 8)
-      *reinterpret_cast<u32x2*>(lds + lane * S::kRow + 16 * S::kC16) = sr.tail;
-    else
-      *reinterpret_cast<uint32_t*>(lds + lane * S::kRow + 16 * S::kC16) = sr.tail[0];
-  }
-}
-
-// operands of one lane from the LDS copy of the slab (slot of row t at
-// t * kRow + sh, sh = 0 or 2; reads stay inside the fetched span)
-template <int KB, int SLOT>
-__device__ __forceinline__ SlabOps<KB> staged_ops(const uint8_t* lds, int r16, int g4, uint32_t sh) {
-  using S = StageShape<SLOT>;
-  constexpr int kKCB = (kD * KB) / 8;
-  constexpr int kKP = kKCB + 2;
-  constexpr int kVCB = kD / 2;
-  constexpr int kLaneKB = KB == 4 ? 16 : 12;
-  SlabOps<KB> op;
-  {
-    const uint32_t o = r16 * S::kRow + sh + kLaneKB * g4;
-    const uint32_t* p = reinterpret_cast<const uint32_t*>(lds + (o & ~3u));
-    uint32_t w[kLaneKB / 4 + 1];
-#pragma unroll
-    for (int i = 0; i < kLaneKB / 4 + 1; ++i) w[i] = p[i];
-#pragma unroll
-    for (int i = 0; i < kLaneKB / 4; ++i) op.kw[i] = funnel(w[i + 1], w[i], o & 3u);
-  }
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    const uint32_t rowo = (4 * g4 + r) * S::kRow + sh;
-    const uint32_t vo = rowo + kKP + 4 * r16;
-    const uint32_t* pv = reinterpret_cast<const uint32_t*>(lds + (vo & ~3u));
-    op.X[r] = funnel(pv[1], pv[0], vo & 3u);
-    op.n[r] = *reinterpret_cast<const uint16_t*>(lds + rowo + kKCB);
-    const uint32_t so = rowo + kKP + kVCB;
-    const uint32_t* ps = reinterpret_cast<const uint32_t*>(lds + (so & ~3u));
-    op.sz[r] = funnel(ps[1], ps[0], so & 3u);
+    d.X[r] = __builtin_amdgcn_raw_buffer_load_b32(rs, o.x[r], 0, 0);
+    if constexpr (KB != 8) d.n[r] = __builtin_amdgcn_raw_buffer_load_b16(rs, o.row[r] + kKCB, 0, 0);
+    d.sz[r] = __builtin_amdgcn_raw_buffer_load_b32(rs, o.row[r] + kKP + kD / 2, 0, 0);
   }
-  return op;
 }
 
-// resident wavefronts per SIMD the staged kernel is built for (its register
-// budget: 512 / waves): FP8 keys need the fewest registers, 3-bit keys the most
+// Resident wavefronts per SIMD the kernel is built for (its register budget
+// is 512 / waves), and whether a slab's registers are copied so the next
+// loads go out before the slab is processed (two slabs ahead) or the loads
+// follow the processing (one slab ahead, fewer registers).  Chosen by
+// measurement on the llama3-, k3v4- and k8v4-shaped decodes.
 template <int KB>
-constexpr int kStagedWavesPerSimd = KB == 8 ? 4 : (KB == 4 ? 3 : 2);
-
-// operands of one lane from the LDS copy of a slab of 196-byte slots (row t
-// at t * kRow, every field 4-byte aligned)
-__device__ __forceinline__ SlabOps8 staged_ops8(const uint8_t* lds, int r16, int g4) {
-  using S = StageShape<196>;
-  SlabOps8 op;
-  const uint8_t* kp = lds + r16 * S::kRow + 32 * g4;
-  op.k[0] = *reinterpret_cast<const u32x4*>(kp);
-  op.k[1] = *reinterpret_cast<const u32x4*>(kp + 16);
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const uint8_t* row = lds + (4 * g4 + r) * S::kRow;
-    op.X[r] = *reinterpret_cast<const uint32_t*>(row + kD + 4 * r16);
-    op.sz[r] = *reinterpret_cast<const uint32_t*>(row + kD + kD / 2);
-  }
-  return op;
-}
+constexpr int kSlabWavesPerSimd = KB == 8 ? 4 : 2;
+template <int KB>
+constexpr bool kLoadEarly = KB == 3;
 
 template <int KB, int SLOT>
-__global__ void __launch_bounds__(64, kStagedWavesPerSimd<KB>) decode_staged_kernel(MfmaArgs a) {
-  using S = StageShape<SLOT>;
-
+__global__ void __launch_bounds__(64, kSlabWavesPerSimd<KB>) decode_slab_kernel(MfmaArgs a) {
   __shared__ u32x2 s_tab[256];
   __shared__ int64_t s_page_off[kMaxChunkPages];
-  __shared__ __align__(16) uint8_t s_stage[S::kStage + 16];
 
   const int lane = threadIdx.x;
   const int r16 = lane & 15;
@@ -847,71 +638,76 @@ __global__ void __launch_bounds__(64, kStagedWavesPerSimd<KB>) decode_staged_ker
   const int t1 = min(T, t0 + a.chunk);
   stage_page_offsets(a, b, t0, t1, page_bytes, s_page_off);
   __syncthreads();
+  if (t0 >= t1) return;
 
-  if (t0 < t1) {
-    h8 qhi[4], qlo[4];
-    bf8v qb[4];
-    if constexpr (KB == 8)
-      load_queries_bf16(a, b, g, r16, g4, qb);
-    else
-      load_queries(a, b, g, r16, g4, a.scale_log2, qhi, qlo);
-    const uint32_t rb = static_cast<uint32_t>(row_bytes);
-    const uint32_t head_off = static_cast<uint32_t>(g * SLOT);
-    const uint32_t head_off4 = head_off & ~3u;   // rows start 4-aligned (H even or 196-byte slots)
-    const uint32_t sh = head_off & 3u;
-    RunState st;
+  h8 qhi[4], qlo[4];
+  bf8v qb[4];
+  if constexpr (KB == 8)
+    load_queries_bf16(a, b, g, r16, g4, qb);
+  else
+    load_queries(a, b, g, r16, g4, a.scale_log2, qhi, qlo);
+  RunState st;
 #pragma unroll
-    for (int m = 0; m < 8; ++m) st.O[m] = f4{0.f, 0.f, 0.f, 0.f};
-    st.m_run = -INFINITY;
-    st.l_part = 0.0f;
-    st.z_part = 0.0f;
-    const int p_first = t0 >> a.bs_shift;
-    // One LDS buffer suffices: a wavefront's LDS accesses complete in issue
-    // order, so the next slab's writes never overtake this slab's reads.
-    uint8_t* lds = s_stage;
-    const StageOffsets<SLOT> so = stage_offsets<SLOT>(lane, head_off4, rb);
+  for (int m = 0; m < 8; ++m) st.O[m] = f4{0.f, 0.f, 0.f, 0.f};
+  st.m_run = -INFINITY;
+  st.l_part = 0.0f;
+  st.z_part = 0.0f;
+  const int p_first = t0 >> a.bs_shift;
+  const DirectOffsets off = direct_offsets<KB, SLOT>(r16, g4, static_cast<uint32_t>(g * SLOT),
+                                                     static_cast<uint32_t>(row_bytes));
 
-    // two slabs in flight in registers
-    StageRegs<SLOT> r0, r1;
-    auto load = [&](int t, StageRegs<SLOT>& r) {
-      bool ok;
-      const __amdgpu_buffer_rsrc_t rs = slab_rsrc(a, s_page_off, p_first, t, t1, row_bytes, ok);
-      r.ok = ok;
-      stage_load<SLOT>(rs, so, r);
-    };
-    auto step = [&](int t, StageRegs<SLOT>& r) {
-      // slab t is in r: park it in LDS, refill r with slab t + 32, compute slab t
-      const bool ok = r.ok;
-      stage_store<SLOT>(lds, lane, r);
+  // slabs in flight in two register sets; every step issues the same loads
+  // (an empty buffer range past the split end or on a bad page), so a wait
+  // covers one slab
+  DirectRegs<KB> r0, r1;
+  auto load = [&](int t, DirectRegs<KB>& r) {
+    bool ok;
+    const __amdgpu_buffer_rsrc_t rs = slab_rsrc(a, s_page_off, p_first, t, t1, row_bytes, ok);
+    r.ok = ok;
+    direct_load2<KB, SLOT>(rs, off, r);
+  };
+  auto step = [&](int t, DirectRegs<KB>& r) {
+    DirectRegs<KB> cur_copy;
+    if constexpr (kLoadEarly<KB>) {
+      cur_copy = r;
       load(t + 32, r);
-      if (ok) {
-        if constexpr (KB == 8) {
-          const SlabOps8 op = staged_ops8(lds, r16, g4);
-          float sc[4];
-          score_slab8(op, t1 - t, qb, a.scale_log2, g4, sc);
-          softmax_pv(sc, t1 - t, op.sz, op.X, g4, st);
-        } else {
-          process_slab<KB>(staged_ops<KB, SLOT>(lds, r16, g4, sh), t1 - t, s_tab, qhi, qlo, g4, st);
-        }
-      }
-    };
-    load(t0, r0);
-    load(t0 + 16, r1);
-    // whole rounds of two steps, no early exit: a step past the split end
-    // only moves a dummy slab, which keeps the load count per step fixed
-    for (int t = t0; t < t1; t += 32) {
-      step(t, r0);
-      step(t + 16, r1);
     }
-    store_partials(a, b, g, split, g4, r16, st);
+    const DirectRegs<KB>& cur = kLoadEarly<KB> ? cur_copy : r;
+    if (cur.ok) {
+      float sc[4];
+      if constexpr (KB == 8) {
+        SlabOps8 op;
+        op.k[0] = u32x4{cur.k[0], cur.k[1], cur.k[2], cur.k[3]};
+        op.k[1] = u32x4{cur.k[4], cur.k[5], cur.k[6], cur.k[7]};
+        score_slab8(op, t1 - t, qb, a.scale_log2, g4, sc);
+      } else {
+        SlabOps<KB> op;
+#pragma unroll
+        for (int i = 0; i < (KB == 4 ? 4 : 3); ++i) op.kw[i] = cur.k[i];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) op.n[i] = cur.n[i];
+        score_slab<KB>(op, t1 - t, s_tab, qhi, qlo, g4, sc);
+      }
+      softmax_pv(sc, t1 - t, cur.sz, cur.X, g4, st);
+    }
+    if constexpr (!kLoadEarly<KB>) load(t + 32, r);
+  };
+  load(t0, r0);
+  load(t0 + 16, r1);
+  // whole rounds of two steps, no early exit: a step past the split end only
+  // issues empty loads, which keeps the load count per step fixed
+  for (int t = t0; t < t1; t += 32) {
+    step(t, r0);
+    step(t + 16, r1);
   }
+  store_partials(a, b, g, split, g4, r16, st);
 }
 
 }  // namespace
 
 int mfma_waves_per_cu(const Geometry& g) {
-  const int per_simd = g.key_bits == 8 ? kStagedWavesPerSimd<8>
-                     : (g.key_bits == 4 ? kStagedWavesPerSimd<4> : kStagedWavesPerSimd<3>);
+  const int per_simd = g.key_bits == 8 ? kSlabWavesPerSimd<8>
+                     : (g.key_bits == 4 ? kSlabWavesPerSimd<4> : kSlabWavesPerSimd<3>);
   return 4 * per_simd;
 }
 
@@ -919,10 +715,7 @@ bool mfma_decode_eligible(const Geometry& g, int num_q_heads) {
   const int G = num_q_heads / g.num_kv_heads;
   if (g.head_dim != kD || g.block_size % 16 != 0 || G < 1 || G > 16) return false;
   if (g.key_bits == 8) return g.slot == 196;
-  // odd head counts leave rows 2-byte aligned: the direct kernel, one
-  // workgroup of one wavefront per kv head, takes them (at most 8 heads)
-  return (g.key_bits == 4 || g.key_bits == 3) && (g.slot == 134 || g.slot == 118) &&
-         (g.num_kv_heads % 2 == 0 || g.num_kv_heads <= 8);
+  return (g.key_bits == 4 || g.key_bits == 3) && (g.slot == 134 || g.slot == 118);
 }
 
 size_t mfma_partial_bytes(int batch, int num_q_heads, int num_splits) {
@@ -952,25 +745,14 @@ hipError_t launch_decode_mfma(const Geometry& g, const DevTables* tables, const 
   a.part = static_cast<float*>(workspace);
   a.out = out;
   a.out_fp32 = out_is_fp32;
-  const bool staged = g.key_bits == 8 || (g.num_kv_heads % 2) == 0;
-  if (staged) {
-    // one wavefront per workgroup: (split, sequence, kv head)
-    const dim3 grid(plan.num_splits, batch, g.num_kv_heads);
-    if (g.key_bits == 8)
-      hipLaunchKernelGGL((decode_staged_kernel<8, 196>), grid, dim3(64), 0, stream, a);
-    else if (g.key_bits == 4)
-      hipLaunchKernelGGL((decode_staged_kernel<4, 134>), grid, dim3(64), 0, stream, a);
-    else
-      hipLaunchKernelGGL((decode_staged_kernel<3, 118>), grid, dim3(64), 0, stream, a);
-  } else {
-    // one wavefront per kv head in a workgroup per (split, sequence)
-    const dim3 grid(plan.num_splits, batch);
-    const dim3 block(64 * g.num_kv_heads);
-    if (g.key_bits == 4)
-      hipLaunchKernelGGL((decode_direct_kernel<4, 134>), grid, block, 0, stream, a);
-    else
-      hipLaunchKernelGGL((decode_direct_kernel<3, 118>), grid, block, 0, stream, a);
-  }
+  // one wavefront per workgroup: (split, sequence, kv head)
+  const dim3 grid(plan.num_splits, batch, g.num_kv_heads);
+  if (g.key_bits == 8)
+    hipLaunchKernelGGL((decode_slab_kernel<8, 196>), grid, dim3(64), 0, stream, a);
+  else if (g.key_bits == 4)
+    hipLaunchKernelGGL((decode_slab_kernel<4, 134>), grid, dim3(64), 0, stream, a);
+  else
+    hipLaunchKernelGGL((decode_slab_kernel<3, 118>), grid, dim3(64), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   // merge: one workgroup per (sequence, query head)

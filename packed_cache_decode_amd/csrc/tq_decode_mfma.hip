@@ -80,6 +80,7 @@ struct MfmaArgs {
   int bs_shift;
   int chunk;           // tokens per split, a multiple of 16
   int num_splits;
+  int batch;
   float scale_log2;    // sm_scale * log2(e)
   float* part;         // [B][Hq][S][kRec]
   void* out;
@@ -443,10 +444,10 @@ __device__ __forceinline__ int effective_len(const MfmaArgs& a, int b) {
   return a.num_blocks > 0 ? T : 0;
 }
 
-__device__ __forceinline__ int clamp_len(const MfmaArgs& a, int b, int split) {
+__device__ __forceinline__ int clamp_len(const MfmaArgs& a, int b, int split, int g) {
   const int T = a.seq_lens[b];
   const int t_cap = min(a.num_splits * a.chunk, a.max_blocks << a.bs_shift);
-  if (threadIdx.x == 0 && split == 0 && blockIdx.z == 0) {
+  if (threadIdx.x == 0 && split == 0 && g == 0) {
     if (T < 0 || T > t_cap) const_cast<DevTables*>(a.tables)->err_len = 1;
     if (T > 0 && a.num_blocks <= 0) const_cast<DevTables*>(a.tables)->err_page = 1;
   }
@@ -625,15 +626,25 @@ __global__ void __launch_bounds__(64, kSlabWavesPerSimd<KB>) decode_slab_kernel(
   const int lane = threadIdx.x;
   const int r16 = lane & 15;
   const int g4 = lane >> 4;
-  const int split = blockIdx.x;
-  const int b = blockIdx.y;
-  const int g = blockIdx.z;                  // kv head
+  // XCD-aware order: workgroups go to the 8 XCDs round robin, so block id
+  // x serves item (x % 8) * per_xcd + x / 8 of the (split, sequence, kv head)
+  // items, kv head fastest.  The heads of one page row share cache lines (a
+  // slot is not a multiple of the line), and this puts them on one XCD, in
+  // consecutive slots, so the shared lines come from its L2 rather than
+  // twice from HBM.
+  const int n_items = a.num_splits * a.batch * a.H;
+  const int per_xcd = (n_items + 7) / 8;
+  const int item = static_cast<int>(blockIdx.x % 8) * per_xcd + static_cast<int>(blockIdx.x / 8);
+  if (item >= n_items) return;
+  const int g = item % a.H;                  // kv head
+  const int split = (item / a.H) % a.num_splits;
+  const int b = item / (a.H * a.num_splits);
   const int H = a.H;
   const int64_t row_bytes = static_cast<int64_t>(H) * SLOT;
   const int64_t page_bytes = static_cast<int64_t>(1 << a.bs_shift) * row_bytes;
 
   if constexpr (KB != 8) build_tables<KB>(a, s_tab);
-  const int T = clamp_len(a, b, split);
+  const int T = clamp_len(a, b, split, g);
   const int t0 = split * a.chunk;
   const int t1 = min(T, t0 + a.chunk);
   stage_page_offsets(a, b, t0, t1, page_bytes, s_page_off);
@@ -741,12 +752,14 @@ hipError_t launch_decode_mfma(const Geometry& g, const DevTables* tables, const 
   a.bs_shift = __builtin_ctz(static_cast<unsigned>(g.block_size));
   a.chunk = plan.chunk;
   a.num_splits = plan.num_splits;
+  a.batch = batch;
   a.scale_log2 = sm_scale * kLog2e;
   a.part = static_cast<float*>(workspace);
   a.out = out;
   a.out_fp32 = out_is_fp32;
   // one wavefront per workgroup: (split, sequence, kv head)
-  const dim3 grid(plan.num_splits, batch, g.num_kv_heads);
+  const int n_items = plan.num_splits * batch * g.num_kv_heads;
+  const dim3 grid(8 * ((n_items + 7) / 8));
   if (g.key_bits == 8)
     hipLaunchKernelGGL((decode_slab_kernel<8, 196>), grid, dim3(64), 0, stream, a);
   else if (g.key_bits == 4)

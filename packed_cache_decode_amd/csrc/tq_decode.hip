@@ -18,6 +18,8 @@
 //   every V load is coalesced), accumulating p * v for all G heads.
 //   Partials per (sequence, q head, split): acc[d], running max m (base 2),
 //   running sum l.  The combine weights split s by 2^(m_s - max m).
+#include <cstdlib>
+
 #include "tq_internal.h"
 
 namespace tq {
@@ -363,6 +365,27 @@ hipError_t launch_g(const DecodeArgs& a, int G, int batch, hipStream_t stream) {
 
 DecodePlan plan_decode(const Geometry& g, int batch, int num_q_heads, int max_seq_len) {
   DecodePlan p;
+  // TQ_DECODE_PAGE_MSE=1 selects the page-cooperative kernel for 3/4-bit keys
+  // as well (for tests and measurements of that path)
+  const char* env = getenv("TQ_DECODE_PAGE_MSE");
+  const bool page_mse = env != nullptr && env[0] == '1';
+  if (page_decode_eligible(g, num_q_heads, page_mse)) {
+    // one resident round of workgroups (256 CUs x the workgroups that fit per
+    // CU) over (sequence, split), at least 4 slabs of 16 tokens per split so
+    // the load pipeline's start is amortised
+    const int slabs = max_seq_len > 0 ? (max_seq_len + 15) / 16 : 1;
+    const int target = 256 * page_wgs_per_cu(g);
+    int s = batch > 0 ? (target + batch - 1) / batch : 1;
+    const int s_max = (slabs + 3) / 4;
+    s = s < 1 ? 1 : (s > s_max ? s_max : s);
+    p.mfma = 2;
+    p.chunk = 16 * ((slabs + s - 1) / s);
+    if (p.chunk > 16 * 256) p.chunk = 16 * 256;       // page ids of a split fit in LDS
+    p.num_splits = max_seq_len > 0 ? (max_seq_len + p.chunk - 1) / p.chunk : 1;
+    p.workspace_bytes = mfma_partial_bytes(batch, num_q_heads, p.num_splits);
+    p.workspace_bytes = (p.workspace_bytes + 255) & ~static_cast<size_t>(255);
+    return p;
+  }
   if (mfma_decode_eligible(g, num_q_heads)) {
     // one resident round of wavefronts (256 CUs x the kernel's wavefronts per
     // CU) over (split, sequence, kv head), 16-token slabs, at least 8 slabs

@@ -381,6 +381,79 @@ __device__ __forceinline__ void softmax_pv(const float (&s)[4], int valid_rows, 
   }
 }
 
+// The same online softmax and P.V split in three steps, so a caller can keep
+// the rare rescale of the accumulators out of its main loop (a conditional
+// update of the accumulators inside the loop costs register copies of all of
+// them on every slab).
+struct SlabSoftmax {
+  float sc[4], zr[4];
+  float pm;
+  bool grow;        // the wavefront must rescale before this slab's P.V
+};
+
+template <bool FULL>
+__device__ __forceinline__ SlabSoftmax softmax_check(const float (&s)[4], int valid_rows,
+                                                     const uint32_t (&sz)[4], int g4, const RunState& st) {
+  SlabSoftmax r;
+  r.pm = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t szm = (FULL || 4 * g4 + i < valid_rows) ? sz[i] : 0u;
+    r.sc[i] = f16_bits_to_f32(szm & 0xFFFFu);
+    r.zr[i] = f16_bits_to_f32(szm >> 16);
+  }
+  const float sc_max = fmaxf(fmaxf(r.sc[0], r.sc[1]), fmaxf(r.sc[2], r.sc[3]));
+  const float thr = sc_max > 1000.0f ? 0.0f : kLazy;
+  r.grow = __any(r.pm > st.m_run + thr);
+  return r;
+}
+
+__device__ __forceinline__ void softmax_rescale(const SlabSoftmax& sm, int g4, RunState& st) {
+  const float m_new = fmaxf(st.m_run, max_x32(max_x16(sm.pm)));
+  const float corr = __builtin_amdgcn_exp2f(st.m_run - m_new);   // 0 on the first slab
+  st.l_part *= corr;
+  st.z_part *= corr;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const float cr = lane_value(corr, 4 * g4 + r);
+#pragma unroll
+    for (int m = 0; m < 8; ++m) st.O[m][r] *= cr;
+  }
+  st.m_run = m_new;
+}
+
+__device__ __forceinline__ void softmax_accumulate(const float (&s)[4], const SlabSoftmax& sm,
+                                                   const uint32_t (&X)[4], RunState& st) {
+  h4 W;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const float p = __builtin_amdgcn_exp2f(s[r] - st.m_run);
+    st.l_part += p;
+    st.z_part += p * sm.zr[r];
+    W[r] = static_cast<_Float16>(p * sm.sc[r]);
+  }
+  const h2 b1024 = {static_cast<_Float16>(1024.0f), static_cast<_Float16>(1024.0f)};
+  const h2 b64 = {static_cast<_Float16>(64.0f), static_cast<_Float16>(64.0f)};
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    const uint32_t sel = kb | (0x0Cu << 8) | ((4u + kb) << 16) | (0x0Cu << 24);
+    const uint32_t p01 = __builtin_amdgcn_perm(X[1], X[0], sel);
+    const uint32_t p23 = __builtin_amdgcn_perm(X[3], X[2], sel);
+    h2 lo01 = __builtin_bit_cast(h2, insert_bits(p01, 0x000F000Fu, 0x64006400u));
+    h2 lo23 = __builtin_bit_cast(h2, insert_bits(p23, 0x000F000Fu, 0x64006400u));
+    h2 hi01 = __builtin_bit_cast(h2, insert_bits(p01, 0x00F000F0u, 0x54005400u));
+    h2 hi23 = __builtin_bit_cast(h2, insert_bits(p23, 0x00F000F0u, 0x54005400u));
+    lo01 -= b1024;
+    lo23 -= b1024;
+    hi01 -= b64;
+    hi23 -= b64;
+    const h4 Blo = {lo01[0], lo01[1], lo23[0], lo23[1]};
+    const h4 Bhi = {hi01[0], hi01[1], hi23[0], hi23[1]};
+    st.O[2 * kb] = __builtin_amdgcn_mfma_f32_16x16x16f16(W, Blo, st.O[2 * kb], 0, 0, 0);
+    st.O[2 * kb + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(W, Bhi, st.O[2 * kb + 1], 0, 0, 0);
+  }
+}
+
 // One slab of 3/4-bit keys: scores, norm correction, online softmax, P.V.
 template <int KB>
 __device__ __forceinline__ void process_slab(const SlabOps<KB>& op, int valid_rows,
@@ -714,12 +787,405 @@ __global__ void __launch_bounds__(64, kSlabWavesPerSimd<KB>) decode_slab_kernel(
   store_partials(a, b, g, split, g4, r16, st);
 }
 
+
+// ============================================================================
+// page: one workgroup per (sequence, split), one wavefront per kv head (H = 1,
+// 2, 4 or 8).  The H heads' rows of a 16-token slab are one contiguous block
+// of a page (16 rows of H slots), so the workgroup streams whole slabs into an
+// LDS ring with 16-byte buffer loads that write LDS directly, marked
+// non-temporal: the cache is read once per decode step, and loads that do not
+// allocate in the caches sustain about twice the read rate of plain loads on
+// MI355X.  Every wavefront then takes its own head's operands from LDS.
+//
+// The centroid table holds hi = f16(c) and lo = f16(2 (c - hi)), the queries
+// qhi = f16(q) and qlo = f16(q - qhi).  With at most 8 query heads per kv
+// head one B operand carries both query parts: column h < 8 holds qhi of head
+// h and column h + 8 its qlo, so hi.Q gives hi.qhi in column h and hi.qlo in
+// column h + 8 (added back across the row), and lo.Q gives lo.qhi: the score
+// hi.qhi + hi.qlo + lo.qhi / 2 = c.q to about 2^-20.  One norm accumulator
+// takes hi.hi + hi.lo = sum c^2 to the same order.  The norm factor n / ||c||
+// of a token is computed once, in the lane that holds its diagonal element,
+// and handed to the lanes of its rows by ds_bpermute.
+// ============================================================================
+
+constexpr int kMaxChunkSlabs = 256;          // slabs (and pages) of one split
+constexpr int kTabLo = 1024;                 // byte offset of the lo centroid table
+constexpr int kPageWavesPerSimd = 4;         // two workgroups of eight wavefronts per CU
+
+template <int KB, int SLOT, int H>
+struct PageGeom {
+  static constexpr int kRow = H * SLOT;                     // bytes of one page row
+  static constexpr int kSlab = 16 * kRow;                   // bytes of one slab in the cache
+  static constexpr int kKCB = KB == 8 ? kD : kD * KB / 8;   // K code bytes
+  static constexpr int kKP = KB == 8 ? kD : kKCB + 2;       // K bytes with the norm
+  // In LDS every slot is re-laid in two parts that start on 16-byte
+  // boundaries: the K codes (and norm), then the V codes, scale and zero, so
+  // every operand read is aligned (unaligned LDS reads stall the LDS pipe).
+  // The loads gather the 16-byte chunks of each part from its byte offset in
+  // the cache.
+  static constexpr int kNK = (kKP + 15) / 16;               // 16-byte chunks of the K part
+  static constexpr int kNV = (SLOT - kKP + 15) / 16;        // ... of the V part
+  static constexpr int kSlotL = 16 * (kNK + kNV);           // LDS bytes of one slot
+  static constexpr int kVOff = 16 * kNK;                    // LDS offset of the V part
+  static constexpr int kRowL = H * kSlotL;
+  static constexpr int kSlabChunks = 16 * H * (kNK + kNV);
+  static constexpr int kWaveLoads = (kSlabChunks + 63) / 64;  // wavefront loads of one slab
+  static constexpr int kLoads = (kWaveLoads + H - 1) / H;   // loads per wavefront per slab, at most
+  static constexpr int kFull = kWaveLoads - H * (kLoads - 1);  // wavefronts below this issue kLoads
+  static constexpr int kBuf = kWaveLoads * 1024;            // LDS bytes of one slab buffer
+  static constexpr int kTabBytes = KB == 8 ? 0 : 2 * kTabLo;
+  static constexpr int kExtra = kTabBytes + 4 * kMaxChunkSlabs;
+  // workgroups per CU the register budget allows, and as many slab buffers
+  // (3 to 8) as their share of the 160 KB of LDS holds
+  static constexpr int kWgsPerCu = 4 * kPageWavesPerSimd / H;
+  static constexpr int kNbufFit = (160 * 1024 / kWgsPerCu - kExtra) / kBuf;
+  static constexpr int kNbuf = kNbufFit > 8 ? 8 : (kNbufFit < 3 ? 3 : kNbufFit);
+  // the centroid table first, so a lookup address is just the byte times 4
+  static constexpr int kTabOff = 0;
+  static constexpr int kPidOff = kTabOff + kTabBytes;
+  static constexpr int kRingOff = kPidOff + 4 * kMaxChunkSlabs;
+  static constexpr int kLds = kRingOff + kNbuf * kBuf;
+  static_assert(kLoads * (kNbuf - 2) < 64, "vmcnt out of range");
+  static_assert(kVOff + 64 + 4 <= kSlotL, "V part does not fit");
+
+  // cache byte offset, within the slab, of LDS chunk c (past the slab: an
+  // offset beyond every buffer range, so the load returns zeros)
+  __device__ static uint32_t chunk_src(int c) {
+    if (c >= kSlabChunks) return 0x7FFFFFF0u;
+    const int si = c / (kNK + kNV), k = c - si * (kNK + kNV);
+    const int row = si / H, head = si - row * H;
+    const int off = k < kNK ? 16 * k : kKP + 16 * (k - kNK);
+    return static_cast<uint32_t>(row * kRow + head * SLOT + off);
+  }
+};
+
+// centroid tables: entry e covers the codes e & (2^KB - 1) and e >> KB, as
+// the pair of hi parts (tab[e]) and the pair of lo parts (tab[kTabLo / 4 + e]);
+// two 4-byte lookups per code byte land directly in the MFMA operand registers
+template <int KB>
+__device__ __forceinline__ void build_tables_page(const MfmaArgs& a, uint32_t* tab) {
+  constexpr int kTab = KB == 4 ? 256 : 64;
+  for (int e = threadIdx.x; e < kTab; e += blockDim.x) {
+    const int c0 = e & ((1 << KB) - 1), c1 = e >> KB;
+    const float v0 = a.tables->centroids[c0], v1 = a.tables->centroids[c1];
+    const _Float16 h0 = static_cast<_Float16>(v0), h1 = static_cast<_Float16>(v1);
+    const _Float16 l0 = static_cast<_Float16>(2.0f * (v0 - static_cast<float>(h0)));
+    const _Float16 l1 = static_cast<_Float16>(2.0f * (v1 - static_cast<float>(h1)));
+    tab[e] = pack_h2(h0, h1);
+    tab[kTabLo / 4 + e] = pack_h2(l0, l1);
+  }
+}
+
+// rotated queries of kv head g packed as one B operand: lane (r16, g4) holds
+// coordinates [32*g4, 32*g4 + 32) of head r16 % 8, its f16 hi part for
+// r16 < 8 and its lo part for r16 >= 8 (zero for heads >= G)
+__device__ __forceinline__ void load_queries_packed(const MfmaArgs& a, int b, int g, int r16, int g4,
+                                                    h8 (&qc)[4]) {
+  h8 qhi[4], qlo[4];
+  load_queries(a, b, g, r16 & 7, g4, a.scale_log2, qhi, qlo);
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) qc[kk] = r16 < 8 ? qhi[kk] : qlo[kk];
+}
+
+// page ids of the split's pages -> LDS (-1: outside the cache)
+__device__ __forceinline__ void stage_page_ids(const MfmaArgs& a, int b, int t0, int t1, int32_t* s_pid) {
+  const int p_first = t0 >> a.bs_shift;
+  const int n_pages = ((t1 - 1) >> a.bs_shift) - p_first + 1;
+  const int32_t* bt = a.block_table + static_cast<int64_t>(b) * a.max_blocks;
+  for (int i = threadIdx.x; i < n_pages; i += blockDim.x) {
+    const int page = bt[p_first + i];
+    const bool ok = page >= 0 && page < a.num_blocks;
+    if (!ok) const_cast<DevTables*>(a.tables)->err_page = 1;
+    s_pid[i] = ok ? page : -1;
+  }
+}
+
+// 16 bytes per lane from buffer offset voff into LDS at dst + 16 * lane,
+// non-temporal.  Written as inline assembly so the compiler does not treat
+// the load as an LDS store it must wait for before every LDS read (it cannot
+// tell the ring's slots apart); the kernel waits for these loads itself.
+__device__ __forceinline__ void lds_dma_16(__amdgpu_buffer_rsrc_t rs, const uint8_t* dst, uint32_t voff) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(
+      static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const uint8_t*)dst)));
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen nt lds"
+               :: "s"(m0), "v"(voff), "s"(rs) : "memory", "m0");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+__device__ __forceinline__ void wave_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// scores (base 2) of this wavefront's head for the slab in buf, and the V
+// operands of its rows; rows at or past valid_rows score -inf
+template <int KB, int SLOT, int H, bool FULL>
+__device__ __forceinline__ void page_scores(const uint8_t* buf, int valid_rows, int w, int r16, int g4,
+                                            const uint32_t* tab, const h8 (&qc)[4],
+                                            const bf8v (&qb)[4], float scale_log2, bool sel1, bool sel2,
+                                            float (&s)[4], uint32_t (&X)[4], uint32_t (&sz)[4]) {
+  using Geo = PageGeom<KB, SLOT, H>;
+  constexpr int kRow = Geo::kRowL;
+  const uint8_t* hb = buf + w * Geo::kSlotL;              // this head's slot in row 0
+  const uint8_t* rb = hb + 4 * g4 * kRow;                 // ... in row 4*g4
+  if constexpr (KB == 8) {
+    const uint8_t* kp = hb + r16 * kRow + 32 * g4;
+    SlabOps8 op;
+    op.k[0] = *reinterpret_cast<const u32x4*>(kp);
+    op.k[1] = *reinterpret_cast<const u32x4*>(kp + 16);
+    f4 S = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const uint32_t w0 = op.k[kk >> 1][2 * (kk & 1)], w1 = op.k[kk >> 1][2 * (kk & 1) + 1];
+      const bf2 c0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false);
+      const bf2 c1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true);
+      const bf2 c2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false);
+      const bf2 c3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true);
+      const bf8v av = {c0[0], c0[1], c1[0], c1[1], c2[0], c2[1], c3[0], c3[1]};
+      S = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, qb[kk], S, 0, 0, 0);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) s[r] = (FULL || 4 * g4 + r < valid_rows) ? S[r] * scale_log2 : -INFINITY;
+  } else {
+    uint32_t kw[KB == 4 ? 4 : 3];
+    if constexpr (KB == 4) {
+      const u32x4 t = *reinterpret_cast<const u32x4*>(hb + r16 * kRow + 16 * g4);
+      kw[0] = t[0]; kw[1] = t[1]; kw[2] = t[2]; kw[3] = t[3];
+    } else {
+      typedef uint32_t u32x3a __attribute__((ext_vector_type(3), aligned(4)));
+      const u32x3a t = *reinterpret_cast<const u32x3a*>(hb + r16 * kRow + 12 * g4);
+      kw[0] = t[0]; kw[1] = t[1]; kw[2] = t[2];
+    }
+    // norm of token 4*g4 + (r16 & 3): only the lanes that hold its diagonal
+    // element use it
+    const uint32_t nb = *reinterpret_cast<const uint16_t*>(hb + (4 * g4 + (r16 & 3)) * kRow + Geo::kKCB);
+    f4 S = {0.f, 0.f, 0.f, 0.f}, Slo = {0.f, 0.f, 0.f, 0.f};
+    f4 N = {1e-16f, 1e-16f, 1e-16f, 1e-16f};
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      uint32_t idx[4];
+      if constexpr (KB == 4) {
+#pragma unroll
+        for (int p = 0; p < 4; ++p) idx[p] = (kw[kk] >> (8 * p)) & 0xFFu;
+      } else {
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const int bit = 24 * kk + 6 * p;
+          const int wd = bit >> 5, o = bit & 31;
+          uint32_t v = kw[wd] >> o;
+          if (o > 26) v |= kw[wd + 1] << (32 - o);
+          idx[p] = v & 63u;
+        }
+      }
+      // volatile: two separate 4-byte reads (a merged 8-byte read would land
+      // hi and lo in adjacent registers and cost moves into the operands)
+      typedef __attribute__((address_space(3))) const volatile uint32_t lds_u32;
+      lds_u32* vt = (lds_u32*)(tab);
+      u32x4 hi, lo;
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        hi[p] = vt[idx[p]];
+        lo[p] = vt[kTabLo / 4 + idx[p]];
+      }
+      const h8 chi = __builtin_bit_cast(h8, hi);
+      const h8 clo = __builtin_bit_cast(h8, lo);
+      S = __builtin_amdgcn_mfma_f32_16x16x32_f16(chi, qc[kk], S, 0, 0, 0);
+      Slo = __builtin_amdgcn_mfma_f32_16x16x32_f16(clo, qc[kk], Slo, 0, 0, 0);
+      N = __builtin_amdgcn_mfma_f32_16x16x32_f16(chi, chi, N, 0, 0, 0);
+      N = __builtin_amdgcn_mfma_f32_16x16x32_f16(chi, clo, N, 0, 0, 0);
+    }
+    // lane (r16, g4) with r16 = 4*g4 + i holds N[4*g4 + i][4*g4 + i] as element i
+    const float nd = sel2 ? (sel1 ? N[3] : N[2]) : (sel1 ? N[1] : N[0]);
+    const float fq = f16_bits_to_f32(nb) * __builtin_amdgcn_rsqf(nd);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float fac = lane_value(fq, 20 * g4 + r);
+      // column h + 8 (row rotation by 8) holds hi.qlo of head h; lanes
+      // r16 >= 8 get a copy of head r16 - 8's score, which is never stored
+      const float sr = S[r];
+      const float other = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(sr), 0x128, 0xF, 0xF, false));
+      s[r] = (FULL || 4 * g4 + r < valid_rows) ? (S[r] + other + 0.5f * Slo[r]) * fac : -INFINITY;
+    }
+  }
+  // the V operands are read after the scores (fewer registers live at once)
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    X[r] = *reinterpret_cast<const uint32_t*>(rb + r * kRow + Geo::kVOff + 4 * r16);
+    sz[r] = *reinterpret_cast<const uint32_t*>(rb + r * kRow + Geo::kVOff + kD / 2);
+  }
+}
+
+template <int KB, int SLOT, int H>
+__global__ void __launch_bounds__(64 * H, kPageWavesPerSimd) decode_page_kernel(MfmaArgs a) {
+  using Geo = PageGeom<KB, SLOT, H>;
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  uint32_t* tab = reinterpret_cast<uint32_t*>(smem + Geo::kTabOff);
+  int32_t* s_pid = reinterpret_cast<int32_t*>(smem + Geo::kPidOff);
+
+  const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));   // kv head
+  const int lane = threadIdx.x & 63;
+  const int r16 = lane & 15;
+  const int g4 = lane >> 4;
+  const int b = blockIdx.x / a.num_splits;
+  const int split = blockIdx.x % a.num_splits;
+
+  const int T = clamp_len(a, b, split, w);
+  const int t0 = split * a.chunk;
+  const int t1 = min(T, t0 + a.chunk);
+  if (t0 >= t1) return;                      // the whole workgroup, before any barrier
+  if constexpr (KB != 8) build_tables_page<KB>(a, tab);
+  stage_page_ids(a, b, t0, t1, s_pid);
+  __syncthreads();
+
+  h8 qc[4];
+  bf8v qb[4];
+  if constexpr (KB == 8)
+    load_queries_bf16(a, b, w, r16, g4, qb);
+  else
+    load_queries_packed(a, b, w, r16, g4, qc);
+  RunState st;
+#pragma unroll
+  for (int m = 0; m < 8; ++m) st.O[m] = f4{0.f, 0.f, 0.f, 0.f};
+  st.m_run = -INFINITY;
+  st.l_part = 0.0f;
+  st.z_part = 0.0f;
+  const bool sel1 = (r16 & 1) != 0, sel2 = (r16 & 2) != 0;
+
+  const int p_first = t0 >> a.bs_shift;
+  const int bs_mask = (1 << a.bs_shift) - 1;
+  const int64_t page_bytes = static_cast<int64_t>(1 << a.bs_shift) * Geo::kRow;
+  const int n_slabs = (t1 - t0 + 15) >> 4;
+  const bool full_loads = w < Geo::kFull;
+  uint32_t src_off[Geo::kLoads];
+#pragma unroll
+  for (int l = 0; l < Geo::kLoads; ++l) src_off[l] = Geo::chunk_src((w + H * l) * 64 + lane);
+  // the query loads are done before the first slab is requested, so every
+  // wait in the loop counts slab loads only
+  wait_vmcnt<0>();
+
+  // slab j -> ring buffer j % kNbuf; a slab past the split end or on a bad
+  // page gets an empty buffer range (its loads return zeros and touch no
+  // memory), so every wavefront issues the same loads for every slab
+  auto issue = [&](int j) {
+    const int t = t0 + 16 * j;
+    int pid = -1;
+    if (t < t1) pid = s_pid[(t >> a.bs_shift) - p_first];
+    pid = __builtin_amdgcn_readfirstlane(pid);
+    const int64_t off = pid >= 0 ? pid * page_bytes + static_cast<int64_t>(t & bs_mask) * Geo::kRow : 0;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(a.cache) + off, 0, pid >= 0 ? Geo::kSlab : 0, kBufferWord3);
+    uint8_t* dst = smem + Geo::kRingOff + (j % Geo::kNbuf) * Geo::kBuf;
+#pragma unroll
+    for (int l = 0; l < Geo::kLoads; ++l)
+      if (l < Geo::kLoads - 1 || full_loads) lds_dma_16(rs, dst + (w + H * l) * 1024, src_off[l]);
+  };
+#pragma unroll
+  for (int j = 0; j < Geo::kNbuf - 1; ++j) issue(j);
+
+  // The inner loop never changes the accumulators except through the P.V
+  // MFMAs; a slab that raises a head's running max past the lazy threshold
+  // leaves it, and the rescale and that slab's P.V happen outside.
+  int j = 0;
+  while (true) {
+    float s[4];
+    uint32_t X[4], sz[4];
+    SlabSoftmax sm;
+    bool grow = false;
+    for (; j < n_slabs; ++j) {
+      // this wavefront's part of slab j has landed: slabs j+1 .. j+kNbuf-2
+      // may still be in flight
+      if (full_loads)
+        wait_vmcnt<Geo::kLoads * (Geo::kNbuf - 2)>();
+      else
+        wait_vmcnt<(Geo::kLoads - 1) * (Geo::kNbuf - 2)>();
+      wave_barrier();                        // every part of slab j landed; slab j-1 is consumed
+      issue(j + Geo::kNbuf - 1);             // into the buffer of slab j-1
+      const int t = t0 + 16 * j;
+      const int pid = s_pid[(t >> a.bs_shift) - p_first];
+      if (__builtin_amdgcn_readfirstlane(pid) < 0) continue;
+      const uint8_t* buf = smem + Geo::kRingOff + (j % Geo::kNbuf) * Geo::kBuf;
+      const int valid = t1 - t;
+      if (valid >= 16) {
+        page_scores<KB, SLOT, H, true>(buf, 16, w, r16, g4, tab, qc, qb, a.scale_log2, sel1, sel2, s, X, sz);
+        sm = softmax_check<true>(s, 16, sz, g4, st);
+      } else {
+        page_scores<KB, SLOT, H, false>(buf, valid, w, r16, g4, tab, qc, qb, a.scale_log2, sel1, sel2, s, X, sz);
+        sm = softmax_check<false>(s, valid, sz, g4, st);
+      }
+      if (sm.grow) {
+        grow = true;
+        break;
+      }
+      softmax_accumulate(s, sm, X, st);
+    }
+    if (!grow) break;
+    softmax_rescale(sm, g4, st);
+    softmax_accumulate(s, sm, X, st);
+    ++j;
+  }
+  wait_vmcnt<0>();                           // no load may still write LDS at exit
+  store_partials(a, b, w, split, g4, r16, st);
+}
+
+template <int KB, int SLOT, int H>
+hipError_t launch_page_t(const MfmaArgs& a, int batch, hipStream_t stream) {
+  using Geo = PageGeom<KB, SLOT, H>;
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_page_kernel<KB, SLOT, H>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, Geo::kLds);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL((decode_page_kernel<KB, SLOT, H>), dim3(batch * a.num_splits), dim3(64 * H),
+                     Geo::kLds, stream, a);
+  return hipGetLastError();
+}
+
+template <int KB, int SLOT>
+hipError_t launch_page_h(const MfmaArgs& a, int batch, hipStream_t stream) {
+  switch (a.H) {
+    case 1: return launch_page_t<KB, SLOT, 1>(a, batch, stream);
+    case 2: return launch_page_t<KB, SLOT, 2>(a, batch, stream);
+    case 4: return launch_page_t<KB, SLOT, 4>(a, batch, stream);
+    case 8: return launch_page_t<KB, SLOT, 8>(a, batch, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 }  // namespace
 
 int mfma_waves_per_cu(const Geometry& g) {
   const int per_simd = g.key_bits == 8 ? kSlabWavesPerSimd<8>
                      : (g.key_bits == 4 ? kSlabWavesPerSimd<4> : kSlabWavesPerSimd<3>);
   return 4 * per_simd;
+}
+
+bool page_decode_eligible(const Geometry& g, int num_q_heads, bool mse_keys_too) {
+  const int H = g.num_kv_heads;
+  // query hi and lo parts share one B operand for up to 8 heads per kv head
+  const bool g_ok = g.key_bits == 8 || num_q_heads <= 8 * H;
+  // 3/4-bit keys: the per-head kernel is still the faster one (the page
+  // kernel's centroid lookups are bound by LDS bank conflicts), unless asked
+  const bool kind_ok = g.key_bits == 8 || mse_keys_too;
+  return mfma_decode_eligible(g, num_q_heads) && g_ok && kind_ok && (H == 1 || H == 2 || H == 4 || H == 8);
+}
+
+int page_wgs_per_cu(const Geometry& g) {
+  const int H = g.num_kv_heads;
+  int lds = 0;
+#define TQ_PAGE_LDS(KB_, SLOT_)                                                   \
+  if (g.key_bits == KB_) {                                                        \
+    lds = H == 1 ? PageGeom<KB_, SLOT_, 1>::kLds : H == 2 ? PageGeom<KB_, SLOT_, 2>::kLds \
+        : H == 4 ? PageGeom<KB_, SLOT_, 4>::kLds : PageGeom<KB_, SLOT_, 8>::kLds;  \
+  }
+  TQ_PAGE_LDS(8, 196) TQ_PAGE_LDS(4, 134) TQ_PAGE_LDS(3, 118)
+#undef TQ_PAGE_LDS
+  int n = lds > 0 ? (160 * 1024) / lds : 1;
+  const int by_regs = 4 * kPageWavesPerSimd / H;
+  if (n > by_regs) n = by_regs;
+  return n < 1 ? 1 : n;
 }
 
 bool mfma_decode_eligible(const Geometry& g, int num_q_heads) {
@@ -757,6 +1223,14 @@ hipError_t launch_decode_mfma(const Geometry& g, const DevTables* tables, const 
   a.part = static_cast<float*>(workspace);
   a.out = out;
   a.out_fp32 = out_is_fp32;
+  if (plan.mfma == 2) {
+    hipError_t e = g.key_bits == 8 ? launch_page_h<8, 196>(a, batch, stream)
+                 : g.key_bits == 4 ? launch_page_h<4, 134>(a, batch, stream)
+                                   : launch_page_h<3, 118>(a, batch, stream);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(decode_merge_kernel, dim3(batch * num_q_heads), dim3(256), 0, stream, a);
+    return hipGetLastError();
+  }
   // one wavefront per workgroup: (split, sequence, kv head)
   const int n_items = plan.num_splits * batch * g.num_kv_heads;
   const dim3 grid(8 * ((n_items + 7) / 8));

@@ -60,6 +60,34 @@ def test_decode_small_parity_fp32(preset, G):
 
 
 @pytest.mark.parametrize("preset", PRESETS)
+@pytest.mark.parametrize("G,H", [(4, 3), (12, 2), (16, 1)])
+def test_decode_per_head_kernel_shapes(preset, G, H):
+    # odd kv-head counts and more than 8 query heads per kv head take the
+    # per-head matrix-core kernel instead of the page-cooperative one
+    got, want = _decode_from_oracle_cache(_wl(preset, G=G, H=H, B=3, seed=G + H))
+    check_decode(got, want, bf16_out=False)
+
+
+@pytest.mark.parametrize("preset", PRESETS)
+@pytest.mark.parametrize("H", [1, 4, 8])
+@pytest.mark.parametrize("page_mse", ["0", "1"])
+def test_decode_page_kernel_head_counts(preset, H, page_mse, monkeypatch):
+    # with TQ_DECODE_PAGE_MSE=1 the page-cooperative kernel also takes the
+    # 3/4-bit presets (it always takes FP8 keys)
+    monkeypatch.setenv("TQ_DECODE_PAGE_MSE", page_mse)
+    got, want = _decode_from_oracle_cache(_wl(preset, G=8 if H < 8 else 4, H=H, B=3, lens=(1, 300), seed=30 + H))
+    check_decode(got, want, bf16_out=False)
+
+
+@pytest.mark.parametrize("preset", ["turboquant_4bit_nc", "turboquant_k3v4_nc"])
+def test_decode_page_kernel_mse_ragged(preset, monkeypatch):
+    monkeypatch.setenv("TQ_DECODE_PAGE_MSE", "1")
+    w = _wl(preset, G=4, H=2, B=7, lens=(600, 600), seed=9)
+    got, want = _decode_from_oracle_cache(w, lens=[0, 1, 15, 16, 17, 257, 600])
+    check_decode(got, want, bf16_out=False)
+
+
+@pytest.mark.parametrize("preset", PRESETS)
 def test_decode_small_parity_bf16(preset):
     got, want = _decode_from_oracle_cache(_wl(preset, G=4, seed=21), out_fp32=False)
     check_decode(got, want, bf16_out=True)

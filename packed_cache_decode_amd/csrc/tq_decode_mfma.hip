@@ -15,7 +15,7 @@
 // MFMA contractions:
 //   scores  S[t][h] = sum_c C[t][c] Q[h][c]     v_mfma_f32_16x16x32_f16 / _bf16
 //   norms   N[t][t] = sum_c C[t][c] C[t][c]     (diagonal of C C^T, MSE keys)
-//   values  O[h][c] += sum_t W[h][t] V[t][c]    v_mfma_f32_16x16x16_f16
+//   values  O[h][c] += sum_t W[h][t] V[t][c]    v_mfma_f32_16x16x16_f16 (W as f16 hi + lo)
 // For MSE keys C are the centroids of the slab's K codes, looked up per code
 // byte (two codes) in an LDS table; f16 alone is not precise enough for the
 // scores (outlier keys make them large), so C and Q are carried as f16 hi +
@@ -347,13 +347,17 @@ __device__ __forceinline__ void softmax_pv(const float (&s)[4], int valid_rows, 
     }
     st.m_run = m_new;
   }
-  h4 W;
+  // p * scale as f16 hi + lo: one f16 alone (2^-11) is not precise enough
+  // when a single token dominates and its V range is wide
+  h4 W, Wl;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const float p = __builtin_amdgcn_exp2f(s[r] - st.m_run);      // 0 for masked rows
     st.l_part += p;
     st.z_part += p * zr[r];
-    W[r] = static_cast<_Float16>(p * sc[r]);
+    const float wf = p * sc[r];
+    W[r] = static_cast<_Float16>(wf);
+    Wl[r] = static_cast<_Float16>(wf - static_cast<float>(W[r]));
   }
 
   // ---- V: codes of tokens 4*g4 + r at coordinates 8*r16 + m ----
@@ -378,6 +382,8 @@ __device__ __forceinline__ void softmax_pv(const float (&s)[4], int valid_rows, 
     const h4 Bhi = {hi01[0], hi01[1], hi23[0], hi23[1]};
     st.O[2 * kb] = __builtin_amdgcn_mfma_f32_16x16x16f16(W, Blo, st.O[2 * kb], 0, 0, 0);
     st.O[2 * kb + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(W, Bhi, st.O[2 * kb + 1], 0, 0, 0);
+    st.O[2 * kb] = __builtin_amdgcn_mfma_f32_16x16x16f16(Wl, Blo, st.O[2 * kb], 0, 0, 0);
+    st.O[2 * kb + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(Wl, Bhi, st.O[2 * kb + 1], 0, 0, 0);
   }
 }
 
@@ -424,13 +430,17 @@ __device__ __forceinline__ void softmax_rescale(const SlabSoftmax& sm, int g4, R
 
 __device__ __forceinline__ void softmax_accumulate(const float (&s)[4], const SlabSoftmax& sm,
                                                    const uint32_t (&X)[4], RunState& st) {
-  h4 W;
+  // p * scale as f16 hi + lo: one f16 alone (2^-11) is not precise enough
+  // when a single token dominates and its V range is wide
+  h4 W, Wl;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const float p = __builtin_amdgcn_exp2f(s[r] - st.m_run);
     st.l_part += p;
     st.z_part += p * sm.zr[r];
-    W[r] = static_cast<_Float16>(p * sm.sc[r]);
+    const float wf = p * sm.sc[r];
+    W[r] = static_cast<_Float16>(wf);
+    Wl[r] = static_cast<_Float16>(wf - static_cast<float>(W[r]));
   }
   const h2 b1024 = {static_cast<_Float16>(1024.0f), static_cast<_Float16>(1024.0f)};
   const h2 b64 = {static_cast<_Float16>(64.0f), static_cast<_Float16>(64.0f)};
@@ -451,6 +461,9 @@ __device__ __forceinline__ void softmax_accumulate(const float (&s)[4], const Sl
     const h4 Bhi = {hi01[0], hi01[1], hi23[0], hi23[1]};
     st.O[2 * kb] = __builtin_amdgcn_mfma_f32_16x16x16f16(W, Blo, st.O[2 * kb], 0, 0, 0);
     st.O[2 * kb + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(W, Bhi, st.O[2 * kb + 1], 0, 0, 0);
+    st.O[2 * kb] = __builtin_amdgcn_mfma_f32_16x16x16f16(Wl, Blo, st.O[2 * kb], 0, 0, 0);
+    st.O[2 * kb + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(Wl, Bhi, st.O[2 * kb + 1], 0, 0, 0);
+    if (kb & 1) __builtin_amdgcn_sched_barrier(0);     // bounded operand registers
   }
 }
 
@@ -552,68 +565,73 @@ __device__ __forceinline__ void store_partials(const MfmaArgs& a, int b, int g, 
   }
 }
 
-// Merge the splits of one (sequence, query head): 8 groups of 32 threads
-// take every 8th split, each thread four coordinates; the groups' partial
-// sums meet in LDS.  Split s is weighted by 2^(m_s - max m).
+// Merge the splits of one (sequence, query head): four wavefronts take every
+// fourth split, lane = coordinates 2*lane and 2*lane + 1.  Each wavefront
+// merges its splits online (running max, a split weighted by 2^(m_s - max)),
+// with all loads of a group of splits issued together, and the four meet in
+// LDS.  o = sum_s w_s (O_s + z_s) / sum_s w_s l_s.
 __global__ void __launch_bounds__(256) decode_merge_kernel(MfmaArgs a) {
-  __shared__ float s_m[8];
-  __shared__ float4 s_acc[8][kD / 4];
-  __shared__ float s_l[8];
+  __shared__ float s_m[4], s_l[4];
+  __shared__ float2 s_acc[4][64];
   const int bh = blockIdx.x;                 // b * Hq + hq
   const int b = bh / a.Hq;
-  const int grp = threadIdx.x >> 5, ln = threadIdx.x & 31;
-  const int c4 = ln * 4;
+  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int T = effective_len(a, b);
   const int nsp = (T + a.chunk - 1) / a.chunk;
   const float* recs = a.part + static_cast<int64_t>(bh) * a.num_splits * kRec;
-  float M = -INFINITY;
-  for (int sp = grp; sp < nsp; sp += 8) M = fmaxf(M, recs[sp * kRec + kD]);
-  if (ln == 0) s_m[grp] = M;
-  __syncthreads();
+  float M = -INFINITY, L = 0.0f;
+  float2 acc = make_float2(0.0f, 0.0f);
+  constexpr int kU = 4;                      // splits per wavefront whose loads are in flight together
+  for (int s0 = wv; s0 < nsp; s0 += 4 * kU) {
+    float4 mlz[kU];
+    float2 o[kU];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) M = fmaxf(M, s_m[i]);
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  float L = 0.0f;
-#pragma unroll 4
-  for (int sp = grp; sp < nsp; sp += 8) {
-    const float* rec = recs + sp * kRec;
-    const float w = __builtin_amdgcn_exp2f(rec[kD] - M);
-    const float z = rec[kD + 2];
-    const float4 v = *reinterpret_cast<const float4*>(rec + c4);
-    acc.x += w * (v.x + z);
-    acc.y += w * (v.y + z);
-    acc.z += w * (v.z + z);
-    acc.w += w * (v.w + z);
-    L += w * rec[kD + 1];
-  }
-  s_acc[grp][ln] = acc;
-  if (ln == 0) s_l[grp] = L;
-  __syncthreads();
-  if (grp != 0) return;
-#pragma unroll
-  for (int i = 1; i < 8; ++i) {
-    const float4 o = s_acc[i][ln];
-    acc.x += o.x;
-    acc.y += o.y;
-    acc.z += o.z;
-    acc.w += o.w;
-    L += s_l[i];
-  }
-  const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-  const float r4[4] = {acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv};
-  const int64_t oi = static_cast<int64_t>(bh) * kD + c4;
-  if (a.out_fp32) {
-    *reinterpret_cast<float4*>(static_cast<float*>(a.out) + oi) = make_float4(r4[0], r4[1], r4[2], r4[3]);
-  } else {
-    uint32_t pk[2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      uint32_t u0 = __float_as_uint(r4[2 * i]), u1 = __float_as_uint(r4[2 * i + 1]);
-      u0 = (u0 + 0x7FFFu + ((u0 >> 16) & 1u)) >> 16;     // round to nearest even
-      u1 = (u1 + 0x7FFFu + ((u1 >> 16) & 1u)) >> 16;
-      pk[i] = u0 | (u1 << 16);
+    for (int u = 0; u < kU; ++u) {
+      const int sp = s0 + 4 * u;
+      const float* rec = recs + static_cast<int64_t>(sp < nsp ? sp : s0) * kRec;
+      mlz[u] = *reinterpret_cast<const float4*>(rec + kD);      // m, l, z, pad
+      o[u] = *reinterpret_cast<const float2*>(rec + 2 * lane);
     }
-    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + oi) = make_uint2(pk[0], pk[1]);
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      if (s0 + 4 * u >= nsp) break;
+      const float m_new = fmaxf(M, mlz[u].x);
+      if (m_new == -INFINITY) continue;                         // nothing attended yet (bad pages)
+      const float c = __builtin_amdgcn_exp2f(M - m_new);        // 0 on the first split
+      const float w = __builtin_amdgcn_exp2f(mlz[u].x - m_new);
+      acc.x = acc.x * c + w * (o[u].x + mlz[u].z);
+      acc.y = acc.y * c + w * (o[u].y + mlz[u].z);
+      L = L * c + w * mlz[u].y;
+      M = m_new;
+    }
+  }
+  if (lane == 0) {
+    s_m[wv] = M;
+    s_l[wv] = L;
+  }
+  s_acc[wv][lane] = acc;
+  __syncthreads();
+  if (wv != 0) return;
+  const float Mx = fmaxf(fmaxf(s_m[0], s_m[1]), fmaxf(s_m[2], s_m[3]));
+  float2 tot = make_float2(0.0f, 0.0f);
+  float Lt = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float w = s_m[i] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(s_m[i] - Mx);
+    tot.x += w * s_acc[i][lane].x;
+    tot.y += w * s_acc[i][lane].y;
+    Lt += w * s_l[i];
+  }
+  const float inv = Lt > 0.0f ? 1.0f / Lt : 0.0f;
+  const float r0 = tot.x * inv, r1 = tot.y * inv;
+  const int64_t oi = static_cast<int64_t>(bh) * kD + 2 * lane;
+  if (a.out_fp32) {
+    *reinterpret_cast<float2*>(static_cast<float*>(a.out) + oi) = make_float2(r0, r1);
+  } else {
+    uint32_t u0 = __float_as_uint(r0), u1 = __float_as_uint(r1);
+    u0 = (u0 + 0x7FFFu + ((u0 >> 16) & 1u)) >> 16;     // round to nearest even
+    u1 = (u1 + 0x7FFFu + ((u1 >> 16) & 1u)) >> 16;
+    *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(a.out) + oi) = u0 | (u1 << 16);
   }
 }
 
@@ -809,7 +827,6 @@ __global__ void __launch_bounds__(64, kSlabWavesPerSimd<KB>) decode_slab_kernel(
 // ============================================================================
 
 constexpr int kMaxChunkSlabs = 256;          // slabs (and pages) of one split
-constexpr int kTabLo = 1024;                 // byte offset of the lo centroid table
 constexpr int kPageWavesPerSimd = 4;         // two workgroups of eight wavefronts per CU
 
 template <int KB, int SLOT, int H>
@@ -833,18 +850,25 @@ struct PageGeom {
   static constexpr int kLoads = (kWaveLoads + H - 1) / H;   // loads per wavefront per slab, at most
   static constexpr int kFull = kWaveLoads - H * (kLoads - 1);  // wavefronts below this issue kLoads
   static constexpr int kBuf = kWaveLoads * 1024;            // LDS bytes of one slab buffer
-  static constexpr int kTabBytes = KB == 8 ? 0 : 2 * kTabLo;
-  static constexpr int kExtra = kTabBytes + 4 * kMaxChunkSlabs;
+  static constexpr int kTabBytes = KB == 8 ? 0 : 256 * 8;   // static LDS centroid table
+  // 3/4-bit keys keep the per-lane load offsets in LDS (16 bytes per lane,
+  // read before each slab's loads) instead of registers
+  static constexpr bool kSrcInLds = KB != 8;
+  static constexpr int kSrcBytes = kSrcInLds ? H * 64 * 16 : 0;
+  static constexpr int kExtra = kTabBytes + 4 * kMaxChunkSlabs + kSrcBytes;
   // workgroups per CU the register budget allows, and as many slab buffers
   // (3 to 8) as their share of the 160 KB of LDS holds
   static constexpr int kWgsPerCu = 4 * kPageWavesPerSimd / H;
   static constexpr int kNbufFit = (160 * 1024 / kWgsPerCu - kExtra) / kBuf;
   static constexpr int kNbuf = kNbufFit > 8 ? 8 : (kNbufFit < 3 ? 3 : kNbufFit);
-  // the centroid table first, so a lookup address is just the byte times 4
-  static constexpr int kTabOff = 0;
-  static constexpr int kPidOff = kTabOff + kTabBytes;
-  static constexpr int kRingOff = kPidOff + 4 * kMaxChunkSlabs;
-  static constexpr int kLds = kRingOff + kNbuf * kBuf;
+  // dynamic LDS: page ids, then the slab ring (the centroid table is a
+  // static array, so its address is a compile-time constant)
+  static constexpr int kPidOff = 0;
+  static constexpr int kSrcOff = kPidOff + 4 * kMaxChunkSlabs;
+  static constexpr int kRingOff = kSrcOff + kSrcBytes;
+  static_assert(kLoads <= 4, "load offsets do not fit 16 bytes per lane");
+  static constexpr int kDynLds = kRingOff + kNbuf * kBuf;
+  static constexpr int kLds = kDynLds + kTabBytes;
   static_assert(kLoads * (kNbuf - 2) < 64, "vmcnt out of range");
   static_assert(kVOff + 64 + 4 <= kSlotL, "V part does not fit");
 
@@ -859,11 +883,11 @@ struct PageGeom {
   }
 };
 
-// centroid tables: entry e covers the codes e & (2^KB - 1) and e >> KB, as
-// the pair of hi parts (tab[e]) and the pair of lo parts (tab[kTabLo / 4 + e]);
-// two 4-byte lookups per code byte land directly in the MFMA operand registers
+// centroid table: entry e covers the codes e & (2^KB - 1) and e >> KB as
+// {pair of hi parts, pair of lo parts}: one 8-byte lookup per code byte (a
+// random lookup costs the same LDS time for 4 and 8 bytes)
 template <int KB>
-__device__ __forceinline__ void build_tables_page(const MfmaArgs& a, uint32_t* tab) {
+__device__ __forceinline__ void build_tables_page(const MfmaArgs& a, u32x2* tab) {
   constexpr int kTab = KB == 4 ? 256 : 64;
   for (int e = threadIdx.x; e < kTab; e += blockDim.x) {
     const int c0 = e & ((1 << KB) - 1), c1 = e >> KB;
@@ -871,8 +895,7 @@ __device__ __forceinline__ void build_tables_page(const MfmaArgs& a, uint32_t* t
     const _Float16 h0 = static_cast<_Float16>(v0), h1 = static_cast<_Float16>(v1);
     const _Float16 l0 = static_cast<_Float16>(2.0f * (v0 - static_cast<float>(h0)));
     const _Float16 l1 = static_cast<_Float16>(2.0f * (v1 - static_cast<float>(h1)));
-    tab[e] = pack_h2(h0, h1);
-    tab[kTabLo / 4 + e] = pack_h2(l0, l1);
+    tab[e] = u32x2{pack_h2(h0, h1), pack_h2(l0, l1)};
   }
 }
 
@@ -921,7 +944,7 @@ __device__ __forceinline__ void wave_barrier() { asm volatile("s_barrier" ::: "m
 // operands of its rows; rows at or past valid_rows score -inf
 template <int KB, int SLOT, int H, bool FULL>
 __device__ __forceinline__ void page_scores(const uint8_t* buf, int valid_rows, int w, int r16, int g4,
-                                            const uint32_t* tab, const h8 (&qc)[4],
+                                            const u32x2* tab, const h8 (&qc)[4],
                                             const bf8v (&qb)[4], float scale_log2, bool sel1, bool sel2,
                                             float (&s)[4], uint32_t (&X)[4], uint32_t (&sz)[4]) {
   using Geo = PageGeom<KB, SLOT, H>;
@@ -977,15 +1000,12 @@ __device__ __forceinline__ void page_scores(const uint8_t* buf, int valid_rows, 
           idx[p] = v & 63u;
         }
       }
-      // volatile: two separate 4-byte reads (a merged 8-byte read would land
-      // hi and lo in adjacent registers and cost moves into the operands)
-      typedef __attribute__((address_space(3))) const volatile uint32_t lds_u32;
-      lds_u32* vt = (lds_u32*)(tab);
       u32x4 hi, lo;
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
-        hi[p] = vt[idx[p]];
-        lo[p] = vt[kTabLo / 4 + idx[p]];
+        const u32x2 e = tab[idx[p]];
+        hi[p] = e[0];
+        lo[p] = e[1];
       }
       const h8 chi = __builtin_bit_cast(h8, hi);
       const h8 clo = __builtin_bit_cast(h8, lo);
@@ -993,6 +1013,8 @@ __device__ __forceinline__ void page_scores(const uint8_t* buf, int valid_rows, 
       Slo = __builtin_amdgcn_mfma_f32_16x16x32_f16(clo, qc[kk], Slo, 0, 0, 0);
       N = __builtin_amdgcn_mfma_f32_16x16x32_f16(chi, chi, N, 0, 0, 0);
       N = __builtin_amdgcn_mfma_f32_16x16x32_f16(chi, clo, N, 0, 0, 0);
+      // at most two groups of lookups in flight (registers)
+      if (kk & 1) __builtin_amdgcn_sched_barrier(0);
     }
     // lane (r16, g4) with r16 = 4*g4 + i holds N[4*g4 + i][4*g4 + i] as element i
     const float nd = sel2 ? (sel1 ? N[3] : N[2]) : (sel1 ? N[1] : N[0]);
@@ -1020,7 +1042,8 @@ template <int KB, int SLOT, int H>
 __global__ void __launch_bounds__(64 * H, kPageWavesPerSimd) decode_page_kernel(MfmaArgs a) {
   using Geo = PageGeom<KB, SLOT, H>;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  uint32_t* tab = reinterpret_cast<uint32_t*>(smem + Geo::kTabOff);
+  __shared__ u32x2 s_tab[KB == 8 ? 1 : 256];
+  u32x2* tab = s_tab;
   int32_t* s_pid = reinterpret_cast<int32_t*>(smem + Geo::kPidOff);
 
   const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));   // kv head
@@ -1060,6 +1083,13 @@ __global__ void __launch_bounds__(64 * H, kPageWavesPerSimd) decode_page_kernel(
   uint32_t src_off[Geo::kLoads];
 #pragma unroll
   for (int l = 0; l < Geo::kLoads; ++l) src_off[l] = Geo::chunk_src((w + H * l) * 64 + lane);
+  u32x4* s_src = reinterpret_cast<u32x4*>(smem + Geo::kSrcOff) + threadIdx.x;
+  if constexpr (Geo::kSrcInLds) {
+    u32x4 v = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int l = 0; l < Geo::kLoads; ++l) v[l] = src_off[l];
+    *s_src = v;                              // read back by this lane only
+  }
   // the query loads are done before the first slab is requested, so every
   // wait in the loop counts slab loads only
   wait_vmcnt<0>();
@@ -1076,9 +1106,16 @@ __global__ void __launch_bounds__(64 * H, kPageWavesPerSimd) decode_page_kernel(
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint8_t*>(a.cache) + off, 0, pid >= 0 ? Geo::kSlab : 0, kBufferWord3);
     uint8_t* dst = smem + Geo::kRingOff + (j % Geo::kNbuf) * Geo::kBuf;
+    u32x4 so;
+    if constexpr (Geo::kSrcInLds) {
+      so = *s_src;
+    } else {
+#pragma unroll
+      for (int l = 0; l < Geo::kLoads; ++l) so[l] = src_off[l];
+    }
 #pragma unroll
     for (int l = 0; l < Geo::kLoads; ++l)
-      if (l < Geo::kLoads - 1 || full_loads) lds_dma_16(rs, dst + (w + H * l) * 1024, src_off[l]);
+      if (l < Geo::kLoads - 1 || full_loads) lds_dma_16(rs, dst + (w + H * l) * 1024, so[l]);
   };
 #pragma unroll
   for (int j = 0; j < Geo::kNbuf - 1; ++j) issue(j);
@@ -1134,12 +1171,12 @@ hipError_t launch_page_t(const MfmaArgs& a, int batch, hipStream_t stream) {
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_page_kernel<KB, SLOT, H>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, Geo::kLds);
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, Geo::kDynLds);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
   hipLaunchKernelGGL((decode_page_kernel<KB, SLOT, H>), dim3(batch * a.num_splits), dim3(64 * H),
-                     Geo::kLds, stream, a);
+                     Geo::kDynLds, stream, a);
   return hipGetLastError();
 }
 

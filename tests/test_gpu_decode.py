@@ -180,3 +180,35 @@ def test_decode_full_size_sampled(name):
         want = ors.decode(qb, local, np.arange(npages)[None], np.array([T]), 1)
         worst = max(worst, check_decode(got[b:b + 1, g * G:(g + 1) * G], want, bf16_out=True))
     print(f"[decode full] {name}: sampled {picks}, max abs err {worst:.2e}", flush=True)
+
+
+@pytest.mark.parametrize("preset,page_mse", [("turboquant_k8v4", "0"), ("turboquant_4bit_nc", "1")])
+def test_decode_workspace_reuse_across_shapes(preset, page_mse, monkeypatch):
+    """One context, one workspace, several calls of different batch and
+    length (the workspace is reused as the split count changes): each result
+    matches the oracle."""
+    from packed_cache_decode_amd.runtime import PackedKVCache
+    monkeypatch.setenv("TQ_DECODE_PAGE_MSE", page_mse)
+    seed = 13
+    tq = PackedKVCache(preset, 128, 2, 16, seed)
+    ors = OracleSide(preset, 128, seed)
+    for B, lens, wseed in [(7, (1, 900), 3), (3, (300, 2000), 4), (9, (1, 64), 5), (7, (1, 900), 3)]:
+        w = _wl(preset, G=4, H=2, B=B, lens=lens, seed=wseed)
+        inp = synth.generate(w)
+        cache = np.zeros((inp.num_blocks, 16, 2, ors.lay.slot_size_aligned), np.uint8)
+        ors.store(cache, inp.k, inp.v, inp.slot_mapping)
+        want = ors.decode(inp.q, cache, inp.block_table, inp.seq_lens, 2)
+        out = tq.decode(to_dev(inp.q), to_dev(cache), to_dev(inp.block_table), to_dev(inp.seq_lens),
+                        int(inp.seq_lens.max()), out_fp32=True)
+        torch.cuda.synchronize()
+        check_decode(out.cpu().numpy(), want, bf16_out=False)
+    assert tq.device_error() == 0
+    tq.close()
+
+
+def test_decode_many_short_sequences():
+    """4100 short sequences (0 to 40 tokens): a single token often dominates
+    the softmax, which is where the P.V weights need more than one f16."""
+    w = _wl("turboquant_k8v4", G=1, H=1, B=4100, lens=(0, 40), seed=17)
+    got, want = _decode_from_oracle_cache(w)
+    check_decode(got, want, bf16_out=False)

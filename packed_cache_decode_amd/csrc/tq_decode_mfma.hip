@@ -117,6 +117,15 @@ __device__ __forceinline__ float lane_value(float x, int src_lane) {
   return __int_as_float(__builtin_amdgcn_ds_bpermute(src_lane << 2, __float_as_int(x)));
 }
 
+// Row values to MFMA tile rows without LDS: lane (i, g) = lane 16*g + i holds
+// v_i, significant where g == i >> 2; returns, as element r, v of row
+// 4*g4 + r (the D layout of a 16x16 MFMA).  One 16x16x4 f32 MFMA with
+// A[i][k] = (k == i >> 2 ? v_i : 0) and B = 1, so D[i][j] = v_i exactly.
+__device__ __forceinline__ f4 rows_to_tile(float v, bool diag) {
+  const f4 z = {0.f, 0.f, 0.f, 0.f};
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(diag ? v : 0.0f, 1.0f, z, 0, 0, 0);
+}
+
 // Running state of one wavefront (G query heads of one kv head).
 struct RunState {
   f4 O[8];          // O[h][8*r16 + m]: tile m, rows 4*g4 + r
@@ -414,17 +423,16 @@ __device__ __forceinline__ SlabSoftmax softmax_check(const float (&s)[4], int va
   return r;
 }
 
-__device__ __forceinline__ void softmax_rescale(const SlabSoftmax& sm, int g4, RunState& st) {
+__device__ __forceinline__ void softmax_rescale(const SlabSoftmax& sm, bool diag, RunState& st) {
   const float m_new = fmaxf(st.m_run, max_x32(max_x16(sm.pm)));
   const float corr = __builtin_amdgcn_exp2f(st.m_run - m_new);   // 0 on the first slab
   st.l_part *= corr;
   st.z_part *= corr;
+  const f4 cr = rows_to_tile(corr, diag);       // O rows are heads 4*g4 + r
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const float cr = lane_value(corr, 4 * g4 + r);
+  for (int r = 0; r < 4; ++r)
 #pragma unroll
-    for (int m = 0; m < 8; ++m) st.O[m][r] *= cr;
-  }
+    for (int m = 0; m < 8; ++m) st.O[m][r] *= cr[r];
   st.m_run = m_new;
 }
 
@@ -827,7 +835,9 @@ __global__ void __launch_bounds__(64, kSlabWavesPerSimd<KB>) decode_slab_kernel(
 // ============================================================================
 
 constexpr int kMaxChunkSlabs = 256;          // slabs (and pages) of one split
-constexpr int kPageWavesPerSimd = 4;         // two workgroups of eight wavefronts per CU
+
+// wavefronts per SIMD (128 VGPRs each)
+constexpr int page_waves_per_simd(int) { return 4; }
 
 template <int KB, int SLOT, int H>
 struct PageGeom {
@@ -856,9 +866,10 @@ struct PageGeom {
   static constexpr bool kSrcInLds = KB != 8;
   static constexpr int kSrcBytes = kSrcInLds ? H * 64 * 16 : 0;
   static constexpr int kExtra = kTabBytes + 4 * kMaxChunkSlabs + kSrcBytes;
+  static constexpr int kWavesPerSimd = page_waves_per_simd(KB);
   // workgroups per CU the register budget allows, and as many slab buffers
   // (3 to 8) as their share of the 160 KB of LDS holds
-  static constexpr int kWgsPerCu = 4 * kPageWavesPerSimd / H;
+  static constexpr int kWgsPerCu = 4 * kWavesPerSimd / H;
   static constexpr int kNbufFit = (160 * 1024 / kWgsPerCu - kExtra) / kBuf;
   static constexpr int kNbuf = kNbufFit > 8 ? 8 : (kNbufFit < 3 ? 3 : kNbufFit);
   // dynamic LDS: page ids, then the slab ring (the centroid table is a
@@ -940,106 +951,148 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 __device__ __forceinline__ void wave_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
-// scores (base 2) of this wavefront's head for the slab in buf, and the V
-// operands of its rows; rows at or past valid_rows score -inf
-template <int KB, int SLOT, int H, bool FULL>
-__device__ __forceinline__ void page_scores(const uint8_t* buf, int valid_rows, int w, int r16, int g4,
-                                            const u32x2* tab, const h8 (&qc)[4],
-                                            const bf8v (&qb)[4], float scale_log2, bool sel1, bool sel2,
-                                            float (&s)[4], uint32_t (&X)[4], uint32_t (&sz)[4]) {
+// What one wavefront holds of one slab.  3/4-bit keys: the lane's code words
+// (token r16, coordinates [32*g4, 32*g4 + 32)) and their centroid lookups;
+// FP8 keys: the lane's 32 key bytes.  Both: the norm bits and V operands.
+template <int KB>
+struct SlabRegs {
+  uint32_t kw[KB == 4 ? 4 : 3];  // code words (3/4-bit keys)
+  u32x2 e[KB == 8 ? 1 : 16];     // {hi pair, lo pair} of code byte 4*kk + p
+  u32x4 k8[KB == 8 ? 2 : 1];     // FP8 key bytes
+  uint32_t nb;                   // norm bits of token 4*g4 + (r16 & 3)
+  uint32_t X[4];                 // V codes of token 4*g4 + r, coordinates [8*r16, 8*r16 + 8)
+  uint32_t sz[4];                // V scale | zero of token 4*g4 + r
+};
+
+// the slab's bytes for this lane, from its LDS buffer
+template <int KB, int SLOT, int H>
+__device__ __forceinline__ void slab_read(const uint8_t* buf, int w, int r16, int g4, SlabRegs<KB>& R) {
   using Geo = PageGeom<KB, SLOT, H>;
   constexpr int kRow = Geo::kRowL;
   const uint8_t* hb = buf + w * Geo::kSlotL;              // this head's slot in row 0
   const uint8_t* rb = hb + 4 * g4 * kRow;                 // ... in row 4*g4
   if constexpr (KB == 8) {
     const uint8_t* kp = hb + r16 * kRow + 32 * g4;
-    SlabOps8 op;
-    op.k[0] = *reinterpret_cast<const u32x4*>(kp);
-    op.k[1] = *reinterpret_cast<const u32x4*>(kp + 16);
-    f4 S = {0.f, 0.f, 0.f, 0.f};
+    R.k8[0] = *reinterpret_cast<const u32x4*>(kp);
+    R.k8[1] = *reinterpret_cast<const u32x4*>(kp + 16);
+    R.nb = 0;
+  } else {
+    if constexpr (KB == 4) {
+      const u32x4 t = *reinterpret_cast<const u32x4*>(hb + r16 * kRow + 16 * g4);
+      R.kw[0] = t[0]; R.kw[1] = t[1]; R.kw[2] = t[2]; R.kw[3] = t[3];
+    } else {
+      typedef uint32_t u32x3a __attribute__((ext_vector_type(3), aligned(4)));
+      const u32x3a t = *reinterpret_cast<const u32x3a*>(hb + r16 * kRow + 12 * g4);
+      R.kw[0] = t[0]; R.kw[1] = t[1]; R.kw[2] = t[2];
+    }
+    // norm of token 4*g4 + (r16 & 3): only the lanes that hold its diagonal
+    // element use it
+    R.nb = *reinterpret_cast<const uint16_t*>(hb + (4 * g4 + (r16 & 3)) * kRow + Geo::kKCB);
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    R.X[r] = *reinterpret_cast<const uint32_t*>(rb + r * kRow + Geo::kVOff + 4 * r16);
+    R.sz[r] = *reinterpret_cast<const uint32_t*>(rb + r * kRow + Geo::kVOff + kD / 2);
+  }
+}
+
+// centroid lookups of the code words (3/4-bit keys)
+template <int KB>
+__device__ __forceinline__ void slab_lookup(const u32x2* tab, SlabRegs<KB>& R) {
+  if constexpr (KB != 8) {
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        uint32_t idx;
+        if constexpr (KB == 4) {
+          idx = (R.kw[kk] >> (8 * p)) & 0xFFu;
+        } else {
+          // 6 bits (two codes) per lookup: bits [24*kk + 6*p, +6) of the lane's 96
+          const int bit = 24 * kk + 6 * p;
+          const int wd = bit >> 5, o = bit & 31;
+          uint32_t v = R.kw[wd] >> o;
+          if (o > 26) v |= R.kw[wd + 1] << (32 - o);
+          idx = v & 63u;
+        }
+        R.e[4 * kk + p] = tab[idx];
+      }
+  }
+}
+
+// score and norm MFMAs of one slab: S = C . [qhi | qlo], Slo = Clo . [qhi | qlo],
+// N = Chi . Chi^T + Chi . Clo^T (the norm accumulator starts at the 1e-16 of
+// the correction's denominator); FP8 keys: S = K . q only
+struct ScoreAcc {
+  f4 S, Slo, Nh, Nx;
+};
+
+template <int KB>
+__device__ __forceinline__ ScoreAcc slab_mfma(const SlabRegs<KB>& R, const h8 (&qc)[4], const bf8v (&qb)[4]) {
+  ScoreAcc A;
+  A.S = f4{0.f, 0.f, 0.f, 0.f};
+  if constexpr (KB == 8) {
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-      const uint32_t w0 = op.k[kk >> 1][2 * (kk & 1)], w1 = op.k[kk >> 1][2 * (kk & 1) + 1];
+      const uint32_t w0 = R.k8[kk >> 1][2 * (kk & 1)], w1 = R.k8[kk >> 1][2 * (kk & 1) + 1];
       const bf2 c0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false);
       const bf2 c1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true);
       const bf2 c2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false);
       const bf2 c3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true);
       const bf8v av = {c0[0], c0[1], c1[0], c1[1], c2[0], c2[1], c3[0], c3[1]};
-      S = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, qb[kk], S, 0, 0, 0);
+      A.S = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, qb[kk], A.S, 0, 0, 0);
     }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) s[r] = (FULL || 4 * g4 + r < valid_rows) ? S[r] * scale_log2 : -INFINITY;
   } else {
-    uint32_t kw[KB == 4 ? 4 : 3];
-    if constexpr (KB == 4) {
-      const u32x4 t = *reinterpret_cast<const u32x4*>(hb + r16 * kRow + 16 * g4);
-      kw[0] = t[0]; kw[1] = t[1]; kw[2] = t[2]; kw[3] = t[3];
-    } else {
-      typedef uint32_t u32x3a __attribute__((ext_vector_type(3), aligned(4)));
-      const u32x3a t = *reinterpret_cast<const u32x3a*>(hb + r16 * kRow + 12 * g4);
-      kw[0] = t[0]; kw[1] = t[1]; kw[2] = t[2];
-    }
-    // norm of token 4*g4 + (r16 & 3): only the lanes that hold its diagonal
-    // element use it
-    const uint32_t nb = *reinterpret_cast<const uint16_t*>(hb + (4 * g4 + (r16 & 3)) * kRow + Geo::kKCB);
-    f4 S = {0.f, 0.f, 0.f, 0.f}, Slo = {0.f, 0.f, 0.f, 0.f};
-    f4 N = {1e-16f, 1e-16f, 1e-16f, 1e-16f};
+    A.Slo = f4{0.f, 0.f, 0.f, 0.f};
+    A.Nh = f4{1e-16f, 1e-16f, 1e-16f, 1e-16f};
+    A.Nx = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-      uint32_t idx[4];
-      if constexpr (KB == 4) {
-#pragma unroll
-        for (int p = 0; p < 4; ++p) idx[p] = (kw[kk] >> (8 * p)) & 0xFFu;
-      } else {
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          const int bit = 24 * kk + 6 * p;
-          const int wd = bit >> 5, o = bit & 31;
-          uint32_t v = kw[wd] >> o;
-          if (o > 26) v |= kw[wd + 1] << (32 - o);
-          idx[p] = v & 63u;
-        }
-      }
       u32x4 hi, lo;
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
-        const u32x2 e = tab[idx[p]];
-        hi[p] = e[0];
-        lo[p] = e[1];
+        hi[p] = R.e[4 * kk + p][0];
+        lo[p] = R.e[4 * kk + p][1];
       }
       const h8 chi = __builtin_bit_cast(h8, hi);
       const h8 clo = __builtin_bit_cast(h8, lo);
-      S = __builtin_amdgcn_mfma_f32_16x16x32_f16(chi, qc[kk], S, 0, 0, 0);
-      Slo = __builtin_amdgcn_mfma_f32_16x16x32_f16(clo, qc[kk], Slo, 0, 0, 0);
-      N = __builtin_amdgcn_mfma_f32_16x16x32_f16(chi, chi, N, 0, 0, 0);
-      N = __builtin_amdgcn_mfma_f32_16x16x32_f16(chi, clo, N, 0, 0, 0);
-      // at most two groups of lookups in flight (registers)
-      if (kk & 1) __builtin_amdgcn_sched_barrier(0);
-    }
-    // lane (r16, g4) with r16 = 4*g4 + i holds N[4*g4 + i][4*g4 + i] as element i
-    const float nd = sel2 ? (sel1 ? N[3] : N[2]) : (sel1 ? N[1] : N[0]);
-    const float fq = f16_bits_to_f32(nb) * __builtin_amdgcn_rsqf(nd);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float fac = lane_value(fq, 20 * g4 + r);
-      // column h + 8 (row rotation by 8) holds hi.qlo of head h; lanes
-      // r16 >= 8 get a copy of head r16 - 8's score, which is never stored
-      const float sr = S[r];
-      const float other = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(sr), 0x128, 0xF, 0xF, false));
-      s[r] = (FULL || 4 * g4 + r < valid_rows) ? (S[r] + other + 0.5f * Slo[r]) * fac : -INFINITY;
+      A.S = __builtin_amdgcn_mfma_f32_16x16x32_f16(chi, qc[kk], A.S, 0, 0, 0);
+      A.Slo = __builtin_amdgcn_mfma_f32_16x16x32_f16(clo, qc[kk], A.Slo, 0, 0, 0);
+      A.Nh = __builtin_amdgcn_mfma_f32_16x16x32_f16(chi, chi, A.Nh, 0, 0, 0);
+      A.Nx = __builtin_amdgcn_mfma_f32_16x16x32_f16(chi, clo, A.Nx, 0, 0, 0);
     }
   }
-  // the V operands are read after the scores (fewer registers live at once)
-  __builtin_amdgcn_sched_barrier(0);
+  return A;
+}
+
+// scores (base 2) of the slab from its MFMA results; rows at or past
+// valid_rows score -inf
+template <int KB, bool FULL>
+__device__ __forceinline__ void slab_tail(const SlabRegs<KB>& R, const ScoreAcc& A, int valid_rows, int g4,
+                                          float scale_log2, bool sel1, bool sel2, bool diag, float (&s)[4]) {
+  if constexpr (KB == 8) {
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    X[r] = *reinterpret_cast<const uint32_t*>(rb + r * kRow + Geo::kVOff + 4 * r16);
-    sz[r] = *reinterpret_cast<const uint32_t*>(rb + r * kRow + Geo::kVOff + kD / 2);
+    for (int r = 0; r < 4; ++r) s[r] = (FULL || 4 * g4 + r < valid_rows) ? A.S[r] * scale_log2 : -INFINITY;
+  } else {
+    // lane (r16, g4) with r16 = 4*g4 + i holds N[4*g4 + i][4*g4 + i] as element i
+    const float n0 = A.Nh[0] + A.Nx[0], n1 = A.Nh[1] + A.Nx[1];
+    const float n2 = A.Nh[2] + A.Nx[2], n3 = A.Nh[3] + A.Nx[3];
+    const float nd = sel2 ? (sel1 ? n3 : n2) : (sel1 ? n1 : n0);
+    const float fq = f16_bits_to_f32(R.nb) * __builtin_amdgcn_rsqf(nd);
+    const f4 fac = rows_to_tile(fq, diag);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      // column h + 8 (row rotation by 8) holds hi.qlo of head h; lanes
+      // r16 >= 8 get a copy of head r16 - 8's score, which is never stored
+      const float sr = A.S[r];
+      const float other = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(sr), 0x128, 0xF, 0xF, false));
+      s[r] = (FULL || 4 * g4 + r < valid_rows) ? (sr + other + 0.5f * A.Slo[r]) * fac[r] : -INFINITY;
+    }
   }
 }
 
 template <int KB, int SLOT, int H>
-__global__ void __launch_bounds__(64 * H, kPageWavesPerSimd) decode_page_kernel(MfmaArgs a) {
+__global__ void __launch_bounds__(64 * H, page_waves_per_simd(KB)) decode_page_kernel(MfmaArgs a) {
   using Geo = PageGeom<KB, SLOT, H>;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   __shared__ u32x2 s_tab[KB == 8 ? 1 : 256];
@@ -1120,45 +1173,58 @@ __global__ void __launch_bounds__(64 * H, kPageWavesPerSimd) decode_page_kernel(
 #pragma unroll
   for (int j = 0; j < Geo::kNbuf - 1; ++j) issue(j);
 
-  // The inner loop never changes the accumulators except through the P.V
-  // MFMAs; a slab that raises a head's running max past the lazy threshold
-  // leaves it, and the rescale and that slab's P.V happen outside.
+  // With slabs 0 .. i + kNbuf - 2 requested: this wavefront's part of slab i
+  // has landed (the kNbuf - 2 newer ones may be in flight), its LDS reads
+  // have completed, and the workgroup meets, so slab i is whole in LDS and
+  // the buffer of slab i - 1 (read before the barrier) may be refilled.
+  auto sync_slab = [&]() {
+    if (full_loads)
+      wait_vmcnt<Geo::kLoads * (Geo::kNbuf - 2)>();
+    else
+      wait_vmcnt<(Geo::kLoads - 1) * (Geo::kNbuf - 2)>();
+    // lgkmcnt(0) as a builtin, so the compiler knows every LDS read has
+    // completed and inserts no waits of its own for them later
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    wave_barrier();
+  };
+  auto slab_buf = [&](int jj) { return smem + Geo::kRingOff + (jj % Geo::kNbuf) * Geo::kBuf; };
+  auto page_of = [&](int jj) { return s_pid[((t0 + 16 * jj) >> a.bs_shift) - p_first]; };
+  const bool diag = (r16 >> 2) == g4;
+
+  // Slab j is read and computed in iteration j.  The inner loop never changes
+  // the accumulators except through the P.V MFMAs; a slab that raises the
+  // running max past the lazy threshold leaves it, and the rescale and that
+  // slab's P.V happen outside.
   int j = 0;
   while (true) {
     float s[4];
-    uint32_t X[4], sz[4];
     SlabSoftmax sm;
+    SlabRegs<KB> c;
     bool grow = false;
     for (; j < n_slabs; ++j) {
-      // this wavefront's part of slab j has landed: slabs j+1 .. j+kNbuf-2
-      // may still be in flight
-      if (full_loads)
-        wait_vmcnt<Geo::kLoads * (Geo::kNbuf - 2)>();
-      else
-        wait_vmcnt<(Geo::kLoads - 1) * (Geo::kNbuf - 2)>();
-      wave_barrier();                        // every part of slab j landed; slab j-1 is consumed
-      issue(j + Geo::kNbuf - 1);             // into the buffer of slab j-1
-      const int t = t0 + 16 * j;
-      const int pid = s_pid[(t >> a.bs_shift) - p_first];
-      if (__builtin_amdgcn_readfirstlane(pid) < 0) continue;
-      const uint8_t* buf = smem + Geo::kRingOff + (j % Geo::kNbuf) * Geo::kBuf;
-      const int valid = t1 - t;
+      sync_slab();
+      issue(j + Geo::kNbuf - 1);           // into the buffer of slab j - 1
+      if (__builtin_amdgcn_readfirstlane(page_of(j)) < 0) continue;
+      slab_read<KB, SLOT, H>(slab_buf(j), w, r16, g4, c);
+      slab_lookup<KB>(tab, c);
+      const ScoreAcc acc = slab_mfma<KB>(c, qc, qb);
+      const int valid = t1 - (t0 + 16 * j);
       if (valid >= 16) {
-        page_scores<KB, SLOT, H, true>(buf, 16, w, r16, g4, tab, qc, qb, a.scale_log2, sel1, sel2, s, X, sz);
-        sm = softmax_check<true>(s, 16, sz, g4, st);
+        slab_tail<KB, true>(c, acc, 16, g4, a.scale_log2, sel1, sel2, diag, s);
+        sm = softmax_check<true>(s, 16, c.sz, g4, st);
       } else {
-        page_scores<KB, SLOT, H, false>(buf, valid, w, r16, g4, tab, qc, qb, a.scale_log2, sel1, sel2, s, X, sz);
-        sm = softmax_check<false>(s, valid, sz, g4, st);
+        slab_tail<KB, false>(c, acc, valid, g4, a.scale_log2, sel1, sel2, diag, s);
+        sm = softmax_check<false>(s, valid, c.sz, g4, st);
       }
       if (sm.grow) {
         grow = true;
         break;
       }
-      softmax_accumulate(s, sm, X, st);
+      softmax_accumulate(s, sm, c.X, st);
     }
     if (!grow) break;
-    softmax_rescale(sm, g4, st);
-    softmax_accumulate(s, sm, X, st);
+    softmax_rescale(sm, diag, st);
+    softmax_accumulate(s, sm, c.X, st);
     ++j;
   }
   wait_vmcnt<0>();                           // no load may still write LDS at exit
@@ -1220,7 +1286,7 @@ int page_wgs_per_cu(const Geometry& g) {
   TQ_PAGE_LDS(8, 196) TQ_PAGE_LDS(4, 134) TQ_PAGE_LDS(3, 118)
 #undef TQ_PAGE_LDS
   int n = lds > 0 ? (160 * 1024) / lds : 1;
-  const int by_regs = 4 * kPageWavesPerSimd / H;
+  const int by_regs = 4 * page_waves_per_simd(g.key_bits) / H;
   if (n > by_regs) n = by_regs;
   return n < 1 ? 1 : n;
 }

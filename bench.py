@@ -19,6 +19,7 @@ over the K timed steps.  The store's tokens/s comes from the same steps.
 """
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -28,6 +29,40 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+
+# kernel sources whose counter-measured HBM traffic profiles/ records
+KERNEL_SOURCES = {
+    "decode": ("packed_cache_decode_amd/csrc/tq_decode.hip", "packed_cache_decode_amd/csrc/tq_decode_mfma.hip",
+               "packed_cache_decode_amd/csrc/tq_internal.h"),
+    "store": ("packed_cache_decode_amd/csrc/tq_store.hip", "packed_cache_decode_amd/csrc/tq_internal.h"),
+}
+
+
+def sources_sha256(kind):
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES[kind]:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def counted_traffic(kind, workload):
+    """HBM bytes per launch of the store or decode on `workload`, as rocprofv3's
+    FETCH_SIZE + WRITE_SIZE counters read them (calibrated against plain
+    streaming kernels of known size), from the summary under profiles/; None
+    when there is no summary taken on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kind}_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    rec = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.lstrip().startswith("#"):
+                k, v = line.split(":", 1)
+                rec[k.strip()] = v.strip()
+    if rec.get("kernel_sources_sha256") != sources_sha256(kind) or "hbm_bytes_per_launch" not in rec:
+        return None
+    return int(float(rec["hbm_bytes_per_launch"]))
 
 
 def decode_alg_bytes(inp, slot):
@@ -233,12 +268,15 @@ def main():
         "store_tokens_per_s": round(n_tok / t_store.mean(), 1),
         "store_us": round(t_store.mean() * 1e6, 2),
         "roofline": {"bound": "hbm", "achieved": round(dec_gbs, 2), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "tq_decode (split + combine)", "alg_bytes_per_launch": dec_bytes},
+                     "unit": "GB/s", "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": counted_traffic("decode", w.name),
+                     "kernel": "tq_decode (split kernel + merge kernel)",
+                     "alg_bytes_per_launch": dec_bytes},
         "roofline_store": {"bound": "hbm", "achieved": round(st_gbs, 2), "peak": HBM_PEAK_GBS,
                            "unit": "GB/s", "frac": round(st_gbs / HBM_PEAK_GBS, 4),
-                           "traffic": None, "kernel": "tq_store",
+                           "traffic": counted_traffic("store", w.name), "kernel": "tq_store",
                            "alg_bytes_per_launch": st_bytes},
+        "kernel_sources_sha256": {k: sources_sha256(k) for k in KERNEL_SOURCES},
         "wall_ms_per_step_incl_flush": round(wall / args.steps * 1e3, 3),
         "hbm_probe": hbm_probe,
     }

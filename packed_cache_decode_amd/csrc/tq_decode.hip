@@ -19,6 +19,7 @@
 //   Partials per (sequence, q head, split): acc[d], running max m (base 2),
 //   running sum l.  The combine weights split s by 2^(m_s - max m).
 #include <cstdlib>
+#include <string>
 
 #include "tq_internal.h"
 
@@ -365,11 +366,15 @@ hipError_t launch_g(const DecodeArgs& a, int G, int batch, hipStream_t stream) {
 
 DecodePlan plan_decode(const Geometry& g, int batch, int num_q_heads, int max_seq_len) {
   DecodePlan p;
-  // TQ_DECODE_PAGE_MSE=1 selects the page-cooperative kernel for 3/4-bit keys
-  // as well (for tests and measurements of that path)
-  const char* env = getenv("TQ_DECODE_PAGE_MSE");
-  const bool page_mse = env != nullptr && env[0] == '1';
-  if (page_decode_eligible(g, num_q_heads, page_mse)) {
+  // Matrix-core kernel by key type (measured on the llama3-, k3v4- and
+  // k8v4-shaped decodes): FP8 keys take the page-cooperative kernel, 4-bit
+  // keys with an even number of kv heads the staged kernel, the rest the
+  // direct one.  TQ_DECODE_KERNEL=page|staged|direct forces one where it
+  // applies (for tests and measurements of each path).
+  const char* env = getenv("TQ_DECODE_KERNEL");
+  const std::string force = env != nullptr ? env : "";
+  const bool auto_pick = force != "page" && force != "staged" && force != "direct";
+  if ((auto_pick || force == "page") && page_decode_eligible(g, num_q_heads, force == "page")) {
     // one resident round of workgroups (256 CUs x the workgroups that fit per
     // CU) over (sequence, split), at least 4 slabs of 16 tokens per split so
     // the load pipeline's start is amortised
@@ -392,11 +397,13 @@ DecodePlan plan_decode(const Geometry& g, int batch, int num_q_heads, int max_se
     // per split so the per-wavefront set-up is amortised
     const int slabs = max_seq_len > 0 ? (max_seq_len + 15) / 16 : 1;
     const int per_split = batch * g.num_kv_heads;
-    const int target = 256 * mfma_waves_per_cu(g);
+    const bool staged = staged_decode_eligible(g, num_q_heads) &&
+                        (force == "staged" || (auto_pick && g.key_bits == 4));
+    const int target = 256 * mfma_waves_per_cu(g, staged);
     int s = per_split > 0 ? (target + per_split - 1) / per_split : 1;
     const int s_max = (slabs + 7) / 8;
     s = s < 1 ? 1 : (s > s_max ? s_max : s);
-    p.mfma = 1;
+    p.mfma = staged ? 3 : 1;
     p.chunk = 16 * ((slabs + s - 1) / s);
     if (p.chunk > 16 * 256) p.chunk = 16 * 256;       // page offsets of a split fit in LDS
     p.num_splits = max_seq_len > 0 ? (max_seq_len + p.chunk - 1) / p.chunk : 1;

@@ -387,12 +387,13 @@ __device__ __forceinline__ void softmax_pv(const float (&s)[4], int valid_rows, 
     lo23 -= b1024;
     hi01 -= b64;
     hi23 -= b64;
-    const h4 Blo = {lo01[0], lo01[1], lo23[0], lo23[1]};
-    const h4 Bhi = {hi01[0], hi01[1], hi23[0], hi23[1]};
-    st.O[2 * kb] = __builtin_amdgcn_mfma_f32_16x16x16f16(W, Blo, st.O[2 * kb], 0, 0, 0);
-    st.O[2 * kb + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(W, Bhi, st.O[2 * kb + 1], 0, 0, 0);
-    st.O[2 * kb] = __builtin_amdgcn_mfma_f32_16x16x16f16(Wl, Blo, st.O[2 * kb], 0, 0, 0);
-    st.O[2 * kb + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(Wl, Bhi, st.O[2 * kb + 1], 0, 0, 0);
+    // one K = 32 product per tile: W and Wl of tokens 4*g4 + r meet the
+    // same codes, listed twice
+    const h8 Blo = {lo01[0], lo01[1], lo23[0], lo23[1], lo01[0], lo01[1], lo23[0], lo23[1]};
+    const h8 Bhi = {hi01[0], hi01[1], hi23[0], hi23[1], hi01[0], hi01[1], hi23[0], hi23[1]};
+    const h8 Ws = {W[0], W[1], W[2], W[3], Wl[0], Wl[1], Wl[2], Wl[3]};
+    st.O[2 * kb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ws, Blo, st.O[2 * kb], 0, 0, 0);
+    st.O[2 * kb + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ws, Bhi, st.O[2 * kb + 1], 0, 0, 0);
   }
 }
 
@@ -813,6 +814,211 @@ __global__ void __launch_bounds__(64, kSlabWavesPerSimd<KB>) decode_slab_kernel(
   store_partials(a, b, g, split, g4, r16, st);
 }
 
+
+// ============================================================================
+// staged: one wavefront per (split, sequence, kv head) loads its head's span
+// of the 16 rows of a slab with 16-byte buffer loads (whole, aligned chunks,
+// three per lane) two slabs ahead in registers, parks the slab in a private
+// LDS buffer and takes its operands from there.  3/4-bit keys with an even
+// number of kv heads (every row then starts 4-byte aligned).
+// ============================================================================
+
+// A wavefront's bytes of one row: from its slot start rounded down to 4 to
+// its slot end rounded up to 4 (136 bytes for 134-byte slots, 120 for 118),
+// fetched as 16-byte chunks plus one 8- or 4-byte tail, never past the slot
+// end rounded up to 4 (the last head's slot ends the row, the last row the
+// page).
+template <int SLOT>
+struct StageShape {
+  static constexpr int kSpan = SLOT % 4 == 0 ? SLOT : SLOT + 2;   // bytes fetched per row
+  static constexpr int kTail = kSpan % 16;             // 4 or 8
+  static_assert(kTail == 4 || kTail == 8, "row span must be 16-byte chunks plus 4 or 8");
+  static constexpr int kC16 = (kSpan - kTail) / 16;    // 16-byte chunks per row
+  static constexpr int kRow = 16 * (kC16 + 1);         // LDS bytes per row (16-aligned)
+  static constexpr int kStage = 16 * kRow;             // LDS bytes per slab
+  static constexpr int kChunks = 16 * kC16;            // 16-byte chunks per slab
+  static constexpr int kLoads16 = (kChunks + 63) / 64; // 16-byte loads per lane
+};
+
+template <int SLOT>
+struct StageRegs {
+  u32x4 d[StageShape<SLOT>::kLoads16];
+  u32x2 tail;                                          // lanes 0..15: the row's last 4 or 8 bytes
+  bool ok;                                             // a real slab (else an empty load)
+};
+
+// Per-lane byte offsets (from a slab's first row) of the lane's 16-byte
+// chunks and its tail; lanes without a chunk of their own re-read the last
+// one and lanes 16..63 re-read a tail, so every lane issues the same loads.
+template <int SLOT>
+struct StageOffsets {
+  uint32_t d[StageShape<SLOT>::kLoads16];
+  uint32_t tail;
+};
+
+template <int SLOT>
+__device__ __forceinline__ StageOffsets<SLOT> stage_offsets(int lane, uint32_t head_off4, uint32_t rb) {
+  using S = StageShape<SLOT>;
+  StageOffsets<SLOT> o;
+#pragma unroll
+  for (int j = 0; j < S::kLoads16; ++j) {
+    int c = lane + 64 * j;
+    if (c >= S::kChunks) c = S::kChunks - 1;
+    const int row = c / S::kC16, cc = c - row * S::kC16;
+    o.d[j] = row * rb + head_off4 + 16u * cc;
+  }
+  o.tail = (lane & 15) * rb + head_off4 + 16u * S::kC16;
+  return o;
+}
+
+// cache policy of the slab loads: default (non-temporal loads measured no
+// faster here, unlike the page kernel's loads into LDS)
+constexpr int kStageLoadAux = 0;
+
+template <int SLOT>
+__device__ __forceinline__ void stage_load(__amdgpu_buffer_rsrc_t rs, const StageOffsets<SLOT>& o,
+                                           StageRegs<SLOT>& sr) {
+  using S = StageShape<SLOT>;
+#pragma unroll
+  for (int j = 0; j < S::kLoads16; ++j)
+    sr.d[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, o.d[j], 0, kStageLoadAux));
+  if constexpr (S::kTail == 8)
+    sr.tail = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, o.tail, 0, kStageLoadAux));
+  else
+    sr.tail[0] = __builtin_amdgcn_raw_buffer_load_b32(rs, o.tail, 0, kStageLoadAux);
+}
+
+template <int SLOT>
+__device__ __forceinline__ void stage_store(uint8_t* lds, int lane, const StageRegs<SLOT>& sr) {
+  using S = StageShape<SLOT>;
+#pragma unroll
+  for (int j = 0; j < S::kLoads16; ++j) {
+    const int c = lane + 64 * j;
+    if (S::kChunks % 64 == 0 || c < S::kChunks) {
+      const int row = c / S::kC16, cc = c - row * S::kC16;
+      *reinterpret_cast<u32x4*>(lds + row * S::kRow + 16 * cc) = sr.d[j];
+    }
+  }
+  if (lane < 16) {
+    if constexpr (S::kTail == 8)
+      *reinterpret_cast<u32x2*>(lds + lane * S::kRow + 16 * S::kC16) = sr.tail;
+    else
+      *reinterpret_cast<uint32_t*>(lds + lane * S::kRow + 16 * S::kC16) = sr.tail[0];
+  }
+}
+
+// operands of one lane from the LDS copy of the slab (slot of row t at
+// t * kRow + sh, sh = 0 or 2; reads stay inside the fetched span)
+template <int KB, int SLOT>
+__device__ __forceinline__ SlabOps<KB> staged_ops(const uint8_t* lds, int r16, int g4, uint32_t sh) {
+  using S = StageShape<SLOT>;
+  constexpr int kKCB = (kD * KB) / 8;
+  constexpr int kKP = kKCB + 2;
+  constexpr int kVCB = kD / 2;
+  constexpr int kLaneKB = KB == 4 ? 16 : 12;
+  SlabOps<KB> op;
+  {
+    const uint32_t o = r16 * S::kRow + sh + kLaneKB * g4;
+    const uint32_t* p = reinterpret_cast<const uint32_t*>(lds + (o & ~3u));
+    uint32_t w[kLaneKB / 4 + 1];
+#pragma unroll
+    for (int i = 0; i < kLaneKB / 4 + 1; ++i) w[i] = p[i];
+#pragma unroll
+    for (int i = 0; i < kLaneKB / 4; ++i) op.kw[i] = __builtin_amdgcn_alignbyte(w[i + 1], w[i], o & 3u);
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const uint32_t rowo = (4 * g4 + r) * S::kRow + sh;
+    const uint32_t vo = rowo + kKP + 4 * r16;
+    const uint32_t* pv = reinterpret_cast<const uint32_t*>(lds + (vo & ~3u));
+    op.X[r] = __builtin_amdgcn_alignbyte(pv[1], pv[0], vo & 3u);
+    op.n[r] = *reinterpret_cast<const uint16_t*>(lds + rowo + kKCB);
+    const uint32_t so = rowo + kKP + kVCB;
+    const uint32_t* ps = reinterpret_cast<const uint32_t*>(lds + (so & ~3u));
+    op.sz[r] = __builtin_amdgcn_alignbyte(ps[1], ps[0], so & 3u);
+  }
+  return op;
+}
+
+// resident wavefronts per SIMD the staged kernel is built for (its register
+// budget: 512 / waves)
+template <int KB>
+constexpr int kStagedWavesPerSimd = KB == 4 ? 3 : 2;
+
+template <int KB, int SLOT>
+__global__ void __launch_bounds__(64, kStagedWavesPerSimd<KB>) decode_staged_kernel(MfmaArgs a) {
+  using S = StageShape<SLOT>;
+  static_assert(KB == 3 || KB == 4, "staged kernel: 3/4-bit keys");
+
+  __shared__ u32x2 s_tab[256];
+  __shared__ int64_t s_page_off[kMaxChunkPages];
+  __shared__ __align__(16) uint8_t s_stage[S::kStage + 16];
+
+  const int lane = threadIdx.x;
+  const int r16 = lane & 15;
+  const int g4 = lane >> 4;
+  // items in launch order, split fastest (measured faster for this kernel
+  // than the direct kernel's XCD-aware order)
+  const int n_items = a.num_splits * a.batch * a.H;
+  const int item = blockIdx.x;
+  if (item >= n_items) return;
+  const int split = item % a.num_splits;
+  const int b = (item / a.num_splits) % a.batch;
+  const int g = item / (a.num_splits * a.batch);   // kv head
+  const int64_t row_bytes = static_cast<int64_t>(a.H) * SLOT;
+  const int64_t page_bytes = static_cast<int64_t>(1 << a.bs_shift) * row_bytes;
+
+  build_tables<KB>(a, s_tab);
+  const int T = clamp_len(a, b, split, g);
+  const int t0 = split * a.chunk;
+  const int t1 = min(T, t0 + a.chunk);
+  stage_page_offsets(a, b, t0, t1, page_bytes, s_page_off);
+  __syncthreads();
+  if (t0 >= t1) return;
+
+  h8 qhi[4], qlo[4];
+  load_queries(a, b, g, r16, g4, a.scale_log2, qhi, qlo);
+  const uint32_t rb = static_cast<uint32_t>(row_bytes);
+  const uint32_t head_off = static_cast<uint32_t>(g * SLOT);
+  const uint32_t head_off4 = head_off & ~3u;   // rows start 4-aligned (H even)
+  const uint32_t sh = head_off & 3u;
+  RunState st;
+#pragma unroll
+  for (int m = 0; m < 8; ++m) st.O[m] = f4{0.f, 0.f, 0.f, 0.f};
+  st.m_run = -INFINITY;
+  st.l_part = 0.0f;
+  st.z_part = 0.0f;
+  const int p_first = t0 >> a.bs_shift;
+  // One LDS buffer suffices: a wavefront's LDS accesses complete in issue
+  // order, so the next slab's writes never overtake this slab's reads.
+  uint8_t* lds = s_stage;
+  const StageOffsets<SLOT> so = stage_offsets<SLOT>(lane, head_off4, rb);
+
+  // two slabs in flight in registers
+  StageRegs<SLOT> r0, r1;
+  auto load = [&](int t, StageRegs<SLOT>& r) {
+    bool ok;
+    const __amdgpu_buffer_rsrc_t rs = slab_rsrc(a, s_page_off, p_first, t, t1, row_bytes, ok);
+    r.ok = ok;
+    stage_load<SLOT>(rs, so, r);
+  };
+  auto step = [&](int t, StageRegs<SLOT>& r) {
+    // slab t is in r: park it in LDS, refill r with slab t + 32, compute slab t
+    const bool ok = r.ok;
+    stage_store<SLOT>(lds, lane, r);
+    load(t + 32, r);
+    if (ok) process_slab<KB>(staged_ops<KB, SLOT>(lds, r16, g4, sh), t1 - t, s_tab, qhi, qlo, g4, st);
+  };
+  load(t0, r0);
+  load(t0 + 16, r1);
+  // whole rounds of two steps, no early exit: a step past the split end only
+  // issues empty loads, which keeps the load count per step fixed
+  for (int t = t0; t < t1; t += 32) {
+    step(t, r0);
+    step(t + 16, r1);
+  }
+  store_partials(a, b, g, split, g4, r16, st);
+}
 
 // ============================================================================
 // page: one workgroup per (sequence, split), one wavefront per kv head (H = 1,
@@ -1259,10 +1465,16 @@ hipError_t launch_page_h(const MfmaArgs& a, int batch, hipStream_t stream) {
 
 }  // namespace
 
-int mfma_waves_per_cu(const Geometry& g) {
+int mfma_waves_per_cu(const Geometry& g, bool staged) {
+  if (staged) return 4 * (g.key_bits == 4 ? kStagedWavesPerSimd<4> : kStagedWavesPerSimd<3>);
   const int per_simd = g.key_bits == 8 ? kSlabWavesPerSimd<8>
                      : (g.key_bits == 4 ? kSlabWavesPerSimd<4> : kSlabWavesPerSimd<3>);
   return 4 * per_simd;
+}
+
+bool staged_decode_eligible(const Geometry& g, int num_q_heads) {
+  return mfma_decode_eligible(g, num_q_heads) && (g.key_bits == 4 || g.key_bits == 3) &&
+         g.num_kv_heads % 2 == 0;
 }
 
 bool page_decode_eligible(const Geometry& g, int num_q_heads, bool mse_keys_too) {
@@ -1337,7 +1549,12 @@ hipError_t launch_decode_mfma(const Geometry& g, const DevTables* tables, const 
   // one wavefront per workgroup: (split, sequence, kv head)
   const int n_items = plan.num_splits * batch * g.num_kv_heads;
   const dim3 grid(8 * ((n_items + 7) / 8));
-  if (g.key_bits == 8)
+  if (plan.mfma == 3) {
+    if (g.key_bits == 4)
+      hipLaunchKernelGGL((decode_staged_kernel<4, 134>), grid, dim3(64), 0, stream, a);
+    else
+      hipLaunchKernelGGL((decode_staged_kernel<3, 118>), grid, dim3(64), 0, stream, a);
+  } else if (g.key_bits == 8)
     hipLaunchKernelGGL((decode_slab_kernel<8, 196>), grid, dim3(64), 0, stream, a);
   else if (g.key_bits == 4)
     hipLaunchKernelGGL((decode_slab_kernel<4, 134>), grid, dim3(64), 0, stream, a);

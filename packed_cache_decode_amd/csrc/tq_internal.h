@@ -63,8 +63,8 @@ hipError_t launch_store(const Geometry& g, const DevTables* tables, const uint16
                         hipStream_t stream);
 
 struct DecodePlan {
-  int mfma;         // 2: page-cooperative matrix-core kernel, 1: per-head matrix-core
-                    // kernel (both tq_decode_mfma.hip), 0: general kernel
+  int mfma;         // matrix-core kernels (tq_decode_mfma.hip): 2 page-cooperative,
+                    // 3 staged per-head, 1 direct per-head; 0: general kernel
   int chunk;        // tokens per split
   int num_splits;   // splits per sequence (grid extent)
   size_t workspace_bytes;
@@ -73,7 +73,8 @@ struct DecodePlan {
 bool mfma_decode_eligible(const Geometry& g, int num_q_heads);
 bool page_decode_eligible(const Geometry& g, int num_q_heads, bool mse_keys_too);
 int page_wgs_per_cu(const Geometry& g);
-int mfma_waves_per_cu(const Geometry& g);
+bool staged_decode_eligible(const Geometry& g, int num_q_heads);
+int mfma_waves_per_cu(const Geometry& g, bool staged);
 size_t mfma_partial_bytes(int batch, int num_q_heads, int num_splits);
 hipError_t launch_decode_mfma(const Geometry& g, const DevTables* tables, const DecodePlan& plan,
                               const uint16_t* q, const uint8_t* cache, int64_t num_blocks,

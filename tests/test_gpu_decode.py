@@ -68,20 +68,25 @@ def test_decode_per_head_kernel_shapes(preset, G, H):
     check_decode(got, want, bf16_out=False)
 
 
+# TQ_DECODE_KERNEL forces one matrix-core kernel where it applies ("" picks
+# by key type: page-cooperative for FP8 keys, staged for 4-bit keys with an
+# even number of kv heads, direct otherwise)
+KERNELS = ["", "page", "staged", "direct"]
+
+
 @pytest.mark.parametrize("preset", PRESETS)
 @pytest.mark.parametrize("H", [1, 4, 8])
-@pytest.mark.parametrize("page_mse", ["0", "1"])
-def test_decode_page_kernel_head_counts(preset, H, page_mse, monkeypatch):
-    # with TQ_DECODE_PAGE_MSE=1 the page-cooperative kernel also takes the
-    # 3/4-bit presets (it always takes FP8 keys)
-    monkeypatch.setenv("TQ_DECODE_PAGE_MSE", page_mse)
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_decode_kernels_head_counts(preset, H, kernel, monkeypatch):
+    monkeypatch.setenv("TQ_DECODE_KERNEL", kernel)
     got, want = _decode_from_oracle_cache(_wl(preset, G=8 if H < 8 else 4, H=H, B=3, lens=(1, 300), seed=30 + H))
     check_decode(got, want, bf16_out=False)
 
 
 @pytest.mark.parametrize("preset", ["turboquant_4bit_nc", "turboquant_k3v4_nc"])
-def test_decode_page_kernel_mse_ragged(preset, monkeypatch):
-    monkeypatch.setenv("TQ_DECODE_PAGE_MSE", "1")
+@pytest.mark.parametrize("kernel", ["page", "staged", "direct"])
+def test_decode_kernels_mse_ragged(preset, kernel, monkeypatch):
+    monkeypatch.setenv("TQ_DECODE_KERNEL", kernel)
     w = _wl(preset, G=4, H=2, B=7, lens=(600, 600), seed=9)
     got, want = _decode_from_oracle_cache(w, lens=[0, 1, 15, 16, 17, 257, 600])
     check_decode(got, want, bf16_out=False)
@@ -182,13 +187,14 @@ def test_decode_full_size_sampled(name):
     print(f"[decode full] {name}: sampled {picks}, max abs err {worst:.2e}", flush=True)
 
 
-@pytest.mark.parametrize("preset,page_mse", [("turboquant_k8v4", "0"), ("turboquant_4bit_nc", "1")])
-def test_decode_workspace_reuse_across_shapes(preset, page_mse, monkeypatch):
+@pytest.mark.parametrize("preset,kernel", [("turboquant_k8v4", ""), ("turboquant_4bit_nc", "page"),
+                                           ("turboquant_4bit_nc", "staged")])
+def test_decode_workspace_reuse_across_shapes(preset, kernel, monkeypatch):
     """One context, one workspace, several calls of different batch and
     length (the workspace is reused as the split count changes): each result
     matches the oracle."""
     from packed_cache_decode_amd.runtime import PackedKVCache
-    monkeypatch.setenv("TQ_DECODE_PAGE_MSE", page_mse)
+    monkeypatch.setenv("TQ_DECODE_KERNEL", kernel)
     seed = 13
     tq = PackedKVCache(preset, 128, 2, 16, seed)
     ors = OracleSide(preset, 128, seed)
@@ -206,9 +212,10 @@ def test_decode_workspace_reuse_across_shapes(preset, page_mse, monkeypatch):
     tq.close()
 
 
-def test_decode_many_short_sequences():
+@pytest.mark.parametrize("preset,H", [("turboquant_k8v4", 1), ("turboquant_4bit_nc", 2)])
+def test_decode_many_short_sequences(preset, H):
     """4100 short sequences (0 to 40 tokens): a single token often dominates
     the softmax, which is where the P.V weights need more than one f16."""
-    w = _wl("turboquant_k8v4", G=1, H=1, B=4100, lens=(0, 40), seed=17)
+    w = _wl(preset, G=1, H=H, B=4100, lens=(0, 40), seed=17)
     got, want = _decode_from_oracle_cache(w)
     check_decode(got, want, bf16_out=False)

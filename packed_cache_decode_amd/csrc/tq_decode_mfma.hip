@@ -466,12 +466,11 @@ __device__ __forceinline__ void softmax_accumulate(const float (&s)[4], const Sl
     lo23 -= b1024;
     hi01 -= b64;
     hi23 -= b64;
-    const h4 Blo = {lo01[0], lo01[1], lo23[0], lo23[1]};
-    const h4 Bhi = {hi01[0], hi01[1], hi23[0], hi23[1]};
-    st.O[2 * kb] = __builtin_amdgcn_mfma_f32_16x16x16f16(W, Blo, st.O[2 * kb], 0, 0, 0);
-    st.O[2 * kb + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(W, Bhi, st.O[2 * kb + 1], 0, 0, 0);
-    st.O[2 * kb] = __builtin_amdgcn_mfma_f32_16x16x16f16(Wl, Blo, st.O[2 * kb], 0, 0, 0);
-    st.O[2 * kb + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(Wl, Bhi, st.O[2 * kb + 1], 0, 0, 0);
+    const h8 Blo = {lo01[0], lo01[1], lo23[0], lo23[1], lo01[0], lo01[1], lo23[0], lo23[1]};
+    const h8 Bhi = {hi01[0], hi01[1], hi23[0], hi23[1], hi01[0], hi01[1], hi23[0], hi23[1]};
+    const h8 Ws = {W[0], W[1], W[2], W[3], Wl[0], Wl[1], Wl[2], Wl[3]};
+    st.O[2 * kb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ws, Blo, st.O[2 * kb], 0, 0, 0);
+    st.O[2 * kb + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ws, Bhi, st.O[2 * kb + 1], 0, 0, 0);
     if (kb & 1) __builtin_amdgcn_sched_barrier(0);     // bounded operand registers
   }
 }
@@ -943,7 +942,7 @@ __device__ __forceinline__ SlabOps<KB> staged_ops(const uint8_t* lds, int r16, i
 // resident wavefronts per SIMD the staged kernel is built for (its register
 // budget: 512 / waves)
 template <int KB>
-constexpr int kStagedWavesPerSimd = KB == 4 ? 3 : 2;
+constexpr int kStagedWavesPerSimd = 3;
 
 template <int KB, int SLOT>
 __global__ void __launch_bounds__(64, kStagedWavesPerSimd<KB>) decode_staged_kernel(MfmaArgs a) {

@@ -100,8 +100,8 @@ def cpu_baseline(inp, slot, budget_s=12.0):
     with lim:
         # store: encode tokens of sequence 0 until half the budget is spent
         n_store, t_store = 0, 0.0
-        step = 1024
-        while t_store < budget_s / 2 and n_store + step <= inp.num_tokens:
+        while t_store < budget_s / 2 and n_store < inp.num_tokens:
+            step = min(1024, inp.num_tokens - n_store)
             t0 = time.perf_counter()
             ost.encode_slots(inp.k[n_store:n_store + step], inp.v[n_store:n_store + step], lay, signs, m)
             t_store += time.perf_counter() - t0

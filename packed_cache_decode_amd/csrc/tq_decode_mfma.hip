@@ -956,14 +956,15 @@ __global__ void __launch_bounds__(64, kStagedWavesPerSimd<KB>) decode_staged_ker
   const int lane = threadIdx.x;
   const int r16 = lane & 15;
   const int g4 = lane >> 4;
-  // items in launch order, split fastest (measured faster for this kernel
-  // than the direct kernel's XCD-aware order)
+  // XCD-aware order, kv head fastest (as in the direct kernel): the heads of
+  // one page row share cache lines and meet in one XCD's L2
   const int n_items = a.num_splits * a.batch * a.H;
-  const int item = blockIdx.x;
+  const int per_xcd = (n_items + 7) / 8;
+  const int item = static_cast<int>(blockIdx.x % 8) * per_xcd + static_cast<int>(blockIdx.x / 8);
   if (item >= n_items) return;
-  const int split = item % a.num_splits;
-  const int b = (item / a.num_splits) % a.batch;
-  const int g = item / (a.num_splits * a.batch);   // kv head
+  const int g = item % a.H;                  // kv head
+  const int split = (item / a.H) % a.num_splits;
+  const int b = item / (a.H * a.num_splits);
   const int64_t row_bytes = static_cast<int64_t>(a.H) * SLOT;
   const int64_t page_bytes = static_cast<int64_t>(1 << a.bs_shift) * row_bytes;
 

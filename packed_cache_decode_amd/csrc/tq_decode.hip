@@ -366,14 +366,15 @@ hipError_t launch_g(const DecodeArgs& a, int G, int batch, hipStream_t stream) {
 
 DecodePlan plan_decode(const Geometry& g, int batch, int num_q_heads, int max_seq_len) {
   DecodePlan p;
-  // Matrix-core kernel by key type (measured on the llama3-, k3v4- and
-  // k8v4-shaped decodes): FP8 keys take the page-cooperative kernel, 4-bit
-  // keys with an even number of kv heads the staged kernel, the rest the
-  // direct one.  TQ_DECODE_KERNEL=page|staged|direct forces one where it
+  // Matrix-core kernel by key type (measured on the llama3-, long-context,
+  // k3v4- and k8v4-shaped decodes): FP8 keys take the page-cooperative
+  // kernel; 3/4-bit keys with at most 8 query heads per kv head the ring
+  // kernel, else (an even number of kv heads) the staged kernel, else the
+  // direct one.  TQ_DECODE_KERNEL=page|ring|staged|direct forces one where it
   // applies (for tests and measurements of each path).
   const char* env = getenv("TQ_DECODE_KERNEL");
   const std::string force = env != nullptr ? env : "";
-  const bool auto_pick = force != "page" && force != "staged" && force != "direct";
+  const bool auto_pick = force != "page" && force != "staged" && force != "direct" && force != "ring";
   if ((auto_pick || force == "page") && page_decode_eligible(g, num_q_heads, force == "page")) {
     // one resident round of workgroups (256 CUs x the workgroups that fit per
     // CU) over (sequence, split), at least 4 slabs of 16 tokens per split so
@@ -397,13 +398,13 @@ DecodePlan plan_decode(const Geometry& g, int batch, int num_q_heads, int max_se
     // per split so the per-wavefront set-up is amortised
     const int slabs = max_seq_len > 0 ? (max_seq_len + 15) / 16 : 1;
     const int per_split = batch * g.num_kv_heads;
-    const bool staged = staged_decode_eligible(g, num_q_heads) &&
-                        (force == "staged" || (auto_pick && g.key_bits == 4));
-    const int target = 256 * mfma_waves_per_cu(g, staged);
+    const bool ring = ring_decode_eligible(g, num_q_heads) && (force == "ring" || auto_pick);
+    const bool staged = !ring && staged_decode_eligible(g, num_q_heads) && (force == "staged" || auto_pick);
+    const int target = 256 * (ring ? ring_waves_per_cu(g) : mfma_waves_per_cu(g, staged));
     int s = per_split > 0 ? (target + per_split - 1) / per_split : 1;
     const int s_max = (slabs + 7) / 8;
     s = s < 1 ? 1 : (s > s_max ? s_max : s);
-    p.mfma = staged ? 3 : 1;
+    p.mfma = ring ? 4 : (staged ? 3 : 1);
     p.chunk = 16 * ((slabs + s - 1) / s);
     if (p.chunk > 16 * 256) p.chunk = 16 * 256;       // page offsets of a split fit in LDS
     p.num_splits = max_seq_len > 0 ? (max_seq_len + p.chunk - 1) / p.chunk : 1;

@@ -1437,6 +1437,148 @@ __global__ void __launch_bounds__(64 * H, page_waves_per_simd(KB)) decode_page_k
   store_partials(a, b, w, split, g4, r16, st);
 }
 
+// ============================================================================
+// ring: one wavefront per (split, sequence, kv head), WPG of them (kv heads
+// of the same split and sequence) per workgroup sharing the centroid table
+// and the page ids.  Each wavefront streams its own head's 16-row slabs into
+// a private LDS ring with non-temporal loads that write LDS directly, in the
+// page kernel's aligned slot layout, and computes them with the page
+// kernel's slab code.  The wavefronts never wait for each other after the
+// set-up: a wavefront waits only for its own loads.  3/4-bit keys, at most 8
+// query heads per kv head.
+// ============================================================================
+
+constexpr int kRingBufs = 3;                 // slabs per wavefront ring (two in flight)
+
+template <int KB, int SLOT, int WPG>
+__global__ void __launch_bounds__(64 * WPG, 4) decode_ring_kernel(MfmaArgs a) {
+  static_assert(KB == 3 || KB == 4, "ring kernel: 3/4-bit keys");
+  using Geo = PageGeom<KB, SLOT, 1>;         // one head's slab layout in LDS
+  constexpr int kLoads = Geo::kWaveLoads;    // 16-byte loads per lane per slab
+  constexpr int kBuf = Geo::kBuf;            // kLoads KB: covers every lane's chunk
+  __shared__ u32x2 s_tab[256];
+  __shared__ int32_t s_pid[kMaxChunkSlabs];
+  __shared__ __attribute__((aligned(16))) uint8_t s_ring[WPG][kRingBufs * kBuf];
+
+  const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+  const int lane = threadIdx.x & 63;
+  const int r16 = lane & 15;
+  const int g4 = lane >> 4;
+  // XCD-aware order, head group fastest: the kv heads of one page row run
+  // on one XCD, where the cache lines their slots share come from its L2
+  const int HG = a.H / WPG;
+  const int n_items = a.num_splits * a.batch * HG;
+  const int per_xcd = (n_items + 7) / 8;
+  const int item = static_cast<int>(blockIdx.x % 8) * per_xcd + static_cast<int>(blockIdx.x / 8);
+  if (item >= n_items) return;
+  const int hg = item % HG;
+  const int split = (item / HG) % a.num_splits;
+  const int b = item / (HG * a.num_splits);
+  const int g = hg * WPG + w;                // this wavefront's kv head
+
+  const int T = clamp_len(a, b, split, g);
+  const int t0 = split * a.chunk;
+  const int t1 = min(T, t0 + a.chunk);
+  if (t0 >= t1) return;                      // the whole workgroup, before the barrier
+  build_tables_page<KB>(a, s_tab);
+  stage_page_ids(a, b, t0, t1, s_pid);
+  __syncthreads();
+
+  h8 qc[4];
+  bf8v qb[4];
+  load_queries_packed(a, b, g, r16, g4, qc);
+  RunState st;
+#pragma unroll
+  for (int m = 0; m < 8; ++m) st.O[m] = f4{0.f, 0.f, 0.f, 0.f};
+  st.m_run = -INFINITY;
+  st.l_part = 0.0f;
+  st.z_part = 0.0f;
+  const bool sel1 = (r16 & 1) != 0, sel2 = (r16 & 2) != 0;
+  const bool diag = (r16 >> 2) == g4;
+
+  const int p_first = t0 >> a.bs_shift;
+  const int bs_mask = (1 << a.bs_shift) - 1;
+  const int64_t row_bytes = static_cast<int64_t>(a.H) * SLOT;
+  const int64_t page_bytes = static_cast<int64_t>(1 << a.bs_shift) * row_bytes;
+  const int n_slabs = (t1 - t0 + 15) >> 4;
+  // the slab of one head: 16 rows row_bytes apart; the lane's chunk of load
+  // l is chunk l*64 + lane of the aligned layout (past the slab: an offset
+  // beyond every buffer range, which loads zeros into the ring's slack)
+  uint32_t src_off[kLoads];
+#pragma unroll
+  for (int l = 0; l < kLoads; ++l) {
+    const int c = l * 64 + lane;
+    if (c >= Geo::kSlabChunks) {
+      src_off[l] = 0x7FFFFFF0u;
+    } else {
+      const int row = c / (Geo::kNK + Geo::kNV), k = c - row * (Geo::kNK + Geo::kNV);
+      const int off = k < Geo::kNK ? 16 * k : Geo::kKP + 16 * (k - Geo::kNK);
+      src_off[l] = static_cast<uint32_t>(row * row_bytes + off);
+    }
+  }
+  const uint32_t head_bytes = static_cast<uint32_t>(g * SLOT);
+  const uint32_t range = static_cast<uint32_t>(16 * row_bytes) - head_bytes;
+  uint8_t* ring = s_ring[w];
+  // the query loads are done before the first slab is requested, so every
+  // wait in the loop counts slab loads only
+  wait_vmcnt<0>();
+
+  auto issue = [&](int j) {
+    const int t = t0 + 16 * j;
+    int pid = -1;
+    if (t < t1) pid = s_pid[(t >> a.bs_shift) - p_first];
+    pid = __builtin_amdgcn_readfirstlane(pid);
+    const int64_t off = pid >= 0 ? pid * page_bytes + static_cast<int64_t>(t & bs_mask) * row_bytes + head_bytes : 0;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(a.cache) + off, 0, pid >= 0 ? static_cast<int>(range) : 0, kBufferWord3);
+    uint8_t* dst = ring + (j % kRingBufs) * kBuf;
+#pragma unroll
+    for (int l = 0; l < kLoads; ++l) lds_dma_16(rs, dst + l * 1024, src_off[l]);
+  };
+#pragma unroll
+  for (int j = 0; j < kRingBufs - 1; ++j) issue(j);
+
+  auto page_of = [&](int jj) { return s_pid[((t0 + 16 * jj) >> a.bs_shift) - p_first]; };
+
+  int j = 0;
+  while (true) {
+    float s[4];
+    SlabSoftmax sm;
+    SlabRegs<KB> c;
+    bool grow = false;
+    for (; j < n_slabs; ++j) {
+      // slab j has landed (slab j + 1 may be in flight); this wavefront's
+      // reads of slab j - 1 have completed, so its buffer takes slab j + 2
+      wait_vmcnt<kLoads * (kRingBufs - 2)>();
+      __builtin_amdgcn_s_waitcnt(0xC07F);    // lgkmcnt(0)
+      issue(j + kRingBufs - 1);
+      if (__builtin_amdgcn_readfirstlane(page_of(j)) < 0) continue;
+      slab_read<KB, SLOT, 1>(ring + (j % kRingBufs) * kBuf, 0, r16, g4, c);
+      slab_lookup<KB>(s_tab, c);
+      const ScoreAcc acc = slab_mfma<KB>(c, qc, qb);
+      const int valid = t1 - (t0 + 16 * j);
+      if (valid >= 16) {
+        slab_tail<KB, true>(c, acc, 16, g4, a.scale_log2, sel1, sel2, diag, s);
+        sm = softmax_check<true>(s, 16, c.sz, g4, st);
+      } else {
+        slab_tail<KB, false>(c, acc, valid, g4, a.scale_log2, sel1, sel2, diag, s);
+        sm = softmax_check<false>(s, valid, c.sz, g4, st);
+      }
+      if (sm.grow) {
+        grow = true;
+        break;
+      }
+      softmax_accumulate(s, sm, c.X, st);
+    }
+    if (!grow) break;
+    softmax_rescale(sm, diag, st);
+    softmax_accumulate(s, sm, c.X, st);
+    ++j;
+  }
+  wait_vmcnt<0>();                           // no load may still write LDS at exit
+  store_partials(a, b, g, split, g4, r16, st);
+}
+
 template <int KB, int SLOT, int H>
 hipError_t launch_page_t(const MfmaArgs& a, int batch, hipStream_t stream) {
   using Geo = PageGeom<KB, SLOT, H>;
@@ -1485,6 +1627,23 @@ bool page_decode_eligible(const Geometry& g, int num_q_heads, bool mse_keys_too)
   // kernel's centroid lookups are bound by LDS bank conflicts), unless asked
   const bool kind_ok = g.key_bits == 8 || mse_keys_too;
   return mfma_decode_eligible(g, num_q_heads) && g_ok && kind_ok && (H == 1 || H == 2 || H == 4 || H == 8);
+}
+
+// kv heads (wavefronts) per workgroup of the ring kernel
+static int ring_wpg(int H) { return H % 4 == 0 ? 4 : (H % 2 == 0 ? 2 : 1); }
+
+bool ring_decode_eligible(const Geometry& g, int num_q_heads) {
+  return mfma_decode_eligible(g, num_q_heads) && (g.key_bits == 4 || g.key_bits == 3) &&
+         num_q_heads <= 8 * g.num_kv_heads;
+}
+
+int ring_waves_per_cu(const Geometry& g) {
+  const int wpg = ring_wpg(g.num_kv_heads);
+  const int buf = g.key_bits == 4 ? PageGeom<4, 134, 1>::kBuf : PageGeom<3, 118, 1>::kBuf;
+  const int lds = 256 * 8 + 4 * kMaxChunkSlabs + wpg * kRingBufs * buf;
+  int wgs = (160 * 1024) / lds;
+  if (wgs * wpg > 16) wgs = 16 / wpg;        // four wavefronts per SIMD (128 VGPRs)
+  return wgs * wpg;
 }
 
 int page_wgs_per_cu(const Geometry& g) {
@@ -1538,6 +1697,22 @@ hipError_t launch_decode_mfma(const Geometry& g, const DevTables* tables, const 
   a.part = static_cast<float*>(workspace);
   a.out = out;
   a.out_fp32 = out_is_fp32;
+  if (plan.mfma == 4) {
+    const int wpg = ring_wpg(g.num_kv_heads);
+    const int n_items = plan.num_splits * batch * (g.num_kv_heads / wpg);
+    const dim3 grid(8 * ((n_items + 7) / 8));
+#define TQ_RING(KB_, SLOT_, WPG_) hipLaunchKernelGGL((decode_ring_kernel<KB_, SLOT_, WPG_>), grid, dim3(64 * WPG_), 0, stream, a)
+    if (g.key_bits == 4) {
+      if (wpg == 4) TQ_RING(4, 134, 4); else if (wpg == 2) TQ_RING(4, 134, 2); else TQ_RING(4, 134, 1);
+    } else {
+      if (wpg == 4) TQ_RING(3, 118, 4); else if (wpg == 2) TQ_RING(3, 118, 2); else TQ_RING(3, 118, 1);
+    }
+#undef TQ_RING
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(decode_merge_kernel, dim3(batch * num_q_heads), dim3(256), 0, stream, a);
+    return hipGetLastError();
+  }
   if (plan.mfma == 2) {
     hipError_t e = g.key_bits == 8 ? launch_page_h<8, 196>(a, batch, stream)
                  : g.key_bits == 4 ? launch_page_h<4, 134>(a, batch, stream)

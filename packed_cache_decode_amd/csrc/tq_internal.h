@@ -64,7 +64,8 @@ hipError_t launch_store(const Geometry& g, const DevTables* tables, const uint16
 
 struct DecodePlan {
   int mfma;         // matrix-core kernels (tq_decode_mfma.hip): 2 page-cooperative,
-                    // 3 staged per-head, 1 direct per-head; 0: general kernel
+                    // 3 staged per-head, 4 ring per-head, 1 direct per-head;
+                    // 0: general kernel
   int chunk;        // tokens per split
   int num_splits;   // splits per sequence (grid extent)
   size_t workspace_bytes;
@@ -74,6 +75,8 @@ bool mfma_decode_eligible(const Geometry& g, int num_q_heads);
 bool page_decode_eligible(const Geometry& g, int num_q_heads, bool mse_keys_too);
 int page_wgs_per_cu(const Geometry& g);
 bool staged_decode_eligible(const Geometry& g, int num_q_heads);
+bool ring_decode_eligible(const Geometry& g, int num_q_heads);
+int ring_waves_per_cu(const Geometry& g);
 int mfma_waves_per_cu(const Geometry& g, bool staged);
 size_t mfma_partial_bytes(int batch, int num_q_heads, int num_splits);
 hipError_t launch_decode_mfma(const Geometry& g, const DevTables* tables, const DecodePlan& plan,

@@ -71,7 +71,7 @@ def test_decode_per_head_kernel_shapes(preset, G, H):
 # TQ_DECODE_KERNEL forces one matrix-core kernel where it applies ("" picks
 # by key type: page-cooperative for FP8 keys, staged for 4-bit keys with an
 # even number of kv heads, direct otherwise)
-KERNELS = ["", "page", "staged", "direct"]
+KERNELS = ["", "page", "staged", "direct", "ring"]
 
 
 @pytest.mark.parametrize("preset", PRESETS)
@@ -84,7 +84,7 @@ def test_decode_kernels_head_counts(preset, H, kernel, monkeypatch):
 
 
 @pytest.mark.parametrize("preset", ["turboquant_4bit_nc", "turboquant_k3v4_nc"])
-@pytest.mark.parametrize("kernel", ["page", "staged", "direct"])
+@pytest.mark.parametrize("kernel", ["page", "staged", "direct", "ring"])
 def test_decode_kernels_mse_ragged(preset, kernel, monkeypatch):
     monkeypatch.setenv("TQ_DECODE_KERNEL", kernel)
     w = _wl(preset, G=4, H=2, B=7, lens=(600, 600), seed=9)
@@ -188,7 +188,7 @@ def test_decode_full_size_sampled(name):
 
 
 @pytest.mark.parametrize("preset,kernel", [("turboquant_k8v4", ""), ("turboquant_4bit_nc", "page"),
-                                           ("turboquant_4bit_nc", "staged")])
+                                           ("turboquant_4bit_nc", "staged"), ("turboquant_k3v4_nc", "ring")])
 def test_decode_workspace_reuse_across_shapes(preset, kernel, monkeypatch):
     """One context, one workspace, several calls of different batch and
     length (the workspace is reused as the split count changes): each result
@@ -212,10 +212,12 @@ def test_decode_workspace_reuse_across_shapes(preset, kernel, monkeypatch):
     tq.close()
 
 
-@pytest.mark.parametrize("preset,H", [("turboquant_k8v4", 1), ("turboquant_4bit_nc", 2)])
-def test_decode_many_short_sequences(preset, H):
+@pytest.mark.parametrize("preset,H,kernel", [("turboquant_k8v4", 1, ""), ("turboquant_4bit_nc", 2, ""),
+                                             ("turboquant_4bit_nc", 2, "ring")])
+def test_decode_many_short_sequences(preset, H, kernel, monkeypatch):
     """4100 short sequences (0 to 40 tokens): a single token often dominates
     the softmax, which is where the P.V weights need more than one f16."""
+    monkeypatch.setenv("TQ_DECODE_KERNEL", kernel)
     w = _wl(preset, G=1, H=H, B=4100, lens=(0, 40), seed=17)
     got, want = _decode_from_oracle_cache(w)
     check_decode(got, want, bf16_out=False)

@@ -1141,14 +1141,20 @@ __device__ __forceinline__ void stage_page_ids(const MfmaArgs& a, int b, int t0,
 }
 
 // 16 bytes per lane from buffer offset voff into LDS at dst + 16 * lane,
-// non-temporal.  Written as inline assembly so the compiler does not treat
-// the load as an LDS store it must wait for before every LDS read (it cannot
-// tell the ring's slots apart); the kernel waits for these loads itself.
+// non-temporal unless NT is false.  Written as inline assembly so the
+// compiler does not treat the load as an LDS store it must wait for before
+// every LDS read (it cannot tell the ring's slots apart); the kernel waits
+// for these loads itself.
+template <bool NT = true>
 __device__ __forceinline__ void lds_dma_16(__amdgpu_buffer_rsrc_t rs, const uint8_t* dst, uint32_t voff) {
   const uint32_t m0 = __builtin_amdgcn_readfirstlane(
       static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const uint8_t*)dst)));
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen nt lds"
-               :: "s"(m0), "v"(voff), "s"(rs) : "memory", "m0");
+  if constexpr (NT)
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen nt lds"
+                 :: "s"(m0), "v"(voff), "s"(rs) : "memory", "m0");
+  else
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :: "s"(m0), "v"(voff), "s"(rs) : "memory", "m0");
 }
 
 template <int N>
@@ -1441,9 +1447,11 @@ __global__ void __launch_bounds__(64 * H, page_waves_per_simd(KB)) decode_page_k
 // ring: one wavefront per (split, sequence, kv head), WPG of them (kv heads
 // of the same split and sequence) per workgroup sharing the centroid table
 // and the page ids.  Each wavefront streams its own head's 16-row slabs into
-// a private LDS ring with non-temporal loads that write LDS directly, in the
-// page kernel's aligned slot layout, and computes them with the page
-// kernel's slab code.  The wavefronts never wait for each other after the
+// a private LDS ring with loads that write LDS directly, in the page
+// kernel's aligned slot layout, and computes them with the page kernel's
+// slab code.  The loads are plain, not non-temporal: a head's 16-byte chunks
+// overlap its neighbours' slots, and those lines are then still in L2 when
+// the neighbouring wavefronts ask for them.  The wavefronts never wait for each other after the
 // set-up: a wavefront waits only for its own loads.  3/4-bit keys, at most 8
 // query heads per kv head.
 // ============================================================================
@@ -1533,7 +1541,7 @@ __global__ void __launch_bounds__(64 * WPG, 4) decode_ring_kernel(MfmaArgs a) {
         const_cast<uint8_t*>(a.cache) + off, 0, pid >= 0 ? static_cast<int>(range) : 0, kBufferWord3);
     uint8_t* dst = ring + (j % kRingBufs) * kBuf;
 #pragma unroll
-    for (int l = 0; l < kLoads; ++l) lds_dma_16(rs, dst + l * 1024, src_off[l]);
+    for (int l = 0; l < kLoads; ++l) lds_dma_16<false>(rs, dst + l * 1024, src_off[l]);
   };
 #pragma unroll
   for (int j = 0; j < kRingBufs - 1; ++j) issue(j);

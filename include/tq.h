@@ -140,7 +140,8 @@ tq_status tq_store(const tq_ctx* ctx, const void* k, const void* v, int64_t kv_t
                    int64_t num_blocks, void* stream);
 
 /* Workspace bytes tq_decode needs for this shape (split-KV partials: P1,
- * section "内存:workspace 预分配").  0 on bad input. */
+ * section "内存:workspace 预分配").  0 when the shape needs none (every
+ * sequence is combined inside one workgroup) or on bad input. */
 size_t tq_decode_workspace_bytes(const tq_ctx* ctx, int batch, int num_q_heads,
                                  int max_seq_len);
 
@@ -172,7 +173,8 @@ size_t tq_decode_workspace_bytes(const tq_ctx* ctx, int batch, int num_q_heads,
  *                  out_is_fp32 == 0, fp32 otherwise
  *   workspace      device, >= tq_decode_workspace_bytes(...) bytes, 256-byte
  *                  aligned; contents need no initialisation; calls that
- *                  share a workspace must not overlap
+ *                  share a workspace must not overlap; may be NULL when
+ *                  that size is 0
  */
 tq_status tq_decode(const tq_ctx* ctx, const void* q, const uint8_t* cache, int64_t num_blocks,
                     const int32_t* block_table, int max_blocks_per_seq, const int32_t* seq_lens,

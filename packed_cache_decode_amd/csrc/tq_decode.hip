@@ -392,19 +392,42 @@ DecodePlan plan_decode(const Geometry& g, int batch, int num_q_heads, int max_se
     p.workspace_bytes = (p.workspace_bytes + 255) & ~static_cast<size_t>(255);
     return p;
   }
+  if (ring_decode_eligible(g, num_q_heads) && (force == "ring" || auto_pick)) {
+    // ring kernel: one workgroup of 16 wavefronts per (sequence, kv head,
+    // workgroup split), at most ring_max_slabs() slabs per split (its page
+    // ids fit in LDS); more splits only to fill whole rounds of the 256 CUs
+    // (one workgroup each), so a round is not left part-empty
+    const int slabs = max_seq_len > 0 ? (max_seq_len + 15) / 16 : 1;
+    const int cap = ring_max_slabs();
+    const int s_min = (slabs + cap - 1) / cap;
+    const int pairs = batch * g.num_kv_heads;
+    int s = s_min;
+    if (pairs > 0) {
+      const int rounds = (pairs * s_min + 255) / 256;
+      const int s_fill = rounds * 256 / pairs;
+      if (s_fill > s) s = s_fill;
+    }
+    if (s > slabs) s = slabs;
+    if (s < 1) s = 1;
+    p.mfma = 4;
+    p.chunk = 16 * ((slabs + s - 1) / s);
+    p.num_splits = max_seq_len > 0 ? (max_seq_len + p.chunk - 1) / p.chunk : 1;
+    p.workspace_bytes = p.num_splits > 1 ? mfma_partial_bytes(batch, num_q_heads, p.num_splits) : 0;
+    p.workspace_bytes = (p.workspace_bytes + 255) & ~static_cast<size_t>(255);
+    return p;
+  }
   if (mfma_decode_eligible(g, num_q_heads)) {
     // one resident round of wavefronts (256 CUs x the kernel's wavefronts per
     // CU) over (split, sequence, kv head), 16-token slabs, at least 8 slabs
     // per split so the per-wavefront set-up is amortised
     const int slabs = max_seq_len > 0 ? (max_seq_len + 15) / 16 : 1;
     const int per_split = batch * g.num_kv_heads;
-    const bool ring = ring_decode_eligible(g, num_q_heads) && (force == "ring" || auto_pick);
-    const bool staged = !ring && staged_decode_eligible(g, num_q_heads) && (force == "staged" || auto_pick);
-    const int target = 256 * (ring ? ring_waves_per_cu(g) : mfma_waves_per_cu(g, staged));
+    const bool staged = staged_decode_eligible(g, num_q_heads) && (force == "staged" || auto_pick);
+    const int target = 256 * mfma_waves_per_cu(g, staged);
     int s = per_split > 0 ? (target + per_split - 1) / per_split : 1;
     const int s_max = (slabs + 7) / 8;
     s = s < 1 ? 1 : (s > s_max ? s_max : s);
-    p.mfma = ring ? 4 : (staged ? 3 : 1);
+    p.mfma = staged ? 3 : 1;
     p.chunk = 16 * ((slabs + s - 1) / s);
     if (p.chunk > 16 * 256) p.chunk = 16 * 256;       // page offsets of a split fit in LDS
     p.num_splits = max_seq_len > 0 ? (max_seq_len + p.chunk - 1) / p.chunk : 1;

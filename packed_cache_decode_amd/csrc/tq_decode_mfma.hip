@@ -1444,52 +1444,66 @@ __global__ void __launch_bounds__(64 * H, page_waves_per_simd(KB)) decode_page_k
 }
 
 // ============================================================================
-// ring: one wavefront per (split, sequence, kv head), WPG of them (kv heads
-// of the same split and sequence) per workgroup sharing the centroid table
-// and the page ids.  Each wavefront streams its own head's 16-row slabs into
-// a private LDS ring with loads that write LDS directly, in the page
-// kernel's aligned slot layout, and computes them with the page kernel's
-// slab code.  The loads are plain, not non-temporal: a head's 16-byte chunks
-// overlap its neighbours' slots, and those lines are then still in L2 when
-// the neighbouring wavefronts ask for them.  The wavefronts never wait for each other after the
-// set-up: a wavefront waits only for its own loads.  3/4-bit keys, at most 8
-// query heads per kv head.
+// ring: one workgroup of 16 wavefronts per (sequence, kv head, workgroup
+// split).  The workgroup's slabs are dealt out in 16 consecutive runs, one per
+// wavefront; each wavefront streams its run's 16-row slabs of its head into a
+// private LDS ring with loads that write LDS directly, in the page kernel's
+// aligned slot layout, and computes them with the page kernel's slab code.
+// The wavefronts never wait for each other inside the loop (each waits only
+// for its own loads).  At the end they combine their partial softmax states
+// in LDS; with one workgroup split per sequence the workgroup writes the
+// output itself, and no merge kernel runs.  The loads are plain, not
+// non-temporal: a head's 16-byte chunks overlap its neighbours' slots, and
+// those lines are then still in L2 when the neighbouring heads ask for them.
+// 3/4-bit keys, at most 8 query heads per kv head.
 // ============================================================================
 
 constexpr int kRingBufs = 3;                 // slabs per wavefront ring (two in flight)
+constexpr int kRingWaves = 16;               // wavefronts per workgroup
+constexpr int kRingMaxSlabs = 1024;          // slabs per workgroup split: its page ids fit in LDS
 
-template <int KB, int SLOT, int WPG>
-__global__ void __launch_bounds__(64 * WPG, 4) decode_ring_kernel(MfmaArgs a) {
+template <int KB, int SLOT>
+__global__ void __launch_bounds__(64 * kRingWaves) decode_ring_kernel(MfmaArgs a) {
   static_assert(KB == 3 || KB == 4, "ring kernel: 3/4-bit keys");
   using Geo = PageGeom<KB, SLOT, 1>;         // one head's slab layout in LDS
   constexpr int kLoads = Geo::kWaveLoads;    // 16-byte loads per lane per slab
   constexpr int kBuf = Geo::kBuf;            // kLoads KB: covers every lane's chunk
+  constexpr int kRing = kRingBufs * kBuf;
+  static_assert(8 * kRec * 4 <= kRing, "a wavefront's partial records must fit its ring");
   __shared__ u32x2 s_tab[256];
-  __shared__ int32_t s_pid[kMaxChunkSlabs];
-  __shared__ __attribute__((aligned(16))) uint8_t s_ring[WPG][kRingBufs * kBuf];
+  __shared__ int32_t s_pid[kRingMaxSlabs];
+  __shared__ __attribute__((aligned(16))) uint8_t s_ring[kRingWaves][kRing];
 
   const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
   const int lane = threadIdx.x & 63;
   const int r16 = lane & 15;
   const int g4 = lane >> 4;
-  // XCD-aware order, head group fastest: the kv heads of one page row run
-  // on one XCD, where the cache lines their slots share come from its L2
-  const int HG = a.H / WPG;
-  const int n_items = a.num_splits * a.batch * HG;
+  // XCD-aware order, kv head fastest: the heads of one page row run on one
+  // XCD, where the cache lines their slots share come from its L2
+  const int n_items = a.num_splits * a.batch * a.H;
   const int per_xcd = (n_items + 7) / 8;
   const int item = static_cast<int>(blockIdx.x % 8) * per_xcd + static_cast<int>(blockIdx.x / 8);
   if (item >= n_items) return;
-  const int hg = item % HG;
-  const int split = (item / HG) % a.num_splits;
-  const int b = item / (HG * a.num_splits);
-  const int g = hg * WPG + w;                // this wavefront's kv head
+  const int g = item % a.H;                  // kv head
+  const int sg = (item / a.H) % a.num_splits;
+  const int b = item / (a.H * a.num_splits);
 
-  const int T = clamp_len(a, b, split, g);
-  const int t0 = split * a.chunk;
-  const int t1 = min(T, t0 + a.chunk);
-  if (t0 >= t1) return;                      // the whole workgroup, before the barrier
+  // this sequence's workgroup splits: a.chunk tokens at most each, the same
+  // count the merge kernel derives; past them the workgroup has nothing to do
+  const int T = clamp_len(a, b, sg, g);
+  const int n_slabs_b = (T + 15) >> 4;
+  const int cap = a.chunk >> 4;              // slabs per workgroup split, at most
+  const int s_b = n_slabs_b > 0 ? (n_slabs_b + cap - 1) / cap : 1;
+  if (sg >= s_b) return;                     // the whole workgroup, before any barrier
+  const int cs = (n_slabs_b + kRingWaves * s_b - 1) / (kRingWaves * s_b);   // slabs per wavefront
+  const int wg0 = sg * kRingWaves * cs;      // the workgroup's first slab
+  const int wg1 = min(n_slabs_b, wg0 + kRingWaves * cs);
+  const int j0 = min(wg1, wg0 + w * cs);     // this wavefront's slabs [j0, j1)
+  const int j1 = min(wg1, j0 + cs);
+  const int t0 = 16 * j0, t1 = min(T, 16 * j1);
+
   build_tables_page<KB>(a, s_tab);
-  stage_page_ids(a, b, t0, t1, s_pid);
+  if (wg1 > wg0) stage_page_ids(a, b, 16 * wg0, min(T, 16 * wg1), s_pid);
   __syncthreads();
 
   h8 qc[4];
@@ -1504,11 +1518,11 @@ __global__ void __launch_bounds__(64 * WPG, 4) decode_ring_kernel(MfmaArgs a) {
   const bool sel1 = (r16 & 1) != 0, sel2 = (r16 & 2) != 0;
   const bool diag = (r16 >> 2) == g4;
 
-  const int p_first = t0 >> a.bs_shift;
+  const int p_first = (16 * wg0) >> a.bs_shift;
   const int bs_mask = (1 << a.bs_shift) - 1;
   const int64_t row_bytes = static_cast<int64_t>(a.H) * SLOT;
   const int64_t page_bytes = static_cast<int64_t>(1 << a.bs_shift) * row_bytes;
-  const int n_slabs = (t1 - t0 + 15) >> 4;
+  const int n_slabs = j1 - j0;
   // the slab of one head: 16 rows row_bytes apart; the lane's chunk of load
   // l is chunk l*64 + lane of the aligned layout (past the slab: an offset
   // beyond every buffer range, which loads zeros into the ring's slack)
@@ -1543,48 +1557,115 @@ __global__ void __launch_bounds__(64 * WPG, 4) decode_ring_kernel(MfmaArgs a) {
 #pragma unroll
     for (int l = 0; l < kLoads; ++l) lds_dma_16<false>(rs, dst + l * 1024, src_off[l]);
   };
-#pragma unroll
-  for (int j = 0; j < kRingBufs - 1; ++j) issue(j);
-
   auto page_of = [&](int jj) { return s_pid[((t0 + 16 * jj) >> a.bs_shift) - p_first]; };
 
-  int j = 0;
-  while (true) {
-    float s[4];
-    SlabSoftmax sm;
-    SlabRegs<KB> c;
-    bool grow = false;
-    for (; j < n_slabs; ++j) {
-      // slab j has landed (slab j + 1 may be in flight); this wavefront's
-      // reads of slab j - 1 have completed, so its buffer takes slab j + 2
-      wait_vmcnt<kLoads * (kRingBufs - 2)>();
-      __builtin_amdgcn_s_waitcnt(0xC07F);    // lgkmcnt(0)
-      issue(j + kRingBufs - 1);
-      if (__builtin_amdgcn_readfirstlane(page_of(j)) < 0) continue;
-      slab_read<KB, SLOT, 1>(ring + (j % kRingBufs) * kBuf, 0, r16, g4, c);
-      slab_lookup<KB>(s_tab, c);
-      const ScoreAcc acc = slab_mfma<KB>(c, qc, qb);
-      const int valid = t1 - (t0 + 16 * j);
-      if (valid >= 16) {
-        slab_tail<KB, true>(c, acc, 16, g4, a.scale_log2, sel1, sel2, diag, s);
-        sm = softmax_check<true>(s, 16, c.sz, g4, st);
-      } else {
-        slab_tail<KB, false>(c, acc, valid, g4, a.scale_log2, sel1, sel2, diag, s);
-        sm = softmax_check<false>(s, valid, c.sz, g4, st);
+  if (n_slabs > 0) {
+#pragma unroll
+    for (int j = 0; j < kRingBufs - 1; ++j) issue(j);
+    int j = 0;
+    while (true) {
+      float s[4];
+      SlabSoftmax sm;
+      SlabRegs<KB> c;
+      bool grow = false;
+      for (; j < n_slabs; ++j) {
+        // slab j has landed (slab j + 1 may be in flight); this wavefront's
+        // reads of slab j - 1 have completed, so its buffer takes slab j + 2
+        wait_vmcnt<kLoads * (kRingBufs - 2)>();
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+        issue(j + kRingBufs - 1);
+        if (__builtin_amdgcn_readfirstlane(page_of(j)) < 0) continue;
+        slab_read<KB, SLOT, 1>(ring + (j % kRingBufs) * kBuf, 0, r16, g4, c);
+        slab_lookup<KB>(s_tab, c);
+        const ScoreAcc acc = slab_mfma<KB>(c, qc, qb);
+        const int valid = t1 - (t0 + 16 * j);
+        if (valid >= 16) {
+          slab_tail<KB, true>(c, acc, 16, g4, a.scale_log2, sel1, sel2, diag, s);
+          sm = softmax_check<true>(s, 16, c.sz, g4, st);
+        } else {
+          slab_tail<KB, false>(c, acc, valid, g4, a.scale_log2, sel1, sel2, diag, s);
+          sm = softmax_check<false>(s, valid, c.sz, g4, st);
+        }
+        if (sm.grow) {
+          grow = true;
+          break;
+        }
+        softmax_accumulate(s, sm, c.X, st);
       }
-      if (sm.grow) {
-        grow = true;
-        break;
-      }
+      if (!grow) break;
+      softmax_rescale(sm, diag, st);
       softmax_accumulate(s, sm, c.X, st);
+      ++j;
     }
-    if (!grow) break;
-    softmax_rescale(sm, diag, st);
-    softmax_accumulate(s, sm, c.X, st);
-    ++j;
+    wait_vmcnt<0>();                         // no load may still write the ring
   }
-  wait_vmcnt<0>();                           // no load may still write LDS at exit
-  store_partials(a, b, g, split, g4, r16, st);
+
+  // ---- combine the 16 wavefronts' states in LDS ----
+  // each wavefront's records (O[128], m, l, z per query head) go into its own
+  // ring, whose reads have all completed
+  float* rec_w = reinterpret_cast<float*>(ring);
+  {
+    const int G = a.G;
+    const float l_part = sum_x32(sum_x16(st.l_part));
+    const float z_part = sum_x32(sum_x16(st.z_part));
+    __builtin_amdgcn_s_waitcnt(0xC07F);      // lgkmcnt(0): no read of the ring in flight
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int h = 4 * g4 + r;
+      if (h < G) {
+        float* rec = rec_w + h * kRec;
+        *reinterpret_cast<float4*>(rec + 8 * r16) = make_float4(st.O[0][r], st.O[1][r], st.O[2][r], st.O[3][r]);
+        *reinterpret_cast<float4*>(rec + 8 * r16 + 4) = make_float4(st.O[4][r], st.O[5][r], st.O[6][r], st.O[7][r]);
+      }
+    }
+    if (g4 == 0 && r16 < G) {
+      float* rec = rec_w + r16 * kRec;
+      rec[kD] = st.m_run;
+      rec[kD + 1] = l_part;
+      rec[kD + 2] = z_part;
+    }
+  }
+  __syncthreads();
+  // thread (h, pair): coordinates 2*pair, 2*pair + 1 of query head h
+  const int h = threadIdx.x >> 6, pr = lane;
+  if (h < a.G) {
+    float M = -INFINITY, L = 0.0f;
+    float2 acc = make_float2(0.0f, 0.0f);
+#pragma unroll 4
+    for (int v = 0; v < kRingWaves; ++v) {
+      const float* rec = reinterpret_cast<const float*>(s_ring[v]) + h * kRec;
+      const float m = rec[kD];
+      const float m_new = fmaxf(M, m);
+      if (m_new == -INFINITY) continue;      // nothing attended yet
+      const float cM = __builtin_amdgcn_exp2f(M - m_new);      // 0 on the first one
+      const float wv = __builtin_amdgcn_exp2f(m - m_new);
+      const float z = rec[kD + 2];
+      const float2 o = *reinterpret_cast<const float2*>(rec + 2 * pr);
+      acc.x = acc.x * cM + wv * (o.x + z);
+      acc.y = acc.y * cM + wv * (o.y + z);
+      L = L * cM + wv * rec[kD + 1];
+      M = m_new;
+    }
+    const int hq = g * a.G + h;
+    if (a.num_splits == 1) {
+      const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+      const float r0 = acc.x * inv, r1 = acc.y * inv;
+      const int64_t oi = (static_cast<int64_t>(b) * a.Hq + hq) * kD + 2 * pr;
+      if (a.out_fp32) {
+        *reinterpret_cast<float2*>(static_cast<float*>(a.out) + oi) = make_float2(r0, r1);
+      } else {
+        uint32_t u0 = __float_as_uint(r0), u1 = __float_as_uint(r1);
+        u0 = (u0 + 0x7FFFu + ((u0 >> 16) & 1u)) >> 16;   // round to nearest even
+        u1 = (u1 + 0x7FFFu + ((u1 >> 16) & 1u)) >> 16;
+        *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(a.out) + oi) = u0 | (u1 << 16);
+      }
+    } else {
+      // the workgroup split's record for the merge kernel (zero term folded in)
+      float* rec = a.part + ((static_cast<int64_t>(b) * a.Hq + hq) * a.num_splits + sg) * kRec;
+      *reinterpret_cast<float2*>(rec + 2 * pr) = acc;
+      if (pr == 0) *reinterpret_cast<float4*>(rec + kD) = make_float4(M, L, 0.0f, 0.0f);
+    }
+  }
 }
 
 template <int KB, int SLOT, int H>
@@ -1637,22 +1718,12 @@ bool page_decode_eligible(const Geometry& g, int num_q_heads, bool mse_keys_too)
   return mfma_decode_eligible(g, num_q_heads) && g_ok && kind_ok && (H == 1 || H == 2 || H == 4 || H == 8);
 }
 
-// kv heads (wavefronts) per workgroup of the ring kernel
-static int ring_wpg(int H) { return H % 4 == 0 ? 4 : (H % 2 == 0 ? 2 : 1); }
-
 bool ring_decode_eligible(const Geometry& g, int num_q_heads) {
   return mfma_decode_eligible(g, num_q_heads) && (g.key_bits == 4 || g.key_bits == 3) &&
          num_q_heads <= 8 * g.num_kv_heads;
 }
 
-int ring_waves_per_cu(const Geometry& g) {
-  const int wpg = ring_wpg(g.num_kv_heads);
-  const int buf = g.key_bits == 4 ? PageGeom<4, 134, 1>::kBuf : PageGeom<3, 118, 1>::kBuf;
-  const int lds = 256 * 8 + 4 * kMaxChunkSlabs + wpg * kRingBufs * buf;
-  int wgs = (160 * 1024) / lds;
-  if (wgs * wpg > 16) wgs = 16 / wpg;        // four wavefronts per SIMD (128 VGPRs)
-  return wgs * wpg;
-}
+int ring_max_slabs() { return kRingMaxSlabs; }
 
 int page_wgs_per_cu(const Geometry& g) {
   const int H = g.num_kv_heads;
@@ -1706,18 +1777,16 @@ hipError_t launch_decode_mfma(const Geometry& g, const DevTables* tables, const 
   a.out = out;
   a.out_fp32 = out_is_fp32;
   if (plan.mfma == 4) {
-    const int wpg = ring_wpg(g.num_kv_heads);
-    const int n_items = plan.num_splits * batch * (g.num_kv_heads / wpg);
+    // one workgroup per (sequence, kv head, workgroup split); the merge runs
+    // only when a sequence has more than one workgroup split
+    const int n_items = plan.num_splits * batch * g.num_kv_heads;
     const dim3 grid(8 * ((n_items + 7) / 8));
-#define TQ_RING(KB_, SLOT_, WPG_) hipLaunchKernelGGL((decode_ring_kernel<KB_, SLOT_, WPG_>), grid, dim3(64 * WPG_), 0, stream, a)
-    if (g.key_bits == 4) {
-      if (wpg == 4) TQ_RING(4, 134, 4); else if (wpg == 2) TQ_RING(4, 134, 2); else TQ_RING(4, 134, 1);
-    } else {
-      if (wpg == 4) TQ_RING(3, 118, 4); else if (wpg == 2) TQ_RING(3, 118, 2); else TQ_RING(3, 118, 1);
-    }
-#undef TQ_RING
+    if (g.key_bits == 4)
+      hipLaunchKernelGGL((decode_ring_kernel<4, 134>), grid, dim3(64 * kRingWaves), 0, stream, a);
+    else
+      hipLaunchKernelGGL((decode_ring_kernel<3, 118>), grid, dim3(64 * kRingWaves), 0, stream, a);
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if (e != hipSuccess || plan.num_splits == 1) return e;
     hipLaunchKernelGGL(decode_merge_kernel, dim3(batch * num_q_heads), dim3(256), 0, stream, a);
     return hipGetLastError();
   }

@@ -76,7 +76,7 @@ bool page_decode_eligible(const Geometry& g, int num_q_heads, bool mse_keys_too)
 int page_wgs_per_cu(const Geometry& g);
 bool staged_decode_eligible(const Geometry& g, int num_q_heads);
 bool ring_decode_eligible(const Geometry& g, int num_q_heads);
-int ring_waves_per_cu(const Geometry& g);
+int ring_max_slabs();
 int mfma_waves_per_cu(const Geometry& g, bool staged);
 size_t mfma_partial_bytes(int batch, int num_q_heads, int num_splits);
 hipError_t launch_decode_mfma(const Geometry& g, const DevTables* tables, const DecodePlan& plan,

@@ -396,7 +396,8 @@ DecodePlan plan_decode(const Geometry& g, int batch, int num_q_heads, int max_se
     // ring kernel: one workgroup of 16 wavefronts per (sequence, kv head,
     // workgroup split), at most ring_max_slabs() slabs per split (its page
     // ids fit in LDS); more splits only to fill whole rounds of the 256 CUs
-    // (one workgroup each), so a round is not left part-empty
+    // (one workgroup each), so a round is not left part-empty, and only while
+    // every wavefront keeps at least 4 slabs
     const int slabs = max_seq_len > 0 ? (max_seq_len + 15) / 16 : 1;
     const int cap = ring_max_slabs();
     const int s_min = (slabs + cap - 1) / cap;
@@ -405,9 +406,10 @@ DecodePlan plan_decode(const Geometry& g, int batch, int num_q_heads, int max_se
     if (pairs > 0) {
       const int rounds = (pairs * s_min + 255) / 256;
       const int s_fill = rounds * 256 / pairs;
-      if (s_fill > s) s = s_fill;
+      const int s_work = slabs / 64;
+      const int s_up = s_fill < s_work ? s_fill : s_work;
+      if (s_up > s) s = s_up;
     }
-    if (s > slabs) s = slabs;
     if (s < 1) s = 1;
     p.mfma = 4;
     p.chunk = 16 * ((slabs + s - 1) / s);

@@ -92,6 +92,17 @@ def test_decode_kernels_mse_ragged(preset, kernel, monkeypatch):
     check_decode(got, want, bf16_out=False)
 
 
+@pytest.mark.parametrize("preset", ["turboquant_4bit_nc", "turboquant_k3v4_nc"])
+def test_decode_ring_workgroup_splits(preset, monkeypatch):
+    # sequences longer than one ring workgroup split (1024 slabs) take several
+    # workgroups and the merge kernel; the short one fits one split, and the
+    # splits past it have nothing to do
+    monkeypatch.setenv("TQ_DECODE_KERNEL", "ring")
+    w = _wl(preset, G=4, H=2, B=3, lens=(100, 20000), seed=41)
+    got, want = _decode_from_oracle_cache(w, lens=[100, 16400, 20000])
+    check_decode(got, want, bf16_out=False)
+
+
 @pytest.mark.parametrize("preset", PRESETS)
 def test_decode_small_parity_bf16(preset):
     got, want = _decode_from_oracle_cache(_wl(preset, G=4, seed=21), out_fp32=False)

@@ -365,7 +365,7 @@ hipError_t launch_g(const DecodeArgs& a, int G, int batch, hipStream_t stream) {
 }  // namespace
 
 DecodePlan plan_decode(const Geometry& g, int batch, int num_q_heads, int max_seq_len) {
-  DecodePlan p;
+  DecodePlan p{};
   // Matrix-core kernel by key type (measured on the llama3-, long-context,
   // k3v4- and k8v4-shaped decodes): FP8 keys take the page-cooperative
   // kernel; 3/4-bit keys with at most 8 query heads per kv head the ring
@@ -379,12 +379,23 @@ DecodePlan plan_decode(const Geometry& g, int batch, int num_q_heads, int max_se
     // one resident round of workgroups (256 CUs x the workgroups that fit per
     // CU) over (sequence, split), at least 4 slabs of 16 tokens per split so
     // the load pipeline's start is amortised
+    // kv heads per workgroup: the whole row, at most 8 (measured fastest:
+    // smaller groups were slower for FP8 keys); TQ_DECODE_PAGE_HEADS=1|2|4
+    // takes smaller groups (for measurements)
+    int group = g.num_kv_heads < 8 ? g.num_kv_heads : 8;
+    const char* ph = getenv("TQ_DECODE_PAGE_HEADS");
+    if (ph != nullptr) {
+      const int want = atoi(ph);
+      if ((want == 1 || want == 2 || want == 4) && g.num_kv_heads % want == 0) group = want;
+    }
     const int slabs = max_seq_len > 0 ? (max_seq_len + 15) / 16 : 1;
-    const int target = 256 * page_wgs_per_cu(g);
-    int s = batch > 0 ? (target + batch - 1) / batch : 1;
+    const int target = 256 * page_wgs_per_cu(g, group);
+    const int per_split = batch * (g.num_kv_heads / group);
+    int s = per_split > 0 ? (target + per_split - 1) / per_split : 1;
     const int s_max = (slabs + 3) / 4;
     s = s < 1 ? 1 : (s > s_max ? s_max : s);
     p.mfma = 2;
+    p.group = group;
     p.chunk = 16 * ((slabs + s - 1) / s);
     if (p.chunk > 16 * 256) p.chunk = 16 * 256;       // page ids of a split fit in LDS
     p.num_splits = max_seq_len > 0 ? (max_seq_len + p.chunk - 1) / p.chunk : 1;

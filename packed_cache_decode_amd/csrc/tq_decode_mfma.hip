@@ -1089,14 +1089,15 @@ struct PageGeom {
   static_assert(kLoads * (kNbuf - 2) < 64, "vmcnt out of range");
   static_assert(kVOff + 64 + 4 <= kSlotL, "V part does not fit");
 
-  // cache byte offset, within the slab, of LDS chunk c (past the slab: an
-  // offset beyond every buffer range, so the load returns zeros)
-  __device__ static uint32_t chunk_src(int c) {
+  // cache byte offset, from the first slot of the workgroup's heads in the
+  // slab's first row (rows row_bytes apart), of LDS chunk c (past the slab:
+  // an offset beyond every buffer range, so the load returns zeros)
+  __device__ static uint32_t chunk_src(int c, uint32_t row_bytes) {
     if (c >= kSlabChunks) return 0x7FFFFFF0u;
     const int si = c / (kNK + kNV), k = c - si * (kNK + kNV);
     const int row = si / H, head = si - row * H;
     const int off = k < kNK ? 16 * k : kKP + 16 * (k - kNK);
-    return static_cast<uint32_t>(row * kRow + head * SLOT + off);
+    return static_cast<uint32_t>(row * row_bytes + head * SLOT + off);
   }
 };
 
@@ -1311,14 +1312,19 @@ __global__ void __launch_bounds__(64 * H, page_waves_per_simd(KB)) decode_page_k
   u32x2* tab = s_tab;
   int32_t* s_pid = reinterpret_cast<int32_t*>(smem + Geo::kPidOff);
 
-  const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));   // kv head
+  // wavefront w takes kv head g = hg*H + w of the workgroup's head group hg
+  // (the H kv heads of a row, or a part of them)
+  const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
   const int lane = threadIdx.x & 63;
   const int r16 = lane & 15;
   const int g4 = lane >> 4;
-  const int b = blockIdx.x / a.num_splits;
-  const int split = blockIdx.x % a.num_splits;
+  const int HG = a.H / H;
+  const int hg = blockIdx.x % HG;
+  const int b = (blockIdx.x / HG) / a.num_splits;
+  const int split = (blockIdx.x / HG) % a.num_splits;
+  const int g = hg * H + w;
 
-  const int T = clamp_len(a, b, split, w);
+  const int T = clamp_len(a, b, split, g);
   const int t0 = split * a.chunk;
   const int t1 = min(T, t0 + a.chunk);
   if (t0 >= t1) return;                      // the whole workgroup, before any barrier
@@ -1329,9 +1335,9 @@ __global__ void __launch_bounds__(64 * H, page_waves_per_simd(KB)) decode_page_k
   h8 qc[4];
   bf8v qb[4];
   if constexpr (KB == 8)
-    load_queries_bf16(a, b, w, r16, g4, qb);
+    load_queries_bf16(a, b, g, r16, g4, qb);
   else
-    load_queries_packed(a, b, w, r16, g4, qc);
+    load_queries_packed(a, b, g, r16, g4, qc);
   RunState st;
 #pragma unroll
   for (int m = 0; m < 8; ++m) st.O[m] = f4{0.f, 0.f, 0.f, 0.f};
@@ -1342,12 +1348,18 @@ __global__ void __launch_bounds__(64 * H, page_waves_per_simd(KB)) decode_page_k
 
   const int p_first = t0 >> a.bs_shift;
   const int bs_mask = (1 << a.bs_shift) - 1;
-  const int64_t page_bytes = static_cast<int64_t>(1 << a.bs_shift) * Geo::kRow;
+  const int64_t row_bytes = static_cast<int64_t>(a.H) * SLOT;
+  const int64_t page_bytes = static_cast<int64_t>(1 << a.bs_shift) * row_bytes;
+  const uint32_t group_off = static_cast<uint32_t>(hg * H * SLOT);
+  // the 16 rows from the group's first slot; the last chunks of its last
+  // slot may run into the next group's first slot (never past the 16 rows)
+  const uint32_t range = static_cast<uint32_t>(16 * row_bytes) - group_off;
   const int n_slabs = (t1 - t0 + 15) >> 4;
   const bool full_loads = w < Geo::kFull;
   uint32_t src_off[Geo::kLoads];
 #pragma unroll
-  for (int l = 0; l < Geo::kLoads; ++l) src_off[l] = Geo::chunk_src((w + H * l) * 64 + lane);
+  for (int l = 0; l < Geo::kLoads; ++l)
+    src_off[l] = Geo::chunk_src((w + H * l) * 64 + lane, static_cast<uint32_t>(row_bytes));
   u32x4* s_src = reinterpret_cast<u32x4*>(smem + Geo::kSrcOff) + threadIdx.x;
   if constexpr (Geo::kSrcInLds) {
     u32x4 v = {0u, 0u, 0u, 0u};
@@ -1367,9 +1379,9 @@ __global__ void __launch_bounds__(64 * H, page_waves_per_simd(KB)) decode_page_k
     int pid = -1;
     if (t < t1) pid = s_pid[(t >> a.bs_shift) - p_first];
     pid = __builtin_amdgcn_readfirstlane(pid);
-    const int64_t off = pid >= 0 ? pid * page_bytes + static_cast<int64_t>(t & bs_mask) * Geo::kRow : 0;
+    const int64_t off = pid >= 0 ? pid * page_bytes + static_cast<int64_t>(t & bs_mask) * row_bytes + group_off : 0;
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint8_t*>(a.cache) + off, 0, pid >= 0 ? Geo::kSlab : 0, kBufferWord3);
+        const_cast<uint8_t*>(a.cache) + off, 0, pid >= 0 ? static_cast<int>(range) : 0, kBufferWord3);
     uint8_t* dst = smem + Geo::kRingOff + (j % Geo::kNbuf) * Geo::kBuf;
     u32x4 so;
     if constexpr (Geo::kSrcInLds) {
@@ -1440,7 +1452,7 @@ __global__ void __launch_bounds__(64 * H, page_waves_per_simd(KB)) decode_page_k
     ++j;
   }
   wait_vmcnt<0>();                           // no load may still write LDS at exit
-  store_partials(a, b, w, split, g4, r16, st);
+  store_partials(a, b, g, split, g4, r16, st);
 }
 
 // ============================================================================
@@ -1670,6 +1682,7 @@ __global__ void __launch_bounds__(64 * kRingWaves) decode_ring_kernel(MfmaArgs a
 
 template <int KB, int SLOT, int H>
 hipError_t launch_page_t(const MfmaArgs& a, int batch, hipStream_t stream) {
+  // one workgroup per (sequence, split, group of H kv heads)
   using Geo = PageGeom<KB, SLOT, H>;
   static bool attr_set = false;
   if (!attr_set) {
@@ -1678,14 +1691,14 @@ hipError_t launch_page_t(const MfmaArgs& a, int batch, hipStream_t stream) {
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL((decode_page_kernel<KB, SLOT, H>), dim3(batch * a.num_splits), dim3(64 * H),
+  hipLaunchKernelGGL((decode_page_kernel<KB, SLOT, H>), dim3(batch * a.num_splits * (a.H / H)), dim3(64 * H),
                      Geo::kDynLds, stream, a);
   return hipGetLastError();
 }
 
 template <int KB, int SLOT>
-hipError_t launch_page_h(const MfmaArgs& a, int batch, hipStream_t stream) {
-  switch (a.H) {
+hipError_t launch_page_h(const MfmaArgs& a, int batch, int group, hipStream_t stream) {
+  switch (group) {
     case 1: return launch_page_t<KB, SLOT, 1>(a, batch, stream);
     case 2: return launch_page_t<KB, SLOT, 2>(a, batch, stream);
     case 4: return launch_page_t<KB, SLOT, 4>(a, batch, stream);
@@ -1715,7 +1728,8 @@ bool page_decode_eligible(const Geometry& g, int num_q_heads, bool mse_keys_too)
   // 3/4-bit keys: the per-head kernel is still the faster one (the page
   // kernel's centroid lookups are bound by LDS bank conflicts), unless asked
   const bool kind_ok = g.key_bits == 8 || mse_keys_too;
-  return mfma_decode_eligible(g, num_q_heads) && g_ok && kind_ok && (H == 1 || H == 2 || H == 4 || H == 8);
+  // a workgroup takes up to 8 kv heads of a row
+  return mfma_decode_eligible(g, num_q_heads) && g_ok && kind_ok && (H == 1 || H == 2 || H == 4 || H % 8 == 0);
 }
 
 bool ring_decode_eligible(const Geometry& g, int num_q_heads) {
@@ -1725,8 +1739,8 @@ bool ring_decode_eligible(const Geometry& g, int num_q_heads) {
 
 int ring_max_slabs() { return kRingMaxSlabs; }
 
-int page_wgs_per_cu(const Geometry& g) {
-  const int H = g.num_kv_heads;
+int page_wgs_per_cu(const Geometry& g, int group) {
+  const int H = group;
   int lds = 0;
 #define TQ_PAGE_LDS(KB_, SLOT_)                                                   \
   if (g.key_bits == KB_) {                                                        \
@@ -1791,9 +1805,9 @@ hipError_t launch_decode_mfma(const Geometry& g, const DevTables* tables, const 
     return hipGetLastError();
   }
   if (plan.mfma == 2) {
-    hipError_t e = g.key_bits == 8 ? launch_page_h<8, 196>(a, batch, stream)
-                 : g.key_bits == 4 ? launch_page_h<4, 134>(a, batch, stream)
-                                   : launch_page_h<3, 118>(a, batch, stream);
+    hipError_t e = g.key_bits == 8 ? launch_page_h<8, 196>(a, batch, plan.group, stream)
+                 : g.key_bits == 4 ? launch_page_h<4, 134>(a, batch, plan.group, stream)
+                                   : launch_page_h<3, 118>(a, batch, plan.group, stream);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(decode_merge_kernel, dim3(batch * num_q_heads), dim3(256), 0, stream, a);
     return hipGetLastError();

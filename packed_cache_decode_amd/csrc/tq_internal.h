@@ -66,6 +66,7 @@ struct DecodePlan {
   int mfma;         // matrix-core kernels (tq_decode_mfma.hip): 2 page-cooperative,
                     // 3 staged per-head, 4 ring per-head, 1 direct per-head;
                     // 0: general kernel
+  int group;        // page kernel: kv heads per workgroup (1, 2, 4 or 8)
   int chunk;        // tokens per split
   int num_splits;   // splits per sequence (grid extent)
   size_t workspace_bytes;
@@ -73,7 +74,7 @@ struct DecodePlan {
 
 bool mfma_decode_eligible(const Geometry& g, int num_q_heads);
 bool page_decode_eligible(const Geometry& g, int num_q_heads, bool mse_keys_too);
-int page_wgs_per_cu(const Geometry& g);
+int page_wgs_per_cu(const Geometry& g, int group);
 bool staged_decode_eligible(const Geometry& g, int num_q_heads);
 bool ring_decode_eligible(const Geometry& g, int num_q_heads);
 int ring_max_slabs();

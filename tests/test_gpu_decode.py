@@ -83,6 +83,23 @@ def test_decode_kernels_head_counts(preset, H, kernel, monkeypatch):
     check_decode(got, want, bf16_out=False)
 
 
+@pytest.mark.parametrize("preset", PRESETS)
+@pytest.mark.parametrize("group", ["1", "2", "4"])
+def test_decode_page_kernel_head_groups(preset, group, monkeypatch):
+    # the page kernel with a workgroup per part of a page row's kv heads
+    monkeypatch.setenv("TQ_DECODE_KERNEL", "page")
+    monkeypatch.setenv("TQ_DECODE_PAGE_HEADS", group)
+    got, want = _decode_from_oracle_cache(_wl(preset, G=4, H=8, B=3, lens=(1, 300), seed=50))
+    check_decode(got, want, bf16_out=False)
+
+
+@pytest.mark.parametrize("preset", ["turboquant_k8v4", "turboquant_4bit_nc"])
+def test_decode_sixteen_kv_heads(preset):
+    # 16 kv heads per row: FP8 keys take the page kernel in groups of 8 heads
+    got, want = _decode_from_oracle_cache(_wl(preset, G=2, H=16, B=2, lens=(1, 200), seed=51))
+    check_decode(got, want, bf16_out=False)
+
+
 @pytest.mark.parametrize("preset", ["turboquant_4bit_nc", "turboquant_k3v4_nc"])
 @pytest.mark.parametrize("kernel", ["page", "staged", "direct", "ring"])
 def test_decode_kernels_mse_ragged(preset, kernel, monkeypatch):

@@ -54,7 +54,9 @@ typedef enum {
 typedef enum {
   TQ_K8V4 = 0,      /* K fp8-e4m3,           V 4-bit, no norm correction */
   TQ_4BIT_NC = 1,   /* K 4-bit Lloyd-Max,    V 4-bit, norm correction    */
-  TQ_K3V4_NC = 2    /* K 3-bit Lloyd-Max,    V 4-bit, norm correction    */
+  TQ_K3V4_NC = 2,   /* K 3-bit Lloyd-Max,    V 4-bit, norm correction    */
+  TQ_3BIT_NC = 3    /* K 3-bit Lloyd-Max,    V 3-bit, norm correction
+                       (V scale = (max - min) / 7, codes packed like 3-bit K) */
 } tq_preset;
 
 /* How the codebook is solved (P1, sections "Lloyd-Max 的两个最优性条件" and

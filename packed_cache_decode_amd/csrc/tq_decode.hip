@@ -78,14 +78,14 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
-template <int D, int KB, int G>
+template <int D, int KB, int G, int VB>
 __global__ void __launch_bounds__(64) decode_split_kernel(DecodeArgs a) {
   constexpr int E = D / 64;
   constexpr bool kFp8 = KB == 8;
   constexpr int kKeyCodeBytes = kFp8 ? D : (D * KB + 7) / 8;
   constexpr int kKeyPacked = kFp8 ? D : kKeyCodeBytes + 2;
   constexpr int kValOff = kKeyPacked;
-  constexpr int kValCodeBytes = D / 2;
+  constexpr int kValCodeBytes = D * VB / 8;
   constexpr int kSlotRaw = kKeyPacked + kValCodeBytes + 4;
   constexpr int kSlot = kSlotRaw + (kSlotRaw & 1);
 
@@ -265,7 +265,16 @@ __global__ void __launch_bounds__(64) decode_split_kernel(DecodeArgs a) {
       if (o < 0) continue;
       const uint8_t* vrow = a.cache + o + kValOff;
       float vh[E];
-      if constexpr (E == 1) {
+      if constexpr (VB == 3) {
+        // code c at stream bits [3c, 3c + 3); the byte after the last code
+        // byte is the scale's first, inside the slot
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const int bit = 3 * (E * lane + e);
+          const uint32_t two = vrow[bit >> 3] | (static_cast<uint32_t>(vrow[(bit >> 3) + 1]) << 8);
+          vh[e] = static_cast<float>((two >> (bit & 7)) & 7u);
+        }
+      } else if constexpr (E == 1) {
         const uint32_t byte = vrow[lane >> 1];
         vh[0] = static_cast<float>((byte >> ((lane & 1) * 4)) & 15u);
       } else {
@@ -340,9 +349,9 @@ __global__ void __launch_bounds__(64) decode_combine_kernel(DecodeArgs a) {
   }
 }
 
-template <int D, int KB, int G>
+template <int D, int KB, int G, int VB>
 hipError_t launch_t(const DecodeArgs& a, int batch, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_split_kernel<D, KB, G>), dim3(a.num_splits, batch, a.H), dim3(64), 0,
+  hipLaunchKernelGGL((decode_split_kernel<D, KB, G, VB>), dim3(a.num_splits, batch, a.H), dim3(64), 0,
                      stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -350,14 +359,14 @@ hipError_t launch_t(const DecodeArgs& a, int batch, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int D, int KB>
+template <int D, int KB, int VB>
 hipError_t launch_g(const DecodeArgs& a, int G, int batch, hipStream_t stream) {
   switch (G) {
-    case 1: return launch_t<D, KB, 1>(a, batch, stream);
-    case 2: return launch_t<D, KB, 2>(a, batch, stream);
-    case 4: return launch_t<D, KB, 4>(a, batch, stream);
-    case 8: return launch_t<D, KB, 8>(a, batch, stream);
-    case 16: return launch_t<D, KB, 16>(a, batch, stream);
+    case 1: return launch_t<D, KB, 1, VB>(a, batch, stream);
+    case 2: return launch_t<D, KB, 2, VB>(a, batch, stream);
+    case 4: return launch_t<D, KB, 4, VB>(a, batch, stream);
+    case 8: return launch_t<D, KB, 8, VB>(a, batch, stream);
+    case 16: return launch_t<D, KB, 16, VB>(a, batch, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -484,11 +493,11 @@ hipError_t launch_decode(const Geometry& g, const DevTables* tables, const Decod
   a.out = out;
   a.out_fp32 = out_is_fp32;
   const int G = num_q_heads / g.num_kv_heads;
-#define TQ_DEC_CASE(D_, KB_) \
-  if (g.head_dim == D_ && g.key_bits == KB_) return launch_g<D_, KB_>(a, G, batch, stream);
-  TQ_DEC_CASE(64, 3) TQ_DEC_CASE(64, 4) TQ_DEC_CASE(64, 8)
-  TQ_DEC_CASE(128, 3) TQ_DEC_CASE(128, 4) TQ_DEC_CASE(128, 8)
-  TQ_DEC_CASE(256, 3) TQ_DEC_CASE(256, 4) TQ_DEC_CASE(256, 8)
+#define TQ_DEC_CASE(D_, KB_, VB_) \
+  if (g.head_dim == D_ && g.key_bits == KB_ && g.value_bits == VB_) return launch_g<D_, KB_, VB_>(a, G, batch, stream);
+  TQ_DEC_CASE(64, 3, 4) TQ_DEC_CASE(64, 4, 4) TQ_DEC_CASE(64, 8, 4) TQ_DEC_CASE(64, 3, 3)
+  TQ_DEC_CASE(128, 3, 4) TQ_DEC_CASE(128, 4, 4) TQ_DEC_CASE(128, 8, 4) TQ_DEC_CASE(128, 3, 3)
+  TQ_DEC_CASE(256, 3, 4) TQ_DEC_CASE(256, 4, 4) TQ_DEC_CASE(256, 8, 4) TQ_DEC_CASE(256, 3, 3)
 #undef TQ_DEC_CASE
   return hipErrorInvalidValue;
 }

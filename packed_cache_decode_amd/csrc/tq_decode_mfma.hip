@@ -321,9 +321,54 @@ __device__ __forceinline__ void score_slab8(const SlabOps8& op, int valid_rows, 
   for (int r = 0; r < 4; ++r) s[r] = 4 * g4 + r < valid_rows ? S[r] * scale_log2 : -INFINITY;
 }
 
+// V bits of the slot sizes the matrix-core kernels take at d = 128: 102-byte
+// slots (3-bit K, 3-bit V), else 4-bit V
+constexpr int vbits_of_slot(int slot) { return slot == 102 ? 3 : 4; }
+
+// MFMA B operands of the V codes of tokens 4*g4 + r (X[r]: the token's codes
+// of coordinates 8*r16 .. 8*r16 + 7) for coordinates 8*r16 + 2*kb (Blo) and
+// 8*r16 + 2*kb + 1 (Bhi), as exact f16 integers: code c becomes the f16 with
+// bits 0x6400 | c (1024 + c) minus 1024, and for the high nibble of a 4-bit
+// byte 0x5400 | (c << 4) (64 + c) minus 64
+template <int VB>
+__device__ __forceinline__ void v_operands(const uint32_t (&X)[4], int kb, h4& Blo, h4& Bhi) {
+  const h2 b1024 = {static_cast<_Float16>(1024.0f), static_cast<_Float16>(1024.0f)};
+  if constexpr (VB == 4) {
+    const h2 b64 = {static_cast<_Float16>(64.0f), static_cast<_Float16>(64.0f)};
+    // byte kb of each token's dword -> [x0, 0, x1, 0]
+    const uint32_t sel = kb | (0x0Cu << 8) | ((4u + kb) << 16) | (0x0Cu << 24);
+    const uint32_t p01 = __builtin_amdgcn_perm(X[1], X[0], sel);
+    const uint32_t p23 = __builtin_amdgcn_perm(X[3], X[2], sel);
+    h2 lo01 = __builtin_bit_cast(h2, insert_bits(p01, 0x000F000Fu, 0x64006400u));
+    h2 lo23 = __builtin_bit_cast(h2, insert_bits(p23, 0x000F000Fu, 0x64006400u));
+    h2 hi01 = __builtin_bit_cast(h2, insert_bits(p01, 0x00F000F0u, 0x54005400u));
+    h2 hi23 = __builtin_bit_cast(h2, insert_bits(p23, 0x00F000F0u, 0x54005400u));
+    lo01 -= b1024;
+    lo23 -= b1024;
+    hi01 -= b64;
+    hi23 -= b64;
+    Blo = h4{lo01[0], lo01[1], lo23[0], lo23[1]};
+    Bhi = h4{hi01[0], hi01[1], hi23[0], hi23[1]};
+  } else {
+    // 3-bit codes: code m of a token at bits [3m, 3m + 3) of its X
+    const uint32_t m0 = 6 * kb, m1 = 6 * kb + 3;
+    h2 lo01 = __builtin_bit_cast(h2, __builtin_amdgcn_ubfe(X[0], m0, 3) | (__builtin_amdgcn_ubfe(X[1], m0, 3) << 16) | 0x64006400u);
+    h2 lo23 = __builtin_bit_cast(h2, __builtin_amdgcn_ubfe(X[2], m0, 3) | (__builtin_amdgcn_ubfe(X[3], m0, 3) << 16) | 0x64006400u);
+    h2 hi01 = __builtin_bit_cast(h2, __builtin_amdgcn_ubfe(X[0], m1, 3) | (__builtin_amdgcn_ubfe(X[1], m1, 3) << 16) | 0x64006400u);
+    h2 hi23 = __builtin_bit_cast(h2, __builtin_amdgcn_ubfe(X[2], m1, 3) | (__builtin_amdgcn_ubfe(X[3], m1, 3) << 16) | 0x64006400u);
+    lo01 -= b1024;
+    lo23 -= b1024;
+    hi01 -= b1024;
+    hi23 -= b1024;
+    Blo = h4{lo01[0], lo01[1], lo23[0], lo23[1]};
+    Bhi = h4{hi01[0], hi01[1], hi23[0], hi23[1]};
+  }
+}
+
 // Online softmax and P.V of one slab from its scores (base 2, -inf for masked
 // rows).  Rows of query heads >= G have q = 0: their scores, weights and O
 // rows are finite and never stored.
+template <int VB>
 __device__ __forceinline__ void softmax_pv(const float (&s)[4], int valid_rows, const uint32_t (&sz)[4],
                                            const uint32_t (&X)[4], int g4, RunState& st) {
   float pm = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
@@ -370,27 +415,14 @@ __device__ __forceinline__ void softmax_pv(const float (&s)[4], int valid_rows, 
   }
 
   // ---- V: codes of tokens 4*g4 + r at coordinates 8*r16 + m ----
-  const h2 b1024 = {static_cast<_Float16>(1024.0f), static_cast<_Float16>(1024.0f)};
-  const h2 b64 = {static_cast<_Float16>(64.0f), static_cast<_Float16>(64.0f)};
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb) {
-    // byte kb of each token's dword -> [x0, 0, x1, 0]
-    const uint32_t sel = kb | (0x0Cu << 8) | ((4u + kb) << 16) | (0x0Cu << 24);
-    const uint32_t p01 = __builtin_amdgcn_perm(X[1], X[0], sel);
-    const uint32_t p23 = __builtin_amdgcn_perm(X[3], X[2], sel);
-    // low nibble -> 1024 + code, high nibble -> 64 + code (exact f16), minus the bias
-    h2 lo01 = __builtin_bit_cast(h2, insert_bits(p01, 0x000F000Fu, 0x64006400u));
-    h2 lo23 = __builtin_bit_cast(h2, insert_bits(p23, 0x000F000Fu, 0x64006400u));
-    h2 hi01 = __builtin_bit_cast(h2, insert_bits(p01, 0x00F000F0u, 0x54005400u));
-    h2 hi23 = __builtin_bit_cast(h2, insert_bits(p23, 0x00F000F0u, 0x54005400u));
-    lo01 -= b1024;
-    lo23 -= b1024;
-    hi01 -= b64;
-    hi23 -= b64;
+    h4 Blo4, Bhi4;
+    v_operands<VB>(X, kb, Blo4, Bhi4);
     // one K = 32 product per tile: W and Wl of tokens 4*g4 + r meet the
     // same codes, listed twice
-    const h8 Blo = {lo01[0], lo01[1], lo23[0], lo23[1], lo01[0], lo01[1], lo23[0], lo23[1]};
-    const h8 Bhi = {hi01[0], hi01[1], hi23[0], hi23[1], hi01[0], hi01[1], hi23[0], hi23[1]};
+    const h8 Blo = {Blo4[0], Blo4[1], Blo4[2], Blo4[3], Blo4[0], Blo4[1], Blo4[2], Blo4[3]};
+    const h8 Bhi = {Bhi4[0], Bhi4[1], Bhi4[2], Bhi4[3], Bhi4[0], Bhi4[1], Bhi4[2], Bhi4[3]};
     const h8 Ws = {W[0], W[1], W[2], W[3], Wl[0], Wl[1], Wl[2], Wl[3]};
     st.O[2 * kb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ws, Blo, st.O[2 * kb], 0, 0, 0);
     st.O[2 * kb + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ws, Bhi, st.O[2 * kb + 1], 0, 0, 0);
@@ -437,6 +469,7 @@ __device__ __forceinline__ void softmax_rescale(const SlabSoftmax& sm, bool diag
   st.m_run = m_new;
 }
 
+template <int VB>
 __device__ __forceinline__ void softmax_accumulate(const float (&s)[4], const SlabSoftmax& sm,
                                                    const uint32_t (&X)[4], RunState& st) {
   // p * scale as f16 hi + lo: one f16 alone (2^-11) is not precise enough
@@ -451,23 +484,12 @@ __device__ __forceinline__ void softmax_accumulate(const float (&s)[4], const Sl
     W[r] = static_cast<_Float16>(wf);
     Wl[r] = static_cast<_Float16>(wf - static_cast<float>(W[r]));
   }
-  const h2 b1024 = {static_cast<_Float16>(1024.0f), static_cast<_Float16>(1024.0f)};
-  const h2 b64 = {static_cast<_Float16>(64.0f), static_cast<_Float16>(64.0f)};
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb) {
-    const uint32_t sel = kb | (0x0Cu << 8) | ((4u + kb) << 16) | (0x0Cu << 24);
-    const uint32_t p01 = __builtin_amdgcn_perm(X[1], X[0], sel);
-    const uint32_t p23 = __builtin_amdgcn_perm(X[3], X[2], sel);
-    h2 lo01 = __builtin_bit_cast(h2, insert_bits(p01, 0x000F000Fu, 0x64006400u));
-    h2 lo23 = __builtin_bit_cast(h2, insert_bits(p23, 0x000F000Fu, 0x64006400u));
-    h2 hi01 = __builtin_bit_cast(h2, insert_bits(p01, 0x00F000F0u, 0x54005400u));
-    h2 hi23 = __builtin_bit_cast(h2, insert_bits(p23, 0x00F000F0u, 0x54005400u));
-    lo01 -= b1024;
-    lo23 -= b1024;
-    hi01 -= b64;
-    hi23 -= b64;
-    const h8 Blo = {lo01[0], lo01[1], lo23[0], lo23[1], lo01[0], lo01[1], lo23[0], lo23[1]};
-    const h8 Bhi = {hi01[0], hi01[1], hi23[0], hi23[1], hi01[0], hi01[1], hi23[0], hi23[1]};
+    h4 Blo4, Bhi4;
+    v_operands<VB>(X, kb, Blo4, Bhi4);
+    const h8 Blo = {Blo4[0], Blo4[1], Blo4[2], Blo4[3], Blo4[0], Blo4[1], Blo4[2], Blo4[3]};
+    const h8 Bhi = {Bhi4[0], Bhi4[1], Bhi4[2], Bhi4[3], Bhi4[0], Bhi4[1], Bhi4[2], Bhi4[3]};
     const h8 Ws = {W[0], W[1], W[2], W[3], Wl[0], Wl[1], Wl[2], Wl[3]};
     st.O[2 * kb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ws, Blo, st.O[2 * kb], 0, 0, 0);
     st.O[2 * kb + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ws, Bhi, st.O[2 * kb + 1], 0, 0, 0);
@@ -476,13 +498,13 @@ __device__ __forceinline__ void softmax_accumulate(const float (&s)[4], const Sl
 }
 
 // One slab of 3/4-bit keys: scores, norm correction, online softmax, P.V.
-template <int KB>
+template <int KB, int VB>
 __device__ __forceinline__ void process_slab(const SlabOps<KB>& op, int valid_rows,
                                              const u32x2* s_tab, const h8 (&qhi)[4],
                                              const h8 (&qlo)[4], int g4, RunState& st) {
   float s[4];
   score_slab<KB>(op, valid_rows, s_tab, qhi, qlo, g4, s);
-  softmax_pv(s, valid_rows, op.sz, op.X, g4, st);
+  softmax_pv<VB>(s, valid_rows, op.sz, op.X, g4, st);
 }
 
 // page ids of this split -> byte offsets in LDS (-1: outside the cache)
@@ -675,7 +697,7 @@ __device__ __forceinline__ DirectOffsets direct_offsets(int r16, int g4, uint32_
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     o.row[r] = (4 * g4 + r) * rb + head_off;
-    o.x[r] = o.row[r] + kKP + 4 * r16;
+    o.x[r] = o.row[r] + kKP + (vbits_of_slot(SLOT) == 3 ? 3 : 4) * r16;
   }
   return o;
 }
@@ -703,7 +725,7 @@ __device__ __forceinline__ void direct_load2(__amdgpu_buffer_rsrc_t rs, const Di
   for (int r = 0; r < 4; ++r) {
     d.X[r] = __builtin_amdgcn_raw_buffer_load_b32(rs, o.x[r], 0, 0);
     if constexpr (KB != 8) d.n[r] = __builtin_amdgcn_raw_buffer_load_b16(rs, o.row[r] + kKCB, 0, 0);
-    d.sz[r] = __builtin_amdgcn_raw_buffer_load_b32(rs, o.row[r] + kKP + kD / 2, 0, 0);
+    d.sz[r] = __builtin_amdgcn_raw_buffer_load_b32(rs, o.row[r] + kKP + kD * vbits_of_slot(SLOT) / 8, 0, 0);
   }
 }
 
@@ -798,7 +820,7 @@ __global__ void __launch_bounds__(64, kSlabWavesPerSimd<KB>) decode_slab_kernel(
         for (int i = 0; i < 4; ++i) op.n[i] = cur.n[i];
         score_slab<KB>(op, t1 - t, s_tab, qhi, qlo, g4, sc);
       }
-      softmax_pv(sc, t1 - t, cur.sz, cur.X, g4, st);
+      softmax_pv<vbits_of_slot(SLOT)>(sc, t1 - t, cur.sz, cur.X, g4, st);
     }
     if constexpr (!kLoadEarly<KB>) load(t + 32, r);
   };
@@ -913,7 +935,7 @@ __device__ __forceinline__ SlabOps<KB> staged_ops(const uint8_t* lds, int r16, i
   using S = StageShape<SLOT>;
   constexpr int kKCB = (kD * KB) / 8;
   constexpr int kKP = kKCB + 2;
-  constexpr int kVCB = kD / 2;
+  constexpr int kVCB = kD * vbits_of_slot(SLOT) / 8;
   constexpr int kLaneKB = KB == 4 ? 16 : 12;
   SlabOps<KB> op;
   {
@@ -928,7 +950,7 @@ __device__ __forceinline__ SlabOps<KB> staged_ops(const uint8_t* lds, int r16, i
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const uint32_t rowo = (4 * g4 + r) * S::kRow + sh;
-    const uint32_t vo = rowo + kKP + 4 * r16;
+    const uint32_t vo = rowo + kKP + (vbits_of_slot(SLOT) == 3 ? 3 : 4) * r16;
     const uint32_t* pv = reinterpret_cast<const uint32_t*>(lds + (vo & ~3u));
     op.X[r] = __builtin_amdgcn_alignbyte(pv[1], pv[0], vo & 3u);
     op.n[r] = *reinterpret_cast<const uint16_t*>(lds + rowo + kKCB);
@@ -1007,7 +1029,7 @@ __global__ void __launch_bounds__(64, kStagedWavesPerSimd<KB>) decode_staged_ker
     const bool ok = r.ok;
     stage_store<SLOT>(lds, lane, r);
     load(t + 32, r);
-    if (ok) process_slab<KB>(staged_ops<KB, SLOT>(lds, r16, g4, sh), t1 - t, s_tab, qhi, qlo, g4, st);
+    if (ok) process_slab<KB, vbits_of_slot(SLOT)>(staged_ops<KB, SLOT>(lds, r16, g4, sh), t1 - t, s_tab, qhi, qlo, g4, st);
   };
   load(t0, r0);
   load(t0 + 16, r1);
@@ -1087,7 +1109,7 @@ struct PageGeom {
   static constexpr int kDynLds = kRingOff + kNbuf * kBuf;
   static constexpr int kLds = kDynLds + kTabBytes;
   static_assert(kLoads * (kNbuf - 2) < 64, "vmcnt out of range");
-  static_assert(kVOff + 64 + 4 <= kSlotL, "V part does not fit");
+  static_assert(kVOff + kD * vbits_of_slot(SLOT) / 8 + 4 <= kSlotL, "V part does not fit");
 
   // cache byte offset, from the first slot of the workgroup's heads in the
   // slab's first row (rows row_bytes apart), of LDS chunk c (past the slab:
@@ -1204,8 +1226,15 @@ __device__ __forceinline__ void slab_read(const uint8_t* buf, int w, int r16, in
   }
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    R.X[r] = *reinterpret_cast<const uint32_t*>(rb + r * kRow + Geo::kVOff + 4 * r16);
-    R.sz[r] = *reinterpret_cast<const uint32_t*>(rb + r * kRow + Geo::kVOff + kD / 2);
+    if constexpr (vbits_of_slot(SLOT) == 4) {
+      R.X[r] = *reinterpret_cast<const uint32_t*>(rb + r * kRow + Geo::kVOff + 4 * r16);
+    } else {
+      // 3-bit codes of coordinates 8*r16 .. + 7: 3 bytes at 3*r16, read as
+      // two aligned dwords and re-aligned
+      const uint32_t* pv = reinterpret_cast<const uint32_t*>(rb + r * kRow + Geo::kVOff + ((3 * r16) & ~3));
+      R.X[r] = __builtin_amdgcn_alignbyte(pv[1], pv[0], (3 * r16) & 3);
+    }
+    R.sz[r] = *reinterpret_cast<const uint32_t*>(rb + r * kRow + Geo::kVOff + kD * vbits_of_slot(SLOT) / 8);
   }
 }
 
@@ -1444,11 +1473,11 @@ __global__ void __launch_bounds__(64 * H, page_waves_per_simd(KB)) decode_page_k
         grow = true;
         break;
       }
-      softmax_accumulate(s, sm, c.X, st);
+      softmax_accumulate<vbits_of_slot(SLOT)>(s, sm, c.X, st);
     }
     if (!grow) break;
     softmax_rescale(sm, diag, st);
-    softmax_accumulate(s, sm, c.X, st);
+    softmax_accumulate<vbits_of_slot(SLOT)>(s, sm, c.X, st);
     ++j;
   }
   wait_vmcnt<0>();                           // no load may still write LDS at exit
@@ -1602,11 +1631,11 @@ __global__ void __launch_bounds__(64 * kRingWaves) decode_ring_kernel(MfmaArgs a
           grow = true;
           break;
         }
-        softmax_accumulate(s, sm, c.X, st);
+        softmax_accumulate<vbits_of_slot(SLOT)>(s, sm, c.X, st);
       }
       if (!grow) break;
       softmax_rescale(sm, diag, st);
-      softmax_accumulate(s, sm, c.X, st);
+      softmax_accumulate<vbits_of_slot(SLOT)>(s, sm, c.X, st);
       ++j;
     }
     wait_vmcnt<0>();                         // no load may still write the ring
@@ -1743,11 +1772,11 @@ int page_wgs_per_cu(const Geometry& g, int group) {
   const int H = group;
   int lds = 0;
 #define TQ_PAGE_LDS(KB_, SLOT_)                                                   \
-  if (g.key_bits == KB_) {                                                        \
+  if (g.key_bits == KB_ && g.slot == SLOT_) {                                     \
     lds = H == 1 ? PageGeom<KB_, SLOT_, 1>::kLds : H == 2 ? PageGeom<KB_, SLOT_, 2>::kLds \
         : H == 4 ? PageGeom<KB_, SLOT_, 4>::kLds : PageGeom<KB_, SLOT_, 8>::kLds;  \
   }
-  TQ_PAGE_LDS(8, 196) TQ_PAGE_LDS(4, 134) TQ_PAGE_LDS(3, 118)
+  TQ_PAGE_LDS(8, 196) TQ_PAGE_LDS(4, 134) TQ_PAGE_LDS(3, 118) TQ_PAGE_LDS(3, 102)
 #undef TQ_PAGE_LDS
   int n = lds > 0 ? (160 * 1024) / lds : 1;
   const int by_regs = 4 * page_waves_per_simd(g.key_bits) / H;
@@ -1759,7 +1788,7 @@ bool mfma_decode_eligible(const Geometry& g, int num_q_heads) {
   const int G = num_q_heads / g.num_kv_heads;
   if (g.head_dim != kD || g.block_size % 16 != 0 || G < 1 || G > 16) return false;
   if (g.key_bits == 8) return g.slot == 196;
-  return (g.key_bits == 4 || g.key_bits == 3) && (g.slot == 134 || g.slot == 118);
+  return (g.key_bits == 4 || g.key_bits == 3) && (g.slot == 134 || g.slot == 118 || g.slot == 102);
 }
 
 size_t mfma_partial_bytes(int batch, int num_q_heads, int num_splits) {
@@ -1797,8 +1826,10 @@ hipError_t launch_decode_mfma(const Geometry& g, const DevTables* tables, const 
     const dim3 grid(8 * ((n_items + 7) / 8));
     if (g.key_bits == 4)
       hipLaunchKernelGGL((decode_ring_kernel<4, 134>), grid, dim3(64 * kRingWaves), 0, stream, a);
-    else
+    else if (g.slot == 118)
       hipLaunchKernelGGL((decode_ring_kernel<3, 118>), grid, dim3(64 * kRingWaves), 0, stream, a);
+    else
+      hipLaunchKernelGGL((decode_ring_kernel<3, 102>), grid, dim3(64 * kRingWaves), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || plan.num_splits == 1) return e;
     hipLaunchKernelGGL(decode_merge_kernel, dim3(batch * num_q_heads), dim3(256), 0, stream, a);
@@ -1807,7 +1838,8 @@ hipError_t launch_decode_mfma(const Geometry& g, const DevTables* tables, const 
   if (plan.mfma == 2) {
     hipError_t e = g.key_bits == 8 ? launch_page_h<8, 196>(a, batch, plan.group, stream)
                  : g.key_bits == 4 ? launch_page_h<4, 134>(a, batch, plan.group, stream)
-                                   : launch_page_h<3, 118>(a, batch, plan.group, stream);
+                 : g.slot == 118   ? launch_page_h<3, 118>(a, batch, plan.group, stream)
+                                   : launch_page_h<3, 102>(a, batch, plan.group, stream);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(decode_merge_kernel, dim3(batch * num_q_heads), dim3(256), 0, stream, a);
     return hipGetLastError();
@@ -1818,14 +1850,18 @@ hipError_t launch_decode_mfma(const Geometry& g, const DevTables* tables, const 
   if (plan.mfma == 3) {
     if (g.key_bits == 4)
       hipLaunchKernelGGL((decode_staged_kernel<4, 134>), grid, dim3(64), 0, stream, a);
-    else
+    else if (g.slot == 118)
       hipLaunchKernelGGL((decode_staged_kernel<3, 118>), grid, dim3(64), 0, stream, a);
+    else
+      hipLaunchKernelGGL((decode_staged_kernel<3, 102>), grid, dim3(64), 0, stream, a);
   } else if (g.key_bits == 8)
     hipLaunchKernelGGL((decode_slab_kernel<8, 196>), grid, dim3(64), 0, stream, a);
   else if (g.key_bits == 4)
     hipLaunchKernelGGL((decode_slab_kernel<4, 134>), grid, dim3(64), 0, stream, a);
-  else
+  else if (g.slot == 118)
     hipLaunchKernelGGL((decode_slab_kernel<3, 118>), grid, dim3(64), 0, stream, a);
+  else
+    hipLaunchKernelGGL((decode_slab_kernel<3, 102>), grid, dim3(64), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   // merge: one workgroup per (sequence, query head)

@@ -276,10 +276,13 @@ bool build_bins(const float* mid, int n_mid, DevTables& t) {
   return false;
 }
 
+int key_bits_of(int preset) { return preset == TQ_K8V4 ? 8 : (preset == TQ_4BIT_NC ? 4 : 3); }
+int value_bits_of(int preset) { return preset == TQ_3BIT_NC ? 3 : 4; }
+
 int slot_bytes_for(int preset, int d) {
-  const int kb = preset == TQ_K8V4 ? 8 : (preset == TQ_4BIT_NC ? 4 : 3);
+  const int kb = key_bits_of(preset);
   const int key = kb == 8 ? d : (d * kb + 7) / 8 + 2;
-  const int s = key + (d * 4 + 7) / 8 + 4;
+  const int s = key + (d * value_bits_of(preset) + 7) / 8 + 4;
   return s + (s % 2);
 }
 
@@ -303,7 +306,7 @@ tq_status tq_host_rotation_signs(uint64_t rot_seed, int head_dim, int sign_flip,
 }
 
 int64_t tq_host_slot_bytes(int preset, int head_dim) {
-  if (preset < TQ_K8V4 || preset > TQ_K3V4_NC) return -1;
+  if (preset < TQ_K8V4 || preset > TQ_3BIT_NC) return -1;
   if (head_dim != 64 && head_dim != 128 && head_dim != 256) return -1;
   return slot_bytes_for(preset, head_dim);
 }
@@ -326,7 +329,7 @@ tq_status tq_codebook_init(tq_ctx** out, int preset, int head_dim, int num_kv_he
                            void* stream) {
   if (!out) return TQ_ERR_INVALID_ARG;
   *out = nullptr;
-  if (preset < TQ_K8V4 || preset > TQ_K3V4_NC) return TQ_ERR_INVALID_ARG;
+  if (preset < TQ_K8V4 || preset > TQ_3BIT_NC) return TQ_ERR_INVALID_ARG;
   if (codebook_mode != TQ_CODEBOOK_LLOYD_MAX_EXACT && codebook_mode != TQ_CODEBOOK_PAGE_TRAPZ)
     return TQ_ERR_INVALID_ARG;
   if (num_kv_heads < 1 || num_kv_heads > 64) return TQ_ERR_INVALID_ARG;
@@ -342,8 +345,8 @@ tq_status tq_codebook_init(tq_ctx** out, int preset, int head_dim, int num_kv_he
   g.head_dim = head_dim;
   g.num_kv_heads = num_kv_heads;
   g.block_size = block_size;
-  g.key_bits = preset == TQ_K8V4 ? 8 : (preset == TQ_4BIT_NC ? 4 : 3);
-  g.value_bits = 4;
+  g.key_bits = key_bits_of(preset);
+  g.value_bits = value_bits_of(preset);
   g.norm_correction = preset == TQ_K8V4 ? 0 : 1;
   g.key_code_bytes = g.key_bits == 8 ? head_dim : (head_dim * g.key_bits + 7) / 8;
   g.key_packed = g.key_bits == 8 ? head_dim : g.key_code_bytes + 2;

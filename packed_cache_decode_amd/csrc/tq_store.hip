@@ -70,14 +70,15 @@ __device__ __forceinline__ uint32_t f32_to_e4m3fn(float x) {
   return sign | r;
 }
 
-template <int D, int KB>
+template <int D, int KB, int VB>
 __global__ void __launch_bounds__(64 * kWaves) store_kernel(StoreArgs a) {
   constexpr int E = D / 64;
   constexpr bool kFp8 = KB == 8;
   constexpr int kLevels = kFp8 ? 0 : (1 << KB);
   constexpr int kKeyCodeBytes = kFp8 ? D : (D * KB + 7) / 8;
   constexpr int kKeyPacked = kFp8 ? D : kKeyCodeBytes + 2;
-  constexpr int kValCodeBytes = D / 2;
+  constexpr int kValCodeBytes = (D * VB + 7) / 8;
+  constexpr int kVmax = (1 << VB) - 1;         // largest V code
   constexpr int kSlotRaw = kKeyPacked + kValCodeBytes + 4;
   constexpr int kSlot = kSlotRaw + (kSlotRaw & 1);
 
@@ -208,7 +209,7 @@ __global__ void __launch_bounds__(64 * kWaves) store_kernel(StoreArgs a) {
       lo = fminf(lo, __shfl_xor(lo, m, 64));
       hi = fmaxf(hi, __shfl_xor(hi, m, 64));
     }
-    float sc = (hi - lo) / 15.0f;
+    float sc = (hi - lo) / static_cast<float>(kVmax);
     if (!(sc > 1e-8f)) sc = 1e-8f;
     const float isc = 1.0f / sc;
     uint32_t q[E];
@@ -216,16 +217,35 @@ __global__ void __launch_bounds__(64 * kWaves) store_kernel(StoreArgs a) {
     for (int e = 0; e < E; ++e) {
       const float t = (vv[e] - lo) * isc + 0.5f;
       int qi = static_cast<int>(truncf(t));
-      qi = qi < 0 ? 0 : (qi > 15 ? 15 : qi);
+      qi = qi < 0 ? 0 : (qi > kVmax ? kVmax : qi);
       q[e] = static_cast<uint32_t>(qi);
     }
-    if constexpr (E == 1) {
-      const uint32_t other = __shfl_xor(q[0], 1, 64);
-      if ((lane & 1) == 0) s_slot[wave][kKeyPacked + (lane >> 1)] = static_cast<uint8_t>(q[0] | (other << 4));
-    } else {
+    if constexpr (VB == 4) {
+      if constexpr (E == 1) {
+        const uint32_t other = __shfl_xor(q[0], 1, 64);
+        if ((lane & 1) == 0) s_slot[wave][kKeyPacked + (lane >> 1)] = static_cast<uint8_t>(q[0] | (other << 4));
+      } else {
 #pragma unroll
-      for (int e = 0; e < E; e += 2)
-        s_slot[wave][kKeyPacked + (E * lane + e) / 2] = static_cast<uint8_t>(q[e] | (q[e + 1] << 4));
+        for (int e = 0; e < E; e += 2)
+          s_slot[wave][kKeyPacked + (E * lane + e) / 2] = static_cast<uint8_t>(q[e] | (q[e + 1] << 4));
+      }
+    } else {
+      // 3-bit codes: LSB-first stream, byte j holds stream bits [8j, 8j + 8)
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+#pragma unroll
+      for (int e = 0; e < E; ++e) s_code[wave][E * lane + e] = static_cast<uint8_t>(q[e]);
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      for (int j = lane; j < kValCodeBytes; j += 64) {
+        uint32_t byte = 0;
+#pragma unroll
+        for (int bit = 0; bit < 8; ++bit) {
+          const int p = 8 * j + bit;
+          byte |= ((s_code[wave][p / VB] >> (p % VB)) & 1u) << bit;
+        }
+        s_slot[wave][kKeyPacked + j] = static_cast<uint8_t>(byte);
+      }
     }
     if (lane == 0) {
       const uint16_t sb = f32_to_f16_bits(sc);
@@ -287,6 +307,15 @@ __device__ __forceinline__ uint32_t trunc_clamp15(float t) {
   return static_cast<uint32_t>(r);
 }
 
+// trunc(t) as int32 (t >= 0 here), clamped to [0, 7]
+__device__ __forceinline__ uint32_t trunc_clamp7(float t) {
+  int i;
+  asm("v_cvt_i32_f32 %0, %1" : "=v"(i) : "v"(t));
+  int r;
+  asm("v_med3_i32 %0, %1, 0, 7" : "=v"(r) : "v"(i));
+  return static_cast<uint32_t>(r);
+}
+
 // butterfly across the quad: the lower lane of the pair keeps a + b, the
 // upper lane a - b, computed as a + (-b) (the same IEEE operation)
 template <int X>
@@ -305,13 +334,15 @@ __device__ __forceinline__ void store_u16s(uint8_t* dst, const uint32_t* w, int 
 // a wavefront's 16 vectors are 16 / H whole tokens; their rows are assembled
 // in LDS and written with 16-byte stores.  Otherwise each lane writes its
 // fields with 2- or 4-byte stores.
-template <int KB, bool kRows>
+template <int KB, int VB, bool kRows>
 __global__ void __launch_bounds__(256) store128_kernel(StoreArgs a) {
   constexpr int D = 128, E = 32;
   constexpr bool kFp8 = KB == 8;
   constexpr int kKeyCodeBytes = kFp8 ? D : (D * KB) / 8;
   constexpr int kKeyPacked = kFp8 ? D : kKeyCodeBytes + 2;
-  constexpr int kValCodeBytes = D / 2;
+  constexpr int kValCodeBytes = (D * VB) / 8;
+  constexpr int kVmax = (1 << VB) - 1;         // largest V code
+  constexpr int kLaneVB = E * VB / 8;           // V code bytes of a lane's 32 coordinates
   constexpr int kSlot = kKeyPacked + kValCodeBytes + 4;    // 196 / 134 / 118, even
   static_assert(kSlot % 2 == 0, "slot must be even");
 
@@ -500,18 +531,37 @@ __global__ void __launch_bounds__(256) store128_kernel(StoreArgs a) {
     hi = fmaxf(hi, quad_xor<1>(hi));
     lo = fminf(lo, quad_xor<2>(lo));
     hi = fmaxf(hi, quad_xor<2>(hi));
-    float sc = (hi - lo) / 15.0f;
+    float sc = (hi - lo) / static_cast<float>(kVmax);
     if (!(sc > 1e-8f)) sc = 1e-8f;
     const float isc = 1.0f / sc;
-    uint32_t vout[4];
+    uint32_t vout[VB];
+    if constexpr (VB == 4) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      uint32_t w = 0;
+      for (int i = 0; i < 4; ++i) {
+        uint32_t w = 0;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        w |= trunc_clamp15((vv_[8 * i + j] - lo) * isc + 0.5f) << (4 * j);
+        for (int j = 0; j < 8; ++j) {
+          w |= trunc_clamp15((vv_[8 * i + j] - lo) * isc + 0.5f) << (4 * j);
+        }
+        vout[i] = w;
       }
-      vout[i] = w;
+    } else {
+      // 96-bit LSB-first stream: code e at bits [3e, 3e + 3)
+      uint64_t vlo = 0, vhi = 0;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const uint32_t c = trunc_clamp7((vv_[e] - lo) * isc + 0.5f);
+        const int b = 3 * e;
+        if (b + 3 <= 64) vlo |= static_cast<uint64_t>(c) << b;
+        else if (b >= 64) vhi |= static_cast<uint64_t>(c) << (b - 64);
+        else {
+          vlo |= static_cast<uint64_t>(c) << b;
+          vhi |= static_cast<uint64_t>(c) >> (64 - b);
+        }
+      }
+      vout[0] = static_cast<uint32_t>(vlo);
+      vout[1] = static_cast<uint32_t>(vlo >> 32);
+      vout[2] = static_cast<uint32_t>(vhi);
     }
 
     // ---------------- slot ----------------
@@ -528,7 +578,7 @@ __global__ void __launch_bounds__(256) store128_kernel(StoreArgs a) {
       } else {
         store_u16s(sp + (kKeyCodeBytes / 4) * qd, kout, kKeyCodeBytes / 8);
         if (qd == 0) *reinterpret_cast<uint16_t*>(sp + kKeyCodeBytes) = static_cast<uint16_t>(norm_bits);
-        store_u16s(sp + kKeyPacked + 16 * qd, vout, 8);
+        store_u16s(sp + kKeyPacked + kLaneVB * qd, vout, kLaneVB / 2);
       }
       if (qd == 3) {
         uint16_t* m = reinterpret_cast<uint16_t*>(sp + kKeyPacked + kValCodeBytes);
@@ -576,7 +626,7 @@ __global__ void __launch_bounds__(256) store128_kernel(StoreArgs a) {
       } else {
         store_u16s(dst + (kKeyCodeBytes / 4) * qd, kout, kKeyCodeBytes / 8);
         if (qd == 0) *reinterpret_cast<uint16_t*>(dst + kKeyCodeBytes) = static_cast<uint16_t>(norm_bits);
-        store_u16s(dst + kKeyPacked + 16 * qd, vout, 8);
+        store_u16s(dst + kKeyPacked + kLaneVB * qd, vout, kLaneVB / 2);
       }
       if (qd == 3) {
         uint16_t* m = reinterpret_cast<uint16_t*>(dst + kKeyPacked + kValCodeBytes);
@@ -589,28 +639,28 @@ __global__ void __launch_bounds__(256) store128_kernel(StoreArgs a) {
   for (uint32_t base = wave_id * 16; base < total; base += stride) process(fetch(base), base);
 }
 
-template <int KB>
+template <int KB, int VB>
 hipError_t launch_store128(const StoreArgs& a, hipStream_t stream) {
-  constexpr int kSlot = KB == 8 ? 196 : (KB == 4 ? 134 : 118);
+  constexpr int kSlot = KB == 8 ? 196 : (KB == 4 ? 134 : (VB == 4 ? 118 : 102));
   const int64_t total = a.num_tokens * a.H;
   int64_t blocks = (total + 63) / 64;               // 64 vectors per 256-thread block
   if (blocks > 8192) blocks = 8192;
   const bool rows = 16 % a.H == 0 && (static_cast<int64_t>(a.H) * kSlot) % 16 == 0;
   if (rows)
-    hipLaunchKernelGGL((store128_kernel<KB, true>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0,
+    hipLaunchKernelGGL((store128_kernel<KB, VB, true>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0,
                        stream, a);
   else
-    hipLaunchKernelGGL((store128_kernel<KB, false>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0,
+    hipLaunchKernelGGL((store128_kernel<KB, VB, false>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0,
                        stream, a);
   return hipGetLastError();
 }
 
-template <int D, int KB>
+template <int D, int KB, int VB>
 hipError_t launch_store_t(const StoreArgs& a, hipStream_t stream) {
   const int64_t total = a.num_tokens * a.H;
   int64_t blocks = (total + kWaves - 1) / kWaves;
   if (blocks > 65536) blocks = 65536;
-  hipLaunchKernelGGL((store_kernel<D, KB>), dim3(static_cast<unsigned>(blocks)),
+  hipLaunchKernelGGL((store_kernel<D, KB, VB>), dim3(static_cast<unsigned>(blocks)),
                      dim3(64 * kWaves), 0, stream, a);
   return hipGetLastError();
 }
@@ -638,15 +688,16 @@ hipError_t launch_store(const Geometry& g, const DevTables* tables, const uint16
   // 32-bit indexing
   if (g.head_dim == 128 && num_tokens * g.num_kv_heads < (int64_t{1} << 31) &&
       (g.key_bits == 8 || g.bins_ok)) {
-    if (g.key_bits == 8) return launch_store128<8>(a, stream);
-    if (g.key_bits == 4) return launch_store128<4>(a, stream);
-    return launch_store128<3>(a, stream);
+    if (g.key_bits == 8) return launch_store128<8, 4>(a, stream);
+    if (g.key_bits == 4) return launch_store128<4, 4>(a, stream);
+    if (g.value_bits == 4) return launch_store128<3, 4>(a, stream);
+    return launch_store128<3, 3>(a, stream);
   }
-#define TQ_STORE_CASE(D_, KB_) \
-  if (g.head_dim == D_ && g.key_bits == KB_) return launch_store_t<D_, KB_>(a, stream);
-  TQ_STORE_CASE(64, 3) TQ_STORE_CASE(64, 4) TQ_STORE_CASE(64, 8)
-  TQ_STORE_CASE(128, 3) TQ_STORE_CASE(128, 4) TQ_STORE_CASE(128, 8)
-  TQ_STORE_CASE(256, 3) TQ_STORE_CASE(256, 4) TQ_STORE_CASE(256, 8)
+#define TQ_STORE_CASE(D_, KB_, VB_) \
+  if (g.head_dim == D_ && g.key_bits == KB_ && g.value_bits == VB_) return launch_store_t<D_, KB_, VB_>(a, stream);
+  TQ_STORE_CASE(64, 3, 4) TQ_STORE_CASE(64, 4, 4) TQ_STORE_CASE(64, 8, 4) TQ_STORE_CASE(64, 3, 3)
+  TQ_STORE_CASE(128, 3, 4) TQ_STORE_CASE(128, 4, 4) TQ_STORE_CASE(128, 8, 4) TQ_STORE_CASE(128, 3, 3)
+  TQ_STORE_CASE(256, 3, 4) TQ_STORE_CASE(256, 4, 4) TQ_STORE_CASE(256, 8, 4) TQ_STORE_CASE(256, 3, 3)
 #undef TQ_STORE_CASE
   return hipErrorInvalidValue;
 }

@@ -61,7 +61,7 @@ def test_host_signs_match_oracle(lib, seed, flip, d):
 
 def test_host_slot_bytes(lib):
     g = load_golden("slot_sizes.json")
-    for name in ("turboquant_k8v4", "turboquant_4bit_nc", "turboquant_k3v4_nc"):
+    for name in ("turboquant_k8v4", "turboquant_4bit_nc", "turboquant_k3v4_nc", "turboquant_3bit_nc"):
         assert _lib.tq_host_slot_bytes(name, 128) == g["presets"][name]["slot_aligned"]
         for d in (64, 256):
             assert _lib.tq_host_slot_bytes(name, d) == layout.slot_layout(name, d).slot_size_aligned

@@ -48,7 +48,7 @@ def _wl(preset, G=4, H=2, d=128, bs=16, lens=(1, 700), B=4, seed=1):
                           head_dim=d, block_size=bs, seed=seed, len_range=lens)
 
 
-PRESETS = ["turboquant_4bit_nc", "turboquant_k3v4_nc", "turboquant_k8v4"]
+PRESETS = ["turboquant_4bit_nc", "turboquant_k3v4_nc", "turboquant_k8v4", "turboquant_3bit_nc"]
 
 
 @pytest.mark.parametrize("preset", PRESETS)
@@ -100,7 +100,7 @@ def test_decode_sixteen_kv_heads(preset):
     check_decode(got, want, bf16_out=False)
 
 
-@pytest.mark.parametrize("preset", ["turboquant_4bit_nc", "turboquant_k3v4_nc"])
+@pytest.mark.parametrize("preset", ["turboquant_4bit_nc", "turboquant_k3v4_nc", "turboquant_3bit_nc"])
 @pytest.mark.parametrize("kernel", ["page", "staged", "direct", "ring"])
 def test_decode_kernels_mse_ragged(preset, kernel, monkeypatch):
     monkeypatch.setenv("TQ_DECODE_KERNEL", kernel)
@@ -109,7 +109,7 @@ def test_decode_kernels_mse_ragged(preset, kernel, monkeypatch):
     check_decode(got, want, bf16_out=False)
 
 
-@pytest.mark.parametrize("preset", ["turboquant_4bit_nc", "turboquant_k3v4_nc"])
+@pytest.mark.parametrize("preset", ["turboquant_4bit_nc", "turboquant_k3v4_nc", "turboquant_3bit_nc"])
 def test_decode_ring_workgroup_splits(preset, monkeypatch):
     # sequences longer than one ring workgroup split (1024 slabs) take several
     # workgroups and the merge kernel; the short one fits one split, and the
@@ -135,9 +135,10 @@ def test_decode_ragged_and_tiny_lengths(preset):
     assert np.all(got[0] == 0.0)
 
 
+@pytest.mark.parametrize("preset", ["turboquant_4bit_nc", "turboquant_3bit_nc"])
 @pytest.mark.parametrize("bs,d", [(32, 128), (128, 128), (16, 64), (16, 256)])
-def test_decode_block_sizes_and_head_dims(bs, d):
-    got, want = _decode_from_oracle_cache(_wl("turboquant_4bit_nc", G=4, d=d, bs=bs, seed=bs + d))
+def test_decode_block_sizes_and_head_dims(bs, d, preset):
+    got, want = _decode_from_oracle_cache(_wl(preset, G=4, d=d, bs=bs, seed=bs + d))
     check_decode(got, want, bf16_out=False)
 
 

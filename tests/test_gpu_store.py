@@ -18,7 +18,7 @@ pytestmark = pytest.mark.gpu
 
 torch = pytest.importorskip("torch")
 
-PRESETS = ["turboquant_4bit_nc", "turboquant_k3v4_nc", "turboquant_k8v4"]
+PRESETS = ["turboquant_4bit_nc", "turboquant_k3v4_nc", "turboquant_k8v4", "turboquant_3bit_nc"]
 
 
 def _run_store(w, seed=77, sign_flip=True, mode="exact", extra_blocks=2, inp=None,
@@ -78,7 +78,7 @@ def test_store_block_sizes_and_head_dims(preset, bs, d):
     assert _assert_parity(inp, got, want, ors)["rows_differing"] == 0
 
 
-@pytest.mark.parametrize("preset", ["turboquant_4bit_nc", "turboquant_k3v4_nc"])
+@pytest.mark.parametrize("preset", ["turboquant_4bit_nc", "turboquant_k3v4_nc", "turboquant_3bit_nc"])
 def test_store_pure_hadamard_and_page_codebook(preset):
     w = _small(preset, seed=9)
     for flip, mode in ((False, "exact"), (True, "page_trapz")):

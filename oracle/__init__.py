@@ -30,6 +30,7 @@ Modules:
   layout    -- presets, slot sizes and byte offsets, page bytes
   store     -- the store (quantise + pack + scatter), contract and float64
   decode    -- dequantise-then-softmax paged decode attention, float64
+  soa       -- the structure-of-arrays page layout with the folded norm
 """
 
-from . import fpfmt, rotation, codebook, layout, store, decode  # noqa: F401,E402
+from . import fpfmt, rotation, codebook, layout, store, decode, soa  # noqa: F401,E402

@@ -24,7 +24,7 @@ from dataclasses import dataclass, field, replace
 
 import numpy as np
 
-PRESET_NAMES = ("turboquant_k8v4", "turboquant_4bit_nc", "turboquant_k3v4_nc")
+PRESET_NAMES = ("turboquant_k8v4", "turboquant_4bit_nc", "turboquant_k3v4_nc", "turboquant_3bit_nc")
 
 
 def f32_to_bf16_bits(x):

@@ -68,6 +68,21 @@ typedef enum {
                                        iterations at most, tolerance 1e-10    */
 } tq_codebook_mode;
 
+/* Byte layout of a cache page (P1, section "AoS 与 SoA:两种页内布局").
+ * Both keep the page size block_size * num_kv_heads * slot bytes.
+ *   AOS  [block_size][H][slot]: every (token, head) slot holds its K codes,
+ *        K norm, V codes, V scale and V zero back to back (the default).
+ *   SOA  a data region [block_size][H][K code bytes + V code bytes] followed
+ *        by a meta region [H][3][block_size] of fp16: each head's K norms,
+ *        then its V scales, then its V zeros.  With norm correction the
+ *        stored K norm is |k| / |c|, c the token's centroid vector (P1,
+ *        section "SoA 的另一项收益:把 norm correction 折进写入端"), so the
+ *        decode multiplies by it directly.  3/4-bit key presets only. */
+typedef enum {
+  TQ_LAYOUT_AOS = 0,
+  TQ_LAYOUT_SOA = 1
+} tq_layout;
+
 typedef struct tq_ctx tq_ctx;   /* opaque; immutable after tq_codebook_init */
 
 /* Solve the Lloyd-Max codebook for a rotated coordinate ~ N(0, 1/head_dim)
@@ -92,6 +107,16 @@ typedef struct tq_ctx tq_ctx;   /* opaque; immutable after tq_codebook_init */
 tq_status tq_codebook_init(tq_ctx** ctx, int preset, int head_dim, int num_kv_heads,
                            int block_size, uint64_t rot_seed, int sign_flip,
                            int codebook_mode, void* stream);
+
+/* tq_codebook_init with a page layout (tq_layout).  tq_codebook_init is this
+ * call with TQ_LAYOUT_AOS.  TQ_LAYOUT_SOA with the FP8-key preset returns
+ * TQ_ERR_UNSUPPORTED (its slot has no K norm to fold). */
+tq_status tq_codebook_init_layout(tq_ctx** ctx, int preset, int head_dim, int num_kv_heads,
+                                  int block_size, uint64_t rot_seed, int sign_flip,
+                                  int codebook_mode, int layout, void* stream);
+
+/* The context's page layout (tq_layout), -1 for a NULL context. */
+int tq_layout_of(const tq_ctx* ctx);
 
 /* Free the context and its device tables.  NULL is accepted. */
 tq_status tq_destroy(tq_ctx* ctx);

@@ -19,9 +19,10 @@ STATUS = {0: "TQ_OK", -1: "TQ_ERR_INVALID_ARG", -2: "TQ_ERR_UNSUPPORTED", -3: "T
           -4: "TQ_ERR_WORKSPACE", -5: "TQ_ERR_HIP", -6: "TQ_ERR_NO_DEVICE"}
 PRESETS = {"turboquant_k8v4": 0, "turboquant_4bit_nc": 1, "turboquant_k3v4_nc": 2, "turboquant_3bit_nc": 3}
 CODEBOOK_MODES = {"exact": 0, "page_trapz": 1}
+LAYOUTS = {"aos": 0, "soa": 1}
 
 # every symbol include/tq.h declares
-EXPORTS = ("tq_codebook_init", "tq_destroy", "tq_slot_bytes", "tq_cache_bytes", "tq_get_tables",
+EXPORTS = ("tq_codebook_init", "tq_codebook_init_layout", "tq_layout_of", "tq_destroy", "tq_slot_bytes", "tq_cache_bytes", "tq_get_tables",
            "tq_store", "tq_decode_workspace_bytes", "tq_decode", "tq_get_device_error",
            "tq_host_codebook", "tq_host_rotation_signs", "tq_host_slot_bytes", "tq_status_str")
 
@@ -52,6 +53,9 @@ def load():
     sig = {
         "tq_codebook_init": (_int, [ctypes.POINTER(_vp), _int, _int, _int, _int, ctypes.c_uint64,
                                     _int, _int, _vp]),
+        "tq_codebook_init_layout": (_int, [ctypes.POINTER(_vp), _int, _int, _int, _int,
+                                           ctypes.c_uint64, _int, _int, _int, _vp]),
+        "tq_layout_of": (_int, [_vp]),
         "tq_destroy": (_int, [_vp]),
         "tq_slot_bytes": (_i64, [_vp]),
         "tq_cache_bytes": (_i64, [_vp, _i64]),
@@ -116,6 +120,27 @@ def tq_codebook_init(preset, head_dim, num_kv_heads, block_size, rot_seed, sign_
                                                     block_size, rot_seed, int(sign_flip),
                                                     codebook_mode, _stream(stream)))
     return h.value
+
+
+def tq_codebook_init_layout(preset, head_dim, num_kv_heads, block_size, rot_seed, sign_flip=1,
+                            codebook_mode=0, layout=0, stream=None):
+    lib = load()
+    if isinstance(preset, str):
+        preset = PRESETS[preset]
+    if isinstance(codebook_mode, str):
+        codebook_mode = CODEBOOK_MODES[codebook_mode]
+    if isinstance(layout, str):
+        layout = LAYOUTS[layout]
+    h = _vp()
+    _check("tq_codebook_init_layout",
+           lib.tq_codebook_init_layout(ctypes.byref(h), preset, head_dim, num_kv_heads, block_size,
+                                       rot_seed, int(sign_flip), codebook_mode, layout,
+                                       _stream(stream)))
+    return h.value
+
+
+def tq_layout_of(ctx):
+    return load().tq_layout_of(ctx)
 
 
 def tq_destroy(ctx):

@@ -45,6 +45,7 @@ struct DecodeArgs {
   float* part;        // [B][Hq][S][D + 2]
   void* out;
   int out_fp32;
+  int soa;            // split page: data region + meta region [H][3][bs], folded K norm
 };
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
@@ -88,6 +89,7 @@ __global__ void __launch_bounds__(64) decode_split_kernel(DecodeArgs a) {
   constexpr int kValCodeBytes = D * VB / 8;
   constexpr int kSlotRaw = kKeyPacked + kValCodeBytes + 4;
   constexpr int kSlot = kSlotRaw + (kSlotRaw & 1);
+  constexpr int kDataBytes = kKeyCodeBytes + kValCodeBytes;   // split page: per (token, head)
 
   __shared__ float s_q[G][D];
   __shared__ float s_cent[16];
@@ -182,15 +184,26 @@ __global__ void __launch_bounds__(64) decode_split_kernel(DecodeArgs a) {
   const int64_t row_bytes = static_cast<int64_t>(a.H) * kSlot;
   const int bs_mask = (1 << a.bs_shift) - 1;
 
+  // split page: V codes follow the K codes in the data region; the token's
+  // K norm, V scale and V zero sit bs fp16 apart in the meta region
+  const int v_off = a.soa ? kKeyCodeBytes : kValOff;
+  const int64_t meta_step = static_cast<int64_t>(2) << a.bs_shift;
+
   for (int tb = t0; tb < t1; tb += 64) {
     const int t = tb + lane;
     bool valid = t < t1;
-    int64_t off = 0;
+    int64_t off = 0;        // the token's slot (split page: its data bytes)
+    int64_t moff = 0;       // split page: its K norm
     if (valid) {
       const int page = bt[t >> a.bs_shift];
       if (page < 0 || page >= a.num_blocks) {
         const_cast<DevTables*>(a.tables)->err_page = 1;
         valid = false;
+      } else if (a.soa) {
+        const int64_t pb = static_cast<int64_t>(page) * (row_bytes << a.bs_shift);
+        off = pb + (static_cast<int64_t>(t & bs_mask) * a.H + g) * kDataBytes;
+        moff = pb + ((static_cast<int64_t>(a.H) * kDataBytes) << a.bs_shift) +
+               static_cast<int64_t>(3 * g) * meta_step + 2 * (t & bs_mask);
       } else {
         off = (static_cast<int64_t>(page) * (bs_mask + 1) + (t & bs_mask)) * row_bytes +
               static_cast<int64_t>(g) * kSlot;
@@ -231,14 +244,20 @@ __global__ void __launch_bounds__(64) decode_split_kernel(DecodeArgs a) {
 #pragma unroll
           for (int j = 0; j < G; ++j) sc[j] += s_q[j][c] * cv;
         }
-        const float nrm = f16_bits_to_f32(s16[kKeyCodeBytes / 2]);
-        const float f = nrm / sqrtf(ss + 1e-16f);
+        // the split page stores the corrected norm |k| / |c| itself
+        const float f = a.soa ? f16_bits_to_f32(*reinterpret_cast<const uint16_t*>(a.cache + moff))
+                              : f16_bits_to_f32(s16[kKeyCodeBytes / 2]) / sqrtf(ss + 1e-16f);
 #pragma unroll
         for (int j = 0; j < G; ++j) sc[j] *= f;
       }
-      const uint16_t* meta = reinterpret_cast<const uint16_t*>(slot + kValOff + kValCodeBytes);
-      vsc = f16_bits_to_f32(meta[0]);
-      vzr = f16_bits_to_f32(meta[1]);
+      if (a.soa) {
+        vsc = f16_bits_to_f32(*reinterpret_cast<const uint16_t*>(a.cache + moff + meta_step));
+        vzr = f16_bits_to_f32(*reinterpret_cast<const uint16_t*>(a.cache + moff + 2 * meta_step));
+      } else {
+        const uint16_t* meta = reinterpret_cast<const uint16_t*>(slot + kValOff + kValCodeBytes);
+        vsc = f16_bits_to_f32(meta[0]);
+        vzr = f16_bits_to_f32(meta[1]);
+      }
     }
     // ---- online softmax over this block of tokens (base 2) ----
 #pragma unroll
@@ -263,11 +282,12 @@ __global__ void __launch_bounds__(64) decode_split_kernel(DecodeArgs a) {
     for (int i = 0; i < nt; ++i) {
       const int64_t o = s_off[i];
       if (o < 0) continue;
-      const uint8_t* vrow = a.cache + o + kValOff;
+      const uint8_t* vrow = a.cache + o + v_off;
       float vh[E];
       if constexpr (VB == 3) {
         // code c at stream bits [3c, 3c + 3); the byte after the last code
-        // byte is the scale's first, inside the slot
+        // byte is the scale's first, inside the slot (split page: the next
+        // data bytes or the meta region, inside the page)
 #pragma unroll
         for (int e = 0; e < E; ++e) {
           const int bit = 3 * (E * lane + e);
@@ -492,6 +512,7 @@ hipError_t launch_decode(const Geometry& g, const DevTables* tables, const Decod
   a.part = static_cast<float*>(workspace);
   a.out = out;
   a.out_fp32 = out_is_fp32;
+  a.soa = g.soa;
   const int G = num_q_heads / g.num_kv_heads;
 #define TQ_DEC_CASE(D_, KB_, VB_) \
   if (g.head_dim == D_ && g.key_bits == KB_ && g.value_bits == VB_) return launch_g<D_, KB_, VB_>(a, G, batch, stream);

@@ -1195,6 +1195,7 @@ struct SlabRegs {
   u32x2 e[KB == 8 ? 1 : 16];     // {hi pair, lo pair} of code byte 4*kk + p
   u32x4 k8[KB == 8 ? 2 : 1];     // FP8 key bytes
   uint32_t nb;                   // norm bits of token 4*g4 + (r16 & 3)
+  uint32_t nf[2];                // split page: folded norms of tokens 4*g4 .. 4*g4 + 3
   uint32_t X[4];                 // V codes of token 4*g4 + r, coordinates [8*r16, 8*r16 + 8)
   uint32_t sz[4];                // V scale | zero of token 4*g4 + r
 };
@@ -1269,7 +1270,7 @@ struct ScoreAcc {
   f4 S, Slo, Nh, Nx;
 };
 
-template <int KB>
+template <int KB, bool NORM = true>
 __device__ __forceinline__ ScoreAcc slab_mfma(const SlabRegs<KB>& R, const h8 (&qc)[4], const bf8v (&qb)[4]) {
   ScoreAcc A;
   A.S = f4{0.f, 0.f, 0.f, 0.f};
@@ -1300,8 +1301,10 @@ __device__ __forceinline__ ScoreAcc slab_mfma(const SlabRegs<KB>& R, const h8 (&
       const h8 clo = __builtin_bit_cast(h8, lo);
       A.S = __builtin_amdgcn_mfma_f32_16x16x32_f16(chi, qc[kk], A.S, 0, 0, 0);
       A.Slo = __builtin_amdgcn_mfma_f32_16x16x32_f16(clo, qc[kk], A.Slo, 0, 0, 0);
-      A.Nh = __builtin_amdgcn_mfma_f32_16x16x32_f16(chi, chi, A.Nh, 0, 0, 0);
-      A.Nx = __builtin_amdgcn_mfma_f32_16x16x32_f16(chi, clo, A.Nx, 0, 0, 0);
+      if constexpr (NORM) {
+        A.Nh = __builtin_amdgcn_mfma_f32_16x16x32_f16(chi, chi, A.Nh, 0, 0, 0);
+        A.Nx = __builtin_amdgcn_mfma_f32_16x16x32_f16(chi, clo, A.Nx, 0, 0, 0);
+      }
     }
   }
   return A;
@@ -1499,16 +1502,89 @@ __global__ void __launch_bounds__(64 * H, page_waves_per_simd(KB)) decode_page_k
 // 3/4-bit keys, at most 8 query heads per kv head.
 // ============================================================================
 
+// ---- split page (data region + meta region) ----
+// One head's slab in LDS: its 16 data rows (K codes, then V codes) kRowL
+// bytes apart, kRowL an odd number of 16-byte chunks so that rows 0..7 of a
+// column start in distinct bank groups; then the slab's 16 folded K norms,
+// 16 V scales and 16 V zeros (fp16), 32 bytes each.
+template <int KB, int VB>
+struct SoaGeom {
+  static constexpr int kKCB = kD * KB / 8;                 // K code bytes
+  static constexpr int kVCB = kD * VB / 8;                 // V code bytes
+  static constexpr int kDB = kKCB + kVCB;                  // data bytes of a (token, head)
+  static_assert(kDB % 16 == 0, "data rows of whole 16-byte chunks");
+  static constexpr int kDataChunks = kDB / 16;
+  static constexpr int kRowChunks = kDataChunks | 1;
+  static constexpr int kRowL = 16 * kRowChunks;
+  static constexpr int kMetaOff = 16 * kRowL;
+  static constexpr int kSlabChunks = 16 * kRowChunks + 6;
+  static constexpr int kWaveLoads = (kSlabChunks + 63) / 64;
+  static constexpr int kBuf = kWaveLoads * 1024;
+};
+
+// the slab's bytes for this lane from its LDS buffer (split page)
+template <int KB, int VB>
+__device__ __forceinline__ void slab_read_soa(const uint8_t* buf, int r16, int g4, SlabRegs<KB>& R) {
+  using Geo = SoaGeom<KB, VB>;
+  if constexpr (KB == 4) {
+    const u32x4 t = *reinterpret_cast<const u32x4*>(buf + r16 * Geo::kRowL + 16 * g4);
+    R.kw[0] = t[0]; R.kw[1] = t[1]; R.kw[2] = t[2]; R.kw[3] = t[3];
+  } else {
+    typedef uint32_t u32x3a __attribute__((ext_vector_type(3), aligned(4)));
+    const u32x3a t = *reinterpret_cast<const u32x3a*>(buf + r16 * Geo::kRowL + 12 * g4);
+    R.kw[0] = t[0]; R.kw[1] = t[1]; R.kw[2] = t[2];
+  }
+  const uint8_t* rb = buf + 4 * g4 * Geo::kRowL + Geo::kKCB;    // V codes of row 4*g4
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    if constexpr (VB == 4) {
+      R.X[r] = *reinterpret_cast<const uint32_t*>(rb + r * Geo::kRowL + 4 * r16);
+    } else {
+      const uint32_t* pv = reinterpret_cast<const uint32_t*>(rb + r * Geo::kRowL + ((3 * r16) & ~3));
+      R.X[r] = __builtin_amdgcn_alignbyte(pv[1], pv[0], (3 * r16) & 3);
+    }
+  }
+  const uint8_t* meta = buf + Geo::kMetaOff + 8 * g4;              // tokens 4*g4 .. 4*g4 + 3
+  const u32x2 n = *reinterpret_cast<const u32x2*>(meta);
+  const u32x2 sc = *reinterpret_cast<const u32x2*>(meta + 32);
+  const u32x2 zr = *reinterpret_cast<const u32x2*>(meta + 64);
+  R.nf[0] = n[0];
+  R.nf[1] = n[1];
+  // V scale | zero << 16 per token
+  R.sz[0] = __builtin_amdgcn_perm(zr[0], sc[0], 0x05040100u);
+  R.sz[1] = __builtin_amdgcn_perm(zr[0], sc[0], 0x07060302u);
+  R.sz[2] = __builtin_amdgcn_perm(zr[1], sc[1], 0x05040100u);
+  R.sz[3] = __builtin_amdgcn_perm(zr[1], sc[1], 0x07060302u);
+}
+
+// scores (base 2) of a split-page slab: the stored norm already holds the
+// correction, so it multiplies the rows directly
+template <bool FULL>
+__device__ __forceinline__ void slab_tail_soa(const uint32_t (&nf)[2], const ScoreAcc& A, int valid_rows,
+                                              int g4, float (&s)[4]) {
+  const float fac[4] = {f16_bits_to_f32(nf[0] & 0xFFFFu), f16_bits_to_f32(nf[0] >> 16),
+                        f16_bits_to_f32(nf[1] & 0xFFFFu), f16_bits_to_f32(nf[1] >> 16)};
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    // column h + 8 holds hi.qlo of head h (as in slab_tail)
+    const float sr = A.S[r];
+    const float other = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(sr), 0x128, 0xF, 0xF, false));
+    s[r] = (FULL || 4 * g4 + r < valid_rows) ? (sr + other + 0.5f * A.Slo[r]) * fac[r] : -INFINITY;
+  }
+}
+
 constexpr int kRingBufs = 3;                 // slabs per wavefront ring (two in flight)
 constexpr int kRingWaves = 16;               // wavefronts per workgroup
 constexpr int kRingMaxSlabs = 1024;          // slabs per workgroup split: its page ids fit in LDS
 
-template <int KB, int SLOT>
+template <int KB, int SLOT, bool SOA>
 __global__ void __launch_bounds__(64 * kRingWaves) decode_ring_kernel(MfmaArgs a) {
   static_assert(KB == 3 || KB == 4, "ring kernel: 3/4-bit keys");
-  using Geo = PageGeom<KB, SLOT, 1>;         // one head's slab layout in LDS
-  constexpr int kLoads = Geo::kWaveLoads;    // 16-byte loads per lane per slab
-  constexpr int kBuf = Geo::kBuf;            // kLoads KB: covers every lane's chunk
+  constexpr int VB = vbits_of_slot(SLOT);
+  using Geo = PageGeom<KB, SLOT, 1>;         // one head's slab layout in LDS (slotted page)
+  using SGeo = SoaGeom<KB, VB>;              // ... (split page)
+  constexpr int kLoads = SOA ? SGeo::kWaveLoads : Geo::kWaveLoads;   // 16-byte loads per lane per slab
+  constexpr int kBuf = 1024 * kLoads;        // covers every lane's chunk
   constexpr int kRing = kRingBufs * kBuf;
   static_assert(8 * kRec * 4 <= kRing, "a wavefront's partial records must fit its ring");
   __shared__ u32x2 s_tab[256];
@@ -1564,23 +1640,40 @@ __global__ void __launch_bounds__(64 * kRingWaves) decode_ring_kernel(MfmaArgs a
   const int64_t row_bytes = static_cast<int64_t>(a.H) * SLOT;
   const int64_t page_bytes = static_cast<int64_t>(1 << a.bs_shift) * row_bytes;
   const int n_slabs = j1 - j0;
-  // the slab of one head: 16 rows row_bytes apart; the lane's chunk of load
-  // l is chunk l*64 + lane of the aligned layout (past the slab: an offset
-  // beyond every buffer range, which loads zeros into the ring's slack)
-  uint32_t src_off[kLoads];
+  // Slotted page: the slab of one head is 16 rows row_bytes apart; the lane's
+  // chunk of load l is chunk l*64 + lane of the aligned layout (past the
+  // slab: an offset beyond every buffer range, which loads zeros into the
+  // ring's slack).  Split page: offsets from the page start, src_off +
+  // r0 * src_mul for the slab starting at row r0 of its page (data rows
+  // advance by a data row, meta fields by one fp16).
+  uint32_t src_off[kLoads], src_mul[kLoads];
 #pragma unroll
   for (int l = 0; l < kLoads; ++l) {
     const int c = l * 64 + lane;
-    if (c >= Geo::kSlabChunks) {
-      src_off[l] = 0x7FFFFFF0u;
-    } else {
+    src_off[l] = 0x7FFFFFF0u;
+    src_mul[l] = 0;
+    if constexpr (SOA) {
+      const uint32_t data_row = static_cast<uint32_t>(a.H) * SGeo::kDB;
+      if (c < 16 * SGeo::kRowChunks) {
+        const int row = c / SGeo::kRowChunks, k = c - row * SGeo::kRowChunks;
+        if (k < SGeo::kDataChunks) {
+          src_off[l] = row * data_row + g * SGeo::kDB + 16 * k;
+          src_mul[l] = data_row;
+        }
+      } else if (c < SGeo::kSlabChunks) {
+        const int m = c - 16 * SGeo::kRowChunks;          // fields norm, scale, zero: 2 chunks each
+        src_off[l] = (data_row << a.bs_shift) + ((3 * g + (m >> 1)) << (a.bs_shift + 1)) + 16 * (m & 1);
+        src_mul[l] = 2;
+      }
+    } else if (c < Geo::kSlabChunks) {
       const int row = c / (Geo::kNK + Geo::kNV), k = c - row * (Geo::kNK + Geo::kNV);
       const int off = k < Geo::kNK ? 16 * k : Geo::kKP + 16 * (k - Geo::kNK);
       src_off[l] = static_cast<uint32_t>(row * row_bytes + off);
     }
   }
-  const uint32_t head_bytes = static_cast<uint32_t>(g * SLOT);
-  const uint32_t range = static_cast<uint32_t>(16 * row_bytes) - head_bytes;
+  const uint32_t head_bytes = SOA ? 0u : static_cast<uint32_t>(g * SLOT);
+  const uint32_t range = SOA ? static_cast<uint32_t>(page_bytes)
+                             : static_cast<uint32_t>(16 * row_bytes) - head_bytes;
   uint8_t* ring = s_ring[w];
   // the query loads are done before the first slab is requested, so every
   // wait in the loop counts slab loads only
@@ -1591,12 +1684,21 @@ __global__ void __launch_bounds__(64 * kRingWaves) decode_ring_kernel(MfmaArgs a
     int pid = -1;
     if (t < t1) pid = s_pid[(t >> a.bs_shift) - p_first];
     pid = __builtin_amdgcn_readfirstlane(pid);
-    const int64_t off = pid >= 0 ? pid * page_bytes + static_cast<int64_t>(t & bs_mask) * row_bytes + head_bytes : 0;
+    const int64_t off = pid < 0 ? 0
+                      : SOA ? pid * page_bytes
+                            : pid * page_bytes + static_cast<int64_t>(t & bs_mask) * row_bytes + head_bytes;
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint8_t*>(a.cache) + off, 0, pid >= 0 ? static_cast<int>(range) : 0, kBufferWord3);
     uint8_t* dst = ring + (j % kRingBufs) * kBuf;
+    if constexpr (SOA) {
+      // whole lines of this head alone (the data rows): non-temporal
+      const uint32_t r0 = static_cast<uint32_t>(t & bs_mask);
 #pragma unroll
-    for (int l = 0; l < kLoads; ++l) lds_dma_16<false>(rs, dst + l * 1024, src_off[l]);
+      for (int l = 0; l < kLoads; ++l) lds_dma_16<true>(rs, dst + l * 1024, src_off[l] + r0 * src_mul[l]);
+    } else {
+#pragma unroll
+      for (int l = 0; l < kLoads; ++l) lds_dma_16<false>(rs, dst + l * 1024, src_off[l]);
+    }
   };
   auto page_of = [&](int jj) { return s_pid[((t0 + 16 * jj) >> a.bs_shift) - p_first]; };
 
@@ -1616,26 +1718,35 @@ __global__ void __launch_bounds__(64 * kRingWaves) decode_ring_kernel(MfmaArgs a
         __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
         issue(j + kRingBufs - 1);
         if (__builtin_amdgcn_readfirstlane(page_of(j)) < 0) continue;
-        slab_read<KB, SLOT, 1>(ring + (j % kRingBufs) * kBuf, 0, r16, g4, c);
+        if constexpr (SOA)
+          slab_read_soa<KB, VB>(ring + (j % kRingBufs) * kBuf, r16, g4, c);
+        else
+          slab_read<KB, SLOT, 1>(ring + (j % kRingBufs) * kBuf, 0, r16, g4, c);
         slab_lookup<KB>(s_tab, c);
-        const ScoreAcc acc = slab_mfma<KB>(c, qc, qb);
+        const ScoreAcc acc = slab_mfma<KB, !SOA>(c, qc, qb);
         const int valid = t1 - (t0 + 16 * j);
         if (valid >= 16) {
-          slab_tail<KB, true>(c, acc, 16, g4, a.scale_log2, sel1, sel2, diag, s);
+          if constexpr (SOA)
+            slab_tail_soa<true>(c.nf, acc, 16, g4, s);
+          else
+            slab_tail<KB, true>(c, acc, 16, g4, a.scale_log2, sel1, sel2, diag, s);
           sm = softmax_check<true>(s, 16, c.sz, g4, st);
         } else {
-          slab_tail<KB, false>(c, acc, valid, g4, a.scale_log2, sel1, sel2, diag, s);
+          if constexpr (SOA)
+            slab_tail_soa<false>(c.nf, acc, valid, g4, s);
+          else
+            slab_tail<KB, false>(c, acc, valid, g4, a.scale_log2, sel1, sel2, diag, s);
           sm = softmax_check<false>(s, valid, c.sz, g4, st);
         }
         if (sm.grow) {
           grow = true;
           break;
         }
-        softmax_accumulate<vbits_of_slot(SLOT)>(s, sm, c.X, st);
+        softmax_accumulate<VB>(s, sm, c.X, st);
       }
       if (!grow) break;
       softmax_rescale(sm, diag, st);
-      softmax_accumulate<vbits_of_slot(SLOT)>(s, sm, c.X, st);
+      softmax_accumulate<VB>(s, sm, c.X, st);
       ++j;
     }
     wait_vmcnt<0>();                         // no load may still write the ring
@@ -1762,8 +1873,9 @@ bool page_decode_eligible(const Geometry& g, int num_q_heads, bool mse_keys_too)
 }
 
 bool ring_decode_eligible(const Geometry& g, int num_q_heads) {
-  return mfma_decode_eligible(g, num_q_heads) && (g.key_bits == 4 || g.key_bits == 3) &&
-         num_q_heads <= 8 * g.num_kv_heads;
+  const int G = num_q_heads / g.num_kv_heads;
+  return g.head_dim == kD && g.block_size % 16 == 0 && G >= 1 && G <= 8 &&
+         ((g.key_bits == 4 && g.slot == 134) || (g.key_bits == 3 && (g.slot == 118 || g.slot == 102)));
 }
 
 int ring_max_slabs() { return kRingMaxSlabs; }
@@ -1785,6 +1897,8 @@ int page_wgs_per_cu(const Geometry& g, int group) {
 }
 
 bool mfma_decode_eligible(const Geometry& g, int num_q_heads) {
+  // slotted pages (the split page has the ring kernel, ring_decode_eligible)
+  if (g.soa) return false;
   const int G = num_q_heads / g.num_kv_heads;
   if (g.head_dim != kD || g.block_size % 16 != 0 || G < 1 || G > 16) return false;
   if (g.key_bits == 8) return g.slot == 196;
@@ -1824,12 +1938,20 @@ hipError_t launch_decode_mfma(const Geometry& g, const DevTables* tables, const 
     // only when a sequence has more than one workgroup split
     const int n_items = plan.num_splits * batch * g.num_kv_heads;
     const dim3 grid(8 * ((n_items + 7) / 8));
-    if (g.key_bits == 4)
-      hipLaunchKernelGGL((decode_ring_kernel<4, 134>), grid, dim3(64 * kRingWaves), 0, stream, a);
+    const dim3 block(64 * kRingWaves);
+    if (g.soa) {
+      if (g.key_bits == 4)
+        hipLaunchKernelGGL((decode_ring_kernel<4, 134, true>), grid, block, 0, stream, a);
+      else if (g.slot == 118)
+        hipLaunchKernelGGL((decode_ring_kernel<3, 118, true>), grid, block, 0, stream, a);
+      else
+        hipLaunchKernelGGL((decode_ring_kernel<3, 102, true>), grid, block, 0, stream, a);
+    } else if (g.key_bits == 4)
+      hipLaunchKernelGGL((decode_ring_kernel<4, 134, false>), grid, block, 0, stream, a);
     else if (g.slot == 118)
-      hipLaunchKernelGGL((decode_ring_kernel<3, 118>), grid, dim3(64 * kRingWaves), 0, stream, a);
+      hipLaunchKernelGGL((decode_ring_kernel<3, 118, false>), grid, block, 0, stream, a);
     else
-      hipLaunchKernelGGL((decode_ring_kernel<3, 102>), grid, dim3(64 * kRingWaves), 0, stream, a);
+      hipLaunchKernelGGL((decode_ring_kernel<3, 102, false>), grid, block, 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || plan.num_splits == 1) return e;
     hipLaunchKernelGGL(decode_merge_kernel, dim3(batch * num_q_heads), dim3(256), 0, stream, a);

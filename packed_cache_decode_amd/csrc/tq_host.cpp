@@ -327,9 +327,20 @@ const char* tq_status_str(int status) {
 tq_status tq_codebook_init(tq_ctx** out, int preset, int head_dim, int num_kv_heads,
                            int block_size, uint64_t rot_seed, int sign_flip, int codebook_mode,
                            void* stream) {
+  return tq_codebook_init_layout(out, preset, head_dim, num_kv_heads, block_size, rot_seed,
+                                 sign_flip, codebook_mode, TQ_LAYOUT_AOS, stream);
+}
+
+int tq_layout_of(const tq_ctx* ctx) { return ctx ? (ctx->geo.soa ? TQ_LAYOUT_SOA : TQ_LAYOUT_AOS) : -1; }
+
+tq_status tq_codebook_init_layout(tq_ctx** out, int preset, int head_dim, int num_kv_heads,
+                                  int block_size, uint64_t rot_seed, int sign_flip,
+                                  int codebook_mode, int layout, void* stream) {
   if (!out) return TQ_ERR_INVALID_ARG;
   *out = nullptr;
   if (preset < TQ_K8V4 || preset > TQ_3BIT_NC) return TQ_ERR_INVALID_ARG;
+  if (layout != TQ_LAYOUT_AOS && layout != TQ_LAYOUT_SOA) return TQ_ERR_INVALID_ARG;
+  if (layout == TQ_LAYOUT_SOA && preset == TQ_K8V4) return TQ_ERR_UNSUPPORTED;
   if (codebook_mode != TQ_CODEBOOK_LLOYD_MAX_EXACT && codebook_mode != TQ_CODEBOOK_PAGE_TRAPZ)
     return TQ_ERR_INVALID_ARG;
   if (num_kv_heads < 1 || num_kv_heads > 64) return TQ_ERR_INVALID_ARG;
@@ -352,6 +363,12 @@ tq_status tq_codebook_init(tq_ctx** out, int preset, int head_dim, int num_kv_he
   g.key_packed = g.key_bits == 8 ? head_dim : g.key_code_bytes + 2;
   g.value_code_bytes = (head_dim * g.value_bits + 7) / 8;
   g.slot = slot_bytes_for(preset, head_dim);
+  g.soa = layout == TQ_LAYOUT_SOA ? 1 : 0;
+  // the split page has the slotted page's size: no slot padding to drop
+  if (g.soa && g.slot != g.key_packed + g.value_code_bytes + 4) {
+    delete c;
+    return TQ_ERR_UNSUPPORTED;
+  }
   c->r_d = static_cast<float>(1.0 / std::sqrt(static_cast<double>(head_dim)));
 
   c->levels = 0;

@@ -53,6 +53,8 @@ struct Geometry {
   int value_code_bytes; // ceil(d*vb/8)
   int slot;             // aligned slot bytes
   int bins_ok;          // the bucketize bins of the device tables exist
+  int soa;              // page layout: 0 = slots back to back, 1 = data region +
+                        // meta region [H][3][block_size] fp16 (folded K norm)
 };
 
 // ---- launchers (defined in the .hip files) ---------------------------------

@@ -39,6 +39,7 @@ struct StoreArgs {
   float r_d;
   int H;
   int bs_shift;              // log2(block_size)
+  int soa;                   // split page (data region + meta region), folded K norm
 };
 
 constexpr int kWaves = 4;
@@ -84,10 +85,16 @@ __global__ void __launch_bounds__(64 * kWaves) store_kernel(StoreArgs a) {
 
   __shared__ uint8_t s_code[kWaves][D];
   __shared__ __align__(4) uint8_t s_slot[kWaves][kSlot + 2];
+  __shared__ float s_csq[16];                  // split page: c_i * c_i per level
 
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
   const int H = a.H;
+  if (!kFp8 && threadIdx.x < 16) {
+    const float c = a.tables->centroids[threadIdx.x];
+    s_csq[threadIdx.x] = c * c;
+  }
+  __syncthreads();
 
   float mid[kLevels > 0 ? kLevels - 1 : 1];
 #pragma unroll
@@ -163,6 +170,7 @@ __global__ void __launch_bounds__(64 * kWaves) store_kernel(StoreArgs a) {
         }
       }
       // y = u * alpha, code = #{m : y >= mid_m}
+      float cq[E];
 #pragma unroll
       for (int e = 0; e < E; ++e) {
         const float y = u[e] * alpha;
@@ -170,9 +178,23 @@ __global__ void __launch_bounds__(64 * kWaves) store_kernel(StoreArgs a) {
 #pragma unroll
         for (int m = 0; m < kLevels - 1; ++m) c += (y >= mid[m]) ? 1 : 0;
         s_code[wave][E * lane + e] = static_cast<uint8_t>(c);
+        cq[e] = s_csq[c];
+      }
+      // split page: the stored norm is |k| / |c|, |c|^2 summed in the same
+      // tree as |k|^2
+      float n_stored = nrm;
+      if (a.soa) {
+#pragma unroll
+        for (int w = 1; w < E; w *= 2)
+#pragma unroll
+          for (int e = 0; e < E; e += 2 * w) cq[e] = cq[e] + cq[e + w];
+        float css = cq[0];
+#pragma unroll
+        for (int m = 1; m < 64; m *= 2) css = css + __shfl_xor(css, m, 64);
+        n_stored = nrm * (1.0f / sqrtf(css + 1e-16f));
       }
       if (lane == 0) {
-        const uint16_t nb = f32_to_f16_bits(nrm);
+        const uint16_t nb = f32_to_f16_bits(n_stored);
         s_slot[wave][kKeyCodeBytes] = static_cast<uint8_t>(nb & 0xFF);
         s_slot[wave][kKeyCodeBytes + 1] = static_cast<uint8_t>(nb >> 8);
       }
@@ -260,10 +282,28 @@ __global__ void __launch_bounds__(64 * kWaves) store_kernel(StoreArgs a) {
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
 
-    // write the assembled slot: kSlot / 2 two-byte stores
-    uint16_t* d16 = reinterpret_cast<uint16_t*>(dst);
-    for (int j = lane; j < kSlot / 2; j += 64)
-      d16[j] = static_cast<uint16_t>(s_slot[wave][2 * j] | (s_slot[wave][2 * j + 1] << 8));
+    if (!kFp8 && a.soa) {
+      // split page: K codes then V codes into the data region, the norm,
+      // scale and zero into the meta region (every part has an even size)
+      constexpr int kDataBytes = kKeyCodeBytes + kValCodeBytes;
+      uint8_t* pg = a.cache + page * ((static_cast<int64_t>(H) * kSlot) << a.bs_shift);
+      uint16_t* d16 = reinterpret_cast<uint16_t*>(pg + (row * H + h) * kDataBytes);
+      for (int j = lane; j < kDataBytes / 2; j += 64) {
+        const int src = 2 * j < kKeyCodeBytes ? 2 * j : kKeyPacked + 2 * j - kKeyCodeBytes;
+        d16[j] = static_cast<uint16_t>(s_slot[wave][src] | (s_slot[wave][src + 1] << 8));
+      }
+      if (lane < 3) {
+        uint16_t* meta = reinterpret_cast<uint16_t*>(pg + ((static_cast<int64_t>(H) * kDataBytes) << a.bs_shift)) +
+                         ((static_cast<int64_t>(h) * 3 + lane) << a.bs_shift) + row;
+        const int src = lane == 0 ? kKeyCodeBytes : kKeyPacked + kValCodeBytes + 2 * (lane - 1);
+        *meta = static_cast<uint16_t>(s_slot[wave][src] | (s_slot[wave][src + 1] << 8));
+      }
+    } else {
+      // write the assembled slot: kSlot / 2 two-byte stores
+      uint16_t* d16 = reinterpret_cast<uint16_t*>(dst);
+      for (int j = lane; j < kSlot / 2; j += 64)
+        d16[j] = static_cast<uint16_t>(s_slot[wave][2 * j] | (s_slot[wave][2 * j + 1] << 8));
+    }
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   }
@@ -324,17 +364,35 @@ __device__ __forceinline__ float butterfly_x(float u, uint32_t upper_sign) {
   return o + __uint_as_float(__float_as_uint(u) ^ upper_sign);
 }
 
+// N dwords (a lane's 32 codes of N bits): one 16-byte store for N = 4 (16-byte
+// aligned), dword stores for N = 3 (4-byte aligned)
+template <int N>
+__device__ __forceinline__ void store_words(uint8_t* dst, const uint32_t* w) {
+  if constexpr (N == 4) {
+    *reinterpret_cast<u32x4s*>(dst) = u32x4s{w[0], w[1], w[2], w[3]};
+  } else {
+    uint32_t* d = reinterpret_cast<uint32_t*>(dst);
+#pragma unroll
+    for (int i = 0; i < N; ++i) d[i] = w[i];
+  }
+}
+
 __device__ __forceinline__ void store_u16s(uint8_t* dst, const uint32_t* w, int n16) {
   uint16_t* d = reinterpret_cast<uint16_t*>(dst);
 #pragma unroll
   for (int i = 0; i < n16; ++i) d[i] = static_cast<uint16_t>(w[i >> 1] >> (16 * (i & 1)));
 }
 
+// SOA: the page is a data region [bs][H][K codes | V codes] and a meta region
+// [H][3][bs] of fp16 (K norm, V scale, V zero); the stored K norm is folded:
+// |k| * (1 / sqrt(sum c_j^2 + 1e-16)) with the centroids c_j of the vector's
+// codes, squared and summed in the same balanced tree as the norm (P1,
+// section "SoA 的另一项收益:把 norm correction 折进写入端").
 // kRows: H divides 16 and a cache row (H slots) is a multiple of 16 bytes, so
 // a wavefront's 16 vectors are 16 / H whole tokens; their rows are assembled
 // in LDS and written with 16-byte stores.  Otherwise each lane writes its
 // fields with 2- or 4-byte stores.
-template <int KB, int VB, bool kRows>
+template <int KB, int VB, bool kRows, bool SOA>
 __global__ void __launch_bounds__(256) store128_kernel(StoreArgs a) {
   constexpr int D = 128, E = 32;
   constexpr bool kFp8 = KB == 8;
@@ -345,13 +403,20 @@ __global__ void __launch_bounds__(256) store128_kernel(StoreArgs a) {
   constexpr int kLaneVB = E * VB / 8;           // V code bytes of a lane's 32 coordinates
   constexpr int kSlot = kKeyPacked + kValCodeBytes + 4;    // 196 / 134 / 118, even
   static_assert(kSlot % 2 == 0, "slot must be even");
+  static_assert(!(SOA && (kRows || kFp8)), "the split page: 3/4-bit keys, per-lane writes");
+  constexpr int kDataBytes = kKeyCodeBytes + kValCodeBytes;   // SOA: data bytes per vector
 
   __shared__ uint32_t s_bins[kMaxBins][2];
+  __shared__ float s_csq[16];                   // SOA: c_i * c_i per level
   __shared__ __align__(16) uint8_t s_rows[kRows ? 4 : 1][kRows ? 16 * kSlot : 16];
   if constexpr (!kFp8) {
     for (int i = threadIdx.x; i < kMaxBins; i += blockDim.x) {
       s_bins[i][0] = a.tables->bins[i][0];
       s_bins[i][1] = a.tables->bins[i][1];
+    }
+    if (SOA && threadIdx.x < 16) {
+      const float c = a.tables->centroids[threadIdx.x];
+      s_csq[threadIdx.x] = c * c;
     }
     __syncthreads();
   }
@@ -483,6 +548,21 @@ __global__ void __launch_bounds__(256) store128_kernel(StoreArgs a) {
         const uint32_t thr = s_bins[bi][0], cb = s_bins[bi][1];
         code[e] = cb + (y >= __uint_as_float(thr) ? 1u : 0u);
       }
+      if constexpr (SOA) {
+        // folded norm: the same tree over the squared centroids
+        float cq[E];
+#pragma unroll
+        for (int e = 0; e < E; ++e) cq[e] = s_csq[code[e]];
+#pragma unroll
+        for (int w = 1; w < E; w *= 2)
+#pragma unroll
+          for (int e = 0; e < E; e += 2 * w) cq[e] = cq[e] + cq[e + w];
+        float css = cq[0];
+        css = css + quad_xor<1>(css);
+        css = css + quad_xor<2>(css);
+        const float inv = 1.0f / sqrtf(css + 1e-16f);
+        norm_bits = f32_to_f16_bits(nrm * inv);
+      }
       if constexpr (KB == 4) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -612,6 +692,22 @@ __global__ void __launch_bounds__(256) store128_kernel(StoreArgs a) {
       }
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    } else if (SOA && do_store) {
+      // split page: the vector's data bytes (16-byte aligned: pages and data
+      // rows are multiples of 16 bytes) and its three meta fields
+      const int64_t page = slot >> a.bs_shift;
+      const int64_t row = slot - (page << a.bs_shift);
+      uint8_t* pg = a.cache + page * ((static_cast<int64_t>(H) * kSlot) << a.bs_shift);
+      uint8_t* dst = pg + (row * H + h) * kDataBytes;
+      store_words<KB>(dst + (kKeyCodeBytes / 4) * qd, kout);
+      store_words<VB>(dst + kKeyCodeBytes + kLaneVB * qd, vout);
+      uint16_t* meta = reinterpret_cast<uint16_t*>(pg + ((static_cast<int64_t>(H) * kDataBytes) << a.bs_shift)) +
+                       ((static_cast<int64_t>(h) * 3) << a.bs_shift) + row;
+      if (qd == 0) meta[0] = static_cast<uint16_t>(norm_bits);
+      if (qd == 3) {
+        meta[1 << a.bs_shift] = f32_to_f16_bits(sc);
+        meta[2 << a.bs_shift] = f32_to_f16_bits(lo);
+      }
     } else if (do_store) {
       const int64_t page = slot >> a.bs_shift;
       const int64_t row = slot - (page << a.bs_shift);
@@ -646,12 +742,19 @@ hipError_t launch_store128(const StoreArgs& a, hipStream_t stream) {
   int64_t blocks = (total + 63) / 64;               // 64 vectors per 256-thread block
   if (blocks > 8192) blocks = 8192;
   const bool rows = 16 % a.H == 0 && (static_cast<int64_t>(a.H) * kSlot) % 16 == 0;
+  if constexpr (KB != 8) {
+    if (a.soa) {
+      hipLaunchKernelGGL((store128_kernel<KB, VB, false, true>), dim3(static_cast<unsigned>(blocks)), dim3(256),
+                         0, stream, a);
+      return hipGetLastError();
+    }
+  }
   if (rows)
-    hipLaunchKernelGGL((store128_kernel<KB, VB, true>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0,
-                       stream, a);
+    hipLaunchKernelGGL((store128_kernel<KB, VB, true, false>), dim3(static_cast<unsigned>(blocks)), dim3(256),
+                       0, stream, a);
   else
-    hipLaunchKernelGGL((store128_kernel<KB, VB, false>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0,
-                       stream, a);
+    hipLaunchKernelGGL((store128_kernel<KB, VB, false, false>), dim3(static_cast<unsigned>(blocks)), dim3(256),
+                       0, stream, a);
   return hipGetLastError();
 }
 
@@ -683,6 +786,7 @@ hipError_t launch_store(const Geometry& g, const DevTables* tables, const uint16
   a.r_d = r_d;
   a.H = g.num_kv_heads;
   a.bs_shift = __builtin_ctz(static_cast<unsigned>(g.block_size));
+  a.soa = g.soa;
   // head_dim 128 takes the four-lanes-per-vector kernel when the bucketize
   // bins exist (always, for the Lloyd-Max codebooks) and the vector count fits
   // 32-bit indexing

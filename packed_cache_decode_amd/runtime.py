@@ -16,15 +16,16 @@ class PackedKVCache:
     """One context (codebook, signs, geometry) on the current device."""
 
     def __init__(self, preset, head_dim, num_kv_heads, block_size, rot_seed, sign_flip=True,
-                 codebook_mode="exact", device="cuda"):
+                 codebook_mode="exact", device="cuda", layout="aos"):
         self.device = torch.device(device)
         self.preset = preset
         self.head_dim = head_dim
         self.num_kv_heads = num_kv_heads
         self.block_size = block_size
+        self.layout = layout
         with torch.cuda.device(self.device):
-            self.ctx = _lib.tq_codebook_init(preset, head_dim, num_kv_heads, block_size, rot_seed,
-                                             sign_flip, codebook_mode)
+            self.ctx = _lib.tq_codebook_init_layout(preset, head_dim, num_kv_heads, block_size,
+                                                    rot_seed, sign_flip, codebook_mode, layout)
         self.slot_bytes = _lib.tq_slot_bytes(self.ctx)
         self._ws = None
 
@@ -40,7 +41,11 @@ class PackedKVCache:
             pass
 
     def new_cache(self, num_blocks, fill=0):
-        shape = (num_blocks, self.block_size, self.num_kv_heads, self.slot_bytes)
+        """uint8 [num_blocks, bs, H, slot] (AoS) or [num_blocks, page bytes] (SoA)."""
+        if self.layout == "soa":
+            shape = (num_blocks, self.block_size * self.num_kv_heads * self.slot_bytes)
+        else:
+            shape = (num_blocks, self.block_size, self.num_kv_heads, self.slot_bytes)
         return torch.full(shape, fill, dtype=torch.uint8, device=self.device)
 
     def store(self, k, v, slot_mapping, cache, stream=None):

@@ -132,6 +132,7 @@ struct RunState {
   float m_run;      // running (lazy) max, base 2, of head r16
   float l_part;     // sum of p over this lane's rows, head r16
   float z_part;     // sum of p * zero over this lane's rows, head r16
+  float w_part;     // sum of p * scale over this lane's rows, head r16 (biased V operands)
 };
 
 // Operand bytes of one slab for one lane, already re-aligned.
@@ -330,11 +331,13 @@ constexpr int vbits_of_slot(int slot) { return slot == 102 ? 3 : 4; }
 // 8*r16 + 2*kb + 1 (Bhi), as exact f16 integers: code c becomes the f16 with
 // bits 0x6400 | c (1024 + c) minus 1024, and for the high nibble of a 4-bit
 // byte 0x5400 | (c << 4) (64 + c) minus 64
-template <int VB>
+// BIASED: the operands keep the 1024 (or 64) and the caller subtracts
+// bias * sum(p * scale) from the accumulators once at the end (unbias).
+template <int VB, bool BIASED = false>
 __device__ __forceinline__ void v_operands(const uint32_t (&X)[4], int kb, h4& Blo, h4& Bhi) {
-  const h2 b1024 = {static_cast<_Float16>(1024.0f), static_cast<_Float16>(1024.0f)};
+  const h2 b1024 = {static_cast<_Float16>(BIASED ? 0.0f : 1024.0f), static_cast<_Float16>(BIASED ? 0.0f : 1024.0f)};
   if constexpr (VB == 4) {
-    const h2 b64 = {static_cast<_Float16>(64.0f), static_cast<_Float16>(64.0f)};
+    const h2 b64 = {static_cast<_Float16>(BIASED ? 0.0f : 64.0f), static_cast<_Float16>(BIASED ? 0.0f : 64.0f)};
     // byte kb of each token's dword -> [x0, 0, x1, 0]
     const uint32_t sel = kb | (0x0Cu << 8) | ((4u + kb) << 16) | (0x0Cu << 24);
     const uint32_t p01 = __builtin_amdgcn_perm(X[1], X[0], sel);
@@ -343,10 +346,12 @@ __device__ __forceinline__ void v_operands(const uint32_t (&X)[4], int kb, h4& B
     h2 lo23 = __builtin_bit_cast(h2, insert_bits(p23, 0x000F000Fu, 0x64006400u));
     h2 hi01 = __builtin_bit_cast(h2, insert_bits(p01, 0x00F000F0u, 0x54005400u));
     h2 hi23 = __builtin_bit_cast(h2, insert_bits(p23, 0x00F000F0u, 0x54005400u));
-    lo01 -= b1024;
-    lo23 -= b1024;
-    hi01 -= b64;
-    hi23 -= b64;
+    if constexpr (!BIASED) {
+      lo01 -= b1024;
+      lo23 -= b1024;
+      hi01 -= b64;
+      hi23 -= b64;
+    }
     Blo = h4{lo01[0], lo01[1], lo23[0], lo23[1]};
     Bhi = h4{hi01[0], hi01[1], hi23[0], hi23[1]};
   } else {
@@ -356,10 +361,12 @@ __device__ __forceinline__ void v_operands(const uint32_t (&X)[4], int kb, h4& B
     h2 lo23 = __builtin_bit_cast(h2, __builtin_amdgcn_ubfe(X[2], m0, 3) | (__builtin_amdgcn_ubfe(X[3], m0, 3) << 16) | 0x64006400u);
     h2 hi01 = __builtin_bit_cast(h2, __builtin_amdgcn_ubfe(X[0], m1, 3) | (__builtin_amdgcn_ubfe(X[1], m1, 3) << 16) | 0x64006400u);
     h2 hi23 = __builtin_bit_cast(h2, __builtin_amdgcn_ubfe(X[2], m1, 3) | (__builtin_amdgcn_ubfe(X[3], m1, 3) << 16) | 0x64006400u);
-    lo01 -= b1024;
-    lo23 -= b1024;
-    hi01 -= b1024;
-    hi23 -= b1024;
+    if constexpr (!BIASED) {
+      lo01 -= b1024;
+      lo23 -= b1024;
+      hi01 -= b1024;
+      hi23 -= b1024;
+    }
     Blo = h4{lo01[0], lo01[1], lo23[0], lo23[1]};
     Bhi = h4{hi01[0], hi01[1], hi23[0], hi23[1]};
   }
@@ -461,6 +468,7 @@ __device__ __forceinline__ void softmax_rescale(const SlabSoftmax& sm, bool diag
   const float corr = __builtin_amdgcn_exp2f(st.m_run - m_new);   // 0 on the first slab
   st.l_part *= corr;
   st.z_part *= corr;
+  st.w_part *= corr;
   const f4 cr = rows_to_tile(corr, diag);       // O rows are heads 4*g4 + r
 #pragma unroll
   for (int r = 0; r < 4; ++r)
@@ -469,6 +477,8 @@ __device__ __forceinline__ void softmax_rescale(const SlabSoftmax& sm, bool diag
   st.m_run = m_new;
 }
 
+// The V operands stay biased (code + 1024, or + 64 for a high nibble); w_part
+// collects sum(p * scale) so that unbias() removes the bias from O at the end.
 template <int VB>
 __device__ __forceinline__ void softmax_accumulate(const float (&s)[4], const SlabSoftmax& sm,
                                                    const uint32_t (&X)[4], RunState& st) {
@@ -481,19 +491,34 @@ __device__ __forceinline__ void softmax_accumulate(const float (&s)[4], const Sl
     st.l_part += p;
     st.z_part += p * sm.zr[r];
     const float wf = p * sm.sc[r];
+    st.w_part += wf;
     W[r] = static_cast<_Float16>(wf);
     Wl[r] = static_cast<_Float16>(wf - static_cast<float>(W[r]));
   }
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb) {
     h4 Blo4, Bhi4;
-    v_operands<VB>(X, kb, Blo4, Bhi4);
+    v_operands<VB, true>(X, kb, Blo4, Bhi4);
     const h8 Blo = {Blo4[0], Blo4[1], Blo4[2], Blo4[3], Blo4[0], Blo4[1], Blo4[2], Blo4[3]};
     const h8 Bhi = {Bhi4[0], Bhi4[1], Bhi4[2], Bhi4[3], Bhi4[0], Bhi4[1], Bhi4[2], Bhi4[3]};
     const h8 Ws = {W[0], W[1], W[2], W[3], Wl[0], Wl[1], Wl[2], Wl[3]};
     st.O[2 * kb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ws, Blo, st.O[2 * kb], 0, 0, 0);
     st.O[2 * kb + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ws, Bhi, st.O[2 * kb + 1], 0, 0, 0);
     if (kb & 1) __builtin_amdgcn_sched_barrier(0);     // bounded operand registers
+  }
+}
+
+// Remove the V-operand bias from the accumulators of softmax_accumulate:
+// tile m holds coordinate 8*r16 + m, a low nibble (bias 1024) for even m and
+// a high nibble (bias 64) for odd m with 4-bit V; 3-bit V codes carry 1024.
+template <int VB>
+__device__ __forceinline__ void unbias(RunState& st, int g4) {
+  const float w = sum_x32(sum_x16(st.w_part));      // head r16's sum, in every g4
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const float wr = lane_value(w, 4 * g4 + r);     // O rows are heads 4*g4 + r
+#pragma unroll
+    for (int m = 0; m < 8; ++m) st.O[m][r] -= ((VB == 4 && (m & 1)) ? 64.0f : 1024.0f) * wr;
   }
 }
 
@@ -784,6 +809,7 @@ __global__ void __launch_bounds__(64, kSlabWavesPerSimd<KB>) decode_slab_kernel(
   st.m_run = -INFINITY;
   st.l_part = 0.0f;
   st.z_part = 0.0f;
+  st.w_part = 0.0f;
   const int p_first = t0 >> a.bs_shift;
   const DirectOffsets off = direct_offsets<KB, SLOT>(r16, g4, static_cast<uint32_t>(g * SLOT),
                                                      static_cast<uint32_t>(row_bytes));
@@ -1010,6 +1036,7 @@ __global__ void __launch_bounds__(64, kStagedWavesPerSimd<KB>) decode_staged_ker
   st.m_run = -INFINITY;
   st.l_part = 0.0f;
   st.z_part = 0.0f;
+  st.w_part = 0.0f;
   const int p_first = t0 >> a.bs_shift;
   // One LDS buffer suffices: a wavefront's LDS accesses complete in issue
   // order, so the next slab's writes never overtake this slab's reads.
@@ -1123,19 +1150,29 @@ struct PageGeom {
   }
 };
 
-// centroid table: entry e covers the codes e & (2^KB - 1) and e >> KB as
-// {pair of hi parts, pair of lo parts}: one 8-byte lookup per code byte (a
-// random lookup costs the same LDS time for 4 and 8 bytes)
+// centroid tables (2 KB): entry e covers the codes e & (2^KB - 1) and
+// e >> KB.  4-bit keys: {pair of hi parts, pair of lo parts} at 8-byte entry
+// e, one lookup per code byte.  3-bit keys: the pair of hi parts at word e
+// and the pair of lo parts at word 256 + e, two lookups from one address
+// that land directly in the hi and lo MFMA operands (no register moves);
+// their 64 entries fill one row of banks, so the lookups never conflict,
+// while a 256-entry 4-bit half table would conflict more than the 8-byte one.
 template <int KB>
 __device__ __forceinline__ void build_tables_page(const MfmaArgs& a, u32x2* tab) {
   constexpr int kTab = KB == 4 ? 256 : 64;
+  uint32_t* t32 = reinterpret_cast<uint32_t*>(tab);
   for (int e = threadIdx.x; e < kTab; e += blockDim.x) {
     const int c0 = e & ((1 << KB) - 1), c1 = e >> KB;
     const float v0 = a.tables->centroids[c0], v1 = a.tables->centroids[c1];
     const _Float16 h0 = static_cast<_Float16>(v0), h1 = static_cast<_Float16>(v1);
     const _Float16 l0 = static_cast<_Float16>(2.0f * (v0 - static_cast<float>(h0)));
     const _Float16 l1 = static_cast<_Float16>(2.0f * (v1 - static_cast<float>(h1)));
-    tab[e] = u32x2{pack_h2(h0, h1), pack_h2(l0, l1)};
+    if constexpr (KB == 4) {
+      tab[e] = u32x2{pack_h2(h0, h1), pack_h2(l0, l1)};
+    } else {
+      t32[e] = pack_h2(h0, h1);
+      t32[256 + e] = pack_h2(l0, l1);
+    }
   }
 }
 
@@ -1242,6 +1279,7 @@ __device__ __forceinline__ void slab_read(const uint8_t* buf, int w, int r16, in
 // centroid lookups of the code words (3/4-bit keys)
 template <int KB>
 __device__ __forceinline__ void slab_lookup(const u32x2* tab, SlabRegs<KB>& R) {
+  const uint32_t* t32 = reinterpret_cast<const uint32_t*>(tab);
   if constexpr (KB != 8) {
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk)
@@ -1258,7 +1296,8 @@ __device__ __forceinline__ void slab_lookup(const u32x2* tab, SlabRegs<KB>& R) {
           if (o > 26) v |= R.kw[wd + 1] << (32 - o);
           idx = v & 63u;
         }
-        R.e[4 * kk + p] = tab[idx];
+        if constexpr (KB == 4) R.e[4 * kk + p] = tab[idx];
+        else R.e[4 * kk + p] = u32x2{t32[idx], t32[256 + idx]};
       }
   }
 }
@@ -1376,6 +1415,7 @@ __global__ void __launch_bounds__(64 * H, page_waves_per_simd(KB)) decode_page_k
   st.m_run = -INFINITY;
   st.l_part = 0.0f;
   st.z_part = 0.0f;
+  st.w_part = 0.0f;
   const bool sel1 = (r16 & 1) != 0, sel2 = (r16 & 2) != 0;
 
   const int p_first = t0 >> a.bs_shift;
@@ -1484,6 +1524,7 @@ __global__ void __launch_bounds__(64 * H, page_waves_per_simd(KB)) decode_page_k
     ++j;
   }
   wait_vmcnt<0>();                           // no load may still write LDS at exit
+  unbias<vbits_of_slot(SLOT)>(st, g4);
   store_partials(a, b, g, split, g4, r16, st);
 }
 
@@ -1503,10 +1544,13 @@ __global__ void __launch_bounds__(64 * H, page_waves_per_simd(KB)) decode_page_k
 // ============================================================================
 
 // ---- split page (data region + meta region) ----
-// One head's slab in LDS: its 16 data rows (K codes, then V codes) kRowL
-// bytes apart, kRowL an odd number of 16-byte chunks so that rows 0..7 of a
-// column start in distinct bank groups; then the slab's 16 folded K norms,
-// 16 V scales and 16 V zeros (fp16), 32 bytes each.
+// One head's slab in LDS: its 16 data rows (K codes, then V codes), then the
+// slab's 16 folded K norms, 16 V scales and 16 V zeros (fp16, 32 bytes each).
+// Rows of 128 bytes (4-bit K and V) are packed, with the 16-byte chunk k of
+// row t at position k ^ (t & 7) of the row, so that the same chunk of rows
+// 0..7 falls in distinct bank groups; other rows are kRowL apart, an odd
+// number of chunks, which spreads them the same way.  The meta chunks fill
+// the last data load's spare lanes, or (128-byte rows) a load of 6 lanes.
 template <int KB, int VB>
 struct SoaGeom {
   static constexpr int kKCB = kD * KB / 8;                 // K code bytes
@@ -1514,12 +1558,18 @@ struct SoaGeom {
   static constexpr int kDB = kKCB + kVCB;                  // data bytes of a (token, head)
   static_assert(kDB % 16 == 0, "data rows of whole 16-byte chunks");
   static constexpr int kDataChunks = kDB / 16;
-  static constexpr int kRowChunks = kDataChunks | 1;
+  static constexpr bool kSwizzle = kDataChunks == 8;
+  static constexpr int kRowChunks = kSwizzle ? 8 : (kDataChunks | 1);
   static constexpr int kRowL = 16 * kRowChunks;
   static constexpr int kMetaOff = 16 * kRowL;
   static constexpr int kSlabChunks = 16 * kRowChunks + 6;
-  static constexpr int kWaveLoads = (kSlabChunks + 63) / 64;
-  static constexpr int kBuf = kWaveLoads * 1024;
+  static constexpr int kDataLoads = (16 * kRowChunks + 63) / 64;
+  static constexpr bool kMetaOwnLoad = kSlabChunks > 64 * kDataLoads;
+  static constexpr int kWaveLoads = kDataLoads + (kMetaOwnLoad ? 1 : 0);
+  static_assert(!kMetaOwnLoad || kMetaOff == 1024 * kDataLoads, "meta load lands after the rows");
+  static constexpr int kBuf = kMetaOwnLoad ? kMetaOff + 128 : 1024 * kWaveLoads;
+  // LDS byte offset of 16-byte data chunk k of row t
+  __device__ static constexpr int chunk_at(int t, int k) { return t * kRowL + 16 * (kSwizzle ? (k ^ (t & 7)) : k); }
 };
 
 // the slab's bytes for this lane from its LDS buffer (split page)
@@ -1527,7 +1577,7 @@ template <int KB, int VB>
 __device__ __forceinline__ void slab_read_soa(const uint8_t* buf, int r16, int g4, SlabRegs<KB>& R) {
   using Geo = SoaGeom<KB, VB>;
   if constexpr (KB == 4) {
-    const u32x4 t = *reinterpret_cast<const u32x4*>(buf + r16 * Geo::kRowL + 16 * g4);
+    const u32x4 t = *reinterpret_cast<const u32x4*>(buf + Geo::chunk_at(r16, g4));
     R.kw[0] = t[0]; R.kw[1] = t[1]; R.kw[2] = t[2]; R.kw[3] = t[3];
   } else {
     typedef uint32_t u32x3a __attribute__((ext_vector_type(3), aligned(4)));
@@ -1537,7 +1587,11 @@ __device__ __forceinline__ void slab_read_soa(const uint8_t* buf, int r16, int g
   const uint8_t* rb = buf + 4 * g4 * Geo::kRowL + Geo::kKCB;    // V codes of row 4*g4
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    if constexpr (VB == 4) {
+    if constexpr (Geo::kSwizzle) {
+      // V bytes [4*r16, 4*r16 + 4) of row 4*g4 + r: chunk kKCB/16 + r16/4
+      R.X[r] = *reinterpret_cast<const uint32_t*>(
+          buf + Geo::chunk_at(4 * g4 + r, Geo::kKCB / 16 + (r16 >> 2)) + 4 * (r16 & 3));
+    } else if constexpr (VB == 4) {
       R.X[r] = *reinterpret_cast<const uint32_t*>(rb + r * Geo::kRowL + 4 * r16);
     } else {
       const uint32_t* pv = reinterpret_cast<const uint32_t*>(rb + r * Geo::kRowL + ((3 * r16) & ~3));
@@ -1584,8 +1638,11 @@ __global__ void __launch_bounds__(64 * kRingWaves) decode_ring_kernel(MfmaArgs a
   using Geo = PageGeom<KB, SLOT, 1>;         // one head's slab layout in LDS (slotted page)
   using SGeo = SoaGeom<KB, VB>;              // ... (split page)
   constexpr int kLoads = SOA ? SGeo::kWaveLoads : Geo::kWaveLoads;   // 16-byte loads per lane per slab
-  constexpr int kBuf = 1024 * kLoads;        // covers every lane's chunk
-  constexpr int kRing = kRingBufs * kBuf;
+  constexpr int kBuf = SOA ? SGeo::kBuf : 1024 * kLoads;   // covers every lane's chunk
+  // slabs per wavefront ring: the split page's smaller slabs leave room for
+  // a fourth (three in flight)
+  constexpr int kBufs = SOA ? 4 : kRingBufs;
+  constexpr int kRing = kBufs * kBuf;
   static_assert(8 * kRec * 4 <= kRing, "a wavefront's partial records must fit its ring");
   __shared__ u32x2 s_tab[256];
   __shared__ int32_t s_pid[kRingMaxSlabs];
@@ -1632,6 +1689,7 @@ __global__ void __launch_bounds__(64 * kRingWaves) decode_ring_kernel(MfmaArgs a
   st.m_run = -INFINITY;
   st.l_part = 0.0f;
   st.z_part = 0.0f;
+  st.w_part = 0.0f;
   const bool sel1 = (r16 & 1) != 0, sel2 = (r16 & 2) != 0;
   const bool diag = (r16 >> 2) == g4;
 
@@ -1654,14 +1712,17 @@ __global__ void __launch_bounds__(64 * kRingWaves) decode_ring_kernel(MfmaArgs a
     src_mul[l] = 0;
     if constexpr (SOA) {
       const uint32_t data_row = static_cast<uint32_t>(a.H) * SGeo::kDB;
-      if (c < 16 * SGeo::kRowChunks) {
-        const int row = c / SGeo::kRowChunks, k = c - row * SGeo::kRowChunks;
-        if (k < SGeo::kDataChunks) {
-          src_off[l] = row * data_row + g * SGeo::kDB + 16 * k;
+      // position c of the slab buffer (the meta load's lanes 0..5 follow the rows)
+      const int pc = SGeo::kMetaOwnLoad && l == kLoads - 1 ? 16 * SGeo::kRowChunks + lane : c;
+      if (pc < 16 * SGeo::kRowChunks) {
+        const int row = pc / SGeo::kRowChunks, k = pc - row * SGeo::kRowChunks;
+        const int dk = SGeo::kSwizzle ? (k ^ (row & 7)) : k;   // the data chunk stored there
+        if (dk < SGeo::kDataChunks) {
+          src_off[l] = row * data_row + g * SGeo::kDB + 16 * dk;
           src_mul[l] = data_row;
         }
-      } else if (c < SGeo::kSlabChunks) {
-        const int m = c - 16 * SGeo::kRowChunks;          // fields norm, scale, zero: 2 chunks each
+      } else if (pc < SGeo::kSlabChunks) {
+        const int m = pc - 16 * SGeo::kRowChunks;         // fields norm, scale, zero: 2 chunks each
         src_off[l] = (data_row << a.bs_shift) + ((3 * g + (m >> 1)) << (a.bs_shift + 1)) + 16 * (m & 1);
         src_mul[l] = 2;
       }
@@ -1689,12 +1750,17 @@ __global__ void __launch_bounds__(64 * kRingWaves) decode_ring_kernel(MfmaArgs a
                             : pid * page_bytes + static_cast<int64_t>(t & bs_mask) * row_bytes + head_bytes;
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint8_t*>(a.cache) + off, 0, pid >= 0 ? static_cast<int>(range) : 0, kBufferWord3);
-    uint8_t* dst = ring + (j % kRingBufs) * kBuf;
+    uint8_t* dst = ring + (j % kBufs) * kBuf;
     if constexpr (SOA) {
       // whole lines of this head alone (the data rows): non-temporal
       const uint32_t r0 = static_cast<uint32_t>(t & bs_mask);
 #pragma unroll
-      for (int l = 0; l < kLoads; ++l) lds_dma_16<true>(rs, dst + l * 1024, src_off[l] + r0 * src_mul[l]);
+      for (int l = 0; l < SGeo::kDataLoads; ++l)
+        lds_dma_16<true>(rs, dst + l * 1024, src_off[l] + r0 * src_mul[l]);
+      if constexpr (SGeo::kMetaOwnLoad) {
+        // 96 bytes: six lanes write LDS, the others are masked off
+        if (lane < 6) lds_dma_16<true>(rs, dst + SGeo::kMetaOff, src_off[kLoads - 1] + r0 * src_mul[kLoads - 1]);
+      }
     } else {
 #pragma unroll
       for (int l = 0; l < kLoads; ++l) lds_dma_16<false>(rs, dst + l * 1024, src_off[l]);
@@ -1704,7 +1770,7 @@ __global__ void __launch_bounds__(64 * kRingWaves) decode_ring_kernel(MfmaArgs a
 
   if (n_slabs > 0) {
 #pragma unroll
-    for (int j = 0; j < kRingBufs - 1; ++j) issue(j);
+    for (int j = 0; j < kBufs - 1; ++j) issue(j);
     int j = 0;
     while (true) {
       float s[4];
@@ -1712,16 +1778,17 @@ __global__ void __launch_bounds__(64 * kRingWaves) decode_ring_kernel(MfmaArgs a
       SlabRegs<KB> c;
       bool grow = false;
       for (; j < n_slabs; ++j) {
-        // slab j has landed (slab j + 1 may be in flight); this wavefront's
-        // reads of slab j - 1 have completed, so its buffer takes slab j + 2
-        wait_vmcnt<kLoads * (kRingBufs - 2)>();
+        // slab j has landed (the next kBufs - 2 may be in flight); this
+        // wavefront's reads of slab j - 1 have completed, so its buffer takes
+        // slab j + kBufs - 1
+        wait_vmcnt<kLoads * (kBufs - 2)>();
         __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-        issue(j + kRingBufs - 1);
+        issue(j + kBufs - 1);
         if (__builtin_amdgcn_readfirstlane(page_of(j)) < 0) continue;
         if constexpr (SOA)
-          slab_read_soa<KB, VB>(ring + (j % kRingBufs) * kBuf, r16, g4, c);
+          slab_read_soa<KB, VB>(ring + (j % kBufs) * kBuf, r16, g4, c);
         else
-          slab_read<KB, SLOT, 1>(ring + (j % kRingBufs) * kBuf, 0, r16, g4, c);
+          slab_read<KB, SLOT, 1>(ring + (j % kBufs) * kBuf, 0, r16, g4, c);
         slab_lookup<KB>(s_tab, c);
         const ScoreAcc acc = slab_mfma<KB, !SOA>(c, qc, qb);
         const int valid = t1 - (t0 + 16 * j);
@@ -1751,6 +1818,7 @@ __global__ void __launch_bounds__(64 * kRingWaves) decode_ring_kernel(MfmaArgs a
     }
     wait_vmcnt<0>();                         // no load may still write the ring
   }
+  unbias<VB>(st, g4);
 
   // ---- combine the 16 wavefronts' states in LDS ----
   // each wavefront's records (O[128], m, l, z per query head) go into its own

@@ -46,12 +46,13 @@ def sources_sha256(kind):
     return h.hexdigest()[:16]
 
 
-def counted_traffic(kind, workload):
+def counted_traffic(kind, workload, layout="aos"):
     """HBM bytes per launch of the store or decode on `workload`, as rocprofv3's
     FETCH_SIZE + WRITE_SIZE counters read them (calibrated against plain
     streaming kernels of known size), from the summary under profiles/; None
     when there is no summary taken on the current kernel sources."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{kind}_{workload}.txt")
+    suffix = "" if layout == "aos" else f"_{layout}"
+    path = os.path.join(ROOT, "profiles", f"traffic_{kind}_{workload}{suffix}.txt")
     if not os.path.exists(path):
         return None
     rec = {}
@@ -141,6 +142,9 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama3_8b")
+    ap.add_argument("--layout", choices=["aos", "soa"], default="aos",
+                    help="page layout: slots back to back (default), or the split page "
+                         "(data region + fp16 meta region, K norm folded at store time)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--flush", choices=["read", "write", "none"], default="read",
                     help="how caches are evicted before each timed kernel: read a 1 GiB buffer "
@@ -171,7 +175,7 @@ def main():
     k, v, q = up(inp.k), up(inp.v), up(inp.q)
     sm, bt, sl = up(inp.slot_mapping), up(inp.block_table), up(inp.seq_lens)
     tq = PackedKVCache(w.preset, w.head_dim, w.num_kv_heads, w.block_size, rot_seed=2024,
-                       device=dev)
+                       device=dev, layout=args.layout)
     cache = tq.new_cache(inp.num_blocks)
     max_len = int(inp.seq_lens.max())
     out = torch.empty((w.batch, w.num_q_heads, w.head_dim), dtype=torch.bfloat16, device=dev)
@@ -260,7 +264,7 @@ def main():
                    "seq_len": int(inp.seq_lens.max()), "num_q_heads": w.num_q_heads,
                    "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
                    "block_size": w.block_size, "cache_bytes": int(n_tok * w.num_kv_heads * slot),
-                   "cache_flush": args.flush},
+                   "layout": args.layout, "cache_flush": args.flush},
         "decode_us": round(t_dec.mean() * 1e6, 2),
         "decode_us_p10_p90": [round(float(np.percentile(t_dec, 10)) * 1e6, 2),
                               round(float(np.percentile(t_dec, 90)) * 1e6, 2)],
@@ -269,12 +273,12 @@ def main():
         "store_us": round(t_store.mean() * 1e6, 2),
         "roofline": {"bound": "hbm", "achieved": round(dec_gbs, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": counted_traffic("decode", w.name),
+                     "traffic": counted_traffic("decode", w.name, args.layout),
                      "kernel": "tq_decode (split kernel + merge kernel)",
                      "alg_bytes_per_launch": dec_bytes},
         "roofline_store": {"bound": "hbm", "achieved": round(st_gbs, 2), "peak": HBM_PEAK_GBS,
                            "unit": "GB/s", "frac": round(st_gbs / HBM_PEAK_GBS, 4),
-                           "traffic": counted_traffic("store", w.name), "kernel": "tq_store",
+                           "traffic": counted_traffic("store", w.name, args.layout), "kernel": "tq_store",
                            "alg_bytes_per_launch": st_bytes},
         "kernel_sources_sha256": {k: sources_sha256(k) for k in KERNEL_SOURCES},
         "wall_ms_per_step_incl_flush": round(wall / args.steps * 1e3, 3),

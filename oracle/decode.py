@@ -23,6 +23,12 @@ For sequence b, query head h and kv head g = h // (Hq / H) (P1, section
   * an empty sequence yields zeros (the pages are silent; this matches the
     page's rule that an empty split contributes nothing, lse = -inf).
 
+``dequant_kv_f64`` expands one sequence back into K and V of the original
+space, and ``decode_continuation_f64`` is the causal attention of a chunk of
+new queries run as decode requests of growing length (P1, sections "反量化
+kernel:_tq_full_dequant_kv" and "续写 prefill:小 chunk 走 decode,大 chunk 走反
+量化").
+
 ``split_partials`` and ``combine_partials`` restate the split-KV scheme
 (P1, sections "读取内核" and "在线 softmax"): each split keeps (max, sum,
 acc), stores acc / sum and lse = max + log(sum); the combine weights each
@@ -143,3 +149,34 @@ def combine_partials(parts):
     den = w.sum(axis=0)
     num = (w[..., None] * outs).sum(axis=0)
     return np.where(den[:, None] > 0, num / np.where(den > 0, den, 1.0)[:, None], 0.0)
+
+
+def dequant_kv_f64(cache, block_table_row, seq_len, layout, signs, centroids):
+    """K and V [seq_len, H, d] of one sequence back in the original space, in
+    float64 (P1, section "反量化 kernel:_tq_full_dequant_kv"): the key is
+    n R^T c with the explicit rotation matrix (FP8 keys: the decoded bytes),
+    the value code * scale + zero."""
+    H = cache.shape[2]
+    d = layout.head_dim
+    K = np.zeros((seq_len, H, d))
+    V = np.zeros((seq_len, H, d))
+    R = None if layout.key_fp8 else rotation_matrix_f64(signs)
+    for g in range(H):
+        slots = gather_slots(cache, block_table_row, seq_len, g)
+        kc, n = dequant_keys(slots, layout, centroids)
+        K[:, g] = kc if layout.key_fp8 else n[:, None] * (kc @ R)
+        V[:, g] = dequant_values(slots, layout)
+    return K, V
+
+
+def decode_continuation_f64(q_bits, cache, block_table_row, seq_len, layout, signs, centroids,
+                            num_kv_heads, sm_scale=None):
+    """Causal attention of a chunk of q_len queries (the last q_len of seq_len
+    stored tokens), P1 section "续写 prefill:小 chunk 走 decode,大 chunk 走反量化":
+    query i is a decode request of length seq_len - q_len + i + 1 over the
+    sequence's block-table row."""
+    q_len = np.asarray(q_bits).shape[0]
+    cached = seq_len - q_len
+    lens = cached + 1 + np.arange(q_len)
+    table = np.repeat(np.asarray(block_table_row)[None], q_len, axis=0)
+    return decode_f64(q_bits, cache, table, lens, layout, signs, centroids, num_kv_heads, sm_scale)

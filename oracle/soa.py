@@ -168,3 +168,18 @@ def decode_f64(q_bits, pages, block_table, seq_lens, layout, signs, centroids, n
             s = scores_f64(q[b, hs], (c, n), layout, signs, sm_scale)
             out[b, hs] = attend_f64(s, v_hat)
     return out
+
+
+def dequant_kv_f64(pages, layout, block_size, H, block_table_row, seq_len, signs, centroids):
+    """K and V [seq_len, H, d] of one sequence of a split-page cache, float64:
+    the key is n R^T c with the stored (folded) norm n."""
+    from .rotation import rotation_matrix_f64
+    d = layout.head_dim
+    R = rotation_matrix_f64(signs)
+    K = np.zeros((seq_len, H, d))
+    V = np.zeros((seq_len, H, d))
+    for g in range(H):
+        c, n, v_hat = dequant(pages, layout, block_size, H, block_table_row, seq_len, g, centroids)
+        K[:, g] = n[:, None] * (c @ R)
+        V[:, g] = v_hat
+    return K, V

@@ -132,7 +132,6 @@ struct RunState {
   float m_run;      // running (lazy) max, base 2, of head r16
   float l_part;     // sum of p over this lane's rows, head r16
   float z_part;     // sum of p * zero over this lane's rows, head r16
-  float w_part;     // sum of p * scale over this lane's rows, head r16 (biased V operands)
 };
 
 // Operand bytes of one slab for one lane, already re-aligned.
@@ -331,13 +330,11 @@ constexpr int vbits_of_slot(int slot) { return slot == 102 ? 3 : 4; }
 // 8*r16 + 2*kb + 1 (Bhi), as exact f16 integers: code c becomes the f16 with
 // bits 0x6400 | c (1024 + c) minus 1024, and for the high nibble of a 4-bit
 // byte 0x5400 | (c << 4) (64 + c) minus 64
-// BIASED: the operands keep the 1024 (or 64) and the caller subtracts
-// bias * sum(p * scale) from the accumulators once at the end (unbias).
-template <int VB, bool BIASED = false>
+template <int VB>
 __device__ __forceinline__ void v_operands(const uint32_t (&X)[4], int kb, h4& Blo, h4& Bhi) {
-  const h2 b1024 = {static_cast<_Float16>(BIASED ? 0.0f : 1024.0f), static_cast<_Float16>(BIASED ? 0.0f : 1024.0f)};
+  const h2 b1024 = {static_cast<_Float16>(1024.0f), static_cast<_Float16>(1024.0f)};
   if constexpr (VB == 4) {
-    const h2 b64 = {static_cast<_Float16>(BIASED ? 0.0f : 64.0f), static_cast<_Float16>(BIASED ? 0.0f : 64.0f)};
+    const h2 b64 = {static_cast<_Float16>(64.0f), static_cast<_Float16>(64.0f)};
     // byte kb of each token's dword -> [x0, 0, x1, 0]
     const uint32_t sel = kb | (0x0Cu << 8) | ((4u + kb) << 16) | (0x0Cu << 24);
     const uint32_t p01 = __builtin_amdgcn_perm(X[1], X[0], sel);
@@ -346,12 +343,10 @@ __device__ __forceinline__ void v_operands(const uint32_t (&X)[4], int kb, h4& B
     h2 lo23 = __builtin_bit_cast(h2, insert_bits(p23, 0x000F000Fu, 0x64006400u));
     h2 hi01 = __builtin_bit_cast(h2, insert_bits(p01, 0x00F000F0u, 0x54005400u));
     h2 hi23 = __builtin_bit_cast(h2, insert_bits(p23, 0x00F000F0u, 0x54005400u));
-    if constexpr (!BIASED) {
-      lo01 -= b1024;
-      lo23 -= b1024;
-      hi01 -= b64;
-      hi23 -= b64;
-    }
+    lo01 -= b1024;
+    lo23 -= b1024;
+    hi01 -= b64;
+    hi23 -= b64;
     Blo = h4{lo01[0], lo01[1], lo23[0], lo23[1]};
     Bhi = h4{hi01[0], hi01[1], hi23[0], hi23[1]};
   } else {
@@ -361,12 +356,10 @@ __device__ __forceinline__ void v_operands(const uint32_t (&X)[4], int kb, h4& B
     h2 lo23 = __builtin_bit_cast(h2, __builtin_amdgcn_ubfe(X[2], m0, 3) | (__builtin_amdgcn_ubfe(X[3], m0, 3) << 16) | 0x64006400u);
     h2 hi01 = __builtin_bit_cast(h2, __builtin_amdgcn_ubfe(X[0], m1, 3) | (__builtin_amdgcn_ubfe(X[1], m1, 3) << 16) | 0x64006400u);
     h2 hi23 = __builtin_bit_cast(h2, __builtin_amdgcn_ubfe(X[2], m1, 3) | (__builtin_amdgcn_ubfe(X[3], m1, 3) << 16) | 0x64006400u);
-    if constexpr (!BIASED) {
-      lo01 -= b1024;
-      lo23 -= b1024;
-      hi01 -= b1024;
-      hi23 -= b1024;
-    }
+    lo01 -= b1024;
+    lo23 -= b1024;
+    hi01 -= b1024;
+    hi23 -= b1024;
     Blo = h4{lo01[0], lo01[1], lo23[0], lo23[1]};
     Bhi = h4{hi01[0], hi01[1], hi23[0], hi23[1]};
   }
@@ -468,7 +461,6 @@ __device__ __forceinline__ void softmax_rescale(const SlabSoftmax& sm, bool diag
   const float corr = __builtin_amdgcn_exp2f(st.m_run - m_new);   // 0 on the first slab
   st.l_part *= corr;
   st.z_part *= corr;
-  st.w_part *= corr;
   const f4 cr = rows_to_tile(corr, diag);       // O rows are heads 4*g4 + r
 #pragma unroll
   for (int r = 0; r < 4; ++r)
@@ -477,8 +469,6 @@ __device__ __forceinline__ void softmax_rescale(const SlabSoftmax& sm, bool diag
   st.m_run = m_new;
 }
 
-// The V operands stay biased (code + 1024, or + 64 for a high nibble); w_part
-// collects sum(p * scale) so that unbias() removes the bias from O at the end.
 template <int VB>
 __device__ __forceinline__ void softmax_accumulate(const float (&s)[4], const SlabSoftmax& sm,
                                                    const uint32_t (&X)[4], RunState& st) {
@@ -491,34 +481,19 @@ __device__ __forceinline__ void softmax_accumulate(const float (&s)[4], const Sl
     st.l_part += p;
     st.z_part += p * sm.zr[r];
     const float wf = p * sm.sc[r];
-    st.w_part += wf;
     W[r] = static_cast<_Float16>(wf);
     Wl[r] = static_cast<_Float16>(wf - static_cast<float>(W[r]));
   }
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb) {
     h4 Blo4, Bhi4;
-    v_operands<VB, true>(X, kb, Blo4, Bhi4);
+    v_operands<VB>(X, kb, Blo4, Bhi4);
     const h8 Blo = {Blo4[0], Blo4[1], Blo4[2], Blo4[3], Blo4[0], Blo4[1], Blo4[2], Blo4[3]};
     const h8 Bhi = {Bhi4[0], Bhi4[1], Bhi4[2], Bhi4[3], Bhi4[0], Bhi4[1], Bhi4[2], Bhi4[3]};
     const h8 Ws = {W[0], W[1], W[2], W[3], Wl[0], Wl[1], Wl[2], Wl[3]};
     st.O[2 * kb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ws, Blo, st.O[2 * kb], 0, 0, 0);
     st.O[2 * kb + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ws, Bhi, st.O[2 * kb + 1], 0, 0, 0);
     if (kb & 1) __builtin_amdgcn_sched_barrier(0);     // bounded operand registers
-  }
-}
-
-// Remove the V-operand bias from the accumulators of softmax_accumulate:
-// tile m holds coordinate 8*r16 + m, a low nibble (bias 1024) for even m and
-// a high nibble (bias 64) for odd m with 4-bit V; 3-bit V codes carry 1024.
-template <int VB>
-__device__ __forceinline__ void unbias(RunState& st, int g4) {
-  const float w = sum_x32(sum_x16(st.w_part));      // head r16's sum, in every g4
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const float wr = lane_value(w, 4 * g4 + r);     // O rows are heads 4*g4 + r
-#pragma unroll
-    for (int m = 0; m < 8; ++m) st.O[m][r] -= ((VB == 4 && (m & 1)) ? 64.0f : 1024.0f) * wr;
   }
 }
 
@@ -809,7 +784,6 @@ __global__ void __launch_bounds__(64, kSlabWavesPerSimd<KB>) decode_slab_kernel(
   st.m_run = -INFINITY;
   st.l_part = 0.0f;
   st.z_part = 0.0f;
-  st.w_part = 0.0f;
   const int p_first = t0 >> a.bs_shift;
   const DirectOffsets off = direct_offsets<KB, SLOT>(r16, g4, static_cast<uint32_t>(g * SLOT),
                                                      static_cast<uint32_t>(row_bytes));
@@ -1036,7 +1010,6 @@ __global__ void __launch_bounds__(64, kStagedWavesPerSimd<KB>) decode_staged_ker
   st.m_run = -INFINITY;
   st.l_part = 0.0f;
   st.z_part = 0.0f;
-  st.w_part = 0.0f;
   const int p_first = t0 >> a.bs_shift;
   // One LDS buffer suffices: a wavefront's LDS accesses complete in issue
   // order, so the next slab's writes never overtake this slab's reads.
@@ -1415,7 +1388,6 @@ __global__ void __launch_bounds__(64 * H, page_waves_per_simd(KB)) decode_page_k
   st.m_run = -INFINITY;
   st.l_part = 0.0f;
   st.z_part = 0.0f;
-  st.w_part = 0.0f;
   const bool sel1 = (r16 & 1) != 0, sel2 = (r16 & 2) != 0;
 
   const int p_first = t0 >> a.bs_shift;
@@ -1524,7 +1496,6 @@ __global__ void __launch_bounds__(64 * H, page_waves_per_simd(KB)) decode_page_k
     ++j;
   }
   wait_vmcnt<0>();                           // no load may still write LDS at exit
-  unbias<vbits_of_slot(SLOT)>(st, g4);
   store_partials(a, b, g, split, g4, r16, st);
 }
 
@@ -1689,7 +1660,6 @@ __global__ void __launch_bounds__(64 * kRingWaves) decode_ring_kernel(MfmaArgs a
   st.m_run = -INFINITY;
   st.l_part = 0.0f;
   st.z_part = 0.0f;
-  st.w_part = 0.0f;
   const bool sel1 = (r16 & 1) != 0, sel2 = (r16 & 2) != 0;
   const bool diag = (r16 >> 2) == g4;
 
@@ -1752,14 +1722,16 @@ __global__ void __launch_bounds__(64 * kRingWaves) decode_ring_kernel(MfmaArgs a
         const_cast<uint8_t*>(a.cache) + off, 0, pid >= 0 ? static_cast<int>(range) : 0, kBufferWord3);
     uint8_t* dst = ring + (j % kBufs) * kBuf;
     if constexpr (SOA) {
-      // whole lines of this head alone (the data rows): non-temporal
+      // plain loads: the meta fields of neighbouring heads share lines, and
+      // so do their data rows when a row is not 128 bytes (measured: the
+      // same time as non-temporal loads for 4-bit rows, less traffic)
       const uint32_t r0 = static_cast<uint32_t>(t & bs_mask);
 #pragma unroll
       for (int l = 0; l < SGeo::kDataLoads; ++l)
-        lds_dma_16<true>(rs, dst + l * 1024, src_off[l] + r0 * src_mul[l]);
+        lds_dma_16<false>(rs, dst + l * 1024, src_off[l] + r0 * src_mul[l]);
       if constexpr (SGeo::kMetaOwnLoad) {
         // 96 bytes: six lanes write LDS, the others are masked off
-        if (lane < 6) lds_dma_16<true>(rs, dst + SGeo::kMetaOff, src_off[kLoads - 1] + r0 * src_mul[kLoads - 1]);
+        if (lane < 6) lds_dma_16<false>(rs, dst + SGeo::kMetaOff, src_off[kLoads - 1] + r0 * src_mul[kLoads - 1]);
       }
     } else {
 #pragma unroll
@@ -1818,7 +1790,6 @@ __global__ void __launch_bounds__(64 * kRingWaves) decode_ring_kernel(MfmaArgs a
     }
     wait_vmcnt<0>();                         // no load may still write the ring
   }
-  unbias<VB>(st, g4);
 
   // ---- combine the 16 wavefronts' states in LDS ----
   // each wavefront's records (O[128], m, l, z per query head) go into its own

@@ -208,6 +208,60 @@ tq_status tq_decode(const tq_ctx* ctx, const void* q, const uint8_t* cache, int6
                     int batch, int num_q_heads, int max_seq_len, float sm_scale, void* out,
                     int out_is_fp32, void* workspace, size_t workspace_bytes, void* stream);
 
+/* tq_dequant -- P1, section "反量化 kernel:_tq_full_dequant_kv".
+ *
+ * Expand the first seq_len tokens of one sequence back into K and V vectors
+ * of the original space (the input of the pages' long-chunk continuation
+ * prefill, section "续写 prefill:小 chunk 走 decode,大 chunk 走反量化"):
+ * token t, head h reads slot row t % block_size of page block_table_row[t /
+ * block_size] and writes
+ *   MSE K:  k = n * R^T c (c the centroids of the codes, n the stored norm,
+ *           divided by sqrt(sum c^2 + 1e-16) on the slotted page; R^T the
+ *           inverse of the store's rotation, applied as butterflies);
+ *   FP8 K:  k = e4m3(byte);
+ *   V:      v = code * scale16 + zero16.
+ *
+ *   cache            device, as written by tq_store, `num_blocks` pages
+ *   block_table_row  device, int32 [max_blocks]; max_blocks * block_size must
+ *                    cover seq_len.  A page id outside [0, num_blocks) writes
+ *                    zeros for its tokens and sets device error bit 1
+ *   k_out, v_out     device, [seq_len][num_kv_heads][head_dim], bf16 (round to
+ *                    nearest even) when out_is_fp32 == 0, fp32 otherwise;
+ *                    16-byte aligned
+ * seq_len 0 is a no-op.  Allocates nothing; asynchronous on `stream`. */
+tq_status tq_dequant(const tq_ctx* ctx, const uint8_t* cache, int64_t num_blocks,
+                     const int32_t* block_table_row, int max_blocks, int seq_len, void* k_out,
+                     void* v_out, int out_is_fp32, void* stream);
+
+/* Workspace bytes tq_decode_continuation needs: the decode's workspace for
+ * q_len requests of length up to seq_len, plus the synthetic lengths and the
+ * expanded block table (q_len * (max_blocks + 1) int32).  0 on bad input. */
+size_t tq_continuation_workspace_bytes(const tq_ctx* ctx, int q_len, int num_q_heads, int seq_len,
+                                       int max_blocks);
+
+/* tq_decode_continuation -- P1, section "续写 prefill:小 chunk 走 decode,大
+ * chunk 走反量化" (the short-chunk path, for chunks of up to 128 queries).
+ *
+ * Causal attention of a chunk of q_len new queries of one sequence whose
+ * seq_len tokens (the cached_len = seq_len - q_len earlier ones and the
+ * chunk's own, already stored with tq_store) are in the cache: query i
+ * attends to tokens [0, cached_len + i + 1).  Each query is run as a decode
+ * request of that length over the sequence's block-table row, which is how
+ * the causal mask arises without a mask tensor.
+ *
+ *   q                [q_len][num_q_heads][head_dim] bf16, 16-byte aligned
+ *   block_table_row  device, int32 [max_blocks]; max_blocks * block_size >= seq_len
+ *   seq_len          cached tokens plus q_len; q_len in [1, seq_len]
+ *   out              [q_len][num_q_heads][head_dim], bf16 or fp32 (out_is_fp32)
+ *   workspace        device, >= tq_continuation_workspace_bytes(...), 256-byte
+ *                    aligned; calls that share it must not overlap
+ * Errors as tq_decode.  Allocates nothing; asynchronous on `stream`. */
+tq_status tq_decode_continuation(const tq_ctx* ctx, const void* q, const uint8_t* cache,
+                                 int64_t num_blocks, const int32_t* block_table_row, int max_blocks,
+                                 int seq_len, int q_len, int num_q_heads, float sm_scale, void* out,
+                                 int out_is_fp32, void* workspace, size_t workspace_bytes,
+                                 void* stream);
+
 /* Read the sticky device error word (synchronises with the device):
  * bit 0 = a store slot beyond the cache, bit 1 = a page id beyond the cache,
  * bit 2 = a seq_lens entry outside [0, max_seq_len] (clamped).

@@ -23,7 +23,8 @@ LAYOUTS = {"aos": 0, "soa": 1}
 
 # every symbol include/tq.h declares
 EXPORTS = ("tq_codebook_init", "tq_codebook_init_layout", "tq_layout_of", "tq_destroy", "tq_slot_bytes", "tq_cache_bytes", "tq_get_tables",
-           "tq_store", "tq_decode_workspace_bytes", "tq_decode", "tq_get_device_error",
+           "tq_store", "tq_decode_workspace_bytes", "tq_decode", "tq_dequant",
+           "tq_continuation_workspace_bytes", "tq_decode_continuation", "tq_get_device_error",
            "tq_host_codebook", "tq_host_rotation_signs", "tq_host_slot_bytes", "tq_status_str")
 
 
@@ -64,6 +65,10 @@ def load():
         "tq_decode_workspace_bytes": (ctypes.c_size_t, [_vp, _int, _int, _int]),
         "tq_decode": (_int, [_vp, _vp, _vp, _i64, _vp, _int, _vp, _int, _int, _int, ctypes.c_float,
                              _vp, _int, _vp, ctypes.c_size_t, _vp]),
+        "tq_dequant": (_int, [_vp, _vp, _i64, _vp, _int, _int, _vp, _vp, _int, _vp]),
+        "tq_continuation_workspace_bytes": (ctypes.c_size_t, [_vp, _int, _int, _int, _int]),
+        "tq_decode_continuation": (_int, [_vp, _vp, _vp, _i64, _vp, _int, _int, _int, _int, ctypes.c_float,
+                                          _vp, _int, _vp, ctypes.c_size_t, _vp]),
         "tq_get_device_error": (_int, [_vp, ctypes.POINTER(_i32), _int]),
         "tq_host_codebook": (_int, [_int, _int, _int, _vp, _vp]),
         "tq_host_rotation_signs": (_int, [ctypes.c_uint64, _int, _int, _vp]),
@@ -175,6 +180,27 @@ def tq_decode(ctx, q, cache, num_blocks, block_table, max_blocks_per_seq, seq_le
                                          max_blocks_per_seq, _ptr(seq_lens), batch, num_q_heads,
                                          max_seq_len, float(sm_scale), _ptr(out), int(out_is_fp32),
                                          _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+def tq_dequant(ctx, cache, num_blocks, block_table_row, max_blocks, seq_len, k_out, v_out, out_is_fp32,
+               stream=None):
+    _check("tq_dequant", load().tq_dequant(ctx, _ptr(cache), num_blocks, _ptr(block_table_row), max_blocks,
+                                           seq_len, _ptr(k_out), _ptr(v_out), int(out_is_fp32),
+                                           _stream(stream)))
+
+
+def tq_continuation_workspace_bytes(ctx, q_len, num_q_heads, seq_len, max_blocks):
+    return load().tq_continuation_workspace_bytes(ctx, q_len, num_q_heads, seq_len, max_blocks)
+
+
+def tq_decode_continuation(ctx, q, cache, num_blocks, block_table_row, max_blocks, seq_len, q_len,
+                           num_q_heads, sm_scale, out, out_is_fp32, workspace, workspace_bytes,
+                           stream=None):
+    _check("tq_decode_continuation",
+           load().tq_decode_continuation(ctx, _ptr(q), _ptr(cache), num_blocks, _ptr(block_table_row),
+                                         max_blocks, seq_len, q_len, num_q_heads, float(sm_scale),
+                                         _ptr(out), int(out_is_fp32), _ptr(workspace), workspace_bytes,
+                                         _stream(stream)))
 
 
 def tq_get_device_error(ctx, clear=True):

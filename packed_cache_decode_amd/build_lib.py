@@ -26,6 +26,7 @@ SOURCES = [
     ("tq_store.hip", ["-ffp-contract=off"]),
     ("tq_decode.hip", []),
     ("tq_decode_mfma.hip", ["-fno-honor-nans"]),
+    ("tq_dequant.hip", []),
 ]
 
 

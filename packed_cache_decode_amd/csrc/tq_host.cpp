@@ -507,6 +507,77 @@ tq_status tq_decode(const tq_ctx* ctx, const void* q, const uint8_t* cache, int6
   return e == hipSuccess ? TQ_OK : TQ_ERR_HIP;
 }
 
+tq_status tq_dequant(const tq_ctx* ctx, const uint8_t* cache, int64_t num_blocks,
+                     const int32_t* block_table_row, int max_blocks, int seq_len, void* k_out,
+                     void* v_out, int out_is_fp32, void* stream) {
+  if (!ctx) return TQ_ERR_INVALID_ARG;
+  const Geometry& g = ctx->geo;
+  if (seq_len < 0 || max_blocks < 0 || num_blocks < 0) return TQ_ERR_INVALID_ARG;
+  if (seq_len == 0) return TQ_OK;
+  if (!cache || !block_table_row || !k_out || !v_out) return TQ_ERR_INVALID_ARG;
+  if (static_cast<int64_t>(max_blocks) * g.block_size < seq_len) return TQ_ERR_INVALID_ARG;
+  if (!aligned(cache, 16) || !aligned(block_table_row, 4) || !aligned(k_out, 16) || !aligned(v_out, 16))
+    return TQ_ERR_ALIGNMENT;
+  tq_status ds = check_device(ctx);
+  if (ds != TQ_OK) return ds;
+  hipError_t e = tq::launch_dequant(g, ctx->d_tables, cache, num_blocks, block_table_row, seq_len, k_out,
+                                    v_out, out_is_fp32, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? TQ_OK : TQ_ERR_HIP;
+}
+
+namespace {
+// workspace of a continuation: decode workspace, then q_len lengths, then the
+// q_len x max_blocks expanded table (each part 256-byte aligned)
+struct ContinuationSpace {
+  size_t decode, lens_off, table_off, total;
+};
+ContinuationSpace continuation_space(const Geometry& g, int q_len, int num_q_heads, int seq_len,
+                                     int max_blocks) {
+  ContinuationSpace c;
+  c.decode = tq::plan_decode(g, q_len, num_q_heads, seq_len).workspace_bytes;
+  c.lens_off = (c.decode + 255) & ~static_cast<size_t>(255);
+  c.table_off = (c.lens_off + 4 * static_cast<size_t>(q_len) + 255) & ~static_cast<size_t>(255);
+  c.total = c.table_off + 4 * static_cast<size_t>(q_len) * max_blocks;
+  return c;
+}
+}  // namespace
+
+size_t tq_continuation_workspace_bytes(const tq_ctx* ctx, int q_len, int num_q_heads, int seq_len,
+                                       int max_blocks) {
+  if (!ctx || q_len <= 0 || num_q_heads <= 0 || seq_len < q_len || max_blocks <= 0) return 0;
+  if (num_q_heads % ctx->geo.num_kv_heads != 0) return 0;
+  return continuation_space(ctx->geo, q_len, num_q_heads, seq_len, max_blocks).total;
+}
+
+tq_status tq_decode_continuation(const tq_ctx* ctx, const void* q, const uint8_t* cache,
+                                 int64_t num_blocks, const int32_t* block_table_row, int max_blocks,
+                                 int seq_len, int q_len, int num_q_heads, float sm_scale, void* out,
+                                 int out_is_fp32, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
+  if (!ctx) return TQ_ERR_INVALID_ARG;
+  const Geometry& g = ctx->geo;
+  if (q_len <= 0 || seq_len < q_len || max_blocks <= 0 || num_q_heads <= 0 || num_blocks < 0)
+    return TQ_ERR_INVALID_ARG;
+  if (num_q_heads % g.num_kv_heads != 0) return TQ_ERR_INVALID_ARG;
+  if (num_q_heads / g.num_kv_heads > 16) return TQ_ERR_UNSUPPORTED;
+  if (!q || !cache || !block_table_row || !out || !workspace) return TQ_ERR_INVALID_ARG;
+  if (static_cast<int64_t>(max_blocks) * g.block_size < seq_len) return TQ_ERR_INVALID_ARG;
+  if (!aligned(workspace, 256)) return TQ_ERR_ALIGNMENT;
+  if (!aligned(block_table_row, 4)) return TQ_ERR_ALIGNMENT;
+  const ContinuationSpace c = continuation_space(g, q_len, num_q_heads, seq_len, max_blocks);
+  if (workspace_bytes < c.total) return TQ_ERR_WORKSPACE;
+  tq_status ds = check_device(ctx);
+  if (ds != TQ_OK) return ds;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  int32_t* lens = reinterpret_cast<int32_t*>(ws + c.lens_off);
+  int32_t* table = reinterpret_cast<int32_t*>(ws + c.table_off);
+  hipError_t e = tq::launch_expand_rows(block_table_row, max_blocks, seq_len - q_len, q_len, lens, table,
+                                        static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return TQ_ERR_HIP;
+  return tq_decode(ctx, q, cache, num_blocks, table, max_blocks, lens, q_len, num_q_heads, seq_len, sm_scale,
+                   out, out_is_fp32, c.decode > 0 ? workspace : nullptr, c.decode, stream);
+}
+
 tq_status tq_get_device_error(const tq_ctx* ctx, int32_t* code_host, int clear) {
   if (!ctx || !code_host) return TQ_ERR_INVALID_ARG;
   if (hipDeviceSynchronize() != hipSuccess) return TQ_ERR_HIP;

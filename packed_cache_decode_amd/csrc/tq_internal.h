@@ -90,6 +90,12 @@ hipError_t launch_decode_mfma(const Geometry& g, const DevTables* tables, const 
 
 DecodePlan plan_decode(const Geometry& g, int batch, int num_q_heads, int max_seq_len);
 
+hipError_t launch_dequant(const Geometry& g, const DevTables* tables, const uint8_t* cache,
+                          int64_t num_blocks, const int32_t* block_table_row, int seq_len,
+                          void* k_out, void* v_out, int out_is_fp32, hipStream_t stream);
+hipError_t launch_expand_rows(const int32_t* row, int max_blocks, int cached_len, int q_len,
+                              int32_t* seq_lens, int32_t* table, hipStream_t stream);
+
 hipError_t launch_decode(const Geometry& g, const DevTables* tables, const DecodePlan& plan,
                          const uint16_t* q, const uint8_t* cache, int64_t num_blocks,
                          const int32_t* block_table, int max_blocks_per_seq,

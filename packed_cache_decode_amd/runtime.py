@@ -75,5 +75,29 @@ class PackedKVCache:
                        ws, ws.numel(), stream)
         return out
 
+    def dequant(self, cache, block_table_row, seq_len, out_fp32=False, stream=None):
+        """K, V [seq_len, H, d] of one sequence, back in the original space."""
+        dt = torch.float32 if out_fp32 else torch.bfloat16
+        k = torch.empty((seq_len, self.num_kv_heads, self.head_dim), dtype=dt, device=self.device)
+        v = torch.empty_like(k)
+        _lib.tq_dequant(self.ctx, cache, cache.shape[0], block_table_row, block_table_row.shape[0],
+                        seq_len, k, v, out_fp32, stream)
+        return k, v
+
+    def decode_continuation(self, q, cache, block_table_row, seq_len, out=None, out_fp32=False,
+                            sm_scale=0.0, stream=None):
+        """q: bf16 [q_len, Hq, d], the chunk's queries; their tokens are the
+        last q_len of the seq_len stored ones.  Causal attention per query."""
+        q_len, Hq, d = q.shape
+        if out is None:
+            out = torch.empty((q_len, Hq, d), dtype=torch.float32 if out_fp32 else torch.bfloat16,
+                              device=q.device)
+        mb = block_table_row.shape[0]
+        nbytes = _lib.tq_continuation_workspace_bytes(self.ctx, q_len, Hq, seq_len, mb)
+        ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=self.device)
+        _lib.tq_decode_continuation(self.ctx, q, cache, cache.shape[0], block_table_row, mb, seq_len, q_len,
+                                    Hq, sm_scale, out, out.dtype == torch.float32, ws, ws.numel(), stream)
+        return out
+
     def device_error(self, clear=True):
         return _lib.tq_get_device_error(self.ctx, clear)

@@ -26,6 +26,19 @@ Two solvers:
   levels held when the loop stops.  The page does not print its trapezoid
   helper; the composite rule with n = 200 equal panels is the reading taken.
 
+A third codebook, ``lloyd_max_beta``: the exact marginal of one coordinate of
+a uniformly random unit vector in R^d, the density of a rotated, normalised
+key coordinate when the rotation is uniformly random (P3, kwkr.cn news
+555717, section on the random orthogonal rotation: a scaled Beta law on
+[-1, 1] that is nearly N(0, 1/d) in high dimension).  Its density is
+  f(x) = C (1 - x^2)^a on [-1, 1],  a = (d - 3) / 2,
+  C = Gamma(d/2) / (sqrt(pi) Gamma((d - 1)/2)).
+The cell mass comes from the regularised incomplete Beta function,
+P(|X| < x) = I_{x^2}(1/2, a + 1), and the first moment has the closed form
+integral of x f(x) over (l, u) = C ((1 - l^2)^(a+1) - (1 - u^2)^(a+1)) / (2 (a + 1)).
+The same fixed point as ``lloyd_max_exact``, with the outer cells ending at
+-1 and +1.
+
 Midpoints are formed from the sorted float32 levels in float32, as the page's
 device set-up does (P1, section "vLLM 内置的 Lloyd-Max 码本"):
 m_i = (c_i + c_{i+1}) / 2.
@@ -126,6 +139,71 @@ def lloyd_max_page_trapz(d, bits, max_iter=200, tol=1e-10):
     return np.array(c, dtype=np.float64), it, converged
 
 
+def _beta_cdf(x, a):
+    """P(X <= x) for the sphere marginal with exponent a (x in [-1, 1])."""
+    from scipy.special import betainc
+    if x <= -1.0:
+        return 0.0
+    if x >= 1.0:
+        return 1.0
+    half = 0.5 * betainc(0.5, a + 1.0, x * x)
+    return 0.5 + half if x >= 0 else 0.5 - half
+
+
+def _beta_mass(l, u, a):
+    """P(l < X < u), from the tail nearer the cell for full relative precision."""
+    from scipy.special import betainc
+    if l >= 0.0:
+        return 0.5 * (betainc(0.5, a + 1.0, u * u) - betainc(0.5, a + 1.0, l * l))
+    if u <= 0.0:
+        return 0.5 * (betainc(0.5, a + 1.0, l * l) - betainc(0.5, a + 1.0, u * u))
+    return _beta_cdf(u, a) - _beta_cdf(l, a)
+
+
+def beta_cell_mean(l, u, d):
+    """E[X | l < X < u] for the sphere marginal in dimension d."""
+    a = (d - 3) / 2.0
+    logC = math.lgamma(d / 2.0) - 0.5 * math.log(math.pi) - math.lgamma((d - 1) / 2.0)
+    m1 = math.exp(logC) * ((1.0 - l * l) ** (a + 1.0) - (1.0 - u * u) ** (a + 1.0)) / (2.0 * (a + 1.0))
+    return m1 / _beta_mass(l, u, a)
+
+
+def lloyd_max_beta(d, bits, tol=EXACT_TOL, max_iter=EXACT_MAX_ITER):
+    """Fixed point of the Lloyd-Max conditions for the sphere marginal in
+    dimension d (d >= 3), float64.  Returns (levels_f64 (symmetrised), iterations)."""
+    n = 2 ** bits
+    # the page's even spread over +-3.5 sigma, or over the support (-1, 1)
+    # when that is narrower (small d)
+    c = _initial_levels(n, min(math.sqrt(1.0 / d), 1.0 / 3.5))
+    for it in range(1, max_iter + 1):
+        edges = [-1.0] + [(c[i] + c[i + 1]) / 2.0 for i in range(n - 1)] + [1.0]
+        new = [beta_cell_mean(edges[i], edges[i + 1], d) for i in range(n)]
+        delta = max(abs(new[i] - c[i]) for i in range(n))
+        c = new
+        if delta < tol:
+            break
+    else:
+        raise RuntimeError("Lloyd-Max fixed point did not converge")
+    pos = c[n // 2:]
+    levels = [-v for v in reversed(pos)] + list(pos)
+    return np.array(levels, dtype=np.float64), it
+
+
+def beta_mse_per_coord(levels, d):
+    """Mean squared error per coordinate of a quantiser with the given sorted
+    levels (midpoint boundaries) under the sphere marginal, by quadrature."""
+    from scipy.integrate import quad
+    a = (d - 3) / 2.0
+    C = math.exp(math.lgamma(d / 2.0) - 0.5 * math.log(math.pi) - math.lgamma((d - 1) / 2.0))
+    lv = list(levels)
+    edges = [-1.0] + [(lv[i] + lv[i + 1]) / 2.0 for i in range(len(lv) - 1)] + [1.0]
+    tot = 0.0
+    for i, c in enumerate(lv):
+        tot += quad(lambda x: (x - c) ** 2 * C * (1.0 - x * x) ** a, edges[i], edges[i + 1],
+                    epsabs=1e-16, epsrel=1e-12, limit=200)[0]
+    return tot
+
+
 def midpoints_f32(levels_f32):
     """Decision boundaries from sorted float32 levels, in float32."""
     c = np.sort(np.asarray(levels_f32, dtype=np.float32))
@@ -138,6 +216,8 @@ def codebook(d, bits, mode="exact"):
         levels, _ = lloyd_max_exact(d, bits)
     elif mode == "page_trapz":
         levels, _, _ = lloyd_max_page_trapz(d, bits)
+    elif mode == "beta":
+        levels, _ = lloyd_max_beta(d, bits)
     else:
         raise ValueError(mode)
     c32 = levels.astype(np.float32)

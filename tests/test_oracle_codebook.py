@@ -97,3 +97,62 @@ def test_page_recipe_reading():
     for bits, lt in ((3, l3), (4, l4)):
         le, _ = cb.lloyd_max_exact(128, bits)
         assert np.max(np.abs(lt - le) / np.abs(le)) < 1e-3
+
+
+# ---------------------------------------------------------------------------
+# exact sphere-marginal (Beta) codebook
+# ---------------------------------------------------------------------------
+
+
+def test_beta_codebook_matches_printed_d128_b3():
+    g = load_golden("codebook_beta_d128_b3_page.json")
+    lv, _ = cb.lloyd_max_beta(g["head_dim"], g["bits"])
+    assert np.max(np.abs(lv - np.array(g["centroids"]))) <= 0.5 * 10.0 ** -g["printed_decimals"] + 1e-12
+    mse = cb.beta_mse_per_coord(lv, g["head_dim"])
+    assert abs(mse - g["mse_per_coord"]) <= 0.005e-4
+    assert abs(mse * g["head_dim"] - g["mse_total"]) <= 0.005e-2
+
+
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
+def test_beta_codebook_d3_is_the_uniform_quantiser(bits):
+    # d = 3: the marginal of a uniform point on the sphere S^2 is uniform on
+    # [-1, 1] (Archimedes), whose Lloyd-Max quantiser is the uniform one
+    lv, _ = cb.lloyd_max_beta(3, bits)
+    n = 2 ** bits
+    want = -1.0 + (2 * np.arange(n) + 1) / n
+    assert np.max(np.abs(lv - want)) < 1e-12
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("bits", [3, 4])
+def test_beta_codebook_fixed_point(d, bits):
+    lv, _ = cb.lloyd_max_beta(d, bits)
+    assert np.array_equal(lv, -lv[::-1])
+    edges = [-1.0] + list((lv[:-1] + lv[1:]) / 2) + [1.0]
+    # each level is its cell's mean, by an independent quadrature of the density
+    from scipy.integrate import quad
+    a = (d - 3) / 2.0
+    for i, c in enumerate(lv):
+        m0 = quad(lambda x: (1 - x * x) ** a, edges[i], edges[i + 1], epsabs=0, epsrel=1e-13, limit=200)[0]
+        m1 = quad(lambda x: x * (1 - x * x) ** a, edges[i], edges[i + 1], epsabs=0, epsrel=1e-13, limit=200)[0]
+        assert abs(m1 / m0 - c) < 1e-11 * max(1.0, abs(c)) + 1e-13
+
+
+def test_beta_codebook_tends_to_gaussian():
+    # the marginal tends to N(0, 1/d); the levels' relative gap shrinks like 1/d
+    gaps = []
+    for d in (128, 1024, 8192):
+        g, _ = cb.lloyd_max_exact(d, 3)
+        b, _ = cb.lloyd_max_beta(d, 3)
+        gaps.append(np.max(np.abs(g - b) / np.abs(g)))
+    assert gaps[0] > gaps[1] > gaps[2]
+    assert gaps[2] < 2e-4
+    assert 4 < gaps[0] / gaps[1] < 16
+
+
+def test_beta_codebook_lower_mse_than_gaussian_on_sphere():
+    # the codebook made for the true marginal distorts less under it
+    for bits in (3, 4):
+        g, _ = cb.lloyd_max_exact(128, bits)
+        b, _ = cb.lloyd_max_beta(128, bits)
+        assert cb.beta_mse_per_coord(b, 128) < cb.beta_mse_per_coord(g, 128)

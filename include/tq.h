@@ -11,6 +11,8 @@
  * Sources, cited by page title and section:
  *   P1  "vLLM 源码完全拆解(十九):TurboQuant KV Cache 量化——Hadamard 旋转、
  *       Lloyd-Max 标量量化与分页缓存内核" (pinghaoyang.com.cn)
+ *   P3  kwkr.cn news 555717, an article on the turboquant project (the
+ *       Beta law of a rotated coordinate and its pre-computed codebooks)
  *   P5  "NVIDIA KV Cache 量化中的 NVFP4 与 TurboQuant" (moonnryan.github.io)
  *
  * Conventions for every call:
@@ -64,8 +66,14 @@ typedef enum {
 typedef enum {
   TQ_CODEBOOK_LLOYD_MAX_EXACT = 0,  /* fixed point with closed-form Gaussian
                                        conditional means, float64, then float32 */
-  TQ_CODEBOOK_PAGE_TRAPZ = 1        /* the page's 200-trapezoid recipe, 200
+  TQ_CODEBOOK_PAGE_TRAPZ = 1,       /* the page's 200-trapezoid recipe, 200
                                        iterations at most, tolerance 1e-10    */
+  TQ_CODEBOOK_BETA_EXACT = 2        /* fixed point for the exact marginal of a
+                                       coordinate of a uniformly random unit
+                                       vector, density ~ (1 - x^2)^((d-3)/2) on
+                                       [-1, 1] (P3, kwkr.cn news 555717, on the
+                                       rotated coordinate's Beta law), float64
+                                       quadrature, then float32 */
 } tq_codebook_mode;
 
 /* Byte layout of a cache page (P1, section "AoS 与 SoA:两种页内布局").

@@ -18,7 +18,7 @@ TQ_OK = 0
 STATUS = {0: "TQ_OK", -1: "TQ_ERR_INVALID_ARG", -2: "TQ_ERR_UNSUPPORTED", -3: "TQ_ERR_ALIGNMENT",
           -4: "TQ_ERR_WORKSPACE", -5: "TQ_ERR_HIP", -6: "TQ_ERR_NO_DEVICE"}
 PRESETS = {"turboquant_k8v4": 0, "turboquant_4bit_nc": 1, "turboquant_k3v4_nc": 2, "turboquant_3bit_nc": 3}
-CODEBOOK_MODES = {"exact": 0, "page_trapz": 1}
+CODEBOOK_MODES = {"exact": 0, "page_trapz": 1, "beta": 2}
 LAYOUTS = {"aos": 0, "soa": 1}
 
 # every symbol include/tq.h declares

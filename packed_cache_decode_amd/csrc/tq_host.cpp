@@ -131,6 +131,85 @@ void solve_page_trapz(int d, int bits, std::vector<double>& c) {
   }
 }
 
+// ---- Lloyd-Max for the exact sphere marginal --------------------------------
+// One coordinate of a uniformly random unit vector in R^d has density
+// proportional to (1 - x^2)^((d-3)/2) on [-1, 1] (a scaled Beta law).  Cell
+// masses and first moments by composite Gauss-Legendre quadrature (32 nodes
+// on each of 32 equal panels of the cell); the same fixed point as
+// solve_exact with the outer cells ending at -1 and +1.
+
+// nodes and weights of the n-point Gauss-Legendre rule on [-1, 1], by Newton's
+// method on the Legendre polynomial P_n (three-term recurrence)
+void gauss_legendre(int n, std::vector<double>& x, std::vector<double>& w) {
+  x.assign(n, 0.0);
+  w.assign(n, 0.0);
+  for (int i = 0; i < (n + 1) / 2; ++i) {
+    double z = std::cos(M_PI * (i + 0.75) / (n + 0.5));
+    double dp = 0.0;
+    for (int it = 0; it < 100; ++it) {
+      double p0 = 1.0, p1 = z;
+      for (int k = 2; k <= n; ++k) {
+        const double p2 = ((2.0 * k - 1.0) * z * p1 - (k - 1.0) * p0) / k;
+        p0 = p1;
+        p1 = p2;
+      }
+      dp = n * (z * p1 - p0) / (z * z - 1.0);
+      const double dz = p1 / dp;
+      z -= dz;
+      if (std::fabs(dz) < 1e-16) break;
+    }
+    x[i] = -z;
+    x[n - 1 - i] = z;
+    w[i] = w[n - 1 - i] = 2.0 / ((1.0 - z * z) * dp * dp);
+  }
+}
+
+bool solve_beta(int d, int bits, std::vector<double>& out) {
+  const int n = 1 << bits;
+  const double a = (d - 3) / 2.0;
+  std::vector<double> gx, gw;
+  gauss_legendre(32, gx, gw);
+  auto moments = [&](double l, double u, double& m0, double& m1) {
+    const int panels = 32;
+    const double h = (u - l) / panels;
+    m0 = m1 = 0.0;
+    for (int p = 0; p < panels; ++p) {
+      const double mid = l + (p + 0.5) * h;
+      for (size_t k = 0; k < gx.size(); ++k) {
+        const double x = mid + 0.5 * h * gx[k];
+        const double f = std::pow(std::fmax(1.0 - x * x, 0.0), a) * gw[k] * 0.5 * h;
+        m0 += f;
+        m1 += x * f;
+      }
+    }
+  };
+  const double spread = std::fmin(3.5 * std::sqrt(1.0 / d), 1.0);
+  std::vector<double> c(n), nc(n), edges(n + 1);
+  for (int i = 0; i < n; ++i) c[i] = -spread + 2.0 * spread * (i + 0.5) / n;
+  bool converged = false;
+  for (int it = 0; it < 100000 && !converged; ++it) {
+    edges[0] = -1.0;
+    edges[n] = 1.0;
+    for (int i = 0; i + 1 < n; ++i) edges[i + 1] = (c[i] + c[i + 1]) / 2.0;
+    double delta = 0.0;
+    for (int i = 0; i < n; ++i) {
+      double m0, m1;
+      moments(edges[i], edges[i + 1], m0, m1);
+      nc[i] = m1 / m0;
+      delta = std::fmax(delta, std::fabs(nc[i] - c[i]));
+    }
+    c.swap(nc);
+    converged = delta < 1e-14;
+  }
+  if (!converged) return false;
+  out.assign(n, 0.0);
+  for (int i = 0; i < n / 2; ++i) {
+    out[n / 2 + i] = c[n / 2 + i];
+    out[n / 2 - 1 - i] = -c[n / 2 + i];
+  }
+  return true;
+}
+
 // SplitMix64 (Steele, Lea and Flood, OOPSLA 2014): sign j is the top bit of
 // the j-th output, 1 -> -1.
 void rotation_signs(uint64_t seed, int d, bool flip, int8_t* s) {
@@ -167,6 +246,8 @@ tq_status host_codebook(int d, int bits, int mode, float* cent, float* mid) {
     if (!solve_exact(d, bits, lv)) return TQ_ERR_UNSUPPORTED;
   } else if (mode == TQ_CODEBOOK_PAGE_TRAPZ) {
     solve_page_trapz(d, bits, lv);
+  } else if (mode == TQ_CODEBOOK_BETA_EXACT) {
+    if (!solve_beta(d, bits, lv)) return TQ_ERR_UNSUPPORTED;
   } else {
     return TQ_ERR_INVALID_ARG;
   }
@@ -341,7 +422,8 @@ tq_status tq_codebook_init_layout(tq_ctx** out, int preset, int head_dim, int nu
   if (preset < TQ_K8V4 || preset > TQ_3BIT_NC) return TQ_ERR_INVALID_ARG;
   if (layout != TQ_LAYOUT_AOS && layout != TQ_LAYOUT_SOA) return TQ_ERR_INVALID_ARG;
   if (layout == TQ_LAYOUT_SOA && preset == TQ_K8V4) return TQ_ERR_UNSUPPORTED;
-  if (codebook_mode != TQ_CODEBOOK_LLOYD_MAX_EXACT && codebook_mode != TQ_CODEBOOK_PAGE_TRAPZ)
+  if (codebook_mode != TQ_CODEBOOK_LLOYD_MAX_EXACT && codebook_mode != TQ_CODEBOOK_PAGE_TRAPZ &&
+      codebook_mode != TQ_CODEBOOK_BETA_EXACT)
     return TQ_ERR_INVALID_ARG;
   if (num_kv_heads < 1 || num_kv_heads > 64) return TQ_ERR_INVALID_ARG;
   if (head_dim != 64 && head_dim != 128 && head_dim != 256) return TQ_ERR_UNSUPPORTED;

@@ -44,6 +44,17 @@ def test_host_codebook_bit_identical_to_oracle(lib, d, bits):
     assert np.array_equal(m.view(np.uint32), om.view(np.uint32))
 
 
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_host_beta_codebook_bit_identical_to_oracle(lib, d, bits):
+    # the host solves with Gauss-Legendre quadrature, the oracle with the
+    # incomplete Beta function and a closed-form first moment
+    c, m = _lib.tq_host_codebook(d, bits, "beta")
+    oc, om = cb.codebook(d, bits, "beta")
+    assert np.array_equal(c.view(np.uint32), oc.view(np.uint32))
+    assert np.array_equal(m.view(np.uint32), om.view(np.uint32))
+
+
 @pytest.mark.parametrize("bits", [3, 4])
 def test_host_page_trapz_codebook_bit_identical_to_oracle(lib, bits):
     c, m = _lib.tq_host_codebook(128, bits, "page_trapz")

@@ -21,18 +21,18 @@ torch = pytest.importorskip("torch")
 
 
 def _decode_from_oracle_cache(w, seed=11, sign_flip=True, lens=None, sm_scale=None, zero_q=False,
-                              out_fp32=True):
+                              out_fp32=True, mode="exact"):
     from packed_cache_decode_amd.runtime import PackedKVCache
     inp = synth.generate(w)
     if lens is not None:
         inp.seq_lens = np.minimum(np.asarray(lens, np.int32), inp.seq_lens)
     if zero_q:
         inp.q = np.zeros_like(inp.q)
-    ors = OracleSide(w.preset, w.head_dim, seed, sign_flip)
+    ors = OracleSide(w.preset, w.head_dim, seed, sign_flip, mode)
     cache = np.zeros((inp.num_blocks, w.block_size, w.num_kv_heads, ors.lay.slot_size_aligned), np.uint8)
     ors.store(cache, inp.k, inp.v, inp.slot_mapping)
     want = ors.decode(inp.q, cache, inp.block_table, inp.seq_lens, w.num_kv_heads, sm_scale)
-    tq = PackedKVCache(w.preset, w.head_dim, w.num_kv_heads, w.block_size, seed, sign_flip)
+    tq = PackedKVCache(w.preset, w.head_dim, w.num_kv_heads, w.block_size, seed, sign_flip, mode)
     max_len = int(max(1, inp.seq_lens.max()))
     out = tq.decode(to_dev(inp.q), to_dev(cache), to_dev(inp.block_table), to_dev(inp.seq_lens),
                     max_len, out_fp32=out_fp32, sm_scale=sm_scale or 0.0)
@@ -139,6 +139,12 @@ def test_decode_ragged_and_tiny_lengths(preset):
 @pytest.mark.parametrize("bs,d", [(32, 128), (128, 128), (16, 64), (16, 256)])
 def test_decode_block_sizes_and_head_dims(bs, d, preset):
     got, want = _decode_from_oracle_cache(_wl(preset, G=4, d=d, bs=bs, seed=bs + d))
+    check_decode(got, want, bf16_out=False)
+
+
+@pytest.mark.parametrize("preset", ["turboquant_4bit_nc", "turboquant_k3v4_nc", "turboquant_3bit_nc"])
+def test_decode_beta_codebook(preset):
+    got, want = _decode_from_oracle_cache(_wl(preset, G=4, seed=31), mode="beta")
     check_decode(got, want, bf16_out=False)
 
 

@@ -81,7 +81,7 @@ def test_store_block_sizes_and_head_dims(preset, bs, d):
 @pytest.mark.parametrize("preset", ["turboquant_4bit_nc", "turboquant_k3v4_nc", "turboquant_3bit_nc"])
 def test_store_pure_hadamard_and_page_codebook(preset):
     w = _small(preset, seed=9)
-    for flip, mode in ((False, "exact"), (True, "page_trapz")):
+    for flip, mode in ((False, "exact"), (True, "page_trapz"), (True, "beta")):
         inp, got, want, ors, err = _run_store(w, seed=123, sign_flip=flip, mode=mode)
         assert _assert_parity(inp, got, want, ors)["rows_differing"] == 0
 

@@ -31,6 +31,7 @@ Modules:
   store     -- the store (quantise + pack + scatter), contract and float64
   decode    -- dequantise-then-softmax paged decode attention, float64
   soa       -- the structure-of-arrays page layout with the folded norm
+  haar      -- the Haar (random orthogonal) rotation, alternative to Hadamard
 """
 
-from . import fpfmt, rotation, codebook, layout, store, decode, soa  # noqa: F401,E402
+from . import fpfmt, rotation, codebook, layout, store, decode, soa, haar  # noqa: F401,E402

@@ -59,7 +59,10 @@ def rotation_signs(seed, d, sign_flip=True):
 
 
 def rotation_matrix_f64(signs):
-    """Explicit R = H diag(s) / sqrt(d) in float64."""
+    """Explicit R = H diag(s) / sqrt(d) in float64; a d x d matrix passed in
+    place of the signs (the Haar rotation's Q32) is returned as float64."""
+    if np.ndim(signs) == 2:
+        return np.asarray(signs, dtype=np.float64)
     d = len(signs)
     H = sylvester_hadamard(d).astype(np.float64)
     return H * np.asarray(signs, dtype=np.float64)[None, :] / np.sqrt(d)

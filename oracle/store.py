@@ -87,11 +87,20 @@ def unpack_codes(packed, bits, d):
 
 
 def quantize_k_contract(k_bits, signs, midpoints):
-    """MSE-K steps 1-8 for bf16 K vectors [..., d].  Returns (codes, nrm, y)."""
+    """MSE-K steps 1-8 for bf16 K vectors [..., d].  Returns (codes, nrm, y).
+
+    ``signs``: the d rotation signs (seeded-sign Hadamard), or a d x d float32
+    matrix Q32 for the Haar rotation (``oracle/haar.py``): then steps 4-7 are
+    y = rotate_contract(x, Q32) * (1 / (nrm + 1e-8))."""
     x = fpfmt.bf16_bits_to_f32(k_bits)
     d = x.shape[-1]
     ss = pairwise_sum_f32(x * x)
     nrm = np.sqrt(ss).astype(F32)
+    if np.ndim(signs) == 2:
+        from .haar import rotate_contract
+        inv = (F32(1.0) / (nrm + F32(1e-8))).astype(F32)
+        y = (rotate_contract(x, signs) * inv[..., None]).astype(F32)
+        return bucketize(y, midpoints), nrm, y
     alpha = ((F32(1.0) / (nrm + F32(1e-8))).astype(F32) * r_d(d)).astype(F32)
     u = (x * np.asarray(signs, dtype=F32)).astype(F32)
     u = fwht_f32_contract(u)
@@ -167,7 +176,8 @@ def store_contract(cache, k_bits, v_bits, slot_mapping, layout, signs, midpoints
 
 
 def rotate_unit_f64(k_bits, signs):
-    """y64 = R k / (|k| + 1e-8) in float64 via the explicit rotation matrix."""
+    """y64 = R k / (|k| + 1e-8) in float64 via the explicit rotation matrix
+    (``signs`` as in quantize_k_contract)."""
     x = fpfmt.bf16_bits_to_f64(k_bits)
     nrm = np.sqrt((x * x).sum(axis=-1))
     R = rotation_matrix_f64(signs)

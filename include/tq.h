@@ -91,6 +91,22 @@ typedef enum {
   TQ_LAYOUT_SOA = 1
 } tq_layout;
 
+/* Values of the `sign_flip` argument of the init calls, i.e. the K rotation.
+ * The Haar matrix is Q diag(sign(diag R)) from the Householder QR of a d x d
+ * Gaussian matrix drawn from rot_seed (SplitMix64 uniforms, Box-Muller pairs,
+ * row by row), rounded to float32: a uniformly random rotation (P3, kwkr.cn
+ * news 555717, on the random orthogonal rotation; P1, section "为什么 vLLM
+ * 选了 Hadamard 而不是随机正交矩阵").  With it the store computes
+ * y = Q k / (|k| + 1e-8) (products summed in a fixed pairwise tree), the
+ * decode q_rot = Q q, the dequantisation k = n Q^T c, and the decode runs on
+ * the general kernel.  FP8 keys are never rotated. */
+typedef enum {
+  TQ_ROTATION_HADAMARD = 0,          /* pure Sylvester Hadamard                  */
+  TQ_ROTATION_SIGNED_HADAMARD = 1,   /* seeded sign flips, then Hadamard (any other
+                                        nonzero value means the same)           */
+  TQ_ROTATION_HAAR = 2
+} tq_rotation;
+
 typedef struct tq_ctx tq_ctx;   /* opaque; immutable after tq_codebook_init */
 
 /* Solve the Lloyd-Max codebook for a rotated coordinate ~ N(0, 1/head_dim)
@@ -107,8 +123,9 @@ typedef struct tq_ctx tq_ctx;   /* opaque; immutable after tq_codebook_init */
  *   num_kv_heads  1..64 kv heads per token in the cache
  *   block_size    tokens per page: 16, 32, 64 or 128 (P1, section
  *                 "为什么 block_size 只有 16/32/64/128")
- *   rot_seed      seed of the sign flips
- *   sign_flip     nonzero: seeded signs; 0: pure Hadamard
+ *   rot_seed      seed of the sign flips (or of the Haar matrix)
+ *   sign_flip     tq_rotation: 0 pure Hadamard, 2 Haar, other nonzero values
+ *                 seeded signs
  *   codebook_mode tq_codebook_mode
  *   stream        stream for the table upload (the call synchronises it)
  * Allocates device memory (once per context); released by tq_destroy. */
@@ -282,6 +299,10 @@ tq_status tq_get_device_error(const tq_ctx* ctx, int32_t* code_host, int clear);
  * and the 2^bits - 1 midpoints of neighbouring levels.  bits 1..4. */
 tq_status tq_host_codebook(int head_dim, int bits, int codebook_mode, float* centroids_host,
                            float* midpoints_host);
+
+/* The head_dim x head_dim float32 Haar matrix (row-major) that
+ * tq_codebook_init draws for TQ_ROTATION_HAAR from rot_seed. */
+tq_status tq_host_haar_matrix(uint64_t rot_seed, int head_dim, float* q_host);
 
 /* The head_dim rotation signs (+1/-1) tq_codebook_init would draw. */
 tq_status tq_host_rotation_signs(uint64_t rot_seed, int head_dim, int sign_flip,

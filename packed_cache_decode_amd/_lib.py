@@ -25,7 +25,8 @@ LAYOUTS = {"aos": 0, "soa": 1}
 EXPORTS = ("tq_codebook_init", "tq_codebook_init_layout", "tq_layout_of", "tq_destroy", "tq_slot_bytes", "tq_cache_bytes", "tq_get_tables",
            "tq_store", "tq_decode_workspace_bytes", "tq_decode", "tq_dequant",
            "tq_continuation_workspace_bytes", "tq_decode_continuation", "tq_get_device_error",
-           "tq_host_codebook", "tq_host_rotation_signs", "tq_host_slot_bytes", "tq_status_str")
+           "tq_host_codebook", "tq_host_rotation_signs", "tq_host_haar_matrix", "tq_host_slot_bytes",
+           "tq_status_str")
 
 
 class TQError(RuntimeError):
@@ -72,6 +73,7 @@ def load():
         "tq_get_device_error": (_int, [_vp, ctypes.POINTER(_i32), _int]),
         "tq_host_codebook": (_int, [_int, _int, _int, _vp, _vp]),
         "tq_host_rotation_signs": (_int, [ctypes.c_uint64, _int, _int, _vp]),
+        "tq_host_haar_matrix": (_int, [ctypes.c_uint64, _int, _vp]),
         "tq_host_slot_bytes": (_i64, [_int, _int]),
         "tq_status_str": (ctypes.c_char_p, [_int]),
     }
@@ -113,6 +115,16 @@ def _check(fn, st):
 # entry points (same names as the C ABI)
 # ---------------------------------------------------------------------------
 
+ROTATIONS = {"hadamard": 0, "signed_hadamard": 1, "haar": 2}
+
+
+def _rotation(sign_flip):
+    """sign_flip as the C ABI's tq_rotation: True/False, 0/1/2 or a name."""
+    if isinstance(sign_flip, str):
+        return ROTATIONS[sign_flip]
+    return int(sign_flip)
+
+
 def tq_codebook_init(preset, head_dim, num_kv_heads, block_size, rot_seed, sign_flip=1,
                      codebook_mode=0, stream=None):
     lib = load()
@@ -122,7 +134,7 @@ def tq_codebook_init(preset, head_dim, num_kv_heads, block_size, rot_seed, sign_
         codebook_mode = CODEBOOK_MODES[codebook_mode]
     h = _vp()
     _check("tq_codebook_init", lib.tq_codebook_init(ctypes.byref(h), preset, head_dim, num_kv_heads,
-                                                    block_size, rot_seed, int(sign_flip),
+                                                    block_size, rot_seed, _rotation(sign_flip),
                                                     codebook_mode, _stream(stream)))
     return h.value
 
@@ -139,7 +151,7 @@ def tq_codebook_init_layout(preset, head_dim, num_kv_heads, block_size, rot_seed
     h = _vp()
     _check("tq_codebook_init_layout",
            lib.tq_codebook_init_layout(ctypes.byref(h), preset, head_dim, num_kv_heads, block_size,
-                                       rot_seed, int(sign_flip), codebook_mode, layout,
+                                       rot_seed, _rotation(sign_flip), codebook_mode, layout,
                                        _stream(stream)))
     return h.value
 
@@ -226,6 +238,13 @@ def tq_host_rotation_signs(rot_seed, head_dim, sign_flip=1):
     _check("tq_host_rotation_signs", load().tq_host_rotation_signs(rot_seed, head_dim, int(sign_flip),
                                                                     s.ctypes.data))
     return s
+
+
+def tq_host_haar_matrix(rot_seed, head_dim):
+    import numpy as np
+    q = np.zeros((head_dim, head_dim), np.float32)
+    _check("tq_host_haar_matrix", load().tq_host_haar_matrix(rot_seed, head_dim, q.ctypes.data))
+    return q
 
 
 def tq_host_slot_bytes(preset, head_dim):

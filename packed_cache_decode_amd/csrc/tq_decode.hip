@@ -136,6 +136,33 @@ __global__ void __launch_bounds__(64) decode_split_kernel(DecodeArgs a) {
     sgn[e] = ((a.tables->sign_bits[j >> 5] >> (j & 31)) & 1u) << 31;
   }
   const float rsd = 1.0f / sqrtf(static_cast<float>(D));
+  if (!kFp8 && a.tables->rot != nullptr) {
+    // Haar rotation: q_rot = Q q, coordinates of every query through LDS
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      const uint16_t* qp = a.q + (static_cast<int64_t>(b) * Hq + g * G + j) * D + E * lane;
+#pragma unroll
+      for (int e = 0; e < E; ++e) s_q[j][E * lane + e] = bf16_bits_to_f32(qp[e]);
+    }
+    __syncthreads();
+    float r[G][E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const float* qrow = a.tables->rot + static_cast<int64_t>(E * lane + e) * D;
+#pragma unroll
+      for (int j = 0; j < G; ++j) r[j][e] = 0.0f;
+      for (int i = 0; i < D; ++i) {
+        const float qi = qrow[i];
+#pragma unroll
+        for (int j = 0; j < G; ++j) r[j][e] += qi * s_q[j][i];
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < G; ++j)
+#pragma unroll
+      for (int e = 0; e < E; ++e) s_q[j][E * lane + e] = r[j][e] * a.scale_log2;
+  } else
 #pragma unroll
   for (int j = 0; j < G; ++j) {
     const uint16_t* qp = a.q + (static_cast<int64_t>(b) * Hq + g * G + j) * D + E * lane;
@@ -395,6 +422,17 @@ hipError_t launch_g(const DecodeArgs& a, int G, int batch, hipStream_t stream) {
 
 DecodePlan plan_decode(const Geometry& g, int batch, int num_q_heads, int max_seq_len) {
   DecodePlan p{};
+  if (g.haar) {
+    // the matrix-core kernels rotate q with butterflies; the Haar rotation's
+    // dense product runs in the general kernel
+    p.mfma = 0;
+    p.chunk = 256;
+    p.num_splits = max_seq_len > 0 ? (max_seq_len + p.chunk - 1) / p.chunk : 1;
+    p.workspace_bytes = static_cast<size_t>(batch) * num_q_heads * p.num_splits *
+                        (g.head_dim + 2) * sizeof(float);
+    p.workspace_bytes = (p.workspace_bytes + 255) & ~static_cast<size_t>(255);
+    return p;
+  }
   // Matrix-core kernel by key type (measured on the llama3-, long-context,
   // k3v4- and k8v4-shaped decodes): FP8 keys take the page-cooperative
   // kernel; 3/4-bit keys with at most 8 query heads per kv head the ring

@@ -83,8 +83,10 @@ __global__ void __launch_bounds__(64 * kWaves) dequant_kernel(DequantArgs a) {
   constexpr int kDataBytes = kKeyCodeBytes + kValCodeBytes;   // split page
 
   __shared__ float s_cent[16];
+  __shared__ float s_c[kWaves][D];            // Haar rotation: the centroid vector
   if (threadIdx.x < 16) s_cent[threadIdx.x] = a.tables->centroids[threadIdx.x];
   __syncthreads();
+  const float* rot = a.tables->rot;
 
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
@@ -154,6 +156,23 @@ __global__ void __launch_bounds__(64 * kWaves) dequant_kernel(DequantArgs a) {
         for (int m = 1; m < 64; m *= 2) ss += __shfl_xor(ss, m, 64);
         n = n_raw / sqrtf(ss + 1e-16f);
       }
+      if (rot != nullptr) {
+        // Haar rotation: k_i = n * sum_j Q[j][i] c_j
+#pragma unroll
+        for (int e = 0; e < E; ++e) s_c[wave][E * lane + e] = k[e];
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          float acc = 0.0f;
+          for (int j = 0; j < D; ++j) acc += rot[static_cast<int64_t>(j) * D + E * lane + e] * s_c[wave][j];
+          k[e] = acc;
+        }
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+#pragma unroll
+        for (int e = 0; e < E; ++e) k[e] *= n;
+      } else {
       // R^T c = diag(s) H c / sqrt(d): butterflies, then signs and scale
 #pragma unroll
       for (int hs = 1; hs < E; hs *= 2)
@@ -176,6 +195,7 @@ __global__ void __launch_bounds__(64 * kWaves) dequant_kernel(DequantArgs a) {
       const float f = n * rsd;
 #pragma unroll
       for (int e = 0; e < E; ++e) k[e] = __uint_as_float(__float_as_uint(k[e] * f) ^ sgn[e]);
+      }
     }
     // ---------------- V ----------------
 #pragma unroll

@@ -33,6 +33,7 @@ struct tq_ctx {
   float r_d;                        // float32(1 / sqrt(head_dim))
   int device;
   DevTables* d_tables;
+  float* d_rot;                     // Haar rotation matrix (device), or null
 };
 
 namespace {
@@ -228,6 +229,70 @@ void rotation_signs(uint64_t seed, int d, bool flip, int8_t* s) {
   }
 }
 
+// ---- Haar rotation ------------------------------------------------------------
+// Gaussian entries from the SplitMix64 stream of rot_seed: uniforms
+// u = ((z >> 11) + 1/2) 2^-53, Box-Muller on consecutive pairs; G filled row by
+// row.  Householder QR of G, then Q diag(sign(diag R)) (Mezzadri 2007), which
+// is Haar distributed; rounded to float32.
+void haar_matrix(uint64_t seed, int d, std::vector<float>& q32) {
+  const int n = d * d;
+  std::vector<double> g(n + (n & 1));
+  uint64_t st = seed;
+  auto next = [&]() {
+    st += 0x9E3779B97F4A7C15ull;
+    uint64_t z = st;
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    z ^= z >> 31;
+    return (static_cast<double>(z >> 11) + 0.5) / 9007199254740992.0;
+  };
+  for (size_t m = 0; m < g.size(); m += 2) {
+    const double u1 = next(), u2 = next();
+    const double r = std::sqrt(-2.0 * std::log(u1));
+    g[m] = r * std::cos(2.0 * M_PI * u2);
+    g[m + 1] = r * std::sin(2.0 * M_PI * u2);
+  }
+  // A = G (row-major); Householder: for column k, v = x + sign(x0)|x| e0 on rows k..d-1
+  std::vector<double> A(g.begin(), g.begin() + n), V(n, 0.0), beta(d, 0.0), rdiag(d, 0.0);
+  for (int k = 0; k < d; ++k) {
+    double norm = 0.0;
+    for (int i = k; i < d; ++i) norm += A[i * d + k] * A[i * d + k];
+    norm = std::sqrt(norm);
+    const double x0 = A[k * d + k];
+    const double alpha = x0 >= 0.0 ? -norm : norm;        // R[k][k]
+    rdiag[k] = alpha;
+    double vnorm2 = 0.0;
+    for (int i = k; i < d; ++i) {
+      V[i * d + k] = A[i * d + k] - (i == k ? alpha : 0.0);
+      vnorm2 += V[i * d + k] * V[i * d + k];
+    }
+    beta[k] = vnorm2 > 0.0 ? 2.0 / vnorm2 : 0.0;
+    // apply H_k = I - beta v v^T to the remaining columns
+    for (int j = k; j < d; ++j) {
+      double dot = 0.0;
+      for (int i = k; i < d; ++i) dot += V[i * d + k] * A[i * d + j];
+      dot *= beta[k];
+      for (int i = k; i < d; ++i) A[i * d + j] -= dot * V[i * d + k];
+    }
+  }
+  // Q = H_0 H_1 ... H_{d-1} applied to the identity, from the last reflector
+  std::vector<double> Q(n, 0.0);
+  for (int i = 0; i < d; ++i) Q[i * d + i] = 1.0;
+  for (int k = d - 1; k >= 0; --k)
+    for (int j = 0; j < d; ++j) {
+      double dot = 0.0;
+      for (int i = k; i < d; ++i) dot += V[i * d + k] * Q[i * d + j];
+      dot *= beta[k];
+      for (int i = k; i < d; ++i) Q[i * d + j] -= dot * V[i * d + k];
+    }
+  q32.assign(n, 0.0f);
+  for (int i = 0; i < d; ++i)
+    for (int j = 0; j < d; ++j) {
+      const double sgn = rdiag[j] < 0.0 ? -1.0 : 1.0;      // sign of R[j][j]
+      q32[i * d + j] = static_cast<float>(Q[i * d + j] * sgn);
+    }
+}
+
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 tq_status check_device(const tq_ctx* ctx) {
@@ -386,6 +451,15 @@ tq_status tq_host_rotation_signs(uint64_t rot_seed, int head_dim, int sign_flip,
   return TQ_OK;
 }
 
+tq_status tq_host_haar_matrix(uint64_t rot_seed, int head_dim, float* q_host) {
+  if (!q_host) return TQ_ERR_INVALID_ARG;
+  if (head_dim != 64 && head_dim != 128 && head_dim != 256) return TQ_ERR_UNSUPPORTED;
+  std::vector<float> q32;
+  haar_matrix(rot_seed, head_dim, q32);
+  std::memcpy(q_host, q32.data(), q32.size() * sizeof(float));
+  return TQ_OK;
+}
+
 int64_t tq_host_slot_bytes(int preset, int head_dim) {
   if (preset < TQ_K8V4 || preset > TQ_3BIT_NC) return -1;
   if (head_dim != 64 && head_dim != 128 && head_dim != 256) return -1;
@@ -464,7 +538,11 @@ tq_status tq_codebook_init_layout(tq_ctx** out, int preset, int head_dim, int nu
     }
     c->levels = 1 << g.key_bits;
   }
-  rotation_signs(rot_seed, head_dim, sign_flip != 0, c->signs);
+  // sign_flip: 0 pure Hadamard, TQ_ROTATION_HAAR the Haar matrix, other
+  // nonzero values the seeded-sign Hadamard
+  g.haar = sign_flip == TQ_ROTATION_HAAR && g.key_bits != 8 ? 1 : 0;
+  rotation_signs(rot_seed, head_dim, sign_flip != 0 && !g.haar, c->signs);
+  c->d_rot = nullptr;
 
   DevTables host{};
   std::memcpy(host.centroids, c->centroids, sizeof(host.centroids));
@@ -485,7 +563,23 @@ tq_status tq_codebook_init_layout(tq_ctx** out, int preset, int head_dim, int nu
     return TQ_ERR_NO_DEVICE;
   }
   hipStream_t st = static_cast<hipStream_t>(stream);
+  if (g.haar) {
+    std::vector<float> q32;
+    haar_matrix(rot_seed, head_dim, q32);
+    const size_t bytes = q32.size() * sizeof(float);
+    if (hipMalloc(&c->d_rot, bytes) != hipSuccess) {
+      delete c;
+      return TQ_ERR_HIP;
+    }
+    if (hipMemcpy(c->d_rot, q32.data(), bytes, hipMemcpyHostToDevice) != hipSuccess) {
+      (void)hipFree(c->d_rot);
+      delete c;
+      return TQ_ERR_HIP;
+    }
+    host.rot = c->d_rot;
+  }
   if (hipMalloc(&c->d_tables, sizeof(DevTables)) != hipSuccess) {
+    if (c->d_rot) (void)hipFree(c->d_rot);
     delete c;
     return TQ_ERR_HIP;
   }
@@ -493,6 +587,7 @@ tq_status tq_codebook_init_layout(tq_ctx** out, int preset, int head_dim, int nu
           hipSuccess ||
       hipStreamSynchronize(st) != hipSuccess) {
     (void)hipFree(c->d_tables);
+    if (c->d_rot) (void)hipFree(c->d_rot);
     delete c;
     return TQ_ERR_HIP;
   }
@@ -504,6 +599,7 @@ tq_status tq_destroy(tq_ctx* ctx) {
   if (!ctx) return TQ_OK;
   tq_status st = TQ_OK;
   if (ctx->d_tables && hipFree(ctx->d_tables) != hipSuccess) st = TQ_ERR_HIP;
+  if (ctx->d_rot && hipFree(ctx->d_rot) != hipSuccess) st = TQ_ERR_HIP;
   delete ctx;
   return st;
 }

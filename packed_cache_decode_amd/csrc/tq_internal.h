@@ -39,6 +39,7 @@ struct DevTables {
   float bin_bias;
   int32_t pad[2];
   uint32_t bins[kMaxBins][2];           // {float bits of thr, base}
+  const float* rot;                     // Haar rotation: Q (d x d, row-major, fp32); null otherwise
 };
 
 struct Geometry {
@@ -55,6 +56,8 @@ struct Geometry {
   int bins_ok;          // the bucketize bins of the device tables exist
   int soa;              // page layout: 0 = slots back to back, 1 = data region +
                         // meta region [H][3][block_size] fp16 (folded K norm)
+  int haar;             // MSE keys rotated by the Haar matrix DevTables::rot
+                        // instead of the (signed) Hadamard transform
 };
 
 // ---- launchers (defined in the .hip files) ---------------------------------

@@ -71,6 +71,34 @@ __device__ __forceinline__ uint32_t f32_to_e4m3fn(float x) {
   return sign | r;
 }
 
+// sum over i of q[i] * x[i] as the balanced tree in index order (products
+// and sums single fp32 operations): a stack of pending partial sums, where
+// element i closes the levels at which its index has a set bit
+template <int D>
+__device__ __forceinline__ float tree_dot(const float* q, const float* x) {
+  constexpr int L = __builtin_ctz(D);
+  float stk[L];
+  float total = 0.0f;
+#pragma unroll
+  for (int i = 0; i < D; ++i) {
+    float v = q[i] * x[i];
+    bool placed = false;
+#pragma unroll
+    for (int l = 0; l < L; ++l) {
+      if (!placed) {
+        if ((i >> l) & 1) {
+          v = stk[l] + v;
+        } else {
+          stk[l] = v;
+          placed = true;
+        }
+      }
+    }
+    if (!placed) total = v;
+  }
+  return total;
+}
+
 template <int D, int KB, int VB>
 __global__ void __launch_bounds__(64 * kWaves) store_kernel(StoreArgs a) {
   constexpr int E = D / 64;
@@ -86,6 +114,7 @@ __global__ void __launch_bounds__(64 * kWaves) store_kernel(StoreArgs a) {
   __shared__ uint8_t s_code[kWaves][D];
   __shared__ __align__(4) uint8_t s_slot[kWaves][kSlot + 2];
   __shared__ float s_csq[16];                  // split page: c_i * c_i per level
+  __shared__ float s_x[kWaves][D];             // Haar rotation: the vector, for every lane
 
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
@@ -145,10 +174,22 @@ __global__ void __launch_bounds__(64 * kWaves) store_kernel(StoreArgs a) {
 #pragma unroll
       for (int m = 1; m < 64; m *= 2) ss = ss + __shfl_xor(ss, m, 64);
       const float nrm = sqrtf(ss);
-      const float alpha = (1.0f / (nrm + 1e-8f)) * a.r_d;
+      float alpha = (1.0f / (nrm + 1e-8f)) * a.r_d;
 
-      // sign flips (exact), then butterflies h = 1, 2, ..., D/2
       float u[E];
+      if (a.tables->rot != nullptr) {
+        // Haar rotation: u_j = tree over i of Q[j][i] * x_i; y = u / (|x| + 1e-8)
+#pragma unroll
+        for (int e = 0; e < E; ++e) s_x[wave][E * lane + e] = x[e];
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+#pragma unroll
+        for (int e = 0; e < E; ++e) u[e] = tree_dot<D>(a.tables->rot + static_cast<int64_t>(E * lane + e) * D, s_x[wave]);
+        alpha = 1.0f / (nrm + 1e-8f);
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      } else {
+      // sign flips (exact), then butterflies h = 1, 2, ..., D/2
 #pragma unroll
       for (int e = 0; e < E; ++e) u[e] = __uint_as_float(__float_as_uint(x[e]) ^ sgn[e]);
 #pragma unroll
@@ -168,6 +209,7 @@ __global__ void __launch_bounds__(64 * kWaves) store_kernel(StoreArgs a) {
           const float o = __shfl_xor(u[e], lm, 64);
           u[e] = upper ? (o - u[e]) : (u[e] + o);
         }
+      }
       }
       // y = u * alpha, code = #{m : y >= mid_m}
       float cq[E];
@@ -788,10 +830,10 @@ hipError_t launch_store(const Geometry& g, const DevTables* tables, const uint16
   a.bs_shift = __builtin_ctz(static_cast<unsigned>(g.block_size));
   a.soa = g.soa;
   // head_dim 128 takes the four-lanes-per-vector kernel when the bucketize
-  // bins exist (always, for the Lloyd-Max codebooks) and the vector count fits
-  // 32-bit indexing
+  // bins exist (always, for the Lloyd-Max codebooks), the vector count fits
+  // 32-bit indexing and the rotation is the Hadamard one
   if (g.head_dim == 128 && num_tokens * g.num_kv_heads < (int64_t{1} << 31) &&
-      (g.key_bits == 8 || g.bins_ok)) {
+      (g.key_bits == 8 || g.bins_ok) && !g.haar) {
     if (g.key_bits == 8) return launch_store128<8, 4>(a, stream);
     if (g.key_bits == 4) return launch_store128<4, 4>(a, stream);
     if (g.value_bits == 4) return launch_store128<3, 4>(a, stream);

@@ -11,7 +11,7 @@ import numpy as np
 
 from oracle import codebook as cb
 from oracle import decode as odec
-from oracle import fpfmt, layout, rotation
+from oracle import fpfmt, haar, layout, rotation
 from oracle import store as ost
 
 CANARY = 0xA5
@@ -29,7 +29,11 @@ class OracleSide:
 
     def __init__(self, preset, head_dim, rot_seed, sign_flip=True, codebook_mode="exact"):
         self.lay = layout.slot_layout(preset, head_dim)
-        self.signs = rotation.rotation_signs(rot_seed, head_dim, sign_flip)
+        if sign_flip == "haar" and not self.lay.key_fp8:
+            # the rotation is the oracle's own Haar matrix, passed where the signs go
+            self.signs = haar.haar_matrix_f32(rot_seed, head_dim)
+        else:
+            self.signs = rotation.rotation_signs(rot_seed, head_dim, sign_flip not in (False, 0, "hadamard"))
         kb = 4 if self.lay.key_fp8 else self.lay.key_bits
         self.centroids, self.midpoints = cb.codebook(head_dim, kb, codebook_mode)
 

@@ -55,6 +55,18 @@ def test_host_beta_codebook_bit_identical_to_oracle(lib, d, bits):
     assert np.array_equal(m.view(np.uint32), om.view(np.uint32))
 
 
+@pytest.mark.parametrize("seed,d", [(0, 64), (7, 128), (2 ** 63 + 5, 256)])
+def test_host_haar_matrix_matches_oracle(lib, seed, d):
+    # the host's own Householder QR against the oracle's library QR of the same
+    # Gaussian matrix: equal after float32 rounding, up to rare last-bit cases
+    from oracle import haar
+    q = _lib.tq_host_haar_matrix(seed, d)
+    oq = haar.haar_matrix_f32(seed, d)
+    ulps = np.abs(q.view(np.int32).astype(np.int64) - oq.view(np.int32).astype(np.int64))
+    assert ulps.max() <= 1
+    assert (ulps > 0).mean() < 1e-3
+
+
 @pytest.mark.parametrize("bits", [3, 4])
 def test_host_page_trapz_codebook_bit_identical_to_oracle(lib, bits):
     c, m = _lib.tq_host_codebook(128, bits, "page_trapz")

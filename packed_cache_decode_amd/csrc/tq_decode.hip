@@ -422,6 +422,10 @@ hipError_t launch_g(const DecodeArgs& a, int G, int batch, hipStream_t stream) {
 
 DecodePlan plan_decode(const Geometry& g, int batch, int num_q_heads, int max_seq_len) {
   DecodePlan p{};
+  // TQ_DECODE_DETERMINISTIC=1: the ring kernel deals slabs out in a fixed
+  // order (results reproducible bit for bit; a few per cent slower)
+  const char* det = getenv("TQ_DECODE_DETERMINISTIC");
+  p.deterministic = det != nullptr && det[0] == '1';
   if (g.haar) {
     // the matrix-core kernels rotate q with butterflies; the Haar rotation's
     // dense product runs in the general kernel

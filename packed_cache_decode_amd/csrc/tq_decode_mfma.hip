@@ -85,6 +85,7 @@ struct MfmaArgs {
   float* part;         // [B][Hq][S][kRec]
   void* out;
   int out_fp32;
+  int dynamic;         // ring kernel: wavefronts claim slabs from a shared counter
 };
 
 __device__ __forceinline__ uint32_t pack_h2(_Float16 a, _Float16 b) {
@@ -1617,6 +1618,7 @@ __global__ void __launch_bounds__(64 * kRingWaves) decode_ring_kernel(MfmaArgs a
   static_assert(8 * kRec * 4 <= kRing, "a wavefront's partial records must fit its ring");
   __shared__ u32x2 s_tab[256];
   __shared__ int32_t s_pid[kRingMaxSlabs];
+  __shared__ int32_t s_next;                 // the workgroup's next unclaimed slab
   __shared__ __attribute__((aligned(16))) uint8_t s_ring[kRingWaves][kRing];
 
   const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
@@ -1640,20 +1642,20 @@ __global__ void __launch_bounds__(64 * kRingWaves) decode_ring_kernel(MfmaArgs a
   const int cap = a.chunk >> 4;              // slabs per workgroup split, at most
   const int s_b = n_slabs_b > 0 ? (n_slabs_b + cap - 1) / cap : 1;
   if (sg >= s_b) return;                     // the whole workgroup, before any barrier
-  const int cs = (n_slabs_b + kRingWaves * s_b - 1) / (kRingWaves * s_b);   // slabs per wavefront
-  const int wg0 = sg * kRingWaves * cs;      // the workgroup's first slab
+  const int cs = (n_slabs_b + kRingWaves * s_b - 1) / (kRingWaves * s_b);   // slabs per wavefront, on average
+  const int wg0 = sg * kRingWaves * cs;      // the workgroup's slabs [wg0, wg1)
   const int wg1 = min(n_slabs_b, wg0 + kRingWaves * cs);
-  const int j0 = min(wg1, wg0 + w * cs);     // this wavefront's slabs [j0, j1)
-  const int j1 = min(wg1, j0 + cs);
-  const int t0 = 16 * j0, t1 = min(T, 16 * j1);
+  const int n_wg = wg1 - wg0;
+  const int t_end = min(T, 16 * wg1);        // the workgroup's last token + 1
 
   build_tables_page<KB>(a, s_tab);
-  if (wg1 > wg0) stage_page_ids(a, b, 16 * wg0, min(T, 16 * wg1), s_pid);
+  if (n_wg > 0) stage_page_ids(a, b, 16 * wg0, t_end, s_pid);
+  if (threadIdx.x == 0) s_next = 0;
   __syncthreads();
 
-  h8 qc[4];
+  h8 qv[4];
   bf8v qb[4];
-  load_queries_packed(a, b, g, r16, g4, qc);
+  load_queries_packed(a, b, g, r16, g4, qv);
   RunState st;
 #pragma unroll
   for (int m = 0; m < 8; ++m) st.O[m] = f4{0.f, 0.f, 0.f, 0.f};
@@ -1667,7 +1669,6 @@ __global__ void __launch_bounds__(64 * kRingWaves) decode_ring_kernel(MfmaArgs a
   const int bs_mask = (1 << a.bs_shift) - 1;
   const int64_t row_bytes = static_cast<int64_t>(a.H) * SLOT;
   const int64_t page_bytes = static_cast<int64_t>(1 << a.bs_shift) * row_bytes;
-  const int n_slabs = j1 - j0;
   // Slotted page: the slab of one head is 16 rows row_bytes apart; the lane's
   // chunk of load l is chunk l*64 + lane of the aligned layout (past the
   // slab: an offset beyond every buffer range, which loads zeros into the
@@ -1710,10 +1711,28 @@ __global__ void __launch_bounds__(64 * kRingWaves) decode_ring_kernel(MfmaArgs a
   // wait in the loop counts slab loads only
   wait_vmcnt<0>();
 
-  auto issue = [&](int j) {
-    const int t = t0 + 16 * j;
+  // Slabs are claimed one at a time from the workgroup's counter (an LDS
+  // atomic), so wavefronts that run ahead take more of them and all finish
+  // within about one slab of each other (the wavefronts of a SIMD do not
+  // progress at one rate; with fixed shares the last one finished up to
+  // ~14 us after the median).  Which wavefront sums which slab then varies
+  // from run to run, and so do the last bits of the result; a.dynamic == 0
+  // deals the slabs out in a fixed order instead (wavefront w takes w,
+  // w + 16, w + 32, ...), which is reproducible bit for bit.  A claim past
+  // the workgroup's slabs still issues its loads, with an empty range (they
+  // load zeros), so the count of loads in flight stays fixed.
+  int n_claims = 0;
+  auto claim = [&]() {
+    if (!a.dynamic) return w + kRingWaves * n_claims++;
+    int v = 0;
+    if (lane == 0) v = atomicAdd(&s_next, 1);
+    return __builtin_amdgcn_readfirstlane(v);
+  };
+  // the loads of claimed slab cj (workgroup-relative) into ring buffer j % kBufs
+  auto issue = [&](int j, int cj) {
+    const int t = 16 * (wg0 + cj);
     int pid = -1;
-    if (t < t1) pid = s_pid[(t >> a.bs_shift) - p_first];
+    if (cj < n_wg) pid = s_pid[(t >> a.bs_shift) - p_first];
     pid = __builtin_amdgcn_readfirstlane(pid);
     const int64_t off = pid < 0 ? 0
                       : SOA ? pid * page_bytes
@@ -1738,32 +1757,39 @@ __global__ void __launch_bounds__(64 * kRingWaves) decode_ring_kernel(MfmaArgs a
       for (int l = 0; l < kLoads; ++l) lds_dma_16<false>(rs, dst + l * 1024, src_off[l]);
     }
   };
-  auto page_of = [&](int jj) { return s_pid[((t0 + 16 * jj) >> a.bs_shift) - p_first]; };
-
-  if (n_slabs > 0) {
+  if (n_wg > 0) {
+    int qc[kBufs - 1];                       // claims in flight, oldest first
 #pragma unroll
-    for (int j = 0; j < kBufs - 1; ++j) issue(j);
-    int j = 0;
+    for (int i = 0; i < kBufs - 1; ++i) {
+      qc[i] = claim();
+      issue(i, qc[i]);
+    }
+    int j = 0;                               // this wavefront's slab count (ring position)
     while (true) {
       float s[4];
       SlabSoftmax sm;
       SlabRegs<KB> c;
       bool grow = false;
-      for (; j < n_slabs; ++j) {
+      for (;; ++j) {
         // slab j has landed (the next kBufs - 2 may be in flight); this
         // wavefront's reads of slab j - 1 have completed, so its buffer takes
-        // slab j + kBufs - 1
+        // the next claim
         wait_vmcnt<kLoads * (kBufs - 2)>();
         __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-        issue(j + kBufs - 1);
-        if (__builtin_amdgcn_readfirstlane(page_of(j)) < 0) continue;
+        const int cur = qc[0];
+#pragma unroll
+        for (int i = 0; i + 1 < kBufs - 1; ++i) qc[i] = qc[i + 1];
+        qc[kBufs - 2] = claim();
+        issue(j + kBufs - 1, qc[kBufs - 2]);
+        if (cur >= n_wg) break;              // claims only grow: nothing left
+        if (__builtin_amdgcn_readfirstlane(s_pid[((16 * (wg0 + cur)) >> a.bs_shift) - p_first]) < 0) continue;
         if constexpr (SOA)
           slab_read_soa<KB, VB>(ring + (j % kBufs) * kBuf, r16, g4, c);
         else
           slab_read<KB, SLOT, 1>(ring + (j % kBufs) * kBuf, 0, r16, g4, c);
         slab_lookup<KB>(s_tab, c);
-        const ScoreAcc acc = slab_mfma<KB, !SOA>(c, qc, qb);
-        const int valid = t1 - (t0 + 16 * j);
+        const ScoreAcc acc = slab_mfma<KB, !SOA>(c, qv, qb);
+        const int valid = t_end - 16 * (wg0 + cur);
         if (valid >= 16) {
           if constexpr (SOA)
             slab_tail_soa<true>(c.nf, acc, 16, g4, s);
@@ -1972,6 +1998,7 @@ hipError_t launch_decode_mfma(const Geometry& g, const DevTables* tables, const 
   a.part = static_cast<float*>(workspace);
   a.out = out;
   a.out_fp32 = out_is_fp32;
+  a.dynamic = plan.deterministic ? 0 : 1;
   if (plan.mfma == 4) {
     // one workgroup per (sequence, kv head, workgroup split); the merge runs
     // only when a sequence has more than one workgroup split

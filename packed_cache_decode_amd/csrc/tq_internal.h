@@ -75,6 +75,7 @@ struct DecodePlan {
   int chunk;        // tokens per split
   int num_splits;   // splits per sequence (grid extent)
   size_t workspace_bytes;
+  int deterministic;  // ring kernel: fixed slab shares (reproducible bits)
 };
 
 bool mfma_decode_eligible(const Geometry& g, int num_q_heads);

@@ -494,6 +494,12 @@ DecodePlan plan_decode(const Geometry& g, int batch, int num_q_heads, int max_se
     }
     if (s < 1) s = 1;
     p.mfma = 4;
+    // two or more rounds of one-per-CU workgroups: half-size workgroups, two
+    // per CU, so one's set-up and drain overlap the other's streaming
+    // (TQ_DECODE_RING_WAVES=8|16 forces either, for measurements)
+    p.ring_waves = pairs * s >= 2 * 256 ? 8 : 16;
+    const char* rw = getenv("TQ_DECODE_RING_WAVES");
+    if (rw != nullptr && (atoi(rw) == 8 || atoi(rw) == 16)) p.ring_waves = atoi(rw);
     p.chunk = 16 * ((slabs + s - 1) / s);
     p.num_splits = max_seq_len > 0 ? (max_seq_len + p.chunk - 1) / p.chunk : 1;
     p.workspace_bytes = p.num_splits > 1 ? mfma_partial_bytes(batch, num_q_heads, p.num_splits) : 0;

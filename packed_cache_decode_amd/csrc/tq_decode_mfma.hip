@@ -1502,17 +1502,19 @@ __global__ void __launch_bounds__(64 * H, page_waves_per_simd(KB)) decode_page_k
 
 // ============================================================================
 // ring: one workgroup of 16 wavefronts per (sequence, kv head, workgroup
-// split).  The workgroup's slabs are dealt out in 16 consecutive runs, one per
-// wavefront; each wavefront streams its run's 16-row slabs of its head into a
-// private LDS ring with loads that write LDS directly, in the page kernel's
-// aligned slot layout, and computes them with the page kernel's slab code.
-// The wavefronts never wait for each other inside the loop (each waits only
-// for its own loads).  At the end they combine their partial softmax states
-// in LDS; with one workgroup split per sequence the workgroup writes the
-// output itself, and no merge kernel runs.  The loads are plain, not
-// non-temporal: a head's 16-byte chunks overlap its neighbours' slots, and
-// those lines are then still in L2 when the neighbouring heads ask for them.
-// 3/4-bit keys, at most 8 query heads per kv head.
+// split), one per CU; or of 8 wavefronts, two per CU, when there are at
+// least two rounds of workgroups (one's set-up and drain then overlap the
+// other's streaming).  The wavefronts claim the workgroup's slabs one at a
+// time from an LDS counter; each streams its claimed 16-row slabs of its head
+// into a private LDS ring with loads that write LDS directly, in the page
+// kernel's aligned slot layout, and computes them with the page kernel's slab
+// code.  The wavefronts never wait for each other inside the loop (each
+// waits only for its own loads).  At the end they combine their partial
+// softmax states in LDS; with one workgroup split per sequence the workgroup
+// writes the output itself, and no merge kernel runs.  The loads are plain,
+// not non-temporal: a head's 16-byte chunks overlap its neighbours' slots,
+// and those lines are then still in L2 when the neighbouring heads ask for
+// them.  3/4-bit keys, at most 8 query heads per kv head.
 // ============================================================================
 
 // ---- split page (data region + meta region) ----
@@ -1600,11 +1602,12 @@ __device__ __forceinline__ void slab_tail_soa(const uint32_t (&nf)[2], const Sco
 }
 
 constexpr int kRingBufs = 3;                 // slabs per wavefront ring (two in flight)
-constexpr int kRingWaves = 16;               // wavefronts per workgroup
+constexpr int kRingWaves = 16;               // wavefronts per workgroup (one workgroup per CU),
+                                             // or half as many (two per CU; see ring_waves)
 constexpr int kRingMaxSlabs = 1024;          // slabs per workgroup split: its page ids fit in LDS
 
-template <int KB, int SLOT, bool SOA>
-__global__ void __launch_bounds__(64 * kRingWaves) decode_ring_kernel(MfmaArgs a) {
+template <int KB, int SLOT, bool SOA, int WAVES>
+__global__ void __launch_bounds__(64 * WAVES, kRingWaves / WAVES) decode_ring_kernel(MfmaArgs a) {
   static_assert(KB == 3 || KB == 4, "ring kernel: 3/4-bit keys");
   constexpr int VB = vbits_of_slot(SLOT);
   using Geo = PageGeom<KB, SLOT, 1>;         // one head's slab layout in LDS (slotted page)
@@ -1619,7 +1622,7 @@ __global__ void __launch_bounds__(64 * kRingWaves) decode_ring_kernel(MfmaArgs a
   __shared__ u32x2 s_tab[256];
   __shared__ int32_t s_pid[kRingMaxSlabs];
   __shared__ int32_t s_next;                 // the workgroup's next unclaimed slab
-  __shared__ __attribute__((aligned(16))) uint8_t s_ring[kRingWaves][kRing];
+  __shared__ __attribute__((aligned(16))) uint8_t s_ring[WAVES][kRing];
 
   const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
   const int lane = threadIdx.x & 63;
@@ -1642,9 +1645,9 @@ __global__ void __launch_bounds__(64 * kRingWaves) decode_ring_kernel(MfmaArgs a
   const int cap = a.chunk >> 4;              // slabs per workgroup split, at most
   const int s_b = n_slabs_b > 0 ? (n_slabs_b + cap - 1) / cap : 1;
   if (sg >= s_b) return;                     // the whole workgroup, before any barrier
-  const int cs = (n_slabs_b + kRingWaves * s_b - 1) / (kRingWaves * s_b);   // slabs per wavefront, on average
-  const int wg0 = sg * kRingWaves * cs;      // the workgroup's slabs [wg0, wg1)
-  const int wg1 = min(n_slabs_b, wg0 + kRingWaves * cs);
+  const int cs = (n_slabs_b + WAVES * s_b - 1) / (WAVES * s_b);   // slabs per wavefront, on average
+  const int wg0 = sg * WAVES * cs;           // the workgroup's slabs [wg0, wg1)
+  const int wg1 = min(n_slabs_b, wg0 + WAVES * cs);
   const int n_wg = wg1 - wg0;
   const int t_end = min(T, 16 * wg1);        // the workgroup's last token + 1
 
@@ -1723,7 +1726,7 @@ __global__ void __launch_bounds__(64 * kRingWaves) decode_ring_kernel(MfmaArgs a
   // load zeros), so the count of loads in flight stays fixed.
   int n_claims = 0;
   auto claim = [&]() {
-    if (!a.dynamic) return w + kRingWaves * n_claims++;
+    if (!a.dynamic) return w + WAVES * n_claims++;
     int v = 0;
     if (lane == 0) v = atomicAdd(&s_next, 1);
     return __builtin_amdgcn_readfirstlane(v);
@@ -1849,7 +1852,7 @@ __global__ void __launch_bounds__(64 * kRingWaves) decode_ring_kernel(MfmaArgs a
     float M = -INFINITY, L = 0.0f;
     float2 acc = make_float2(0.0f, 0.0f);
 #pragma unroll 4
-    for (int v = 0; v < kRingWaves; ++v) {
+    for (int v = 0; v < WAVES; ++v) {
       const float* rec = reinterpret_cast<const float*>(s_ring[v]) + h * kRec;
       const float m = rec[kD];
       const float m_new = fmaxf(M, m);
@@ -1937,6 +1940,24 @@ bool page_decode_eligible(const Geometry& g, int num_q_heads, bool mse_keys_too)
   return mfma_decode_eligible(g, num_q_heads) && g_ok && kind_ok && (H == 1 || H == 2 || H == 4 || H % 8 == 0);
 }
 
+template <int WAVES>
+void launch_ring(const Geometry& g, dim3 grid, const MfmaArgs& a, hipStream_t stream) {
+  const dim3 block(64 * WAVES);
+  if (g.soa) {
+    if (g.key_bits == 4)
+      hipLaunchKernelGGL((decode_ring_kernel<4, 134, true, WAVES>), grid, block, 0, stream, a);
+    else if (g.slot == 118)
+      hipLaunchKernelGGL((decode_ring_kernel<3, 118, true, WAVES>), grid, block, 0, stream, a);
+    else
+      hipLaunchKernelGGL((decode_ring_kernel<3, 102, true, WAVES>), grid, block, 0, stream, a);
+  } else if (g.key_bits == 4)
+    hipLaunchKernelGGL((decode_ring_kernel<4, 134, false, WAVES>), grid, block, 0, stream, a);
+  else if (g.slot == 118)
+    hipLaunchKernelGGL((decode_ring_kernel<3, 118, false, WAVES>), grid, block, 0, stream, a);
+  else
+    hipLaunchKernelGGL((decode_ring_kernel<3, 102, false, WAVES>), grid, block, 0, stream, a);
+}
+
 bool ring_decode_eligible(const Geometry& g, int num_q_heads) {
   const int G = num_q_heads / g.num_kv_heads;
   return g.head_dim == kD && g.block_size % 16 == 0 && G >= 1 && G <= 8 &&
@@ -2004,20 +2025,10 @@ hipError_t launch_decode_mfma(const Geometry& g, const DevTables* tables, const 
     // only when a sequence has more than one workgroup split
     const int n_items = plan.num_splits * batch * g.num_kv_heads;
     const dim3 grid(8 * ((n_items + 7) / 8));
-    const dim3 block(64 * kRingWaves);
-    if (g.soa) {
-      if (g.key_bits == 4)
-        hipLaunchKernelGGL((decode_ring_kernel<4, 134, true>), grid, block, 0, stream, a);
-      else if (g.slot == 118)
-        hipLaunchKernelGGL((decode_ring_kernel<3, 118, true>), grid, block, 0, stream, a);
-      else
-        hipLaunchKernelGGL((decode_ring_kernel<3, 102, true>), grid, block, 0, stream, a);
-    } else if (g.key_bits == 4)
-      hipLaunchKernelGGL((decode_ring_kernel<4, 134, false>), grid, block, 0, stream, a);
-    else if (g.slot == 118)
-      hipLaunchKernelGGL((decode_ring_kernel<3, 118, false>), grid, block, 0, stream, a);
+    if (plan.ring_waves == 8)
+      launch_ring<8>(g, grid, a, stream);
     else
-      hipLaunchKernelGGL((decode_ring_kernel<3, 102, false>), grid, block, 0, stream, a);
+      launch_ring<kRingWaves>(g, grid, a, stream);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || plan.num_splits == 1) return e;
     hipLaunchKernelGGL(decode_merge_kernel, dim3(batch * num_q_heads), dim3(256), 0, stream, a);

@@ -76,6 +76,7 @@ struct DecodePlan {
   int num_splits;   // splits per sequence (grid extent)
   size_t workspace_bytes;
   int deterministic;  // ring kernel: fixed slab shares (reproducible bits)
+  int ring_waves;     // ring kernel: 16 wavefronts per workgroup (one per CU) or 8 (two per CU)
 };
 
 bool mfma_decode_eligible(const Geometry& g, int num_q_heads);

@@ -120,6 +120,30 @@ def test_decode_ring_workgroup_splits(preset, monkeypatch):
     check_decode(got, want, bf16_out=False)
 
 
+@pytest.mark.parametrize("preset", ["turboquant_4bit_nc", "turboquant_k3v4_nc", "turboquant_3bit_nc"])
+@pytest.mark.parametrize("waves", ["8", "16"])
+def test_decode_ring_workgroup_sizes(preset, waves, monkeypatch):
+    # the ring kernel's two workgroup shapes (8 wavefronts two per CU, 16 one
+    # per CU) on empty, ragged and multi-split sequences
+    monkeypatch.setenv("TQ_DECODE_KERNEL", "ring")
+    monkeypatch.setenv("TQ_DECODE_RING_WAVES", waves)
+    w = _wl(preset, G=8, H=2, B=6, lens=(20000, 20000), seed=43)
+    got, want = _decode_from_oracle_cache(w, lens=[0, 1, 17, 600, 16400, 20000])
+    check_decode(got, want, bf16_out=False)
+
+
+@pytest.mark.parametrize("waves", ["8", "16"])
+def test_decode_ring_deterministic_each_workgroup_size(waves, monkeypatch):
+    monkeypatch.setenv("TQ_DECODE_KERNEL", "ring")
+    monkeypatch.setenv("TQ_DECODE_RING_WAVES", waves)
+    monkeypatch.setenv("TQ_DECODE_DETERMINISTIC", "1")
+    w = _wl("turboquant_k3v4_nc", G=4, seed=5, lens=(100, 5000))
+    a, want = _decode_from_oracle_cache(w)
+    b, _ = _decode_from_oracle_cache(w)
+    assert np.array_equal(a, b)
+    check_decode(a, want, bf16_out=False)
+
+
 @pytest.mark.parametrize("preset", PRESETS)
 def test_decode_small_parity_bf16(preset):
     got, want = _decode_from_oracle_cache(_wl(preset, G=4, seed=21), out_fp32=False)

@@ -205,6 +205,15 @@ def test_soa_decode_bf16_ragged_and_long(preset):
     check_decode(got, want, bf16_out=True)
 
 
+@pytest.mark.parametrize("preset", MSE)
+@pytest.mark.parametrize("waves", ["8", "16"])
+def test_soa_decode_ring_workgroup_sizes(preset, waves, monkeypatch):
+    monkeypatch.setenv("TQ_DECODE_RING_WAVES", waves)
+    w = _wl(preset, H=2, Hq=16, lens=(20000, 20000), B=5, seed=7)
+    got, want = _decode_soa(w, lens=[0, 3, 700, 16400, 20000])
+    check_decode(got, want, bf16_out=False)
+
+
 @pytest.mark.parametrize("name", ["llama3_8b", "k3v4_gqa8"])
 def test_soa_full_size_sampled(name):
     """A full-size workload stored by the GPU in the split layout and decoded

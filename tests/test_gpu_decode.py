@@ -216,7 +216,12 @@ def test_decode_dynamic_claims_agree_with_fixed_shares(monkeypatch):
     b, _ = _decode_from_oracle_cache(w)
     check_decode(a, want, bf16_out=False)
     check_decode(b, want, bf16_out=False)
-    assert np.max(np.abs(a - b)) < 1e-5
+    # the two orders differ by rounding only: each wavefront's running max
+    # (and so the f16 hi/lo split of its weights) and the order of the fp32
+    # sums follow which slabs it took.  Random rounding over n = 9000 tokens
+    # moves a result by about sqrt(n) * 2^-24 * max|V| ~ 2.5e-5 (|V| < 4);
+    # the bound is four times that, far inside the oracle bound of 2e-3
+    assert np.max(np.abs(a - b)) < 1e-4
 
 
 FULL = ["tiny", "llama3_8b", "k3v4_gqa8", "k8v4_32k", "long_131k"]

@@ -475,10 +475,10 @@ DecodePlan plan_decode(const Geometry& g, int batch, int num_q_heads, int max_se
     return p;
   }
   if (ring_decode_eligible(g, num_q_heads) && (force == "ring" || auto_pick)) {
-    // ring kernel: one workgroup of 16 wavefronts per (sequence, kv head,
-    // workgroup split), at most ring_max_slabs() slabs per split (its page
-    // ids fit in LDS); more splits only to fill whole rounds of the 256 CUs
-    // (one workgroup each), so a round is not left part-empty, and only while
+    // ring kernel: one workgroup per (sequence, kv head, workgroup split),
+    // at most ring_max_slabs() slabs per split (its page ids fit in LDS);
+    // more splits only to fill whole rounds of the 256 CUs (one 16-wavefront
+    // workgroup each), so a round is not left part-empty, and only while
     // every wavefront keeps at least 4 slabs
     const int slabs = max_seq_len > 0 ? (max_seq_len + 15) / 16 : 1;
     const int cap = ring_max_slabs();

@@ -1820,7 +1820,7 @@ __global__ void __launch_bounds__(64 * WAVES, kRingWaves / WAVES) decode_ring_ke
     wait_vmcnt<0>();                         // no load may still write the ring
   }
 
-  // ---- combine the 16 wavefronts' states in LDS ----
+  // ---- combine the wavefronts' states in LDS ----
   // each wavefront's records (O[128], m, l, z per query head) go into its own
   // ring, whose reads have all completed
   float* rec_w = reinterpret_cast<float*>(ring);

@@ -227,6 +227,20 @@ size_t tq_decode_workspace_bytes(const tq_ctx* ctx, int batch, int num_q_heads,
  *                  aligned; contents need no initialisation; calls that
  *                  share a workspace must not overlap; may be NULL when
  *                  that size is 0
+ *
+ * Reproducibility.  With 3/4-bit keys the default kernel lets its
+ * wavefronts claim 16-token slabs from a shared counter, so the order of the
+ * fp32 sums, and the last bits of `out`, can change from call to call (every
+ * result stays within the same error bound).  Environment variables, read
+ * when the plan is made (tq_decode_workspace_bytes and tq_decode read the
+ * same ones, so set them before both):
+ *   TQ_DECODE_DETERMINISTIC=1          fixed slab order: bit-identical
+ *                                      results for identical inputs
+ *   TQ_DECODE_KERNEL=ring|page|staged|direct
+ *                                      force one decode kernel where it
+ *                                      applies (for tests and measurements)
+ *   TQ_DECODE_PAGE_HEADS=1|2|4         kv heads per page-kernel workgroup
+ *   TQ_DECODE_RING_WAVES=8|16          wavefronts per ring-kernel workgroup
  */
 tq_status tq_decode(const tq_ctx* ctx, const void* q, const uint8_t* cache, int64_t num_blocks,
                     const int32_t* block_table, int max_blocks_per_seq, const int32_t* seq_lens,

@@ -1,21 +1,30 @@
 """Benchmark of the packed KV-cache hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload llama3_8b]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload long_131k]
 
 One step = the whole hot path over one batch of the workload: tq_store of
 every (token, kv head) of the batch into the paged cache, then one tq_decode
-step for every sequence.  Inputs (bf16 K/V/q, slot mapping, block tables) are
-seeded synthetic data of the workload's shape, resident in HBM before timing.
-Before each kernel a 1 GiB buffer is read (outside the event-timed
-intervals) so neither call is served from L2 or the 256 MB Infinity Cache;
-reading, unlike writing, leaves no dirty lines to be written back during the
-timed kernel.
+step for every sequence.  The default workload is the long-context one: a
+bulk store of 4 x 131072 tokens x 8 kv heads (4-bit keys with norm
+correction, 4-bit values, 134-byte slots) through a random slot mapping, then
+one decode with 32 query heads.  Inputs (bf16 K/V/q, slot mapping, block
+tables) are seeded synthetic data of the workload's shape, resident in HBM
+before timing.  Before each kernel a 1 GiB buffer is read (outside the
+event-timed intervals) so neither call is served from L2 or the 256 MB
+Infinity Cache; reading, unlike writing, leaves no dirty lines to be written
+back during the timed kernel.
 
 Printed: one JSON line.  `value` is decode HBM throughput in GB/s: the
 algorithmic bytes of one decode (packed cache of every token and kv head,
 q, output, block-table entries, seq_lens) divided by the event-timed
-duration of tq_decode (its split kernel and its combine kernel), averaged
-over the K timed steps.  The store's tokens/s comes from the same steps.
+duration of tq_decode (all its kernels), averaged over the K timed steps.
+The store's tokens/s comes from the same steps.  `hbm_probe` holds the read
+rates of the library's streaming-read probes (each load form of the kernels)
+and of a device copy, measured in the same session.
+
+`cpu_baseline` times the CPU oracle as it is on the host's cores (one worker
+process per core available to this process, at most 16, one BLAS thread
+each) over a bounded sample of the same workload.
 """
 
 import argparse
@@ -78,12 +87,30 @@ def store_alg_bytes_per_token(w, slot):
     return w.num_kv_heads * (2 * w.head_dim * 2 + slot) + 8
 
 
-def cpu_baseline(inp, slot, budget_s=12.0):
-    """Time the CPU oracle (as it is) on a bounded sample of the workload."""
+def cpu_model():
     try:
-        from threadpoolctl import threadpool_limits
-    except ImportError:           # pragma: no cover
-        threadpool_limits = None
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def oracle_cores():
+    """Worker processes for the oracle baseline: the cores this process may
+    run on, at most 16 (one GPU's share of its host)."""
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def _oracle_worker(barrier, results, idx, preset, head_dim, block_size, slot, k_st, v_st,
+                   groups):
+    """One worker of the oracle baseline.  Untimed: encode the decode groups'
+    slots.  Then, after every worker is ready, two timed phases separated by
+    the barrier: the fp32-contract store oracle on k_st/v_st, and the float64
+    decode oracle on the groups.  Reports wall-clock intervals."""
     import numpy as np
 
     from oracle import codebook as cb
@@ -91,49 +118,94 @@ def cpu_baseline(inp, slot, budget_s=12.0):
     from oracle import layout, rotation
     from oracle import store as ost
 
+    lay = layout.slot_layout(preset, head_dim)
+    signs = rotation.rotation_signs(99, head_dim)
+    c, m = cb.codebook(head_dim, 4 if lay.key_fp8 else lay.key_bits)
+    caches = []
+    for k, v, q, T in groups:
+        slots = ost.encode_slots(k, v, lay, signs, m)
+        npg = -(-T // block_size)
+        local = np.zeros((npg, block_size, 1, slot), np.uint8)
+        t = np.arange(T)
+        local[t // block_size, t % block_size] = slots
+        caches.append((local, q, T, npg))
+    barrier.wait()
+    t0 = time.perf_counter()
+    if len(k_st):
+        ost.encode_slots(k_st, v_st, lay, signs, m)
+    t1 = time.perf_counter()
+    barrier.wait()
+    t2 = time.perf_counter()
+    nbytes = 0
+    for local, q, T, npg in caches:
+        odec.decode_f64(q, local, np.arange(npg)[None], np.array([T]), lay, signs, c, 1)
+        nbytes += T * slot + 2 * q.shape[1] * head_dim * 2 + 4 * npg + 4
+    t3 = time.perf_counter()
+    results.put((idx, t0, t1, t2, t3, nbytes))
+
+
+def cpu_baseline(inp, slot, cores=None, store_tokens_per_core=2048):
+    """Time the CPU oracle (as it is) on the host's cores over a bounded sample
+    of the workload: one (sequence, kv head) decode group per worker, and
+    store_tokens_per_core tokens (all kv heads) per worker for the store.
+    Throughput = the sample's bytes (tokens) / the wall time from the first
+    worker's start to the last one's end of each timed phase."""
+    import multiprocessing as mp
+
     w = inp.w
-    lay = layout.slot_layout(w.preset, w.head_dim)
-    signs = rotation.rotation_signs(99, w.head_dim)
-    kb = 4 if lay.key_fp8 else lay.key_bits
-    c, m = cb.codebook(w.head_dim, kb)
-    import contextlib
-    lim = threadpool_limits(limits=1) if threadpool_limits else contextlib.nullcontext()
-    with lim:
-        # store: encode tokens of sequence 0 until half the budget is spent
-        n_store, t_store = 0, 0.0
-        while t_store < budget_s / 2 and n_store < inp.num_tokens:
-            step = min(1024, inp.num_tokens - n_store)
-            t0 = time.perf_counter()
-            ost.encode_slots(inp.k[n_store:n_store + step], inp.v[n_store:n_store + step], lay, signs, m)
-            t_store += time.perf_counter() - t0
-            n_store += step
-        # decode: whole (sequence, kv head) groups until the other half is spent
-        offs = inp.token_offsets()
-        G = w.gqa
-        n_groups, dec_bytes, t_dec = 0, 0, 0.0
-        for b in range(w.batch):
-            for g in range(w.num_kv_heads):
-                if t_dec >= budget_s / 2:
-                    break
-                T = int(inp.seq_lens[b])
-                slots = ost.encode_slots(inp.k[offs[b]:offs[b] + T, g:g + 1],
-                                         inp.v[offs[b]:offs[b] + T, g:g + 1], lay, signs, m)
-                npg = -(-T // w.block_size)
-                local = np.zeros((npg, w.block_size, 1, slot), np.uint8)
-                t = np.arange(T)
-                local[t // w.block_size, t % w.block_size] = slots
-                t0 = time.perf_counter()
-                odec.decode_f64(inp.q[b:b + 1, g * G:(g + 1) * G], local, np.arange(npg)[None],
-                                np.array([T]), lay, signs, c, 1)
-                t_dec += time.perf_counter() - t0
-                n_groups += 1
-                dec_bytes += T * slot + 2 * G * w.head_dim * 2 + 4 * npg + 4
+    n = cores or oracle_cores()
+    groups = [(b, g) for b in range(w.batch) for g in range(w.num_kv_heads)]
+    n = min(n, len(groups))
+    offs = inp.token_offsets()
+    G = w.gqa
+    ctx = mp.get_context("forkserver")
+    barrier = ctx.Barrier(n)
+    results = ctx.Queue()
+    procs = []
+    n_store = 0
+    for i in range(n):
+        b, g = groups[i]
+        T = int(inp.seq_lens[b])
+        grp = [(inp.k[offs[b]:offs[b] + T, g:g + 1].copy(), inp.v[offs[b]:offs[b] + T, g:g + 1].copy(),
+                inp.q[b:b + 1, g * G:(g + 1) * G].copy(), T)]
+        a = min(inp.num_tokens, i * store_tokens_per_core)
+        e = min(inp.num_tokens, a + store_tokens_per_core)
+        n_store += e - a
+        procs.append(ctx.Process(target=_oracle_worker,
+                                 args=(barrier, results, i, w.preset, w.head_dim, w.block_size, slot,
+                                       inp.k[a:e].copy(), inp.v[a:e].copy(), grp)))
+    for p in procs:
+        p.start()
+    got = [results.get(timeout=900) for _ in procs]
+    for p in procs:
+        p.join()
+    t_store = max(r[2] for r in got) - min(r[1] for r in got)
+    t_dec = max(r[4] for r in got) - min(r[3] for r in got)
+    dec_bytes = sum(r[5] for r in got)
     return dict(
-        value=round(dec_bytes / t_dec / 1e9, 6), unit="GB/s", cores=1, kind="oracle",
-        sample=(f"float64 decode oracle on {n_groups} (sequence, kv head) groups of this workload "
-                f"({dec_bytes} algorithmic bytes, {t_dec:.1f} s); fp32-contract store oracle on "
-                f"{n_store} tokens x {w.num_kv_heads} heads ({t_store:.1f} s); one thread"),
+        value=round(dec_bytes / t_dec / 1e9, 6), unit="GB/s", cores=n, kind="oracle",
+        cpu_model=cpu_model(),
+        sample=(f"float64 decode oracle on {n} (sequence, kv head) groups of this workload, one per "
+                f"worker process ({dec_bytes} algorithmic bytes in {t_dec:.2f} s wall); "
+                f"fp32-contract store oracle on {n_store} tokens x {w.num_kv_heads} heads "
+                f"({t_store:.2f} s wall); {n} processes, one BLAS thread each"),
         store_tokens_per_s=round(n_store / t_store, 1))
+
+
+def start_oracle_server():
+    """Start the process server the oracle workers fork from, before this
+    process initialises the GPU (one BLAS thread per worker)."""
+    import multiprocessing as mp
+    from multiprocessing import forkserver
+    saved = {k: os.environ.get(k) for k in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS")}
+    os.environ.update(OMP_NUM_THREADS="1", OPENBLAS_NUM_THREADS="1")
+    mp.get_context("forkserver").set_forkserver_preload(["numpy", "oracle.store", "oracle.decode"])
+    forkserver.ensure_running()
+    for k, v in saved.items():
+        if v is None:
+            os.environ.pop(k, None)
+        else:
+            os.environ[k] = v
 
 
 def main():
@@ -141,11 +213,20 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="llama3_8b")
+    ap.add_argument("--workload", default="long_131k")
     ap.add_argument("--layout", choices=["aos", "soa"], default="aos",
                     help="page layout: slots back to back (default), or the split page "
                          "(data region + fp16 meta region, K norm folded at store time)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--warm-reps", type=int, default=None,
+                    help="back-to-back decodes with no flush, reported apart (default: --steps; "
+                         "0 leaves them out, so a profile of the run holds cold launches only)")
+    ap.add_argument("--decode-kernel", default="",
+                    choices=["", "ring", "page", "staged", "direct"],
+                    help="force a decode kernel where it applies (default: chosen by shape)")
+    ap.add_argument("--dynamic-claims", action="store_true",
+                    help="ring decode: wavefronts claim slabs from a counter (not reproducible "
+                         "bit for bit)")
     ap.add_argument("--flush", choices=["read", "write", "none"], default="read",
                     help="how caches are evicted before each timed kernel: read a 1 GiB buffer "
                          "(default; leaves no dirty lines), write it, or not at all")
@@ -155,10 +236,13 @@ def main():
               f"--gpus {args.gpus}); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
+    if not args.no_cpu_baseline:
+        start_oracle_server()          # before this process touches the GPU
+
     import numpy as np
     import torch
 
-    from packed_cache_decode_amd import synth
+    from packed_cache_decode_amd import _lib, synth
     from packed_cache_decode_amd.runtime import PackedKVCache
 
     dev = torch.device("cuda:0")
@@ -176,6 +260,7 @@ def main():
     sm, bt, sl = up(inp.slot_mapping), up(inp.block_table), up(inp.seq_lens)
     tq = PackedKVCache(w.preset, w.head_dim, w.num_kv_heads, w.block_size, rot_seed=2024,
                        device=dev, layout=args.layout)
+    tq.set_decode_options(kernel=args.decode_kernel, dynamic_claims=args.dynamic_claims)
     cache = tq.new_cache(inp.num_blocks)
     max_len = int(inp.seq_lens.max())
     out = torch.empty((w.batch, w.num_q_heads, w.head_dim), dtype=torch.bfloat16, device=dev)
@@ -219,12 +304,21 @@ def main():
 
     copy_src = torch.ones(1 << 26, dtype=torch.int32, device=dev)
     copy_dst = torch.empty_like(copy_src)
+    flush_bytes = flush.numel() * 4
+    psink = torch.empty(_lib.tq_probe_sink_words(flush_bytes), dtype=torch.int32, device=dev)
+    hbm_probe = {}
+    for mode in ("regs", "regs_nt", "lds", "lds_nt"):
+        t = probe(lambda: _lib.tq_probe_read(mode, flush, flush_bytes, psink))
+        hbm_probe[f"read_{mode}_gbs"] = round(flush_bytes / t / 1e9, 1)
     t_read = probe(lambda: torch.amax(flush, dim=0, out=sink))
     t_copy = probe(lambda: copy_dst.copy_(copy_src))
-    hbm_probe = {"read_gbs": round(flush.numel() * 4 / t_read / 1e9, 1),
-                 "copy_gbs": round(2 * copy_src.numel() * 4 / t_copy / 1e9, 1),
-                 "note": "torch amax over 1 GiB; torch copy of 256 MiB (read + write bytes)"}
-    del copy_src, copy_dst
+    hbm_probe["read_torch_amax_gbs"] = round(flush_bytes / t_read / 1e9, 1)
+    hbm_probe["copy_gbs"] = round(2 * copy_src.numel() * 4 / t_copy / 1e9, 1)
+    hbm_probe["note"] = ("tq_probe_read over 1 GiB with 16-byte loads into registers or LDS, plain "
+                         "or non-temporal; torch amax over the same 1 GiB; torch copy of 256 MiB "
+                         "(read + write bytes)")
+    best_read = max(hbm_probe[f"read_{m}_gbs"] for m in ("regs", "regs_nt", "lds", "lds_nt"))
+    del copy_src, copy_dst, psink
 
     for _ in range(args.warmup):
         step()
@@ -243,15 +337,18 @@ def main():
 
     # warm cache, reported apart: the same decode back to back with no flush,
     # so the cache is read from L2 / the Infinity Cache where it fits
-    wev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
-    tq.decode(q, cache, bt, sl, max_len, out=out)
-    for e0, e1 in wev:
-        e0.record()
+    warm_reps = args.steps if args.warm_reps is None else args.warm_reps
+    t_warm = None
+    if warm_reps > 0:
+        wev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(warm_reps)]
         tq.decode(q, cache, bt, sl, max_len, out=out)
-        e1.record()
-    torch.cuda.synchronize()
-    t_warm = np.array([e0.elapsed_time(e1) for e0, e1 in wev]) * 1e-3
+        for e0, e1 in wev:
+            e0.record()
+            tq.decode(q, cache, bt, sl, max_len, out=out)
+            e1.record()
+        torch.cuda.synchronize()
+        t_warm = np.array([e0.elapsed_time(e1) for e0, e1 in wev]) * 1e-3
 
     slot = tq.slot_bytes
     dec_bytes = decode_alg_bytes(inp, slot)
@@ -276,14 +373,15 @@ def main():
                    "seq_len": int(inp.seq_lens.max()), "num_q_heads": w.num_q_heads,
                    "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
                    "block_size": w.block_size, "cache_bytes": int(n_tok * w.num_kv_heads * slot),
-                   "layout": args.layout, "cache_flush": args.flush},
+                   "layout": args.layout, "cache_flush": args.flush,
+                   "decode_options": _lib.tq_get_decode_options(tq.ctx)},
         "decode_us": round(t_dec.mean() * 1e6, 2),
         "decode_us_p10_p90": [round(float(np.percentile(t_dec, 10)) * 1e6, 2),
                               round(float(np.percentile(t_dec, 90)) * 1e6, 2)],
         "decode_pct_of_hbm_peak": round(100 * dec_gbs / HBM_PEAK_GBS, 2),
-        "decode_pct_of_probe": {"read": round(100 * dec_gbs / hbm_probe["read_gbs"], 1),
+        "decode_pct_of_probe": {"best_read": round(100 * dec_gbs / best_read, 1),
                                 "copy": round(100 * dec_gbs / hbm_probe["copy_gbs"], 1)},
-        "decode_warm_us": round(float(np.median(t_warm)) * 1e6, 2),
+        "decode_warm_us": None if t_warm is None else round(float(np.median(t_warm)) * 1e6, 2),
         "decode_warm_note": "median of back-to-back decodes with no cache flush (not the metric)",
         "store_tokens_per_s": round(n_tok / t_store.mean(), 1),
         "store_us": round(t_store.mean() * 1e6, 2),

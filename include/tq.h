@@ -107,7 +107,41 @@ typedef enum {
   TQ_ROTATION_HAAR = 2
 } tq_rotation;
 
-typedef struct tq_ctx tq_ctx;   /* opaque; immutable after tq_codebook_init */
+typedef struct tq_ctx tq_ctx;   /* opaque; only tq_set_decode_options changes it after init */
+
+/* Which decode kernel runs (tq_decode_options.kernel).  AUTO picks by key
+ * type and shape; a forced kernel is used where it applies to the shape and
+ * AUTO's choice is taken otherwise.  All of them compute the same attention
+ * within the same error bound; they differ in speed only. */
+typedef enum {
+  TQ_DECODE_KERNEL_AUTO = 0,
+  TQ_DECODE_KERNEL_RING = 1,    /* per (sequence, kv head) workgroups streaming per-head slabs */
+  TQ_DECODE_KERNEL_PAGE = 2,    /* per (sequence, split) workgroups streaming whole page rows */
+  TQ_DECODE_KERNEL_STAGED = 3,  /* one wavefront per (split, sequence, kv head), staged rows */
+  TQ_DECODE_KERNEL_DIRECT = 4   /* one wavefront per (split, sequence, kv head), direct loads */
+} tq_decode_kernel;
+
+/* How a context's decode is planned.  The default (all zero) is AUTO with
+ * reproducible results: for a fixed shape and options, identical inputs give
+ * bit-identical outputs on every call.
+ *   kernel          tq_decode_kernel
+ *   dynamic_claims  nonzero: the ring kernel's wavefronts claim 16-token
+ *                   slabs from a shared counter instead of taking fixed
+ *                   interleaved shares.  It evens out wavefronts that run at
+ *                   different rates (a few per cent faster on long
+ *                   sequences), but which wavefront sums which slab, and so
+ *                   the last bits of `out`, change from call to call (every
+ *                   result stays within the same error bound).
+ *   ring_waves      0 = by shape; 8 or 16 wavefronts per ring workgroup
+ *   page_heads      0 = by shape; 1, 2 or 4 kv heads per page workgroup
+ * These select between implementations of the same operation (P1, section
+ * "读取内核"); they exist for reproducibility and for measurements. */
+typedef struct {
+  int kernel;
+  int dynamic_claims;
+  int ring_waves;
+  int page_heads;
+} tq_decode_options;
 
 /* Solve the Lloyd-Max codebook for a rotated coordinate ~ N(0, 1/head_dim)
  * (P1, section "Lloyd-Max 的两个最优性条件"), derive the decision boundaries
@@ -228,19 +262,11 @@ size_t tq_decode_workspace_bytes(const tq_ctx* ctx, int batch, int num_q_heads,
  *                  share a workspace must not overlap; may be NULL when
  *                  that size is 0
  *
- * Reproducibility.  With 3/4-bit keys the default kernel lets its
- * wavefronts claim 16-token slabs from a shared counter, so the order of the
- * fp32 sums, and the last bits of `out`, can change from call to call (every
- * result stays within the same error bound).  Environment variables, read
- * when the plan is made (tq_decode_workspace_bytes and tq_decode read the
- * same ones, so set them before both):
- *   TQ_DECODE_DETERMINISTIC=1          fixed slab order: bit-identical
- *                                      results for identical inputs
- *   TQ_DECODE_KERNEL=ring|page|staged|direct
- *                                      force one decode kernel where it
- *                                      applies (for tests and measurements)
- *   TQ_DECODE_PAGE_HEADS=1|2|4         kv heads per page-kernel workgroup
- *   TQ_DECODE_RING_WAVES=8|16          wavefronts per ring-kernel workgroup
+ * Reproducibility.  The plan (kernel, split count, order of the fp32 sums)
+ * depends only on the shape arguments and the context's decode options, so
+ * with the default options identical inputs give bit-identical outputs.
+ * tq_decode_workspace_bytes plans with the same options: size the workspace
+ * after the last tq_set_decode_options.
  */
 tq_status tq_decode(const tq_ctx* ctx, const void* q, const uint8_t* cache, int64_t num_blocks,
                     const int32_t* block_table, int max_blocks_per_seq, const int32_t* seq_lens,
@@ -301,11 +327,24 @@ tq_status tq_decode_continuation(const tq_ctx* ctx, const void* q, const uint8_t
                                  int out_is_fp32, void* workspace, size_t workspace_bytes,
                                  void* stream);
 
-/* Read the sticky device error word (synchronises with the device):
+/* Read the context's sticky device error word once the work enqueued on
+ * `stream` (a hipStream_t as void*, NULL = the null stream) has finished:
+ * the call synchronises that stream only, not the device.
  * bit 0 = a store slot beyond the cache, bit 1 = a page id beyond the cache,
  * bit 2 = a seq_lens entry outside [0, max_seq_len] (clamped).
- * `clear` nonzero resets it to 0 afterwards. */
-tq_status tq_get_device_error(const tq_ctx* ctx, int32_t* code_host, int clear);
+ * `clear` nonzero resets it to 0 afterwards (on the same stream, before
+ * returning).  Kernels of this context running on other streams may set the
+ * word while it is read. */
+tq_status tq_get_device_error(const tq_ctx* ctx, int32_t* code_host, int clear, void* stream);
+
+/* Set the context's decode options (see tq_decode_options); NULL restores
+ * the defaults.  Later tq_decode, tq_decode_workspace_bytes and
+ * tq_decode_continuation calls use them.  Not to be called while another
+ * host thread plans a decode on the same context. */
+tq_status tq_set_decode_options(tq_ctx* ctx, const tq_decode_options* opts);
+
+/* Copy the context's decode options to *opts. */
+tq_status tq_get_decode_options(const tq_ctx* ctx, tq_decode_options* opts);
 
 /* ---- host-only helpers (no device needed; for checks and tooling) ------- */
 

@@ -20,13 +20,24 @@ STATUS = {0: "TQ_OK", -1: "TQ_ERR_INVALID_ARG", -2: "TQ_ERR_UNSUPPORTED", -3: "T
 PRESETS = {"turboquant_k8v4": 0, "turboquant_4bit_nc": 1, "turboquant_k3v4_nc": 2, "turboquant_3bit_nc": 3}
 CODEBOOK_MODES = {"exact": 0, "page_trapz": 1, "beta": 2}
 LAYOUTS = {"aos": 0, "soa": 1}
+DECODE_KERNELS = {"": 0, "auto": 0, "ring": 1, "page": 2, "staged": 3, "direct": 4}
+
+
+class DecodeOptions(ctypes.Structure):
+    """tq_decode_options of include/tq.h."""
+    _fields_ = [("kernel", ctypes.c_int), ("dynamic_claims", ctypes.c_int),
+                ("ring_waves", ctypes.c_int), ("page_heads", ctypes.c_int)]
 
 # every symbol include/tq.h declares
 EXPORTS = ("tq_codebook_init", "tq_codebook_init_layout", "tq_layout_of", "tq_destroy", "tq_slot_bytes", "tq_cache_bytes", "tq_get_tables",
            "tq_store", "tq_decode_workspace_bytes", "tq_decode", "tq_dequant",
            "tq_continuation_workspace_bytes", "tq_decode_continuation", "tq_get_device_error",
+           "tq_set_decode_options", "tq_get_decode_options",
            "tq_host_codebook", "tq_host_rotation_signs", "tq_host_haar_matrix", "tq_host_slot_bytes",
            "tq_status_str")
+# every symbol include/tq_probe.h declares (measurement helpers)
+PROBE_EXPORTS = ("tq_probe_sink_words", "tq_probe_read")
+PROBE_MODES = {"regs": 0, "regs_nt": 1, "lds": 2, "lds_nt": 3}
 
 
 class TQError(RuntimeError):
@@ -70,12 +81,16 @@ def load():
         "tq_continuation_workspace_bytes": (ctypes.c_size_t, [_vp, _int, _int, _int, _int]),
         "tq_decode_continuation": (_int, [_vp, _vp, _vp, _i64, _vp, _int, _int, _int, _int, ctypes.c_float,
                                           _vp, _int, _vp, ctypes.c_size_t, _vp]),
-        "tq_get_device_error": (_int, [_vp, ctypes.POINTER(_i32), _int]),
+        "tq_get_device_error": (_int, [_vp, ctypes.POINTER(_i32), _int, _vp]),
+        "tq_set_decode_options": (_int, [_vp, ctypes.POINTER(DecodeOptions)]),
+        "tq_get_decode_options": (_int, [_vp, ctypes.POINTER(DecodeOptions)]),
         "tq_host_codebook": (_int, [_int, _int, _int, _vp, _vp]),
         "tq_host_rotation_signs": (_int, [ctypes.c_uint64, _int, _int, _vp]),
         "tq_host_haar_matrix": (_int, [ctypes.c_uint64, _int, _vp]),
         "tq_host_slot_bytes": (_i64, [_int, _int]),
         "tq_status_str": (ctypes.c_char_p, [_int]),
+        "tq_probe_sink_words": (_i64, [_i64]),
+        "tq_probe_read": (_int, [_int, _vp, _i64, _vp, _vp]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -215,10 +230,26 @@ def tq_decode_continuation(ctx, q, cache, num_blocks, block_table_row, max_block
                                          _stream(stream)))
 
 
-def tq_get_device_error(ctx, clear=True):
+def tq_get_device_error(ctx, clear=True, stream=None):
     code = _i32(0)
-    _check("tq_get_device_error", load().tq_get_device_error(ctx, ctypes.byref(code), int(clear)))
+    _check("tq_get_device_error", load().tq_get_device_error(ctx, ctypes.byref(code), int(clear),
+                                                             _stream(stream)))
     return code.value
+
+
+def tq_set_decode_options(ctx, kernel=0, dynamic_claims=0, ring_waves=0, page_heads=0):
+    """kernel: a tq_decode_kernel value or one of DECODE_KERNELS' names."""
+    if isinstance(kernel, str):
+        kernel = DECODE_KERNELS[kernel]
+    o = DecodeOptions(int(kernel), int(dynamic_claims), int(ring_waves), int(page_heads))
+    _check("tq_set_decode_options", load().tq_set_decode_options(ctx, ctypes.byref(o)))
+
+
+def tq_get_decode_options(ctx):
+    o = DecodeOptions()
+    _check("tq_get_decode_options", load().tq_get_decode_options(ctx, ctypes.byref(o)))
+    return dict(kernel=o.kernel, dynamic_claims=o.dynamic_claims, ring_waves=o.ring_waves,
+                page_heads=o.page_heads)
 
 
 def tq_host_codebook(head_dim, bits, codebook_mode=0):
@@ -255,3 +286,14 @@ def tq_host_slot_bytes(preset, head_dim):
 
 def tq_status_str(status):
     return load().tq_status_str(status).decode()
+
+
+def tq_probe_sink_words(nbytes):
+    return load().tq_probe_sink_words(nbytes)
+
+
+def tq_probe_read(mode, src, nbytes, sink, stream=None):
+    """One streaming read of ``src`` with a load form of PROBE_MODES."""
+    if isinstance(mode, str):
+        mode = PROBE_MODES[mode]
+    _check("tq_probe_read", load().tq_probe_read(mode, _ptr(src), nbytes, _ptr(sink), _stream(stream)))

@@ -27,6 +27,7 @@ SOURCES = [
     ("tq_decode.hip", []),
     ("tq_decode_mfma.hip", ["-fno-honor-nans"]),
     ("tq_dequant.hip", []),
+    ("tq_probe.hip", []),
 ]
 
 
@@ -39,17 +40,22 @@ def _run(cmd):
 
 
 def build(verbose=False):
+    """Compile every translation unit (in parallel) and link the library."""
+    from concurrent.futures import ThreadPoolExecutor
     os.makedirs(BUILD, exist_ok=True)
-    objs = []
+    cmds, objs = [], []
     for src, extra in SOURCES:
         obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-        cmd = [HIPCC, *COMMON, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
-        if src.endswith(".cpp"):
-            cmd = [HIPCC, *COMMON, "-x", "hip", *extra, "-c", os.path.join(CSRC, src), "-o", obj]
-        out = _run(cmd)
-        if verbose and out.strip():
-            print(out)
+        lang = ["-x", "hip"] if src.endswith(".cpp") else []
+        cmds.append([HIPCC, *COMMON, *lang, *extra, "-c", os.path.join(CSRC, src), "-o", obj])
         objs.append(obj)
+    jobs = max(1, min(len(cmds), int(os.environ.get("MAX_JOBS", "8"))))
+    with ThreadPoolExecutor(jobs) as pool:
+        outs = list(pool.map(_run, cmds))
+    if verbose:
+        for out in outs:
+            if out.strip():
+                print(out)
     tmp = LIB + ".tmp"
     _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs])
     os.replace(tmp, LIB)

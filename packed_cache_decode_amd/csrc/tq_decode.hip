@@ -18,8 +18,6 @@
 //   every V load is coalesced), accumulating p * v for all G heads.
 //   Partials per (sequence, q head, split): acc[d], running max m (base 2),
 //   running sum l.  The combine weights split s by 2^(m_s - max m).
-#include <cstdlib>
-#include <string>
 
 #include "tq_internal.h"
 
@@ -30,6 +28,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 struct DecodeArgs {
   const DevTables* tables;
+  DevErrors* errs;
   const uint16_t* q;
   const uint8_t* cache;
   int64_t num_blocks;
@@ -106,7 +105,7 @@ __global__ void __launch_bounds__(64) decode_split_kernel(DecodeArgs a) {
   int T = a.seq_lens[b];
   const int t_cap = min(a.num_splits * a.chunk, a.max_blocks << a.bs_shift);
   if (T < 0 || T > t_cap) {
-    if (lane == 0 && split == 0 && g == 0) const_cast<DevTables*>(a.tables)->err_len = 1;
+    if (lane == 0 && split == 0 && g == 0) a.errs->len = 1;
     T = T < 0 ? 0 : t_cap;
   }
   const int t0 = split * a.chunk;
@@ -224,7 +223,7 @@ __global__ void __launch_bounds__(64) decode_split_kernel(DecodeArgs a) {
     if (valid) {
       const int page = bt[t >> a.bs_shift];
       if (page < 0 || page >= a.num_blocks) {
-        const_cast<DevTables*>(a.tables)->err_page = 1;
+        a.errs->page = 1;
         valid = false;
       } else if (a.soa) {
         const int64_t pb = static_cast<int64_t>(page) * (row_bytes << a.bs_shift);
@@ -420,12 +419,12 @@ hipError_t launch_g(const DecodeArgs& a, int G, int batch, hipStream_t stream) {
 
 }  // namespace
 
-DecodePlan plan_decode(const Geometry& g, int batch, int num_q_heads, int max_seq_len) {
+DecodePlan plan_decode(const Geometry& g, const tq_decode_options& opts, int batch, int num_q_heads,
+                       int max_seq_len) {
   DecodePlan p{};
-  // TQ_DECODE_DETERMINISTIC=1: the ring kernel deals slabs out in a fixed
-  // order (results reproducible bit for bit; a few per cent slower)
-  const char* det = getenv("TQ_DECODE_DETERMINISTIC");
-  p.deterministic = det != nullptr && det[0] == '1';
+  // ring kernel: slabs dealt out in a fixed interleaved order unless the
+  // context asks for dynamic claims (results then vary in the last bits)
+  p.dynamic = opts.dynamic_claims ? 1 : 0;
   if (g.haar) {
     // the matrix-core kernels rotate q with butterflies; the Haar rotation's
     // dense product runs in the general kernel
@@ -441,24 +440,20 @@ DecodePlan plan_decode(const Geometry& g, int batch, int num_q_heads, int max_se
   // k3v4- and k8v4-shaped decodes): FP8 keys take the page-cooperative
   // kernel; 3/4-bit keys with at most 8 query heads per kv head the ring
   // kernel, else (an even number of kv heads) the staged kernel, else the
-  // direct one.  TQ_DECODE_KERNEL=page|ring|staged|direct forces one where it
-  // applies (for tests and measurements of each path).
-  const char* env = getenv("TQ_DECODE_KERNEL");
-  const std::string force = env != nullptr ? env : "";
-  const bool auto_pick = force != "page" && force != "staged" && force != "direct" && force != "ring";
-  if ((auto_pick || force == "page") && page_decode_eligible(g, num_q_heads, force == "page")) {
+  // direct one.  The context's options may force one where it applies.
+  const int force = opts.kernel;
+  const bool auto_pick = force == TQ_DECODE_KERNEL_AUTO;
+  if ((auto_pick || force == TQ_DECODE_KERNEL_PAGE) &&
+      page_decode_eligible(g, num_q_heads, force == TQ_DECODE_KERNEL_PAGE)) {
     // one resident round of workgroups (256 CUs x the workgroups that fit per
     // CU) over (sequence, split), at least 4 slabs of 16 tokens per split so
     // the load pipeline's start is amortised
     // kv heads per workgroup: the whole row, at most 8 (measured fastest:
-    // smaller groups were slower for FP8 keys); TQ_DECODE_PAGE_HEADS=1|2|4
-    // takes smaller groups (for measurements)
+    // smaller groups were slower for FP8 keys); the options may ask for
+    // smaller groups
     int group = g.num_kv_heads < 8 ? g.num_kv_heads : 8;
-    const char* ph = getenv("TQ_DECODE_PAGE_HEADS");
-    if (ph != nullptr) {
-      const int want = atoi(ph);
-      if ((want == 1 || want == 2 || want == 4) && g.num_kv_heads % want == 0) group = want;
-    }
+    const int want = opts.page_heads;
+    if ((want == 1 || want == 2 || want == 4) && g.num_kv_heads % want == 0) group = want;
     const int slabs = max_seq_len > 0 ? (max_seq_len + 15) / 16 : 1;
     const int target = 256 * page_wgs_per_cu(g, group);
     const int per_split = batch * (g.num_kv_heads / group);
@@ -474,7 +469,7 @@ DecodePlan plan_decode(const Geometry& g, int batch, int num_q_heads, int max_se
     p.workspace_bytes = (p.workspace_bytes + 255) & ~static_cast<size_t>(255);
     return p;
   }
-  if (ring_decode_eligible(g, num_q_heads) && (force == "ring" || auto_pick)) {
+  if (ring_decode_eligible(g, num_q_heads) && (force == TQ_DECODE_KERNEL_RING || auto_pick)) {
     // ring kernel: one workgroup per (sequence, kv head, workgroup split),
     // at most ring_max_slabs() slabs per split (its page ids fit in LDS);
     // more splits only to fill whole rounds of the 256 CUs (one 16-wavefront
@@ -495,11 +490,10 @@ DecodePlan plan_decode(const Geometry& g, int batch, int num_q_heads, int max_se
     if (s < 1) s = 1;
     p.mfma = 4;
     // two or more rounds of one-per-CU workgroups: half-size workgroups, two
-    // per CU, so one's set-up and drain overlap the other's streaming
-    // (TQ_DECODE_RING_WAVES=8|16 forces either, for measurements)
+    // per CU, so one's set-up and drain overlap the other's streaming (the
+    // options may force either size)
     p.ring_waves = pairs * s >= 2 * 256 ? 8 : 16;
-    const char* rw = getenv("TQ_DECODE_RING_WAVES");
-    if (rw != nullptr && (atoi(rw) == 8 || atoi(rw) == 16)) p.ring_waves = atoi(rw);
+    if (opts.ring_waves == 8 || opts.ring_waves == 16) p.ring_waves = opts.ring_waves;
     p.chunk = 16 * ((slabs + s - 1) / s);
     p.num_splits = max_seq_len > 0 ? (max_seq_len + p.chunk - 1) / p.chunk : 1;
     p.workspace_bytes = p.num_splits > 1 ? mfma_partial_bytes(batch, num_q_heads, p.num_splits) : 0;
@@ -512,7 +506,8 @@ DecodePlan plan_decode(const Geometry& g, int batch, int num_q_heads, int max_se
     // per split so the per-wavefront set-up is amortised
     const int slabs = max_seq_len > 0 ? (max_seq_len + 15) / 16 : 1;
     const int per_split = batch * g.num_kv_heads;
-    const bool staged = staged_decode_eligible(g, num_q_heads) && (force == "staged" || auto_pick);
+    const bool staged = staged_decode_eligible(g, num_q_heads) &&
+                        (force == TQ_DECODE_KERNEL_STAGED || auto_pick);
     const int target = 256 * mfma_waves_per_cu(g, staged);
     int s = per_split > 0 ? (target + per_split - 1) / per_split : 1;
     const int s_max = (slabs + 7) / 8;
@@ -534,17 +529,18 @@ DecodePlan plan_decode(const Geometry& g, int batch, int num_q_heads, int max_se
   return p;
 }
 
-hipError_t launch_decode(const Geometry& g, const DevTables* tables, const DecodePlan& plan,
+hipError_t launch_decode(const Geometry& g, const DevTables* tables, DevErrors* errs, const DecodePlan& plan,
                          const uint16_t* q, const uint8_t* cache, int64_t num_blocks,
                          const int32_t* block_table, int max_blocks_per_seq,
                          const int32_t* seq_lens, int batch, int num_q_heads, float sm_scale,
                          void* out, int out_is_fp32, void* workspace, hipStream_t stream) {
   DecodeArgs a;
   if (plan.mfma)
-    return launch_decode_mfma(g, tables, plan, q, cache, num_blocks, block_table, max_blocks_per_seq,
+    return launch_decode_mfma(g, tables, errs, plan, q, cache, num_blocks, block_table, max_blocks_per_seq,
                               seq_lens, batch, num_q_heads, sm_scale, out, out_is_fp32, workspace,
                               stream);
   a.tables = tables;
+  a.errs = errs;
   a.q = q;
   a.cache = cache;
   a.num_blocks = num_blocks;

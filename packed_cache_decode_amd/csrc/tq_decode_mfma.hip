@@ -68,6 +68,7 @@ constexpr int kBufferWord3 = 0x00020000;     // raw buffer resource, 32-bit data
 
 struct MfmaArgs {
   const DevTables* tables;
+  DevErrors* errs;
   const uint16_t* q;
   const uint8_t* cache;
   int64_t num_blocks;
@@ -517,7 +518,7 @@ __device__ __forceinline__ void stage_page_offsets(const MfmaArgs& a, int b, int
   for (int i = threadIdx.x; i < n_pages; i += blockDim.x) {
     const int page = bt[p_first + i];
     if (page < 0 || page >= a.num_blocks) {
-      const_cast<DevTables*>(a.tables)->err_page = 1;
+      a.errs->page = 1;
       s_page_off[i] = -1;
     } else {
       s_page_off[i] = static_cast<int64_t>(page) * page_bytes;
@@ -565,8 +566,8 @@ __device__ __forceinline__ int clamp_len(const MfmaArgs& a, int b, int split, in
   const int T = a.seq_lens[b];
   const int t_cap = min(a.num_splits * a.chunk, a.max_blocks << a.bs_shift);
   if (threadIdx.x == 0 && split == 0 && g == 0) {
-    if (T < 0 || T > t_cap) const_cast<DevTables*>(a.tables)->err_len = 1;
-    if (T > 0 && a.num_blocks <= 0) const_cast<DevTables*>(a.tables)->err_page = 1;
+    if (T < 0 || T > t_cap) a.errs->len = 1;
+    if (T > 0 && a.num_blocks <= 0) a.errs->page = 1;
   }
   return effective_len(a, b);
 }
@@ -1169,7 +1170,7 @@ __device__ __forceinline__ void stage_page_ids(const MfmaArgs& a, int b, int t0,
   for (int i = threadIdx.x; i < n_pages; i += blockDim.x) {
     const int page = bt[p_first + i];
     const bool ok = page >= 0 && page < a.num_blocks;
-    if (!ok) const_cast<DevTables*>(a.tables)->err_page = 1;
+    if (!ok) a.errs->page = 1;
     s_pid[i] = ok ? page : -1;
   }
 }
@@ -1995,13 +1996,15 @@ size_t mfma_partial_bytes(int batch, int num_q_heads, int num_splits) {
   return static_cast<size_t>(batch) * num_q_heads * num_splits * kRec * sizeof(float);
 }
 
-hipError_t launch_decode_mfma(const Geometry& g, const DevTables* tables, const DecodePlan& plan,
+hipError_t launch_decode_mfma(const Geometry& g, const DevTables* tables, DevErrors* errs,
+                              const DecodePlan& plan,
                               const uint16_t* q, const uint8_t* cache, int64_t num_blocks,
                               const int32_t* block_table, int max_blocks_per_seq,
                               const int32_t* seq_lens, int batch, int num_q_heads, float sm_scale,
                               void* out, int out_is_fp32, void* workspace, hipStream_t stream) {
   MfmaArgs a;
   a.tables = tables;
+  a.errs = errs;
   a.q = q;
   a.cache = cache;
   a.num_blocks = num_blocks;
@@ -2019,7 +2022,7 @@ hipError_t launch_decode_mfma(const Geometry& g, const DevTables* tables, const 
   a.part = static_cast<float*>(workspace);
   a.out = out;
   a.out_fp32 = out_is_fp32;
-  a.dynamic = plan.deterministic ? 0 : 1;
+  a.dynamic = plan.dynamic;
   if (plan.mfma == 4) {
     // one workgroup per (sequence, kv head, workgroup split); the merge runs
     // only when a sequence has more than one workgroup split

@@ -23,6 +23,7 @@ namespace {
 
 struct DequantArgs {
   const DevTables* tables;
+  DevErrors* errs;
   const uint8_t* cache;
   int64_t num_blocks;
   const int32_t* block_table;   // the sequence's row
@@ -109,7 +110,7 @@ __global__ void __launch_bounds__(64 * kWaves) dequant_kernel(DequantArgs a) {
     const int page = a.block_table[t >> a.bs_shift];
     const int row = t & ((1 << a.bs_shift) - 1);
     if (page < 0 || page >= a.num_blocks) {
-      if (lane == 0) const_cast<DevTables*>(a.tables)->err_page = 1;
+      if (lane == 0) a.errs->page = 1;
 #pragma unroll
       for (int e = 0; e < E; ++e) {
         put(a.k_out, o0 + e, 0.0f, a.out_fp32);
@@ -233,11 +234,12 @@ hipError_t launch_t(const DequantArgs& a, hipStream_t stream) {
 
 }  // namespace
 
-hipError_t launch_dequant(const Geometry& g, const DevTables* tables, const uint8_t* cache,
+hipError_t launch_dequant(const Geometry& g, const DevTables* tables, DevErrors* errs, const uint8_t* cache,
                           int64_t num_blocks, const int32_t* block_table_row, int seq_len,
                           void* k_out, void* v_out, int out_is_fp32, hipStream_t stream) {
   DequantArgs a;
   a.tables = tables;
+  a.errs = errs;
   a.cache = cache;
   a.num_blocks = num_blocks;
   a.block_table = block_table_row;

@@ -20,6 +20,7 @@
 #include "tq_internal.h"
 
 using tq::DevTables;
+using tq::DevErrors;
 using tq::Geometry;
 
 struct tq_ctx {
@@ -32,8 +33,10 @@ struct tq_ctx {
   int8_t signs[tq::kMaxHeadDim];
   float r_d;                        // float32(1 / sqrt(head_dim))
   int device;
-  DevTables* d_tables;
+  DevTables* d_tables;              // read-only to the kernels
+  DevErrors* d_errs;                // sticky error words, written by the kernels
   float* d_rot;                     // Haar rotation matrix (device), or null
+  tq_decode_options opts;           // decode plan options (tq_set_decode_options)
 };
 
 namespace {
@@ -578,19 +581,26 @@ tq_status tq_codebook_init_layout(tq_ctx** out, int preset, int head_dim, int nu
     }
     host.rot = c->d_rot;
   }
+  c->d_errs = nullptr;
   if (hipMalloc(&c->d_tables, sizeof(DevTables)) != hipSuccess) {
     if (c->d_rot) (void)hipFree(c->d_rot);
     delete c;
     return TQ_ERR_HIP;
   }
-  if (hipMemcpyAsync(c->d_tables, &host, sizeof(DevTables), hipMemcpyHostToDevice, st) !=
+  const DevErrors no_errors{};
+  if (hipMalloc(&c->d_errs, sizeof(DevErrors)) != hipSuccess ||
+      hipMemcpyAsync(c->d_tables, &host, sizeof(DevTables), hipMemcpyHostToDevice, st) !=
+          hipSuccess ||
+      hipMemcpyAsync(c->d_errs, &no_errors, sizeof(DevErrors), hipMemcpyHostToDevice, st) !=
           hipSuccess ||
       hipStreamSynchronize(st) != hipSuccess) {
+    if (c->d_errs) (void)hipFree(c->d_errs);
     (void)hipFree(c->d_tables);
     if (c->d_rot) (void)hipFree(c->d_rot);
     delete c;
     return TQ_ERR_HIP;
   }
+  c->opts = tq_decode_options{};
   *out = c;
   return TQ_OK;
 }
@@ -599,6 +609,7 @@ tq_status tq_destroy(tq_ctx* ctx) {
   if (!ctx) return TQ_OK;
   tq_status st = TQ_OK;
   if (ctx->d_tables && hipFree(ctx->d_tables) != hipSuccess) st = TQ_ERR_HIP;
+  if (ctx->d_errs && hipFree(ctx->d_errs) != hipSuccess) st = TQ_ERR_HIP;
   if (ctx->d_rot && hipFree(ctx->d_rot) != hipSuccess) st = TQ_ERR_HIP;
   delete ctx;
   return st;
@@ -637,7 +648,7 @@ tq_status tq_store(const tq_ctx* ctx, const void* k, const void* v, int64_t kv_t
     return TQ_ERR_ALIGNMENT;
   tq_status ds = check_device(ctx);
   if (ds != TQ_OK) return ds;
-  hipError_t e = tq::launch_store(g, ctx->d_tables, static_cast<const uint16_t*>(k),
+  hipError_t e = tq::launch_store(g, ctx->d_tables, ctx->d_errs, static_cast<const uint16_t*>(k),
                                   static_cast<const uint16_t*>(v), kv_token_stride, slot_mapping,
                                   num_tokens, cache, num_blocks, ctx->r_d,
                                   static_cast<hipStream_t>(stream));
@@ -648,7 +659,7 @@ size_t tq_decode_workspace_bytes(const tq_ctx* ctx, int batch, int num_q_heads,
                                  int max_seq_len) {
   if (!ctx || batch < 0 || num_q_heads <= 0 || max_seq_len < 0) return 0;
   if (num_q_heads % ctx->geo.num_kv_heads != 0) return 0;
-  return tq::plan_decode(ctx->geo, batch, num_q_heads, max_seq_len).workspace_bytes;
+  return tq::plan_decode(ctx->geo, ctx->opts, batch, num_q_heads, max_seq_len).workspace_bytes;
 }
 
 tq_status tq_decode(const tq_ctx* ctx, const void* q, const uint8_t* cache, int64_t num_blocks,
@@ -670,7 +681,7 @@ tq_status tq_decode(const tq_ctx* ctx, const void* q, const uint8_t* cache, int6
   if (!aligned(q, 16) || !aligned(cache, 16) || !aligned(out, 16) || !aligned(block_table, 4) ||
       !aligned(seq_lens, 4))
     return TQ_ERR_ALIGNMENT;
-  tq::DecodePlan plan = tq::plan_decode(g, batch, num_q_heads, max_seq_len);
+  tq::DecodePlan plan = tq::plan_decode(g, ctx->opts, batch, num_q_heads, max_seq_len);
   if (plan.workspace_bytes > 0) {
     if (!workspace || workspace_bytes < plan.workspace_bytes) return TQ_ERR_WORKSPACE;
     if (!aligned(workspace, 256)) return TQ_ERR_ALIGNMENT;
@@ -678,7 +689,7 @@ tq_status tq_decode(const tq_ctx* ctx, const void* q, const uint8_t* cache, int6
   tq_status ds = check_device(ctx);
   if (ds != TQ_OK) return ds;
   if (!(sm_scale > 0.0f)) sm_scale = 1.0f / std::sqrt(static_cast<float>(g.head_dim));
-  hipError_t e = tq::launch_decode(g, ctx->d_tables, plan, static_cast<const uint16_t*>(q), cache,
+  hipError_t e = tq::launch_decode(g, ctx->d_tables, ctx->d_errs, plan, static_cast<const uint16_t*>(q), cache,
                                    num_blocks, block_table, max_blocks_per_seq, seq_lens, batch,
                                    num_q_heads, sm_scale, out, out_is_fp32, workspace,
                                    static_cast<hipStream_t>(stream));
@@ -698,7 +709,7 @@ tq_status tq_dequant(const tq_ctx* ctx, const uint8_t* cache, int64_t num_blocks
     return TQ_ERR_ALIGNMENT;
   tq_status ds = check_device(ctx);
   if (ds != TQ_OK) return ds;
-  hipError_t e = tq::launch_dequant(g, ctx->d_tables, cache, num_blocks, block_table_row, seq_len, k_out,
+  hipError_t e = tq::launch_dequant(g, ctx->d_tables, ctx->d_errs, cache, num_blocks, block_table_row, seq_len, k_out,
                                     v_out, out_is_fp32, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? TQ_OK : TQ_ERR_HIP;
 }
@@ -709,10 +720,10 @@ namespace {
 struct ContinuationSpace {
   size_t decode, lens_off, table_off, total;
 };
-ContinuationSpace continuation_space(const Geometry& g, int q_len, int num_q_heads, int seq_len,
-                                     int max_blocks) {
+ContinuationSpace continuation_space(const Geometry& g, const tq_decode_options& opts, int q_len,
+                                     int num_q_heads, int seq_len, int max_blocks) {
   ContinuationSpace c;
-  c.decode = tq::plan_decode(g, q_len, num_q_heads, seq_len).workspace_bytes;
+  c.decode = tq::plan_decode(g, opts, q_len, num_q_heads, seq_len).workspace_bytes;
   c.lens_off = (c.decode + 255) & ~static_cast<size_t>(255);
   c.table_off = (c.lens_off + 4 * static_cast<size_t>(q_len) + 255) & ~static_cast<size_t>(255);
   c.total = c.table_off + 4 * static_cast<size_t>(q_len) * max_blocks;
@@ -724,7 +735,7 @@ size_t tq_continuation_workspace_bytes(const tq_ctx* ctx, int q_len, int num_q_h
                                        int max_blocks) {
   if (!ctx || q_len <= 0 || num_q_heads <= 0 || seq_len < q_len || max_blocks <= 0) return 0;
   if (num_q_heads % ctx->geo.num_kv_heads != 0) return 0;
-  return continuation_space(ctx->geo, q_len, num_q_heads, seq_len, max_blocks).total;
+  return continuation_space(ctx->geo, ctx->opts, q_len, num_q_heads, seq_len, max_blocks).total;
 }
 
 tq_status tq_decode_continuation(const tq_ctx* ctx, const void* q, const uint8_t* cache,
@@ -742,7 +753,7 @@ tq_status tq_decode_continuation(const tq_ctx* ctx, const void* q, const uint8_t
   if (static_cast<int64_t>(max_blocks) * g.block_size < seq_len) return TQ_ERR_INVALID_ARG;
   if (!aligned(workspace, 256)) return TQ_ERR_ALIGNMENT;
   if (!aligned(block_table_row, 4)) return TQ_ERR_ALIGNMENT;
-  const ContinuationSpace c = continuation_space(g, q_len, num_q_heads, seq_len, max_blocks);
+  const ContinuationSpace c = continuation_space(g, ctx->opts, q_len, num_q_heads, seq_len, max_blocks);
   if (workspace_bytes < c.total) return TQ_ERR_WORKSPACE;
   tq_status ds = check_device(ctx);
   if (ds != TQ_OK) return ds;
@@ -756,20 +767,46 @@ tq_status tq_decode_continuation(const tq_ctx* ctx, const void* q, const uint8_t
                    out, out_is_fp32, c.decode > 0 ? workspace : nullptr, c.decode, stream);
 }
 
-tq_status tq_get_device_error(const tq_ctx* ctx, int32_t* code_host, int clear) {
+tq_status tq_get_device_error(const tq_ctx* ctx, int32_t* code_host, int clear, void* stream) {
   if (!ctx || !code_host) return TQ_ERR_INVALID_ARG;
-  if (hipDeviceSynchronize() != hipSuccess) return TQ_ERR_HIP;
-  int32_t words[3] = {0, 0, 0};
-  if (hipMemcpy(words, &ctx->d_tables->err_slot, sizeof(words), hipMemcpyDeviceToHost) !=
-      hipSuccess)
+  tq_status ds = check_device(ctx);
+  if (ds != TQ_OK) return ds;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  // both host buffers live until the stream has synchronised
+  DevErrors w{};
+  const DevErrors zero{};
+  if (hipMemcpyAsync(&w, ctx->d_errs, sizeof(w), hipMemcpyDeviceToHost, st) != hipSuccess)
     return TQ_ERR_HIP;
-  *code_host = (words[0] ? 1 : 0) | (words[1] ? 2 : 0) | (words[2] ? 4 : 0);
   if (clear) {
-    const int32_t zero[3] = {0, 0, 0};
-    if (hipMemcpy(&ctx->d_tables->err_slot, zero, sizeof(zero), hipMemcpyHostToDevice) !=
-        hipSuccess)
+    if (hipMemcpyAsync(ctx->d_errs, &zero, sizeof(zero), hipMemcpyHostToDevice, st) != hipSuccess)
       return TQ_ERR_HIP;
   }
+  if (hipStreamSynchronize(st) != hipSuccess) return TQ_ERR_HIP;
+  *code_host = (w.slot ? 1 : 0) | (w.page ? 2 : 0) | (w.len ? 4 : 0);
+  return TQ_OK;
+}
+
+tq_status tq_set_decode_options(tq_ctx* ctx, const tq_decode_options* opts) {
+  if (!ctx) return TQ_ERR_INVALID_ARG;
+  if (!opts) {
+    ctx->opts = tq_decode_options{};
+    return TQ_OK;
+  }
+  if (opts->kernel < TQ_DECODE_KERNEL_AUTO || opts->kernel > TQ_DECODE_KERNEL_DIRECT)
+    return TQ_ERR_INVALID_ARG;
+  if (opts->ring_waves != 0 && opts->ring_waves != 8 && opts->ring_waves != 16)
+    return TQ_ERR_INVALID_ARG;
+  if (opts->page_heads != 0 && opts->page_heads != 1 && opts->page_heads != 2 &&
+      opts->page_heads != 4)
+    return TQ_ERR_INVALID_ARG;
+  ctx->opts = *opts;
+  ctx->opts.dynamic_claims = opts->dynamic_claims != 0 ? 1 : 0;
+  return TQ_OK;
+}
+
+tq_status tq_get_decode_options(const tq_ctx* ctx, tq_decode_options* opts) {
+  if (!ctx || !opts) return TQ_ERR_INVALID_ARG;
+  *opts = ctx->opts;
   return TQ_OK;
 }
 

@@ -31,15 +31,23 @@ struct DevTables {
   float centroids[kMaxLevels];
   float midpoints[kMaxLevels];          // 2^b - 1 entries used
   uint32_t sign_bits[kMaxHeadDim / 32];
-  int32_t err_slot;                     // sticky: a store slot beyond the cache
-  int32_t err_page;                     // sticky: a page id beyond the cache
-  int32_t err_len;                      // sticky: a sequence length beyond the grid/table
   int32_t bin_count;
   float bin_scale;
   float bin_bias;
-  int32_t pad[2];
+  int32_t pad[1];
   uint32_t bins[kMaxBins][2];           // {float bits of thr, base}
   const float* rot;                     // Haar rotation: Q (d x d, row-major, fp32); null otherwise
+};
+
+// Sticky error words of a context, in their own device allocation (the
+// tables above are read-only to the kernels; these are the only device
+// memory of a context that kernels write).  A kernel sets a word to 1 and
+// skips the offending item; tq_get_device_error reads and clears them.
+struct DevErrors {
+  int32_t slot;   // a store slot beyond the cache
+  int32_t page;   // a page id beyond the cache
+  int32_t len;    // a sequence length beyond the grid or the block table
+  int32_t pad;
 };
 
 struct Geometry {
@@ -62,7 +70,7 @@ struct Geometry {
 
 // ---- launchers (defined in the .hip files) ---------------------------------
 
-hipError_t launch_store(const Geometry& g, const DevTables* tables, const uint16_t* k,
+hipError_t launch_store(const Geometry& g, const DevTables* tables, DevErrors* errs, const uint16_t* k,
                         const uint16_t* v, int64_t kv_token_stride, const int64_t* slot_mapping,
                         int64_t num_tokens, uint8_t* cache, int64_t num_blocks, float r_d,
                         hipStream_t stream);
@@ -75,7 +83,9 @@ struct DecodePlan {
   int chunk;        // tokens per split
   int num_splits;   // splits per sequence (grid extent)
   size_t workspace_bytes;
-  int deterministic;  // ring kernel: fixed slab shares (reproducible bits)
+  int dynamic;        // ring kernel: wavefronts claim slabs from a counter (the order of
+                      // the fp32 sums, and so the last bits, vary run to run); 0: fixed
+                      // interleaved shares (reproducible bit for bit)
   int ring_waves;     // ring kernel: 16 wavefronts per workgroup (one per CU) or 8 (two per CU)
 };
 
@@ -87,21 +97,23 @@ bool ring_decode_eligible(const Geometry& g, int num_q_heads);
 int ring_max_slabs();
 int mfma_waves_per_cu(const Geometry& g, bool staged);
 size_t mfma_partial_bytes(int batch, int num_q_heads, int num_splits);
-hipError_t launch_decode_mfma(const Geometry& g, const DevTables* tables, const DecodePlan& plan,
+hipError_t launch_decode_mfma(const Geometry& g, const DevTables* tables, DevErrors* errs,
+                              const DecodePlan& plan,
                               const uint16_t* q, const uint8_t* cache, int64_t num_blocks,
                               const int32_t* block_table, int max_blocks_per_seq,
                               const int32_t* seq_lens, int batch, int num_q_heads, float sm_scale,
                               void* out, int out_is_fp32, void* workspace, hipStream_t stream);
 
-DecodePlan plan_decode(const Geometry& g, int batch, int num_q_heads, int max_seq_len);
+DecodePlan plan_decode(const Geometry& g, const tq_decode_options& opts, int batch, int num_q_heads,
+                       int max_seq_len);
 
-hipError_t launch_dequant(const Geometry& g, const DevTables* tables, const uint8_t* cache,
+hipError_t launch_dequant(const Geometry& g, const DevTables* tables, DevErrors* errs, const uint8_t* cache,
                           int64_t num_blocks, const int32_t* block_table_row, int seq_len,
                           void* k_out, void* v_out, int out_is_fp32, hipStream_t stream);
 hipError_t launch_expand_rows(const int32_t* row, int max_blocks, int cached_len, int q_len,
                               int32_t* seq_lens, int32_t* table, hipStream_t stream);
 
-hipError_t launch_decode(const Geometry& g, const DevTables* tables, const DecodePlan& plan,
+hipError_t launch_decode(const Geometry& g, const DevTables* tables, DevErrors* errs, const DecodePlan& plan,
                          const uint16_t* q, const uint8_t* cache, int64_t num_blocks,
                          const int32_t* block_table, int max_blocks_per_seq,
                          const int32_t* seq_lens, int batch, int num_q_heads, float sm_scale,

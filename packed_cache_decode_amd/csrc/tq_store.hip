@@ -29,6 +29,7 @@ namespace {
 
 struct StoreArgs {
   const DevTables* tables;
+  DevErrors* errs;
   const uint16_t* k;
   const uint16_t* v;
   int64_t stride;            // elements between tokens
@@ -143,7 +144,7 @@ __global__ void __launch_bounds__(64 * kWaves) store_kernel(StoreArgs a) {
     const int64_t slot = a.slot_mapping[n];
     if (slot < 0) continue;                       // padding token
     if (slot >= a.num_slots) {
-      if (lane == 0) const_cast<DevTables*>(a.tables)->err_slot = 1;
+      if (lane == 0) a.errs->slot = 1;
       continue;
     }
     const int64_t page = slot >> a.bs_shift;
@@ -515,7 +516,7 @@ __global__ void __launch_bounds__(256) store128_kernel(StoreArgs a) {
     const int h = f.h;
     const int64_t slot = f.slot;
     const bool in_range = slot < a.num_slots;
-    if (live && slot >= 0 && !in_range && qd == 0) const_cast<DevTables*>(a.tables)->err_slot = 1;
+    if (live && slot >= 0 && !in_range && qd == 0) a.errs->slot = 1;
     const bool do_store = live && slot >= 0 && in_range;
     (void)n;
 
@@ -812,12 +813,13 @@ hipError_t launch_store_t(const StoreArgs& a, hipStream_t stream) {
 
 }  // namespace
 
-hipError_t launch_store(const Geometry& g, const DevTables* tables, const uint16_t* k,
+hipError_t launch_store(const Geometry& g, const DevTables* tables, DevErrors* errs, const uint16_t* k,
                         const uint16_t* v, int64_t kv_token_stride, const int64_t* slot_mapping,
                         int64_t num_tokens, uint8_t* cache, int64_t num_blocks, float r_d,
                         hipStream_t stream) {
   StoreArgs a;
   a.tables = tables;
+  a.errs = errs;
   a.k = k;
   a.v = v;
   a.stride = kv_token_stride;

@@ -99,5 +99,12 @@ class PackedKVCache:
                                     Hq, sm_scale, out, out.dtype == torch.float32, ws, ws.numel(), stream)
         return out
 
-    def device_error(self, clear=True):
-        return _lib.tq_get_device_error(self.ctx, clear)
+    def set_decode_options(self, kernel="", dynamic_claims=False, ring_waves=0, page_heads=0):
+        """Decode plan options of the context (tq_set_decode_options)."""
+        _lib.tq_set_decode_options(self.ctx, kernel, dynamic_claims, ring_waves, page_heads)
+        self._ws = None
+
+    def device_error(self, clear=True, stream=None):
+        """Sticky error bits once the work on ``stream`` (default: torch's
+        current stream) has finished."""
+        return _lib.tq_get_device_error(self.ctx, clear, stream)

@@ -16,8 +16,8 @@ from oracle import layout, rotation
 from packed_cache_decode_amd import _lib
 
 
-def _header_functions():
-    src = open(os.path.join(ROOT, "include", "tq.h")).read()
+def _header_functions(name="tq.h"):
+    src = open(os.path.join(ROOT, "include", name)).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
     return sorted(set(re.findall(r"\b(tq_[a-z_0-9]+)\s*\(", src)))
 
@@ -33,6 +33,20 @@ def test_exports_every_declared_symbol(lib):
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(_lib.EXPORTS) == names
+    probes = _header_functions("tq_probe.h")
+    for n in probes:
+        assert hasattr(lib, n), n
+    assert sorted(_lib.PROBE_EXPORTS) == probes
+    headers = sorted(f for f in os.listdir(os.path.join(ROOT, "include")) if f.endswith(".h"))
+    assert headers == ["tq.h", "tq_probe.h"]
+
+
+def test_probe_argument_checks(lib):
+    assert lib.tq_probe_sink_words(1000) == -1
+    assert lib.tq_probe_sink_words(1 << 30) == 2048 * 256
+    assert lib.tq_probe_read(0, None, 1 << 20, None, None) == -1
+    assert lib.tq_probe_read(7, 16, 1 << 20, 16, None) == -1
+    assert lib.tq_probe_read(0, 8, 1 << 20, 16, None) == -3
 
 
 @pytest.mark.parametrize("bits", [1, 2, 3, 4])
@@ -121,3 +135,21 @@ def test_init_rejects_bad_arguments_before_touching_a_device(lib):
     want = [-1, -2, -1, -2, -1]
     for (p, d, H, bs, mode), w in zip(bad, want):
         assert lib.tq_codebook_init(ctypes.byref(h), p, d, H, bs, 0, 1, mode, None) == w
+
+
+def test_decode_option_calls_reject_a_null_context(lib):
+    import ctypes
+    o = _lib.DecodeOptions(0, 0, 0, 0)
+    assert lib.tq_set_decode_options(None, ctypes.byref(o)) == -1
+    assert lib.tq_get_decode_options(None, ctypes.byref(o)) == -1
+    code = _lib._i32(0)
+    assert lib.tq_get_device_error(None, ctypes.byref(code), 1, None) == -1
+
+
+def test_library_reads_no_environment():
+    # decode planning depends only on the call's arguments and the context's
+    # options, never on the process environment
+    csrc = os.path.join(ROOT, "packed_cache_decode_amd", "csrc")
+    for name in os.listdir(csrc):
+        src = open(os.path.join(csrc, name)).read()
+        assert "getenv" not in src, name

@@ -66,3 +66,23 @@ def test_more_than_one_gpu_is_refused():
     assert r.returncode == 2
     assert "one GPU" in r.stderr
     assert r.stdout.strip() == ""
+
+
+def test_default_workload_is_the_long_context_store_and_decode():
+    import argparse
+    src = open(os.path.join(ROOT, "bench.py")).read()
+    assert 'ap.add_argument("--workload", default="long_131k")' in src
+    w = synth.WORKLOADS["long_131k"]
+    assert (w.batch, w.num_kv_heads, w.num_q_heads, w.head_dim) == (4, 8, 32, 128)
+
+
+def test_cpu_baseline_runs_on_several_cores():
+    """The oracle baseline on a small workload with two worker processes:
+    rates are positive and the core count is the number of workers."""
+    bench.start_oracle_server()
+    w = synth.scaled_down(synth.WORKLOADS["llama3_8b"], batch=1, seq_len=256, name="bench_small")
+    inp = synth.generate(w)
+    r = bench.cpu_baseline(inp, 134, cores=2, store_tokens_per_core=64)
+    assert r["cores"] == 2 and r["kind"] == "oracle" and r["unit"] == "GB/s"
+    assert r["value"] > 0 and r["store_tokens_per_s"] > 0
+    assert r["cpu_model"]

@@ -119,7 +119,7 @@ def test_decode_continuation_parity(preset, T, q_len, G):
     _continuation_case(preset, T, q_len, G)
 
 
-def _continuation_case(preset, T, q_len, G):
+def _continuation_case(preset, T, q_len, G, kernel=""):
     from packed_cache_decode_amd.runtime import PackedKVCache
     H, seed = 2, 8
     w, inp = _seq(preset, T, H, Hq=G * H, seed=T + q_len)
@@ -130,6 +130,7 @@ def _continuation_case(preset, T, q_len, G):
     want = odec.decode_continuation_f64(qb, cache, inp.block_table[0], T, ors.lay, ors.signs,
                                         ors.centroids, H)
     tq = PackedKVCache(preset, 128, H, 16, seed)
+    tq.set_decode_options(kernel=kernel)
     out = tq.decode_continuation(to_dev(qb), to_dev(cache), to_dev(inp.block_table[0].copy()), T,
                                  out_fp32=True)
     torch.cuda.synchronize()
@@ -139,11 +140,10 @@ def _continuation_case(preset, T, q_len, G):
 
 
 @pytest.mark.parametrize("kernel", ["ring", "page", "staged", "direct"])
-def test_decode_continuation_each_kernel(kernel, monkeypatch):
+def test_decode_continuation_each_kernel(kernel):
     """Short sequences with peaked softmax (the case that exposed an
     accumulation that lost precision) through each decode kernel."""
-    monkeypatch.setenv("TQ_DECODE_KERNEL", kernel)
-    _continuation_case("turboquant_k3v4_nc", 300, 37, 4)
+    _continuation_case("turboquant_k3v4_nc", 300, 37, 4, kernel)
 
 
 @pytest.mark.parametrize("preset", ["turboquant_4bit_nc", "turboquant_3bit_nc"])

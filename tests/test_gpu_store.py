@@ -137,36 +137,3 @@ def test_store_deterministic():
     a = _run_store(w)[1]
     b = _run_store(w)[1]
     assert np.array_equal(a, b)
-
-
-FULL = ["tiny", "llama3_8b", "k3v4_gqa8", "k8v4_32k", "long_131k"]
-
-
-@pytest.mark.parametrize("name", FULL)
-def test_store_full_size_sampled(name):
-    """The workload at full size, in the launch configuration the benchmark
-    times; 4096 sampled vectors compared with the oracle, spare pages
-    untouched, no device error."""
-    from packed_cache_decode_amd.runtime import PackedKVCache
-    w = synth.WORKLOADS[name]
-    print(f"[store full] {name}: generating", flush=True)
-    inp = synth.generate(w)
-    seed = 4242
-    tq = PackedKVCache(w.preset, w.head_dim, w.num_kv_heads, w.block_size, seed)
-    cache = tq.new_cache(inp.num_blocks + 2, CANARY)
-    tq.store(to_dev(inp.k), to_dev(inp.v), to_dev(inp.slot_mapping), cache)
-    torch.cuda.synchronize()
-    assert tq.device_error() == 0
-    spare = cache[inp.num_blocks:].cpu().numpy()
-    assert np.all(spare == CANARY)
-    rng = np.random.default_rng(0)
-    n = inp.num_tokens
-    pick = rng.choice(n, size=min(n, 4096 // w.num_kv_heads * w.num_kv_heads), replace=False)
-    sm = inp.slot_mapping[pick]
-    got = cache.view(-1, w.num_kv_heads, tq.slot_bytes)[torch.from_numpy(sm).cuda()].cpu().numpy()
-    tq.close()
-    ors = OracleSide(w.preset, w.head_dim, seed)
-    want = ors.encode(inp.k[pick], inp.v[pick])
-    res = compare_slots(got, want, inp.k[pick], inp.v[pick], ors)
-    print(f"[store full] {name}: {res}", flush=True)
-    assert res["rows_differing"] == 0

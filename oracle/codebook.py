@@ -20,11 +20,12 @@ Two solvers:
   until no level moves by 1e-14 or more, then make the table exactly
   symmetric by mirroring the positive half (the page states the solution is
   symmetric about 0) and round to float32.  This is the default codebook.
-* ``lloyd_max_page_trapz``: the numerical recipe printed in P1 ("vLLM 的实
-  现:数值积分而不是解析解"): 200-trapezoid integrals, outer edges at
-  +-10.5 sigma, tolerance 1e-10, at most 200 iterations, returning the
-  levels held when the loop stops.  The page does not print its trapezoid
-  helper; the composite rule with n = 200 equal panels is the reading taken.
+* ``lloyd_max_page_trapz``: the numerical recipe of P1 ("vLLM 的实现:数值积分
+  而不是解析解"), from the parameters the page gives: 200-trapezoid
+  integrals, outer edges at +-10.5 sigma, tolerance 1e-10, at most 200
+  iterations, returning the levels held when the loop stops.  The page does
+  not say how its trapezoid rule is formed; the composite rule with 200
+  equal panels is the reading taken.
 
 A third codebook, ``lloyd_max_beta``: the exact marginal of one coordinate of
 a uniformly random unit vector in R^d, the density of a rotated, normalised
@@ -101,42 +102,56 @@ def lloyd_max_exact(d, bits, tol=EXACT_TOL, max_iter=EXACT_MAX_ITER):
     return np.array(levels, dtype=np.float64), it
 
 
-def _page_pdf(x, sigma2):
-    return math.exp(-x * x / (2.0 * sigma2)) / math.sqrt(2.0 * math.pi * sigma2)
+# The page's numerical recipe, from the parameters its text states: levels
+# start evenly spread over +-3.5 sigma; the outer cells end at +-10.5 sigma
+# (three times that spread) instead of +-inf; each cell's mass and first
+# moment come from the composite trapezoid rule on 200 equal panels; the
+# iteration stops as soon as an update would move no level by 1e-10 or more
+# (keeping the levels it had), or after 200 updates.
+PAGE_PANELS = 200
+PAGE_OUTER_SIGMAS = 10.5
+PAGE_TOL = 1e-10
+PAGE_MAX_ITER = 200
 
 
-def _trapz(f, a, b, n=200):
-    h = (b - a) / n
-    s = 0.5 * (f(a) + f(b))
-    for i in range(1, n):
-        s += f(a + i * h)
-    return s * h
+def _gauss_density(x, var):
+    return math.exp(-x * x / (2.0 * var)) / math.sqrt(2.0 * math.pi * var)
 
 
-def lloyd_max_page_trapz(d, bits, max_iter=200, tol=1e-10):
-    """The page's numerical recipe (see module docstring).  Returns
-    (levels_f64, iterations run, converged flag)."""
-    n = 2 ** bits
-    sigma2 = 1.0 / d
-    sigma = math.sqrt(sigma2)
-    lo, hi = -3.5 * sigma, 3.5 * sigma
-    c = [lo + (hi - lo) * (i + 0.5) / n for i in range(n)]
-    converged = False
-    it = 0
+def trapezoid_cell_moments(a, b, var, panels=PAGE_PANELS):
+    """(mass, first moment) of N(0, var) over [a, b] by the composite
+    trapezoid rule on `panels` equal panels: nodes x_j = a + j h, weight h
+    (h / 2 at the two ends); both sums taken in node order."""
+    h = (b - a) / panels
+    mass = 0.0
+    first = 0.0
+    for j in range(panels + 1):
+        x = a + j * h
+        fx = _gauss_density(x, var)
+        if j == 0 or j == panels:
+            fx = 0.5 * fx
+        mass += fx
+        first += x * fx
+    return mass * h, first * h
+
+
+def lloyd_max_page_trapz(d, bits, max_iter=PAGE_MAX_ITER, tol=PAGE_TOL):
+    """The page's numerical recipe (see the comment above).  Returns
+    (levels_f64, updates tried, converged flag).  Every cell has positive
+    mass for these parameters, so each update is a plain ratio."""
+    var = 1.0 / d
+    outer = PAGE_OUTER_SIGMAS * math.sqrt(var)
+    levels = _initial_levels(2 ** bits, math.sqrt(var))
     for it in range(1, max_iter + 1):
-        bnd = [(c[i] + c[i + 1]) / 2.0 for i in range(n - 1)]
-        edges = [lo * 3] + bnd + [hi * 3]
-        new = []
-        for i in range(n):
-            a, b = edges[i], edges[i + 1]
-            num = _trapz(lambda x: x * _page_pdf(x, sigma2), a, b)
-            den = _trapz(lambda x: _page_pdf(x, sigma2), a, b)
-            new.append(num / den if den > 1e-15 else c[i])
-        if max(abs(new[i] - c[i]) for i in range(n)) < tol:
-            converged = True
-            break
-        c = new
-    return np.array(c, dtype=np.float64), it, converged
+        bounds = [-outer] + [(u + w) / 2.0 for u, w in zip(levels, levels[1:])] + [outer]
+        means = []
+        for a, b in zip(bounds, bounds[1:]):
+            mass, first = trapezoid_cell_moments(a, b, var)
+            means.append(first / mass)
+        if max(abs(m - c) for m, c in zip(means, levels)) < tol:
+            return np.array(levels, dtype=np.float64), it, True
+        levels = means
+    return np.array(levels, dtype=np.float64), max_iter, False
 
 
 def _beta_cdf(x, a):

@@ -94,44 +94,60 @@ bool solve_exact(int d, int bits, std::vector<double>& out) {
   return true;
 }
 
-double page_pdf(double x, double sigma2) {
-  return std::exp(-x * x / (2.0 * sigma2)) / std::sqrt(2.0 * M_PI * sigma2);
+// ---- the page's numerical recipe ----------------------------------------
+// From the parameters the page states: levels start evenly spread over
+// +-3.5 sigma; the outer cells end at +-10.5 sigma instead of +-infinity;
+// each cell's mass and first moment come from the composite trapezoid rule on
+// 200 equal panels; the iteration stops as soon as an update would move no
+// level by 1e-10 or more (keeping the levels it had), or after 200 updates.
+// Sums run in node order, so the tables equal the test oracle's bit for bit.
+constexpr int kPagePanels = 200;
+constexpr double kPageOuterSigmas = 10.5;
+constexpr double kPageTol = 1e-10;
+constexpr int kPageMaxIter = 200;
+
+double gauss_density(double x, double var) {
+  return std::exp(-x * x / (2.0 * var)) / std::sqrt(2.0 * M_PI * var);
 }
 
-template <class F>
-double trapz200(F f, double a, double b) {
-  const int n = 200;
-  const double h = (b - a) / n;
-  double s = 0.5 * (f(a) + f(b));
-  for (int i = 1; i < n; ++i) s += f(a + i * h);
-  return s * h;
+// (mass, first moment) of N(0, var) over [a, b]: nodes a + j h, weight h
+// (h / 2 at both ends)
+void trapezoid_cell_moments(double a, double b, double var, double& mass, double& first) {
+  const double h = (b - a) / kPagePanels;
+  double m = 0.0, f = 0.0;
+  for (int j = 0; j <= kPagePanels; ++j) {
+    const double x = a + j * h;
+    double fx = gauss_density(x, var);
+    if (j == 0 || j == kPagePanels) fx = 0.5 * fx;
+    m += fx;
+    f += x * fx;
+  }
+  mass = m * h;
+  first = f * h;
 }
 
-// The page's recipe: 200 trapezoids per integral, outer edges at +-10.5 sigma,
-// stop when no level moves by 1e-10 (returning the levels held at that
-// point), at most 200 iterations.
-void solve_page_trapz(int d, int bits, std::vector<double>& c) {
+void solve_page_trapz(int d, int bits, std::vector<double>& levels) {
   const int n = 1 << bits;
-  const double sigma2 = 1.0 / d;
-  const double sigma = std::sqrt(sigma2);
+  const double var = 1.0 / d;
+  const double sigma = std::sqrt(var);
+  const double outer = kPageOuterSigmas * sigma;
   const double lo = -3.5 * sigma, hi = 3.5 * sigma;
-  c.assign(n, 0.0);
-  for (int i = 0; i < n; ++i) c[i] = lo + (hi - lo) * (i + 0.5) / n;
-  std::vector<double> nc(n), edges(n + 1);
-  for (int it = 0; it < 200; ++it) {
-    edges[0] = lo * 3;
-    edges[n] = hi * 3;
-    for (int i = 0; i + 1 < n; ++i) edges[i + 1] = (c[i] + c[i + 1]) / 2.0;
-    double delta = 0.0;
+  levels.assign(n, 0.0);
+  for (int i = 0; i < n; ++i) levels[i] = lo + (hi - lo) * (i + 0.5) / n;
+  std::vector<double> bounds(n + 1), means(n);
+  for (int it = 0; it < kPageMaxIter; ++it) {
+    bounds[0] = -outer;
+    bounds[n] = outer;
+    for (int i = 1; i < n; ++i) bounds[i] = (levels[i - 1] + levels[i]) / 2.0;
+    double moved = 0.0;
     for (int i = 0; i < n; ++i) {
-      const double a = edges[i], b = edges[i + 1];
-      const double num = trapz200([&](double x) { return x * page_pdf(x, sigma2); }, a, b);
-      const double den = trapz200([&](double x) { return page_pdf(x, sigma2); }, a, b);
-      nc[i] = den > 1e-15 ? num / den : c[i];
-      delta = std::fmax(delta, std::fabs(nc[i] - c[i]));
+      double mass, first;
+      trapezoid_cell_moments(bounds[i], bounds[i + 1], var, mass, first);
+      means[i] = first / mass;          // every cell has positive mass here
+      moved = std::fmax(moved, std::fabs(means[i] - levels[i]));
     }
-    if (delta < 1e-10) break;
-    c.swap(nc);
+    if (moved < kPageTol) return;
+    levels.swap(means);
   }
 }
 

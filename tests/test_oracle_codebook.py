@@ -156,3 +156,28 @@ def test_beta_codebook_lower_mse_than_gaussian_on_sphere():
         g, _ = cb.lloyd_max_exact(128, bits)
         b, _ = cb.lloyd_max_beta(128, bits)
         assert cb.beta_mse_per_coord(b, 128) < cb.beta_mse_per_coord(g, 128)
+
+
+def test_page_recipe_levels_near_the_printed_table():
+    """The page's recipe lands within its own quadrature bias (200 panels over
+    cells reaching +-10.5 sigma) of the levels the page prints: 3e-4."""
+    g = load_golden("codebook_d128_page.json")
+    for bits in (3, 4):
+        lt, _, _ = cb.lloyd_max_page_trapz(g["head_dim"], bits)
+        pos = lt[len(lt) // 2:]
+        assert np.max(np.abs(pos - np.array(g["positive_levels"][str(bits)]))) < 3e-4
+
+
+@pytest.mark.parametrize("a,b", [(-10.5, -2.0), (-0.3, 0.7), (1.1, 10.5)])
+def test_trapezoid_cell_moments_within_the_rule_error_bound(a, b):
+    """The composite trapezoid rule against the closed forms of a Gaussian
+    cell's mass and first moment, within the rule's bound (b - a) h^2 / 12
+    max|f''| (f'' of the density and of x times the density are below
+    0.5 and 0.8 over R for unit variance)."""
+    var = 1.0
+    mass, first = cb.trapezoid_cell_moments(a, b, var)
+    want_mass = 0.5 * (math.erf(b / math.sqrt(2)) - math.erf(a / math.sqrt(2)))
+    want_first = (math.exp(-a * a / 2) - math.exp(-b * b / 2)) / math.sqrt(2 * math.pi)
+    h = (b - a) / cb.PAGE_PANELS
+    assert abs(mass - want_mass) <= (b - a) * h * h / 12 * 0.5
+    assert abs(first - want_first) <= (b - a) * h * h / 12 * 0.8

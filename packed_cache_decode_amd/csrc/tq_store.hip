@@ -48,7 +48,14 @@ constexpr int kWaves = 4;
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
 // binary32 -> binary16, round to nearest even (v_cvt_f16_f32 in the default mode)
+// binary32 -> binary16, round to nearest even, of x as a binary32 value: the
+// empty asm makes x a finished binary32 result, so the compiler cannot fuse
+// the conversion with the multiply that produced x into one rounding straight
+// to binary16 (v_fma_mixlo_f16), which differs from the contract's two
+// roundings when the binary32 product sits exactly halfway between two
+// binary16 values
 __device__ __forceinline__ uint16_t f32_to_f16_bits(float x) {
+  asm volatile("" : "+v"(x));
   return __builtin_bit_cast(uint16_t, static_cast<_Float16>(x));
 }
 

@@ -25,6 +25,7 @@ import os
 import numpy as np
 
 from oracle import codebook as cb
+from oracle import fpfmt
 from oracle import decode as odec
 from oracle import haar, layout, rotation
 from oracle import soa as osoa
@@ -227,10 +228,19 @@ def compare_store(got, want, k_rows_of, v_rows_of, slot_rows, lay, signs, centro
             w16 = w2[:, o].astype(np.uint16) | (w2[:, o + 1].astype(np.uint16) << 8)
             _, nrm, _ = ost.quantize_k_contract(kb, signs, midpoints)
             alt = tie_alternative_codes(y64, wc, midpoints, kd)
-            from oracle import fpfmt
             a16 = fpfmt.f32_to_f16_bits(osoa.folded_norm_contract(alt, nrm, centroids))
             ok = (g16 == w16) | ((g16 == a16) & kd.any(axis=1))
-            assert ok.all(), f"{int((~ok).sum())} folded norms differ from the oracle's"
+            if not ok.all():
+                bad = np.nonzero(~ok)[0][:6]
+                c64 = np.asarray(centroids, np.float64)[wc[bad]]
+                exact = nrm[bad].astype(np.float64) / np.sqrt((c64 * c64).sum(axis=-1) + 1e-16)
+                detail = [dict(gpu=float(fpfmt.f16_bits_to_f64(g16[i])),
+                               oracle=float(fpfmt.f16_bits_to_f64(w16[i])),
+                               fold_f32=float(osoa.folded_norm_contract(wc[i], nrm[i], centroids)),
+                               f64=float(e), codes_differ=bool(kd[i].any()))
+                          for i, e in zip(bad, exact)]
+                raise AssertionError(f"{int((~ok).sum())} of {len(ok)} folded norms differ from "
+                                     f"the oracle's: {detail}")
     o = lay.off_value
     gv = ost.unpack_codes(g2[:, o:o + lay.value_code_bytes], lay.value_bits, d)
     wv = ost.unpack_codes(w2[:, o:o + lay.value_code_bytes], lay.value_bits, d)

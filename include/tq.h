@@ -273,6 +273,29 @@ tq_status tq_decode(const tq_ctx* ctx, const void* q, const uint8_t* cache, int6
                     int batch, int num_q_heads, int max_seq_len, float sm_scale, void* out,
                     int out_is_fp32, void* workspace, size_t workspace_bytes, void* stream);
 
+/* tq_decode_noalloc -- tq_decode for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same operation, kernels and results (bit for bit,
+ * with the same decode options), with the split partials kept in the
+ * library's own scratch array instead of a caller workspace.
+ *
+ * The array is a file-scope device array of tq_decode_noalloc_max_bytes()
+ * bytes (32 MiB); each GPU the library runs on holds its own copy until the
+ * process ends.  A shape whose plan needs more scratch than that returns
+ * TQ_ERR_WORKSPACE before anything is enqueued.  The call allocates nothing
+ * and synchronises nothing.  Every call on a GPU shares that GPU's array,
+ * which keeps the last call's partials: calls that overlap on one GPU (two
+ * streams, or two host threads) race and give wrong results.  The partials
+ * need no initialisation.  Arguments and errors otherwise as tq_decode. */
+tq_status tq_decode_noalloc(const tq_ctx* ctx, const void* q, const uint8_t* cache,
+                            int64_t num_blocks, const int32_t* block_table, int max_blocks_per_seq,
+                            const int32_t* seq_lens, int batch, int num_q_heads, int max_seq_len,
+                            float sm_scale, void* out, int out_is_fp32, void* stream);
+
+/* Bytes of the scratch array tq_decode_noalloc uses (the largest workspace
+ * it accepts). */
+size_t tq_decode_noalloc_max_bytes(void);
+
 /* tq_dequant -- P1, section "反量化 kernel:_tq_full_dequant_kv".
  *
  * Expand the first seq_len tokens of one sequence back into K and V vectors

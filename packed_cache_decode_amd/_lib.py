@@ -32,7 +32,8 @@ class DecodeOptions(ctypes.Structure):
 EXPORTS = ("tq_codebook_init", "tq_codebook_init_layout", "tq_layout_of", "tq_destroy", "tq_slot_bytes", "tq_cache_bytes", "tq_get_tables",
            "tq_store", "tq_decode_workspace_bytes", "tq_decode", "tq_dequant",
            "tq_continuation_workspace_bytes", "tq_decode_continuation", "tq_get_device_error",
-           "tq_set_decode_options", "tq_get_decode_options",
+           "tq_set_decode_options", "tq_get_decode_options", "tq_decode_noalloc",
+           "tq_decode_noalloc_max_bytes",
            "tq_host_codebook", "tq_host_rotation_signs", "tq_host_haar_matrix", "tq_host_slot_bytes",
            "tq_status_str")
 # every symbol include/tq_probe.h declares (measurement helpers)
@@ -77,6 +78,9 @@ def load():
         "tq_decode_workspace_bytes": (ctypes.c_size_t, [_vp, _int, _int, _int]),
         "tq_decode": (_int, [_vp, _vp, _vp, _i64, _vp, _int, _vp, _int, _int, _int, ctypes.c_float,
                              _vp, _int, _vp, ctypes.c_size_t, _vp]),
+        "tq_decode_noalloc": (_int, [_vp, _vp, _vp, _i64, _vp, _int, _vp, _int, _int, _int,
+                                     ctypes.c_float, _vp, _int, _vp]),
+        "tq_decode_noalloc_max_bytes": (ctypes.c_size_t, []),
         "tq_dequant": (_int, [_vp, _vp, _i64, _vp, _int, _int, _vp, _vp, _int, _vp]),
         "tq_continuation_workspace_bytes": (ctypes.c_size_t, [_vp, _int, _int, _int, _int]),
         "tq_decode_continuation": (_int, [_vp, _vp, _vp, _i64, _vp, _int, _int, _int, _int, ctypes.c_float,
@@ -207,6 +211,19 @@ def tq_decode(ctx, q, cache, num_blocks, block_table, max_blocks_per_seq, seq_le
                                          max_blocks_per_seq, _ptr(seq_lens), batch, num_q_heads,
                                          max_seq_len, float(sm_scale), _ptr(out), int(out_is_fp32),
                                          _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+def tq_decode_noalloc(ctx, q, cache, num_blocks, block_table, max_blocks_per_seq, seq_lens, batch,
+                      num_q_heads, max_seq_len, sm_scale, out, out_is_fp32, stream=None):
+    _check("tq_decode_noalloc",
+           load().tq_decode_noalloc(ctx, _ptr(q), _ptr(cache), num_blocks, _ptr(block_table),
+                                    max_blocks_per_seq, _ptr(seq_lens), batch, num_q_heads,
+                                    max_seq_len, float(sm_scale), _ptr(out), int(out_is_fp32),
+                                    _stream(stream)))
+
+
+def tq_decode_noalloc_max_bytes():
+    return load().tq_decode_noalloc_max_bytes()
 
 
 def tq_dequant(ctx, cache, num_blocks, block_table_row, max_blocks, seq_len, k_out, v_out, out_is_fp32,

@@ -15,6 +15,7 @@
 #include <cstring>
 #include <new>
 #include <limits>
+#include <mutex>
 #include <vector>
 
 #include "tq_internal.h"
@@ -37,9 +38,37 @@ struct tq_ctx {
   DevErrors* d_errs;                // sticky error words, written by the kernels
   float* d_rot;                     // Haar rotation matrix (device), or null
   tq_decode_options opts;           // decode plan options (tq_set_decode_options)
+  void* scratch;                    // this device's allocation-free decode scratch
 };
 
+// ---- scratch of the allocation-free decode --------------------------------
+// tq_decode_noalloc keeps its split partials in this file-scope device array
+// instead of a caller workspace: each GPU the library runs on holds its own
+// copy until the process ends.  In host code the array's name is not a device
+// address; the address of a device's copy comes from hipGetSymbolAddress,
+// taken once per device with that device current (in tq_codebook_init), and
+// only that address is passed to kernels.
+constexpr size_t kNoAllocScratchBytes = size_t{32} << 20;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
 namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// this device's copy of the scratch array (the device must be current);
+// null if its address cannot be taken
+void* noalloc_scratch(int device) {
+  if (device < 0 || device >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[device] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    g_scratch_ptr[device] = p;
+  }
+  return g_scratch_ptr[device];
+}
 
 // ---- Lloyd-Max for N(0, sigma^2) ------------------------------------------
 // Fixed point of the two optimality conditions: boundaries at midpoints of
@@ -453,6 +482,45 @@ int slot_bytes_for(int preset, int d) {
 
 }  // namespace
 
+namespace {
+// tq_decode's checks, plan and launch, with the split partials in
+// `workspace` (workspace_bytes long): the caller's buffer, or the
+// allocation-free entry point's scratch array
+tq_status decode_impl(const tq_ctx* ctx, const void* q, const uint8_t* cache, int64_t num_blocks,
+                    const int32_t* block_table, int max_blocks_per_seq, const int32_t* seq_lens,
+                    int batch, int num_q_heads, int max_seq_len, float sm_scale, void* out,
+                    int out_is_fp32, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!ctx) return TQ_ERR_INVALID_ARG;
+  const Geometry& g = ctx->geo;
+  if (batch < 0 || num_q_heads <= 0 || max_seq_len < 0 || num_blocks < 0 ||
+      max_blocks_per_seq < 0)
+    return TQ_ERR_INVALID_ARG;
+  if (num_q_heads % g.num_kv_heads != 0) return TQ_ERR_INVALID_ARG;
+  const int G = num_q_heads / g.num_kv_heads;
+  if (G > 16) return TQ_ERR_UNSUPPORTED;
+  if (batch == 0) return TQ_OK;
+  if (!q || !cache || !block_table || !seq_lens || !out) return TQ_ERR_INVALID_ARG;
+  if (static_cast<int64_t>(max_blocks_per_seq) * g.block_size < max_seq_len)
+    return TQ_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(cache, 16) || !aligned(out, 16) || !aligned(block_table, 4) ||
+      !aligned(seq_lens, 4))
+    return TQ_ERR_ALIGNMENT;
+  tq::DecodePlan plan = tq::plan_decode(g, ctx->opts, batch, num_q_heads, max_seq_len);
+  if (plan.workspace_bytes > 0) {
+    if (!workspace || workspace_bytes < plan.workspace_bytes) return TQ_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return TQ_ERR_ALIGNMENT;
+  }
+  tq_status ds = check_device(ctx);
+  if (ds != TQ_OK) return ds;
+  if (!(sm_scale > 0.0f)) sm_scale = 1.0f / std::sqrt(static_cast<float>(g.head_dim));
+  hipError_t e = tq::launch_decode(g, ctx->d_tables, ctx->d_errs, plan, static_cast<const uint16_t*>(q), cache,
+                                   num_blocks, block_table, max_blocks_per_seq, seq_lens, batch,
+                                   num_q_heads, sm_scale, out, out_is_fp32, workspace,
+                                   static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? TQ_OK : TQ_ERR_HIP;
+}
+}  // namespace
+
 extern "C" {
 
 tq_status tq_host_codebook(int head_dim, int bits, int codebook_mode, float* centroids_host,
@@ -581,6 +649,11 @@ tq_status tq_codebook_init_layout(tq_ctx** out, int preset, int head_dim, int nu
     delete c;
     return TQ_ERR_NO_DEVICE;
   }
+  c->scratch = noalloc_scratch(c->device);
+  if (c->scratch == nullptr) {
+    delete c;
+    return TQ_ERR_HIP;
+  }
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (g.haar) {
     std::vector<float> q32;
@@ -682,35 +755,24 @@ tq_status tq_decode(const tq_ctx* ctx, const void* q, const uint8_t* cache, int6
                     const int32_t* block_table, int max_blocks_per_seq, const int32_t* seq_lens,
                     int batch, int num_q_heads, int max_seq_len, float sm_scale, void* out,
                     int out_is_fp32, void* workspace, size_t workspace_bytes, void* stream) {
-  if (!ctx) return TQ_ERR_INVALID_ARG;
-  const Geometry& g = ctx->geo;
-  if (batch < 0 || num_q_heads <= 0 || max_seq_len < 0 || num_blocks < 0 ||
-      max_blocks_per_seq < 0)
-    return TQ_ERR_INVALID_ARG;
-  if (num_q_heads % g.num_kv_heads != 0) return TQ_ERR_INVALID_ARG;
-  const int G = num_q_heads / g.num_kv_heads;
-  if (G > 16) return TQ_ERR_UNSUPPORTED;
-  if (batch == 0) return TQ_OK;
-  if (!q || !cache || !block_table || !seq_lens || !out) return TQ_ERR_INVALID_ARG;
-  if (static_cast<int64_t>(max_blocks_per_seq) * g.block_size < max_seq_len)
-    return TQ_ERR_INVALID_ARG;
-  if (!aligned(q, 16) || !aligned(cache, 16) || !aligned(out, 16) || !aligned(block_table, 4) ||
-      !aligned(seq_lens, 4))
-    return TQ_ERR_ALIGNMENT;
-  tq::DecodePlan plan = tq::plan_decode(g, ctx->opts, batch, num_q_heads, max_seq_len);
-  if (plan.workspace_bytes > 0) {
-    if (!workspace || workspace_bytes < plan.workspace_bytes) return TQ_ERR_WORKSPACE;
-    if (!aligned(workspace, 256)) return TQ_ERR_ALIGNMENT;
-  }
-  tq_status ds = check_device(ctx);
-  if (ds != TQ_OK) return ds;
-  if (!(sm_scale > 0.0f)) sm_scale = 1.0f / std::sqrt(static_cast<float>(g.head_dim));
-  hipError_t e = tq::launch_decode(g, ctx->d_tables, ctx->d_errs, plan, static_cast<const uint16_t*>(q), cache,
-                                   num_blocks, block_table, max_blocks_per_seq, seq_lens, batch,
-                                   num_q_heads, sm_scale, out, out_is_fp32, workspace,
-                                   static_cast<hipStream_t>(stream));
-  return e == hipSuccess ? TQ_OK : TQ_ERR_HIP;
+  return decode_impl(ctx, q, cache, num_blocks, block_table, max_blocks_per_seq, seq_lens, batch,
+                     num_q_heads, max_seq_len, sm_scale, out, out_is_fp32, workspace,
+                     workspace_bytes, stream);
 }
+
+tq_status tq_decode_noalloc(const tq_ctx* ctx, const void* q, const uint8_t* cache,
+                            int64_t num_blocks, const int32_t* block_table, int max_blocks_per_seq,
+                            const int32_t* seq_lens, int batch, int num_q_heads, int max_seq_len,
+                            float sm_scale, void* out, int out_is_fp32, void* stream) {
+  if (!ctx) return TQ_ERR_INVALID_ARG;
+  // the scratch array is the workspace: a plan that needs more is refused
+  // before anything is enqueued (decode_impl checks the size)
+  return decode_impl(ctx, q, cache, num_blocks, block_table, max_blocks_per_seq, seq_lens, batch,
+                     num_q_heads, max_seq_len, sm_scale, out, out_is_fp32, ctx->scratch,
+                     kNoAllocScratchBytes, stream);
+}
+
+size_t tq_decode_noalloc_max_bytes(void) { return kNoAllocScratchBytes; }
 
 tq_status tq_dequant(const tq_ctx* ctx, const uint8_t* cache, int64_t num_blocks,
                      const int32_t* block_table_row, int max_blocks, int seq_len, void* k_out,

@@ -224,6 +224,10 @@ def main():
     ap.add_argument("--decode-kernel", default="",
                     choices=["", "ring", "page", "staged", "direct"],
                     help="force a decode kernel where it applies (default: chosen by shape)")
+    ap.add_argument("--page-heads", type=int, default=0, choices=[0, 1, 2, 4],
+                    help="page decode: kv heads per workgroup (default: the whole row, at most 8)")
+    ap.add_argument("--ring-waves", type=int, default=0, choices=[0, 8, 16],
+                    help="ring decode: wavefronts per workgroup (default: chosen by shape)")
     ap.add_argument("--dynamic-claims", action="store_true",
                     help="ring decode: wavefronts claim slabs from a counter (not reproducible "
                          "bit for bit)")
@@ -260,7 +264,8 @@ def main():
     sm, bt, sl = up(inp.slot_mapping), up(inp.block_table), up(inp.seq_lens)
     tq = PackedKVCache(w.preset, w.head_dim, w.num_kv_heads, w.block_size, rot_seed=2024,
                        device=dev, layout=args.layout)
-    tq.set_decode_options(kernel=args.decode_kernel, dynamic_claims=args.dynamic_claims)
+    tq.set_decode_options(kernel=args.decode_kernel, dynamic_claims=args.dynamic_claims,
+                          ring_waves=args.ring_waves, page_heads=args.page_heads)
     cache = tq.new_cache(inp.num_blocks)
     max_len = int(inp.seq_lens.max())
     out = torch.empty((w.batch, w.num_q_heads, w.head_dim), dtype=torch.bfloat16, device=dev)

@@ -10,22 +10,40 @@
 // (code * scale + zero), "在线 softmax" and "读取内核" (split partials,
 // log-sum-exp merge).
 //
-// Mapping.  A workgroup is one wavefront for one (split, sequence, kv head).
-// It walks the split 16 tokens at a time (a slab: 16 rows of a page) with
-// MFMA contractions:
+// Kernels.  Four kernels walk a split's keys 16 tokens at a time (a slab:
+// 16 rows of a page); they differ in how the slab's bytes reach the lanes,
+// and each section below states its mapping:
+//   direct  (decode_slab_kernel)    one wavefront per (split, sequence, kv
+//           head); every lane buffer-loads exactly its operand bytes
+//   staged  (decode_staged_kernel)  the same wavefronts; 16-byte loads of the
+//           head's row span, parked in a private LDS buffer
+//   page    (decode_page_kernel)    one workgroup per (sequence, split), one
+//           wavefront per kv head of a row group; whole slabs into an LDS
+//           ring by non-temporal loads that write LDS directly (FP8 keys)
+//   ring    (decode_ring_kernel)    one workgroup per (sequence, kv head,
+//           split); every wavefront claims slabs and streams them into its
+//           own LDS ring (3/4-bit keys, slotted and split pages)
+// decode_merge_kernel merges the split partials by log-sum-exp (a fused
+// last-workgroup merge needs a device-scope release in every workgroup,
+// which on this part costs far more than a launch).
+//
+// Contractions, 16x16 MFMA tiles:
 //   scores  S[t][h] = sum_c C[t][c] Q[h][c]     v_mfma_f32_16x16x32_f16 / _bf16
-//   norms   N[t][t] = sum_c C[t][c] C[t][c]     (diagonal of C C^T, MSE keys)
-//   values  O[h][c] += sum_t W[h][t] V[t][c]    v_mfma_f32_16x16x16_f16 (W as f16 hi + lo)
+//   norms   N[t][t] = sum_c C[t][c] C[t][c]     diagonal of C C^T (MSE keys)
+//   values  O[h][c] += sum_t W[h][t] V[t][c]    v_mfma_f32_16x16x32_f16
 // For MSE keys C are the centroids of the slab's K codes, looked up per code
-// byte (two codes) in an LDS table; f16 alone is not precise enough for the
-// scores (outlier keys make them large), so C and Q are carried as f16 hi +
-// lo pairs (lo scaled by 2^11 to stay normal): the score uses Chi.Qhi +
-// Chi.Qlo + 2^-11 Clo.Qhi and the norm Chi.Chi + 2^-10 Chi.Clo.  FP8 keys
-// convert exactly to bf16 and meet the bf16 query directly.  Q holds the
-// (rotated) queries, rows >= G zero; W = p * scale and V the integer V codes,
-// exact in f16.  The per-token term zero * p and the softmax sums stay in
-// fp32.  The running maximum is lazy: the accumulators are rescaled only
-// when a head's maximum grows by more than kLazy (base 2), so p <= 2^kLazy.
+// byte (two codes) in an LDS table.  f16 alone is not precise enough for the
+// scores (centroids rounded to f16 move the decode output by up to 2.7e-3
+// on outlier-channel keys), so centroids and rotated queries are carried as
+// f16 hi + lo pairs; the table and operand layouts of each kernel are given
+// with it.  FP8 keys convert exactly to bf16 and meet the bf16 query
+// directly.  Q holds the (rotated) queries, rows >= G zero.  V operands are
+// the integer codes as f16 subnormals (code * 2^-24, exact), W = p * scale
+// as an f16 hi + lo pair in one operand; kVScale undoes the 2^-24 when the
+// accumulators are written out.  The per-token term zero * p and the
+// softmax sums stay in fp32.  The running maximum is lazy: the accumulators
+// are rescaled only when a head's maximum grows by more than kLazy (base 2),
+// so p <= 2^kLazy.
 //
 // Layouts (lane l, row r16 = l % 16, group g4 = l / 16):
 //   A operand  : row r16, k = [8*g4, 8*g4+8) (x32) or [4*g4, 4*g4+4) (x16)
@@ -34,16 +52,9 @@
 // Coordinates are permuted so each lane reads contiguous bytes: score MFMA
 // kk in group g4 covers coordinates 32*g4 + 8*kk + [0, 8); value tile m,
 // column j covers coordinate 8*j + m.
-//
-// Loads.  Each lane fetches exactly its operand bytes with buffer loads
-// (K bytes of one token; V codes, norm, scale and zero of four tokens).
-// Slots of 134 / 118 bytes leave rows only 2-byte aligned; the loads are
-// unaligned, which the memory path serves.  The buffer range of a slab
-// covers its 16 rows; a slab past the split end or on a bad page gets an
-// empty range, so every step issues the same loads and the compiler's waits
-// cover one slab.  A second small kernel merges the splits (a fused
-// last-workgroup merge needs a device-scope release in every workgroup,
-// which on this part costs far more than a launch).
+#include <cstddef>
+
+
 #include "tq_internal.h"
 
 namespace tq {
@@ -329,41 +340,35 @@ constexpr int vbits_of_slot(int slot) { return slot == 102 ? 3 : 4; }
 
 // MFMA B operands of the V codes of tokens 4*g4 + r (X[r]: the token's codes
 // of coordinates 8*r16 .. 8*r16 + 7) for coordinates 8*r16 + 2*kb (Blo) and
-// 8*r16 + 2*kb + 1 (Bhi), as exact f16 integers: code c becomes the f16 with
-// bits 0x6400 | c (1024 + c) minus 1024, and for the high nibble of a 4-bit
-// byte 0x5400 | (c << 4) (64 + c) minus 64
+// 8*r16 + 2*kb + 1 (Bhi).  A code c (0 .. 15) placed in the low bits of a
+// 16-bit lane is the f16 subnormal c * 2^-24, exactly, so the operands are
+// the codes themselves moved into place; the matrix cores multiply
+// subnormal inputs exactly, and the accumulated P.V carries the factor
+// 2^-24, which kVScale undoes when the accumulators are written out.
+constexpr float kVScale = 16777216.0f;       // 2^24
 template <int VB>
 __device__ __forceinline__ void v_operands(const uint32_t (&X)[4], int kb, h4& Blo, h4& Bhi) {
-  const h2 b1024 = {static_cast<_Float16>(1024.0f), static_cast<_Float16>(1024.0f)};
   if constexpr (VB == 4) {
-    const h2 b64 = {static_cast<_Float16>(64.0f), static_cast<_Float16>(64.0f)};
-    // byte kb of each token's dword -> [x0, 0, x1, 0]
+    // byte kb of each token's dword -> [x0, 0, x1, 0]; low nibbles by a mask,
+    // high nibbles by a packed 16-bit shift
+    typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
     const uint32_t sel = kb | (0x0Cu << 8) | ((4u + kb) << 16) | (0x0Cu << 24);
     const uint32_t p01 = __builtin_amdgcn_perm(X[1], X[0], sel);
     const uint32_t p23 = __builtin_amdgcn_perm(X[3], X[2], sel);
-    h2 lo01 = __builtin_bit_cast(h2, insert_bits(p01, 0x000F000Fu, 0x64006400u));
-    h2 lo23 = __builtin_bit_cast(h2, insert_bits(p23, 0x000F000Fu, 0x64006400u));
-    h2 hi01 = __builtin_bit_cast(h2, insert_bits(p01, 0x00F000F0u, 0x54005400u));
-    h2 hi23 = __builtin_bit_cast(h2, insert_bits(p23, 0x00F000F0u, 0x54005400u));
-    lo01 -= b1024;
-    lo23 -= b1024;
-    hi01 -= b64;
-    hi23 -= b64;
-    Blo = h4{lo01[0], lo01[1], lo23[0], lo23[1]};
-    Bhi = h4{hi01[0], hi01[1], hi23[0], hi23[1]};
+    const uint32_t lo01 = p01 & 0x000F000Fu, lo23 = p23 & 0x000F000Fu;
+    const uint32_t hi01 = __builtin_bit_cast(uint32_t, __builtin_bit_cast(u16x2, p01) >> (uint16_t)4);
+    const uint32_t hi23 = __builtin_bit_cast(uint32_t, __builtin_bit_cast(u16x2, p23) >> (uint16_t)4);
+    Blo = __builtin_bit_cast(h4, (u32x2{lo01, lo23}));
+    Bhi = __builtin_bit_cast(h4, (u32x2{hi01, hi23}));
   } else {
     // 3-bit codes: code m of a token at bits [3m, 3m + 3) of its X
     const uint32_t m0 = 6 * kb, m1 = 6 * kb + 3;
-    h2 lo01 = __builtin_bit_cast(h2, __builtin_amdgcn_ubfe(X[0], m0, 3) | (__builtin_amdgcn_ubfe(X[1], m0, 3) << 16) | 0x64006400u);
-    h2 lo23 = __builtin_bit_cast(h2, __builtin_amdgcn_ubfe(X[2], m0, 3) | (__builtin_amdgcn_ubfe(X[3], m0, 3) << 16) | 0x64006400u);
-    h2 hi01 = __builtin_bit_cast(h2, __builtin_amdgcn_ubfe(X[0], m1, 3) | (__builtin_amdgcn_ubfe(X[1], m1, 3) << 16) | 0x64006400u);
-    h2 hi23 = __builtin_bit_cast(h2, __builtin_amdgcn_ubfe(X[2], m1, 3) | (__builtin_amdgcn_ubfe(X[3], m1, 3) << 16) | 0x64006400u);
-    lo01 -= b1024;
-    lo23 -= b1024;
-    hi01 -= b1024;
-    hi23 -= b1024;
-    Blo = h4{lo01[0], lo01[1], lo23[0], lo23[1]};
-    Bhi = h4{hi01[0], hi01[1], hi23[0], hi23[1]};
+    const uint32_t lo01 = __builtin_amdgcn_ubfe(X[0], m0, 3) | (__builtin_amdgcn_ubfe(X[1], m0, 3) << 16);
+    const uint32_t lo23 = __builtin_amdgcn_ubfe(X[2], m0, 3) | (__builtin_amdgcn_ubfe(X[3], m0, 3) << 16);
+    const uint32_t hi01 = __builtin_amdgcn_ubfe(X[0], m1, 3) | (__builtin_amdgcn_ubfe(X[1], m1, 3) << 16);
+    const uint32_t hi23 = __builtin_amdgcn_ubfe(X[2], m1, 3) | (__builtin_amdgcn_ubfe(X[3], m1, 3) << 16);
+    Blo = __builtin_bit_cast(h4, (u32x2{lo01, lo23}));
+    Bhi = __builtin_bit_cast(h4, (u32x2{hi01, hi23}));
   }
 }
 
@@ -585,8 +590,10 @@ __device__ __forceinline__ void store_partials(const MfmaArgs& a, int b, int g, 
     if (h < G) {
       float* rec = a.part + (rec0 + static_cast<int64_t>(h) * a.num_splits) * kRec;
       // tile m column r16 is coordinate 8*r16 + m
-      *reinterpret_cast<float4*>(rec + 8 * r16) = make_float4(st.O[0][r], st.O[1][r], st.O[2][r], st.O[3][r]);
-      *reinterpret_cast<float4*>(rec + 8 * r16 + 4) = make_float4(st.O[4][r], st.O[5][r], st.O[6][r], st.O[7][r]);
+      *reinterpret_cast<float4*>(rec + 8 * r16) = make_float4(
+          st.O[0][r] * kVScale, st.O[1][r] * kVScale, st.O[2][r] * kVScale, st.O[3][r] * kVScale);
+      *reinterpret_cast<float4*>(rec + 8 * r16 + 4) = make_float4(
+          st.O[4][r] * kVScale, st.O[5][r] * kVScale, st.O[6][r] * kVScale, st.O[7][r] * kVScale);
     }
   }
   if (g4 == 0 && r16 < G) {
@@ -1053,15 +1060,18 @@ __global__ void __launch_bounds__(64, kStagedWavesPerSimd<KB>) decode_staged_ker
 // allocate in the caches sustain about twice the read rate of plain loads on
 // MI355X.  Every wavefront then takes its own head's operands from LDS.
 //
-// The centroid table holds hi = f16(c) and lo = f16(2 (c - hi)), the queries
-// qhi = f16(q) and qlo = f16(q - qhi).  With at most 8 query heads per kv
-// head one B operand carries both query parts: column h < 8 holds qhi of head
-// h and column h + 8 its qlo, so hi.Q gives hi.qhi in column h and hi.qlo in
-// column h + 8 (added back across the row), and lo.Q gives lo.qhi: the score
-// hi.qhi + hi.qlo + lo.qhi / 2 = c.q to about 2^-20.  One norm accumulator
-// takes hi.hi + hi.lo = sum c^2 to the same order.  The norm factor n / ||c||
-// of a token is computed once, in the lane that holds its diagonal element,
-// and handed to the lanes of its rows by ds_bpermute.
+// The centroid table holds hi = f16(c) and lo = f16(c - hi) for 4-bit keys
+// (lo often subnormal; the matrix cores take subnormal inputs exactly) and
+// lo = f16(2 (c - hi)) for 3-bit keys; the queries qhi = f16(q) and qlo =
+// f16(q - qhi).  With at most 8 query heads per kv head one B operand
+// carries both query parts: column h < 8 holds qhi of head h and column
+// h + 8 its qlo, so hi.Q gives hi.qhi in column h and hi.qlo in column h + 8
+// (added back across the row), and lo.Q gives lo.qhi: the score c.q to
+// about 2^-20.  The norm takes hi.hi + 2 hi.lo = sum c^2 to the same order.
+// The norm factor n / ||c|| of a token is computed once, in the lane that
+// holds its diagonal element, and spread to the tile rows by one f32 MFMA
+// (rows_to_tile).  4-bit keys here take score4 (below), whose A operands
+// hold hi and lo side by side against duplicated queries.
 // ============================================================================
 
 constexpr int kMaxChunkSlabs = 256;          // slabs (and pages) of one split
@@ -1127,7 +1137,7 @@ struct PageGeom {
 
 // centroid tables (2 KB): entry e covers the codes e & (2^KB - 1) and
 // e >> KB.  4-bit keys: {pair of hi parts, pair of lo parts} at 8-byte entry
-// e, one lookup per code byte.  3-bit keys: the pair of hi parts at word e
+// e, one lookup per code byte, lo = c - hi.  3-bit keys: the pair of hi parts at word e
 // and the pair of lo parts at word 256 + e, two lookups from one address
 // that land directly in the hi and lo MFMA operands (no register moves);
 // their 64 entries fill one row of banks, so the lookups never conflict,
@@ -1140,11 +1150,15 @@ __device__ __forceinline__ void build_tables_page(const MfmaArgs& a, u32x2* tab)
     const int c0 = e & ((1 << KB) - 1), c1 = e >> KB;
     const float v0 = a.tables->centroids[c0], v1 = a.tables->centroids[c1];
     const _Float16 h0 = static_cast<_Float16>(v0), h1 = static_cast<_Float16>(v1);
-    const _Float16 l0 = static_cast<_Float16>(2.0f * (v0 - static_cast<float>(h0)));
-    const _Float16 l1 = static_cast<_Float16>(2.0f * (v1 - static_cast<float>(h1)));
     if constexpr (KB == 4) {
+      // lo = c - hi unscaled (subnormal for the small levels; the matrix
+      // cores and v_dot2 take subnormal inputs exactly)
+      const _Float16 l0 = static_cast<_Float16>(v0 - static_cast<float>(h0));
+      const _Float16 l1 = static_cast<_Float16>(v1 - static_cast<float>(h1));
       tab[e] = u32x2{pack_h2(h0, h1), pack_h2(l0, l1)};
     } else {
+      const _Float16 l0 = static_cast<_Float16>(2.0f * (v0 - static_cast<float>(h0)));
+      const _Float16 l1 = static_cast<_Float16>(2.0f * (v1 - static_cast<float>(h1)));
       t32[e] = pack_h2(h0, h1);
       t32[256 + e] = pack_h2(l0, l1);
     }
@@ -1324,6 +1338,11 @@ __device__ __forceinline__ ScoreAcc slab_mfma(const SlabRegs<KB>& R, const h8 (&
   return A;
 }
 
+// weight of the Clo . q products: the 4-bit table holds lo = c - hi, the
+// 3-bit table 2 (c - hi)
+template <int KB>
+__device__ __forceinline__ constexpr float lo_weight() { return KB == 4 ? 1.0f : 0.5f; }
+
 // scores (base 2) of the slab from its MFMA results; rows at or past
 // valid_rows score -inf
 template <int KB, bool FULL>
@@ -1334,8 +1353,9 @@ __device__ __forceinline__ void slab_tail(const SlabRegs<KB>& R, const ScoreAcc&
     for (int r = 0; r < 4; ++r) s[r] = (FULL || 4 * g4 + r < valid_rows) ? A.S[r] * scale_log2 : -INFINITY;
   } else {
     // lane (r16, g4) with r16 = 4*g4 + i holds N[4*g4 + i][4*g4 + i] as element i
-    const float n0 = A.Nh[0] + A.Nx[0], n1 = A.Nh[1] + A.Nx[1];
-    const float n2 = A.Nh[2] + A.Nx[2], n3 = A.Nh[3] + A.Nx[3];
+    constexpr float kx = KB == 4 ? 2.0f : 1.0f;   // Nx = hi . lo (4-bit) or hi . 2 lo
+    const float n0 = A.Nh[0] + kx * A.Nx[0], n1 = A.Nh[1] + kx * A.Nx[1];
+    const float n2 = A.Nh[2] + kx * A.Nx[2], n3 = A.Nh[3] + kx * A.Nx[3];
     const float nd = sel2 ? (sel1 ? n3 : n2) : (sel1 ? n1 : n0);
     const float fq = f16_bits_to_f32(R.nb) * __builtin_amdgcn_rsqf(nd);
     const f4 fac = rows_to_tile(fq, diag);
@@ -1345,8 +1365,129 @@ __device__ __forceinline__ void slab_tail(const SlabRegs<KB>& R, const ScoreAcc&
       // r16 >= 8 get a copy of head r16 - 8's score, which is never stored
       const float sr = A.S[r];
       const float other = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(sr), 0x128, 0xF, 0xF, false));
-      s[r] = (FULL || 4 * g4 + r < valid_rows) ? (sr + other + 0.5f * A.Slo[r]) * fac[r] : -INFINITY;
+      s[r] = (FULL || 4 * g4 + r < valid_rows) ? (sr + other + lo_weight<KB>() * A.Slo[r]) * fac[r] : -INFINITY;
     }
+  }
+}
+
+// ---- 4-bit keys: lookups that are the score MFMA's A operand ----
+// Two table entries (code bytes 2m and 2m + 1 of a lane) are read into one
+// 4-register A operand as they come out of LDS: k-slots [hi c0, hi c1, lo c0,
+// lo c1, hi c2, hi c3, lo c2, lo c3] for coordinates c0 .. c3.  The query
+// operand lists each coordinate's query value in both its hi and its lo
+// slot, so one MFMA per four coordinates sums (hi + lo) q = c q, with no
+// register moves between the lookups and the MFMAs.  The norm of the
+// centroid vector is sum (hi + lo)^2 = diag(A A^T) + 2 sum hi lo: the
+// diagonal from MFMAs of each A operand with itself, the cross term from one
+// v_dot2 (hi pair . lo pair) per entry.
+
+// byte B of w times 8 (the byte offset of its table entry), one SDWA shift
+template <int B>
+__device__ __forceinline__ uint32_t byte_x8(uint32_t w) {
+  uint32_t r;
+  if constexpr (B == 0)
+    asm("v_lshlrev_b32_sdwa %0, 3, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_0" : "=v"(r) : "v"(w));
+  else if constexpr (B == 1)
+    asm("v_lshlrev_b32_sdwa %0, 3, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_1" : "=v"(r) : "v"(w));
+  else if constexpr (B == 2)
+    asm("v_lshlrev_b32_sdwa %0, 3, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_2" : "=v"(r) : "v"(w));
+  else
+    asm("v_lshlrev_b32_sdwa %0, 3, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_3" : "=v"(r) : "v"(w));
+  return r;
+}
+
+// one 8-byte entry (8-byte aligned, so a single ds_read_b64 with the table's
+// LDS address in its offset field)
+typedef uint32_t u32x2a8 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ u32x2a8 tab_entry(const u32x2* tab, uint32_t byte_off) {
+  return *reinterpret_cast<const u32x2a8*>(reinterpret_cast<const uint8_t*>(tab) + byte_off);
+}
+
+// query operands of the 4-bit path from the packed [qhi | qlo] columns:
+// operand kk covers coordinates 32*g4 + 4*kk + [0, 4), each listed twice
+__device__ __forceinline__ void queries_dup(const h8 (&qc)[4], h8 (&qd)[8]) {
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk) {
+    const h8 x = qc[kk >> 1];
+    const int o = 4 * (kk & 1);
+    qd[kk] = h8{x[o], x[o + 1], x[o], x[o + 1], x[o + 2], x[o + 3], x[o + 2], x[o + 3]};
+  }
+}
+
+// a word as two halves, taken by value: __builtin_bit_cast applied directly
+// to an element of a vector register value reads element 0 whatever the
+// subscript (seen with this compiler), so elements go through a copy
+__device__ __forceinline__ h2 as_h2(uint32_t v) { return __builtin_bit_cast(h2, v); }
+
+struct Acc4 {
+  f4 S, N;
+  float cross;       // sum hi * lo over the lane's 32 coordinates
+};
+
+// lookups and MFMAs of the slab in four quarters (two A operands live at a
+// time); the query operand of MFMA kk comes from q(kk): registers, or the
+// workgroup's copy in LDS
+template <bool NORM, class QSrc>
+__device__ __forceinline__ Acc4 score4(const u32x2* tab, const uint32_t (&kw)[4], QSrc q) {
+  Acc4 r;
+  r.S = f4{0.f, 0.f, 0.f, 0.f};
+  r.N = f4{1e-16f, 1e-16f, 1e-16f, 1e-16f};     // the correction's 1e-16
+  r.cross = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t w = kw[i];
+    const u32x2a8 e0 = tab_entry(tab, byte_x8<0>(w));
+    const u32x2a8 e1 = tab_entry(tab, byte_x8<1>(w));
+    const u32x2a8 e2 = tab_entry(tab, byte_x8<2>(w));
+    const u32x2a8 e3 = tab_entry(tab, byte_x8<3>(w));
+    const u32x4 A[2] = {u32x4{e0[0], e0[1], e1[0], e1[1]}, u32x4{e2[0], e2[1], e3[0], e3[1]}};
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int kk = 2 * i + j;
+      const h8 av = __builtin_bit_cast(h8, A[j]);
+      r.S = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, q(kk), r.S, 0, 0, 0);
+      if constexpr (NORM) {
+        r.N = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, av, r.N, 0, 0, 0);
+        r.cross = __builtin_amdgcn_fdot2(as_h2(A[j][0]), as_h2(A[j][1]),
+                                         r.cross, false);
+        r.cross = __builtin_amdgcn_fdot2(as_h2(A[j][2]), as_h2(A[j][3]),
+                                         r.cross, false);
+      }
+    }
+  }
+  return r;
+}
+
+// scores (base 2) of the slab, 4-bit keys on the slotted page: column h + 8
+// (row rotation by 8) holds the qlo part of head h; the norm factor n / |c|
+// of token t is formed in the lane holding N[t][t] (lane (t, t / 4), element
+// t % 4) and spread to the tile rows by one f32 MFMA
+template <bool FULL>
+__device__ __forceinline__ void tail4(uint32_t nb, const Acc4& A, int valid_rows, int g4, bool sel1,
+                                      bool sel2, bool diag, float (&s)[4]) {
+  const float cross = sum_x32(sum_x16(A.cross));        // token r16, all 128 coordinates
+  const float nd = sel2 ? (sel1 ? A.N[3] : A.N[2]) : (sel1 ? A.N[1] : A.N[0]);
+  const float fq = f16_bits_to_f32(nb) * __builtin_amdgcn_rsqf(__builtin_fmaf(2.0f, cross, nd));
+  const f4 fac = rows_to_tile(fq, diag);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const float sr = A.S[r];
+    const float other = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(sr), 0x128, 0xF, 0xF, false));
+    s[r] = (FULL || 4 * g4 + r < valid_rows) ? (sr + other) * fac[r] : -INFINITY;
+  }
+}
+
+// scores (base 2) of the slab, 4-bit keys on the split page (folded norms)
+template <bool FULL>
+__device__ __forceinline__ void tail4_soa(const uint32_t (&nf)[2], const Acc4& A, int valid_rows, int g4,
+                                          float (&s)[4]) {
+  const float fac[4] = {f16_bits_to_f32(nf[0] & 0xFFFFu), f16_bits_to_f32(nf[0] >> 16),
+                        f16_bits_to_f32(nf[1] & 0xFFFFu), f16_bits_to_f32(nf[1] >> 16)};
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const float sr = A.S[r];
+    const float other = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(sr), 0x128, 0xF, 0xF, false));
+    s[r] = (FULL || 4 * g4 + r < valid_rows) ? (sr + other) * fac[r] : -INFINITY;
   }
 }
 
@@ -1354,7 +1495,7 @@ template <int KB, int SLOT, int H>
 __global__ void __launch_bounds__(64 * H, page_waves_per_simd(KB)) decode_page_kernel(MfmaArgs a) {
   using Geo = PageGeom<KB, SLOT, H>;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  __shared__ u32x2 s_tab[KB == 8 ? 1 : 256];
+  __shared__ __attribute__((aligned(16))) u32x2 s_tab[KB == 8 ? 1 : 256];
   u32x2* tab = s_tab;
   int32_t* s_pid = reinterpret_cast<int32_t*>(smem + Geo::kPidOff);
 
@@ -1384,6 +1525,8 @@ __global__ void __launch_bounds__(64 * H, page_waves_per_simd(KB)) decode_page_k
     load_queries_bf16(a, b, g, r16, g4, qb);
   else
     load_queries_packed(a, b, g, r16, g4, qc);
+  h8 qd[8];                                  // 4-bit keys: the duplicated query operands
+  if constexpr (KB == 4) queries_dup(qc, qd);
   RunState st;
 #pragma unroll
   for (int m = 0; m < 8; ++m) st.O[m] = f4{0.f, 0.f, 0.f, 0.f};
@@ -1476,15 +1619,26 @@ __global__ void __launch_bounds__(64 * H, page_waves_per_simd(KB)) decode_page_k
       issue(j + Geo::kNbuf - 1);           // into the buffer of slab j - 1
       if (__builtin_amdgcn_readfirstlane(page_of(j)) < 0) continue;
       slab_read<KB, SLOT, H>(slab_buf(j), w, r16, g4, c);
-      slab_lookup<KB>(tab, c);
-      const ScoreAcc acc = slab_mfma<KB>(c, qc, qb);
       const int valid = t1 - (t0 + 16 * j);
-      if (valid >= 16) {
-        slab_tail<KB, true>(c, acc, 16, g4, a.scale_log2, sel1, sel2, diag, s);
-        sm = softmax_check<true>(s, 16, c.sz, g4, st);
+      if constexpr (KB == 4) {
+        const Acc4 acc = score4<true>(tab, c.kw, [&](int kk) { return qd[kk]; });
+        if (valid >= 16) {
+          tail4<true>(c.nb, acc, 16, g4, sel1, sel2, diag, s);
+          sm = softmax_check<true>(s, 16, c.sz, g4, st);
+        } else {
+          tail4<false>(c.nb, acc, valid, g4, sel1, sel2, diag, s);
+          sm = softmax_check<false>(s, valid, c.sz, g4, st);
+        }
       } else {
-        slab_tail<KB, false>(c, acc, valid, g4, a.scale_log2, sel1, sel2, diag, s);
-        sm = softmax_check<false>(s, valid, c.sz, g4, st);
+        slab_lookup<KB>(tab, c);
+        const ScoreAcc acc = slab_mfma<KB>(c, qc, qb);
+        if (valid >= 16) {
+          slab_tail<KB, true>(c, acc, 16, g4, a.scale_log2, sel1, sel2, diag, s);
+          sm = softmax_check<true>(s, 16, c.sz, g4, st);
+        } else {
+          slab_tail<KB, false>(c, acc, valid, g4, a.scale_log2, sel1, sel2, diag, s);
+          sm = softmax_check<false>(s, valid, c.sz, g4, st);
+        }
       }
       if (sm.grow) {
         grow = true;
@@ -1588,7 +1742,7 @@ __device__ __forceinline__ void slab_read_soa(const uint8_t* buf, int r16, int g
 
 // scores (base 2) of a split-page slab: the stored norm already holds the
 // correction, so it multiplies the rows directly
-template <bool FULL>
+template <int KB, bool FULL>
 __device__ __forceinline__ void slab_tail_soa(const uint32_t (&nf)[2], const ScoreAcc& A, int valid_rows,
                                               int g4, float (&s)[4]) {
   const float fac[4] = {f16_bits_to_f32(nf[0] & 0xFFFFu), f16_bits_to_f32(nf[0] >> 16),
@@ -1598,7 +1752,7 @@ __device__ __forceinline__ void slab_tail_soa(const uint32_t (&nf)[2], const Sco
     // column h + 8 holds hi.qlo of head h (as in slab_tail)
     const float sr = A.S[r];
     const float other = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(sr), 0x128, 0xF, 0xF, false));
-    s[r] = (FULL || 4 * g4 + r < valid_rows) ? (sr + other + 0.5f * A.Slo[r]) * fac[r] : -INFINITY;
+    s[r] = (FULL || 4 * g4 + r < valid_rows) ? (sr + other + lo_weight<KB>() * A.Slo[r]) * fac[r] : -INFINITY;
   }
 }
 
@@ -1620,10 +1774,23 @@ __global__ void __launch_bounds__(64 * WAVES, kRingWaves / WAVES) decode_ring_ke
   constexpr int kBufs = SOA ? 4 : kRingBufs;
   constexpr int kRing = kBufs * kBuf;
   static_assert(8 * kRec * 4 <= kRing, "a wavefront's partial records must fit its ring");
-  __shared__ u32x2 s_tab[256];
-  __shared__ int32_t s_pid[kRingMaxSlabs];
-  __shared__ int32_t s_next;                 // the workgroup's next unclaimed slab
-  __shared__ __attribute__((aligned(16))) uint8_t s_ring[WAVES][kRing];
+  // one LDS block, carved by hand so the centroid table sits at address 0
+  // (its entries are then addressed by the byte offset alone, the ds
+  // instruction's 16-bit offset field holding nothing), then the page ids,
+  // the claim counter and the wavefronts' rings
+  struct RingLds {
+    u32x2 tab[256];
+    int32_t pid[kRingMaxSlabs];
+    int32_t next;                            // the workgroup's next unclaimed slab
+    int32_t pad[3];
+    uint8_t ring[WAVES][kRing];
+  };
+  static_assert(offsetof(RingLds, ring) % 16 == 0, "rings on 16-byte boundaries");
+  __shared__ __attribute__((aligned(16))) RingLds lds;
+  u32x2* const s_tab = lds.tab;
+  int32_t* const s_pid = lds.pid;
+  int32_t& s_next = lds.next;
+  auto& s_ring = lds.ring;
 
   const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
   const int lane = threadIdx.x & 63;
@@ -1655,11 +1822,16 @@ __global__ void __launch_bounds__(64 * WAVES, kRingWaves / WAVES) decode_ring_ke
   build_tables_page<KB>(a, s_tab);
   if (n_wg > 0) stage_page_ids(a, b, 16 * wg0, t_end, s_pid);
   if (threadIdx.x == 0) s_next = 0;
-  __syncthreads();
-
+  // 4-bit keys on the split page: the duplicated query operands of score4
+  // (the slotted page keeps the separate hi and lo MFMAs, whose norm terms
+  // it needs anyway; measured faster there)
+  constexpr bool kDup = KB == 4 && SOA;
   h8 qv[4];
   bf8v qb[4];
+  h8 qd[kDup ? 8 : 1];
+  __syncthreads();
   load_queries_packed(a, b, g, r16, g4, qv);
+  if constexpr (kDup) queries_dup(qv, qd);
   RunState st;
 #pragma unroll
   for (int m = 0; m < 8; ++m) st.O[m] = f4{0.f, 0.f, 0.f, 0.f};
@@ -1791,21 +1963,32 @@ __global__ void __launch_bounds__(64 * WAVES, kRingWaves / WAVES) decode_ring_ke
           slab_read_soa<KB, VB>(ring + (j % kBufs) * kBuf, r16, g4, c);
         else
           slab_read<KB, SLOT, 1>(ring + (j % kBufs) * kBuf, 0, r16, g4, c);
-        slab_lookup<KB>(s_tab, c);
-        const ScoreAcc acc = slab_mfma<KB, !SOA>(c, qv, qb);
         const int valid = t_end - 16 * (wg0 + cur);
-        if (valid >= 16) {
-          if constexpr (SOA)
-            slab_tail_soa<true>(c.nf, acc, 16, g4, s);
-          else
-            slab_tail<KB, true>(c, acc, 16, g4, a.scale_log2, sel1, sel2, diag, s);
-          sm = softmax_check<true>(s, 16, c.sz, g4, st);
+        if constexpr (kDup) {
+          const Acc4 acc = score4<false>(s_tab, c.kw, [&](int kk) { return qd[kk]; });
+          if (valid >= 16) {
+            tail4_soa<true>(c.nf, acc, 16, g4, s);
+            sm = softmax_check<true>(s, 16, c.sz, g4, st);
+          } else {
+            tail4_soa<false>(c.nf, acc, valid, g4, s);
+            sm = softmax_check<false>(s, valid, c.sz, g4, st);
+          }
         } else {
-          if constexpr (SOA)
-            slab_tail_soa<false>(c.nf, acc, valid, g4, s);
-          else
-            slab_tail<KB, false>(c, acc, valid, g4, a.scale_log2, sel1, sel2, diag, s);
-          sm = softmax_check<false>(s, valid, c.sz, g4, st);
+          slab_lookup<KB>(s_tab, c);
+          const ScoreAcc acc = slab_mfma<KB, !SOA>(c, qv, qb);
+          if (valid >= 16) {
+            if constexpr (SOA)
+              slab_tail_soa<KB, true>(c.nf, acc, 16, g4, s);
+            else
+              slab_tail<KB, true>(c, acc, 16, g4, a.scale_log2, sel1, sel2, diag, s);
+            sm = softmax_check<true>(s, 16, c.sz, g4, st);
+          } else {
+            if constexpr (SOA)
+              slab_tail_soa<KB, false>(c.nf, acc, valid, g4, s);
+            else
+              slab_tail<KB, false>(c, acc, valid, g4, a.scale_log2, sel1, sel2, diag, s);
+            sm = softmax_check<false>(s, valid, c.sz, g4, st);
+          }
         }
         if (sm.grow) {
           grow = true;
@@ -1835,8 +2018,10 @@ __global__ void __launch_bounds__(64 * WAVES, kRingWaves / WAVES) decode_ring_ke
       const int h = 4 * g4 + r;
       if (h < G) {
         float* rec = rec_w + h * kRec;
-        *reinterpret_cast<float4*>(rec + 8 * r16) = make_float4(st.O[0][r], st.O[1][r], st.O[2][r], st.O[3][r]);
-        *reinterpret_cast<float4*>(rec + 8 * r16 + 4) = make_float4(st.O[4][r], st.O[5][r], st.O[6][r], st.O[7][r]);
+        *reinterpret_cast<float4*>(rec + 8 * r16) = make_float4(
+            st.O[0][r] * kVScale, st.O[1][r] * kVScale, st.O[2][r] * kVScale, st.O[3][r] * kVScale);
+        *reinterpret_cast<float4*>(rec + 8 * r16 + 4) = make_float4(
+            st.O[4][r] * kVScale, st.O[5][r] * kVScale, st.O[6][r] * kVScale, st.O[7][r] * kVScale);
       }
     }
     if (g4 == 0 && r16 < G) {

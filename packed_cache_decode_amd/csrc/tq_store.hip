@@ -16,10 +16,15 @@
 // implementation that follows these steps, and the bytes are comparable bit
 // for bit.
 //
-// Mapping: one wavefront (64 lanes) per vector pair; lane l holds the E = d/64
-// contiguous elements [E*l, E*l + E).  Butterflies with stride below E stay in
-// the lane, larger strides pair lane l with lane l ^ (h / E).  The slot is
-// assembled in LDS and written with 2-byte stores (slots are 2-byte aligned).
+// Kernels.  store128_kernel (head_dim 128 with the Hadamard rotation, every
+// preset and both page layouts) gives each vector four lanes of 32
+// contiguous coordinates, 16 vectors per wavefront; its section below has
+// the details.  store_kernel serves the rest (head dims 64 and 256, the Haar
+// rotation, codebooks without bucketize bins): one wavefront (64 lanes) per
+// vector pair, lane l holding the E = d/64 contiguous elements [E*l, E*l +
+// E), butterflies with stride below E inside the lane and larger strides
+// pairing lane l with lane l ^ (h / E); its slot is assembled in LDS and
+// written with 2-byte stores (slots are 2-byte aligned).
 #include "tq_internal.h"
 
 #pragma clang fp contract(off)

@@ -28,7 +28,6 @@ each) over a bounded sample of the same workload.
 """
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -37,22 +36,9 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
+from packed_cache_decode_amd.profile_summary import KERNEL_SOURCES, sources_sha256  # noqa: E402
+
 HBM_PEAK_GBS = 8000.0
-
-# kernel sources whose counter-measured HBM traffic profiles/ records
-KERNEL_SOURCES = {
-    "decode": ("packed_cache_decode_amd/csrc/tq_decode.hip", "packed_cache_decode_amd/csrc/tq_decode_mfma.hip",
-               "packed_cache_decode_amd/csrc/tq_internal.h"),
-    "store": ("packed_cache_decode_amd/csrc/tq_store.hip", "packed_cache_decode_amd/csrc/tq_internal.h"),
-}
-
-
-def sources_sha256(kind):
-    h = hashlib.sha256()
-    for rel in KERNEL_SOURCES[kind]:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()[:16]
 
 
 def counted_traffic(kind, workload, layout="aos"):

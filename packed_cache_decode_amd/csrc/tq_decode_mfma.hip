@@ -30,7 +30,8 @@
 // Contractions, 16x16 MFMA tiles:
 //   scores  S[t][h] = sum_c C[t][c] Q[h][c]     v_mfma_f32_16x16x32_f16 / _bf16
 //   norms   N[t][t] = sum_c C[t][c] C[t][c]     diagonal of C C^T (MSE keys)
-//   values  O[h][c] += sum_t W[h][t] V[t][c]    v_mfma_f32_16x16x32_f16
+//   values  O[h][c] += sum_t W[h][t] V[t][c]    v_mfma_f32_16x16x32_f16 (direct, staged)
+//                                               v_mfma_f32_16x16x16_f16 (page, ring)
 // For MSE keys C are the centroids of the slab's K codes, looked up per code
 // byte (two codes) in an LDS table.  f16 alone is not precise enough for the
 // scores (centroids rounded to f16 move the decode output by up to 2.7e-3
@@ -38,12 +39,12 @@
 // f16 hi + lo pairs; the table and operand layouts of each kernel are given
 // with it.  FP8 keys convert exactly to bf16 and meet the bf16 query
 // directly.  Q holds the (rotated) queries, rows >= G zero.  V operands are
-// the integer codes as f16 subnormals (code * 2^-24, exact), W = p * scale
-// as an f16 hi + lo pair in one operand; kVScale undoes the 2^-24 when the
-// accumulators are written out.  The per-token term zero * p and the
-// softmax sums stay in fp32.  The running maximum is lazy: the accumulators
-// are rescaled only when a head's maximum grows by more than kLazy (base 2),
-// so p <= 2^kLazy.
+// the integer codes as exact f16 integers, W = p * scale as an f16 hi + lo
+// pair: side by side in k (direct, staged kernels), or in tile rows h and
+// h + 8 (page, ring kernels, at most 8 query heads per kv head).  The
+// per-token term zero * p and the softmax sums stay in fp32.  The running
+// maximum is lazy: the accumulators are rescaled only when a head's maximum
+// grows by more than kLazy (base 2), so p <= 2^kLazy.
 //
 // Layouts (lane l, row r16 = l % 16, group g4 = l / 16):
 //   A operand  : row r16, k = [8*g4, 8*g4+8) (x32) or [4*g4, 4*g4+4) (x16)
@@ -53,7 +54,6 @@
 // kk in group g4 covers coordinates 32*g4 + 8*kk + [0, 8); value tile m,
 // column j covers coordinate 8*j + m.
 #include <cstddef>
-
 
 #include "tq_internal.h"
 
@@ -118,6 +118,11 @@ __device__ __forceinline__ float max_x32(float x) {
   auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
 }
+// a word as two halves, taken by value: __builtin_bit_cast applied directly
+// to an element of a vector register value reads element 0 whatever the
+// subscript (seen with this compiler), so elements go through a copy
+__device__ __forceinline__ h2 as_h2(uint32_t v) { return __builtin_bit_cast(h2, v); }
+
 __device__ __forceinline__ float sum_x16(float x) {
   auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(s[0]) + __uint_as_float(s[1]);
@@ -125,6 +130,12 @@ __device__ __forceinline__ float sum_x16(float x) {
 __device__ __forceinline__ float sum_x32(float x) {
   auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(s[0]) + __uint_as_float(s[1]);
+}
+// lanes 8 .. 15 of each row of 16 take the value of lane - 8 (a row rotation
+// by 8 written to DPP banks 2 and 3 only): the P.V lo rows then work from
+// exactly the scores of their head
+__device__ __forceinline__ float copy_to_upper8(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(x), __float_as_int(x), 0x128, 0xF, 0xC, false));
 }
 __device__ __forceinline__ float lane_value(float x, int src_lane) {
   return __int_as_float(__builtin_amdgcn_ds_bpermute(src_lane << 2, __float_as_int(x)));
@@ -340,35 +351,40 @@ constexpr int vbits_of_slot(int slot) { return slot == 102 ? 3 : 4; }
 
 // MFMA B operands of the V codes of tokens 4*g4 + r (X[r]: the token's codes
 // of coordinates 8*r16 .. 8*r16 + 7) for coordinates 8*r16 + 2*kb (Blo) and
-// 8*r16 + 2*kb + 1 (Bhi).  A code c (0 .. 15) placed in the low bits of a
-// 16-bit lane is the f16 subnormal c * 2^-24, exactly, so the operands are
-// the codes themselves moved into place; the matrix cores multiply
-// subnormal inputs exactly, and the accumulated P.V carries the factor
-// 2^-24, which kVScale undoes when the accumulators are written out.
-constexpr float kVScale = 16777216.0f;       // 2^24
+// 8*r16 + 2*kb + 1 (Bhi), as exact f16 integers: code c goes into the
+// mantissa of a power of two (1024 + c, or 64 + c for the high nibble of a
+// 4-bit byte), and one packed f16 subtraction removes the power of two.
+// (Codes left as f16 subnormals, c * 2^-24, need no subtraction, but the
+// matrix cores do not sum products with subnormal inputs exactly: decode
+// errors grew about 100-fold.)
 template <int VB>
 __device__ __forceinline__ void v_operands(const uint32_t (&X)[4], int kb, h4& Blo, h4& Bhi) {
+  const h2 b1024 = {static_cast<_Float16>(1024.0f), static_cast<_Float16>(1024.0f)};
   if constexpr (VB == 4) {
-    // byte kb of each token's dword -> [x0, 0, x1, 0]; low nibbles by a mask,
-    // high nibbles by a packed 16-bit shift
-    typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+    const h2 b64 = {static_cast<_Float16>(64.0f), static_cast<_Float16>(64.0f)};
+    // byte kb of each token's dword -> [x0, 0, x1, 0]
     const uint32_t sel = kb | (0x0Cu << 8) | ((4u + kb) << 16) | (0x0Cu << 24);
     const uint32_t p01 = __builtin_amdgcn_perm(X[1], X[0], sel);
     const uint32_t p23 = __builtin_amdgcn_perm(X[3], X[2], sel);
-    const uint32_t lo01 = p01 & 0x000F000Fu, lo23 = p23 & 0x000F000Fu;
-    const uint32_t hi01 = __builtin_bit_cast(uint32_t, __builtin_bit_cast(u16x2, p01) >> (uint16_t)4);
-    const uint32_t hi23 = __builtin_bit_cast(uint32_t, __builtin_bit_cast(u16x2, p23) >> (uint16_t)4);
-    Blo = __builtin_bit_cast(h4, (u32x2{lo01, lo23}));
-    Bhi = __builtin_bit_cast(h4, (u32x2{hi01, hi23}));
+    const h2 lo01 = __builtin_bit_cast(h2, (p01 & 0x000F000Fu) | 0x64006400u) - b1024;
+    const h2 lo23 = __builtin_bit_cast(h2, (p23 & 0x000F000Fu) | 0x64006400u) - b1024;
+    const h2 hi01 = __builtin_bit_cast(h2, (p01 & 0x00F000F0u) | 0x54005400u) - b64;
+    const h2 hi23 = __builtin_bit_cast(h2, (p23 & 0x00F000F0u) | 0x54005400u) - b64;
+    Blo = h4{lo01[0], lo01[1], lo23[0], lo23[1]};
+    Bhi = h4{hi01[0], hi01[1], hi23[0], hi23[1]};
   } else {
     // 3-bit codes: code m of a token at bits [3m, 3m + 3) of its X
     const uint32_t m0 = 6 * kb, m1 = 6 * kb + 3;
-    const uint32_t lo01 = __builtin_amdgcn_ubfe(X[0], m0, 3) | (__builtin_amdgcn_ubfe(X[1], m0, 3) << 16);
-    const uint32_t lo23 = __builtin_amdgcn_ubfe(X[2], m0, 3) | (__builtin_amdgcn_ubfe(X[3], m0, 3) << 16);
-    const uint32_t hi01 = __builtin_amdgcn_ubfe(X[0], m1, 3) | (__builtin_amdgcn_ubfe(X[1], m1, 3) << 16);
-    const uint32_t hi23 = __builtin_amdgcn_ubfe(X[2], m1, 3) | (__builtin_amdgcn_ubfe(X[3], m1, 3) << 16);
-    Blo = __builtin_bit_cast(h4, (u32x2{lo01, lo23}));
-    Bhi = __builtin_bit_cast(h4, (u32x2{hi01, hi23}));
+    const h2 lo01 = __builtin_bit_cast(h2, __builtin_amdgcn_ubfe(X[0], m0, 3) |
+                                               (__builtin_amdgcn_ubfe(X[1], m0, 3) << 16) | 0x64006400u) - b1024;
+    const h2 lo23 = __builtin_bit_cast(h2, __builtin_amdgcn_ubfe(X[2], m0, 3) |
+                                               (__builtin_amdgcn_ubfe(X[3], m0, 3) << 16) | 0x64006400u) - b1024;
+    const h2 hi01 = __builtin_bit_cast(h2, __builtin_amdgcn_ubfe(X[0], m1, 3) |
+                                               (__builtin_amdgcn_ubfe(X[1], m1, 3) << 16) | 0x64006400u) - b1024;
+    const h2 hi23 = __builtin_bit_cast(h2, __builtin_amdgcn_ubfe(X[2], m1, 3) |
+                                               (__builtin_amdgcn_ubfe(X[3], m1, 3) << 16) | 0x64006400u) - b1024;
+    Blo = h4{lo01[0], lo01[1], lo23[0], lo23[1]};
+    Bhi = h4{hi01[0], hi01[1], hi23[0], hi23[1]};
   }
 }
 
@@ -476,32 +492,41 @@ __device__ __forceinline__ void softmax_rescale(const SlabSoftmax& sm, bool diag
   st.m_run = m_new;
 }
 
+// p * scale as f16 hi + lo: one f16 alone (2^-11) is not precise enough when
+// a single token dominates and its V range is wide.  The two parts sit in
+// different rows of the P.V tile: rows h < 8 take the hi part of head h,
+// rows h + 8 its lo part (those lanes hold a copy of head h's scores and
+// running state), so each MFMA has k = 16 tokens and V operands that are
+// exactly the decoded codes; fold_lo_rows adds the lo rows in at the end.
 template <int VB>
 __device__ __forceinline__ void softmax_accumulate(const float (&s)[4], const SlabSoftmax& sm,
                                                    const uint32_t (&X)[4], RunState& st) {
-  // p * scale as f16 hi + lo: one f16 alone (2^-11) is not precise enough
-  // when a single token dominates and its V range is wide
-  h4 W, Wl;
+  const bool lo_row = (threadIdx.x & 8) != 0;
+  h4 W;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const float p = __builtin_amdgcn_exp2f(s[r] - st.m_run);
     st.l_part += p;
     st.z_part += p * sm.zr[r];
     const float wf = p * sm.sc[r];
-    W[r] = static_cast<_Float16>(wf);
-    Wl[r] = static_cast<_Float16>(wf - static_cast<float>(W[r]));
+    const float hi = static_cast<float>(static_cast<_Float16>(wf));
+    W[r] = static_cast<_Float16>(lo_row ? wf - hi : wf);
   }
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb) {
-    h4 Blo4, Bhi4;
-    v_operands<VB>(X, kb, Blo4, Bhi4);
-    const h8 Blo = {Blo4[0], Blo4[1], Blo4[2], Blo4[3], Blo4[0], Blo4[1], Blo4[2], Blo4[3]};
-    const h8 Bhi = {Bhi4[0], Bhi4[1], Bhi4[2], Bhi4[3], Bhi4[0], Bhi4[1], Bhi4[2], Bhi4[3]};
-    const h8 Ws = {W[0], W[1], W[2], W[3], Wl[0], Wl[1], Wl[2], Wl[3]};
-    st.O[2 * kb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ws, Blo, st.O[2 * kb], 0, 0, 0);
-    st.O[2 * kb + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ws, Bhi, st.O[2 * kb + 1], 0, 0, 0);
-    if (kb & 1) __builtin_amdgcn_sched_barrier(0);     // bounded operand registers
+    h4 Blo, Bhi;
+    v_operands<VB>(X, kb, Blo, Bhi);
+    st.O[2 * kb] = __builtin_amdgcn_mfma_f32_16x16x16f16(W, Blo, st.O[2 * kb], 0, 0, 0);
+    st.O[2 * kb + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(W, Bhi, st.O[2 * kb + 1], 0, 0, 0);
   }
+}
+
+// rows h + 8 of the accumulators (lane groups 2, 3) into rows h (groups 0, 1)
+__device__ __forceinline__ void fold_lo_rows(RunState& st) {
+#pragma unroll
+  for (int m = 0; m < 8; ++m)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) st.O[m][r] = sum_x32(st.O[m][r]);
 }
 
 // One slab of 3/4-bit keys: scores, norm correction, online softmax, P.V.
@@ -591,9 +616,9 @@ __device__ __forceinline__ void store_partials(const MfmaArgs& a, int b, int g, 
       float* rec = a.part + (rec0 + static_cast<int64_t>(h) * a.num_splits) * kRec;
       // tile m column r16 is coordinate 8*r16 + m
       *reinterpret_cast<float4*>(rec + 8 * r16) = make_float4(
-          st.O[0][r] * kVScale, st.O[1][r] * kVScale, st.O[2][r] * kVScale, st.O[3][r] * kVScale);
+          st.O[0][r], st.O[1][r], st.O[2][r], st.O[3][r]);
       *reinterpret_cast<float4*>(rec + 8 * r16 + 4) = make_float4(
-          st.O[4][r] * kVScale, st.O[5][r] * kVScale, st.O[6][r] * kVScale, st.O[7][r] * kVScale);
+          st.O[4][r], st.O[5][r], st.O[6][r], st.O[7][r]);
     }
   }
   if (g4 == 0 && r16 < G) {
@@ -1061,7 +1086,9 @@ __global__ void __launch_bounds__(64, kStagedWavesPerSimd<KB>) decode_staged_ker
 // MI355X.  Every wavefront then takes its own head's operands from LDS.
 //
 // The centroid table holds hi = f16(c) and lo = f16(c - hi) for 4-bit keys
-// (lo often subnormal; the matrix cores take subnormal inputs exactly) and
+// (lo often subnormal: the matrix cores then sum its products less than
+// exactly, but the lo term is about 2^-12 of the score, so that loss stays
+// far below the score's own rounding) and
 // lo = f16(2 (c - hi)) for 3-bit keys; the queries qhi = f16(q) and qlo =
 // f16(q - qhi).  With at most 8 query heads per kv head one B operand
 // carries both query parts: column h < 8 holds qhi of head h and column
@@ -1151,8 +1178,8 @@ __device__ __forceinline__ void build_tables_page(const MfmaArgs& a, u32x2* tab)
     const float v0 = a.tables->centroids[c0], v1 = a.tables->centroids[c1];
     const _Float16 h0 = static_cast<_Float16>(v0), h1 = static_cast<_Float16>(v1);
     if constexpr (KB == 4) {
-      // lo = c - hi unscaled (subnormal for the small levels; the matrix
-      // cores and v_dot2 take subnormal inputs exactly)
+      // lo = c - hi unscaled (subnormal for the small levels, whose products
+      // the matrix cores sum less than exactly: immaterial at 2^-12 of c)
       const _Float16 l0 = static_cast<_Float16>(v0 - static_cast<float>(h0));
       const _Float16 l1 = static_cast<_Float16>(v1 - static_cast<float>(h1));
       tab[e] = u32x2{pack_h2(h0, h1), pack_h2(l0, l1)};
@@ -1366,6 +1393,8 @@ __device__ __forceinline__ void slab_tail(const SlabRegs<KB>& R, const ScoreAcc&
       const float sr = A.S[r];
       const float other = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(sr), 0x128, 0xF, 0xF, false));
       s[r] = (FULL || 4 * g4 + r < valid_rows) ? (sr + other + lo_weight<KB>() * A.Slo[r]) * fac[r] : -INFINITY;
+      // columns h and h + 8 differ in the lo term (lo.qhi against lo.qlo)
+      s[r] = copy_to_upper8(s[r]);
     }
   }
 }
@@ -1413,11 +1442,6 @@ __device__ __forceinline__ void queries_dup(const h8 (&qc)[4], h8 (&qd)[8]) {
     qd[kk] = h8{x[o], x[o + 1], x[o], x[o + 1], x[o + 2], x[o + 3], x[o + 2], x[o + 3]};
   }
 }
-
-// a word as two halves, taken by value: __builtin_bit_cast applied directly
-// to an element of a vector register value reads element 0 whatever the
-// subscript (seen with this compiler), so elements go through a copy
-__device__ __forceinline__ h2 as_h2(uint32_t v) { return __builtin_bit_cast(h2, v); }
 
 struct Acc4 {
   f4 S, N;
@@ -1522,7 +1546,7 @@ __global__ void __launch_bounds__(64 * H, page_waves_per_simd(KB)) decode_page_k
   h8 qc[4];
   bf8v qb[4];
   if constexpr (KB == 8)
-    load_queries_bf16(a, b, g, r16, g4, qb);
+    load_queries_bf16(a, b, g, r16 & 7, g4, qb);    // columns h + 8 repeat head h
   else
     load_queries_packed(a, b, g, r16, g4, qc);
   h8 qd[8];                                  // 4-bit keys: the duplicated query operands
@@ -1652,6 +1676,7 @@ __global__ void __launch_bounds__(64 * H, page_waves_per_simd(KB)) decode_page_k
     ++j;
   }
   wait_vmcnt<0>();                           // no load may still write LDS at exit
+  fold_lo_rows(st);
   store_partials(a, b, g, split, g4, r16, st);
 }
 
@@ -1753,6 +1778,7 @@ __device__ __forceinline__ void slab_tail_soa(const uint32_t (&nf)[2], const Sco
     const float sr = A.S[r];
     const float other = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(sr), 0x128, 0xF, 0xF, false));
     s[r] = (FULL || 4 * g4 + r < valid_rows) ? (sr + other + lo_weight<KB>() * A.Slo[r]) * fac[r] : -INFINITY;
+    s[r] = copy_to_upper8(s[r]);
   }
 }
 
@@ -2008,6 +2034,7 @@ __global__ void __launch_bounds__(64 * WAVES, kRingWaves / WAVES) decode_ring_ke
   // each wavefront's records (O[128], m, l, z per query head) go into its own
   // ring, whose reads have all completed
   float* rec_w = reinterpret_cast<float*>(ring);
+  fold_lo_rows(st);
   {
     const int G = a.G;
     const float l_part = sum_x32(sum_x16(st.l_part));
@@ -2019,9 +2046,9 @@ __global__ void __launch_bounds__(64 * WAVES, kRingWaves / WAVES) decode_ring_ke
       if (h < G) {
         float* rec = rec_w + h * kRec;
         *reinterpret_cast<float4*>(rec + 8 * r16) = make_float4(
-            st.O[0][r] * kVScale, st.O[1][r] * kVScale, st.O[2][r] * kVScale, st.O[3][r] * kVScale);
+            st.O[0][r], st.O[1][r], st.O[2][r], st.O[3][r]);
         *reinterpret_cast<float4*>(rec + 8 * r16 + 4) = make_float4(
-            st.O[4][r] * kVScale, st.O[5][r] * kVScale, st.O[6][r] * kVScale, st.O[7][r] * kVScale);
+            st.O[4][r], st.O[5][r], st.O[6][r], st.O[7][r]);
       }
     }
     if (g4 == 0 && r16 < G) {
@@ -2117,8 +2144,9 @@ bool staged_decode_eligible(const Geometry& g, int num_q_heads) {
 
 bool page_decode_eligible(const Geometry& g, int num_q_heads, bool mse_keys_too) {
   const int H = g.num_kv_heads;
-  // query hi and lo parts share one B operand for up to 8 heads per kv head
-  const bool g_ok = g.key_bits == 8 || num_q_heads <= 8 * H;
+  // up to 8 query heads per kv head: the query hi and lo parts share one B
+  // operand, and the P.V tile keeps the weights' lo parts in rows 8 .. 15
+  const bool g_ok = num_q_heads <= 8 * H;
   // 3/4-bit keys: the per-head kernel is still the faster one (the page
   // kernel's centroid lookups are bound by LDS bank conflicts), unless asked
   const bool kind_ok = g.key_bits == 8 || mse_keys_too;

@@ -32,6 +32,7 @@ pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
 
 FULL = ["tiny", "llama3_8b", "k3v4_gqa8", "k8v4_32k", "long_131k"]
+MEAN_GUARD = 5e-6
 SEED = 4242
 
 
@@ -137,6 +138,13 @@ def run_full(name, layout, pool):
                        f"(sequence, head, coordinate) {s['argmax']}, mean-abs {s['mean_abs']:.3e}, "
                        f"beyond tolerance {s['beyond']}")
         assert s32["beyond"] == 0 and s16["beyond"] == 0
+        # A guard on the arithmetic itself, beside the 2e-3 parity bound:
+        # scores and weights carried as f16 hi + lo pairs (about 2^-20 of
+        # each) and fp32 sums leave a mean error of a few 1e-7 on these
+        # unit-scale outputs.  A lossy change that still passes 2e-3 shows
+        # here (V codes fed to the matrix cores as f16 subnormals, whose
+        # products are not summed exactly, put the mean near 2e-5).
+        assert s32["mean_abs"] < MEAN_GUARD, s32
         return res, s32, s16
     finally:
         shutil.rmtree(tmp, ignore_errors=True)

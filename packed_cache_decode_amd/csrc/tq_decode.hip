@@ -419,15 +419,16 @@ hipError_t launch_g(const DecodeArgs& a, int G, int batch, hipStream_t stream) {
 
 }  // namespace
 
-DecodePlan plan_decode(const Geometry& g, const tq_decode_options& opts, int batch, int num_q_heads,
-                       int max_seq_len) {
+namespace {
+DecodePlan plan_decode_kernels(const Geometry& g, const tq_decode_options& opts, int batch, int num_q_heads,
+                               int max_seq_len) {
   DecodePlan p{};
   // ring kernel: slabs dealt out in a fixed interleaved order unless the
   // context asks for dynamic claims (results then vary in the last bits)
   p.dynamic = opts.dynamic_claims ? 1 : 0;
-  if (g.haar) {
-    // the matrix-core kernels rotate q with butterflies; the Haar rotation's
-    // dense product runs in the general kernel
+  if (g.haar && g.head_dim != 128) {
+    // the matrix-core kernels are built for d = 128; other head dims with the
+    // Haar rotation's dense product run in the general kernel
     p.mfma = 0;
     p.chunk = 256;
     p.num_splits = max_seq_len > 0 ? (max_seq_len + p.chunk - 1) / p.chunk : 1;
@@ -526,6 +527,22 @@ DecodePlan plan_decode(const Geometry& g, const tq_decode_options& opts, int bat
   p.workspace_bytes = static_cast<size_t>(batch) * num_q_heads * p.num_splits *
                       (g.head_dim + 2) * sizeof(float);
   p.workspace_bytes = (p.workspace_bytes + 255) & ~static_cast<size_t>(255);
+  return p;
+}
+
+}  // namespace
+
+DecodePlan plan_decode(const Geometry& g, const tq_decode_options& opts, int batch, int num_q_heads,
+                       int max_seq_len) {
+  DecodePlan p = plan_decode_kernels(g, opts, batch, num_q_heads, max_seq_len);
+  if (g.haar && p.mfma != 0) {
+    // the matrix-core kernels read the queries rotated by the Haar matrix
+    // from the workspace, after the split partials
+    p.qrot = 1;
+    p.qrot_off = (p.workspace_bytes + 255) & ~static_cast<size_t>(255);
+    p.workspace_bytes = p.qrot_off + static_cast<size_t>(batch) * num_q_heads * g.head_dim * sizeof(float);
+    p.workspace_bytes = (p.workspace_bytes + 255) & ~static_cast<size_t>(255);
+  }
   return p;
 }
 

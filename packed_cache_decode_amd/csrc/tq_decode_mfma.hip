@@ -98,6 +98,7 @@ struct MfmaArgs {
   void* out;
   int out_fp32;
   int dynamic;         // ring kernel: wavefronts claim slabs from a shared counter
+  const float* q_rot;  // Haar rotation: the rotated queries [B][Hq][d] (fp32), else null
 };
 
 __device__ __forceinline__ uint32_t pack_h2(_Float16 a, _Float16 b) {
@@ -185,12 +186,36 @@ __device__ __forceinline__ void build_tables(const MfmaArgs& a, u32x2* s_tab) {
 
 // rotate the G queries of kv head g (q_rot = H diag(s) q / sqrt(128)) and
 // split them into f16 hi / lo; lane (h = r16, g4) holds coordinates
-// [32*g4, 32*g4 + 32) of head h, as the four score-MFMA B operands
+// [32*g4, 32*g4 + 32) of head h, as the four score-MFMA B operands.  With
+// the Haar rotation the queries come rotated already (a.q_rot, from
+// rotate_queries_haar_kernel; that rotation has no 1/sqrt(d) factor).
 __device__ __forceinline__ void load_queries(const MfmaArgs& a, int b, int g, int r16, int g4,
                                              float fscale, h8 (&qhi)[4], h8 (&qlo)[4]) {
   float x[32];
   const bool live = r16 < a.G;
-  const uint16_t* qp = a.q + (static_cast<int64_t>(b) * a.Hq + g * a.G + (live ? r16 : 0)) * kD + 32 * g4;
+  const int64_t row = (static_cast<int64_t>(b) * a.Hq + g * a.G + (live ? r16 : 0)) * kD + 32 * g4;
+  if (a.q_rot != nullptr) {
+    const float4* rp = reinterpret_cast<const float4*>(a.q_rot + row);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float4 v = rp[i];
+      x[4 * i] = v.x;
+      x[4 * i + 1] = v.y;
+      x[4 * i + 2] = v.z;
+      x[4 * i + 3] = v.w;
+    }
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float v = live ? x[8 * kk + e] * fscale : 0.0f;
+        const _Float16 hv = static_cast<_Float16>(v);
+        qhi[kk][e] = hv;
+        qlo[kk][e] = static_cast<_Float16>(v - static_cast<float>(hv));
+      }
+    return;
+  }
+  const uint16_t* qp = a.q + row;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const u32x4 w = *reinterpret_cast<const u32x4*>(qp + 8 * i);
@@ -634,6 +659,34 @@ __device__ __forceinline__ void store_partials(const MfmaArgs& a, int b, int g, 
 // merges its splits online (running max, a split weighted by 2^(m_s - max)),
 // with all loads of a group of splits issued together, and the four meet in
 // LDS.  o = sum_s w_s (O_s + z_s) / sum_s w_s l_s.
+// Haar rotation of the queries, once per decode: q_rot = Q q for every
+// (sequence, query head), fp32, with Q the d x d matrix the store applied to
+// the keys (readings of the pages: the Haar rotation).  One workgroup per
+// (sequence, kv head): thread i forms coordinate i of its G queries, so
+// each row of Q is read once per workgroup.
+__global__ void __launch_bounds__(kD) rotate_queries_haar_kernel(MfmaArgs a, float* q_rot) {
+  __shared__ float s_q[16][kD];
+  const int b = blockIdx.x / a.H, g = blockIdx.x - b * a.H;
+  const int i = threadIdx.x;
+  const int64_t base = (static_cast<int64_t>(b) * a.Hq + g * a.G) * kD;
+  for (int h = 0; h < a.G; ++h)
+    s_q[h][i] = __uint_as_float(static_cast<uint32_t>(a.q[base + h * kD + i]) << 16);
+  __syncthreads();
+  float acc[16];
+#pragma unroll
+  for (int h = 0; h < 16; ++h) acc[h] = 0.0f;
+  const float* rowq = a.tables->rot + static_cast<int64_t>(i) * kD;
+  for (int j = 0; j < kD; ++j) {
+    const float qij = rowq[j];
+#pragma unroll
+    for (int h = 0; h < 16; ++h)
+      if (h < a.G) acc[h] = __builtin_fmaf(qij, s_q[h][j], acc[h]);
+  }
+#pragma unroll
+  for (int h = 0; h < 16; ++h)
+    if (h < a.G) q_rot[base + h * kD + i] = acc[h];
+}
+
 __global__ void __launch_bounds__(256) decode_merge_kernel(MfmaArgs a) {
   __shared__ float s_m[4], s_l[4];
   __shared__ float2 s_acc[4][64];
@@ -2236,6 +2289,14 @@ hipError_t launch_decode_mfma(const Geometry& g, const DevTables* tables, DevErr
   a.out = out;
   a.out_fp32 = out_is_fp32;
   a.dynamic = plan.dynamic;
+  a.q_rot = nullptr;
+  if (plan.qrot) {
+    float* q_rot = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.qrot_off);
+    hipLaunchKernelGGL(rotate_queries_haar_kernel, dim3(batch * g.num_kv_heads), dim3(kD), 0, stream, a, q_rot);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    a.q_rot = q_rot;
+  }
   if (plan.mfma == 4) {
     // one workgroup per (sequence, kv head, workgroup split); the merge runs
     // only when a sequence has more than one workgroup split

@@ -72,6 +72,36 @@ def test_haar_decode_parity(preset, G, d):
     check_decode(out.cpu().numpy(), want, bf16_out=False)
 
 
+@pytest.mark.parametrize("preset", MSE)
+@pytest.mark.parametrize("kernel", ["ring", "page", "staged", "direct"])
+def test_haar_decode_matrix_core_kernels(preset, kernel):
+    # head_dim 128 with the Haar rotation runs on the matrix-core kernels
+    # (the queries rotated once by a small kernel into the workspace): each
+    # of them on a ragged batch, 8 query heads per kv head (16 for the
+    # per-head kernels), fp32 and bf16 outputs
+    from packed_cache_decode_amd.runtime import PackedKVCache
+    H, seed = 2, 79
+    G = 8 if kernel in ("ring", "page") else 16
+    w = _wl(preset, H=H, Hq=G * H, d=128, seed=5, lens=(1, 900), B=5)
+    inp = synth.generate(w)
+    inp.seq_lens[0] = 0
+    ors = OracleSide(preset, 128, seed, "haar")
+    cache = np.zeros((inp.num_blocks, 16, H, ors.lay.slot_size_aligned), np.uint8)
+    ors.store(cache, inp.k, inp.v, inp.slot_mapping)
+    want = ors.decode(inp.q, cache, inp.block_table, inp.seq_lens, H)
+    tq = PackedKVCache(preset, 128, H, 16, seed, sign_flip="haar")
+    tq.set_decode_options(kernel=kernel)
+    args = (to_dev(inp.q), to_dev(cache), to_dev(inp.block_table), to_dev(inp.seq_lens),
+            int(max(1, inp.seq_lens.max())))
+    out32 = tq.decode(*args, out_fp32=True)
+    out16 = tq.decode(*args, out_fp32=False)
+    torch.cuda.synchronize()
+    assert tq.device_error() == 0
+    tq.close()
+    check_decode(out32.cpu().numpy(), want, bf16_out=False)
+    check_decode(out16.float().cpu().numpy(), want, bf16_out=True)
+
+
 @pytest.mark.parametrize("preset", ["turboquant_4bit_nc", "turboquant_3bit_nc"])
 def test_haar_split_page_store_decode_dequant(preset):
     from packed_cache_decode_amd.runtime import PackedKVCache

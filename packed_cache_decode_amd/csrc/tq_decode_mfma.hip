@@ -1434,9 +1434,12 @@ __device__ __forceinline__ void slab_tail(const SlabRegs<KB>& R, const ScoreAcc&
   } else {
     // lane (r16, g4) with r16 = 4*g4 + i holds N[4*g4 + i][4*g4 + i] as element i
     constexpr float kx = KB == 4 ? 2.0f : 1.0f;   // Nx = hi . lo (4-bit) or hi . 2 lo
-    const float n0 = A.Nh[0] + kx * A.Nx[0], n1 = A.Nh[1] + kx * A.Nx[1];
-    const float n2 = A.Nh[2] + kx * A.Nx[2], n3 = A.Nh[3] + kx * A.Nx[3];
-    const float nd = sel2 ? (sel1 ? n3 : n2) : (sel1 ? n1 : n0);
+    // the sums first, then one two-level select by the lane's row (the two
+    // lane masks are loop-invariant)
+    const f4 n = A.Nh + kx * A.Nx;
+    const float n01 = sel1 ? n[1] : n[0];
+    const float n23 = sel1 ? n[3] : n[2];
+    const float nd = sel2 ? n23 : n01;
     const float fq = f16_bits_to_f32(R.nb) * __builtin_amdgcn_rsqf(nd);
     const f4 fac = rows_to_tile(fq, diag);
 #pragma unroll

@@ -499,6 +499,14 @@ DecodePlan plan_decode_kernels(const Geometry& g, const tq_decode_options& opts,
     p.num_splits = max_seq_len > 0 ? (max_seq_len + p.chunk - 1) / p.chunk : 1;
     p.workspace_bytes = p.num_splits > 1 ? mfma_partial_bytes(batch, num_q_heads, p.num_splits) : 0;
     p.workspace_bytes = (p.workspace_bytes + 255) & ~static_cast<size_t>(255);
+    // more workgroups than one per CU: dispatch the sequences longest first,
+    // so the ones that start late are short (lengths may be ragged; the plan
+    // sees only the longest)
+    if (pairs * s > 256 && batch <= 1024) {
+      p.order = 1;
+      p.order_off = p.workspace_bytes;
+      p.workspace_bytes += (4 * static_cast<size_t>(batch) + 255) & ~static_cast<size_t>(255);
+    }
     return p;
   }
   if (mfma_decode_eligible(g, num_q_heads)) {

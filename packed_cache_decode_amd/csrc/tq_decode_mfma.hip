@@ -99,6 +99,7 @@ struct MfmaArgs {
   int out_fp32;
   int dynamic;         // ring kernel: wavefronts claim slabs from a shared counter
   const float* q_rot;  // Haar rotation: the rotated queries [B][Hq][d] (fp32), else null
+  const int32_t* order;  // ring kernel: sequence of each length rank (longest first), else null
 };
 
 __device__ __forceinline__ uint32_t pack_h2(_Float16 a, _Float16 b) {
@@ -685,6 +686,27 @@ __global__ void __launch_bounds__(kD) rotate_queries_haar_kernel(MfmaArgs a, flo
 #pragma unroll
   for (int h = 0; h < 16; ++h)
     if (h < a.G) q_rot[base + h * kD + i] = acc[h];
+}
+
+// The sequences ranked by length, longest first (ties by index):
+// order[rank] = b.  One thread per sequence; it counts the longer ones.
+__global__ void __launch_bounds__(256) order_sequences_kernel(MfmaArgs a, int32_t* order) {
+  __shared__ int s_len[256];
+  const int b = static_cast<int>(blockIdx.x) * 256 + static_cast<int>(threadIdx.x);
+  const int T = b < a.batch ? effective_len(a, b) : 0;
+  int rank = 0;
+  for (int c0 = 0; c0 < a.batch; c0 += 256) {
+    __syncthreads();
+    const int c = c0 + static_cast<int>(threadIdx.x);
+    s_len[threadIdx.x] = c < a.batch ? effective_len(a, c) : -1;
+    __syncthreads();
+    const int n = min(256, a.batch - c0);
+    for (int i = 0; i < n; ++i) {
+      const int U = s_len[i];
+      rank += (U > T || (U == T && c0 + i < b)) ? 1 : 0;
+    }
+  }
+  if (b < a.batch) order[rank] = b;
 }
 
 __global__ void __launch_bounds__(256) decode_merge_kernel(MfmaArgs a) {
@@ -1880,13 +1902,27 @@ __global__ void __launch_bounds__(64 * WAVES, kRingWaves / WAVES) decode_ring_ke
   const int g4 = lane >> 4;
   // XCD-aware order, kv head fastest: the heads of one page row run on one
   // XCD, where the cache lines their slots share come from its L2
-  const int n_items = a.num_splits * a.batch * a.H;
-  const int per_xcd = (n_items + 7) / 8;
-  const int item = static_cast<int>(blockIdx.x % 8) * per_xcd + static_cast<int>(blockIdx.x / 8);
-  if (item >= n_items) return;
-  const int g = item % a.H;                  // kv head
-  const int sg = (item / a.H) % a.num_splits;
-  const int b = item / (a.H * a.num_splits);
+  int b, g, sg;                              // sequence, kv head, workgroup split
+  if (a.order != nullptr) {
+    // sequences in length order: XCD x takes ranks x, x + 8, x + 16, ...,
+    // each with its H * splits workgroups in a row, so the workgroups the
+    // dispatcher starts first on an XCD are its longest sequences'
+    const int hs = a.H * a.num_splits;
+    const int k = static_cast<int>(blockIdx.x / 8);
+    const int rank = static_cast<int>(blockIdx.x % 8) + 8 * (k / hs);
+    if (rank >= a.batch) return;
+    b = __builtin_amdgcn_readfirstlane(a.order[rank]);
+    sg = (k % hs) / a.H;
+    g = k % a.H;
+  } else {
+    const int n_items = a.num_splits * a.batch * a.H;
+    const int per_xcd = (n_items + 7) / 8;
+    const int item = static_cast<int>(blockIdx.x % 8) * per_xcd + static_cast<int>(blockIdx.x / 8);
+    if (item >= n_items) return;
+    g = item % a.H;
+    sg = (item / a.H) % a.num_splits;
+    b = item / (a.H * a.num_splits);
+  }
 
   // this sequence's workgroup splits: a.chunk tokens at most each, the same
   // count the merge kernel derives; past them the workgroup has nothing to do
@@ -2293,6 +2329,14 @@ hipError_t launch_decode_mfma(const Geometry& g, const DevTables* tables, DevErr
   a.out_fp32 = out_is_fp32;
   a.dynamic = plan.dynamic;
   a.q_rot = nullptr;
+  a.order = nullptr;
+  if (plan.order) {
+    int32_t* order = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + plan.order_off);
+    hipLaunchKernelGGL(order_sequences_kernel, dim3((batch + 255) / 256), dim3(256), 0, stream, a, order);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    a.order = order;
+  }
   if (plan.qrot) {
     float* q_rot = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.qrot_off);
     hipLaunchKernelGGL(rotate_queries_haar_kernel, dim3(batch * g.num_kv_heads), dim3(kD), 0, stream, a, q_rot);
@@ -2303,7 +2347,8 @@ hipError_t launch_decode_mfma(const Geometry& g, const DevTables* tables, DevErr
   if (plan.mfma == 4) {
     // one workgroup per (sequence, kv head, workgroup split); the merge runs
     // only when a sequence has more than one workgroup split
-    const int n_items = plan.num_splits * batch * g.num_kv_heads;
+    const int n_items = plan.order ? 8 * ((batch + 7) / 8) * plan.num_splits * g.num_kv_heads
+                                   : plan.num_splits * batch * g.num_kv_heads;
     const dim3 grid(8 * ((n_items + 7) / 8));
     if (plan.ring_waves == 8)
       launch_ring<8>(g, grid, a, stream);

@@ -87,6 +87,9 @@ struct DecodePlan {
                       // the fp32 sums, and so the last bits, vary run to run); 0: fixed
                       // interleaved shares (reproducible bit for bit)
   int ring_waves;     // ring kernel: 16 wavefronts per workgroup (one per CU) or 8 (two per CU)
+  int order;          // ring kernel: sequences ranked by length (longest first, int32 [B])
+                      // in the workspace at byte order_off, workgroups dispatched in that order
+  size_t order_off;
   int qrot;           // Haar rotation on a matrix-core kernel: the rotated queries (fp32
                       // [B][Hq][d]) sit in the workspace at byte qrot_off
   size_t qrot_off;

@@ -119,6 +119,20 @@ def test_decode_ring_workgroup_splits(preset):
     check_decode(got, want, bf16_out=False)
 
 
+@pytest.mark.parametrize("preset", ["turboquant_4bit_nc", "turboquant_k3v4_nc"])
+@pytest.mark.parametrize("waves", ["8", "16"])
+def test_decode_ring_length_order(preset, waves):
+    # more (sequence, kv head) pairs than compute units: the ring workgroups
+    # are dispatched in the order of a device-side ranking of the lengths
+    # (ragged, with empty, one-token and equal lengths)
+    rng = np.random.default_rng(17)
+    lens = [int(x) for x in rng.integers(0, 1500, size=40)]
+    lens[:5] = [0, 1, 700, 700, 1499]
+    w = _wl(preset, G=2, H=8, B=40, lens=(1500, 1500), seed=67)
+    got, want = _decode_from_oracle_cache(w, lens=lens, opts=dict(kernel="ring", ring_waves=int(waves)))
+    check_decode(got, want, bf16_out=False)
+
+
 @pytest.mark.parametrize("preset", ["turboquant_4bit_nc", "turboquant_k3v4_nc", "turboquant_3bit_nc"])
 @pytest.mark.parametrize("waves", ["8", "16"])
 def test_decode_ring_workgroup_sizes(preset, waves):

@@ -226,3 +226,15 @@ def test_soa_decode_ring_workgroup_sizes(preset, waves):
         got, want = _decode_soa(w, lens=[0, 3, 700, 16400, 20000],
                                 opts=dict(ring_waves=int(waves), dynamic_claims=dyn))
         check_decode(got, want, bf16_out=False)
+
+
+@pytest.mark.parametrize("preset", MSE)
+def test_soa_decode_ring_length_order(preset):
+    # more (sequence, kv head) pairs than compute units, ragged lengths: the
+    # length-ordered dispatch on the split page
+    rng = np.random.default_rng(19)
+    lens = [int(x) for x in rng.integers(0, 1200, size=36)]
+    lens[:3] = [0, 1, 1199]
+    w = _wl(preset, H=8, Hq=32, lens=(1200, 1200), B=36, seed=75)
+    got, want = _decode_soa(w, lens=lens)
+    check_decode(got, want, bf16_out=False)

@@ -131,6 +131,12 @@ def test_decode_ring_length_order(preset, waves):
     w = _wl(preset, G=2, H=8, B=40, lens=(1500, 1500), seed=67)
     got, want = _decode_from_oracle_cache(w, lens=lens, opts=dict(kernel="ring", ring_waves=int(waves)))
     check_decode(got, want, bf16_out=False)
+    # a larger batch (150 sequences, more ranks than one wavefront holds)
+    lens = [int(x) for x in rng.integers(0, 500, size=150)]
+    lens[:3] = [0, 499, 499]
+    w = _wl(preset, G=4, H=2, B=150, lens=(500, 500), seed=69)
+    got, want = _decode_from_oracle_cache(w, lens=lens, opts=dict(kernel="ring", ring_waves=int(waves)))
+    check_decode(got, want, bf16_out=False)
 
 
 @pytest.mark.parametrize("preset", ["turboquant_4bit_nc", "turboquant_k3v4_nc", "turboquant_3bit_nc"])

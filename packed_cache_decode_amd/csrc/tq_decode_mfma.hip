@@ -383,7 +383,7 @@ constexpr int vbits_of_slot(int slot) { return slot == 102 ? 3 : 4; }
 // (Codes left as f16 subnormals, c * 2^-24, need no subtraction, but the
 // matrix cores do not sum products with subnormal inputs exactly: decode
 // errors grew about 100-fold.)
-template <int VB>
+template <int VB, bool BFI = true>
 __device__ __forceinline__ void v_operands(const uint32_t (&X)[4], int kb, h4& Blo, h4& Bhi) {
   const h2 b1024 = {static_cast<_Float16>(1024.0f), static_cast<_Float16>(1024.0f)};
   if constexpr (VB == 4) {
@@ -392,10 +392,14 @@ __device__ __forceinline__ void v_operands(const uint32_t (&X)[4], int kb, h4& B
     const uint32_t sel = kb | (0x0Cu << 8) | ((4u + kb) << 16) | (0x0Cu << 24);
     const uint32_t p01 = __builtin_amdgcn_perm(X[1], X[0], sel);
     const uint32_t p23 = __builtin_amdgcn_perm(X[3], X[2], sel);
-    const h2 lo01 = __builtin_bit_cast(h2, (p01 & 0x000F000Fu) | 0x64006400u) - b1024;
-    const h2 lo23 = __builtin_bit_cast(h2, (p23 & 0x000F000Fu) | 0x64006400u) - b1024;
-    const h2 hi01 = __builtin_bit_cast(h2, (p01 & 0x00F000F0u) | 0x54005400u) - b64;
-    const h2 hi23 = __builtin_bit_cast(h2, (p23 & 0x00F000F0u) | 0x54005400u) - b64;
+    // nibbles into the mantissas: one bit-field insert each (its two masks
+    // take two registers; BFI = false spells it as and + or where that
+    // pressure would spill)
+    auto ins = [](uint32_t x, uint32_t m, uint32_t c) { return BFI ? insert_bits(x, m, c) : (x & m) | c; };
+    const h2 lo01 = __builtin_bit_cast(h2, ins(p01, 0x000F000Fu, 0x64006400u)) - b1024;
+    const h2 lo23 = __builtin_bit_cast(h2, ins(p23, 0x000F000Fu, 0x64006400u)) - b1024;
+    const h2 hi01 = __builtin_bit_cast(h2, ins(p01, 0x00F000F0u, 0x54005400u)) - b64;
+    const h2 hi23 = __builtin_bit_cast(h2, ins(p23, 0x00F000F0u, 0x54005400u)) - b64;
     Blo = h4{lo01[0], lo01[1], lo23[0], lo23[1]};
     Bhi = h4{hi01[0], hi01[1], hi23[0], hi23[1]};
   } else {
@@ -524,7 +528,7 @@ __device__ __forceinline__ void softmax_rescale(const SlabSoftmax& sm, bool diag
 // rows h + 8 its lo part (those lanes hold a copy of head h's scores and
 // running state), so each MFMA has k = 16 tokens and V operands that are
 // exactly the decoded codes; fold_lo_rows adds the lo rows in at the end.
-template <int VB>
+template <int VB, bool BFI = true>
 __device__ __forceinline__ void softmax_accumulate(const float (&s)[4], const SlabSoftmax& sm,
                                                    const uint32_t (&X)[4], RunState& st) {
   const bool lo_row = (threadIdx.x & 8) != 0;
@@ -541,7 +545,7 @@ __device__ __forceinline__ void softmax_accumulate(const float (&s)[4], const Sl
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb) {
     h4 Blo, Bhi;
-    v_operands<VB>(X, kb, Blo, Bhi);
+    v_operands<VB, BFI>(X, kb, Blo, Bhi);
     st.O[2 * kb] = __builtin_amdgcn_mfma_f32_16x16x16f16(W, Blo, st.O[2 * kb], 0, 0, 0);
     st.O[2 * kb + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(W, Bhi, st.O[2 * kb + 1], 0, 0, 0);
   }
@@ -2112,11 +2116,11 @@ __global__ void __launch_bounds__(64 * WAVES, kRingWaves / WAVES) decode_ring_ke
           grow = true;
           break;
         }
-        softmax_accumulate<VB>(s, sm, c.X, st);
+        softmax_accumulate<VB, !kDup>(s, sm, c.X, st);
       }
       if (!grow) break;
       softmax_rescale(sm, diag, st);
-      softmax_accumulate<VB>(s, sm, c.X, st);
+      softmax_accumulate<VB, !kDup>(s, sm, c.X, st);
       ++j;
     }
     wait_vmcnt<0>();                         // no load may still write the ring

@@ -1868,6 +1868,7 @@ constexpr int kRingBufs = 3;                 // slabs per wavefront ring (two in
 constexpr int kRingWaves = 16;               // wavefronts per workgroup (one workgroup per CU),
                                              // or half as many (two per CU; see ring_waves)
 constexpr int kRingMaxSlabs = 1024;          // slabs per workgroup split: its page ids fit in LDS
+constexpr int kXcdCus = 32;                  // CUs of one XCD (256 CUs in 8 XCDs)
 
 template <int KB, int SLOT, bool SOA, int WAVES>
 __global__ void __launch_bounds__(64 * WAVES, kRingWaves / WAVES) decode_ring_kernel(MfmaArgs a) {
@@ -1910,10 +1911,24 @@ __global__ void __launch_bounds__(64 * WAVES, kRingWaves / WAVES) decode_ring_ke
   if (a.order != nullptr) {
     // sequences in length order: XCD x takes ranks x, x + 8, x + 16, ...,
     // each with its H * splits workgroups in a row, so the workgroups the
-    // dispatcher starts first on an XCD are its longest sequences'
+    // dispatcher starts first on an XCD are its longest sequences'.  The
+    // dispatcher gives each of an XCD's 32 CUs one workgroup of the first 32
+    // before any CU a second; with two workgroups per CU (8 wavefronts) the
+    // second 32 take their sequences in reverse order, so a CU that runs one
+    // of the longest sequences also runs one of the shortest of the pair of
+    // layers (k3v4-shaped ragged decode 120 -> 108 us); later layers start as
+    // CUs free up and keep the longest-first order.
     const int hs = a.H * a.num_splits;
     const int k = static_cast<int>(blockIdx.x / 8);
-    const int rank = static_cast<int>(blockIdx.x % 8) + 8 * (k / hs);
+    int q = k / hs;                          // this XCD's q-th sequence in length order
+    // (both layers whole: every XCD has at least 2 * kXcdCus workgroups, so
+    // the reversed layer's positions all exist)
+    const bool two_layers = ((a.batch + 7) / 8) * hs >= 2 * kXcdCus;
+    if (kRingWaves / WAVES == 2 && kXcdCus % hs == 0 && two_layers && k < 2 * kXcdCus) {
+      const int per_layer = kXcdCus / hs, u = (k % kXcdCus) / hs;
+      q = k < kXcdCus ? u : 2 * per_layer - 1 - u;
+    }
+    const int rank = static_cast<int>(blockIdx.x % 8) + 8 * q;
     if (rank >= a.batch) return;
     b = __builtin_amdgcn_readfirstlane(a.order[rank]);
     sg = (k % hs) / a.H;

@@ -137,6 +137,16 @@ def test_decode_ring_length_order(preset, waves):
     w = _wl(preset, G=4, H=2, B=150, lens=(500, 500), seed=69)
     got, want = _decode_from_oracle_cache(w, lens=lens, opts=dict(kernel="ring", ring_waves=int(waves)))
     check_decode(got, want, bf16_out=False)
+    # at least two whole layers of workgroups per XCD (the 8-wavefront
+    # workgroups then pair long with short sequences on each CU): 61
+    # sequences x 8 kv heads (some XCDs one sequence short), and 150 x 4
+    # (more layers than the two resident ones)
+    for B, H, seed in ((61, 8, 71), (150, 4, 73)):
+        lens = [int(x) for x in rng.integers(0, 400, size=B)]
+        lens[:4] = [0, 1, 399, 399]
+        w = _wl(preset, G=2, H=H, B=B, lens=(400, 400), seed=seed)
+        got, want = _decode_from_oracle_cache(w, lens=lens, opts=dict(kernel="ring", ring_waves=int(waves)))
+        check_decode(got, want, bf16_out=False)
 
 
 @pytest.mark.parametrize("preset", ["turboquant_4bit_nc", "turboquant_k3v4_nc", "turboquant_3bit_nc"])

@@ -238,3 +238,10 @@ def test_soa_decode_ring_length_order(preset):
     w = _wl(preset, H=8, Hq=32, lens=(1200, 1200), B=36, seed=75)
     got, want = _decode_soa(w, lens=lens)
     check_decode(got, want, bf16_out=False)
+    # two whole layers of 8-wavefront workgroups per XCD (long and short
+    # sequences paired on each CU), some XCDs one sequence short
+    lens = [int(x) for x in rng.integers(0, 400, size=61)]
+    lens[:3] = [0, 1, 399]
+    w = _wl(preset, H=8, Hq=16, lens=(400, 400), B=61, seed=77)
+    got, want = _decode_soa(w, lens=lens, opts=dict(ring_waves=8))
+    check_decode(got, want, bf16_out=False)

@@ -1913,22 +1913,25 @@ __global__ void __launch_bounds__(64 * WAVES, kRingWaves / WAVES) decode_ring_ke
     // each with its H * splits workgroups in a row, so the workgroups the
     // dispatcher starts first on an XCD are its longest sequences'.  The
     // dispatcher gives each of an XCD's 32 CUs one workgroup of the first 32
-    // before any CU a second; with two workgroups per CU (8 wavefronts) the
-    // second 32 take their sequences in reverse order, so a CU that runs one
-    // of the longest sequences also runs one of the shortest of the pair of
-    // layers (k3v4-shaped ragged decode 120 -> 108 us); later layers start as
-    // CUs free up and keep the longest-first order.
+    // before any CU a second.  With two workgroups per CU (8 wavefronts) and
+    // two whole layers on every XCD, the second layer takes the ranks of the
+    // first mirrored about the middle of the two layers' ranks, so the CU
+    // that runs rank i also runs rank 16 P - 1 - i (P sequences per layer):
+    // the longest with the shortest, as even a pairing as the lengths allow
+    // (k3v4-shaped ragged decode 120 -> 108 us).  Later layers start as CUs
+    // free up and keep the longest-first order.
     const int hs = a.H * a.num_splits;
     const int k = static_cast<int>(blockIdx.x / 8);
-    int q = k / hs;                          // this XCD's q-th sequence in length order
+    const int x = static_cast<int>(blockIdx.x % 8);
+    int rank = x + 8 * (k / hs);
     // (both layers whole: every XCD has at least 2 * kXcdCus workgroups, so
-    // the reversed layer's positions all exist)
+    // the ranks below 16 P are all dealt out once)
     const bool two_layers = ((a.batch + 7) / 8) * hs >= 2 * kXcdCus;
     if (kRingWaves / WAVES == 2 && kXcdCus % hs == 0 && two_layers && k < 2 * kXcdCus) {
-      const int per_layer = kXcdCus / hs, u = (k % kXcdCus) / hs;
-      q = k < kXcdCus ? u : 2 * per_layer - 1 - u;
+      const int per_layer = kXcdCus / hs;
+      const int r0 = x + 8 * ((k % kXcdCus) / hs);
+      rank = k < kXcdCus ? r0 : 16 * per_layer - 1 - r0;
     }
-    const int rank = static_cast<int>(blockIdx.x % 8) + 8 * q;
     if (rank >= a.batch) return;
     b = __builtin_amdgcn_readfirstlane(a.order[rank]);
     sg = (k % hs) / a.H;

@@ -240,6 +240,7 @@ def main():
     w = synth.WORKLOADS[args.workload]
     print(f"[bench] generating {w.name}", file=sys.stderr, flush=True)
     inp = synth.generate(w)
+    synth.assert_unique_slots(inp.slot_mapping)      # one store may not write a slot twice
 
     def up(a):
         if a.dtype == np.uint16:

@@ -55,15 +55,18 @@ _i32 = ctypes.c_int32
 _int = ctypes.c_int
 
 
-def load():
-    """Load the in-tree HIP library (raises OSError if it is not built)."""
+def load(path=None):
+    """Load the in-tree HIP library (raises OSError if it is not built).
+    ``path`` loads another build of it instead (the host-sanitizer build of
+    build_lib.build_host_asan); that one becomes the module's library."""
     global _lib
-    if _lib is not None:
+    if _lib is not None and path is None:
         return _lib
-    if not os.path.exists(LIB_PATH):
-        raise OSError(f"HIP library not built: {LIB_PATH} (run python -m "
+    path = path or LIB_PATH
+    if not os.path.exists(path):
+        raise OSError(f"HIP library not built: {path} (run python -m "
                       f"packed_cache_decode_amd.build_lib)")
-    lib = ctypes.CDLL(LIB_PATH)
+    lib = ctypes.CDLL(path)
     sig = {
         "tq_codebook_init": (_int, [ctypes.POINTER(_vp), _int, _int, _int, _int, ctypes.c_uint64,
                                     _int, _int, _vp]),

@@ -62,5 +62,40 @@ def build(verbose=False):
     return LIB
 
 
+ASAN_DIR = os.path.join(BUILD, "asan")
+ASAN_LIB = os.path.join(ASAN_DIR, "libtq_mi355x_asan.so")
+
+
+def asan_runtime():
+    """Path of the compiler's shared AddressSanitizer runtime (None if absent)."""
+    import glob
+    root = os.path.dirname(os.path.dirname(os.path.realpath(HIPCC)))
+    hits = sorted(glob.glob(os.path.join(root, "lib", "llvm", "lib", "clang", "*", "lib", "linux",
+                                         "libclang_rt.asan-x86_64.so")))
+    return hits[-1] if hits else None
+
+
+def build_host_asan():
+    """The library with its host code (tq_host.cpp: codebook solvers, tables,
+    planning, argument checks) built with AddressSanitizer, device code as in
+    build(); for CPU checks of the host logic (load it in a process started
+    with the sanitizer runtime preloaded).  Needs build()'s objects."""
+    os.makedirs(ASAN_DIR, exist_ok=True)
+    objs = []
+    for src, extra in SOURCES:
+        obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+        if src == "tq_host.cpp":
+            obj = os.path.join(ASAN_DIR, "tq_host.o")
+            # host pass only: each sanitizer flag behind -Xarch_host
+            _run([HIPCC, *COMMON, "-x", "hip", *extra, "-Xarch_host", "-fsanitize=address",
+                  "-Xarch_host", "-fno-omit-frame-pointer", "-c", os.path.join(CSRC, src), "-o", obj])
+        elif not os.path.exists(obj):
+            raise RuntimeError(f"{obj} missing: run build() first")
+        objs.append(obj)
+    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Xarch_host", "-fsanitize=address",
+          "-shared-libasan", "-o", ASAN_LIB, *objs])
+    return ASAN_LIB
+
+
 if __name__ == "__main__":
     print(build(verbose=True))

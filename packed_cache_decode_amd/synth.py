@@ -18,6 +18,10 @@ distributions stand in for real activations:
     next ceil(T_b / block_size) page ids; unused table entries are 0.
   * slot_mapping for the cache fill: token t of sequence b goes to slot
     block_table[b][t // bs] * bs + t % bs.
+
+Two tokens written to one slot in one store race (the library leaves that
+undefined; a serving scheduler hands out unique slots), so every mapping
+drawn here passes assert_unique_slots, which the benchmark also applies.
 """
 
 from dataclasses import dataclass, field, replace
@@ -25,6 +29,18 @@ from dataclasses import dataclass, field, replace
 import numpy as np
 
 PRESET_NAMES = ("turboquant_k8v4", "turboquant_4bit_nc", "turboquant_k3v4_nc", "turboquant_3bit_nc")
+
+
+def assert_unique_slots(slot_mapping):
+    """Raise ValueError if two tokens of one store map to the same slot
+    (negative entries are padding tokens and may repeat)."""
+    sm = np.asarray(slot_mapping).reshape(-1)
+    live = sm[sm >= 0]
+    if live.size:
+        u, counts = np.unique(live, return_counts=True)
+        if (counts > 1).any():
+            dup = u[counts > 1]
+            raise ValueError(f"slot_mapping holds {dup.size} duplicate slots (first: {int(dup[0])})")
 
 
 def f32_to_bf16_bits(x):
@@ -159,6 +175,7 @@ def generate(w, with_kv=True):
         t = np.arange(int(seq_lens[b]), dtype=np.int64)
         slot_parts.append(block_table[b, t // bs].astype(np.int64) * bs + t % bs)
     slot_mapping = np.concatenate(slot_parts) if slot_parts else np.zeros(0, np.int64)
+    assert_unique_slots(slot_mapping)
     S = _channel_scales(rng, w)
     q = f32_to_bf16_bits(rng.standard_normal((B, Hq, d), dtype=np.float32))
     N = int(seq_lens.sum())

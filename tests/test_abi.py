@@ -23,8 +23,8 @@ def _header_functions(name="tq.h"):
 
 
 @pytest.fixture(scope="module")
-def lib():
-    return _lib.load()
+def lib(request):
+    return _lib.load(request.config.getoption("--tq-lib"))
 
 
 def test_exports_every_declared_symbol(lib):

@@ -1891,7 +1891,8 @@ __global__ void __launch_bounds__(64 * WAVES, kRingWaves / WAVES) decode_ring_ke
     u32x2 tab[256];
     int32_t pid[kRingMaxSlabs];
     int32_t next;                            // the workgroup's next unclaimed slab
-    int32_t pad[3];
+    int32_t started;                         // slabs its wavefronts have started, all told
+    int32_t pad[2];
     uint8_t ring[WAVES][kRing];
   };
   static_assert(offsetof(RingLds, ring) % 16 == 0, "rings on 16-byte boundaries");
@@ -1961,11 +1962,15 @@ __global__ void __launch_bounds__(64 * WAVES, kRingWaves / WAVES) decode_ring_ke
 
   build_tables_page<KB>(a, s_tab);
   if (n_wg > 0) stage_page_ids(a, b, 16 * wg0, t_end, s_pid);
-  if (threadIdx.x == 0) s_next = 0;
+  if (threadIdx.x == 0) {
+    s_next = 0;
+    lds.started = 0;
+  }
   // 4-bit keys on the split page: the duplicated query operands of score4
   // (the slotted page keeps the separate hi and lo MFMAs, whose norm terms
   // it needs anyway; measured faster there)
   constexpr bool kDup = KB == 4 && SOA;
+  constexpr bool kBalance = WAVES == kRingWaves;   // issue priority to lagging wavefronts (below)
   h8 qv[4];
   bf8v qb[4];
   h8 qd[kDup ? 8 : 1];
@@ -2091,7 +2096,21 @@ __global__ void __launch_bounds__(64 * WAVES, kRingWaves / WAVES) decode_ring_ke
         // wavefront's reads of slab j - 1 have completed, so its buffer takes
         // the next claim
         wait_vmcnt<kLoads * (kBufs - 2)>();
+        // One workgroup per CU (16 wavefronts): the wavefronts of a SIMD do
+        // not progress at one rate, and the slowest sets the workgroup's
+        // end.  A wavefront more than one slab behind the workgroup's mean
+        // takes the highest issue priority until it has caught up (which
+        // slabs it sums is unchanged, so the result is too; long_131k-shaped
+        // decode 161 -> 147 us).  With two workgroups per CU the priorities
+        // would also reorder the workgroups against each other: left off.
+        int started = 0;
+        if (kBalance && lane == 0) started = atomicAdd(&lds.started, 1);
         __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+        if constexpr (kBalance) {
+          started = __builtin_amdgcn_readfirstlane(started);
+          if ((j + 1) * WAVES < started) __builtin_amdgcn_s_setprio(3);
+          else __builtin_amdgcn_s_setprio(0);
+        }
         const int cur = qc[0];
 #pragma unroll
         for (int i = 0; i + 1 < kBufs - 1; ++i) qc[i] = qc[i + 1];
@@ -2141,6 +2160,7 @@ __global__ void __launch_bounds__(64 * WAVES, kRingWaves / WAVES) decode_ring_ke
       softmax_accumulate<VB, !kDup>(s, sm, c.X, st);
       ++j;
     }
+    if constexpr (kBalance) __builtin_amdgcn_s_setprio(0);
     wait_vmcnt<0>();                         // no load may still write the ring
   }
 

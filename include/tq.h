@@ -262,6 +262,11 @@ size_t tq_decode_workspace_bytes(const tq_ctx* ctx, int batch, int num_q_heads,
  *                  share a workspace must not overlap; may be NULL when
  *                  that size is 0
  *
+ * More than 16 query heads per kv head run on the matrix-core kernels
+ * (head_dim 128, block_size a multiple of 16) in passes of 16 query heads
+ * (8 on the split page), each pass reading the cache; other shapes with
+ * more than 16 return TQ_ERR_UNSUPPORTED.
+ *
  * Reproducibility.  The plan (kernel, split count, order of the fp32 sums)
  * depends only on the shape arguments and the context's decode options, so
  * with the default options identical inputs give bit-identical outputs.

@@ -543,6 +543,10 @@ DecodePlan plan_decode_kernels(const Geometry& g, const tq_decode_options& opts,
 DecodePlan plan_decode(const Geometry& g, const tq_decode_options& opts, int batch, int num_q_heads,
                        int max_seq_len) {
   DecodePlan p = plan_decode_kernels(g, opts, batch, num_q_heads, max_seq_len);
+  if (p.mfma != 0) {
+    const int G = num_q_heads / g.num_kv_heads;
+    p.g_pass = G < mfma_max_g(p.mfma) ? G : mfma_max_g(p.mfma);
+  }
   if (g.haar && p.mfma != 0) {
     // the matrix-core kernels read the queries rotated by the Haar matrix
     // from the workspace, after the split partials

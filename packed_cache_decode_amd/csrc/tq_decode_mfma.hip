@@ -88,7 +88,9 @@ struct MfmaArgs {
   const int32_t* seq_lens;
   int Hq;
   int H;
-  int G;
+  int G;               // query heads of this pass (per kv head)
+  int Gq;              // query heads per kv head in q, out and the partials
+  int h0;              // first query head (of its kv head) of this pass
   int bs_shift;
   int chunk;           // tokens per split, a multiple of 16
   int num_splits;
@@ -194,7 +196,7 @@ __device__ __forceinline__ void load_queries(const MfmaArgs& a, int b, int g, in
                                              float fscale, h8 (&qhi)[4], h8 (&qlo)[4]) {
   float x[32];
   const bool live = r16 < a.G;
-  const int64_t row = (static_cast<int64_t>(b) * a.Hq + g * a.G + (live ? r16 : 0)) * kD + 32 * g4;
+  const int64_t row = (static_cast<int64_t>(b) * a.Hq + g * a.Gq + a.h0 + (live ? r16 : 0)) * kD + 32 * g4;
   if (a.q_rot != nullptr) {
     const float4* rp = reinterpret_cast<const float4*>(a.q_rot + row);
 #pragma unroll
@@ -280,7 +282,7 @@ __device__ __forceinline__ uint32_t insert_bits(uint32_t x, uint32_t m, uint32_t
 __device__ __forceinline__ void load_queries_bf16(const MfmaArgs& a, int b, int g, int r16, int g4,
                                                   bf8v (&qb)[4]) {
   const bool live = r16 < a.G;
-  const uint16_t* qp = a.q + (static_cast<int64_t>(b) * a.Hq + g * a.G + (live ? r16 : 0)) * kD + 32 * g4;
+  const uint16_t* qp = a.q + (static_cast<int64_t>(b) * a.Hq + g * a.Gq + a.h0 + (live ? r16 : 0)) * kD + 32 * g4;
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) {
     u32x4 w = *reinterpret_cast<const u32x4*>(qp + 8 * kk);
@@ -638,7 +640,7 @@ __device__ __forceinline__ void store_partials(const MfmaArgs& a, int b, int g, 
   const float l_part = sum_x32(sum_x16(st.l_part));
   const float z_part = sum_x32(sum_x16(st.z_part));
   const int G = a.G;
-  const int64_t rec0 = (static_cast<int64_t>(b) * a.Hq + g * G) * a.num_splits + split;
+  const int64_t rec0 = (static_cast<int64_t>(b) * a.Hq + g * a.Gq + a.h0) * a.num_splits + split;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int h = 4 * g4 + r;
@@ -673,7 +675,7 @@ __global__ void __launch_bounds__(kD) rotate_queries_haar_kernel(MfmaArgs a, flo
   __shared__ float s_q[16][kD];
   const int b = blockIdx.x / a.H, g = blockIdx.x - b * a.H;
   const int i = threadIdx.x;
-  const int64_t base = (static_cast<int64_t>(b) * a.Hq + g * a.G) * kD;
+  const int64_t base = (static_cast<int64_t>(b) * a.Hq + g * a.Gq + a.h0) * kD;
   for (int h = 0; h < a.G; ++h)
     s_q[h][i] = __uint_as_float(static_cast<uint32_t>(a.q[base + h * kD + i]) << 16);
   __syncthreads();
@@ -2213,7 +2215,7 @@ __global__ void __launch_bounds__(64 * WAVES, kRingWaves / WAVES) decode_ring_ke
       L = L * cM + wv * rec[kD + 1];
       M = m_new;
     }
-    const int hq = g * a.G + h;
+    const int hq = g * a.Gq + a.h0 + h;
     if (a.num_splits == 1) {
       const float inv = L > 0.0f ? 1.0f / L : 0.0f;
       const float r0 = acc.x * inv, r1 = acc.y * inv;
@@ -2306,11 +2308,18 @@ void launch_ring(const Geometry& g, dim3 grid, const MfmaArgs& a, hipStream_t st
     hipLaunchKernelGGL((decode_ring_kernel<3, 102, false, WAVES>), grid, block, 0, stream, a);
 }
 
+// 3/4-bit keys with up to 8 query heads per kv head on the slotted page (more
+// take the per-head kernels' 16), any count on the split page (passes of 8)
 bool ring_decode_eligible(const Geometry& g, int num_q_heads) {
   const int G = num_q_heads / g.num_kv_heads;
-  return g.head_dim == kD && g.block_size % 16 == 0 && G >= 1 && G <= 8 &&
+  return g.head_dim == kD && g.block_size % 16 == 0 && G >= 1 && (G <= 8 || g.soa) &&
          ((g.key_bits == 4 && g.slot == 134) || (g.key_bits == 3 && (g.slot == 118 || g.slot == 102)));
 }
+
+// query heads per kv head one pass of a matrix-core kernel takes: the ring
+// and page kernels hold a head's query hi and lo parts in one 16-column
+// operand (8), the per-head kernels 16
+int mfma_max_g(int mfma) { return mfma == 2 || mfma == 4 ? 8 : 16; }
 
 int ring_max_slabs() { return kRingMaxSlabs; }
 
@@ -2334,7 +2343,7 @@ bool mfma_decode_eligible(const Geometry& g, int num_q_heads) {
   // slotted pages (the split page has the ring kernel, ring_decode_eligible)
   if (g.soa) return false;
   const int G = num_q_heads / g.num_kv_heads;
-  if (g.head_dim != kD || g.block_size % 16 != 0 || G < 1 || G > 16) return false;
+  if (g.head_dim != kD || g.block_size % 16 != 0 || G < 1) return false;   // G > 16: passes of 16
   if (g.key_bits == 8) return g.slot == 196;
   return (g.key_bits == 4 || g.key_bits == 3) && (g.slot == 134 || g.slot == 118 || g.slot == 102);
 }
@@ -2360,7 +2369,7 @@ hipError_t launch_decode_mfma(const Geometry& g, const DevTables* tables, DevErr
   a.seq_lens = seq_lens;
   a.Hq = num_q_heads;
   a.H = g.num_kv_heads;
-  a.G = num_q_heads / g.num_kv_heads;
+  a.Gq = num_q_heads / g.num_kv_heads;
   a.bs_shift = __builtin_ctz(static_cast<unsigned>(g.block_size));
   a.chunk = plan.chunk;
   a.num_splits = plan.num_splits;
@@ -2373,64 +2382,72 @@ hipError_t launch_decode_mfma(const Geometry& g, const DevTables* tables, DevErr
   a.q_rot = nullptr;
   a.order = nullptr;
   if (plan.order) {
+    a.h0 = 0;
+    a.G = a.Gq;
     int32_t* order = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + plan.order_off);
     hipLaunchKernelGGL(order_sequences_kernel, dim3((batch + 255) / 256), dim3(256), 0, stream, a, order);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     a.order = order;
   }
-  if (plan.qrot) {
-    float* q_rot = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.qrot_off);
-    hipLaunchKernelGGL(rotate_queries_haar_kernel, dim3(batch * g.num_kv_heads), dim3(kD), 0, stream, a, q_rot);
+  float* q_rot = plan.qrot ? reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.qrot_off) : nullptr;
+  // query heads in passes of at most plan.g_pass per kv head (each pass
+  // reads the cache again); every pass writes its heads' outputs or split
+  // records, and one merge at the end combines the records of all heads
+  const int g_pass = plan.g_pass > 0 ? plan.g_pass : a.Gq;
+  for (int h0 = 0; h0 < a.Gq; h0 += g_pass) {
+    a.h0 = h0;
+    a.G = a.Gq - h0 < g_pass ? a.Gq - h0 : g_pass;
+    if (q_rot != nullptr) {
+      a.q_rot = nullptr;
+      hipLaunchKernelGGL(rotate_queries_haar_kernel, dim3(batch * g.num_kv_heads), dim3(kD), 0, stream, a, q_rot);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      a.q_rot = q_rot;
+    }
+    if (plan.mfma == 4) {
+      // one workgroup per (sequence, kv head, workgroup split)
+      const int n_items = plan.order ? 8 * ((batch + 7) / 8) * plan.num_splits * g.num_kv_heads
+                                     : plan.num_splits * batch * g.num_kv_heads;
+      const dim3 grid(8 * ((n_items + 7) / 8));
+      if (plan.ring_waves == 8)
+        launch_ring<8>(g, grid, a, stream);
+      else
+        launch_ring<kRingWaves>(g, grid, a, stream);
+    } else if (plan.mfma == 2) {
+      hipError_t e = g.key_bits == 8 ? launch_page_h<8, 196>(a, batch, plan.group, stream)
+                   : g.key_bits == 4 ? launch_page_h<4, 134>(a, batch, plan.group, stream)
+                   : g.slot == 118   ? launch_page_h<3, 118>(a, batch, plan.group, stream)
+                                     : launch_page_h<3, 102>(a, batch, plan.group, stream);
+      if (e != hipSuccess) return e;
+    } else {
+      // one wavefront per workgroup: (split, sequence, kv head)
+      const int n_items = plan.num_splits * batch * g.num_kv_heads;
+      const dim3 grid(8 * ((n_items + 7) / 8));
+      if (plan.mfma == 3) {
+        if (g.key_bits == 4)
+          hipLaunchKernelGGL((decode_staged_kernel<4, 134>), grid, dim3(64), 0, stream, a);
+        else if (g.slot == 118)
+          hipLaunchKernelGGL((decode_staged_kernel<3, 118>), grid, dim3(64), 0, stream, a);
+        else
+          hipLaunchKernelGGL((decode_staged_kernel<3, 102>), grid, dim3(64), 0, stream, a);
+      } else if (g.key_bits == 8)
+        hipLaunchKernelGGL((decode_slab_kernel<8, 196>), grid, dim3(64), 0, stream, a);
+      else if (g.key_bits == 4)
+        hipLaunchKernelGGL((decode_slab_kernel<4, 134>), grid, dim3(64), 0, stream, a);
+      else if (g.slot == 118)
+        hipLaunchKernelGGL((decode_slab_kernel<3, 118>), grid, dim3(64), 0, stream, a);
+      else
+        hipLaunchKernelGGL((decode_slab_kernel<3, 102>), grid, dim3(64), 0, stream, a);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    a.q_rot = q_rot;
   }
-  if (plan.mfma == 4) {
-    // one workgroup per (sequence, kv head, workgroup split); the merge runs
-    // only when a sequence has more than one workgroup split
-    const int n_items = plan.order ? 8 * ((batch + 7) / 8) * plan.num_splits * g.num_kv_heads
-                                   : plan.num_splits * batch * g.num_kv_heads;
-    const dim3 grid(8 * ((n_items + 7) / 8));
-    if (plan.ring_waves == 8)
-      launch_ring<8>(g, grid, a, stream);
-    else
-      launch_ring<kRingWaves>(g, grid, a, stream);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess || plan.num_splits == 1) return e;
-    hipLaunchKernelGGL(decode_merge_kernel, dim3(batch * num_q_heads), dim3(256), 0, stream, a);
-    return hipGetLastError();
-  }
-  if (plan.mfma == 2) {
-    hipError_t e = g.key_bits == 8 ? launch_page_h<8, 196>(a, batch, plan.group, stream)
-                 : g.key_bits == 4 ? launch_page_h<4, 134>(a, batch, plan.group, stream)
-                 : g.slot == 118   ? launch_page_h<3, 118>(a, batch, plan.group, stream)
-                                   : launch_page_h<3, 102>(a, batch, plan.group, stream);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(decode_merge_kernel, dim3(batch * num_q_heads), dim3(256), 0, stream, a);
-    return hipGetLastError();
-  }
-  // one wavefront per workgroup: (split, sequence, kv head)
-  const int n_items = plan.num_splits * batch * g.num_kv_heads;
-  const dim3 grid(8 * ((n_items + 7) / 8));
-  if (plan.mfma == 3) {
-    if (g.key_bits == 4)
-      hipLaunchKernelGGL((decode_staged_kernel<4, 134>), grid, dim3(64), 0, stream, a);
-    else if (g.slot == 118)
-      hipLaunchKernelGGL((decode_staged_kernel<3, 118>), grid, dim3(64), 0, stream, a);
-    else
-      hipLaunchKernelGGL((decode_staged_kernel<3, 102>), grid, dim3(64), 0, stream, a);
-  } else if (g.key_bits == 8)
-    hipLaunchKernelGGL((decode_slab_kernel<8, 196>), grid, dim3(64), 0, stream, a);
-  else if (g.key_bits == 4)
-    hipLaunchKernelGGL((decode_slab_kernel<4, 134>), grid, dim3(64), 0, stream, a);
-  else if (g.slot == 118)
-    hipLaunchKernelGGL((decode_slab_kernel<3, 118>), grid, dim3(64), 0, stream, a);
-  else
-    hipLaunchKernelGGL((decode_slab_kernel<3, 102>), grid, dim3(64), 0, stream, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  // merge: one workgroup per (sequence, query head)
+  // merge: one workgroup per (sequence, query head); the ring kernel writes
+  // the output itself when a sequence has one workgroup split
+  if (plan.mfma == 4 && plan.num_splits == 1) return hipSuccess;
+  a.h0 = 0;
+  a.G = a.Gq;
   hipLaunchKernelGGL(decode_merge_kernel, dim3(batch * num_q_heads), dim3(256), 0, stream, a);
   return hipGetLastError();
 }

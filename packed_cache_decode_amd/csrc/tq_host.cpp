@@ -496,8 +496,11 @@ tq_status decode_impl(const tq_ctx* ctx, const void* q, const uint8_t* cache, in
       max_blocks_per_seq < 0)
     return TQ_ERR_INVALID_ARG;
   if (num_q_heads % g.num_kv_heads != 0) return TQ_ERR_INVALID_ARG;
+  // more than 16 query heads per kv head: only the matrix-core kernels,
+  // which take them in passes (head_dim 128)
   const int G = num_q_heads / g.num_kv_heads;
-  if (G > 16) return TQ_ERR_UNSUPPORTED;
+  if (G > 16 && tq::plan_decode(g, ctx->opts, batch > 0 ? batch : 1, num_q_heads, max_seq_len).mfma == 0)
+    return TQ_ERR_UNSUPPORTED;
   if (batch == 0) return TQ_OK;
   if (!q || !cache || !block_table || !seq_lens || !out) return TQ_ERR_INVALID_ARG;
   if (static_cast<int64_t>(max_blocks_per_seq) * g.block_size < max_seq_len)
@@ -826,7 +829,9 @@ tq_status tq_decode_continuation(const tq_ctx* ctx, const void* q, const uint8_t
   if (q_len <= 0 || seq_len < q_len || max_blocks <= 0 || num_q_heads <= 0 || num_blocks < 0)
     return TQ_ERR_INVALID_ARG;
   if (num_q_heads % g.num_kv_heads != 0) return TQ_ERR_INVALID_ARG;
-  if (num_q_heads / g.num_kv_heads > 16) return TQ_ERR_UNSUPPORTED;
+  if (num_q_heads / g.num_kv_heads > 16 &&
+      tq::plan_decode(g, ctx->opts, q_len, num_q_heads, seq_len).mfma == 0)
+    return TQ_ERR_UNSUPPORTED;
   if (!q || !cache || !block_table_row || !out || !workspace) return TQ_ERR_INVALID_ARG;
   if (static_cast<int64_t>(max_blocks) * g.block_size < seq_len) return TQ_ERR_INVALID_ARG;
   if (!aligned(workspace, 256)) return TQ_ERR_ALIGNMENT;

@@ -93,6 +93,9 @@ struct DecodePlan {
   int qrot;           // Haar rotation on a matrix-core kernel: the rotated queries (fp32
                       // [B][Hq][d]) sit in the workspace at byte qrot_off
   size_t qrot_off;
+  int g_pass;         // matrix-core kernels: query heads per kv head in one pass of the
+                      // kernel (its limit: 8 ring and page, 16 staged and direct); more
+                      // query heads run as several passes over the cache
 };
 
 bool mfma_decode_eligible(const Geometry& g, int num_q_heads);
@@ -101,6 +104,7 @@ int page_wgs_per_cu(const Geometry& g, int group);
 bool staged_decode_eligible(const Geometry& g, int num_q_heads);
 bool ring_decode_eligible(const Geometry& g, int num_q_heads);
 int ring_max_slabs();
+int mfma_max_g(int mfma);
 int mfma_waves_per_cu(const Geometry& g, bool staged);
 size_t mfma_partial_bytes(int batch, int num_q_heads, int num_splits);
 hipError_t launch_decode_mfma(const Geometry& g, const DevTables* tables, DevErrors* errs,

@@ -69,6 +69,27 @@ def test_decode_per_head_kernel_shapes(preset, G, H):
     check_decode(got, want, bf16_out=False)
 
 
+@pytest.mark.parametrize("preset", PRESETS)
+@pytest.mark.parametrize("G,H", [(24, 2), (40, 1)])
+def test_decode_query_head_passes(preset, G, H):
+    # more query heads per kv head than one pass of a per-head matrix-core
+    # kernel takes (16): passes of 16 (the last one short) over the cache,
+    # one merge for every head; empty, one-token and multi-split lengths
+    w = _wl(preset, G=G, H=H, B=4, lens=(3000, 3000), seed=G + H)
+    got, want = _decode_from_oracle_cache(w, lens=[0, 1, 1500, 3000])
+    check_decode(got, want, bf16_out=False)
+    got16, want16 = _decode_from_oracle_cache(w, lens=[0, 1, 1500, 3000], out_fp32=False)
+    check_decode(got16, want16, bf16_out=True)
+
+
+def test_decode_more_than_16_query_heads_needs_head_dim_128():
+    # the general kernel (other head dims) takes at most 16 query heads per kv head
+    from packed_cache_decode_amd import _lib
+    w = _wl("turboquant_4bit_nc", G=24, H=1, d=64, B=1, lens=(20, 20), seed=3)
+    with pytest.raises(_lib.TQError, match="UNSUPPORTED"):
+        _decode_from_oracle_cache(w)
+
+
 # the context's decode options force one matrix-core kernel where it applies
 # ("" picks by key type and shape: page-cooperative for FP8 keys, ring for
 # 3/4-bit keys with up to 8 query heads per kv head, staged or direct

@@ -7,8 +7,8 @@ store tests); where a K code differs at a proven tie, the folded norm may be
 the oracle's fold of the tie-alternative codes it derives itself.  Decode:
 the GPU decode of an oracle-written cache against the oracle's float64
 attention, max-abs 2e-3 (fp32 output), through the ring kernel (3/4-bit
-keys, up to 8 query heads per kv head) and the general kernel (other head
-dims, 16 query heads per kv head).  The full-size workloads in this layout
+keys, in passes of up to 8 query heads per kv head) and the general kernel
+(other head dims).  The full-size workloads in this layout
 are compared output by output in test_gpu_fullsize.py.
 """
 
@@ -203,7 +203,17 @@ def test_soa_decode_block_sizes(preset, bs):
 
 
 @pytest.mark.parametrize("preset", MSE)
-@pytest.mark.parametrize("G,H,d", [(16, 1, 128), (4, 2, 64), (4, 2, 256)])
+@pytest.mark.parametrize("G,H", [(16, 1), (12, 2), (24, 1)])
+def test_soa_decode_query_head_passes(preset, G, H):
+    # more than 8 query heads per kv head: the ring kernel in passes of 8 (the
+    # last one short), one merge for every head; empty and multi-split lengths
+    w = _wl(preset, H=H, Hq=G * H, lens=(20000, 20000), B=3, seed=G + 3 * H)
+    got, want = _decode_soa(w, lens=[0, 700, 20000])
+    check_decode(got, want, bf16_out=False)
+
+
+@pytest.mark.parametrize("preset", MSE)
+@pytest.mark.parametrize("G,H,d", [(4, 2, 64), (4, 2, 256)])
 def test_soa_decode_general_kernel(preset, G, H, d):
     got, want = _decode_soa(_wl(preset, H=H, Hq=G * H, d=d, lens=(1, 500), B=3, seed=G + d))
     check_decode(got, want, bf16_out=False)

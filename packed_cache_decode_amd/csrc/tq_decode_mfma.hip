@@ -1245,11 +1245,17 @@ struct PageGeom {
 
 // centroid tables (2 KB): entry e covers the codes e & (2^KB - 1) and
 // e >> KB.  4-bit keys: {pair of hi parts, pair of lo parts} at 8-byte entry
-// e, one lookup per code byte, lo = c - hi.  3-bit keys: the pair of hi parts at word e
-// and the pair of lo parts at word 256 + e, two lookups from one address
-// that land directly in the hi and lo MFMA operands (no register moves);
-// their 64 entries fill one row of banks, so the lookups never conflict,
-// while a 256-entry 4-bit half table would conflict more than the 8-byte one.
+// e, one lookup per code byte, lo = c - hi.  3-bit keys: the pair of hi parts
+// at byte 4e and the pair of lo parts (lo = 2 (c - hi)) at byte kLoOff + 4e,
+// two lookups from one address.  kLoOff = 1028 (257 words) is beyond a paired
+// LDS read's reach (up to 255 words, or multiples of 64 words), so the
+// compiler cannot fuse the two into one read into a register pair: each
+// lands directly in its MFMA operand (fused, the pairs took 28 register moves
+// per slab); the 64 entries of each half fill one row of banks, so the
+// lookups never conflict.  A split 4-bit table (256 entries a half) measured
+// slower than the 8-byte entries.
+constexpr int kLoOff = 1028;
+static_assert(kLoOff + 64 * 4 <= 256 * 8, "3-bit table halves within the 2 KB table");
 template <int KB>
 __device__ __forceinline__ void build_tables_page(const MfmaArgs& a, u32x2* tab) {
   constexpr int kTab = KB == 4 ? 256 : 64;
@@ -1268,7 +1274,7 @@ __device__ __forceinline__ void build_tables_page(const MfmaArgs& a, u32x2* tab)
       const _Float16 l0 = static_cast<_Float16>(2.0f * (v0 - static_cast<float>(h0)));
       const _Float16 l1 = static_cast<_Float16>(2.0f * (v1 - static_cast<float>(h1)));
       t32[e] = pack_h2(h0, h1);
-      t32[256 + e] = pack_h2(l0, l1);
+      t32[kLoOff / 4 + e] = pack_h2(l0, l1);
     }
   }
 }
@@ -1394,7 +1400,7 @@ __device__ __forceinline__ void slab_lookup(const u32x2* tab, SlabRegs<KB>& R) {
           idx = v & 63u;
         }
         if constexpr (KB == 4) R.e[4 * kk + p] = tab[idx];
-        else R.e[4 * kk + p] = u32x2{t32[idx], t32[256 + idx]};
+        else R.e[4 * kk + p] = u32x2{t32[idx], t32[kLoOff / 4 + idx]};
       }
   }
 }

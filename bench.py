@@ -208,7 +208,7 @@ def main():
                     help="back-to-back decodes with no flush, reported apart (default: --steps; "
                          "0 leaves them out, so a profile of the run holds cold launches only)")
     ap.add_argument("--decode-kernel", default="",
-                    choices=["", "ring", "page", "staged", "direct"],
+                    choices=["", "ring", "page", "staged", "direct", "general"],
                     help="force a decode kernel where it applies (default: chosen by shape)")
     ap.add_argument("--page-heads", type=int, default=0, choices=[0, 1, 2, 4],
                     help="page decode: kv heads per workgroup (default: the whole row, at most 8)")

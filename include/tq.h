@@ -118,7 +118,11 @@ typedef enum {
   TQ_DECODE_KERNEL_RING = 1,    /* per (sequence, kv head) workgroups streaming per-head slabs */
   TQ_DECODE_KERNEL_PAGE = 2,    /* per (sequence, split) workgroups streaming whole page rows */
   TQ_DECODE_KERNEL_STAGED = 3,  /* one wavefront per (split, sequence, kv head), staged rows */
-  TQ_DECODE_KERNEL_DIRECT = 4   /* one wavefront per (split, sequence, kv head), direct loads */
+  TQ_DECODE_KERNEL_DIRECT = 4,  /* one wavefront per (split, sequence, kv head), direct loads */
+  TQ_DECODE_KERNEL_GENERAL = 5  /* fp32 vector-ALU kernel, no matrix cores: one wavefront per
+                                   (256-token split, sequence, kv head); any head dim, up to 16
+                                   query heads per kv head (the measure the matrix-core kernels
+                                   are compared with) */
 } tq_decode_kernel;
 
 /* How a context's decode is planned.  The default (all zero) is AUTO with

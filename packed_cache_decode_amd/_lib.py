@@ -20,7 +20,7 @@ STATUS = {0: "TQ_OK", -1: "TQ_ERR_INVALID_ARG", -2: "TQ_ERR_UNSUPPORTED", -3: "T
 PRESETS = {"turboquant_k8v4": 0, "turboquant_4bit_nc": 1, "turboquant_k3v4_nc": 2, "turboquant_3bit_nc": 3}
 CODEBOOK_MODES = {"exact": 0, "page_trapz": 1, "beta": 2}
 LAYOUTS = {"aos": 0, "soa": 1}
-DECODE_KERNELS = {"": 0, "auto": 0, "ring": 1, "page": 2, "staged": 3, "direct": 4}
+DECODE_KERNELS = {"": 0, "auto": 0, "ring": 1, "page": 2, "staged": 3, "direct": 4, "general": 5}
 
 
 class DecodeOptions(ctypes.Structure):

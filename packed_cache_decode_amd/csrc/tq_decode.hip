@@ -426,9 +426,10 @@ DecodePlan plan_decode_kernels(const Geometry& g, const tq_decode_options& opts,
   // ring kernel: slabs dealt out in a fixed interleaved order unless the
   // context asks for dynamic claims (results then vary in the last bits)
   p.dynamic = opts.dynamic_claims ? 1 : 0;
-  if (g.haar && g.head_dim != 128) {
+  if ((g.haar && g.head_dim != 128) || opts.kernel == TQ_DECODE_KERNEL_GENERAL) {
     // the matrix-core kernels are built for d = 128; other head dims with the
-    // Haar rotation's dense product run in the general kernel
+    // Haar rotation's dense product run in the general kernel, as does any
+    // shape when the options ask for it
     p.mfma = 0;
     p.chunk = 256;
     p.num_splits = max_seq_len > 0 ? (max_seq_len + p.chunk - 1) / p.chunk : 1;

@@ -875,7 +875,7 @@ tq_status tq_set_decode_options(tq_ctx* ctx, const tq_decode_options* opts) {
     ctx->opts = tq_decode_options{};
     return TQ_OK;
   }
-  if (opts->kernel < TQ_DECODE_KERNEL_AUTO || opts->kernel > TQ_DECODE_KERNEL_DIRECT)
+  if (opts->kernel < TQ_DECODE_KERNEL_AUTO || opts->kernel > TQ_DECODE_KERNEL_GENERAL)
     return TQ_ERR_INVALID_ARG;
   if (opts->ring_waves != 0 && opts->ring_waves != 8 && opts->ring_waves != 16)
     return TQ_ERR_INVALID_ARG;

@@ -90,11 +90,11 @@ def test_decode_more_than_16_query_heads_needs_head_dim_128():
         _decode_from_oracle_cache(w)
 
 
-# the context's decode options force one matrix-core kernel where it applies
-# ("" picks by key type and shape: page-cooperative for FP8 keys, ring for
-# 3/4-bit keys with up to 8 query heads per kv head, staged or direct
-# otherwise)
-KERNELS = ["", "page", "staged", "direct", "ring"]
+# the context's decode options force one kernel where it applies ("" picks by
+# key type and shape: page-cooperative for FP8 keys, ring for 3/4-bit keys
+# with up to 8 query heads per kv head, staged or direct otherwise; "general"
+# is the fp32 vector-ALU kernel)
+KERNELS = ["", "page", "staged", "direct", "ring", "general"]
 
 
 @pytest.mark.parametrize("preset", PRESETS)
@@ -123,7 +123,7 @@ def test_decode_sixteen_kv_heads(preset):
 
 
 @pytest.mark.parametrize("preset", ["turboquant_4bit_nc", "turboquant_k3v4_nc", "turboquant_3bit_nc"])
-@pytest.mark.parametrize("kernel", ["page", "staged", "direct", "ring"])
+@pytest.mark.parametrize("kernel", ["page", "staged", "direct", "ring", "general"])
 def test_decode_kernels_mse_ragged(preset, kernel):
     w = _wl(preset, G=4, H=2, B=7, lens=(600, 600), seed=9)
     got, want = _decode_from_oracle_cache(w, lens=[0, 1, 15, 16, 17, 257, 600], opts=dict(kernel=kernel))
@@ -318,7 +318,10 @@ def test_decode_options_round_trip_and_validation():
     tq.set_decode_options(kernel="page", dynamic_claims=True, ring_waves=8, page_heads=2)
     want = dict(kernel=2, dynamic_claims=1, ring_waves=8, page_heads=2)
     assert _lib.tq_get_decode_options(tq.ctx) == want
-    for bad in (dict(kernel=9), dict(ring_waves=12), dict(page_heads=3)):
+    tq.set_decode_options(kernel="general")
+    assert _lib.tq_get_decode_options(tq.ctx)["kernel"] == 5
+    tq.set_decode_options(kernel="page", dynamic_claims=True, ring_waves=8, page_heads=2)
+    for bad in (dict(kernel=6), dict(kernel=-1), dict(ring_waves=12), dict(page_heads=3)):
         with pytest.raises(_lib.TQError):
             _lib.tq_set_decode_options(tq.ctx, **bad)
         assert _lib.tq_get_decode_options(tq.ctx) == want

@@ -73,12 +73,13 @@ def test_haar_decode_parity(preset, G, d):
 
 
 @pytest.mark.parametrize("preset", MSE)
-@pytest.mark.parametrize("kernel", ["ring", "page", "staged", "direct"])
+@pytest.mark.parametrize("kernel", ["ring", "page", "staged", "direct", "general"])
 def test_haar_decode_matrix_core_kernels(preset, kernel):
     # head_dim 128 with the Haar rotation runs on the matrix-core kernels
     # (the queries rotated once by a small kernel into the workspace): each
     # of them on a ragged batch, 8 query heads per kv head (16 for the
-    # per-head kernels), fp32 and bf16 outputs
+    # per-head kernels), fp32 and bf16 outputs; and, when asked for, on the
+    # general fp32 kernel (its own dense rotation)
     from packed_cache_decode_amd.runtime import PackedKVCache
     H, seed = 2, 79
     G = 8 if kernel in ("ring", "page") else 16

@@ -28,6 +28,7 @@ each) over a bounded sample of the same workload.
 """
 
 import argparse
+import dataclasses
 import json
 import os
 import sys
@@ -207,6 +208,9 @@ def main():
     ap.add_argument("--warm-reps", type=int, default=None,
                     help="back-to-back decodes with no flush, reported apart (default: --steps; "
                          "0 leaves them out, so a profile of the run holds cold launches only)")
+    ap.add_argument("--head-dim", type=int, default=0, choices=[0, 64, 128, 256],
+                    help="run the workload's shapes at another head dim (default: its own); the "
+                         "line then names the workload <name>_d<dim>")
     ap.add_argument("--decode-kernel", default="",
                     choices=["", "ring", "page", "staged", "direct", "general"],
                     help="force a decode kernel where it applies (default: chosen by shape)")
@@ -238,6 +242,8 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     w = synth.WORKLOADS[args.workload]
+    if args.head_dim and args.head_dim != w.head_dim:
+        w = dataclasses.replace(w, head_dim=args.head_dim, name=f"{w.name}_d{args.head_dim}")
     print(f"[bench] generating {w.name}", file=sys.stderr, flush=True)
     inp = synth.generate(w)
     synth.assert_unique_slots(inp.slot_mapping)      # one store may not write a slot twice

@@ -40,6 +40,7 @@ struct DecodeArgs {
   int bs_shift;
   int chunk;
   int num_splits;
+  int G;              // query heads per kv head (the kernel is built for a power of two >= G)
   float scale_log2;   // sm_scale * log2(e)
   float* part;        // [B][Hq][S][D + 2]
   void* out;
@@ -78,8 +79,12 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
-template <int D, int KB, int G, int VB>
+// GP: query heads per kv head the kernel is built for, a power of two; the
+// a.G <= GP heads of the kv head are computed in the first slots (the rest
+// repeat head 0 and are never stored)
+template <int D, int KB, int GP, int VB>
 __global__ void __launch_bounds__(64) decode_split_kernel(DecodeArgs a) {
+  constexpr int G = GP;
   constexpr int E = D / 64;
   constexpr bool kFp8 = KB == 8;
   constexpr int kKeyCodeBytes = kFp8 ? D : (D * KB + 7) / 8;
@@ -110,12 +115,14 @@ __global__ void __launch_bounds__(64) decode_split_kernel(DecodeArgs a) {
   }
   const int t0 = split * a.chunk;
   const int t1 = min(T, t0 + a.chunk);
-  float* part0 = a.part + ((static_cast<int64_t>(b) * Hq + g * G) * a.num_splits + split) * (D + 2);
+  const int Gr = a.G;
+  float* part0 = a.part + ((static_cast<int64_t>(b) * Hq + g * Gr) * a.num_splits + split) * (D + 2);
   const int64_t head_stride = static_cast<int64_t>(a.num_splits) * (D + 2);
 
   if (t0 >= t1) {                      // empty split: acc 0, m -inf, l 0
 #pragma unroll
     for (int j = 0; j < G; ++j) {
+      if (j >= Gr) break;
       float* p = part0 + j * head_stride;
       for (int c = lane; c < D; c += 64) p[c] = 0.0f;
       if (lane == 0) {
@@ -139,7 +146,7 @@ __global__ void __launch_bounds__(64) decode_split_kernel(DecodeArgs a) {
     // Haar rotation: q_rot = Q q, coordinates of every query through LDS
 #pragma unroll
     for (int j = 0; j < G; ++j) {
-      const uint16_t* qp = a.q + (static_cast<int64_t>(b) * Hq + g * G + j) * D + E * lane;
+      const uint16_t* qp = a.q + (static_cast<int64_t>(b) * Hq + g * Gr + (j < Gr ? j : 0)) * D + E * lane;
 #pragma unroll
       for (int e = 0; e < E; ++e) s_q[j][E * lane + e] = bf16_bits_to_f32(qp[e]);
     }
@@ -164,7 +171,7 @@ __global__ void __launch_bounds__(64) decode_split_kernel(DecodeArgs a) {
   } else
 #pragma unroll
   for (int j = 0; j < G; ++j) {
-    const uint16_t* qp = a.q + (static_cast<int64_t>(b) * Hq + g * G + j) * D + E * lane;
+    const uint16_t* qp = a.q + (static_cast<int64_t>(b) * Hq + g * Gr + (j < Gr ? j : 0)) * D + E * lane;
     float u[E];
 #pragma unroll
     for (int e = 0; e < E; ++e) u[e] = bf16_bits_to_f32(qp[e]);
@@ -346,6 +353,7 @@ __global__ void __launch_bounds__(64) decode_split_kernel(DecodeArgs a) {
 
 #pragma unroll
   for (int j = 0; j < G; ++j) {
+    if (j >= Gr) break;
     float* p = part0 + j * head_stride;
 #pragma unroll
     for (int e = 0; e < E; ++e) p[E * lane + e] = acc[j][e];
@@ -407,14 +415,14 @@ hipError_t launch_t(const DecodeArgs& a, int batch, hipStream_t stream) {
 
 template <int D, int KB, int VB>
 hipError_t launch_g(const DecodeArgs& a, int G, int batch, hipStream_t stream) {
-  switch (G) {
-    case 1: return launch_t<D, KB, 1, VB>(a, batch, stream);
-    case 2: return launch_t<D, KB, 2, VB>(a, batch, stream);
-    case 4: return launch_t<D, KB, 4, VB>(a, batch, stream);
-    case 8: return launch_t<D, KB, 8, VB>(a, batch, stream);
-    case 16: return launch_t<D, KB, 16, VB>(a, batch, stream);
-    default: return hipErrorInvalidValue;
-  }
+  // the kernel built for the next power of two
+  if (G < 1) return hipErrorInvalidValue;
+  if (G <= 1) return launch_t<D, KB, 1, VB>(a, batch, stream);
+  if (G <= 2) return launch_t<D, KB, 2, VB>(a, batch, stream);
+  if (G <= 4) return launch_t<D, KB, 4, VB>(a, batch, stream);
+  if (G <= 8) return launch_t<D, KB, 8, VB>(a, batch, stream);
+  if (G <= 16) return launch_t<D, KB, 16, VB>(a, batch, stream);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace
@@ -426,10 +434,35 @@ DecodePlan plan_decode_kernels(const Geometry& g, const tq_decode_options& opts,
   // ring kernel: slabs dealt out in a fixed interleaved order unless the
   // context asks for dynamic claims (results then vary in the last bits)
   p.dynamic = opts.dynamic_claims ? 1 : 0;
+  if (opts.kernel != TQ_DECODE_KERNEL_GENERAL && dslab_decode_eligible(g, num_q_heads)) {
+    // head dims 64 and 256 on the slotted page: the direct matrix-core
+    // kernel's design at those dims (the forced d = 128 kernels do not apply),
+    // one resident round of wavefronts over (split, sequence, kv head), at
+    // least 8 slabs per split; the queries rotated once into the workspace
+    const int slabs = max_seq_len > 0 ? (max_seq_len + 15) / 16 : 1;
+    const int per_split = batch * g.num_kv_heads;
+    const int target = 256 * dslab_waves_per_cu(g);
+    int s = per_split > 0 ? (target + per_split - 1) / per_split : 1;
+    const int s_max = (slabs + 7) / 8;
+    s = s < 1 ? 1 : (s > s_max ? s_max : s);
+    p.mfma = 5;
+    p.chunk = 16 * ((slabs + s - 1) / s);
+    if (p.chunk > 16 * 256) p.chunk = 16 * 256;       // page offsets of a split fit in LDS
+    p.num_splits = max_seq_len > 0 ? (max_seq_len + p.chunk - 1) / p.chunk : 1;
+    p.workspace_bytes = dslab_partial_bytes(g, batch, num_q_heads, p.num_splits);
+    p.workspace_bytes = (p.workspace_bytes + 255) & ~static_cast<size_t>(255);
+    if (g.key_bits != 8) {
+      p.qrot = 1;
+      p.qrot_off = p.workspace_bytes;
+      p.workspace_bytes += static_cast<size_t>(batch) * num_q_heads * g.head_dim * sizeof(float);
+      p.workspace_bytes = (p.workspace_bytes + 255) & ~static_cast<size_t>(255);
+    }
+    return p;
+  }
   if ((g.haar && g.head_dim != 128) || opts.kernel == TQ_DECODE_KERNEL_GENERAL) {
-    // the matrix-core kernels are built for d = 128; other head dims with the
-    // Haar rotation's dense product run in the general kernel, as does any
-    // shape when the options ask for it
+    // the general kernel: the Haar rotation at other head dims where the
+    // matrix-core kernels do not apply (the split page), and any shape when
+    // the options ask for it
     p.mfma = 0;
     p.chunk = 256;
     p.num_splits = max_seq_len > 0 ? (max_seq_len + p.chunk - 1) / p.chunk : 1;
@@ -548,7 +581,7 @@ DecodePlan plan_decode(const Geometry& g, const tq_decode_options& opts, int bat
     const int G = num_q_heads / g.num_kv_heads;
     p.g_pass = G < mfma_max_g(p.mfma) ? G : mfma_max_g(p.mfma);
   }
-  if (g.haar && p.mfma != 0) {
+  if (g.haar && p.mfma != 0 && !p.qrot) {
     // the matrix-core kernels read the queries rotated by the Haar matrix
     // from the workspace, after the split partials
     p.qrot = 1;
@@ -588,6 +621,7 @@ hipError_t launch_decode(const Geometry& g, const DevTables* tables, DevErrors* 
   a.out_fp32 = out_is_fp32;
   a.soa = g.soa;
   const int G = num_q_heads / g.num_kv_heads;
+  a.G = G;
 #define TQ_DEC_CASE(D_, KB_, VB_) \
   if (g.head_dim == D_ && g.key_bits == KB_ && g.value_bits == VB_) return launch_g<D_, KB_, VB_>(a, G, batch, stream);
   TQ_DEC_CASE(64, 3, 4) TQ_DEC_CASE(64, 4, 4) TQ_DEC_CASE(64, 8, 4) TQ_DEC_CASE(64, 3, 3)

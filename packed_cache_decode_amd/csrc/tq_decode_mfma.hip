@@ -1,7 +1,8 @@
 // tq_decode on gfx950 matrix cores: split-KV paged decode attention over
 // packed slots for head_dim 128 (4- or 3-bit Lloyd-Max keys, or FP8 E4M3
-// keys), block sizes that are multiples of 16 and up to 16 query heads per
-// kv head.
+// keys), block sizes that are multiples of 16, any number of query heads per
+// kv head (passes of 16); and, by one direct kernel, head dims 64 and 256 on
+// the slotted page with up to 16 query heads per kv head.
 //
 // What is computed is the same as in the general kernel (tq_decode.hip),
 // following P1 ("vLLM 源码完全拆解(十九):TurboQuant KV Cache 量化"),
@@ -23,6 +24,8 @@
 //   ring    (decode_ring_kernel)    one workgroup per (sequence, kv head,
 //           split); every wavefront claims slabs and streams them into its
 //           own LDS ring (3/4-bit keys, slotted and split pages)
+//   dslab   (decode_dslab_kernel)   the direct kernel's design at head dims
+//           64 and 256 (its own section below)
 // decode_merge_kernel merges the split partials by log-sum-exp (a fused
 // last-workgroup merge needs a device-scope release in every workgroup,
 // which on this part costs far more than a launch).
@@ -2270,6 +2273,535 @@ hipError_t launch_page_h(const MfmaArgs& a, int batch, int group, hipStream_t st
   }
 }
 
+// ============================================================================
+// direct, head dims 64 and 256: the direct kernel's design at the other head
+// dims of the slotted page, up to 16 query heads per kv head, one wavefront
+// per (split, sequence, kv head), each lane loading its operand bytes.
+// Lane (r16, g4) holds K coordinates [(D/4)*g4, (D/4)*(g4+1)) of token r16
+// (score step kk: (D/4)*g4 + 8*kk + [0, 8)), and the V codes of tokens
+// 4*g4 + r for coordinates [(D/16)*r16, (D/16)*(r16+1)); value tile m column
+// j covers coordinate (D/16)*j + m.  The queries are rotated once per decode
+// by rotate_queries_d_kernel (signed Hadamard or Haar) into the workspace.
+// Scores, norm correction, softmax and P.V are those of the d = 128 direct
+// kernel (score_slab, softmax_pv), over D/32 score steps and D/16 tiles.
+// ============================================================================
+
+template <int D, int KB, int VB>
+struct DGeom {
+  static constexpr int kKK = D / 32;                          // score MFMA steps
+  static constexpr int kTiles = D / 16;                       // value tiles (coordinates per lane and token)
+  static constexpr int kKCB = KB == 8 ? D : D * KB / 8;       // K code bytes
+  static constexpr int kKP = KB == 8 ? D : kKCB + 2;          // + the fp16 norm (MSE keys)
+  static constexpr int kVCB = D * VB / 8;                     // V code bytes
+  static constexpr int kSlotRaw = kKP + kVCB + 4;             // + fp16 scale and zero
+  static constexpr int kSlot = kSlotRaw + kSlotRaw % 2;
+  static constexpr int kLaneKB = (D / 4) * KB / 8;            // K bytes of a lane
+  // dwords loaded: 3-bit keys at d = 64 take 6 bytes and two bytes of the
+  // norm ride along
+  static constexpr int kLaneKW = (kLaneKB + 3) / 4;
+  // V dwords of a lane per token: 4-bit 2 bytes (d 64) or 8 (d 256); 3-bit
+  // 12 bits in a 2-byte-aligned dword (d 64) or 6 bytes (d 256)
+  static constexpr int kVW = D == 256 ? 2 : 1;
+  static constexpr int kRecD = D + 4;                         // partial record: O[D], m, l, z, pad
+  static_assert(D == 64 || D == 256, "head dims 64 and 256");
+};
+
+template <int D>
+constexpr int kDWavesPerSimd = D == 256 ? 2 : 4;
+
+template <int D>
+struct RunStateD {
+  f4 O[D / 16];     // O[h][(D/16)*r16 + m]: tile m, rows 4*g4 + r
+  float m_run;
+  float l_part;
+  float z_part;
+};
+
+template <int D, int KB, int VB>
+struct DRegs {
+  uint32_t kw[DGeom<D, KB, VB>::kLaneKW];
+  uint32_t X[4][DGeom<D, KB, VB>::kVW];
+  uint32_t n[4];
+  uint32_t sz[4];
+  bool ok;
+};
+
+template <int D, int KB, int VB>
+struct DOffsets {
+  uint32_t k;
+  uint32_t row[4];
+  uint32_t v[4];
+  uint32_t vshift;   // 3-bit V at d = 64: bit offset of the lane's codes in its dword
+};
+
+template <int D, int KB, int VB>
+__device__ __forceinline__ DOffsets<D, KB, VB> dslab_offsets(int r16, int g4, uint32_t head_off, uint32_t rb) {
+  using DG = DGeom<D, KB, VB>;
+  DOffsets<D, KB, VB> o;
+  o.k = r16 * rb + head_off + DG::kLaneKB * g4;
+  uint32_t vb;
+  if constexpr (VB == 3 && D == 64) {
+    // bits [12*r16, 12*r16 + 12) of the V codes, from the 2-byte word holding
+    // their first bit (the dword read stays inside the slot: the V scale follows)
+    const uint32_t bit = 12u * r16;
+    vb = 2u * (bit >> 4);
+    o.vshift = bit & 15u;
+  } else {
+    vb = static_cast<uint32_t>(DG::kTiles * VB / 8) * r16;
+    o.vshift = 0;
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    o.row[r] = (4 * g4 + r) * rb + head_off;
+    o.v[r] = o.row[r] + DG::kKP + vb;
+  }
+  return o;
+}
+
+template <int D, int KB, int VB>
+__device__ __forceinline__ void dslab_load(__amdgpu_buffer_rsrc_t rs, const DOffsets<D, KB, VB>& o,
+                                           DRegs<D, KB, VB>& d) {
+  using DG = DGeom<D, KB, VB>;
+  constexpr int W = DG::kLaneKW;
+  int i = 0;
+#pragma unroll
+  for (; i + 4 <= W; i += 4) {
+    const u32x4 t = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, o.k + 4 * i, 0, 0));
+    d.kw[i] = t[0]; d.kw[i + 1] = t[1]; d.kw[i + 2] = t[2]; d.kw[i + 3] = t[3];
+  }
+  if constexpr (W % 4 >= 2) {
+    const u32x2 t = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, o.k + 4 * (W - W % 4), 0, 0));
+    d.kw[W - W % 4] = t[0];
+    d.kw[W - W % 4 + 1] = t[1];
+  }
+  if constexpr (W % 2 == 1) d.kw[W - 1] = __builtin_amdgcn_raw_buffer_load_b32(rs, o.k + 4 * (W - 1), 0, 0);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    if constexpr (DG::kVW == 2) {
+      const u32x2 t = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, o.v[r], 0, 0));
+      d.X[r][0] = t[0];
+      d.X[r][1] = t[1];
+    } else if constexpr (VB == 4) {
+      d.X[r][0] = __builtin_amdgcn_raw_buffer_load_b16(rs, o.v[r], 0, 0);
+    } else {
+      d.X[r][0] = __builtin_amdgcn_raw_buffer_load_b32(rs, o.v[r], 0, 0);
+    }
+    if constexpr (KB != 8) d.n[r] = __builtin_amdgcn_raw_buffer_load_b16(rs, o.row[r] + DG::kKCB, 0, 0);
+    d.sz[r] = __builtin_amdgcn_raw_buffer_load_b32(rs, o.row[r] + DG::kKP + DG::kVCB, 0, 0);
+  }
+}
+
+// rotated queries of kv head g (fp32, from the workspace) as f16 hi / lo B
+// operands, times the softmax scale (base 2); lane (h = r16, g4), step kk:
+// coordinates (D/4)*g4 + 8*kk + [0, 8)
+template <int D>
+__device__ __forceinline__ void load_queries_d(const MfmaArgs& a, int b, int g, int r16, int g4,
+                                               h8 (&qhi)[D / 32], h8 (&qlo)[D / 32]) {
+  const bool live = r16 < a.G;
+  const int64_t row = (static_cast<int64_t>(b) * a.Hq + g * a.Gq + a.h0 + (live ? r16 : 0)) * D + (D / 4) * g4;
+  const float4* rp = reinterpret_cast<const float4*>(a.q_rot + row);
+#pragma unroll
+  for (int kk = 0; kk < D / 32; ++kk) {
+    const float4 v0 = rp[2 * kk], v1 = rp[2 * kk + 1];
+    const float x[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float v = live ? x[e] * a.scale_log2 : 0.0f;
+      const _Float16 hv = static_cast<_Float16>(v);
+      qhi[kk][e] = hv;
+      qlo[kk][e] = static_cast<_Float16>(v - static_cast<float>(hv));
+    }
+  }
+}
+
+// FP8 keys: the queries as given (bf16), same coordinates
+template <int D>
+__device__ __forceinline__ void load_queries_bf16_d(const MfmaArgs& a, int b, int g, int r16, int g4,
+                                                    bf8v (&qb)[D / 32]) {
+  const bool live = r16 < a.G;
+  const uint16_t* qp =
+      a.q + (static_cast<int64_t>(b) * a.Hq + g * a.Gq + a.h0 + (live ? r16 : 0)) * D + (D / 4) * g4;
+#pragma unroll
+  for (int kk = 0; kk < D / 32; ++kk) {
+    u32x4 w = *reinterpret_cast<const u32x4*>(qp + 8 * kk);
+    if (!live) w = u32x4{0u, 0u, 0u, 0u};
+    qb[kk] = __builtin_bit_cast(bf8v, w);
+  }
+}
+
+// scores (base 2) of the lane's 4 rows for 3/4-bit keys (as score_slab)
+template <int D, int KB, int VB>
+__device__ __forceinline__ void score_slab_d(const DRegs<D, KB, VB>& op, int valid_rows, const u32x2* s_tab,
+                                             const h8 (&qhi)[D / 32], const h8 (&qlo)[D / 32], int g4,
+                                             float (&s)[4]) {
+  f4 Shi = {0.f, 0.f, 0.f, 0.f}, Slo = {0.f, 0.f, 0.f, 0.f};
+  f4 Nhi = {1e-16f, 1e-16f, 1e-16f, 1e-16f}, Nx = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kk = 0; kk < D / 32; ++kk) {
+    uint32_t idx[4];
+    if constexpr (KB == 4) {
+#pragma unroll
+      for (int p = 0; p < 4; ++p) idx[p] = (op.kw[kk] >> (8 * p)) & 0xFFu;
+    } else {
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const int bit = 24 * kk + 6 * p;
+        const int w = bit >> 5, o = bit & 31;
+        uint32_t v = op.kw[w] >> o;
+        if (o > 26) v |= op.kw[w + 1] << (32 - o);
+        idx[p] = v & 63u;
+      }
+    }
+    u32x4 hi, lo;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const u32x2 e = s_tab[idx[p]];
+      hi[p] = e[0];
+      lo[p] = e[1];
+    }
+    const h8 chi = __builtin_bit_cast(h8, hi);
+    const h8 clo = __builtin_bit_cast(h8, lo);
+    Shi = __builtin_amdgcn_mfma_f32_16x16x32_f16(chi, qhi[kk], Shi, 0, 0, 0);
+    Shi = __builtin_amdgcn_mfma_f32_16x16x32_f16(chi, qlo[kk], Shi, 0, 0, 0);
+    Slo = __builtin_amdgcn_mfma_f32_16x16x32_f16(clo, qhi[kk], Slo, 0, 0, 0);
+    Nhi = __builtin_amdgcn_mfma_f32_16x16x32_f16(chi, chi, Nhi, 0, 0, 0);
+    Nx = __builtin_amdgcn_mfma_f32_16x16x32_f16(chi, clo, Nx, 0, 0, 0);
+  }
+  const int diag_src = 20 * g4;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const float nd = Nhi[r] + (2.0f / kLoScale) * Nx[r];
+    const float nn = lane_value(nd, diag_src + r);
+    const float fac = f16_bits_to_f32(op.n[r]) * __builtin_amdgcn_rsqf(nn);
+    const float dot = Shi[r] + Slo[r] * (1.0f / kLoScale);
+    s[r] = 4 * g4 + r < valid_rows ? dot * fac : -INFINITY;
+  }
+}
+
+// scores (base 2) for FP8 keys (as score_slab8)
+template <int D, int KB, int VB>
+__device__ __forceinline__ void score_slab8_d(const DRegs<D, KB, VB>& op, int valid_rows, const bf8v (&qb)[D / 32],
+                                              float scale_log2, int g4, float (&s)[4]) {
+  f4 S = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kk = 0; kk < D / 32; ++kk) {
+    const uint32_t w0 = op.kw[2 * kk], w1 = op.kw[2 * kk + 1];
+    const bf2 c0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false);
+    const bf2 c1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true);
+    const bf2 c2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false);
+    const bf2 c3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true);
+    const bf8v av = {c0[0], c0[1], c1[0], c1[1], c2[0], c2[1], c3[0], c3[1]};
+    S = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, qb[kk], S, 0, 0, 0);
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) s[r] = 4 * g4 + r < valid_rows ? S[r] * scale_log2 : -INFINITY;
+}
+
+// online softmax and P.V of one slab (as softmax_pv, over D/16 tiles); the
+// lane's V codes of token 4*g4 + r are X[r] (kVW dwords, from bit 0)
+template <int D, int KB, int VB>
+__device__ __forceinline__ void softmax_pv_d(const float (&s)[4], int valid_rows, const DRegs<D, KB, VB>& op,
+                                             uint32_t vshift, int g4, RunStateD<D>& st) {
+  float pm = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+  float sc[4], zr[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const uint32_t szm = 4 * g4 + r < valid_rows ? op.sz[r] : 0u;
+    sc[r] = f16_bits_to_f32(szm & 0xFFFFu);
+    zr[r] = f16_bits_to_f32(szm >> 16);
+  }
+  const float sc_max = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+  const float thr = sc_max > 1000.0f ? 0.0f : kLazy;
+  if (__any(pm > st.m_run + thr)) {
+    const float m_new = fmaxf(st.m_run, max_x32(max_x16(pm)));
+    const float corr = __builtin_amdgcn_exp2f(st.m_run - m_new);
+    st.l_part *= corr;
+    st.z_part *= corr;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float cr = lane_value(corr, 4 * g4 + r);
+#pragma unroll
+      for (int m = 0; m < D / 16; ++m) st.O[m][r] *= cr;
+    }
+    st.m_run = m_new;
+  }
+  h4 W, Wl;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const float p = __builtin_amdgcn_exp2f(s[r] - st.m_run);
+    st.l_part += p;
+    st.z_part += p * zr[r];
+    const float wf = p * sc[r];
+    W[r] = static_cast<_Float16>(wf);
+    Wl[r] = static_cast<_Float16>(wf - static_cast<float>(W[r]));
+  }
+  const h8 Ws = {W[0], W[1], W[2], W[3], Wl[0], Wl[1], Wl[2], Wl[3]};
+  // kb: coordinates 2*kb and 2*kb + 1 of the lane (tiles 2*kb, 2*kb + 1);
+  // 4-bit codes: byte kb % 4 of dword kb / 4; 3-bit codes: bits 6*kb on,
+  // taken from the 24-bit group kb / 4
+#pragma unroll
+  for (int kb = 0; kb < D / 32; ++kb) {
+    uint32_t Xk[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      if constexpr (VB == 4)
+        Xk[r] = op.X[r][kb / 4];
+      else if constexpr (D == 64)
+        Xk[r] = op.X[r][0] >> vshift;
+      else
+        Xk[r] = kb < 4 ? op.X[r][0] : ((op.X[r][0] >> 24) | (op.X[r][1] << 8));
+    }
+    h4 Blo4, Bhi4;
+    v_operands<VB>(Xk, kb % 4, Blo4, Bhi4);
+    const h8 Blo = {Blo4[0], Blo4[1], Blo4[2], Blo4[3], Blo4[0], Blo4[1], Blo4[2], Blo4[3]};
+    const h8 Bhi = {Bhi4[0], Bhi4[1], Bhi4[2], Bhi4[3], Bhi4[0], Bhi4[1], Bhi4[2], Bhi4[3]};
+    st.O[2 * kb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ws, Blo, st.O[2 * kb], 0, 0, 0);
+    st.O[2 * kb + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ws, Bhi, st.O[2 * kb + 1], 0, 0, 0);
+  }
+}
+
+// split partials of this wavefront: record [O[D], m, l, z, pad] per
+// (sequence, query head, split); O rows are heads 4*g4 + r
+template <int D>
+__device__ __forceinline__ void store_partials_d(const MfmaArgs& a, int b, int g, int split, int g4, int r16,
+                                                 const RunStateD<D>& st) {
+  constexpr int kRecD = D + 4;
+  constexpr int NT = D / 16;
+  const float l_part = sum_x32(sum_x16(st.l_part));
+  const float z_part = sum_x32(sum_x16(st.z_part));
+  const int64_t rec0 = (static_cast<int64_t>(b) * a.Hq + g * a.Gq + a.h0) * a.num_splits + split;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int h = 4 * g4 + r;
+    if (h < a.G) {
+      float* rec = a.part + (rec0 + static_cast<int64_t>(h) * a.num_splits) * kRecD + NT * r16;
+#pragma unroll
+      for (int m = 0; m < NT; m += 4)
+        *reinterpret_cast<float4*>(rec + m) = make_float4(st.O[m][r], st.O[m + 1][r], st.O[m + 2][r], st.O[m + 3][r]);
+    }
+  }
+  if (g4 == 0 && r16 < a.G) {
+    float* rec = a.part + (rec0 + static_cast<int64_t>(r16) * a.num_splits) * kRecD;
+    rec[D] = st.m_run;
+    rec[D + 1] = l_part;
+    rec[D + 2] = z_part;
+  }
+}
+
+template <int D, int KB, int VB>
+__global__ void __launch_bounds__(64, kDWavesPerSimd<D>) decode_dslab_kernel(MfmaArgs a) {
+  using DG = DGeom<D, KB, VB>;
+  __shared__ u32x2 s_tab[256];
+  __shared__ int64_t s_page_off[kMaxChunkPages];
+
+  const int lane = threadIdx.x;
+  const int r16 = lane & 15;
+  const int g4 = lane >> 4;
+  // XCD-aware order, kv head fastest (as the d = 128 direct kernel)
+  const int n_items = a.num_splits * a.batch * a.H;
+  const int per_xcd = (n_items + 7) / 8;
+  const int item = static_cast<int>(blockIdx.x % 8) * per_xcd + static_cast<int>(blockIdx.x / 8);
+  if (item >= n_items) return;
+  const int g = item % a.H;
+  const int split = (item / a.H) % a.num_splits;
+  const int b = item / (a.H * a.num_splits);
+  const int64_t row_bytes = static_cast<int64_t>(a.H) * DG::kSlot;
+  const int64_t page_bytes = static_cast<int64_t>(1 << a.bs_shift) * row_bytes;
+
+  if constexpr (KB != 8) build_tables<KB>(a, s_tab);
+  const int T = clamp_len(a, b, split, g);
+  const int t0 = split * a.chunk;
+  const int t1 = min(T, t0 + a.chunk);
+  stage_page_offsets(a, b, t0, t1, page_bytes, s_page_off);
+  __syncthreads();
+  if (t0 >= t1) return;
+
+  h8 qhi[KB == 8 ? 1 : D / 32], qlo[KB == 8 ? 1 : D / 32];
+  bf8v qb[KB == 8 ? D / 32 : 1];
+  if constexpr (KB == 8)
+    load_queries_bf16_d<D>(a, b, g, r16, g4, qb);
+  else
+    load_queries_d<D>(a, b, g, r16, g4, qhi, qlo);
+  RunStateD<D> st;
+#pragma unroll
+  for (int m = 0; m < D / 16; ++m) st.O[m] = f4{0.f, 0.f, 0.f, 0.f};
+  st.m_run = -INFINITY;
+  st.l_part = 0.0f;
+  st.z_part = 0.0f;
+  const int p_first = t0 >> a.bs_shift;
+  const DOffsets<D, KB, VB> off = dslab_offsets<D, KB, VB>(r16, g4, static_cast<uint32_t>(g * DG::kSlot),
+                                                           static_cast<uint32_t>(row_bytes));
+
+  // two slabs in flight in two register sets, the same loads every step (an
+  // empty range past the split end or on a bad page)
+  DRegs<D, KB, VB> r0, r1;
+  auto load = [&](int t, DRegs<D, KB, VB>& r) {
+    bool ok;
+    const __amdgpu_buffer_rsrc_t rs = slab_rsrc(a, s_page_off, p_first, t, t1, row_bytes, ok);
+    r.ok = ok;
+    dslab_load<D, KB, VB>(rs, off, r);
+  };
+  auto step = [&](int t, DRegs<D, KB, VB>& r) {
+    if (r.ok) {
+      float sc[4];
+      if constexpr (KB == 8)
+        score_slab8_d<D, KB, VB>(r, t1 - t, qb, a.scale_log2, g4, sc);
+      else
+        score_slab_d<D, KB, VB>(r, t1 - t, s_tab, qhi, qlo, g4, sc);
+      softmax_pv_d<D, KB, VB>(sc, t1 - t, r, off.vshift, g4, st);
+    }
+    load(t + 32, r);
+  };
+  load(t0, r0);
+  load(t0 + 16, r1);
+  for (int t = t0; t < t1; t += 32) {
+    step(t, r0);
+    step(t + 16, r1);
+  }
+  store_partials_d<D>(a, b, g, split, g4, r16, st);
+}
+
+// the queries of kv head g rotated as the store rotated the keys, fp32 into
+// q_rot [B][Hq][D]: signed Hadamard q_rot = H diag(s) q / sqrt(D) by
+// butterflies in LDS, or the Haar matrix's product q_rot = Q q.  One
+// workgroup per (sequence, kv head), thread i forms coordinate i.
+template <int D>
+__global__ void __launch_bounds__(D) rotate_queries_d_kernel(MfmaArgs a, float* q_rot, int haar) {
+  __shared__ float s_q[16][D];
+  const int b = blockIdx.x / a.H, g = blockIdx.x - b * a.H;
+  const int i = threadIdx.x;
+  const int64_t base = (static_cast<int64_t>(b) * a.Hq + g * a.Gq + a.h0) * D;
+  const uint32_t neg = haar ? 0u : ((a.tables->sign_bits[i >> 5] >> (i & 31)) & 1u) << 31;
+  for (int h = 0; h < a.G; ++h)
+    s_q[h][i] = __uint_as_float((static_cast<uint32_t>(a.q[base + h * D + i]) << 16) ^ neg);
+  __syncthreads();
+  if (haar) {
+    float acc[16];
+#pragma unroll
+    for (int h = 0; h < 16; ++h) acc[h] = 0.0f;
+    const float* rowq = a.tables->rot + static_cast<int64_t>(i) * D;
+    for (int j = 0; j < D; ++j) {
+      const float qij = rowq[j];
+#pragma unroll
+      for (int h = 0; h < 16; ++h)
+        if (h < a.G) acc[h] = __builtin_fmaf(qij, s_q[h][j], acc[h]);
+    }
+#pragma unroll
+    for (int h = 0; h < 16; ++h)
+      if (h < a.G) q_rot[base + h * D + i] = acc[h];
+    return;
+  }
+  for (int hs = 1; hs < D; hs *= 2) {
+    float v[16];
+#pragma unroll
+    for (int h = 0; h < 16; ++h)
+      if (h < a.G) {
+        const float x = s_q[h][i], y = s_q[h][i ^ hs];
+        v[h] = (i & hs) ? (y - x) : (x + y);
+      }
+    __syncthreads();
+#pragma unroll
+    for (int h = 0; h < 16; ++h)
+      if (h < a.G) s_q[h][i] = v[h];
+    __syncthreads();
+  }
+  const float inv = D == 64 ? 0.125f : 0.0625f;   // 1 / sqrt(D)
+  for (int h = 0; h < a.G; ++h) q_rot[base + h * D + i] = s_q[h][i] * inv;
+}
+
+// merge of the splits of one (sequence, query head), as decode_merge_kernel:
+// four wavefronts take every fourth split, lane = coordinates E*lane + e
+template <int D>
+__global__ void __launch_bounds__(256) decode_merge_d_kernel(MfmaArgs a) {
+  constexpr int E = D / 64;
+  constexpr int kRecD = D + 4;
+  __shared__ float s_m[4], s_l[4];
+  __shared__ float s_acc[4][D];
+  const int bh = blockIdx.x;
+  const int b = bh / a.Hq;
+  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int T = effective_len(a, b);
+  const int nsp = (T + a.chunk - 1) / a.chunk;
+  const float* recs = a.part + static_cast<int64_t>(bh) * a.num_splits * kRecD;
+  float M = -INFINITY, L = 0.0f;
+  float acc[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) acc[e] = 0.0f;
+  for (int sp = wv; sp < nsp; sp += 4) {
+    const float* rec = recs + static_cast<int64_t>(sp) * kRecD;
+    const float4 mlz = *reinterpret_cast<const float4*>(rec + D);   // m, l, z, pad
+    float o[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) o[e] = rec[E * lane + e];
+    const float m_new = fmaxf(M, mlz.x);
+    if (m_new == -INFINITY) continue;                         // nothing attended yet (bad pages)
+    const float c = __builtin_amdgcn_exp2f(M - m_new);
+    const float w = __builtin_amdgcn_exp2f(mlz.x - m_new);
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[e] = acc[e] * c + w * (o[e] + mlz.z);
+    L = L * c + w * mlz.y;
+    M = m_new;
+  }
+  if (lane == 0) {
+    s_m[wv] = M;
+    s_l[wv] = L;
+  }
+#pragma unroll
+  for (int e = 0; e < E; ++e) s_acc[wv][E * lane + e] = acc[e];
+  __syncthreads();
+  if (wv != 0) return;
+  const float Mx = fmaxf(fmaxf(s_m[0], s_m[1]), fmaxf(s_m[2], s_m[3]));
+  float Lt = 0.0f, tot[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) tot[e] = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float w = s_m[i] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(s_m[i] - Mx);
+#pragma unroll
+    for (int e = 0; e < E; ++e) tot[e] += w * s_acc[i][E * lane + e];
+    Lt += w * s_l[i];
+  }
+  const float inv = Lt > 0.0f ? 1.0f / Lt : 0.0f;
+  const int64_t oi = static_cast<int64_t>(bh) * D + E * lane;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const float r = tot[e] * inv;
+    if (a.out_fp32) {
+      static_cast<float*>(a.out)[oi + e] = r;
+    } else {
+      uint32_t u = __float_as_uint(r);
+      u = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;     // round to nearest even
+      static_cast<uint16_t*>(a.out)[oi + e] = static_cast<uint16_t>(u);
+    }
+  }
+}
+
+template <int D>
+hipError_t launch_dslab_d(const Geometry& g, const DecodePlan& plan, MfmaArgs& a, int batch, float* q_rot,
+                          hipStream_t stream) {
+  if (g.key_bits != 8) {
+    hipLaunchKernelGGL((rotate_queries_d_kernel<D>), dim3(batch * g.num_kv_heads), dim3(D), 0, stream, a, q_rot,
+                       g.haar ? 1 : 0);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    a.q_rot = q_rot;
+  }
+  const int n_items = plan.num_splits * batch * g.num_kv_heads;
+  const dim3 grid(8 * ((n_items + 7) / 8));
+  if (g.key_bits == 8)
+    hipLaunchKernelGGL((decode_dslab_kernel<D, 8, 4>), grid, dim3(64), 0, stream, a);
+  else if (g.key_bits == 4)
+    hipLaunchKernelGGL((decode_dslab_kernel<D, 4, 4>), grid, dim3(64), 0, stream, a);
+  else if (g.value_bits == 4)
+    hipLaunchKernelGGL((decode_dslab_kernel<D, 3, 4>), grid, dim3(64), 0, stream, a);
+  else
+    hipLaunchKernelGGL((decode_dslab_kernel<D, 3, 3>), grid, dim3(64), 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((decode_merge_d_kernel<D>), dim3(batch * a.Hq), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 int mfma_waves_per_cu(const Geometry& g, bool staged) {
@@ -2354,6 +2886,27 @@ bool mfma_decode_eligible(const Geometry& g, int num_q_heads) {
   return (g.key_bits == 4 || g.key_bits == 3) && (g.slot == 134 || g.slot == 118 || g.slot == 102);
 }
 
+// slotted pages at head dims 64 and 256, up to 16 query heads per kv head,
+// the presets' key / value bit pairs, and the slot size the kernel's layout
+// assumes
+bool dslab_decode_eligible(const Geometry& g, int num_q_heads) {
+  if (g.soa || (g.head_dim != 64 && g.head_dim != 256) || g.block_size % 16 != 0) return false;
+  const int G = num_q_heads / g.num_kv_heads;
+  if (G < 1 || G > 16) return false;
+  const int kb = g.key_bits, vb = g.value_bits, D = g.head_dim;
+  if (!((vb == 4 && (kb == 4 || kb == 3 || kb == 8)) || (kb == 3 && vb == 3))) return false;
+  const int s = (kb == 8 ? D : D * kb / 8 + 2) + D * vb / 8 + 4;
+  return g.slot == s + s % 2;
+}
+
+int dslab_waves_per_cu(const Geometry& g) {
+  return 4 * (g.head_dim == 256 ? kDWavesPerSimd<256> : kDWavesPerSimd<64>);
+}
+
+size_t dslab_partial_bytes(const Geometry& g, int batch, int num_q_heads, int num_splits) {
+  return static_cast<size_t>(batch) * num_q_heads * num_splits * (g.head_dim + 4) * sizeof(float);
+}
+
 size_t mfma_partial_bytes(int batch, int num_q_heads, int num_splits) {
   return static_cast<size_t>(batch) * num_q_heads * num_splits * kRec * sizeof(float);
 }
@@ -2387,6 +2940,16 @@ hipError_t launch_decode_mfma(const Geometry& g, const DevTables* tables, DevErr
   a.dynamic = plan.dynamic;
   a.q_rot = nullptr;
   a.order = nullptr;
+  if (plan.mfma == 5) {
+    // head dims 64 and 256: queries rotated into the workspace, the direct
+    // kernel, the merge
+    a.h0 = 0;
+    a.G = a.Gq;
+    float* q_rot = plan.qrot ? reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.qrot_off) : nullptr;
+    if (g.key_bits != 8 && q_rot == nullptr) return hipErrorInvalidValue;
+    return g.head_dim == 64 ? launch_dslab_d<64>(g, plan, a, batch, q_rot, stream)
+                            : launch_dslab_d<256>(g, plan, a, batch, q_rot, stream);
+  }
   if (plan.order) {
     a.h0 = 0;
     a.G = a.Gq;

@@ -77,8 +77,8 @@ hipError_t launch_store(const Geometry& g, const DevTables* tables, DevErrors* e
 
 struct DecodePlan {
   int mfma;         // matrix-core kernels (tq_decode_mfma.hip): 2 page-cooperative,
-                    // 3 staged per-head, 4 ring per-head, 1 direct per-head;
-                    // 0: general kernel
+                    // 3 staged per-head, 4 ring per-head, 1 direct per-head,
+                    // 5 direct per-head at head dims 64 and 256; 0: general kernel
   int group;        // page kernel: kv heads per workgroup (1, 2, 4 or 8)
   int chunk;        // tokens per split
   int num_splits;   // splits per sequence (grid extent)
@@ -90,8 +90,9 @@ struct DecodePlan {
   int order;          // ring kernel: sequences ranked by length (longest first, int32 [B])
                       // in the workspace at byte order_off, workgroups dispatched in that order
   size_t order_off;
-  int qrot;           // Haar rotation on a matrix-core kernel: the rotated queries (fp32
-                      // [B][Hq][d]) sit in the workspace at byte qrot_off
+  int qrot;           // Haar rotation on a matrix-core kernel, or any MSE keys at head dims
+                      // 64 and 256: the rotated queries (fp32 [B][Hq][d]) sit in the
+                      // workspace at byte qrot_off
   size_t qrot_off;
   int g_pass;         // matrix-core kernels: query heads per kv head in one pass of the
                       // kernel (its limit: 8 ring and page, 16 staged and direct); more
@@ -105,6 +106,9 @@ bool staged_decode_eligible(const Geometry& g, int num_q_heads);
 bool ring_decode_eligible(const Geometry& g, int num_q_heads);
 int ring_max_slabs();
 int mfma_max_g(int mfma);
+bool dslab_decode_eligible(const Geometry& g, int num_q_heads);
+int dslab_waves_per_cu(const Geometry& g);
+size_t dslab_partial_bytes(const Geometry& g, int batch, int num_q_heads, int num_splits);
 int mfma_waves_per_cu(const Geometry& g, bool staged);
 size_t mfma_partial_bytes(int batch, int num_q_heads, int num_splits);
 hipError_t launch_decode_mfma(const Geometry& g, const DevTables* tables, DevErrors* errs,

@@ -217,6 +217,25 @@ def test_decode_block_sizes_and_head_dims(bs, d, preset):
     check_decode(got, want, bf16_out=False)
 
 
+@pytest.mark.parametrize("preset", PRESETS)
+@pytest.mark.parametrize("d", [64, 256])
+@pytest.mark.parametrize("G,H,bs", [(1, 3, 16), (7, 2, 32), (16, 1, 16)])
+@pytest.mark.parametrize("kernel", ["", "general"])
+def test_decode_head_dims_64_256(preset, d, G, H, bs, kernel):
+    # head dims 64 and 256 on the slotted page take the direct matrix-core
+    # kernel at those dims (queries rotated into the workspace, D/32 score
+    # steps, D/16 value tiles, its own merge); the general fp32 kernel on the
+    # same inputs when asked.  Empty, one-token, page-edge and multi-split
+    # lengths; fp32 and bf16 outputs.
+    w = _wl(preset, G=G, H=H, d=d, bs=bs, B=6, lens=(1200, 1200), seed=G + H + d)
+    lens = [0, 1, 15, 16, 33, 1200]
+    got, want = _decode_from_oracle_cache(w, lens=lens, opts=dict(kernel=kernel))
+    check_decode(got, want, bf16_out=False)
+    assert np.all(got[0] == 0.0)
+    got16, want16 = _decode_from_oracle_cache(w, lens=lens, out_fp32=False, opts=dict(kernel=kernel))
+    check_decode(got16, want16, bf16_out=True)
+
+
 @pytest.mark.parametrize("preset", ["turboquant_4bit_nc", "turboquant_k3v4_nc", "turboquant_3bit_nc"])
 def test_decode_beta_codebook(preset):
     got, want = _decode_from_oracle_cache(_wl(preset, G=4, seed=31), mode="beta")

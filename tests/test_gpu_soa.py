@@ -213,8 +213,10 @@ def test_soa_decode_query_head_passes(preset, G, H):
 
 
 @pytest.mark.parametrize("preset", MSE)
-@pytest.mark.parametrize("G,H,d", [(4, 2, 64), (4, 2, 256)])
+@pytest.mark.parametrize("G,H,d", [(4, 2, 64), (4, 2, 256), (3, 2, 64), (7, 1, 256), (12, 1, 64)])
 def test_soa_decode_general_kernel(preset, G, H, d):
+    # other head dims on the split page: the general kernel, built for the
+    # next power of two of the query heads per kv head
     got, want = _decode_soa(_wl(preset, H=H, Hq=G * H, d=d, lens=(1, 500), B=3, seed=G + d))
     check_decode(got, want, bf16_out=False)
 

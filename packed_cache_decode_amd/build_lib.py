@@ -24,6 +24,7 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
 SOURCES = [
     ("tq_host.cpp", []),
     ("tq_store.hip", ["-ffp-contract=off"]),
+    ("tq_store_quad.hip", ["-ffp-contract=off"]),
     ("tq_decode.hip", []),
     ("tq_decode_mfma.hip", ["-fno-honor-nans"]),
     ("tq_dequant.hip", []),

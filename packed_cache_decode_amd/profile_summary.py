@@ -58,7 +58,8 @@ def short_name(name):
 KERNEL_SOURCES = {
     "decode": ("packed_cache_decode_amd/csrc/tq_decode.hip", "packed_cache_decode_amd/csrc/tq_decode_mfma.hip",
                "packed_cache_decode_amd/csrc/tq_internal.h"),
-    "store": ("packed_cache_decode_amd/csrc/tq_store.hip", "packed_cache_decode_amd/csrc/tq_internal.h"),
+    "store": ("packed_cache_decode_amd/csrc/tq_store.hip", "packed_cache_decode_amd/csrc/tq_store_common.h",
+              "packed_cache_decode_amd/csrc/tq_store_quad.hip", "packed_cache_decode_amd/csrc/tq_internal.h"),
 }
 
 

@@ -78,6 +78,18 @@ def test_store_block_sizes_and_head_dims(preset, bs, d):
     assert _assert_parity(inp, got, want, ors)["rows_differing"] == 0
 
 
+@pytest.mark.parametrize("preset", PRESETS)
+@pytest.mark.parametrize("d", [64, 256])
+@pytest.mark.parametrize("H", [1, 3, 8])
+def test_store_head_dims_64_256(preset, d, H):
+    # head dims 64 and 256 take the four-lanes-per-vector kernel (16 or 64
+    # coordinates per lane): rows assembled in LDS (8 kv heads) or written
+    # per lane (1 and 3), against the oracle byte for byte
+    inp, got, want, ors, err = _run_store(_small(preset, H=H, d=d, lens=(1, 200), B=4, seed=d + H))
+    assert err == 0
+    assert _assert_parity(inp, got, want, ors)["rows_differing"] == 0
+
+
 @pytest.mark.parametrize("preset", ["turboquant_4bit_nc", "turboquant_k3v4_nc", "turboquant_3bit_nc"])
 def test_store_pure_hadamard_and_page_codebook(preset):
     w = _small(preset, seed=9)
@@ -87,10 +99,11 @@ def test_store_pure_hadamard_and_page_codebook(preset):
 
 
 @pytest.mark.parametrize("preset", PRESETS)
-def test_store_degenerate_vectors(preset):
+@pytest.mark.parametrize("d", [128, 64, 256])
+def test_store_degenerate_vectors(preset, d):
     """zero K, constant V, K beyond the e4m3 range, tiny and huge magnitudes,
     and padding tokens (slot < 0) that must be skipped."""
-    w = _small(preset, H=2, lens=(40, 40), B=1, seed=3)
+    w = _small(preset, H=2, d=d, lens=(40, 40), B=1, seed=3)
     inp = synth.generate(w)
     k = fpfmt.bf16_bits_to_f32(inp.k).copy()
     v = fpfmt.bf16_bits_to_f32(inp.v).copy()
@@ -111,8 +124,9 @@ def test_store_degenerate_vectors(preset):
     assert _assert_parity(inp, got, want, ors, sm)["rows_differing"] == 0
 
 
-def test_store_out_of_range_slot_sets_error_and_skips():
-    w = _small("turboquant_4bit_nc", H=2, lens=(20, 20), B=1)
+@pytest.mark.parametrize("d", [128, 64, 256])
+def test_store_out_of_range_slot_sets_error_and_skips(d):
+    w = _small("turboquant_4bit_nc", H=2, d=d, lens=(20, 20), B=1)
     inp = synth.generate(w)
     sm = inp.slot_mapping.copy()
     sm[3] = (inp.num_blocks + 2) * 16 + 5      # beyond the cache (which has 2 spare pages)

@@ -438,7 +438,7 @@ DecodePlan plan_decode_kernels(const Geometry& g, const tq_decode_options& opts,
     // head dims 64 and 256 on the slotted page: the direct matrix-core
     // kernel's design at those dims (the forced d = 128 kernels do not apply),
     // one resident round of wavefronts over (split, sequence, kv head), at
-    // least 8 slabs per split; the queries rotated once into the workspace
+    // least 8 slabs per split; Haar-rotated queries once into the workspace
     const int slabs = max_seq_len > 0 ? (max_seq_len + 15) / 16 : 1;
     const int per_split = batch * g.num_kv_heads;
     const int target = 256 * dslab_waves_per_cu(g);
@@ -451,7 +451,7 @@ DecodePlan plan_decode_kernels(const Geometry& g, const tq_decode_options& opts,
     p.num_splits = max_seq_len > 0 ? (max_seq_len + p.chunk - 1) / p.chunk : 1;
     p.workspace_bytes = dslab_partial_bytes(g, batch, num_q_heads, p.num_splits);
     p.workspace_bytes = (p.workspace_bytes + 255) & ~static_cast<size_t>(255);
-    if (g.key_bits != 8) {
+    if (g.key_bits != 8 && g.haar) {
       p.qrot = 1;
       p.qrot_off = p.workspace_bytes;
       p.workspace_bytes += static_cast<size_t>(batch) * num_q_heads * g.head_dim * sizeof(float);

@@ -2391,27 +2391,80 @@ __device__ __forceinline__ void dslab_load(__amdgpu_buffer_rsrc_t rs, const DOff
   }
 }
 
-// rotated queries of kv head g (fp32, from the workspace) as f16 hi / lo B
-// operands, times the softmax scale (base 2); lane (h = r16, g4), step kk:
-// coordinates (D/4)*g4 + 8*kk + [0, 8)
+// queries of kv head g rotated as the store rotated the keys, times the
+// softmax scale (base 2), as f16 hi / lo B operands; lane (h = r16, g4), step
+// kk: coordinates (D/4)*g4 + 8*kk + [0, 8).  Signed Hadamard: the lane's
+// D/4 coordinates flipped and butterflied in registers (strides below D/4),
+// strides D/4 and D/2 with the partner lanes l ^ 16 and l ^ 32, times
+// 1/sqrt(D) (as load_queries at d = 128).  Haar: read rotated from the
+// workspace (a.q_rot, rotate_queries_d_kernel).
 template <int D>
 __device__ __forceinline__ void load_queries_d(const MfmaArgs& a, int b, int g, int r16, int g4,
                                                h8 (&qhi)[D / 32], h8 (&qlo)[D / 32]) {
+  constexpr int E = D / 4;
   const bool live = r16 < a.G;
-  const int64_t row = (static_cast<int64_t>(b) * a.Hq + g * a.Gq + a.h0 + (live ? r16 : 0)) * D + (D / 4) * g4;
-  const float4* rp = reinterpret_cast<const float4*>(a.q_rot + row);
+  const int64_t row = (static_cast<int64_t>(b) * a.Hq + g * a.Gq + a.h0 + (live ? r16 : 0)) * D + E * g4;
+  float x[E];
+  float fs = a.scale_log2;
+  if (a.q_rot != nullptr) {
+    const float4* rp = reinterpret_cast<const float4*>(a.q_rot + row);
 #pragma unroll
-  for (int kk = 0; kk < D / 32; ++kk) {
-    const float4 v0 = rp[2 * kk], v1 = rp[2 * kk + 1];
-    const float x[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+    for (int i = 0; i < E / 4; ++i) {
+      const float4 v = rp[i];
+      x[4 * i] = v.x;
+      x[4 * i + 1] = v.y;
+      x[4 * i + 2] = v.z;
+      x[4 * i + 3] = v.w;
+    }
+  } else {
+    const uint16_t* qp = a.q + row;
+#pragma unroll
+    for (int i = 0; i < E / 8; ++i) {
+      const u32x4 w = *reinterpret_cast<const u32x4*>(qp + 8 * i);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        x[8 * i + 2 * j] = __uint_as_float(w[j] << 16);
+        x[8 * i + 2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < E; ++j) {
+      const int c = E * g4 + j;
+      const uint32_t sb = (a.tables->sign_bits[c >> 5] >> (c & 31)) & 1u;
+      x[j] = __uint_as_float(__float_as_uint(x[j]) ^ (sb << 31));
+    }
+#pragma unroll
+    for (int hs = 1; hs < E; hs *= 2)
+#pragma unroll
+      for (int j = 0; j < E; ++j)
+        if ((j & hs) == 0) {
+          const float p = x[j], r = x[j + hs];
+          x[j] = p + r;
+          x[j + hs] = p - r;
+        }
+#pragma unroll
+    for (int j = 0; j < E; ++j) {
+      auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(x[j]), __float_as_uint(x[j]), false, false);
+      const float o = (g4 & 1) ? __uint_as_float(sw[0]) : __uint_as_float(sw[1]);
+      x[j] = (g4 & 1) ? (o - x[j]) : (x[j] + o);
+    }
+#pragma unroll
+    for (int j = 0; j < E; ++j) {
+      auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x[j]), __float_as_uint(x[j]), false, false);
+      const float o = (g4 & 2) ? __uint_as_float(sw[0]) : __uint_as_float(sw[1]);
+      x[j] = (g4 & 2) ? (o - x[j]) : (x[j] + o);
+    }
+    fs *= D == 64 ? 0.125f : 0.0625f;          // 1 / sqrt(D)
+  }
+#pragma unroll
+  for (int kk = 0; kk < D / 32; ++kk)
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float v = live ? x[e] * a.scale_log2 : 0.0f;
+      const float v = live ? x[8 * kk + e] * fs : 0.0f;
       const _Float16 hv = static_cast<_Float16>(v);
       qhi[kk][e] = hv;
       qlo[kk][e] = static_cast<_Float16>(v - static_cast<float>(hv));
     }
-  }
 }
 
 // FP8 keys: the queries as given (bf16), same coordinates
@@ -2662,9 +2715,11 @@ __global__ void __launch_bounds__(64, kDWavesPerSimd<D>) decode_dslab_kernel(Mfm
 }
 
 // the queries of kv head g rotated as the store rotated the keys, fp32 into
-// q_rot [B][Hq][D]: signed Hadamard q_rot = H diag(s) q / sqrt(D) by
-// butterflies in LDS, or the Haar matrix's product q_rot = Q q.  One
-// workgroup per (sequence, kv head), thread i forms coordinate i.
+// q_rot [B][Hq][D]: the Haar matrix's product q_rot = Q q (haar), or the
+// signed Hadamard q_rot = H diag(s) q / sqrt(D) by butterflies in LDS (the
+// decode kernel rotates Hadamard queries itself; this form is kept for any
+// caller that wants the rotated queries).  One workgroup per (sequence, kv
+// head), thread i forms coordinate i.
 template <int D>
 __global__ void __launch_bounds__(D) rotate_queries_d_kernel(MfmaArgs a, float* q_rot, int haar) {
   __shared__ float s_q[16][D];
@@ -2779,9 +2834,8 @@ __global__ void __launch_bounds__(256) decode_merge_d_kernel(MfmaArgs a) {
 template <int D>
 hipError_t launch_dslab_d(const Geometry& g, const DecodePlan& plan, MfmaArgs& a, int batch, float* q_rot,
                           hipStream_t stream) {
-  if (g.key_bits != 8) {
-    hipLaunchKernelGGL((rotate_queries_d_kernel<D>), dim3(batch * g.num_kv_heads), dim3(D), 0, stream, a, q_rot,
-                       g.haar ? 1 : 0);
+  if (g.key_bits != 8 && g.haar) {
+    hipLaunchKernelGGL((rotate_queries_d_kernel<D>), dim3(batch * g.num_kv_heads), dim3(D), 0, stream, a, q_rot, 1);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     a.q_rot = q_rot;
@@ -2946,7 +3000,7 @@ hipError_t launch_decode_mfma(const Geometry& g, const DevTables* tables, DevErr
     a.h0 = 0;
     a.G = a.Gq;
     float* q_rot = plan.qrot ? reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.qrot_off) : nullptr;
-    if (g.key_bits != 8 && q_rot == nullptr) return hipErrorInvalidValue;
+    if (g.key_bits != 8 && g.haar && q_rot == nullptr) return hipErrorInvalidValue;
     return g.head_dim == 64 ? launch_dslab_d<64>(g, plan, a, batch, q_rot, stream)
                             : launch_dslab_d<256>(g, plan, a, batch, q_rot, stream);
   }

@@ -26,8 +26,8 @@ from collections import defaultdict
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
-DECODE_KERNELS = re.compile(r"decode_(ring|page|slab|staged|split|combine|merge)_kernel")
-STORE_KERNELS = re.compile(r"store(128)?_kernel")
+DECODE_KERNELS = re.compile(r"decode_(ring|page|slab|dslab|staged|split|combine|merge|merge_d)_kernel")
+STORE_KERNELS = re.compile(r"store(128|_quad)?_kernel")
 
 
 def short_name(name):

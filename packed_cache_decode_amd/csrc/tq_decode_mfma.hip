@@ -2714,58 +2714,37 @@ __global__ void __launch_bounds__(64, kDWavesPerSimd<D>) decode_dslab_kernel(Mfm
   store_partials_d<D>(a, b, g, split, g4, r16, st);
 }
 
-// the queries of kv head g rotated as the store rotated the keys, fp32 into
-// q_rot [B][Hq][D]: the Haar matrix's product q_rot = Q q (haar), or the
-// signed Hadamard q_rot = H diag(s) q / sqrt(D) by butterflies in LDS (the
-// decode kernel rotates Hadamard queries itself; this form is kept for any
-// caller that wants the rotated queries).  One workgroup per (sequence, kv
-// head), thread i forms coordinate i.
+// Haar rotation of the queries at head dims 64 and 256, once per decode:
+// q_rot = Q q into the workspace (fp32 [B][Hq][D]), Q the D x D matrix the
+// store applied to the keys.  One workgroup per (sequence, kv head), thread i
+// forms coordinate i of its G queries (each row of Q read once).
 template <int D>
-__global__ void __launch_bounds__(D) rotate_queries_d_kernel(MfmaArgs a, float* q_rot, int haar) {
+__global__ void __launch_bounds__(D) rotate_queries_d_kernel(MfmaArgs a, float* q_rot) {
   __shared__ float s_q[16][D];
   const int b = blockIdx.x / a.H, g = blockIdx.x - b * a.H;
   const int i = threadIdx.x;
   const int64_t base = (static_cast<int64_t>(b) * a.Hq + g * a.Gq + a.h0) * D;
-  const uint32_t neg = haar ? 0u : ((a.tables->sign_bits[i >> 5] >> (i & 31)) & 1u) << 31;
   for (int h = 0; h < a.G; ++h)
-    s_q[h][i] = __uint_as_float((static_cast<uint32_t>(a.q[base + h * D + i]) << 16) ^ neg);
+    s_q[h][i] = __uint_as_float(static_cast<uint32_t>(a.q[base + h * D + i]) << 16);
   __syncthreads();
-  if (haar) {
-    float acc[16];
+  float acc[16];
 #pragma unroll
-    for (int h = 0; h < 16; ++h) acc[h] = 0.0f;
-    const float* rowq = a.tables->rot + static_cast<int64_t>(i) * D;
-    for (int j = 0; j < D; ++j) {
-      const float qij = rowq[j];
-#pragma unroll
-      for (int h = 0; h < 16; ++h)
-        if (h < a.G) acc[h] = __builtin_fmaf(qij, s_q[h][j], acc[h]);
-    }
+  for (int h = 0; h < 16; ++h) acc[h] = 0.0f;
+  const float* rowq = a.tables->rot + static_cast<int64_t>(i) * D;
+  for (int j = 0; j < D; ++j) {
+    const float qij = rowq[j];
 #pragma unroll
     for (int h = 0; h < 16; ++h)
-      if (h < a.G) q_rot[base + h * D + i] = acc[h];
-    return;
+      if (h < a.G) acc[h] = __builtin_fmaf(qij, s_q[h][j], acc[h]);
   }
-  for (int hs = 1; hs < D; hs *= 2) {
-    float v[16];
 #pragma unroll
-    for (int h = 0; h < 16; ++h)
-      if (h < a.G) {
-        const float x = s_q[h][i], y = s_q[h][i ^ hs];
-        v[h] = (i & hs) ? (y - x) : (x + y);
-      }
-    __syncthreads();
-#pragma unroll
-    for (int h = 0; h < 16; ++h)
-      if (h < a.G) s_q[h][i] = v[h];
-    __syncthreads();
-  }
-  const float inv = D == 64 ? 0.125f : 0.0625f;   // 1 / sqrt(D)
-  for (int h = 0; h < a.G; ++h) q_rot[base + h * D + i] = s_q[h][i] * inv;
+  for (int h = 0; h < 16; ++h)
+    if (h < a.G) q_rot[base + h * D + i] = acc[h];
 }
 
 // merge of the splits of one (sequence, query head), as decode_merge_kernel:
-// four wavefronts take every fourth split, lane = coordinates E*lane + e
+// four wavefronts take every fourth split (the loads of four of its splits
+// issued together), lane = coordinates E*lane + e
 template <int D>
 __global__ void __launch_bounds__(256) decode_merge_d_kernel(MfmaArgs a) {
   constexpr int E = D / 64;
@@ -2782,20 +2761,30 @@ __global__ void __launch_bounds__(256) decode_merge_d_kernel(MfmaArgs a) {
   float acc[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) acc[e] = 0.0f;
-  for (int sp = wv; sp < nsp; sp += 4) {
-    const float* rec = recs + static_cast<int64_t>(sp) * kRecD;
-    const float4 mlz = *reinterpret_cast<const float4*>(rec + D);   // m, l, z, pad
-    float o[E];
+  constexpr int kU = 4;
+  for (int s0 = wv; s0 < nsp; s0 += 4 * kU) {
+    float4 mlz[kU];
+    float o[kU][E];
 #pragma unroll
-    for (int e = 0; e < E; ++e) o[e] = rec[E * lane + e];
-    const float m_new = fmaxf(M, mlz.x);
-    if (m_new == -INFINITY) continue;                         // nothing attended yet (bad pages)
-    const float c = __builtin_amdgcn_exp2f(M - m_new);
-    const float w = __builtin_amdgcn_exp2f(mlz.x - m_new);
+    for (int u = 0; u < kU; ++u) {
+      const int sp = s0 + 4 * u;
+      const float* rec = recs + static_cast<int64_t>(sp < nsp ? sp : s0) * kRecD;
+      mlz[u] = *reinterpret_cast<const float4*>(rec + D);     // m, l, z, pad
 #pragma unroll
-    for (int e = 0; e < E; ++e) acc[e] = acc[e] * c + w * (o[e] + mlz.z);
-    L = L * c + w * mlz.y;
-    M = m_new;
+      for (int e = 0; e < E; ++e) o[u][e] = rec[E * lane + e];
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      if (s0 + 4 * u >= nsp) break;
+      const float m_new = fmaxf(M, mlz[u].x);
+      if (m_new == -INFINITY) continue;                       // nothing attended yet (bad pages)
+      const float c = __builtin_amdgcn_exp2f(M - m_new);
+      const float w = __builtin_amdgcn_exp2f(mlz[u].x - m_new);
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[e] = acc[e] * c + w * (o[u][e] + mlz[u].z);
+      L = L * c + w * mlz[u].y;
+      M = m_new;
+    }
   }
   if (lane == 0) {
     s_m[wv] = M;
@@ -2835,7 +2824,7 @@ template <int D>
 hipError_t launch_dslab_d(const Geometry& g, const DecodePlan& plan, MfmaArgs& a, int batch, float* q_rot,
                           hipStream_t stream) {
   if (g.key_bits != 8 && g.haar) {
-    hipLaunchKernelGGL((rotate_queries_d_kernel<D>), dim3(batch * g.num_kv_heads), dim3(D), 0, stream, a, q_rot, 1);
+    hipLaunchKernelGGL((rotate_queries_d_kernel<D>), dim3(batch * g.num_kv_heads), dim3(D), 0, stream, a, q_rot);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     a.q_rot = q_rot;

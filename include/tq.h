@@ -271,8 +271,8 @@ size_t tq_decode_workspace_bytes(const tq_ctx* ctx, int batch, int num_q_heads,
  * (8 on the split page), each pass reading the cache; other shapes with
  * more than 16 return TQ_ERR_UNSUPPORTED.  Head dims 64 and 256 run on a
  * matrix-core kernel of their own on the slotted page (block_size a multiple
- * of 16, up to 16 query heads per kv head), on the general fp32 kernel on
- * the split page.
+ * of 16, any number of query heads per kv head, in passes of 16), on the
+ * general fp32 kernel (at most 16) on the split page.
  *
  * Reproducibility.  The plan (kernel, split count, order of the fp32 sums)
  * depends only on the shape arguments and the context's decode options, so

@@ -2820,27 +2820,36 @@ __global__ void __launch_bounds__(256) decode_merge_d_kernel(MfmaArgs a) {
   }
 }
 
+// query heads in passes of at most 16 per kv head (each pass reads the
+// cache; Haar queries rotated per pass), one merge for every head
 template <int D>
 hipError_t launch_dslab_d(const Geometry& g, const DecodePlan& plan, MfmaArgs& a, int batch, float* q_rot,
                           hipStream_t stream) {
-  if (g.key_bits != 8 && g.haar) {
-    hipLaunchKernelGGL((rotate_queries_d_kernel<D>), dim3(batch * g.num_kv_heads), dim3(D), 0, stream, a, q_rot);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    a.q_rot = q_rot;
-  }
   const int n_items = plan.num_splits * batch * g.num_kv_heads;
   const dim3 grid(8 * ((n_items + 7) / 8));
-  if (g.key_bits == 8)
-    hipLaunchKernelGGL((decode_dslab_kernel<D, 8, 4>), grid, dim3(64), 0, stream, a);
-  else if (g.key_bits == 4)
-    hipLaunchKernelGGL((decode_dslab_kernel<D, 4, 4>), grid, dim3(64), 0, stream, a);
-  else if (g.value_bits == 4)
-    hipLaunchKernelGGL((decode_dslab_kernel<D, 3, 4>), grid, dim3(64), 0, stream, a);
-  else
-    hipLaunchKernelGGL((decode_dslab_kernel<D, 3, 3>), grid, dim3(64), 0, stream, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  for (int h0 = 0; h0 < a.Gq; h0 += 16) {
+    a.h0 = h0;
+    a.G = a.Gq - h0 < 16 ? a.Gq - h0 : 16;
+    if (g.key_bits != 8 && g.haar) {
+      a.q_rot = nullptr;
+      hipLaunchKernelGGL((rotate_queries_d_kernel<D>), dim3(batch * g.num_kv_heads), dim3(D), 0, stream, a, q_rot);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      a.q_rot = q_rot;
+    }
+    if (g.key_bits == 8)
+      hipLaunchKernelGGL((decode_dslab_kernel<D, 8, 4>), grid, dim3(64), 0, stream, a);
+    else if (g.key_bits == 4)
+      hipLaunchKernelGGL((decode_dslab_kernel<D, 4, 4>), grid, dim3(64), 0, stream, a);
+    else if (g.value_bits == 4)
+      hipLaunchKernelGGL((decode_dslab_kernel<D, 3, 4>), grid, dim3(64), 0, stream, a);
+    else
+      hipLaunchKernelGGL((decode_dslab_kernel<D, 3, 3>), grid, dim3(64), 0, stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  a.h0 = 0;
+  a.G = a.Gq;
   hipLaunchKernelGGL((decode_merge_d_kernel<D>), dim3(batch * a.Hq), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
@@ -2929,13 +2938,13 @@ bool mfma_decode_eligible(const Geometry& g, int num_q_heads) {
   return (g.key_bits == 4 || g.key_bits == 3) && (g.slot == 134 || g.slot == 118 || g.slot == 102);
 }
 
-// slotted pages at head dims 64 and 256, up to 16 query heads per kv head,
-// the presets' key / value bit pairs, and the slot size the kernel's layout
-// assumes
+// slotted pages at head dims 64 and 256 (more than 16 query heads per kv
+// head in passes of 16), the presets' key / value bit pairs, and the slot
+// size the kernel's layout assumes
 bool dslab_decode_eligible(const Geometry& g, int num_q_heads) {
   if (g.soa || (g.head_dim != 64 && g.head_dim != 256) || g.block_size % 16 != 0) return false;
   const int G = num_q_heads / g.num_kv_heads;
-  if (G < 1 || G > 16) return false;
+  if (G < 1) return false;
   const int kb = g.key_bits, vb = g.value_bits, D = g.head_dim;
   if (!((vb == 4 && (kb == 4 || kb == 3 || kb == 8)) || (kb == 3 && vb == 3))) return false;
   const int s = (kb == 8 ? D : D * kb / 8 + 2) + D * vb / 8 + 4;
@@ -2984,10 +2993,8 @@ hipError_t launch_decode_mfma(const Geometry& g, const DevTables* tables, DevErr
   a.q_rot = nullptr;
   a.order = nullptr;
   if (plan.mfma == 5) {
-    // head dims 64 and 256: queries rotated into the workspace, the direct
-    // kernel, the merge
-    a.h0 = 0;
-    a.G = a.Gq;
+    // head dims 64 and 256: the direct kernel in passes of 16 query heads,
+    // the merge
     float* q_rot = plan.qrot ? reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.qrot_off) : nullptr;
     if (g.key_bits != 8 && g.haar && q_rot == nullptr) return hipErrorInvalidValue;
     return g.head_dim == 64 ? launch_dslab_d<64>(g, plan, a, batch, q_rot, stream)

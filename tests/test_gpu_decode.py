@@ -82,12 +82,22 @@ def test_decode_query_head_passes(preset, G, H):
     check_decode(got16, want16, bf16_out=True)
 
 
-def test_decode_more_than_16_query_heads_needs_head_dim_128():
-    # the general kernel (other head dims) takes at most 16 query heads per kv head
+def test_decode_more_than_16_query_heads_general_kernel_refuses():
+    # the general kernel takes at most 16 query heads per kv head
     from packed_cache_decode_amd import _lib
     w = _wl("turboquant_4bit_nc", G=24, H=1, d=64, B=1, lens=(20, 20), seed=3)
     with pytest.raises(_lib.TQError, match="UNSUPPORTED"):
-        _decode_from_oracle_cache(w)
+        _decode_from_oracle_cache(w, opts=dict(kernel="general"))
+
+
+@pytest.mark.parametrize("preset", PRESETS)
+@pytest.mark.parametrize("d", [64, 256])
+def test_decode_head_dims_64_256_query_head_passes(preset, d):
+    # more than 16 query heads per kv head at head dims 64 and 256: the
+    # direct kernel in passes of 16 (the last one short), one merge for all
+    w = _wl(preset, G=24, H=2, d=d, B=4, lens=(900, 900), seed=d + 7)
+    got, want = _decode_from_oracle_cache(w, lens=[0, 1, 450, 900])
+    check_decode(got, want, bf16_out=False)
 
 
 # the context's decode options force one kernel where it applies ("" picks by

@@ -104,19 +104,20 @@ def test_haar_decode_matrix_core_kernels(preset, kernel):
 
 
 @pytest.mark.parametrize("preset", MSE)
-@pytest.mark.parametrize("kernel", ["", "direct"])
-def test_haar_decode_query_head_passes(preset, kernel):
+@pytest.mark.parametrize("kernel,d", [("", 128), ("direct", 128), ("", 64), ("", 256)])
+def test_haar_decode_query_head_passes(preset, kernel, d):
     # 24 query heads per kv head: the per-head kernels in passes of 16, the
-    # queries of each pass rotated into the workspace before it
+    # queries of each pass rotated into the workspace before it (head dims
+    # 64 and 256: the direct kernel at those dims)
     from packed_cache_decode_amd.runtime import PackedKVCache
     H, G, seed = 2, 24, 81
-    w = _wl(preset, H=H, Hq=G * H, d=128, seed=6, lens=(1, 700), B=3)
+    w = _wl(preset, H=H, Hq=G * H, d=d, seed=6, lens=(1, 700), B=3)
     inp = synth.generate(w)
-    ors = OracleSide(preset, 128, seed, "haar")
+    ors = OracleSide(preset, d, seed, "haar")
     cache = np.zeros((inp.num_blocks, 16, H, ors.lay.slot_size_aligned), np.uint8)
     ors.store(cache, inp.k, inp.v, inp.slot_mapping)
     want = ors.decode(inp.q, cache, inp.block_table, inp.seq_lens, H)
-    tq = PackedKVCache(preset, 128, H, 16, seed, sign_flip="haar")
+    tq = PackedKVCache(preset, d, H, 16, seed, sign_flip="haar")
     tq.set_decode_options(kernel=kernel)
     out = tq.decode(to_dev(inp.q), to_dev(cache), to_dev(inp.block_table), to_dev(inp.seq_lens),
                     int(max(1, inp.seq_lens.max())), out_fp32=True)

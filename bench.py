@@ -70,6 +70,15 @@ def decode_alg_bytes(inp, slot):
                + 4 * pages.sum() + 4 * w.batch)
 
 
+def workload_for(name, head_dim=0):
+    """The named workload, or its shapes at another head dim (named <name>_d<dim>)."""
+    from packed_cache_decode_amd import synth
+    w = synth.WORKLOADS[name]
+    if head_dim and head_dim != w.head_dim:
+        w = dataclasses.replace(w, head_dim=head_dim, name=f"{w.name}_d{head_dim}")
+    return w
+
+
 def store_alg_bytes_per_token(w, slot):
     return w.num_kv_heads * (2 * w.head_dim * 2 + slot) + 8
 
@@ -241,9 +250,7 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    w = synth.WORKLOADS[args.workload]
-    if args.head_dim and args.head_dim != w.head_dim:
-        w = dataclasses.replace(w, head_dim=args.head_dim, name=f"{w.name}_d{args.head_dim}")
+    w = workload_for(args.workload, args.head_dim)
     print(f"[bench] generating {w.name}", file=sys.stderr, flush=True)
     inp = synth.generate(w)
     synth.assert_unique_slots(inp.slot_mapping)      # one store may not write a slot twice

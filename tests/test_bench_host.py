@@ -54,6 +54,20 @@ def test_decode_algorithmic_bytes_ragged():
     assert got == want
 
 
+def test_workload_at_another_head_dim():
+    # --head-dim: the same shapes at d = 64, named apart; 32 x 4096 tokens x
+    # 8 heads x 70 B + 2 x 32 x 32 x 64 x 2 B + 4 x 8192 pages + 4 x 32
+    w = bench.workload_for("llama3_8b", 64)
+    base = synth.WORKLOADS["llama3_8b"]
+    assert (w.name, w.head_dim) == ("llama3_8b_d64", 64)
+    assert (w.batch, w.num_q_heads, w.num_kv_heads, w.seq_len, w.seed) == (
+        base.batch, base.num_q_heads, base.num_kv_heads, base.seq_len, base.seed)
+    assert bench.workload_for("llama3_8b", 128) is base
+    assert bench.workload_for("llama3_8b") is base
+    inp = SimpleNamespace(w=w, seq_lens=np.full(w.batch, 4096, np.int32))
+    assert bench.decode_alg_bytes(inp, 70) == 73_695_360
+
+
 @pytest.mark.parametrize("slot,want", [(134, 5176), (118, 5048), (196, 5672)])
 def test_store_algorithmic_bytes_per_token(slot, want):
     # 8 heads x (K and V bf16 in: 2 x 128 x 2 B, plus the slot out) + 8 B slot index

@@ -2275,13 +2275,15 @@ hipError_t launch_page_h(const MfmaArgs& a, int batch, int group, hipStream_t st
 
 // ============================================================================
 // direct, head dims 64 and 256: the direct kernel's design at the other head
-// dims of the slotted page, up to 16 query heads per kv head, one wavefront
-// per (split, sequence, kv head), each lane loading its operand bytes.
+// dims of the slotted page, up to 16 query heads per kv head in one pass
+// (more in passes of 16), one wavefront per (split, sequence, kv head), each
+// lane loading its operand bytes.
 // Lane (r16, g4) holds K coordinates [(D/4)*g4, (D/4)*(g4+1)) of token r16
 // (score step kk: (D/4)*g4 + 8*kk + [0, 8)), and the V codes of tokens
 // 4*g4 + r for coordinates [(D/16)*r16, (D/16)*(r16+1)); value tile m column
-// j covers coordinate (D/16)*j + m.  The queries are rotated once per decode
-// by rotate_queries_d_kernel (signed Hadamard or Haar) into the workspace.
+// j covers coordinate (D/16)*j + m.  Signed-Hadamard queries are rotated in
+// the kernel's prologue (load_queries_d); Haar queries once per pass by
+// rotate_queries_d_kernel into the workspace.
 // Scores, norm correction, softmax and P.V are those of the d = 128 direct
 // kernel (score_slab, softmax_pv), over D/32 score steps and D/16 tiles.
 // ============================================================================

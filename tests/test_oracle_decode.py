@@ -24,14 +24,14 @@ from oracle import store as st
 from packed_cache_decode_amd import synth
 
 
-def _tiny_case(preset="turboquant_4bit_nc", T=77, H=2, Hq=4, seed=0, permute=True):
-    w = synth.Workload("t", preset, batch=3, num_q_heads=Hq, num_kv_heads=H, head_dim=128,
+def _tiny_case(preset="turboquant_4bit_nc", T=77, H=2, Hq=4, seed=0, permute=True, d=128):
+    w = synth.Workload("t", preset, batch=3, num_q_heads=Hq, num_kv_heads=H, head_dim=d,
                        block_size=16, seed=seed, len_range=(1, T), permute_pages=permute)
     inp = synth.generate(w)
-    lay = layout.slot_layout(preset, 128)
-    signs = rotation.rotation_signs(seed + 11, 128)
+    lay = layout.slot_layout(preset, d)
+    signs = rotation.rotation_signs(seed + 11, d)
     kb = lay.key_bits if not lay.key_fp8 else 4
-    c, m = cb.codebook(128, kb)
+    c, m = cb.codebook(d, kb)
     cache = np.zeros((inp.num_blocks, 16, H, lay.slot_size_aligned), np.uint8)
     st.store_contract(cache, inp.k, inp.v, inp.slot_mapping, lay, signs, m)
     return inp, lay, signs, c, m, cache
@@ -70,11 +70,13 @@ def _dense_reference(inp, lay, signs, c, m, sm_scale):
     return out.numpy()
 
 
-@pytest.mark.parametrize("preset", ["turboquant_4bit_nc", "turboquant_k3v4_nc", "turboquant_k8v4"])
-def test_decode_matches_dense_bruteforce(preset):
-    inp, lay, signs, c, m, cache = _tiny_case(preset)
+@pytest.mark.parametrize("preset", ["turboquant_4bit_nc", "turboquant_k3v4_nc", "turboquant_k8v4",
+                                    "turboquant_3bit_nc"])
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_decode_matches_dense_bruteforce(preset, d):
+    inp, lay, signs, c, m, cache = _tiny_case(preset, d=d)
     got = dec.decode_f64(inp.q, cache, inp.block_table, inp.seq_lens, lay, signs, c, 2)
-    ref = _dense_reference(inp, lay, signs, c, m, 1 / math.sqrt(128))
+    ref = _dense_reference(inp, lay, signs, c, m, 1 / math.sqrt(d))
     assert np.max(np.abs(got - ref)) < 1e-12
 
 

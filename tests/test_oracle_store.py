@@ -97,11 +97,11 @@ def _rand_keys(n, d, seed, outliers=True):
 
 
 @pytest.mark.parametrize("bits", [3, 4])
-def test_contract_agrees_with_float64_except_at_ties(bits):
-    d = 128
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_contract_agrees_with_float64_except_at_ties(bits, d):
     signs = rotation.rotation_signs(42, d)
     c, m = cb.codebook(d, bits)
-    kb = _rand_keys(20000, d, bits)
+    kb = _rand_keys(20000 if d == 128 else 6000, d, bits)
     codes, nrm, y32 = st.quantize_k_contract(kb, signs, m)
     y64 = st.rotate_unit_f64(kb, signs)
     assert np.max(np.abs(y32 - y64)) < 2e-7
@@ -178,10 +178,10 @@ def test_value_rounding_follows_float64_except_at_ties():
 
 
 @pytest.mark.parametrize("bits", [3, 4])
-def test_key_direction_distortion(bits):
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_key_direction_distortion(bits, d):
     """Reconstructing k / |k| as R^T c(code) gives the codebook's distortion
     (rotation makes every coordinate N(0, 1/d); P1, section "旋转的关键定理")."""
-    d = 128
     signs = rotation.rotation_signs(77, d)
     c, m = cb.codebook(d, bits)
     kb = _rand_keys(4000, d, 21)
